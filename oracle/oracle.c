@@ -1,0 +1,270 @@
+/*
+ * oracle.c -- float64 CPU oracle for the causal long convolution and its 2D variant.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path may link, load or call this file;
+ * only the tests, the smoke check and the bench's CPU-baseline leg use it. It shares no code,
+ * headers, tables or helpers with the HIP library.
+ *
+ * What it computes (the plain definitions, not the fast algorithm):
+ *
+ *  1D, causal.  "FlashFFTConv: Efficient Convolutions for Long Sequences with Tensor Cores"
+ *  (abstract) says the method speeds up *exact* FFT convolutions; "Simple Hardware-Efficient
+ *  Long Convolutions for Sequence Modeling" (abstract) frames the operator as a long
+ *  convolution over the sequence; the Caracal abstract (on the "RubiConv" page) makes an FFT
+ *  mixer causal by zero padding on one side and truncating.  With the FFT length at least
+ *  2N-1 the padded FFT product, truncated to N samples, equals the causal linear
+ *  convolution, so the oracle is that convolution summed directly:
+ *
+ *      x[b,h,s]  = q[b,h,s] * u[b,h,s]                    (q = 1 when absent)
+ *      y[b,h,t]  = v[b,h,t] * ( sum_{s=0..t} k[h,t-s] * x[b,h,s]  +  D[h] * x[b,h,t] )
+ *                                                          (v = 1 when absent)
+ *
+ *  2D, non-causal.  "Native Multi-Dimensional Subquadratic Operators via Input Dependent Long
+ *  Convolutions" (abstract) convolves images on their native grid with global kernels.  The
+ *  kernel k[c] has S x S taps, tap (a,b) sitting at offset (a - S/2, b - S/2); the full
+ *  linear convolution (size 2S-1) is cropped to the S x S window starting at (S/2, S/2):
+ *
+ *      y[b,c,i,j] = sum_{a,bb} k[c,a,bb] * u[b,c, i + S/2 - a, j + S/2 - bb] + D[c] * u[b,c,i,j]
+ *
+ *  with u = 0 outside [0,S)^2.
+ *
+ * Inputs arrive in their storage dtype (fp32, fp16 or bf16 bit patterns) and are widened
+ * exactly to double.  All sums run in ascending index order in double precision.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2 };
+
+/* IEEE binary16 -> double, exact (written out from the binary16 format definition). */
+static double or_half_to_double(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1f;
+    int mant = h & 0x3ff;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)mant, -24);                 /* subnormal: mant * 2^-24 */
+    else if (expo == 31)
+        v = mant ? NAN : INFINITY;
+    else
+        v = ldexp((double)(mant | 0x400), expo - 25); /* (1.mant) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* bfloat16 -> double, exact: the 16 bits are the top half of a binary32. */
+static double or_bf16_to_double(uint16_t h) {
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, 4);
+    return (double)f;
+}
+
+static double or_load(const void* p, int dt, int64_t i) {
+    switch (dt) {
+    case OR_F32: return (double)((const float*)p)[i];
+    case OR_F16: return or_half_to_double(((const uint16_t*)p)[i]);
+    default:     return or_bf16_to_double(((const uint16_t*)p)[i]);
+    }
+}
+
+static void or_widen(const void* p, int dt, int64_t off, int64_t n, double* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = or_load(p, dt, off + i);
+}
+
+/* Exported for the tests: widen n elements of a dtype array into doubles. */
+void oracle_widen(const void* p, int dt, int64_t n, double* out) { or_widen(p, dt, 0, n, out); }
+
+/* A job is one slice [lo, hi) of a selection list, run on one thread. */
+typedef struct {
+    const void *u, *q, *v, *k, *D;
+    int dt;
+    int64_t B, H, N;   /* 1D: batch, channels, length.  2D: batch, channels, side S. */
+    const int64_t* sel;
+    double* out;
+    int64_t lo, hi;
+} or_job;
+
+static void or_parallel(void* (*fn)(void*), or_job proto, int64_t n, int nthreads) {
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((int64_t)nthreads > n) nthreads = (int)(n > 0 ? n : 1);
+    or_job* jobs = (or_job*)calloc((size_t)nthreads, sizeof(or_job));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    int64_t per = (n + nthreads - 1) / nthreads;
+    int used = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        int64_t lo = (int64_t)i * per, hi = lo + per < n ? lo + per : n;
+        if (lo >= hi) break;
+        jobs[used] = proto;
+        jobs[used].lo = lo;
+        jobs[used].hi = hi;
+        pthread_create(&th[used], NULL, fn, &jobs[used]);
+        ++used;
+    }
+    for (int i = 0; i < used; ++i) pthread_join(th[i], NULL);
+    free(th);
+    free(jobs);
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* 1D                                                                                          */
+/* ------------------------------------------------------------------------------------------ */
+
+/* x[s] = q*u for s in [0, len) of row (b,h), widened. */
+static void or_row_x(const or_job* J, int64_t b, int64_t h, int64_t len, double* x) {
+    int64_t off = (b * J->H + h) * J->N;
+    or_widen(J->u, J->dt, off, len, x);
+    if (J->q)
+        for (int64_t s = 0; s < len; ++s) x[s] *= or_load(J->q, J->dt, off + s);
+}
+
+/* Full output rows.  Four outputs are carried at once so that their independent sums overlap
+ * in the FPU; each one is still accumulated in ascending s, exactly as the one-at-a-time
+ * loop would do it. */
+static void* or_rows_worker(void* arg) {
+    or_job* J = (or_job*)arg;
+    const int64_t N = J->N;
+    double* x = (double*)malloc(sizeof(double) * (size_t)N);
+    double* k = (double*)malloc(sizeof(double) * (size_t)N);
+    for (int64_t r = J->lo; r < J->hi; ++r) {
+        int64_t b = J->sel[2 * r], h = J->sel[2 * r + 1];
+        or_row_x(J, b, h, N, x);
+        or_widen(J->k, J->dt, h * N, N, k);
+        double d = or_load(J->D, J->dt, h);
+        double* y = J->out + r * N;
+        int64_t t0 = 0;
+        for (; t0 + 4 <= N; t0 += 4) {
+            double a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+            for (int64_t s = 0; s <= t0; ++s) {
+                double xs = x[s];
+                a0 += k[t0 - s] * xs;
+                a1 += k[t0 + 1 - s] * xs;
+                a2 += k[t0 + 2 - s] * xs;
+                a3 += k[t0 + 3 - s] * xs;
+            }
+            a1 += k[0] * x[t0 + 1];
+            a2 += k[1] * x[t0 + 1];
+            a2 += k[0] * x[t0 + 2];
+            a3 += k[2] * x[t0 + 1];
+            a3 += k[1] * x[t0 + 2];
+            a3 += k[0] * x[t0 + 3];
+            y[t0] = a0; y[t0 + 1] = a1; y[t0 + 2] = a2; y[t0 + 3] = a3;
+        }
+        for (; t0 < N; ++t0) {
+            double a = 0;
+            for (int64_t s = 0; s <= t0; ++s) a += k[t0 - s] * x[s];
+            y[t0] = a;
+        }
+        int64_t off = (b * J->H + h) * N;
+        for (int64_t t = 0; t < N; ++t) {
+            double val = y[t] + d * x[t];
+            if (J->v) val *= or_load(J->v, J->dt, off + t);
+            y[t] = val;
+        }
+    }
+    free(x);
+    free(k);
+    return NULL;
+}
+
+/* Single output positions (b,h,t); each costs t+1 multiply-adds. */
+static void* or_points_worker(void* arg) {
+    or_job* J = (or_job*)arg;
+    const int64_t N = J->N;
+    for (int64_t r = J->lo; r < J->hi; ++r) {
+        int64_t b = J->sel[3 * r], h = J->sel[3 * r + 1], t = J->sel[3 * r + 2];
+        int64_t off = (b * J->H + h) * N;
+        double a = 0;
+        for (int64_t s = 0; s <= t; ++s) {
+            double xs = or_load(J->u, J->dt, off + s);
+            if (J->q) xs *= or_load(J->q, J->dt, off + s);
+            a += or_load(J->k, J->dt, h * N + (t - s)) * xs;
+        }
+        double xt = or_load(J->u, J->dt, off + t);
+        if (J->q) xt *= or_load(J->q, J->dt, off + t);
+        double val = a + or_load(J->D, J->dt, h) * xt;
+        if (J->v) val *= or_load(J->v, J->dt, off + t);
+        J->out[r] = val;
+    }
+    return NULL;
+}
+
+static int or_check1d(const void* u, const void* k, const void* D, const int64_t* sel,
+                      int64_t nsel, double* out, int64_t B, int64_t H, int64_t N, int dt) {
+    if (!u || !k || !D || !out || (nsel > 0 && !sel)) return -1;
+    if (B < 1 || H < 1 || N < 1 || nsel < 0 || dt < 0 || dt > 2) return -1;
+    return 0;
+}
+
+/* Full rows y[b,h,0:N] for each (b,h) in rows[2*nrows]; out is [nrows][N]. */
+int oracle_conv1d_rows(const void* u, const void* q, const void* v, const void* k, const void* D,
+                       int dt, int64_t B, int64_t H, int64_t N, const int64_t* rows,
+                       int64_t nrows, double* out, int nthreads) {
+    if (or_check1d(u, k, D, rows, nrows, out, B, H, N, dt)) return -1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[2 * r] < 0 || rows[2 * r] >= B || rows[2 * r + 1] < 0 || rows[2 * r + 1] >= H)
+            return -1;
+    or_job J = {u, q, v, k, D, dt, B, H, N, rows, out, 0, 0};
+    or_parallel(or_rows_worker, J, nrows, nthreads);
+    return 0;
+}
+
+/* Output values y[b,h,t] for each (b,h,t) in pts[3*npts]; out is [npts]. */
+int oracle_conv1d_points(const void* u, const void* q, const void* v, const void* k,
+                         const void* D, int dt, int64_t B, int64_t H, int64_t N,
+                         const int64_t* pts, int64_t npts, double* out, int nthreads) {
+    if (or_check1d(u, k, D, pts, npts, out, B, H, N, dt)) return -1;
+    for (int64_t r = 0; r < npts; ++r)
+        if (pts[3 * r] < 0 || pts[3 * r] >= B || pts[3 * r + 1] < 0 || pts[3 * r + 1] >= H ||
+            pts[3 * r + 2] < 0 || pts[3 * r + 2] >= N)
+            return -1;
+    or_job J = {u, q, v, k, D, dt, B, H, N, pts, out, 0, 0};
+    or_parallel(or_points_worker, J, npts, nthreads);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* 2D: direct summation at single positions                                                    */
+/* ------------------------------------------------------------------------------------------ */
+
+static void* or_points2d_worker(void* arg) {
+    or_job* J = (or_job*)arg;
+    const int64_t S = J->N, C = J->H, half = S / 2;
+    for (int64_t r = J->lo; r < J->hi; ++r) {
+        int64_t b = J->sel[4 * r], c = J->sel[4 * r + 1];
+        int64_t i = J->sel[4 * r + 2], j = J->sel[4 * r + 3];
+        int64_t uoff = (b * C + c) * S * S, koff = c * S * S;
+        double acc = 0;
+        for (int64_t a = 0; a < S; ++a) {
+            int64_t ii = i + half - a;
+            if (ii < 0 || ii >= S) continue;
+            for (int64_t bb = 0; bb < S; ++bb) {
+                int64_t jj = j + half - bb;
+                if (jj < 0 || jj >= S) continue;
+                acc += or_load(J->k, J->dt, koff + a * S + bb) *
+                       or_load(J->u, J->dt, uoff + ii * S + jj);
+            }
+        }
+        J->out[r] = acc + or_load(J->D, J->dt, c) * or_load(J->u, J->dt, uoff + i * S + j);
+    }
+    return NULL;
+}
+
+/* y[b,c,i,j] for each (b,c,i,j) in pts[4*npts]; u is [B][C][S][S], k is [C][S][S], D is [C]. */
+int oracle_conv2d_points(const void* u, const void* k, const void* D, int dt, int64_t B,
+                         int64_t C, int64_t S, const int64_t* pts, int64_t npts, double* out,
+                         int nthreads) {
+    if (!u || !k || !D || !out || (npts > 0 && !pts)) return -1;
+    if (B < 1 || C < 1 || S < 2 || (S % 2) || npts < 0 || dt < 0 || dt > 2) return -1;
+    for (int64_t r = 0; r < npts; ++r)
+        if (pts[4 * r] < 0 || pts[4 * r] >= B || pts[4 * r + 1] < 0 || pts[4 * r + 1] >= C ||
+            pts[4 * r + 2] < 0 || pts[4 * r + 2] >= S || pts[4 * r + 3] < 0 ||
+            pts[4 * r + 3] >= S)
+            return -1;
+    or_job J = {u, NULL, NULL, k, D, dt, B, C, S, pts, out, 0, 0};
+    or_parallel(or_points2d_worker, J, npts, nthreads);
+    return 0;
+}

@@ -1,0 +1,211 @@
+"""float64 CPU oracle: ctypes wrappers over oracle.c plus a naive-DFT 2D oracle in numpy.
+
+TEST INFRASTRUCTURE ONLY.  Used by tests/, the smoke check and the bench's CPU-baseline leg;
+never by the product path.  Shares no code with the HIP library.
+
+Definitions (restated from the pages; the derivation is in oracle.c's header):
+
+* 1D causal long convolution -- "FlashFFTConv: Efficient Convolutions for Long Sequences with
+  Tensor Cores" (abstract: the method computes exact FFT convolutions) and the Caracal abstract
+  on the "RubiConv" page (causality from one-sided zero padding plus truncation):
+      y[b,h,t] = v[b,h,t] * ( sum_{s<=t} k[h,t-s] x[b,h,s] + D[h] x[b,h,t] ),  x = q*u.
+* 2D linear (non-circular) convolution with a centred, full-size kernel -- "Native
+  Multi-Dimensional Subquadratic Operators via Input Dependent Long Convolutions" (abstract):
+      y[b,c,i,j] = sum_{a,bb} k[c,a,bb] u[b,c,i+S/2-a,j+S/2-bb] + D[c] u[b,c,i,j].
+
+Arrays are passed in their storage dtype: float32, float16, or bfloat16 carried as uint16 bit
+patterns (the caller says which via ``dt``).  The C code widens them exactly to float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+DT_F32, DT_F16, DT_BF16 = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (host code only)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-pthread", "-std=c11",
+                               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        vp, i64, dp, ip = ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        lib.oracle_conv1d_rows.argtypes = [vp, vp, vp, vp, vp, ip, i64, i64, i64, vp, i64, dp, ip]
+        lib.oracle_conv1d_points.argtypes = [vp, vp, vp, vp, vp, ip, i64, i64, i64, vp, i64, dp, ip]
+        lib.oracle_conv2d_points.argtypes = [vp, vp, vp, ip, i64, i64, i64, vp, i64, dp, ip]
+        lib.oracle_widen.argtypes = [vp, ip, i64, dp]
+        for f in (lib.oracle_conv1d_rows, lib.oracle_conv1d_points, lib.oracle_conv2d_points):
+            f.restype = ctypes.c_int
+        lib.oracle_widen.restype = None
+        _lib = lib
+    return _lib
+
+
+def _dt_of(a: np.ndarray, dt):
+    if dt is not None:
+        return dt
+    if a.dtype == np.float32:
+        return DT_F32
+    if a.dtype == np.float16:
+        return DT_F16
+    raise ValueError("uint16 arrays are bfloat16 bit patterns: pass dt=DT_BF16 explicitly")
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {dtype}, got {a.dtype}")
+    return a
+
+
+def _storage(dt):
+    return {DT_F32: np.float32, DT_F16: np.float16, DT_BF16: np.uint16}[dt]
+
+
+def _threads(nthreads):
+    if nthreads:
+        return int(nthreads)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def widen(a: np.ndarray, dt=None) -> np.ndarray:
+    """Exact float64 value of every element of a storage-dtype array (C widening)."""
+    dt = _dt_of(a, dt)
+    a = _c(a, _storage(dt))
+    out = np.empty(a.size, np.float64)
+    _load().oracle_widen(_ptr(a), dt, a.size, out.ctypes.data)
+    return out.reshape(a.shape)
+
+
+def conv1d_rows(u, k, D, rows, q=None, v=None, dt=None, nthreads=None):
+    """Full output rows: returns float64 [len(rows), N] for rows = [(b,h), ...]."""
+    dt = _dt_of(u, dt)
+    st = _storage(dt)
+    u, k, D, q, v = (_c(a, st) for a in (u, k, D, q, v))
+    B, H, N = u.shape
+    assert k.shape == (H, N) and D.shape == (H,)
+    rows = np.ascontiguousarray(np.asarray(rows, np.int64).reshape(-1, 2))
+    out = np.empty((rows.shape[0], N), np.float64)
+    rc = _load().oracle_conv1d_rows(_ptr(u), _ptr(q), _ptr(v), _ptr(k), _ptr(D), dt, B, H, N,
+                                    _ptr(rows), rows.shape[0], out.ctypes.data,
+                                    _threads(nthreads))
+    if rc:
+        raise ValueError("oracle_conv1d_rows rejected its arguments")
+    return out
+
+
+def conv1d_points(u, k, D, pts, q=None, v=None, dt=None, nthreads=None):
+    """Single outputs y[b,h,t] for pts = [(b,h,t), ...]; returns float64 [len(pts)]."""
+    dt = _dt_of(u, dt)
+    st = _storage(dt)
+    u, k, D, q, v = (_c(a, st) for a in (u, k, D, q, v))
+    B, H, N = u.shape
+    pts = np.ascontiguousarray(np.asarray(pts, np.int64).reshape(-1, 3))
+    out = np.empty(pts.shape[0], np.float64)
+    rc = _load().oracle_conv1d_points(_ptr(u), _ptr(q), _ptr(v), _ptr(k), _ptr(D), dt, B, H, N,
+                                      _ptr(pts), pts.shape[0], out.ctypes.data,
+                                      _threads(nthreads))
+    if rc:
+        raise ValueError("oracle_conv1d_points rejected its arguments")
+    return out
+
+
+def conv2d_points(u, k, D, pts, dt=None, nthreads=None):
+    """Direct 2D sums y[b,c,i,j] for pts = [(b,c,i,j), ...]; returns float64 [len(pts)]."""
+    dt = _dt_of(u, dt)
+    st = _storage(dt)
+    u, k, D = (_c(a, st) for a in (u, k, D))
+    B, C, S, S2 = u.shape
+    assert S == S2 and k.shape == (C, S, S) and D.shape == (C,)
+    pts = np.ascontiguousarray(np.asarray(pts, np.int64).reshape(-1, 4))
+    out = np.empty(pts.shape[0], np.float64)
+    rc = _load().oracle_conv2d_points(_ptr(u), _ptr(k), _ptr(D), dt, B, C, S, _ptr(pts),
+                                      pts.shape[0], out.ctypes.data, _threads(nthreads))
+    if rc:
+        raise ValueError("oracle_conv2d_points rejected its arguments")
+    return out
+
+
+def _dft_matrix(P: int, rows, cols, sign: int) -> np.ndarray:
+    """exp(sign * 2*pi*i * (r*c mod P) / P) with the exponent reduced exactly in integers."""
+    r = np.asarray(rows, np.int64)[:, None]
+    c = np.asarray(cols, np.int64)[None, :]
+    red = (r * c) % P
+    ang = (2.0 * np.pi / P) * red.astype(np.float64)
+    return np.cos(ang) + sign * 1j * np.sin(ang)
+
+
+def conv2d_dft(u, k, D, images, dt=None, P=None):
+    """Naive separable-DFT 2D oracle (independent of the direct sums).
+
+    For each image (b,c): zero pad u and k from S x S to P x P (P >= 2S-1, default 2S, so the
+    product of spectra is a *linear* convolution), multiply the 2D DFTs, invert only the
+    S x S window of rows/columns [S/2, S/2+S) and add D*u.  The DFTs are explicit matrices
+    applied with matmul; no FFT routine is involved.  Returns float64 [len(images), S, S].
+    """
+    dt = _dt_of(u, dt)
+    uw = widen(u, dt)
+    kw = widen(k, dt)
+    Dw = widen(D, dt)
+    B, C, S, _ = uw.shape
+    P = P or 2 * S
+    assert P >= 2 * S - 1
+    F = _dft_matrix(P, range(P), range(S), -1)                 # [P, S]  forward, nonzero part
+    G = _dft_matrix(P, range(S // 2, S // 2 + S), range(P), +1)  # [S, P] inverse, crop rows
+    out = []
+    kf_cache = {}
+    for (b, c) in np.asarray(images, np.int64).reshape(-1, 2):
+        b, c = int(b), int(c)
+        if c not in kf_cache:
+            kf_cache[c] = F @ kw[c] @ F.T
+        U = F @ uw[b, c] @ F.T
+        Y = (G @ (U * kf_cache[c]) @ G.T) / (P * P)
+        out.append(Y.real + Dw[c] * uw[b, c])
+    return np.stack(out) if out else np.zeros((0, S, S))
+
+
+# --------------------------------------------------------------------------------------------
+# Small-case references used to pin the C oracle (pure Python / explicit matrices).
+# --------------------------------------------------------------------------------------------
+
+def conv1d_toeplitz(x: np.ndarray, k: np.ndarray, d: float) -> np.ndarray:
+    """y = T x + d x with T[t,s] = k[t-s] for s <= t (explicit lower-triangular Toeplitz)."""
+    N = x.shape[-1]
+    T = np.zeros((N, N), np.float64)
+    for t in range(N):
+        T[t, : t + 1] = k[t::-1]
+    return T @ x + d * x
+
+
+def conv1d_python_int(x, k, d):
+    """Exact integer causal convolution with Python ints (for N <= 64 brute force)."""
+    N = len(x)
+    return [sum(int(k[t - s]) * int(x[s]) for s in range(t + 1)) + int(d) * int(x[t])
+            for t in range(N)]
