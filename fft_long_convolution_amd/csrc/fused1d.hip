@@ -1,0 +1,525 @@
+// fused1d.hip -- the fused causal FFT convolution for transform lengths M = 256 R <= 8192.
+//
+// One workgroup (8 waves) transforms 32 tiles of 256 points at a time: one (pair of) sequence
+// rows when R = 32, or 32 / R of them for shorter transforms.  Digits:
+//     n = 256 n1 + 16 n2 + n3,     f = k1 + R k2 + 16 R k3.
+// Forward (zero-padded input: n1 < R/2 only):
+//   F1  radix-R over n1, matrix-core blocks, columns (n2, n3)              LDS V -> LDS XY
+//   F2  radix-16 over n2 with w_{16R}^{n2 k1} folded into the block         registers
+//   T   w_256^{n3 k2} (the only twiddle that needs the vector ALU)         registers
+//   F3  radix-16 over n3 with w_M^{n3 k1} folded into the block            registers
+// Pointwise product with the filter spectrum (D folded in: (K + D) / M), then the mirror
+// image of the forward chain, and I3 computes only n1 < R/2: the causal truncation
+// (Caracal abstract on the "RubiConv" page).  Two real rows b, b+1 with the same filter ride
+// in one complex sequence x_b + i x_{b+1}: the filter is real, so the real and imaginary
+// parts of the result are the two convolutions.
+//
+// The chain follows the fusion the pages describe -- FFT, pointwise spectral product and
+// inverse FFT with no intermediate off-chip traffic ("FlashConv" page, Mechanism; FlashFFTConv
+// abstract) -- and the block-matrix form of the FFT (same passages).  Block sizes, the
+// register-resident tiles and the twiddle folding are this implementation's own.
+#include "kernels.h"
+#include "lconv_device.h"
+
+namespace lcv {
+
+namespace {
+
+template <int IO>
+__device__ __forceinline__ float load1(const void* base, int64_t i) {
+    if constexpr (IO == CT_F32) {
+        return ((const float*)base)[i];
+    } else {
+        uint32_t w = ((const uint16_t*)base)[i];
+        return unpack_lo<IO>(w);
+    }
+}
+
+template <int IO>
+__device__ __forceinline__ void load8(const void* base, int64_t off, float* x) {
+    if constexpr (IO == CT_F32) {
+        const float4* p = (const float4*)((const float*)base + off);
+        float4 a = p[0], b = p[1];
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else {
+        uint4 w = *(const uint4*)((const uint16_t*)base + off);
+        x[0] = unpack_lo<IO>(w.x); x[1] = unpack_hi<IO>(w.x);
+        x[2] = unpack_lo<IO>(w.y); x[3] = unpack_hi<IO>(w.y);
+        x[4] = unpack_lo<IO>(w.z); x[5] = unpack_hi<IO>(w.z);
+        x[6] = unpack_lo<IO>(w.w); x[7] = unpack_hi<IO>(w.w);
+    }
+}
+
+template <int IO>
+__device__ __forceinline__ void store8(void* base, int64_t off, const float* x) {
+    if constexpr (IO == CT_F32) {
+        float4* p = (float4*)((float*)base + off);
+        p[0] = make_float4(x[0], x[1], x[2], x[3]);
+        p[1] = make_float4(x[4], x[5], x[6], x[7]);
+    } else {
+        uint4 w;
+        w.x = pack2<IO>(x[0], x[1]);
+        w.y = pack2<IO>(x[2], x[3]);
+        w.z = pack2<IO>(x[4], x[5]);
+        w.w = pack2<IO>(x[6], x[7]);
+        *(uint4*)((uint16_t*)base + off) = w;
+    }
+}
+
+// 4 consecutive complex values of a spectrum stored in type IO -> fp32.
+template <int IO>
+__device__ __forceinline__ void load_c4(const void* base, int64_t off, float* re, float* im) {
+    if constexpr (IO == CT_F32) {
+        const float4* p = (const float4*)((const float*)base + 2 * off);
+        float4 a = p[0], b = p[1];
+        re[0] = a.x; im[0] = a.y; re[1] = a.z; im[1] = a.w;
+        re[2] = b.x; im[2] = b.y; re[3] = b.z; im[3] = b.w;
+    } else {
+        uint4 w = *(const uint4*)((const uint32_t*)base + off);
+        re[0] = unpack_lo<IO>(w.x); im[0] = unpack_hi<IO>(w.x);
+        re[1] = unpack_lo<IO>(w.y); im[1] = unpack_hi<IO>(w.y);
+        re[2] = unpack_lo<IO>(w.z); im[2] = unpack_hi<IO>(w.z);
+        re[3] = unpack_lo<IO>(w.w); im[3] = unpack_hi<IO>(w.w);
+    }
+}
+
+template <int IO>
+__device__ __forceinline__ void store_c4(void* base, int64_t off, const float* re, const float* im) {
+    if constexpr (IO == CT_F32) {
+        float4* p = (float4*)((float*)base + 2 * off);
+        p[0] = make_float4(re[0], im[0], re[1], im[1]);
+        p[1] = make_float4(re[2], im[2], re[3], im[3]);
+    } else {
+        uint4 w;
+        w.x = pack2<IO>(re[0], im[0]);
+        w.y = pack2<IO>(re[1], im[1]);
+        w.z = pack2<IO>(re[2], im[2]);
+        w.w = pack2<IO>(re[3], im[3]);
+        *(uint4*)((uint32_t*)base + off) = w;
+    }
+}
+
+// LDS complex element in compute type: one packed word (16-bit) or two floats.
+template <int CT>
+__device__ __forceinline__ void lds_put(uint32_t* base, int idx, float re, float im) {
+    if constexpr (CT == CT_F32) {
+        *(float2*)(base + 2 * idx) = make_float2(re, im);
+    } else {
+        base[idx] = pack2<CT>(re, im);
+    }
+}
+
+// Read a tile operand: element (K index 4g + j, L index c) at base + idx(j).
+template <int CT, typename F>
+__device__ __forceinline__ Operand<CT> lds_operand(const uint32_t* base, F idx) {
+    Operand<CT> o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = idx(j);
+        if constexpr (CT == CT_F32) {
+            float2 v = e >= 0 ? *(const float2*)(base + 2 * e) : make_float2(0.f, 0.f);
+            o.s[2 * j] = v.x;
+            o.s[2 * j + 1] = v.y;
+        } else {
+            o.w[j] = e >= 0 ? base[e] : 0u;
+        }
+    }
+    return o;
+}
+
+}  // namespace
+
+template <int R, int CT, int IO, int MODE, bool GATED>
+__global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
+    constexpr int P = 32 / R;                  // sequences per workgroup iteration
+    constexpr int M = 256 * R;
+    constexpr bool HALF_IN = (MODE == MODE_CONV || MODE == MODE_FILTER);
+    constexpr bool HALF_OUT = (MODE == MODE_CONV);
+    constexpr bool INV = (MODE == MODE_CONV || MODE == MODE_ROW);
+    constexpr int NIN = HALF_IN ? R / 2 : R;   // nonzero n1 rows
+    constexpr int NOUT = HALF_OUT ? R / 2 : R; // n1 rows produced
+    constexpr int KCF = (R + 15) / 16;         // table grid (full variant)
+    constexpr int KC1 = (NIN + 15) / 16;
+    constexpr int RB1 = (R + 15) / 16;
+    constexpr int KC3 = (R + 15) / 16;
+    constexpr int RB3 = (NOUT + 15) / 16;
+    constexpr int EW = CT == CT_F32 ? 2 : 1;   // LDS words per complex element
+    constexpr int SV = 260;                    // V: row stride (elements) per n1 row
+    constexpr int ST = 324, SR = 20;           // XY: tile stride, row stride inside a tile
+    constexpr int SO = 260;                    // O: row stride (complex fp32)
+    constexpr int V_W = P * NIN * SV * EW;
+    constexpr int XY_W = 32 * ST * EW;
+    // fp32 row pass: O (same size as V) aliases V, with one extra barrier per iteration
+    constexpr bool O_ALIAS = (MODE == MODE_ROW && CT == CT_F32);
+    constexpr int O_W = (INV && !O_ALIAS) ? P * NOUT * SO * 2 : 0;
+    constexpr bool RES = (CT != CT_F32);       // matrix images resident in registers
+    constexpr int IMG = ImgBytes<CT>::value;
+    constexpr int T_F1 = 0;
+    constexpr int T_I3 = T_F1 + IMG * RB1 * KCF;
+    constexpr int T_F2 = T_I3 + IMG * KCF * KCF;
+    constexpr int T_F3 = T_F2 + IMG * R;
+    constexpr int T_I1 = T_F3 + IMG * R;
+    constexpr int T_I2 = T_I1 + IMG * R;
+    constexpr int T_TW = T_I2 + IMG * R;
+    constexpr int NBLK = P * 16;               // (sequence, n2) column blocks
+    constexpr int BPW = NBLK / 8;              // blocks per wave
+
+    __shared__ __attribute__((aligned(16))) uint32_t lds[V_W + XY_W + O_W];
+    uint32_t* V = lds;
+    uint32_t* XY = lds + V_W;
+    float* O = (float*)(O_ALIAS ? lds : lds + V_W + XY_W);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    const char* tab = (const char*)a.tables;
+
+    // ---- loop-invariant registers: twiddles and matrix images ------------------------------
+    float twr[4], twi[4];
+    {
+        const float4* tp = (const float4*)(tab + T_TW) + lane * 2;
+        float4 t0 = tp[0], t1 = tp[1];
+        twr[0] = t0.x; twi[0] = t0.y; twr[1] = t0.z; twi[1] = t0.w;
+        twr[2] = t1.x; twi[2] = t1.y; twr[3] = t1.z; twi[3] = t1.w;
+    }
+    MatImg<CT> mf2[4], mf3[4], mi1[4], mi2[4], mf1[RB1][KC1], mi3[RB3][KC3];
+    if constexpr (RES) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k1 = (wave * 4 + i) % R;
+            mf2[i] = load_img<CT>(tab + T_F2, k1, lane);
+            mf3[i] = load_img<CT>(tab + T_F3, k1, lane);
+            if constexpr (INV) {
+                mi1[i] = load_img<CT>(tab + T_I1, k1, lane);
+                mi2[i] = load_img<CT>(tab + T_I2, k1, lane);
+            }
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB1; ++rb)
+#pragma unroll
+            for (int kc = 0; kc < KC1; ++kc) mf1[rb][kc] = load_img<CT>(tab + T_F1, rb * KCF + kc, lane);
+        if constexpr (INV) {
+#pragma unroll
+            for (int rb = 0; rb < RB3; ++rb)
+#pragma unroll
+                for (int kc = 0; kc < KC3; ++kc) mi3[rb][kc] = load_img<CT>(tab + T_I3, rb * KCF + kc, lane);
+        }
+    }
+    auto F1 = [&](int rb, int kc) { return RES ? mf1[rb][kc] : load_img<CT>(tab + T_F1, rb * KCF + kc, lane); };
+    auto I3 = [&](int rb, int kc) { return RES ? mi3[rb][kc] : load_img<CT>(tab + T_I3, rb * KCF + kc, lane); };
+    auto F2 = [&](int i) { return RES ? mf2[i] : load_img<CT>(tab + T_F2, (wave * 4 + i) % R, lane); };
+    auto F3 = [&](int i) { return RES ? mf3[i] : load_img<CT>(tab + T_F3, (wave * 4 + i) % R, lane); };
+    auto I1 = [&](int i) { return RES ? mi1[i] : load_img<CT>(tab + T_I1, (wave * 4 + i) % R, lane); };
+    auto I2 = [&](int i) { return RES ? mi2[i] : load_img<CT>(tab + T_I2, (wave * 4 + i) % R, lane); };
+
+    const int64_t Bp = (a.B + 1) / 2;  // pairs per channel (CONV)
+    const int64_t first = (int64_t)blockIdx.x * a.per_wg;
+    const int64_t last = first + a.per_wg < a.nitems ? first + a.per_wg : a.nitems;
+
+    for (int64_t it0 = first; it0 < last; it0 += P) {
+        // ================= P0: inputs -> V =================================================
+        if constexpr (HALF_IN) {
+            const int p = tid / (16 * R), n0 = 8 * (tid % (16 * R));
+            const int64_t item = it0 + p;
+            float xr[8], xi[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) { xr[i] = 0.f; xi[i] = 0.f; }
+            if (item < last && n0 < a.N) {
+                if constexpr (MODE == MODE_CONV) {
+                    const int64_t h = item / Bp, b = 2 * (item % Bp);
+                    const int64_t o0 = (b * a.H + h) * a.N + n0;
+                    load8<IO>(a.u, o0, xr);
+                    if (GATED && a.q) {
+                        float t[8];
+                        load8<IO>(a.q, o0, t);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) xr[i] *= t[i];
+                    }
+                    if (b + 1 < a.B) {
+                        const int64_t o1 = o0 + a.H * a.N;
+                        load8<IO>(a.u, o1, xi);
+                        if (GATED && a.q) {
+                            float t[8];
+                            load8<IO>(a.q, o1, t);
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) xi[i] *= t[i];
+                        }
+                    }
+                } else {  // FILTER: one real channel per sequence
+                    load8<IO>(a.u, item * a.N + n0, xr);
+                }
+            }
+            uint32_t* dst = V + ((p * NIN + (n0 >> 8)) * SV + (n0 & 255)) * EW;
+            if constexpr (CT == CT_F32) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    ((float4*)dst)[i] = make_float4(xr[2 * i], xi[2 * i], xr[2 * i + 1], xi[2 * i + 1]);
+            } else {
+                uint4 w0, w1;
+                w0.x = pack2<CT>(xr[0], xi[0]); w0.y = pack2<CT>(xr[1], xi[1]);
+                w0.z = pack2<CT>(xr[2], xi[2]); w0.w = pack2<CT>(xr[3], xi[3]);
+                w1.x = pack2<CT>(xr[4], xi[4]); w1.y = pack2<CT>(xr[5], xi[5]);
+                w1.z = pack2<CT>(xr[6], xi[6]); w1.w = pack2<CT>(xr[7], xi[7]);
+                ((uint4*)dst)[0] = w0;
+                ((uint4*)dst)[1] = w1;
+            }
+        } else {  // ROW / ROWFWD: one complex row of 8192 from the workspace (P == 1)
+            const int64_t item = it0;
+            const uint32_t* src = (const uint32_t*)a.u + item * (int64_t)M * EW;
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int n0 = 8 * (tid + 512 * r);
+                uint32_t* dst = V + ((n0 >> 8) * SV + (n0 & 255)) * EW;
+#pragma unroll
+                for (int i = 0; i < 2 * EW; ++i)
+                    ((uint4*)dst)[i] = ((const uint4*)(src + (int64_t)n0 * EW))[i];
+            }
+        }
+
+        // filter spectrum for this wave's tiles (issued before the transforms need it)
+        float kr[4][4], ki[4][4];
+        if constexpr (INV) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = wave * 4 + i, p = t / R, k1 = t % R;
+                const int64_t item = it0 + p;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) { kr[i][j] = 0.f; ki[i][j] = 0.f; }
+                if (item < last) {
+                    int64_t h, base;
+                    if constexpr (MODE == MODE_CONV) {
+                        h = item / Bp;
+                        base = h * M;
+                    } else {
+                        const int64_t s = a.seq0 + item / a.M1, khi = item % a.M1;
+                        h = s / a.seq_per_h;
+                        base = h * a.M + khi * M;
+                    }
+                    load_c4<IO>(a.kf, base + ((int64_t)k1 * 64 + lane) * 4, kr[i], ki[i]);
+                    const float d = load1<IO>(a.D, h) * a.inv_m;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) kr[i][j] += d;
+                }
+            }
+        }
+        __syncthreads();
+
+        // ================= P1: F1 (radix R over n1), V -> XY =================================
+#pragma unroll 2
+        for (int bi = 0; bi < BPW; ++bi) {
+            const int blk = wave * BPW + bi, p = blk >> 4, b = blk & 15;
+            Operand<CT> din[KC1];
+#pragma unroll
+            for (int kc = 0; kc < KC1; ++kc)
+                din[kc] = lds_operand<CT>(V, [&](int j) {
+                    const int n1 = 16 * kc + 4 * g + j;
+                    return n1 < NIN ? (p * NIN + n1) * SV + 16 * b + c : -1;
+                });
+#pragma unroll
+            for (int rb = 0; rb < RB1; ++rb) {
+                f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kc = 0; kc < KC1; ++kc) stage_keep_acc<CT>(F1(rb, kc), din[kc], re, im);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int k1 = 16 * rb + 4 * g + j;
+                    if (k1 < R) lds_put<CT>(XY, (p * R + k1) * ST + b * SR + c, re[j], im[j]);
+                }
+            }
+        }
+        __syncthreads();
+
+        // ================= P2: F2, twiddle, F3, product, I1, twiddle, I2 (registers) =========
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = wave * 4 + i;
+            Operand<CT> d = lds_operand<CT>(XY, [&](int j) { return t * ST + (4 * g + j) * SR + c; });
+            Tile x = stage_swap<CT>(F2(i), d);  // (L = k2, K = n3)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cmul(x.re[j], x.im[j], twr[j], twi[j]);
+            x = stage_keep<CT>(F3(i), to_operand<CT>(x));  // (L = k2, K = k3)
+            if constexpr (!INV) {
+                // spectrum in transform order, scaled by 1/M
+                const int p = t / R, k1 = t % R;
+                const int64_t item = it0 + p;
+                if (item < last) {
+                    int64_t base;
+                    if constexpr (MODE == MODE_FILTER) {
+                        base = item * M;
+                    } else {
+                        const int64_t h = a.seq0 + item / a.M1, khi = item % a.M1;
+                        base = h * a.M + khi * M;
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) { x.re[j] *= a.inv_m; x.im[j] *= a.inv_m; }
+                    store_c4<IO>(a.y, base + ((int64_t)k1 * 64 + lane) * 4, x.re, x.im);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) cmul(x.re[j], x.im[j], kr[i][j], ki[i][j]);
+                x = stage_swap<CT>(I1(i), to_operand<CT>(x));  // (L = n3, K = k2)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) cmulc(x.re[j], x.im[j], twr[j], twi[j]);
+                x = stage_keep<CT>(I2(i), to_operand<CT>(x));  // (L = n3, K = n2)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) lds_put<CT>(XY, t * ST + (4 * g + j) * SR + c, x.re[j], x.im[j]);
+            }
+        }
+        if constexpr (!INV) {
+            __syncthreads();  // V / XY are rewritten by the next iteration
+            continue;
+        }
+        __syncthreads();
+
+        // ================= P3: I3 (inverse radix R over k1, n1 < NOUT), XY -> O ================
+#pragma unroll 2
+        for (int bi = 0; bi < BPW; ++bi) {
+            const int blk = wave * BPW + bi, p = blk >> 4, b = blk & 15;
+            Operand<CT> din[KC3];
+#pragma unroll
+            for (int kc = 0; kc < KC3; ++kc)
+                din[kc] = lds_operand<CT>(XY, [&](int j) {
+                    const int k1 = 16 * kc + 4 * g + j;
+                    return k1 < R ? (p * R + k1) * ST + b * SR + c : -1;
+                });
+#pragma unroll
+            for (int rb = 0; rb < RB3; ++rb) {
+                f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kc = 0; kc < KC3; ++kc) stage_keep_acc<CT>(I3(rb, kc), din[kc], re, im);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int n1 = 16 * rb + 4 * g + j;
+                    if (n1 < NOUT) *(float2*)(O + 2 * ((p * NOUT + n1) * SO + 16 * b + c)) = make_float2(re[j], im[j]);
+                }
+            }
+        }
+        __syncthreads();
+
+        // ================= P4: epilogue ======================================================
+        if constexpr (MODE == MODE_CONV) {
+            const int p = tid / (16 * R), n0 = 8 * (tid % (16 * R));
+            const int64_t item = it0 + p;
+            if (item < last && n0 < a.N) {
+                const int64_t h = item / Bp, b = 2 * (item % Bp);
+                const float4* src = (const float4*)(O + 2 * ((p * NOUT + (n0 >> 8)) * SO + (n0 & 255)));
+                float yr[8], yi[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float4 w = src[i];
+                    yr[2 * i] = w.x; yi[2 * i] = w.y; yr[2 * i + 1] = w.z; yi[2 * i + 1] = w.w;
+                }
+                const int64_t o0 = (b * a.H + h) * a.N + n0;
+                if (GATED && a.v) {
+                    float t[8];
+                    load8<IO>(a.v, o0, t);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) yr[i] *= t[i];
+                }
+                store8<IO>(a.y, o0, yr);
+                if (b + 1 < a.B) {
+                    const int64_t o1 = o0 + a.H * a.N;
+                    if (GATED && a.v) {
+                        float t[8];
+                        load8<IO>(a.v, o1, t);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) yi[i] *= t[i];
+                    }
+                    store8<IO>(a.y, o1, yi);
+                }
+            }
+        } else {  // ROW: complex row back to the workspace, in compute type
+            uint32_t* dstrow = (uint32_t*)a.y + it0 * (int64_t)M * EW;
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int n0 = 8 * (tid + 512 * r);
+                const float4* src = (const float4*)(O + 2 * ((n0 >> 8) * SO + (n0 & 255)));
+                float w[16];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float4 s = src[i];
+                    w[4 * i] = s.x; w[4 * i + 1] = s.y; w[4 * i + 2] = s.z; w[4 * i + 3] = s.w;
+                }
+                if constexpr (CT == CT_F32) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        ((float4*)(dstrow + (int64_t)n0 * 2))[i] = make_float4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+                } else {
+                    uint4 o0, o1;
+                    o0.x = pack2<CT>(w[0], w[1]);   o0.y = pack2<CT>(w[2], w[3]);
+                    o0.z = pack2<CT>(w[4], w[5]);   o0.w = pack2<CT>(w[6], w[7]);
+                    o1.x = pack2<CT>(w[8], w[9]);   o1.y = pack2<CT>(w[10], w[11]);
+                    o1.z = pack2<CT>(w[12], w[13]); o1.w = pack2<CT>(w[14], w[15]);
+                    ((uint4*)(dstrow + n0))[0] = o0;
+                    ((uint4*)(dstrow + n0))[1] = o1;
+                }
+            }
+        }
+        // next iteration's P0 writes only V, which P1 finished reading two barriers ago
+        if constexpr (O_ALIAS) __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// launch
+// ------------------------------------------------------------------------------------------
+
+template <int R, int CT, int IO, int MODE, bool GATED>
+static hipError_t launch_t(const Fused1DArgs& a0, int cus, hipStream_t st) {
+    Fused1DArgs a = a0;
+    constexpr int P = 32 / R;
+    if (a.nitems <= 0) return hipSuccess;
+    const int64_t groups = (a.nitems + P - 1) / P;
+    int64_t nwg = groups < cus ? groups : cus;
+    const int64_t gpw = (groups + nwg - 1) / nwg;
+    a.per_wg = gpw * P;
+    nwg = (a.nitems + a.per_wg - 1) / a.per_wg;
+    hipLaunchKernelGGL((fused1d_kernel<R, CT, IO, MODE, GATED>), dim3((unsigned)nwg), dim3(512), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int R>
+static hipError_t launch_r(int dtype, int mode, bool gated, const Fused1DArgs& a, int cus, hipStream_t st) {
+    switch (mode) {
+    case MODE_CONV:
+        if (dtype == CT_F32) return gated ? launch_t<R, CT_F32, CT_F32, MODE_CONV, true>(a, cus, st)
+                                          : launch_t<R, CT_F32, CT_F32, MODE_CONV, false>(a, cus, st);
+        if (dtype == CT_F16) return gated ? launch_t<R, CT_F16, CT_F16, MODE_CONV, true>(a, cus, st)
+                                          : launch_t<R, CT_F16, CT_F16, MODE_CONV, false>(a, cus, st);
+        return gated ? launch_t<R, CT_BF16, CT_BF16, MODE_CONV, true>(a, cus, st)
+                     : launch_t<R, CT_BF16, CT_BF16, MODE_CONV, false>(a, cus, st);
+    case MODE_FILTER:
+        if (dtype == CT_F32) return launch_t<R, CT_F32, CT_F32, MODE_FILTER, false>(a, cus, st);
+        if (dtype == CT_F16) return launch_t<R, CT_F32, CT_F16, MODE_FILTER, false>(a, cus, st);
+        return launch_t<R, CT_F32, CT_BF16, MODE_FILTER, false>(a, cus, st);
+    default:
+        break;
+    }
+    if constexpr (R == 32) {
+        if (mode == MODE_ROW) {
+            if (dtype == CT_F32) return launch_t<32, CT_F32, CT_F32, MODE_ROW, false>(a, cus, st);
+            if (dtype == CT_F16) return launch_t<32, CT_F16, CT_F16, MODE_ROW, false>(a, cus, st);
+            return launch_t<32, CT_BF16, CT_BF16, MODE_ROW, false>(a, cus, st);
+        }
+        if (mode == MODE_ROWFWD) {
+            if (dtype == CT_F32) return launch_t<32, CT_F32, CT_F32, MODE_ROWFWD, false>(a, cus, st);
+            if (dtype == CT_F16) return launch_t<32, CT_F32, CT_F16, MODE_ROWFWD, false>(a, cus, st);
+            return launch_t<32, CT_F32, CT_BF16, MODE_ROWFWD, false>(a, cus, st);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fused1d(int R, int dtype, int mode, bool gated, const Fused1DArgs& a, int cus,
+                          hipStream_t stream) {
+    switch (R) {
+    case 2: return launch_r<2>(dtype, mode, gated, a, cus, stream);
+    case 4: return launch_r<4>(dtype, mode, gated, a, cus, stream);
+    case 8: return launch_r<8>(dtype, mode, gated, a, cus, stream);
+    case 16: return launch_r<16>(dtype, mode, gated, a, cus, stream);
+    case 32: return launch_r<32>(dtype, mode, gated, a, cus, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace lcv

@@ -1,0 +1,68 @@
+// kernels.h -- launchers of the gfx950 kernels (host-callable, defined in the .hip files).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lcv {
+
+enum Mode1D { MODE_CONV = 0, MODE_FILTER = 1, MODE_ROW = 2, MODE_ROWFWD = 3 };
+
+struct Fused1DArgs {
+    const void* u;       // CONV: u [B][H][N]; FILTER: k [H][N]; ROW/ROWFWD: workspace rows
+    const void* q;       // CONV: pre-gate (nullable)
+    const void* v;       // CONV: post-gate (nullable)
+    void* y;             // CONV: y; FILTER/ROWFWD: k_f; ROW: workspace rows (in place)
+    const void* kf;      // CONV/ROW: k_f
+    const void* D;       // CONV/ROW: D [H]
+    const void* tables;  // fused-path tables for (R, compute type)
+    int64_t B, H, N;     // CONV/FILTER shape
+    int64_t nitems;      // CONV: pairs; FILTER: channels; ROW/ROWFWD: rows
+    int64_t per_wg;      // items per workgroup (set by the launcher)
+    float inv_m;         // 1 / M
+    int64_t M;           // full transform length (ROW/ROWFWD: M1 * 8192)
+    int64_t M1;          // ROW/ROWFWD: rows per sequence
+    int64_t seq0;        // ROW/ROWFWD: global index of the chunk's first sequence
+    int64_t seq_per_h;   // ROW: sequences per channel (h = seq / seq_per_h); ROWFWD: 1
+};
+
+// dtype: io element type (ComputeType values); the compute type is fp32 for fp32 io and for
+// the filter transforms, else the io type.
+hipError_t launch_fused1d(int R, int dtype, int mode, bool gated, const Fused1DArgs& a,
+                          int cus, hipStream_t stream);
+
+struct ColArgs {
+    const void* u;       // pass A input: u [B][H][N] (CONV) or k [H][N] (FILTER)
+    const void* q;       // pass A pre-gate (nullable)
+    const void* v;       // pass C post-gate (nullable)
+    void* y;             // pass C output y [B][H][N]
+    void* ws;            // workspace [S_chunk][M1][8192] complex (compute type)
+    const float* tw_lo;  // exp(-2 pi i r / M), r < 2048
+    const float* tw_hi;  // exp(-2 pi i 2048 r / M)
+    const float* tw_col; // exp(-2 pi i e / M1)
+    int64_t B, H, N;
+    int64_t M, M1;
+    int64_t seq0;        // first sequence (pair or channel) of this chunk
+    int64_t nseq;        // sequences in this chunk
+    int64_t seq_per_h;   // pairs per channel (CONV) or 1 (FILTER)
+    int filter;          // 1: input is k (one real channel per sequence)
+};
+
+// Pass A: per sequence and column n_lo, DFT over n_hi < M1/2 (zero above), twiddle
+// exp(-2 pi i n_lo k_hi / M), store row-major [k_hi][n_lo] into the workspace.
+hipError_t launch_col_fwd(int dtype, const ColArgs& a, hipStream_t stream);
+// Pass C: inverse twiddle, inverse DFT over k_hi for n_hi < M1/2, gate, store y.
+hipError_t launch_col_inv(int dtype, const ColArgs& a, hipStream_t stream);
+
+struct Conv2DArgs {
+    const void* u;       // [B][C][S][S]
+    const void* kf;      // 2D spectrum (transform order)
+    const void* D;       // [C]
+    void* y;             // [B][C][S][S]
+    const void* tables;
+    int64_t B, C;
+    float inv_p2;
+    int filter;          // 1: u = k [C][S][S], write k_f instead of y
+};
+hipError_t launch_conv2d(int dtype, const Conv2DArgs& a, hipStream_t stream);
+
+}  // namespace lcv

@@ -1,0 +1,262 @@
+// lconv_api.cpp -- the C ABI: argument validation (host only, before any HIP call), plan
+// selection and kernel dispatch.  See include/lconv.h for the contract.
+#include "lconv.h"
+
+#include <cstdint>
+#include <cstring>
+
+#include "kernels.h"
+#include "plan.h"
+
+using namespace lcv;
+
+namespace {
+
+constexpr size_t kChunkTarget = (size_t)64 << 20;  // multi-pass workspace per chunk (MALL-sized)
+
+size_t dtype_size(lconv_dtype_t dt) { return dt == LCONV_F32 ? 4 : 2; }
+bool dtype_ok(int dt) { return dt == LCONV_F32 || dt == LCONV_F16 || dt == LCONV_BF16; }
+// complex element bytes of the compute type used on the multi-pass path
+size_t work_complex_size(lconv_dtype_t dt, bool filter) { return (filter || dt == LCONV_F32) ? 8 : 4; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool n_supported(int64_t N) { return N >= 1 && N <= LCONV_MAX_N && (N % 8) == 0; }
+
+// sequences = complex transforms: pairs of batch rows per channel
+int64_t pairs_per_channel(int64_t B) { return (B + 1) / 2; }
+
+int64_t chunk_seqs(int64_t total, int64_t M, size_t csz) {
+    int64_t per = (int64_t)(kChunkTarget / ((size_t)M * csz));
+    if (per < 1) per = 1;
+    return per < total ? per : total;
+}
+
+lconv_status_t hip_status(hipError_t e) { return e == hipSuccess ? LCONV_SUCCESS : LCONV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int lconv_abi_version(void) { return LCONV_ABI_VERSION; }
+
+const char* lconv_status_string(lconv_status_t s) {
+    switch (s) {
+    case LCONV_SUCCESS: return "success";
+    case LCONV_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case LCONV_ERR_INVALID_SHAPE: return "invalid shape (negative size or size overflow)";
+    case LCONV_ERR_UNSUPPORTED: return "unsupported dtype or size";
+    case LCONV_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
+    case LCONV_ERR_ALIASING: return "the output overlaps an input";
+    case LCONV_ERR_WORKSPACE: return "workspace missing or too small";
+    case LCONV_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t lconv_filter_fft_bytes(int64_t H, int64_t N, lconv_dtype_t dtype) {
+    Plan1D p;
+    int64_t t;
+    if (!dtype_ok(dtype) || H < 0 || !n_supported(N) || !make_plan_1d(N, &p)) return 0;
+    if (!mul_ok(H, p.M, &t) || !mul_ok(t, 2 * (int64_t)dtype_size(dtype), &t)) return 0;
+    return (size_t)t;
+}
+
+size_t lconv_filter_fft_workspace_bytes(int64_t H, int64_t N, lconv_dtype_t dtype) {
+    Plan1D p;
+    if (!dtype_ok(dtype) || H < 0 || !n_supported(N) || !make_plan_1d(N, &p)) return 0;
+    if (!p.multipass || H == 0) return 0;
+    const size_t csz = work_complex_size(dtype, true);
+    return (size_t)chunk_seqs(H, p.M, csz) * (size_t)p.M * csz;
+}
+
+size_t lconv_fftconv_workspace_bytes(int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype) {
+    Plan1D p;
+    int64_t seqs;
+    if (!dtype_ok(dtype) || B < 0 || H < 0 || !n_supported(N) || !make_plan_1d(N, &p)) return 0;
+    if (!p.multipass || B == 0 || H == 0) return 0;
+    if (!mul_ok(pairs_per_channel(B), H, &seqs)) return 0;
+    const size_t csz = work_complex_size(dtype, false);
+    return (size_t)chunk_seqs(seqs, p.M, csz) * (size_t)p.M * csz;
+}
+
+size_t lconv_filter_fft2d_bytes(int64_t C, int64_t S, lconv_dtype_t dtype) {
+    int64_t t;
+    if (!dtype_ok(dtype) || dtype == LCONV_F32 || C < 0 || S != LCONV_2D_SIDE) return 0;
+    // spectrum of the (2S x 2S) transform in the 2D kernel's order, complex in dtype
+    if (!mul_ok(C, 4 * S * S, &t) || !mul_ok(t, 2 * (int64_t)dtype_size(dtype), &t)) return 0;
+    return (size_t)t;
+}
+
+lconv_status_t lconv_filter_fft(const void* k, void* k_f, int64_t H, int64_t N, lconv_dtype_t dtype,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
+    if (H < 0 || N < 0) return LCONV_ERR_INVALID_SHAPE;
+    int64_t t;
+    if (!mul_ok(H, N, &t) || !mul_ok(t, 8, &t)) return LCONV_ERR_INVALID_SHAPE;
+    if (H == 0 || N == 0) return LCONV_SUCCESS;
+    if (!n_supported(N)) return LCONV_ERR_UNSUPPORTED;
+    if (!k || !k_f) return LCONV_ERR_NULL_POINTER;
+    if (!aligned16(k) || !aligned16(k_f)) return LCONV_ERR_MISALIGNED;
+    const size_t kf_bytes = lconv_filter_fft_bytes(H, N, dtype);
+    if (kf_bytes == 0) return LCONV_ERR_INVALID_SHAPE;
+    if (overlap(k_f, kf_bytes, k, (size_t)(H * N) * dtype_size(dtype))) return LCONV_ERR_ALIASING;
+    const size_t need = lconv_filter_fft_workspace_bytes(H, N, dtype);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return LCONV_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return LCONV_ERR_MISALIGNED;
+        if (overlap(workspace, need, k_f, kf_bytes) || overlap(workspace, need, k, (size_t)(H * N) * dtype_size(dtype)))
+            return LCONV_ERR_ALIASING;
+    }
+    Plan1D p;
+    make_plan_1d(N, &p);
+    hipError_t err = hipSuccess;
+    const int cus = device_cu_count(&err);
+    if (!cus) return LCONV_ERR_HIP;
+    const void* tabs = fused_tables(p.R, CT_F32, &err);
+    if (!tabs) return LCONV_ERR_HIP;
+    if (!p.multipass) {
+        Fused1DArgs a{};
+        a.u = k; a.y = k_f; a.tables = tabs;
+        a.B = 1; a.H = H; a.N = N; a.nitems = H;
+        a.inv_m = 1.0f / (float)p.M; a.M = p.M; a.M1 = 1;
+        return hip_status(launch_fused1d(p.R, dtype, MODE_FILTER, false, a, cus, stream));
+    }
+    ColTables ct;
+    if (!col_tables(p.M, p.M1, &ct, &err)) return LCONV_ERR_HIP;
+    const int64_t per = chunk_seqs(H, p.M, work_complex_size(dtype, true));
+    for (int64_t h0 = 0; h0 < H; h0 += per) {
+        const int64_t ns = per < H - h0 ? per : H - h0;
+        ColArgs c{};
+        c.u = k; c.ws = workspace; c.tw_lo = ct.lo; c.tw_hi = ct.hi; c.tw_col = ct.col;
+        c.B = 1; c.H = H; c.N = N; c.M = p.M; c.M1 = p.M1; c.seq0 = h0; c.nseq = ns;
+        c.seq_per_h = 1; c.filter = 1;
+        err = launch_col_fwd(dtype, c, stream);
+        if (err != hipSuccess) return LCONV_ERR_HIP;
+        Fused1DArgs a{};
+        a.u = workspace; a.y = k_f; a.tables = tabs;
+        a.nitems = ns * p.M1; a.inv_m = 1.0f / (float)p.M; a.M = p.M; a.M1 = p.M1;
+        a.seq0 = h0; a.seq_per_h = 1;
+        err = launch_fused1d(32, dtype, MODE_ROWFWD, false, a, cus, stream);
+        if (err != hipSuccess) return LCONV_ERR_HIP;
+    }
+    return LCONV_SUCCESS;
+}
+
+lconv_status_t lconv_fftconv_fwd(const void* u, const void* k_f, const void* D, void* y, const void* q,
+                                 const void* v, int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
+    if (B < 0 || H < 0 || N < 0) return LCONV_ERR_INVALID_SHAPE;
+    int64_t elems, t;
+    if (!mul_ok(B, H, &t) || !mul_ok(t, N, &elems) || !mul_ok(elems, 8, &t)) return LCONV_ERR_INVALID_SHAPE;
+    if (B == 0 || H == 0 || N == 0) return LCONV_SUCCESS;
+    if (!n_supported(N)) return LCONV_ERR_UNSUPPORTED;
+    if (!u || !k_f || !D || !y) return LCONV_ERR_NULL_POINTER;
+    if (!aligned16(u) || !aligned16(k_f) || !aligned16(D) || !aligned16(y) || (q && !aligned16(q)) ||
+        (v && !aligned16(v)))
+        return LCONV_ERR_MISALIGNED;
+    const size_t es = dtype_size(dtype), act = (size_t)elems * es;
+    const size_t kf_bytes = lconv_filter_fft_bytes(H, N, dtype);
+    if (kf_bytes == 0) return LCONV_ERR_INVALID_SHAPE;
+    if (overlap(y, act, u, act) || overlap(y, act, q, act) || overlap(y, act, v, act) ||
+        overlap(y, act, k_f, kf_bytes) || overlap(y, act, D, (size_t)H * es))
+        return LCONV_ERR_ALIASING;
+    const size_t need = lconv_fftconv_workspace_bytes(B, H, N, dtype);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return LCONV_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return LCONV_ERR_MISALIGNED;
+        if (overlap(workspace, need, y, act) || overlap(workspace, need, u, act) ||
+            overlap(workspace, need, q, act) || overlap(workspace, need, v, act) ||
+            overlap(workspace, need, k_f, kf_bytes) || overlap(workspace, need, D, (size_t)H * es))
+            return LCONV_ERR_ALIASING;
+    }
+    Plan1D p;
+    make_plan_1d(N, &p);
+    hipError_t err = hipSuccess;
+    const int cus = device_cu_count(&err);
+    if (!cus) return LCONV_ERR_HIP;
+    const int ct = dtype == LCONV_F32 ? CT_F32 : (int)dtype;
+    const void* tabs = fused_tables(p.R, ct, &err);
+    if (!tabs) return LCONV_ERR_HIP;
+    const int64_t Bp = pairs_per_channel(B), seqs = Bp * H;
+    const bool gated = q || v;
+    if (!p.multipass) {
+        Fused1DArgs a{};
+        a.u = u; a.q = q; a.v = v; a.y = y; a.kf = k_f; a.D = D; a.tables = tabs;
+        a.B = B; a.H = H; a.N = N; a.nitems = seqs;
+        a.inv_m = 1.0f / (float)p.M; a.M = p.M; a.M1 = 1;
+        return hip_status(launch_fused1d(p.R, dtype, MODE_CONV, gated, a, cus, stream));
+    }
+    ColTables ctab;
+    if (!col_tables(p.M, p.M1, &ctab, &err)) return LCONV_ERR_HIP;
+    const int64_t per = chunk_seqs(seqs, p.M, work_complex_size(dtype, false));
+    for (int64_t s0 = 0; s0 < seqs; s0 += per) {
+        const int64_t ns = per < seqs - s0 ? per : seqs - s0;
+        ColArgs c{};
+        c.u = u; c.q = q; c.v = v; c.y = y; c.ws = workspace;
+        c.tw_lo = ctab.lo; c.tw_hi = ctab.hi; c.tw_col = ctab.col;
+        c.B = B; c.H = H; c.N = N; c.M = p.M; c.M1 = p.M1; c.seq0 = s0; c.nseq = ns;
+        c.seq_per_h = Bp; c.filter = 0;
+        if (launch_col_fwd(dtype, c, stream) != hipSuccess) return LCONV_ERR_HIP;
+        Fused1DArgs a{};
+        a.u = workspace; a.y = workspace; a.kf = k_f; a.D = D; a.tables = tabs;
+        a.nitems = ns * p.M1; a.inv_m = 1.0f / (float)p.M; a.M = p.M; a.M1 = p.M1;
+        a.seq0 = s0; a.seq_per_h = Bp;
+        if (launch_fused1d(32, dtype, MODE_ROW, false, a, cus, stream) != hipSuccess) return LCONV_ERR_HIP;
+        if (launch_col_inv(dtype, c, stream) != hipSuccess) return LCONV_ERR_HIP;
+    }
+    return LCONV_SUCCESS;
+}
+
+lconv_status_t lconv_filter_fft2d(const void* k, void* k_f, int64_t C, int64_t S, lconv_dtype_t dtype,
+                                  hipStream_t stream) {
+    if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
+    if (C < 0 || S < 0) return LCONV_ERR_INVALID_SHAPE;
+    if (C == 0) return LCONV_SUCCESS;
+    if (S != LCONV_2D_SIDE || dtype == LCONV_F32) return LCONV_ERR_UNSUPPORTED;
+    if (!k || !k_f) return LCONV_ERR_NULL_POINTER;
+    if (!aligned16(k) || !aligned16(k_f)) return LCONV_ERR_MISALIGNED;
+    const size_t kf_bytes = lconv_filter_fft2d_bytes(C, S, dtype);
+    if (overlap(k_f, kf_bytes, k, (size_t)(C * S * S) * dtype_size(dtype))) return LCONV_ERR_ALIASING;
+    (void)stream;
+    return LCONV_ERR_UNSUPPORTED;  // 2D path: see fftconv2d.hip
+}
+
+lconv_status_t lconv_fftconv2d_fwd(const void* u, const void* k_f, const void* D, void* y, int64_t B, int64_t C,
+                                   int64_t S, lconv_dtype_t dtype, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
+    if (B < 0 || C < 0 || S < 0) return LCONV_ERR_INVALID_SHAPE;
+    int64_t elems, t;
+    if (!mul_ok(B, C, &t) || !mul_ok(t, S * S, &elems)) return LCONV_ERR_INVALID_SHAPE;
+    if (B == 0 || C == 0) return LCONV_SUCCESS;
+    if (S != LCONV_2D_SIDE || dtype == LCONV_F32) return LCONV_ERR_UNSUPPORTED;
+    if (!u || !k_f || !D || !y) return LCONV_ERR_NULL_POINTER;
+    if (!aligned16(u) || !aligned16(k_f) || !aligned16(D) || !aligned16(y)) return LCONV_ERR_MISALIGNED;
+    const size_t es = dtype_size(dtype), act = (size_t)elems * es;
+    if (overlap(y, act, u, act) || overlap(y, act, k_f, lconv_filter_fft2d_bytes(C, S, dtype)) ||
+        overlap(y, act, D, (size_t)C * es))
+        return LCONV_ERR_ALIASING;
+    (void)stream;
+    return LCONV_ERR_UNSUPPORTED;  // 2D path: see fftconv2d.hip
+}
+
+lconv_status_t lconv_release(void) {
+    release_tables();
+    return LCONV_SUCCESS;
+}
+
+}  // extern "C"

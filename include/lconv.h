@@ -1,0 +1,145 @@
+/*
+ * lconv.h -- C ABI of the MI355X (gfx950) causal long-convolution library.
+ *
+ * The operation (restated from the pages):
+ *   * "FlashFFTConv: Efficient Convolutions for Long Sequences with Tensor Cores", abstract:
+ *     long convolutions computed exactly through the FFT, with the FFT factored into matrix
+ *     multiplications for matrix units and the whole chain fused to avoid memory traffic.
+ *   * "FlashConv" (AIMech curated page), Mechanism: FFT, pointwise spectral product and inverse
+ *     FFT fused on chip; sequences past the on-chip capacity are handled in chunks.
+ *   * Caracal abstract on the "RubiConv" page: causality from one-sided zero padding plus
+ *     truncation in the frequency domain.
+ *   * "Native Multi-Dimensional Subquadratic Operators via Input Dependent Long
+ *     Convolutions", abstract: global convolutions applied on the native 2D grid.
+ *
+ *   1D:  x = q (.) u                       (q optional, elementwise)
+ *        y = v (.) ( irfft(rfft(x, M) * rfft(k, M))[:N] + D * x )   (v optional), M >= 2N
+ *        i.e. y[b,h,t] = v[b,h,t] * ( sum_{s<=t} k[h,t-s] x[b,h,s] + D[h] x[b,h,t] ).
+ *   2D:  y[b,c,i,j] = sum_{a,e} k[c,a,e] u[b,c,i+S/2-a,j+S/2-e] + D[c] u[b,c,i,j]
+ *        (linear, not circular; kernel tap (a,e) sits at offset (a-S/2, e-S/2)).
+ *
+ * Conventions shared by every entry point
+ *   * All data pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors) on the
+ *     current HIP device.  The caller owns and frees every buffer, including k_f and any
+ *     workspace; sizes come from the *_bytes queries below.
+ *   * Layouts are dense row-major: u, q, v, y are [B][H][N] with N contiguous; k is [H][N];
+ *     D is [H].  2D: u, y are [B][C][S][S]; k is [C][S][S]; D is [C].  All share `dtype`.
+ *   * k_f (the filter spectrum) is OPAQUE: produced by lconv_filter_fft* for one
+ *     (H, N, dtype) or (C, S, dtype) and valid only for that shape and dtype.  Its size is
+ *     lconv_filter_fft*_bytes().
+ *   * Every call is asynchronous on `stream` (0 = the null stream); nothing synchronises.
+ *     Faults during execution surface at the caller's next synchronising call.
+ *   * Arguments are validated on the host before any HIP call.  On any error nothing is
+ *     launched and outputs are untouched.  B, H, N (or B, C) equal to 0 is a valid no-op.
+ *   * Pointers must be 16-byte aligned; y must not overlap any input.
+ *   * The library allocates only its per-device constant tables (built once, lazily, kept
+ *     until lconv_release()).  Calls are thread-safe.
+ */
+#ifndef LCONV_H
+#define LCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LCONV_ABI_VERSION 1
+
+typedef enum { LCONV_F32 = 0, LCONV_F16 = 1, LCONV_BF16 = 2 } lconv_dtype_t;
+
+typedef enum {
+    LCONV_SUCCESS = 0,
+    LCONV_ERR_NULL_POINTER = 1,  /* a required pointer is NULL                              */
+    LCONV_ERR_INVALID_SHAPE = 2, /* negative size, size product overflow                    */
+    LCONV_ERR_UNSUPPORTED = 3,   /* unknown dtype or a size outside the supported set       */
+    LCONV_ERR_MISALIGNED = 4,    /* a pointer is not 16-byte aligned                        */
+    LCONV_ERR_ALIASING = 5,      /* y overlaps an input                                     */
+    LCONV_ERR_WORKSPACE = 6,     /* workspace NULL or smaller than the *_workspace_bytes    */
+    LCONV_ERR_HIP = 7            /* a HIP runtime call failed (including: no device)        */
+} lconv_status_t;
+
+/* Largest supported sequence length (1D) and the only supported 2D side. */
+#define LCONV_MAX_N   ((int64_t)1 << 21)
+#define LCONV_2D_SIDE 128
+
+/* ---- size queries (pure host functions; 0 for invalid or unsupported arguments) ---------- */
+
+/* Bytes of the opaque filter spectrum for H channels of length N. */
+size_t lconv_filter_fft_bytes(int64_t H, int64_t N, lconv_dtype_t dtype);
+/* Scratch bytes lconv_filter_fft needs (0: none). */
+size_t lconv_filter_fft_workspace_bytes(int64_t H, int64_t N, lconv_dtype_t dtype);
+/* Scratch bytes lconv_fftconv_fwd needs (0 when the whole transform fits one workgroup). */
+size_t lconv_fftconv_workspace_bytes(int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype);
+/* Bytes of the opaque 2D filter spectrum for C channels of S x S kernels. */
+size_t lconv_filter_fft2d_bytes(int64_t C, int64_t S, lconv_dtype_t dtype);
+
+/* ---- 1D --------------------------------------------------------------------------------- */
+
+/*
+ * Filter spectrum k_f from k[H][N]: the length-M DFT of each zero-padded filter, scaled by
+ * 1/M and stored in the library's transform order (FlashConv page, Mechanism: the pointwise
+ * spectral product needs the filter's spectrum; computing it once per filter keeps it out of
+ * the per-call path).  Computed in fp32 arithmetic, stored in `dtype`.
+ *   k         [H][N] dtype, device
+ *   k_f       lconv_filter_fft_bytes(H, N, dtype) bytes, device, written
+ *   workspace lconv_filter_fft_workspace_bytes(H, N, dtype) bytes (may be NULL if that is 0)
+ * Supported: 1 <= N <= LCONV_MAX_N, N a multiple of 8.
+ */
+lconv_status_t lconv_filter_fft(const void* k, void* k_f, int64_t H, int64_t N,
+                                lconv_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
+ * Causal long convolution, optional Hyena-style gating:
+ *   y = v (.) ( (k * x)[:N] + D (.) x ),  x = q (.) u
+ * (FlashFFTConv abstract: exact FFT convolution; Caracal abstract: causality by padding and
+ * truncation; FlashConv Mechanism: fused FFT -> spectral product -> inverse FFT, chunked when
+ * the sequence exceeds one compute unit).
+ *   u, y      [B][H][N] dtype, device (y written)
+ *   k_f       from lconv_filter_fft(k, ..., H, N, dtype)
+ *   D         [H] dtype, device
+ *   q, v      [B][H][N] dtype, device, or NULL (then treated as all ones)
+ *   workspace lconv_fftconv_workspace_bytes(B, H, N, dtype) bytes (may be NULL if that is 0)
+ * Arithmetic: fp32 I/O uses fp32 matrix-core products; bf16 and fp16 use bf16/fp16
+ * matrix-core operands with fp32 accumulation, fp32 twiddles and fp32 pointwise products.
+ */
+lconv_status_t lconv_fftconv_fwd(const void* u, const void* k_f, const void* D, void* y,
+                                 const void* q, const void* v, int64_t B, int64_t H, int64_t N,
+                                 lconv_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/* ---- 2D (HyenaND-style) ------------------------------------------------------------------ */
+
+/*
+ * 2D filter spectrum from k[C][S][S] (S = LCONV_2D_SIDE): the (2S x 2S) DFT of each
+ * zero-padded kernel, scaled by 1/(2S)^2, in the library's transform order.  fp32 arithmetic.
+ */
+lconv_status_t lconv_filter_fft2d(const void* k, void* k_f, int64_t C, int64_t S,
+                                  lconv_dtype_t dtype, hipStream_t stream);
+
+/*
+ * 2D linear convolution with centred full-size kernels, cropped to the input window, plus
+ * the D skip ("Native Multi-Dimensional Subquadratic Operators..." abstract):
+ *   u, y [B][C][S][S] dtype, device;  k_f from lconv_filter_fft2d;  D [C] dtype, device.
+ * One fused kernel: row DFTs, column DFTs, spectral product, inverse column and row DFTs
+ * restricted to the output window.  Supported: S = LCONV_2D_SIDE, dtype bf16 or fp16.
+ */
+lconv_status_t lconv_fftconv2d_fwd(const void* u, const void* k_f, const void* D, void* y,
+                                   int64_t B, int64_t C, int64_t S, lconv_dtype_t dtype,
+                                   hipStream_t stream);
+
+/* ---- misc ------------------------------------------------------------------------------- */
+
+const char* lconv_status_string(lconv_status_t s);
+int lconv_abi_version(void);
+/* Frees the per-device constant tables (they are rebuilt on next use). Not thread-safe
+ * against concurrent calls. */
+lconv_status_t lconv_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LCONV_H */

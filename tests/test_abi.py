@@ -1,0 +1,112 @@
+"""C-ABI tests that need no GPU: the library loads, exports every declared symbol, answers
+size queries, and rejects bad arguments with the documented status before any HIP call."""
+import ctypes
+
+import pytest
+
+from fft_long_convolution_amd import lconv
+
+F32, F16, BF16 = lconv.F32, lconv.F16, lconv.BF16
+OK, NULLP, SHAPE, UNSUP, MISAL, ALIAS, WSERR, HIPERR = range(8)
+
+# fake, 16-byte aligned "device" addresses: validation must reject before touching them
+A, Bq, C, Dd, Y, W = (0x100000 * (i + 1) for i in range(6))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return lconv.load()
+
+
+def test_exports_every_header_symbol(lib):
+    names = lconv.header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+        assert callable(getattr(lconv, n)), n
+
+
+def test_abi_version_and_strings(lib):
+    assert lconv.lconv_abi_version() == 1
+    for s in range(8):
+        assert lconv.status_string(s)
+    assert "unknown" in lconv.status_string(99)
+
+
+def test_size_queries():
+    # N=4096 -> M=8192 complex per channel
+    assert lconv.lconv_filter_fft_bytes(768, 4096, BF16) == 768 * 8192 * 4
+    assert lconv.lconv_filter_fft_bytes(4, 1024, F32) == 4 * 2048 * 8
+    assert lconv.lconv_filter_fft_bytes(1, 8, F16) == 512 * 4           # minimum transform 512
+    assert lconv.lconv_fftconv_workspace_bytes(16, 768, 4096, BF16) == 0  # single pass
+    assert lconv.lconv_fftconv_workspace_bytes(4, 256, 65536, F16) > 0    # multi-pass
+    assert lconv.lconv_filter_fft_workspace_bytes(64, 2 ** 21, BF16) > 0
+    assert lconv.lconv_filter_fft_bytes(1, 12, BF16) == 0                 # N % 8 != 0
+    assert lconv.lconv_filter_fft_bytes(1, 2 ** 22, BF16) == 0            # too long
+    assert lconv.lconv_filter_fft_bytes(1, 8, 7) == 0                     # bad dtype
+    assert lconv.lconv_filter_fft2d_bytes(256, 128, BF16) == 256 * 256 * 256 * 4
+    assert lconv.lconv_filter_fft2d_bytes(1, 64, BF16) == 0
+
+
+def fwd(u=A, kf=Bq, D=C, y=Y, q=None, v=None, B=2, H=3, N=64, dt=BF16, ws=None, wsb=0):
+    return lconv.lconv_fftconv_fwd(u, kf, D, y, q, v, B, H, N, dt, ws, wsb, None)
+
+
+def test_fwd_validation_errors():
+    assert fwd(dt=5) == UNSUP
+    assert fwd(B=-1) == SHAPE
+    assert fwd(N=-8) == SHAPE
+    assert fwd(B=2 ** 40, H=2 ** 20, N=2 ** 10) == SHAPE                 # overflow
+    assert fwd(N=12) == UNSUP
+    assert fwd(N=2 ** 22) == UNSUP
+    assert fwd(u=None) == NULLP
+    assert fwd(kf=None) == NULLP
+    assert fwd(D=None) == NULLP
+    assert fwd(y=None) == NULLP
+    assert fwd(u=A + 2) == MISAL
+    assert fwd(q=Bq + 8 + 0x1000) == MISAL
+    assert fwd(y=A) == ALIAS                                               # y == u
+    assert fwd(y=A + 16) == ALIAS                                          # overlap
+    assert fwd(q=Y) == ALIAS
+    assert fwd(N=65536, B=4, H=4) == WSERR                                 # multi-pass, no ws
+    need = lconv.lconv_fftconv_workspace_bytes(4, 4, 65536, BF16)
+    assert fwd(N=65536, B=4, H=4, ws=W + 0x10000000, wsb=need - 1) == WSERR
+
+
+def test_empty_is_noop():
+    assert fwd(B=0) == OK
+    assert fwd(H=0) == OK
+    assert fwd(N=0) == OK
+    assert fwd(B=0, u=None, y=None) == OK
+    assert lconv.lconv_filter_fft(None, None, 0, 64, BF16, None, 0, None) == OK
+    assert lconv.lconv_fftconv2d_fwd(None, None, None, None, 0, 4, 128, BF16, None) == OK
+
+
+def test_filter_fft_validation_errors():
+    f = lconv.lconv_filter_fft
+    assert f(A, Y, 3, 64, 9, None, 0, None) == UNSUP
+    assert f(A, Y, -1, 64, BF16, None, 0, None) == SHAPE
+    assert f(None, Y, 3, 64, BF16, None, 0, None) == NULLP
+    assert f(A, None, 3, 64, BF16, None, 0, None) == NULLP
+    assert f(A + 4, Y, 3, 64, BF16, None, 0, None) == MISAL
+    assert f(A, A, 3, 64, BF16, None, 0, None) == ALIAS
+    far = 1 << 40  # k_f far from k so only the missing workspace is wrong
+    assert f(A, far, 3, 2 ** 21, BF16, None, 0, None) == WSERR
+
+
+def test_2d_validation_errors():
+    f = lconv.lconv_fftconv2d_fwd
+    assert f(A, Bq, C, Y, 2, 3, 64, BF16, None) == UNSUP
+    assert f(A, Bq, C, Y, 2, 3, 128, F32, None) == UNSUP
+    assert f(None, Bq, C, Y, 2, 3, 128, BF16, None) == NULLP
+    assert f(A + 2, Bq, C, Y, 2, 3, 128, BF16, None) == MISAL
+    assert f(A, Bq, C, A, 2, 3, 128, BF16, None) == ALIAS
+    assert f(A, Bq, C, Y, -2, 3, 128, BF16, None) == SHAPE
+
+
+def test_no_device_gives_hip_error():
+    """Valid arguments reach the HIP runtime; without a GPU that is LCONV_ERR_HIP."""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert fwd() == HIPERR
