@@ -1,0 +1,224 @@
+"""Benchmark of the fused causal FFT convolution on one MI355X.
+
+One step = one lconv_fftconv_fwd call over the whole synthetic batch (load, gate, forward
+transform, spectral product, inverse transform, truncation, skip, gate, store).  The filter
+spectrum is computed once beforehand (timed separately).  Prints ONE JSON line.
+
+Algorithmic bytes (what the method must move): (n_in + 1) * B*H*N * s for the activations
+(n_in = 3 gated, 1 otherwise), plus the filter spectrum once at its minimal size
+H*(N+1)*2*s (Hermitian half in the I/O dtype), plus D.  Nominal flops per row:
+2 * 2.5 M log2 M + 6 (N+1) + g N with M = 2N (g = 4 gated, 2 otherwise).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # dense TFLOP/s
+
+
+def algorithmic_bytes(spec):
+    s = {"f32": 4, "f16": 2, "bf16": 2}[spec.dtype]
+    if spec.kind == "2d":
+        P = 2 * spec.S
+        act = 2 * spec.B * spec.C * spec.S * spec.S * s
+        kf = spec.C * P * (P // 2 + 1) * 2 * s
+        return act + kf + spec.C * s
+    n_in = 3 if spec.gated else 1
+    act = (n_in + 1) * spec.B * spec.H * spec.N * s
+    kf = spec.H * (spec.N + 1) * 2 * s
+    return act + kf + spec.H * s
+
+
+def nominal_flops(spec):
+    if spec.kind == "2d":
+        P = 2 * spec.S
+        per = 2 * 2.5 * P * P * math.log2(P * P) + 6 * P * (P // 2 + 1) + 2 * spec.S ** 2
+        return per * spec.B * spec.C
+    M = 2 * spec.N
+    g = 4 if spec.gated else 2
+    per = 2 * 2.5 * M * math.log2(M) + 6 * (spec.N + 1) + g * spec.N
+    return per * spec.B * spec.H
+
+
+def to_dev(a, dtype):
+    import torch
+    if a is None:
+        return None
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def cpu_baseline(d, budget_s=12.0):
+    """The float64 oracle on a bounded sample of the same workload (full rows)."""
+    import oracle
+    spec = d["spec"]
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    dt = {"f32": oracle.DT_F32, "f16": oracle.DT_F16, "bf16": oracle.DT_BF16}[spec.dtype]
+    s = {"f32": 4, "f16": 2, "bf16": 2}[spec.dtype]
+    rng = np.random.default_rng(9)
+    if spec.kind == "2d":
+        raise NotImplementedError
+    n_in = 3 if spec.gated else 1
+    row_bytes = (n_in + 1) * spec.N * s
+    # calibrate on a few rows, then size the sample for about budget_s seconds
+    nrows = cores
+    while True:
+        rows = np.stack([rng.integers(0, spec.B, nrows), rng.integers(0, spec.H, nrows)], 1)
+        t0 = time.perf_counter()
+        oracle.conv1d_rows(d["u"], d["k"], d["D"], rows, q=d["q"], v=d["v"], dt=dt, nthreads=cores)
+        el = time.perf_counter() - t0
+        if el >= budget_s or nrows >= spec.B * spec.H:
+            break
+        nrows = int(min(spec.B * spec.H, max(nrows * 2, nrows * budget_s / max(el, 1e-3) * 1.05)))
+    gbs = nrows * row_bytes / el / 1e9
+    return {"value": round(gbs, 6), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nrows} full rows (b,h) of {spec.name}, direct float64 sum, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibrate", action="store_true",
+                    help="run only a plain 256 MiB device copy (reads and writes 256 MiB per "
+                         "launch): the reference for scaling FETCH_SIZE / WRITE_SIZE counters")
+    args = ap.parse_args()
+    if args.copy_calibrate:
+        import torch
+        x = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": 256 << 20, "launches": 5}))
+        return
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the per-(b,h) rows would shard over GPUs with no exchange, but no multi-GPU run "
+              "is part of it.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from fft_long_convolution_amd import lconv
+    from fft_long_convolution_amd import workloads as wl
+
+    name = args.workload or wl.HEADLINE
+    d = wl.make(name)
+    spec = d["spec"]
+    torch.cuda.set_device(0)
+    dt = spec.dtype
+    lconv.load()
+
+    if spec.kind == "2d":
+        u, k, D = (to_dev(d[x], dt) for x in ("u", "k", "D"))
+        run_filter = lambda: lconv.filter_fft2d(k)
+        kf = run_filter()
+        y = torch.empty_like(u)
+        step = lambda: lconv.fftconv2d(u, kf, D, out=y)
+    else:
+        u, q, v, k, D = (to_dev(d[x], dt) for x in ("u", "q", "v", "k", "D"))
+        run_filter = lambda: lconv.filter_fft(k)
+        kf = run_filter()
+        y = torch.empty_like(u)
+        wsb = lconv.lconv_fftconv_workspace_bytes(spec.B, spec.H, spec.N, lconv.dtype_code(u.dtype))
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        dtc = lconv.dtype_code(u.dtype)
+        stream = torch.cuda.current_stream()
+
+        def step():
+            st = lconv.lconv_fftconv_fwd(u.data_ptr(), kf.data_ptr(), D.data_ptr(), y.data_ptr(),
+                                         None if q is None else q.data_ptr(),
+                                         None if v is None else v.data_ptr(),
+                                         spec.B, spec.H, spec.N, dtc,
+                                         ws.data_ptr() if wsb else None, wsb, stream.cuda_stream)
+            if st != 0:
+                raise lconv.LconvError(st, "lconv_fftconv_fwd")
+
+    torch.cuda.synchronize()
+    # filter spectrum timing (not part of a step)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    kf2 = run_filter()
+    e1.record()
+    torch.cuda.synchronize()
+    filter_ms = e0.elapsed_time(e1)
+    del kf2
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # timed region: exactly K steps, events on the stream the kernels run on
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record()
+        step()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_ms = float(np.mean(per))
+    ms_per_step = wall * 1e3 / args.steps
+
+    nbytes = algorithmic_bytes(spec)
+    flops = nominal_flops(spec)
+    elems = spec.B * (spec.H if spec.kind == "1d" else spec.C) * (spec.N if spec.kind == "1d" else spec.S ** 2)
+    gbs = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+
+    out = {
+        "metric": "fftconv GB/s (algorithmic bytes), causal long conv, 1 GPU",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": spec.name, "B": spec.B,
+                   ("H" if spec.kind == "1d" else "C"): (spec.H if spec.kind == "1d" else spec.C),
+                   ("N" if spec.kind == "1d" else "S"): (spec.N if spec.kind == "1d" else spec.S),
+                   "gated": bool(getattr(spec, "gated", False)), "parallelism": "none"},
+        "tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "elements_per_s": float("%.4g" % (elems / (ms_per_step * 1e-3))),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "filter_fft_ms": round(filter_ms, 4),
+        "algorithmic_bytes": nbytes,
+        "nominal_flops": flops,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel_avg_us": round(avg_ms * 1e3, 3)},
+    }
+    if not args.no_cpu and spec.kind == "1d":
+        out["cpu_baseline"] = cpu_baseline(d, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -67,6 +67,57 @@ __device__ __forceinline__ void store8(void* base, int64_t off, const float* x) 
     }
 }
 
+// 8 consecutive elements as raw bits (1 uint4 for 16-bit types, 2 for fp32) and their unpacking.
+template <int IO>
+__device__ __forceinline__ void load_raw(const void* base, int64_t off, uint4* r) {
+    if constexpr (IO == CT_F32) {
+        const uint4* p = (const uint4*)((const float*)base + off);
+        r[0] = p[0];
+        r[1] = p[1];
+    } else {
+        r[0] = *(const uint4*)((const uint16_t*)base + off);
+    }
+}
+template <int IO>
+__device__ __forceinline__ void unpack_raw(const uint4* r, float* x) {
+    if constexpr (IO == CT_F32) {
+        x[0] = __uint_as_float(r[0].x); x[1] = __uint_as_float(r[0].y);
+        x[2] = __uint_as_float(r[0].z); x[3] = __uint_as_float(r[0].w);
+        x[4] = __uint_as_float(r[1].x); x[5] = __uint_as_float(r[1].y);
+        x[6] = __uint_as_float(r[1].z); x[7] = __uint_as_float(r[1].w);
+    } else {
+        x[0] = unpack_lo<IO>(r[0].x); x[1] = unpack_hi<IO>(r[0].x);
+        x[2] = unpack_lo<IO>(r[0].y); x[3] = unpack_hi<IO>(r[0].y);
+        x[4] = unpack_lo<IO>(r[0].z); x[5] = unpack_hi<IO>(r[0].z);
+        x[6] = unpack_lo<IO>(r[0].w); x[7] = unpack_hi<IO>(r[0].w);
+    }
+}
+// 4 consecutive complex values (raw bits) of a spectrum stored in type IO.
+template <int IO>
+__device__ __forceinline__ void load_raw_c4(const void* base, int64_t off, uint4* r) {
+    if constexpr (IO == CT_F32) {
+        const uint4* p = (const uint4*)((const float*)base + 2 * off);
+        r[0] = p[0];
+        r[1] = p[1];
+    } else {
+        r[0] = *(const uint4*)((const uint32_t*)base + off);
+    }
+}
+template <int IO>
+__device__ __forceinline__ void unpack_raw_c4(const uint4* r, float* re, float* im) {
+    if constexpr (IO == CT_F32) {
+        re[0] = __uint_as_float(r[0].x); im[0] = __uint_as_float(r[0].y);
+        re[1] = __uint_as_float(r[0].z); im[1] = __uint_as_float(r[0].w);
+        re[2] = __uint_as_float(r[1].x); im[2] = __uint_as_float(r[1].y);
+        re[3] = __uint_as_float(r[1].z); im[3] = __uint_as_float(r[1].w);
+    } else {
+        re[0] = unpack_lo<IO>(r[0].x); im[0] = unpack_hi<IO>(r[0].x);
+        re[1] = unpack_lo<IO>(r[0].y); im[1] = unpack_hi<IO>(r[0].y);
+        re[2] = unpack_lo<IO>(r[0].z); im[2] = unpack_hi<IO>(r[0].z);
+        re[3] = unpack_lo<IO>(r[0].w); im[3] = unpack_hi<IO>(r[0].w);
+    }
+}
+
 // 4 consecutive complex values of a spectrum stored in type IO -> fp32.
 template <int IO>
 __device__ __forceinline__ void load_c4(const void* base, int64_t off, float* re, float* im) {
@@ -165,10 +216,15 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
     constexpr int NBLK = P * 16;               // (sequence, n2) column blocks
     constexpr int BPW = NBLK / 8;              // blocks per wave
 
-    __shared__ __attribute__((aligned(16))) uint32_t lds[V_W + XY_W + O_W];
+    // The radix-R blocks (F1, I3) are shared by all waves: on the convolution path they live in
+    // LDS (copied once), which keeps the per-tile blocks in registers without spills.
+    constexpr bool IMG_LDS = RES && MODE == MODE_CONV;
+    constexpr int IMGS_W = IMG_LDS ? (T_F2 - T_F1) / 4 : 0;
+    __shared__ __attribute__((aligned(16))) uint32_t lds[V_W + XY_W + O_W + IMGS_W];
     uint32_t* V = lds;
     uint32_t* XY = lds + V_W;
     float* O = (float*)(O_ALIAS ? lds : lds + V_W + XY_W);
+    uint32_t* IMGS = lds + V_W + XY_W + O_W;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c = lane & 15;
@@ -194,59 +250,107 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                 mi2[i] = load_img<CT>(tab + T_I2, k1, lane);
             }
         }
+        if constexpr (IMG_LDS) {
+            for (int w = tid; w < IMGS_W / 4; w += 512)
+                ((uint4*)IMGS)[w] = ((const uint4*)(tab + T_F1))[w];
+        } else {
 #pragma unroll
-        for (int rb = 0; rb < RB1; ++rb)
+            for (int rb = 0; rb < RB1; ++rb)
 #pragma unroll
-            for (int kc = 0; kc < KC1; ++kc) mf1[rb][kc] = load_img<CT>(tab + T_F1, rb * KCF + kc, lane);
-        if constexpr (INV) {
+                for (int kc = 0; kc < KC1; ++kc) mf1[rb][kc] = load_img<CT>(tab + T_F1, rb * KCF + kc, lane);
+            if constexpr (INV) {
 #pragma unroll
-            for (int rb = 0; rb < RB3; ++rb)
+                for (int rb = 0; rb < RB3; ++rb)
 #pragma unroll
-                for (int kc = 0; kc < KC3; ++kc) mi3[rb][kc] = load_img<CT>(tab + T_I3, rb * KCF + kc, lane);
+                    for (int kc = 0; kc < KC3; ++kc) mi3[rb][kc] = load_img<CT>(tab + T_I3, rb * KCF + kc, lane);
+            }
         }
     }
-    auto F1 = [&](int rb, int kc) { return RES ? mf1[rb][kc] : load_img<CT>(tab + T_F1, rb * KCF + kc, lane); };
-    auto I3 = [&](int rb, int kc) { return RES ? mi3[rb][kc] : load_img<CT>(tab + T_I3, rb * KCF + kc, lane); };
+    auto F1 = [&](int rb, int kc) {
+        if constexpr (IMG_LDS) return load_img_lds<CT>(IMGS, rb * KCF + kc, lane);
+        else return RES ? mf1[rb][kc] : load_img<CT>(tab + T_F1, rb * KCF + kc, lane);
+    };
+    auto I3 = [&](int rb, int kc) {
+        if constexpr (IMG_LDS) return load_img_lds<CT>(IMGS + (T_I3 - T_F1) / 4, rb * KCF + kc, lane);
+        else return RES ? mi3[rb][kc] : load_img<CT>(tab + T_I3, rb * KCF + kc, lane);
+    };
     auto F2 = [&](int i) { return RES ? mf2[i] : load_img<CT>(tab + T_F2, (wave * 4 + i) % R, lane); };
     auto F3 = [&](int i) { return RES ? mf3[i] : load_img<CT>(tab + T_F3, (wave * 4 + i) % R, lane); };
     auto I1 = [&](int i) { return RES ? mi1[i] : load_img<CT>(tab + T_I1, (wave * 4 + i) % R, lane); };
     auto I2 = [&](int i) { return RES ? mi2[i] : load_img<CT>(tab + T_I2, (wave * 4 + i) % R, lane); };
 
-    const int64_t Bp = (a.B + 1) / 2;  // pairs per channel (CONV)
+    const uint32_t Bp = (uint32_t)((a.B + 1) / 2);  // pairs per channel (CONV)
     const int64_t first = (int64_t)blockIdx.x * a.per_wg;
     const int64_t last = first + a.per_wg < a.nitems ? first + a.per_wg : a.nitems;
+    const int64_t HN = a.H * a.N;
+    const int m1s = a.M1 > 1 ? __builtin_ctzll((unsigned long long)a.M1) : 0;  // M1 is a power of 2
+    // CONV item -> (channel h, first batch row b); 32-bit: item counts stay below 2^32
+    auto decode = [&](int64_t item, int64_t& h, int64_t& b) {
+        const uint32_t it = (uint32_t)item, hh = it / Bp;
+        h = hh;
+        b = 2 * (int64_t)(it - hh * Bp);
+    };
+    // ROW/ROWFWD item -> (channel h, row k_hi)
+    auto decode_row = [&](int64_t item, int64_t& h, int64_t& khi) {
+        const int64_t s = a.seq0 + (item >> m1s);
+        khi = item & (a.M1 - 1);
+        h = (int64_t)((uint32_t)s / (uint32_t)a.seq_per_h);
+    };
+
+    // this thread's slot in P0 / P4: sequence p_io of the iteration, elements n0_io .. +8
+    const int p_io = tid / (16 * R), n0_io = 8 * (tid % (16 * R));
+    constexpr int IOW = IO == CT_F32 ? 2 : 1;  // uint4 per 8 elements
+    // Software pipeline: u, q of the NEXT iteration and v of this one are loaded into
+    // registers while the transforms run, so HBM latency overlaps the work.
+    uint4 ru[2][IOW], rq[2][IOW], rv[2][IOW];
+    auto issue_in = [&](int64_t it_base) {
+        const int64_t item = it_base + p_io;
+        if (item < last && n0_io < a.N) {
+            if constexpr (MODE == MODE_CONV) {
+                int64_t h, b;
+                decode(item, h, b);
+                const int64_t o0 = (b * a.H + h) * a.N + n0_io;
+                load_raw<IO>(a.u, o0, ru[0]);
+                if (GATED && a.q) load_raw<IO>(a.q, o0, rq[0]);
+                if (b + 1 < a.B) {
+                    load_raw<IO>(a.u, o0 + HN, ru[1]);
+                    if (GATED && a.q) load_raw<IO>(a.q, o0 + HN, rq[1]);
+                }
+            } else if constexpr (MODE == MODE_FILTER) {
+                load_raw<IO>(a.u, item * a.N + n0_io, ru[0]);
+            }
+        }
+    };
+    if constexpr (HALF_IN) issue_in(first);
 
     for (int64_t it0 = first; it0 < last; it0 += P) {
         // ================= P0: inputs -> V =================================================
         if constexpr (HALF_IN) {
-            const int p = tid / (16 * R), n0 = 8 * (tid % (16 * R));
+            const int p = p_io, n0 = n0_io;
             const int64_t item = it0 + p;
             float xr[8], xi[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) { xr[i] = 0.f; xi[i] = 0.f; }
             if (item < last && n0 < a.N) {
+                unpack_raw<IO>(ru[0], xr);
                 if constexpr (MODE == MODE_CONV) {
-                    const int64_t h = item / Bp, b = 2 * (item % Bp);
-                    const int64_t o0 = (b * a.H + h) * a.N + n0;
-                    load8<IO>(a.u, o0, xr);
+                    int64_t h, b;
+                    decode(item, h, b);
                     if (GATED && a.q) {
                         float t[8];
-                        load8<IO>(a.q, o0, t);
+                        unpack_raw<IO>(rq[0], t);
 #pragma unroll
                         for (int i = 0; i < 8; ++i) xr[i] *= t[i];
                     }
                     if (b + 1 < a.B) {
-                        const int64_t o1 = o0 + a.H * a.N;
-                        load8<IO>(a.u, o1, xi);
+                        unpack_raw<IO>(ru[1], xi);
                         if (GATED && a.q) {
                             float t[8];
-                            load8<IO>(a.q, o1, t);
+                            unpack_raw<IO>(rq[1], t);
 #pragma unroll
                             for (int i = 0; i < 8; ++i) xi[i] *= t[i];
                         }
                     }
-                } else {  // FILTER: one real channel per sequence
-                    load8<IO>(a.u, item * a.N + n0, xr);
                 }
             }
             uint32_t* dst = V + ((p * NIN + (n0 >> 8)) * SV + (n0 & 255)) * EW;
@@ -276,31 +380,54 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
             }
         }
 
-        // filter spectrum for this wave's tiles (issued before the transforms need it)
-        float kr[4][4], ki[4][4];
+        // Loads issued now, in the order they are needed: the filter spectrum of this wave's
+        // tiles (P2), the post-gate v (P4), the next iteration's u, q (next P0).
+        uint4 rk[4][IOW];
+        float dk[4];
         if constexpr (INV) {
+            // the 4 tiles of a wave belong to one sequence when R >= 4 (two when R == 2)
+            int64_t hs[2] = {0, 0}, bases[2] = {0, 0};
+            bool oks[2] = {false, false};
+            float ds[2] = {0.f, 0.f};
+            constexpr int NSEQ_W = R >= 4 ? 1 : 2;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = wave * 4 + i, p = t / R, k1 = t % R;
-                const int64_t item = it0 + p;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) { kr[i][j] = 0.f; ki[i][j] = 0.f; }
-                if (item < last) {
-                    int64_t h, base;
+            for (int s = 0; s < NSEQ_W; ++s) {
+                const int64_t item = it0 + (wave * 4 + 2 * s) / R;
+                oks[s] = item < last;
+                if (oks[s]) {
                     if constexpr (MODE == MODE_CONV) {
-                        h = item / Bp;
-                        base = h * M;
+                        int64_t b;
+                        decode(item, hs[s], b);
+                        bases[s] = hs[s] * M;
                     } else {
-                        const int64_t s = a.seq0 + item / a.M1, khi = item % a.M1;
-                        h = s / a.seq_per_h;
-                        base = h * a.M + khi * M;
+                        int64_t khi;
+                        decode_row(item, hs[s], khi);
+                        bases[s] = hs[s] * a.M + khi * M;
                     }
-                    load_c4<IO>(a.kf, base + ((int64_t)k1 * 64 + lane) * 4, kr[i], ki[i]);
-                    const float d = load1<IO>(a.D, h) * a.inv_m;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) kr[i][j] += d;
+                    ds[s] = load1<IO>(a.D, hs[s]) * a.inv_m;
                 }
             }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s = NSEQ_W == 1 ? 0 : i / 2, k1 = (wave * 4 + i) % R;
+                dk[i] = ds[s];
+#pragma unroll
+                for (int w = 0; w < IOW; ++w) rk[i][w] = make_uint4(0, 0, 0, 0);
+                if (oks[s]) load_raw_c4<IO>(a.kf, bases[s] + ((int64_t)k1 * 64 + lane) * 4, rk[i]);
+            }
+        }
+        if constexpr (MODE == MODE_CONV && GATED) {
+            const int64_t item = it0 + p_io;
+            if (a.v && item < last && n0_io < a.N) {
+                int64_t h, b;
+                decode(item, h, b);
+                const int64_t o0 = (b * a.H + h) * a.N + n0_io;
+                load_raw<IO>(a.v, o0, rv[0]);
+                if (b + 1 < a.B) load_raw<IO>(a.v, o0 + HN, rv[1]);
+            }
+        }
+        if constexpr (HALF_IN) {
+            if (it0 + P < last) issue_in(it0 + P);
         }
         __syncthreads();
 
@@ -347,7 +474,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                     if constexpr (MODE == MODE_FILTER) {
                         base = item * M;
                     } else {
-                        const int64_t h = a.seq0 + item / a.M1, khi = item % a.M1;
+                        const int64_t h = a.seq0 + (item >> m1s), khi = item & (a.M1 - 1);
                         base = h * a.M + khi * M;
                     }
 #pragma unroll
@@ -355,8 +482,10 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                     store_c4<IO>(a.y, base + ((int64_t)k1 * 64 + lane) * 4, x.re, x.im);
                 }
             } else {
+                float kr[4], ki[4];
+                unpack_raw_c4<IO>(rk[i], kr, ki);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) cmul(x.re[j], x.im[j], kr[i][j], ki[i][j]);
+                for (int j = 0; j < 4; ++j) cmul(x.re[j], x.im[j], kr[j] + dk[i], ki[j]);
                 x = stage_swap<CT>(I1(i), to_operand<CT>(x));  // (L = n3, K = k2)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) cmulc(x.re[j], x.im[j], twr[j], twi[j]);
@@ -398,10 +527,11 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
 
         // ================= P4: epilogue ======================================================
         if constexpr (MODE == MODE_CONV) {
-            const int p = tid / (16 * R), n0 = 8 * (tid % (16 * R));
+            const int p = p_io, n0 = n0_io;
             const int64_t item = it0 + p;
             if (item < last && n0 < a.N) {
-                const int64_t h = item / Bp, b = 2 * (item % Bp);
+                int64_t h, b;
+                decode(item, h, b);
                 const float4* src = (const float4*)(O + 2 * ((p * NOUT + (n0 >> 8)) * SO + (n0 & 255)));
                 float yr[8], yi[8];
 #pragma unroll
@@ -412,16 +542,16 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                 const int64_t o0 = (b * a.H + h) * a.N + n0;
                 if (GATED && a.v) {
                     float t[8];
-                    load8<IO>(a.v, o0, t);
+                    unpack_raw<IO>(rv[0], t);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) yr[i] *= t[i];
                 }
                 store8<IO>(a.y, o0, yr);
                 if (b + 1 < a.B) {
-                    const int64_t o1 = o0 + a.H * a.N;
+                    const int64_t o1 = o0 + HN;
                     if (GATED && a.v) {
                         float t[8];
-                        load8<IO>(a.v, o1, t);
+                        unpack_raw<IO>(rv[1], t);
 #pragma unroll
                         for (int i = 0; i < 8; ++i) yi[i] *= t[i];
                     }

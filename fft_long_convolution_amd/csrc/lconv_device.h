@@ -220,4 +220,16 @@ __device__ __forceinline__ MatImg<CT> load_img(const void* base, int idx, int la
     return m;
 }
 
+// The same image layout, read from LDS (16-bit compute types only).
+template <int CT>
+__device__ __forceinline__ MatImg<CT> load_img_lds(const uint32_t* base, int idx, int lane) {
+    static_assert(CT != CT_F32, "LDS images are used for 16-bit operands");
+    MatImg<CT> m;
+    const uint4* p = (const uint4*)(base + idx * (ImgBytes<CT>::value / 4)) + lane * 2;
+    uint4 a = p[0], b = p[1];
+    m.re.w[0] = a.x; m.re.w[1] = a.y; m.re.w[2] = a.z; m.re.w[3] = a.w;
+    m.im.w[0] = b.x; m.im.w[1] = b.y; m.im.w[2] = b.z; m.im.w[3] = b.w;
+    return m;
+}
+
 }  // namespace lcv
