@@ -18,6 +18,8 @@
 // inverse FFT with no intermediate off-chip traffic ("FlashConv" page, Mechanism; FlashFFTConv
 // abstract) -- and the block-matrix form of the FFT (same passages).  Block sizes, the
 // register-resident tiles and the twiddle folding are this implementation's own.
+#include <type_traits>
+
 #include "kernels.h"
 #include "lconv_device.h"
 
@@ -181,7 +183,21 @@ __device__ __forceinline__ Operand<CT> lds_operand(const uint32_t* base, F idx) 
 
 }  // namespace
 
-template <int R, int CT, int IO, int MODE, bool GATED>
+
+// D[h] as raw bits (converted where it is used, so the load's latency is not waited for early)
+template <int IO>
+__device__ __forceinline__ uint32_t load1_raw(const void* base, int64_t i) {
+    if constexpr (IO == CT_F32) return ((const uint32_t*)base)[i];
+    else return ((const uint16_t*)base)[i];
+}
+template <int IO>
+__device__ __forceinline__ float raw1_to_f32(uint32_t w) {
+    if constexpr (IO == CT_F32) return __uint_as_float(w);
+    else return unpack_lo<IO>(w);
+}
+
+// MODE: conv / filter / row / row-forward.  GQ, GV: pre-gate q and post-gate v present (conv).
+template <int R, int CT, int IO, int MODE, bool GQ, bool GV>
 __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
     constexpr int P = 32 / R;                  // sequences per workgroup iteration
     constexpr int M = 256 * R;
@@ -215,11 +231,12 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
     constexpr int T_TW = T_I2 + IMG * R;
     constexpr int NBLK = P * 16;               // (sequence, n2) column blocks
     constexpr int BPW = NBLK / 8;              // blocks per wave
-
     // The radix-R blocks (F1, I3) are shared by all waves: on the convolution path they live in
     // LDS (copied once), which keeps the per-tile blocks in registers without spills.
     constexpr bool IMG_LDS = RES && MODE == MODE_CONV;
     constexpr int IMGS_W = IMG_LDS ? (T_F2 - T_F1) / 4 : 0;
+    constexpr int IOW = IO == CT_F32 ? 2 : 1;  // uint4 per 8 io elements
+
     __shared__ __attribute__((aligned(16))) uint32_t lds[V_W + XY_W + O_W + IMGS_W];
     uint32_t* V = lds;
     uint32_t* XY = lds + V_W;
@@ -251,8 +268,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
             }
         }
         if constexpr (IMG_LDS) {
-            for (int w = tid; w < IMGS_W / 4; w += 512)
-                ((uint4*)IMGS)[w] = ((const uint4*)(tab + T_F1))[w];
+            for (int w = tid; w < IMGS_W / 4; w += 512) ((uint4*)IMGS)[w] = ((const uint4*)(tab + T_F1))[w];
         } else {
 #pragma unroll
             for (int rb = 0; rb < RB1; ++rb)
@@ -279,6 +295,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
     auto I1 = [&](int i) { return RES ? mi1[i] : load_img<CT>(tab + T_I1, (wave * 4 + i) % R, lane); };
     auto I2 = [&](int i) { return RES ? mi2[i] : load_img<CT>(tab + T_I2, (wave * 4 + i) % R, lane); };
 
+    // ---- work decomposition ---------------------------------------------------------------
     const uint32_t Bp = (uint32_t)((a.B + 1) / 2);  // pairs per channel (CONV)
     const int64_t first = (int64_t)blockIdx.x * a.per_wg;
     const int64_t last = first + a.per_wg < a.nitems ? first + a.per_wg : a.nitems;
@@ -297,63 +314,77 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
         h = (int64_t)((uint32_t)s / (uint32_t)a.seq_per_h);
     };
 
-    // this thread's slot in P0 / P4: sequence p_io of the iteration, elements n0_io .. +8
+    // This thread's slot in P0 / P4: sequence p_io of the iteration, elements n0_io .. +8.
     const int p_io = tid / (16 * R), n0_io = 8 * (tid % (16 * R));
-    constexpr int IOW = IO == CT_F32 ? 2 : 1;  // uint4 per 8 elements
-    // Software pipeline: u, q of the NEXT iteration and v of this one are loaded into
-    // registers while the transforms run, so HBM latency overlaps the work.
+    // Element offsets of the slot's two rows, clamped into range so that every load can be
+    // issued unconditionally (out-of-range slots are masked where the data is used).  With no
+    // branches around memory instructions the compiler's wait counts stay exact, which keeps
+    // the software pipeline below intact.
+    auto io_offsets = [&](int64_t item, int64_t& o0, int64_t& o1, bool& ok0, bool& ok1) {
+        ok0 = item < last && n0_io < a.N;
+        const int64_t itc = item < last ? item : last - 1;
+        const int64_t n0c = n0_io < a.N ? n0_io : a.N - 8;
+        if constexpr (MODE == MODE_CONV) {
+            int64_t h, b;
+            decode(itc, h, b);
+            o0 = (b * a.H + h) * a.N + n0c;
+            ok1 = ok0 && b + 1 < a.B;
+            o1 = b + 1 < a.B ? o0 + HN : o0;
+        } else {
+            o0 = itc * a.N + n0c;
+            o1 = o0;
+            ok1 = false;
+        }
+    };
+    // Software pipeline: u, q of the NEXT iteration and v of this one are in flight while the
+    // transforms run, so HBM latency overlaps the work.
     uint4 ru[2][IOW], rq[2][IOW], rv[2][IOW];
     auto issue_in = [&](int64_t it_base) {
-        const int64_t item = it_base + p_io;
-        if (item < last && n0_io < a.N) {
-            if constexpr (MODE == MODE_CONV) {
-                int64_t h, b;
-                decode(item, h, b);
-                const int64_t o0 = (b * a.H + h) * a.N + n0_io;
-                load_raw<IO>(a.u, o0, ru[0]);
-                if (GATED && a.q) load_raw<IO>(a.q, o0, rq[0]);
-                if (b + 1 < a.B) {
-                    load_raw<IO>(a.u, o0 + HN, ru[1]);
-                    if (GATED && a.q) load_raw<IO>(a.q, o0 + HN, rq[1]);
-                }
-            } else if constexpr (MODE == MODE_FILTER) {
-                load_raw<IO>(a.u, item * a.N + n0_io, ru[0]);
+        int64_t o0, o1;
+        bool k0, k1;
+        io_offsets(it_base + p_io, o0, o1, k0, k1);
+        load_raw<IO>(a.u, o0, ru[0]);
+        if constexpr (MODE == MODE_CONV) {
+            load_raw<IO>(a.u, o1, ru[1]);
+            if constexpr (GQ) {
+                load_raw<IO>(a.q, o0, rq[0]);
+                load_raw<IO>(a.q, o1, rq[1]);
             }
         }
     };
     if constexpr (HALF_IN) issue_in(first);
 
-    for (int64_t it0 = first; it0 < last; it0 += P) {
+    // One iteration.  FULL: every slot is in range (no stores need guarding).
+    auto body = [&](const int64_t it0, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
         // ================= P0: inputs -> V =================================================
         if constexpr (HALF_IN) {
-            const int p = p_io, n0 = n0_io;
-            const int64_t item = it0 + p;
+            int64_t o0, o1;
+            bool ok0, ok1;
+            io_offsets(it0 + p_io, o0, o1, ok0, ok1);
             float xr[8], xi[8];
+            unpack_raw<IO>(ru[0], xr);
+            if constexpr (MODE == MODE_CONV) {
+                unpack_raw<IO>(ru[1], xi);
+                if constexpr (GQ) {
+                    float t[8];
+                    unpack_raw<IO>(rq[0], t);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) { xr[i] = 0.f; xi[i] = 0.f; }
-            if (item < last && n0 < a.N) {
-                unpack_raw<IO>(ru[0], xr);
-                if constexpr (MODE == MODE_CONV) {
-                    int64_t h, b;
-                    decode(item, h, b);
-                    if (GATED && a.q) {
-                        float t[8];
-                        unpack_raw<IO>(rq[0], t);
+                    for (int i = 0; i < 8; ++i) xr[i] *= t[i];
+                    unpack_raw<IO>(rq[1], t);
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) xr[i] *= t[i];
-                    }
-                    if (b + 1 < a.B) {
-                        unpack_raw<IO>(ru[1], xi);
-                        if (GATED && a.q) {
-                            float t[8];
-                            unpack_raw<IO>(rq[1], t);
-#pragma unroll
-                            for (int i = 0; i < 8; ++i) xi[i] *= t[i];
-                        }
-                    }
+                    for (int i = 0; i < 8; ++i) xi[i] *= t[i];
                 }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) xi[i] = 0.f;
             }
-            uint32_t* dst = V + ((p * NIN + (n0 >> 8)) * SV + (n0 & 255)) * EW;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                xr[i] = ok0 ? xr[i] : 0.f;
+                xi[i] = ok1 ? xi[i] : 0.f;
+            }
+            uint32_t* dst = V + ((p_io * NIN + (n0_io >> 8)) * SV + (n0_io & 255)) * EW;
             if constexpr (CT == CT_F32) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -368,67 +399,56 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                 ((uint4*)dst)[1] = w1;
             }
         } else {  // ROW / ROWFWD: one complex row of 8192 from the workspace (P == 1)
-            const int64_t item = it0;
-            const uint32_t* src = (const uint32_t*)a.u + item * (int64_t)M * EW;
+            const uint32_t* src = (const uint32_t*)a.u + it0 * (int64_t)M * EW;
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
                 const int n0 = 8 * (tid + 512 * r);
                 uint32_t* dst = V + ((n0 >> 8) * SV + (n0 & 255)) * EW;
 #pragma unroll
-                for (int i = 0; i < 2 * EW; ++i)
-                    ((uint4*)dst)[i] = ((const uint4*)(src + (int64_t)n0 * EW))[i];
+                for (int i = 0; i < 2 * EW; ++i) ((uint4*)dst)[i] = ((const uint4*)(src + (int64_t)n0 * EW))[i];
             }
         }
 
         // Loads issued now, in the order they are needed: the filter spectrum of this wave's
-        // tiles (P2), the post-gate v (P4), the next iteration's u, q (next P0).
+        // tiles and D (P2), the post-gate v (P4), the next iteration's u, q (next P0).
         uint4 rk[4][IOW];
-        float dk[4];
+        uint32_t dk[4];
         if constexpr (INV) {
             // the 4 tiles of a wave belong to one sequence when R >= 4 (two when R == 2)
-            int64_t hs[2] = {0, 0}, bases[2] = {0, 0};
-            bool oks[2] = {false, false};
-            float ds[2] = {0.f, 0.f};
             constexpr int NSEQ_W = R >= 4 ? 1 : 2;
+            int64_t bases[2] = {0, 0};
+            uint32_t ds[2] = {0, 0};
 #pragma unroll
             for (int s = 0; s < NSEQ_W; ++s) {
-                const int64_t item = it0 + (wave * 4 + 2 * s) / R;
-                oks[s] = item < last;
-                if (oks[s]) {
-                    if constexpr (MODE == MODE_CONV) {
-                        int64_t b;
-                        decode(item, hs[s], b);
-                        bases[s] = hs[s] * M;
-                    } else {
-                        int64_t khi;
-                        decode_row(item, hs[s], khi);
-                        bases[s] = hs[s] * a.M + khi * M;
-                    }
-                    ds[s] = load1<IO>(a.D, hs[s]) * a.inv_m;
+                int64_t item = it0 + (wave * 4 + 2 * s) / R;
+                item = item < last ? item : last - 1;
+                int64_t h;
+                if constexpr (MODE == MODE_CONV) {
+                    int64_t b;
+                    decode(item, h, b);
+                    bases[s] = h * M;
+                } else {
+                    int64_t khi;
+                    decode_row(item, h, khi);
+                    bases[s] = h * a.M + khi * M;
                 }
+                ds[s] = load1_raw<IO>(a.D, h);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int s = NSEQ_W == 1 ? 0 : i / 2, k1 = (wave * 4 + i) % R;
                 dk[i] = ds[s];
-#pragma unroll
-                for (int w = 0; w < IOW; ++w) rk[i][w] = make_uint4(0, 0, 0, 0);
-                if (oks[s]) load_raw_c4<IO>(a.kf, bases[s] + ((int64_t)k1 * 64 + lane) * 4, rk[i]);
+                load_raw_c4<IO>(a.kf, bases[s] + ((int64_t)k1 * 64 + lane) * 4, rk[i]);
             }
         }
-        if constexpr (MODE == MODE_CONV && GATED) {
-            const int64_t item = it0 + p_io;
-            if (a.v && item < last && n0_io < a.N) {
-                int64_t h, b;
-                decode(item, h, b);
-                const int64_t o0 = (b * a.H + h) * a.N + n0_io;
-                load_raw<IO>(a.v, o0, rv[0]);
-                if (b + 1 < a.B) load_raw<IO>(a.v, o0 + HN, rv[1]);
-            }
+        if constexpr (MODE == MODE_CONV && GV) {
+            int64_t o0, o1;
+            bool k0, k1;
+            io_offsets(it0 + p_io, o0, o1, k0, k1);
+            load_raw<IO>(a.v, o0, rv[0]);
+            load_raw<IO>(a.v, o1, rv[1]);
         }
-        if constexpr (HALF_IN) {
-            if (it0 + P < last) issue_in(it0 + P);
-        }
+        if constexpr (HALF_IN) issue_in(it0 + P);  // clamped: harmless past the end
         __syncthreads();
 
         // ================= P1: F1 (radix R over n1), V -> XY =================================
@@ -469,7 +489,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                 // spectrum in transform order, scaled by 1/M
                 const int p = t / R, k1 = t % R;
                 const int64_t item = it0 + p;
-                if (item < last) {
+                if (FULL || item < last) {
                     int64_t base;
                     if constexpr (MODE == MODE_FILTER) {
                         base = item * M;
@@ -484,8 +504,9 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
             } else {
                 float kr[4], ki[4];
                 unpack_raw_c4<IO>(rk[i], kr, ki);
+                const float d = raw1_to_f32<IO>(dk[i]) * a.inv_m;  // D folded: (K + D) / M
 #pragma unroll
-                for (int j = 0; j < 4; ++j) cmul(x.re[j], x.im[j], kr[j] + dk[i], ki[j]);
+                for (int j = 0; j < 4; ++j) cmul(x.re[j], x.im[j], kr[j] + d, ki[j]);
                 x = stage_swap<CT>(I1(i), to_operand<CT>(x));  // (L = n3, K = k2)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) cmulc(x.re[j], x.im[j], twr[j], twi[j]);
@@ -494,107 +515,109 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                 for (int j = 0; j < 4; ++j) lds_put<CT>(XY, t * ST + (4 * g + j) * SR + c, x.re[j], x.im[j]);
             }
         }
-        if constexpr (!INV) {
-            __syncthreads();  // V / XY are rewritten by the next iteration
-            continue;
-        }
         __syncthreads();
-
-        // ================= P3: I3 (inverse radix R over k1, n1 < NOUT), XY -> O ================
+        if constexpr (INV) {
+            // ================= P3: I3 (inverse radix R over k1, n1 < NOUT), XY -> O ============
 #pragma unroll 2
-        for (int bi = 0; bi < BPW; ++bi) {
-            const int blk = wave * BPW + bi, p = blk >> 4, b = blk & 15;
-            Operand<CT> din[KC3];
+            for (int bi = 0; bi < BPW; ++bi) {
+                const int blk = wave * BPW + bi, p = blk >> 4, b = blk & 15;
+                Operand<CT> din[KC3];
 #pragma unroll
-            for (int kc = 0; kc < KC3; ++kc)
-                din[kc] = lds_operand<CT>(XY, [&](int j) {
-                    const int k1 = 16 * kc + 4 * g + j;
-                    return k1 < R ? (p * R + k1) * ST + b * SR + c : -1;
-                });
+                for (int kc = 0; kc < KC3; ++kc)
+                    din[kc] = lds_operand<CT>(XY, [&](int j) {
+                        const int k1 = 16 * kc + 4 * g + j;
+                        return k1 < R ? (p * R + k1) * ST + b * SR + c : -1;
+                    });
 #pragma unroll
-            for (int rb = 0; rb < RB3; ++rb) {
-                f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
+                for (int rb = 0; rb < RB3; ++rb) {
+                    f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kc = 0; kc < KC3; ++kc) stage_keep_acc<CT>(I3(rb, kc), din[kc], re, im);
+                    for (int kc = 0; kc < KC3; ++kc) stage_keep_acc<CT>(I3(rb, kc), din[kc], re, im);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int n1 = 16 * rb + 4 * g + j;
-                    if (n1 < NOUT) *(float2*)(O + 2 * ((p * NOUT + n1) * SO + 16 * b + c)) = make_float2(re[j], im[j]);
+                    for (int j = 0; j < 4; ++j) {
+                        const int n1 = 16 * rb + 4 * g + j;
+                        if (n1 < NOUT) *(float2*)(O + 2 * ((p * NOUT + n1) * SO + 16 * b + c)) = make_float2(re[j], im[j]);
+                    }
                 }
             }
-        }
-        __syncthreads();
+            __syncthreads();
 
-        // ================= P4: epilogue ======================================================
-        if constexpr (MODE == MODE_CONV) {
-            const int p = p_io, n0 = n0_io;
-            const int64_t item = it0 + p;
-            if (item < last && n0 < a.N) {
-                int64_t h, b;
-                decode(item, h, b);
-                const float4* src = (const float4*)(O + 2 * ((p * NOUT + (n0 >> 8)) * SO + (n0 & 255)));
+            // ================= P4: epilogue ==================================================
+            if constexpr (MODE == MODE_CONV) {
+                int64_t o0, o1;
+                bool ok0, ok1;
+                io_offsets(it0 + p_io, o0, o1, ok0, ok1);
+                const float4* src = (const float4*)(O + 2 * ((p_io * NOUT + (n0_io >> 8)) * SO + (n0_io & 255)));
                 float yr[8], yi[8];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float4 w = src[i];
                     yr[2 * i] = w.x; yi[2 * i] = w.y; yr[2 * i + 1] = w.z; yi[2 * i + 1] = w.w;
                 }
-                const int64_t o0 = (b * a.H + h) * a.N + n0;
-                if (GATED && a.v) {
+                if constexpr (GV) {
                     float t[8];
                     unpack_raw<IO>(rv[0], t);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) yr[i] *= t[i];
-                }
-                store8<IO>(a.y, o0, yr);
-                if (b + 1 < a.B) {
-                    const int64_t o1 = o0 + HN;
-                    if (GATED && a.v) {
-                        float t[8];
-                        unpack_raw<IO>(rv[1], t);
+                    unpack_raw<IO>(rv[1], t);
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) yi[i] *= t[i];
-                    }
+                    for (int i = 0; i < 8; ++i) yi[i] *= t[i];
+                }
+                // odd B: the last pair has one row; its second store repeats the first
+#pragma unroll
+                for (int i = 0; i < 8; ++i) yi[i] = o1 != o0 ? yi[i] : yr[i];
+                if (FULL || ok0) {
+                    store8<IO>(a.y, o0, yr);
                     store8<IO>(a.y, o1, yi);
                 }
-            }
-        } else {  // ROW: complex row back to the workspace, in compute type
-            uint32_t* dstrow = (uint32_t*)a.y + it0 * (int64_t)M * EW;
+            } else {  // ROW: complex row back to the workspace, in compute type
+                uint32_t* dstrow = (uint32_t*)a.y + it0 * (int64_t)M * EW;
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int n0 = 8 * (tid + 512 * r);
-                const float4* src = (const float4*)(O + 2 * ((n0 >> 8) * SO + (n0 & 255)));
-                float w[16];
+                for (int r = 0; r < 2; ++r) {
+                    const int n0 = 8 * (tid + 512 * r);
+                    const float4* src = (const float4*)(O + 2 * ((n0 >> 8) * SO + (n0 & 255)));
+                    float w[16];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float4 s = src[i];
-                    w[4 * i] = s.x; w[4 * i + 1] = s.y; w[4 * i + 2] = s.z; w[4 * i + 3] = s.w;
+                    for (int i = 0; i < 4; ++i) {
+                        float4 s = src[i];
+                        w[4 * i] = s.x; w[4 * i + 1] = s.y; w[4 * i + 2] = s.z; w[4 * i + 3] = s.w;
+                    }
+                    if constexpr (CT == CT_F32) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            ((float4*)(dstrow + (int64_t)n0 * 2))[i] =
+                                make_float4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+                    } else {
+                        uint4 q0, q1;
+                        q0.x = pack2<CT>(w[0], w[1]);   q0.y = pack2<CT>(w[2], w[3]);
+                        q0.z = pack2<CT>(w[4], w[5]);   q0.w = pack2<CT>(w[6], w[7]);
+                        q1.x = pack2<CT>(w[8], w[9]);   q1.y = pack2<CT>(w[10], w[11]);
+                        q1.z = pack2<CT>(w[12], w[13]); q1.w = pack2<CT>(w[14], w[15]);
+                        ((uint4*)(dstrow + n0))[0] = q0;
+                        ((uint4*)(dstrow + n0))[1] = q1;
+                    }
                 }
-                if constexpr (CT == CT_F32) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        ((float4*)(dstrow + (int64_t)n0 * 2))[i] = make_float4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
-                } else {
-                    uint4 o0, o1;
-                    o0.x = pack2<CT>(w[0], w[1]);   o0.y = pack2<CT>(w[2], w[3]);
-                    o0.z = pack2<CT>(w[4], w[5]);   o0.w = pack2<CT>(w[6], w[7]);
-                    o1.x = pack2<CT>(w[8], w[9]);   o1.y = pack2<CT>(w[10], w[11]);
-                    o1.z = pack2<CT>(w[12], w[13]); o1.w = pack2<CT>(w[14], w[15]);
-                    ((uint4*)(dstrow + n0))[0] = o0;
-                    ((uint4*)(dstrow + n0))[1] = o1;
-                }
             }
+            // the next iteration's P0 writes only V, which P1 finished reading two barriers ago
+            if constexpr (O_ALIAS) __syncthreads();
         }
-        // next iteration's P0 writes only V, which P1 finished reading two barriers ago
-        if constexpr (O_ALIAS) __syncthreads();
+    };
+
+    // Full iterations (every slot in range) run without store guards; a partial last
+    // iteration, or a length that does not fill the half transform, takes the guarded body.
+    const bool whole_rows = !HALF_IN || a.N == M / 2;
+    int64_t it0 = first;
+    if (whole_rows) {
+        for (; it0 + P <= last; it0 += P) body(it0, std::integral_constant<bool, true>{});
     }
+    for (; it0 < last; it0 += P) body(it0, std::integral_constant<bool, false>{});
 }
 
 // ------------------------------------------------------------------------------------------
 // launch
 // ------------------------------------------------------------------------------------------
 
-template <int R, int CT, int IO, int MODE, bool GATED>
+template <int R, int CT, int IO, int MODE, bool GQ, bool GV>
 static hipError_t launch_t(const Fused1DArgs& a0, int cus, hipStream_t st) {
     Fused1DArgs a = a0;
     constexpr int P = 32 / R;
@@ -604,50 +627,56 @@ static hipError_t launch_t(const Fused1DArgs& a0, int cus, hipStream_t st) {
     const int64_t gpw = (groups + nwg - 1) / nwg;
     a.per_wg = gpw * P;
     nwg = (a.nitems + a.per_wg - 1) / a.per_wg;
-    hipLaunchKernelGGL((fused1d_kernel<R, CT, IO, MODE, GATED>), dim3((unsigned)nwg), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((fused1d_kernel<R, CT, IO, MODE, GQ, GV>), dim3((unsigned)nwg), dim3(512), 0, st, a);
     return hipGetLastError();
 }
 
+template <int R, int T>
+static hipError_t launch_conv(bool gq, bool gv, const Fused1DArgs& a, int cus, hipStream_t st) {
+    if (gq && gv) return launch_t<R, T, T, MODE_CONV, true, true>(a, cus, st);
+    if (gq) return launch_t<R, T, T, MODE_CONV, true, false>(a, cus, st);
+    if (gv) return launch_t<R, T, T, MODE_CONV, false, true>(a, cus, st);
+    return launch_t<R, T, T, MODE_CONV, false, false>(a, cus, st);
+}
+
 template <int R>
-static hipError_t launch_r(int dtype, int mode, bool gated, const Fused1DArgs& a, int cus, hipStream_t st) {
+static hipError_t launch_r(int dtype, int mode, bool gq, bool gv, const Fused1DArgs& a, int cus,
+                           hipStream_t st) {
     switch (mode) {
     case MODE_CONV:
-        if (dtype == CT_F32) return gated ? launch_t<R, CT_F32, CT_F32, MODE_CONV, true>(a, cus, st)
-                                          : launch_t<R, CT_F32, CT_F32, MODE_CONV, false>(a, cus, st);
-        if (dtype == CT_F16) return gated ? launch_t<R, CT_F16, CT_F16, MODE_CONV, true>(a, cus, st)
-                                          : launch_t<R, CT_F16, CT_F16, MODE_CONV, false>(a, cus, st);
-        return gated ? launch_t<R, CT_BF16, CT_BF16, MODE_CONV, true>(a, cus, st)
-                     : launch_t<R, CT_BF16, CT_BF16, MODE_CONV, false>(a, cus, st);
+        if (dtype == CT_F32) return launch_conv<R, CT_F32>(gq, gv, a, cus, st);
+        if (dtype == CT_F16) return launch_conv<R, CT_F16>(gq, gv, a, cus, st);
+        return launch_conv<R, CT_BF16>(gq, gv, a, cus, st);
     case MODE_FILTER:
-        if (dtype == CT_F32) return launch_t<R, CT_F32, CT_F32, MODE_FILTER, false>(a, cus, st);
-        if (dtype == CT_F16) return launch_t<R, CT_F32, CT_F16, MODE_FILTER, false>(a, cus, st);
-        return launch_t<R, CT_F32, CT_BF16, MODE_FILTER, false>(a, cus, st);
+        if (dtype == CT_F32) return launch_t<R, CT_F32, CT_F32, MODE_FILTER, false, false>(a, cus, st);
+        if (dtype == CT_F16) return launch_t<R, CT_F32, CT_F16, MODE_FILTER, false, false>(a, cus, st);
+        return launch_t<R, CT_F32, CT_BF16, MODE_FILTER, false, false>(a, cus, st);
     default:
         break;
     }
     if constexpr (R == 32) {
         if (mode == MODE_ROW) {
-            if (dtype == CT_F32) return launch_t<32, CT_F32, CT_F32, MODE_ROW, false>(a, cus, st);
-            if (dtype == CT_F16) return launch_t<32, CT_F16, CT_F16, MODE_ROW, false>(a, cus, st);
-            return launch_t<32, CT_BF16, CT_BF16, MODE_ROW, false>(a, cus, st);
+            if (dtype == CT_F32) return launch_t<32, CT_F32, CT_F32, MODE_ROW, false, false>(a, cus, st);
+            if (dtype == CT_F16) return launch_t<32, CT_F16, CT_F16, MODE_ROW, false, false>(a, cus, st);
+            return launch_t<32, CT_BF16, CT_BF16, MODE_ROW, false, false>(a, cus, st);
         }
         if (mode == MODE_ROWFWD) {
-            if (dtype == CT_F32) return launch_t<32, CT_F32, CT_F32, MODE_ROWFWD, false>(a, cus, st);
-            if (dtype == CT_F16) return launch_t<32, CT_F32, CT_F16, MODE_ROWFWD, false>(a, cus, st);
-            return launch_t<32, CT_F32, CT_BF16, MODE_ROWFWD, false>(a, cus, st);
+            if (dtype == CT_F32) return launch_t<32, CT_F32, CT_F32, MODE_ROWFWD, false, false>(a, cus, st);
+            if (dtype == CT_F16) return launch_t<32, CT_F32, CT_F16, MODE_ROWFWD, false, false>(a, cus, st);
+            return launch_t<32, CT_F32, CT_BF16, MODE_ROWFWD, false, false>(a, cus, st);
         }
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_fused1d(int R, int dtype, int mode, bool gated, const Fused1DArgs& a, int cus,
+hipError_t launch_fused1d(int R, int dtype, int mode, bool gq, bool gv, const Fused1DArgs& a, int cus,
                           hipStream_t stream) {
     switch (R) {
-    case 2: return launch_r<2>(dtype, mode, gated, a, cus, stream);
-    case 4: return launch_r<4>(dtype, mode, gated, a, cus, stream);
-    case 8: return launch_r<8>(dtype, mode, gated, a, cus, stream);
-    case 16: return launch_r<16>(dtype, mode, gated, a, cus, stream);
-    case 32: return launch_r<32>(dtype, mode, gated, a, cus, stream);
+    case 2: return launch_r<2>(dtype, mode, gq, gv, a, cus, stream);
+    case 4: return launch_r<4>(dtype, mode, gq, gv, a, cus, stream);
+    case 8: return launch_r<8>(dtype, mode, gq, gv, a, cus, stream);
+    case 16: return launch_r<16>(dtype, mode, gq, gv, a, cus, stream);
+    case 32: return launch_r<32>(dtype, mode, gq, gv, a, cus, stream);
     default: return hipErrorInvalidValue;
     }
 }

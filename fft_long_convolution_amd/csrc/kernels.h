@@ -27,7 +27,8 @@ struct Fused1DArgs {
 
 // dtype: io element type (ComputeType values); the compute type is fp32 for fp32 io and for
 // the filter transforms, else the io type.
-hipError_t launch_fused1d(int R, int dtype, int mode, bool gated, const Fused1DArgs& a,
+// gq / gv: the pre-gate q / post-gate v pointers are set (conv mode).
+hipError_t launch_fused1d(int R, int dtype, int mode, bool gq, bool gv, const Fused1DArgs& a,
                           int cus, hipStream_t stream);
 
 struct ColArgs {

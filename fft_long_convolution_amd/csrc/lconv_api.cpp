@@ -133,7 +133,7 @@ lconv_status_t lconv_filter_fft(const void* k, void* k_f, int64_t H, int64_t N, 
         a.u = k; a.y = k_f; a.tables = tabs;
         a.B = 1; a.H = H; a.N = N; a.nitems = H;
         a.inv_m = 1.0f / (float)p.M; a.M = p.M; a.M1 = 1;
-        return hip_status(launch_fused1d(p.R, dtype, MODE_FILTER, false, a, cus, stream));
+        return hip_status(launch_fused1d(p.R, dtype, MODE_FILTER, false, false, a, cus, stream));
     }
     ColTables ct;
     if (!col_tables(p.M, p.M1, &ct, &err)) return LCONV_ERR_HIP;
@@ -150,7 +150,7 @@ lconv_status_t lconv_filter_fft(const void* k, void* k_f, int64_t H, int64_t N, 
         a.u = workspace; a.y = k_f; a.tables = tabs;
         a.nitems = ns * p.M1; a.inv_m = 1.0f / (float)p.M; a.M = p.M; a.M1 = p.M1;
         a.seq0 = h0; a.seq_per_h = 1;
-        err = launch_fused1d(32, dtype, MODE_ROWFWD, false, a, cus, stream);
+        err = launch_fused1d(32, dtype, MODE_ROWFWD, false, false, a, cus, stream);
         if (err != hipSuccess) return LCONV_ERR_HIP;
     }
     return LCONV_SUCCESS;
@@ -193,13 +193,12 @@ lconv_status_t lconv_fftconv_fwd(const void* u, const void* k_f, const void* D, 
     const void* tabs = fused_tables(p.R, ct, &err);
     if (!tabs) return LCONV_ERR_HIP;
     const int64_t Bp = pairs_per_channel(B), seqs = Bp * H;
-    const bool gated = q || v;
     if (!p.multipass) {
         Fused1DArgs a{};
         a.u = u; a.q = q; a.v = v; a.y = y; a.kf = k_f; a.D = D; a.tables = tabs;
         a.B = B; a.H = H; a.N = N; a.nitems = seqs;
         a.inv_m = 1.0f / (float)p.M; a.M = p.M; a.M1 = 1;
-        return hip_status(launch_fused1d(p.R, dtype, MODE_CONV, gated, a, cus, stream));
+        return hip_status(launch_fused1d(p.R, dtype, MODE_CONV, q != nullptr, v != nullptr, a, cus, stream));
     }
     ColTables ctab;
     if (!col_tables(p.M, p.M1, &ctab, &err)) return LCONV_ERR_HIP;
@@ -216,7 +215,7 @@ lconv_status_t lconv_fftconv_fwd(const void* u, const void* k_f, const void* D, 
         a.u = workspace; a.y = workspace; a.kf = k_f; a.D = D; a.tables = tabs;
         a.nitems = ns * p.M1; a.inv_m = 1.0f / (float)p.M; a.M = p.M; a.M1 = p.M1;
         a.seq0 = s0; a.seq_per_h = Bp;
-        if (launch_fused1d(32, dtype, MODE_ROW, false, a, cus, stream) != hipSuccess) return LCONV_ERR_HIP;
+        if (launch_fused1d(32, dtype, MODE_ROW, false, false, a, cus, stream) != hipSuccess) return LCONV_ERR_HIP;
         if (launch_col_inv(dtype, c, stream) != hipSuccess) return LCONV_ERR_HIP;
     }
     return LCONV_SUCCESS;
