@@ -120,6 +120,14 @@ __device__ __forceinline__ void unpack_raw_c4(const uint4* r, float* re, float* 
     }
 }
 
+template <int IO>
+__device__ __forceinline__ void unpack_raw_c4v(const uint4* r, f32x4& re, f32x4& im) {
+    float a[4], b[4];
+    unpack_raw_c4<IO>(r, a, b);
+    re = f32x4{a[0], a[1], a[2], a[3]};
+    im = f32x4{b[0], b[1], b[2], b[3]};
+}
+
 // 4 consecutive complex values of a spectrum stored in type IO -> fp32.
 template <int IO>
 __device__ __forceinline__ void load_c4(const void* base, int64_t off, float* re, float* im) {
@@ -138,7 +146,7 @@ __device__ __forceinline__ void load_c4(const void* base, int64_t off, float* re
 }
 
 template <int IO>
-__device__ __forceinline__ void store_c4(void* base, int64_t off, const float* re, const float* im) {
+__device__ __forceinline__ void store_c4v(void* base, int64_t off, const f32x4 re, const f32x4 im) {
     if constexpr (IO == CT_F32) {
         float4* p = (float4*)((float*)base + 2 * off);
         p[0] = make_float4(re[0], im[0], re[1], im[1]);
@@ -248,12 +256,12 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
     const char* tab = (const char*)a.tables;
 
     // ---- loop-invariant registers: twiddles and matrix images ------------------------------
-    float twr[4], twi[4];
+    f32x4 twr, twi;
     {
         const float4* tp = (const float4*)(tab + T_TW) + lane * 2;
         float4 t0 = tp[0], t1 = tp[1];
-        twr[0] = t0.x; twi[0] = t0.y; twr[1] = t0.z; twi[1] = t0.w;
-        twr[2] = t1.x; twi[2] = t1.y; twr[3] = t1.z; twi[3] = t1.w;
+        twr = f32x4{t0.x, t0.z, t1.x, t1.z};
+        twi = f32x4{t0.y, t0.w, t1.y, t1.w};
     }
     MatImg<CT> mf2[4], mf3[4], mi1[4], mi2[4], mf1[RB1][KC1], mi3[RB3][KC3];
     if constexpr (RES) {
@@ -282,18 +290,18 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
             }
         }
     }
-    auto F1 = [&](int rb, int kc) {
+    auto F1 = [&](int rb, int kc) LCV_INLINE {
         if constexpr (IMG_LDS) return load_img_lds<CT>(IMGS, rb * KCF + kc, lane);
         else return RES ? mf1[rb][kc] : load_img<CT>(tab + T_F1, rb * KCF + kc, lane);
     };
-    auto I3 = [&](int rb, int kc) {
+    auto I3 = [&](int rb, int kc) LCV_INLINE {
         if constexpr (IMG_LDS) return load_img_lds<CT>(IMGS + (T_I3 - T_F1) / 4, rb * KCF + kc, lane);
         else return RES ? mi3[rb][kc] : load_img<CT>(tab + T_I3, rb * KCF + kc, lane);
     };
-    auto F2 = [&](int i) { return RES ? mf2[i] : load_img<CT>(tab + T_F2, (wave * 4 + i) % R, lane); };
-    auto F3 = [&](int i) { return RES ? mf3[i] : load_img<CT>(tab + T_F3, (wave * 4 + i) % R, lane); };
-    auto I1 = [&](int i) { return RES ? mi1[i] : load_img<CT>(tab + T_I1, (wave * 4 + i) % R, lane); };
-    auto I2 = [&](int i) { return RES ? mi2[i] : load_img<CT>(tab + T_I2, (wave * 4 + i) % R, lane); };
+    auto F2 = [&](int i) LCV_INLINE { return RES ? mf2[i] : load_img<CT>(tab + T_F2, (wave * 4 + i) % R, lane); };
+    auto F3 = [&](int i) LCV_INLINE { return RES ? mf3[i] : load_img<CT>(tab + T_F3, (wave * 4 + i) % R, lane); };
+    auto I1 = [&](int i) LCV_INLINE { return RES ? mi1[i] : load_img<CT>(tab + T_I1, (wave * 4 + i) % R, lane); };
+    auto I2 = [&](int i) LCV_INLINE { return RES ? mi2[i] : load_img<CT>(tab + T_I2, (wave * 4 + i) % R, lane); };
 
     // ---- work decomposition ---------------------------------------------------------------
     const uint32_t Bp = (uint32_t)((a.B + 1) / 2);  // pairs per channel (CONV)
@@ -302,13 +310,13 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
     const int64_t HN = a.H * a.N;
     const int m1s = a.M1 > 1 ? __builtin_ctzll((unsigned long long)a.M1) : 0;  // M1 is a power of 2
     // CONV item -> (channel h, first batch row b); 32-bit: item counts stay below 2^32
-    auto decode = [&](int64_t item, int64_t& h, int64_t& b) {
+    auto decode = [&](int64_t item, int64_t& h, int64_t& b) LCV_INLINE {
         const uint32_t it = (uint32_t)item, hh = it / Bp;
         h = hh;
         b = 2 * (int64_t)(it - hh * Bp);
     };
     // ROW/ROWFWD item -> (channel h, row k_hi)
-    auto decode_row = [&](int64_t item, int64_t& h, int64_t& khi) {
+    auto decode_row = [&](int64_t item, int64_t& h, int64_t& khi) LCV_INLINE {
         const int64_t s = a.seq0 + (item >> m1s);
         khi = item & (a.M1 - 1);
         h = (int64_t)((uint32_t)s / (uint32_t)a.seq_per_h);
@@ -320,7 +328,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
     // issued unconditionally (out-of-range slots are masked where the data is used).  With no
     // branches around memory instructions the compiler's wait counts stay exact, which keeps
     // the software pipeline below intact.
-    auto io_offsets = [&](int64_t item, int64_t& o0, int64_t& o1, bool& ok0, bool& ok1) {
+    auto io_offsets = [&](int64_t item, int64_t& o0, int64_t& o1, bool& ok0, bool& ok1) LCV_INLINE {
         ok0 = item < last && n0_io < a.N;
         const int64_t itc = item < last ? item : last - 1;
         const int64_t n0c = n0_io < a.N ? n0_io : a.N - 8;
@@ -339,7 +347,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
     // Software pipeline: u, q of the NEXT iteration and v of this one are in flight while the
     // transforms run, so HBM latency overlaps the work.
     uint4 ru[2][IOW], rq[2][IOW], rv[2][IOW];
-    auto issue_in = [&](int64_t it_base) {
+    auto issue_in = [&](int64_t it_base) LCV_INLINE {
         int64_t o0, o1;
         bool k0, k1;
         io_offsets(it_base + p_io, o0, o1, k0, k1);
@@ -355,7 +363,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
     if constexpr (HALF_IN) issue_in(first);
 
     // One iteration.  FULL: every slot is in range (no stores need guarding).
-    auto body = [&](const int64_t it0, auto full_tag) {
+    auto body = [&](const int64_t it0, auto full_tag) LCV_INLINE {
         constexpr bool FULL = decltype(full_tag)::value;
         // ================= P0: inputs -> V =================================================
         if constexpr (HALF_IN) {
@@ -477,44 +485,81 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
         __syncthreads();
 
         // ================= P2: F2, twiddle, F3, product, I1, twiddle, I2 (registers) =========
+        // The wave's four tiles are independent.  They are processed in groups of TG, each
+        // stage issued for the whole group before the next starts, so 2*TG products are in
+        // flight while earlier results drain (TG = 2 fits the register budget).
+        constexpr int TG = 2;
+        static_for<0, 4 / TG>([&](auto gi) LCV_INLINE {
+            constexpr int i0 = decltype(gi)::value * TG;
+            Operand<CT> opd[TG];
+            Tile xs[TG];
+            static_for<0, TG>([&](auto uu) LCV_INLINE {
+                constexpr int u = decltype(uu)::value;
+                const int t = wave * 4 + i0 + u;
+                opd[u] = lds_operand<CT>(XY, [&](int j) { return t * ST + (4 * g + j) * SR + c; });
+            });
+            static_for<0, TG>([&](auto uu) LCV_INLINE {
+                constexpr int u = decltype(uu)::value;
+                xs[u] = stage_swap<CT>(F2(i0 + u), opd[u]);  // (L = k2, K = n3)
+            });
+            static_for<0, TG>([&](auto uu) LCV_INLINE {
+                constexpr int u = decltype(uu)::value;
+                cmul4(xs[u], twr, twi);
+                opd[u] = to_operand<CT>(xs[u]);
+            });
+            static_for<0, TG>([&](auto uu) LCV_INLINE {
+                constexpr int u = decltype(uu)::value;
+                xs[u] = stage_keep<CT>(F3(i0 + u), opd[u]);  // (L = k2, K = k3)
+            });
+            if constexpr (INV) {
+                static_for<0, TG>([&](auto uu) LCV_INLINE {
+                    constexpr int u = decltype(uu)::value;
+                    f32x4 kr, ki;
+                    unpack_raw_c4v<IO>(rk[i0 + u], kr, ki);
+                    const float d = raw1_to_f32<IO>(dk[i0 + u]) * a.inv_m;  // D folded: (K + D) / M
+                    cmul4(xs[u], kr + d, ki);
+                    opd[u] = to_operand<CT>(xs[u]);
+                });
+                static_for<0, TG>([&](auto uu) LCV_INLINE {
+                    constexpr int u = decltype(uu)::value;
+                    xs[u] = stage_swap<CT>(I1(i0 + u), opd[u]);  // (L = n3, K = k2)
+                });
+                static_for<0, TG>([&](auto uu) LCV_INLINE {
+                    constexpr int u = decltype(uu)::value;
+                    cmulc4(xs[u], twr, twi);
+                    opd[u] = to_operand<CT>(xs[u]);
+                });
+                static_for<0, TG>([&](auto uu) LCV_INLINE {
+                    constexpr int u = decltype(uu)::value;
+                    xs[u] = stage_keep<CT>(I2(i0 + u), opd[u]);  // (L = n3, K = n2)
+                });
+                static_for<0, TG>([&](auto uu) LCV_INLINE {
+                    constexpr int u = decltype(uu)::value;
+                    const int t = wave * 4 + i0 + u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = wave * 4 + i;
-            Operand<CT> d = lds_operand<CT>(XY, [&](int j) { return t * ST + (4 * g + j) * SR + c; });
-            Tile x = stage_swap<CT>(F2(i), d);  // (L = k2, K = n3)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) cmul(x.re[j], x.im[j], twr[j], twi[j]);
-            x = stage_keep<CT>(F3(i), to_operand<CT>(x));  // (L = k2, K = k3)
-            if constexpr (!INV) {
-                // spectrum in transform order, scaled by 1/M
-                const int p = t / R, k1 = t % R;
-                const int64_t item = it0 + p;
-                if (FULL || item < last) {
-                    int64_t base;
-                    if constexpr (MODE == MODE_FILTER) {
-                        base = item * M;
-                    } else {
-                        const int64_t h = a.seq0 + (item >> m1s), khi = item & (a.M1 - 1);
-                        base = h * a.M + khi * M;
-                    }
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) { x.re[j] *= a.inv_m; x.im[j] *= a.inv_m; }
-                    store_c4<IO>(a.y, base + ((int64_t)k1 * 64 + lane) * 4, x.re, x.im);
-                }
+                    for (int j = 0; j < 4; ++j)
+                        lds_put<CT>(XY, t * ST + (4 * g + j) * SR + c, xs[u].re[j], xs[u].im[j]);
+                });
             } else {
-                float kr[4], ki[4];
-                unpack_raw_c4<IO>(rk[i], kr, ki);
-                const float d = raw1_to_f32<IO>(dk[i]) * a.inv_m;  // D folded: (K + D) / M
-#pragma unroll
-                for (int j = 0; j < 4; ++j) cmul(x.re[j], x.im[j], kr[j] + d, ki[j]);
-                x = stage_swap<CT>(I1(i), to_operand<CT>(x));  // (L = n3, K = k2)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) cmulc(x.re[j], x.im[j], twr[j], twi[j]);
-                x = stage_keep<CT>(I2(i), to_operand<CT>(x));  // (L = n3, K = n2)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) lds_put<CT>(XY, t * ST + (4 * g + j) * SR + c, x.re[j], x.im[j]);
+                // spectrum in transform order, scaled by 1/M
+                static_for<0, TG>([&](auto uu) LCV_INLINE {
+                    constexpr int u = decltype(uu)::value;
+                    const int t = wave * 4 + i0 + u, p = t / R, k1 = t % R;
+                    const int64_t item = it0 + p;
+                    if (FULL || item < last) {
+                        int64_t base;
+                        if constexpr (MODE == MODE_FILTER) {
+                            base = item * M;
+                        } else {
+                            const int64_t h = a.seq0 + (item >> m1s), khi = item & (a.M1 - 1);
+                            base = h * a.M + khi * M;
+                        }
+                        store_c4v<IO>(a.y, base + ((int64_t)k1 * 64 + lane) * 4, xs[u].re * a.inv_m,
+                                      xs[u].im * a.inv_m);
+                    }
+                });
             }
-        }
+        });
         __syncthreads();
         if constexpr (INV) {
             // ================= P3: I3 (inverse radix R over k1, n1 < NOUT), XY -> O ============

@@ -24,7 +24,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "plan.h"
+
+// Kernel-local lambdas must inline: an out-of-line call would move the register arrays they
+// capture into memory (which the compiler then places in LDS).
+#define LCV_INLINE __attribute__((always_inline))
 
 namespace lcv {
 
@@ -49,6 +55,8 @@ __device__ __forceinline__ float f16hi_to_f32(uint32_t w) {
 
 // (lo, hi) -> packed 2 x 16-bit, round to nearest even (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32)
 template <int CT> __device__ __forceinline__ uint32_t pack2(float lo, float hi);
+// One packed convert.  (Inline asm is not an option here: the compiler does not track the
+// matrix-core result hazard for an asm instruction that reads those registers.)
 template <> __device__ __forceinline__ uint32_t pack2<CT_BF16>(float lo, float hi) {
     f32x2 t = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(t, bf16x2));
@@ -56,6 +64,17 @@ template <> __device__ __forceinline__ uint32_t pack2<CT_BF16>(float lo, float h
 template <> __device__ __forceinline__ uint32_t pack2<CT_F16>(float lo, float hi) {
     f32x2 t = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(t, f16x2));
+}
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i in [B, E).  Arrays indexed by
+// these constants are split into registers from the start; a #pragma-unrolled loop index is
+// still a variable when the optimiser first sees the arrays, which can leave them in memory.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
 }
 template <int CT> __device__ __forceinline__ float unpack_lo(uint32_t w) {
     return CT == CT_BF16 ? bf16lo_to_f32(w) : f16lo_to_f32(w);
@@ -67,8 +86,10 @@ template <int CT> __device__ __forceinline__ float unpack_hi(uint32_t w) {
 // ---- tiles and operands ------------------------------------------------------------------
 
 // fp32 tile: 4 complex values per lane (the MFMA accumulators of the re and im products).
+// Kept as two 4-vectors, never as float arrays: element updates then stay register values
+// instead of memory the optimiser may leave in place.
 struct Tile {
-    float re[4], im[4];
+    f32x4 re, im;
 };
 
 // Operand image of a tile (or of a matrix): 8 K-slots per lane.
@@ -160,12 +181,7 @@ __device__ __forceinline__ void stage_swap_acc(const MatImg<CT>& m, const Operan
     im = mma<CT>(d, m.im, im);
 }
 
-__device__ __forceinline__ Tile tile_from_acc(const f32x4& re, const f32x4& im) {
-    Tile t;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { t.re[j] = re[j]; t.im[j] = im[j]; }
-    return t;
-}
+__device__ __forceinline__ Tile tile_from_acc(const f32x4& re, const f32x4& im) { return Tile{re, im}; }
 
 template <int CT>
 __device__ __forceinline__ Tile stage_keep(const MatImg<CT>& m, const Operand<CT>& d) {
@@ -193,6 +209,19 @@ __device__ __forceinline__ void cmulc(float& a, float& b, float c, float d) {
     float i = b * c - a * d;
     a = r;
     b = i;
+}
+// Tile-wide complex products: x *= (c + id), x *= conj(c + id), elementwise over the 4 values.
+__device__ __forceinline__ void cmul4(Tile& x, const f32x4 c, const f32x4 d) {
+    const f32x4 r = x.re * c - x.im * d;
+    const f32x4 i = x.re * d + x.im * c;
+    x.re = r;
+    x.im = i;
+}
+__device__ __forceinline__ void cmulc4(Tile& x, const f32x4 c, const f32x4 d) {
+    const f32x4 r = x.re * c + x.im * d;
+    const f32x4 i = x.im * c - x.re * d;
+    x.re = r;
+    x.im = i;
 }
 
 // ---- matrix images in global memory --------------------------------------------------------
