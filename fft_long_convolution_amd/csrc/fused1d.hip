@@ -328,16 +328,21 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
     // issued unconditionally (out-of-range slots are masked where the data is used).  With no
     // branches around memory instructions the compiler's wait counts stay exact, which keeps
     // the software pipeline below intact.
+    // For R >= 4 the 64 lanes of a wave share one sequence slot (16R is a multiple of 64), so
+    // the row arithmetic is wave-uniform: readfirstlane moves it to the scalar unit.
     auto io_offsets = [&](int64_t item, int64_t& o0, int64_t& o1, bool& ok0, bool& ok1) LCV_INLINE {
         ok0 = item < last && n0_io < a.N;
-        const int64_t itc = item < last ? item : last - 1;
+        int64_t itc = item < last ? item : last - 1;
+        if constexpr (R >= 4) itc = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)itc);
         const int64_t n0c = n0_io < a.N ? n0_io : a.N - 8;
         if constexpr (MODE == MODE_CONV) {
             int64_t h, b;
             decode(itc, h, b);
-            o0 = (b * a.H + h) * a.N + n0c;
+            const int64_t row0 = (b * a.H + h) * a.N;
+            const int64_t row1 = b + 1 < a.B ? row0 + HN : row0;
+            o0 = row0 + n0c;
+            o1 = row1 + n0c;
             ok1 = ok0 && b + 1 < a.B;
-            o1 = b + 1 < a.B ? o0 + HN : o0;
         } else {
             o0 = itc * a.N + n0c;
             o1 = o0;
