@@ -61,8 +61,9 @@ struct Conv2DArgs {
     void* y;             // [B][C][S][S]
     const void* tables;
     int64_t B, C;
-    float inv_p2;
-    int filter;          // 1: u = k [C][S][S], write k_f instead of y
+    float inv_p2;        // 1 / (2S)^2
+    int filter;          // 1: u = k [C][S][S]; the spectrum is written to kf
+    int cus;             // compute units (persistent grid size)
 };
 hipError_t launch_conv2d(int dtype, const Conv2DArgs& a, hipStream_t stream);
 

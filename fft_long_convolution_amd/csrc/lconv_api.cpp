@@ -231,8 +231,10 @@ lconv_status_t lconv_filter_fft2d(const void* k, void* k_f, int64_t C, int64_t S
     if (!aligned16(k) || !aligned16(k_f)) return LCONV_ERR_MISALIGNED;
     const size_t kf_bytes = lconv_filter_fft2d_bytes(C, S, dtype);
     if (overlap(k_f, kf_bytes, k, (size_t)(C * S * S) * dtype_size(dtype))) return LCONV_ERR_ALIASING;
-    (void)stream;
-    return LCONV_ERR_UNSUPPORTED;  // 2D path: see fftconv2d.hip
+    Conv2DArgs a{};
+    a.u = k; a.kf = k_f; a.C = C; a.B = 1; a.filter = 1;
+    a.inv_p2 = 1.0f / (float)(4 * S * S);
+    return hip_status(launch_conv2d(dtype, a, stream));
 }
 
 lconv_status_t lconv_fftconv2d_fwd(const void* u, const void* k_f, const void* D, void* y, int64_t B, int64_t C,
@@ -249,8 +251,16 @@ lconv_status_t lconv_fftconv2d_fwd(const void* u, const void* k_f, const void* D
     if (overlap(y, act, u, act) || overlap(y, act, k_f, lconv_filter_fft2d_bytes(C, S, dtype)) ||
         overlap(y, act, D, (size_t)C * es))
         return LCONV_ERR_ALIASING;
-    (void)stream;
-    return LCONV_ERR_UNSUPPORTED;  // 2D path: see fftconv2d.hip
+    hipError_t err = hipSuccess;
+    const int cus = device_cu_count(&err);
+    if (!cus) return LCONV_ERR_HIP;
+    const void* tabs = fused_tables(1, (int)dtype, &err);  // 256-point transform blocks
+    if (!tabs) return LCONV_ERR_HIP;
+    Conv2DArgs a{};
+    a.u = u; a.kf = k_f; a.D = D; a.y = y; a.tables = tabs;
+    a.B = B; a.C = C; a.filter = 0; a.cus = cus;
+    a.inv_p2 = 1.0f / (float)(4 * S * S);
+    return hip_status(launch_conv2d(dtype, a, stream));
 }
 
 lconv_status_t lconv_release(void) {
