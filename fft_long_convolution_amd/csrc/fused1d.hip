@@ -244,12 +244,18 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
     constexpr bool IMG_LDS = RES && MODE == MODE_CONV;
     constexpr int IMGS_W = IMG_LDS ? (T_F2 - T_F1) / 4 : 0;
     constexpr int IOW = IO == CT_F32 ? 2 : 1;  // uint4 per 8 io elements
+    // One sequence per iteration (R = 32) and 16-bit spectra: the filter spectrum of the
+    // current channel stays in LDS and is reloaded only when the channel changes (consecutive
+    // items are the batch pairs of one channel).
+    constexpr bool KF_LDS = MODE == MODE_CONV && R == 32 && IO != CT_F32;
+    constexpr int KF_W = KF_LDS ? 32 * 64 * 4 : 0;
 
-    __shared__ __attribute__((aligned(16))) uint32_t lds[V_W + XY_W + O_W + IMGS_W];
+    __shared__ __attribute__((aligned(16))) uint32_t lds[V_W + XY_W + O_W + IMGS_W + KF_W];
     uint32_t* V = lds;
     uint32_t* XY = lds + V_W;
     float* O = (float*)(O_ALIAS ? lds : lds + V_W + XY_W);
     uint32_t* IMGS = lds + V_W + XY_W + O_W;
+    uint4* KFL = (uint4*)(lds + V_W + XY_W + O_W + IMGS_W);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c = lane & 15;
@@ -366,10 +372,13 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
         }
     };
     if constexpr (HALF_IN) issue_in(first);
+    int64_t kf_h = -1;   // channel whose spectrum KFL holds (wave-uniform)
 
     // One iteration.  FULL: every slot is in range (no stores need guarding).
     auto body = [&](const int64_t it0, auto full_tag) LCV_INLINE {
         constexpr bool FULL = decltype(full_tag)::value;
+        // phases are kept apart: the compiler does not move work across the barriers
+        __builtin_amdgcn_sched_barrier(0);
         // ================= P0: inputs -> V =================================================
         if constexpr (HALF_IN) {
             int64_t o0, o1;
@@ -392,10 +401,14 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) xi[i] = 0.f;
             }
+            // Full iterations need no masks: every slot is in range, and the second row of an
+            // odd batch's last pair duplicates the first (same results, same address).
+            if constexpr (!FULL) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                xr[i] = ok0 ? xr[i] : 0.f;
-                xi[i] = ok1 ? xi[i] : 0.f;
+                for (int i = 0; i < 8; ++i) {
+                    xr[i] = ok0 ? xr[i] : 0.f;
+                    xi[i] = ok1 ? xi[i] : 0.f;
+                }
             }
             uint32_t* dst = V + ((p_io * NIN + (n0_io >> 8)) * SV + (n0_io & 255)) * EW;
             if constexpr (CT == CT_F32) {
@@ -422,11 +435,32 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
             }
         }
 
-        // Loads issued now, in the order they are needed: the filter spectrum of this wave's
-        // tiles and D (P2), the post-gate v (P4), the next iteration's u, q (next P0).
+        // Loads issued now: the filter spectrum of this wave's tiles and D (P2), then the
+        // post-gate v (P4).  The next iteration's u, q follow after F1, so that the loads of
+        // one iteration do not all queue at once.
         uint4 rk[4][IOW];
         uint32_t dk[4];
-        if constexpr (INV) {
+        if constexpr (KF_LDS) {
+            // Each wave reads back only the spectrum slices it stores itself (its own four
+            // tiles), so no barrier is needed; the loads are waited for inside the branch,
+            // which is taken once per channel.
+            const int64_t item = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)(it0 < last ? it0 : last - 1));
+            int64_t h, b;
+            decode(item, h, b);
+            if (h != kf_h) {
+                // D is folded in here, (K + D) / M, rounded once to the spectrum's type
+                const uint4* src = (const uint4*)((const uint32_t*)a.kf + h * M) + wave * 4 * 64 + lane;
+                const uint4 t0 = src[0], t1 = src[64], t2 = src[128], t3 = src[192];
+                const float d = raw1_to_f32<IO>(load1_raw<IO>(a.D, h)) * a.inv_m;
+                auto fold = [&](uint32_t w) LCV_INLINE { return pack2<IO>(unpack_lo<IO>(w) + d, unpack_hi<IO>(w)); };
+                auto fold4 = [&](uint4 t) LCV_INLINE { return make_uint4(fold(t.x), fold(t.y), fold(t.z), fold(t.w)); };
+                KFL[(wave * 4 + 0) * 64 + lane] = fold4(t0);
+                KFL[(wave * 4 + 1) * 64 + lane] = fold4(t1);
+                KFL[(wave * 4 + 2) * 64 + lane] = fold4(t2);
+                KFL[(wave * 4 + 3) * 64 + lane] = fold4(t3);
+                kf_h = h;
+            }
+        } else if constexpr (INV) {
             // the 4 tiles of a wave belong to one sequence when R >= 4 (two when R == 2)
             constexpr int NSEQ_W = R >= 4 ? 1 : 2;
             int64_t bases[2] = {0, 0};
@@ -461,95 +495,118 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
             load_raw<IO>(a.v, o0, rv[0]);
             load_raw<IO>(a.v, o1, rv[1]);
         }
-        if constexpr (HALF_IN) issue_in(it0 + P);  // clamped: harmless past the end
         __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
 
         // ================= P1: F1 (radix R over n1), V -> XY =================================
-#pragma unroll 2
-        for (int bi = 0; bi < BPW; ++bi) {
-            const int blk = wave * BPW + bi, p = blk >> 4, b = blk & 15;
-            Operand<CT> din[KC1];
-#pragma unroll
-            for (int kc = 0; kc < KC1; ++kc)
-                din[kc] = lds_operand<CT>(V, [&](int j) {
-                    const int n1 = 16 * kc + 4 * g + j;
-                    return n1 < NIN ? (p * NIN + n1) * SV + 16 * b + c : -1;
+        // Chunks of CH1 column blocks: all LDS reads of a chunk are issued before its matrix
+        // products and all writes after them (a write to XY may not be reordered before a read
+        // of V, so interleaving them would serialise the chunk on LDS latency).
+        {
+            constexpr int CH1 = BPW < 2 ? BPW : 2;
+            MatImg<CT> img1[RB1][KC1];
+            static_for<0, RB1>([&](auto rr) LCV_INLINE {
+                static_for<0, KC1>([&](auto kk) LCV_INLINE {
+                    img1[decltype(rr)::value][decltype(kk)::value] = F1(decltype(rr)::value, decltype(kk)::value);
                 });
+            });
+#pragma unroll 1
+            for (int b0 = 0; b0 < BPW; b0 += CH1) {
+                Operand<CT> din[CH1][KC1];
+                static_for<0, CH1>([&](auto cc) LCV_INLINE {
+                    constexpr int ci = decltype(cc)::value;
+                    const int blk = wave * BPW + b0 + ci, p = blk >> 4, b = blk & 15;
+                    static_for<0, KC1>([&](auto kk) LCV_INLINE {
+                        constexpr int kc = decltype(kk)::value;
+                        din[ci][kc] = lds_operand<CT>(V, [&](int j) {
+                            const int n1 = 16 * kc + 4 * g + j;
+                            return n1 < NIN ? (p * NIN + n1) * SV + 16 * b + c : -1;
+                        });
+                    });
+                });
+                Tile acc[CH1][RB1];
+                static_for<0, CH1>([&](auto cc) LCV_INLINE {
+                    constexpr int ci = decltype(cc)::value;
+                    static_for<0, RB1>([&](auto rr) LCV_INLINE {
+                        constexpr int rb = decltype(rr)::value;
+                        acc[ci][rb].re = f32x4{0.f, 0.f, 0.f, 0.f};
+                        acc[ci][rb].im = f32x4{0.f, 0.f, 0.f, 0.f};
+                        static_for<0, KC1>([&](auto kk) LCV_INLINE {
+                            constexpr int kc = decltype(kk)::value;
+                            stage_keep_acc<CT>(img1[rb][kc], din[ci][kc], acc[ci][rb].re, acc[ci][rb].im);
+                        });
+                    });
+                });
+                static_for<0, CH1>([&](auto cc) LCV_INLINE {
+                    constexpr int ci = decltype(cc)::value;
+                    const int blk = wave * BPW + b0 + ci, p = blk >> 4, b = blk & 15;
+                    static_for<0, RB1>([&](auto rr) LCV_INLINE {
+                        constexpr int rb = decltype(rr)::value;
 #pragma unroll
-            for (int rb = 0; rb < RB1; ++rb) {
-                f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kc = 0; kc < KC1; ++kc) stage_keep_acc<CT>(F1(rb, kc), din[kc], re, im);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int k1 = 16 * rb + 4 * g + j;
-                    if (k1 < R) lds_put<CT>(XY, (p * R + k1) * ST + b * SR + c, re[j], im[j]);
-                }
+                        for (int j = 0; j < 4; ++j) {
+                            const int k1 = 16 * rb + 4 * g + j;
+                            if (k1 < R) lds_put<CT>(XY, (p * R + k1) * ST + b * SR + c, acc[ci][rb].re[j], acc[ci][rb].im[j]);
+                        }
+                    });
+                });
             }
         }
         __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
 
         // ================= P2: F2, twiddle, F3, product, I1, twiddle, I2 (registers) =========
-        // The wave's four tiles are independent.  They are processed in groups of TG, each
-        // stage issued for the whole group before the next starts, so 2*TG products are in
-        // flight while earlier results drain (TG = 2 fits the register budget).
-        constexpr int TG = 2;
-        static_for<0, 4 / TG>([&](auto gi) LCV_INLINE {
-            constexpr int i0 = decltype(gi)::value * TG;
-            Operand<CT> opd[TG];
-            Tile xs[TG];
-            static_for<0, TG>([&](auto uu) LCV_INLINE {
-                constexpr int u = decltype(uu)::value;
-                const int t = wave * 4 + i0 + u;
-                opd[u] = lds_operand<CT>(XY, [&](int j) { return t * ST + (4 * g + j) * SR + c; });
+        // The wave's four tiles form two independent groups of two.  The stages of the two
+        // groups are skewed by one: the matrix products of one group are issued next to the
+        // vector work (twiddles, spectral product, packing) of the other, so both units stay
+        // busy inside one wave.  A scheduling fence between steps keeps the skew.
+        Operand<CT> opd[4];
+        Tile xs[4];
+        auto ld_op = [&](auto grp) LCV_INLINE {
+            constexpr int i0 = 2 * decltype(grp)::value;
+            static_for<i0, i0 + 2>([&](auto ii) LCV_INLINE {
+                constexpr int i = decltype(ii)::value;
+                const int t = wave * 4 + i;
+                opd[i] = lds_operand<CT>(XY, [&](int j) { return t * ST + (4 * g + j) * SR + c; });
             });
-            static_for<0, TG>([&](auto uu) LCV_INLINE {
-                constexpr int u = decltype(uu)::value;
-                xs[u] = stage_swap<CT>(F2(i0 + u), opd[u]);  // (L = k2, K = n3)
+        };
+        // matrix stage st (1: F2, 2: F3, 3: I1, 4: I2) of a group
+        auto mstage = [&](auto grp, auto stg) LCV_INLINE {
+            constexpr int i0 = 2 * decltype(grp)::value, st = decltype(stg)::value;
+            // raised priority while issuing: the products start as early as possible and run
+            // under the other wave's vector work
+            __builtin_amdgcn_s_setprio(1);
+            static_for<i0, i0 + 2>([&](auto ii) LCV_INLINE {
+                constexpr int i = decltype(ii)::value;
+                if constexpr (st == 1) xs[i] = stage_swap<CT>(F2(i), opd[i]);       // (L = k2, K = n3)
+                else if constexpr (st == 2) xs[i] = stage_keep<CT>(F3(i), opd[i]);  // (L = k2, K = k3)
+                else if constexpr (st == 3) xs[i] = stage_swap<CT>(I1(i), opd[i]);  // (L = n3, K = k2)
+                else xs[i] = stage_keep<CT>(I2(i), opd[i]);                         // (L = n3, K = n2)
             });
-            static_for<0, TG>([&](auto uu) LCV_INLINE {
-                constexpr int u = decltype(uu)::value;
-                cmul4(xs[u], twr, twi);
-                opd[u] = to_operand<CT>(xs[u]);
-            });
-            static_for<0, TG>([&](auto uu) LCV_INLINE {
-                constexpr int u = decltype(uu)::value;
-                xs[u] = stage_keep<CT>(F3(i0 + u), opd[u]);  // (L = k2, K = k3)
-            });
-            if constexpr (INV) {
-                static_for<0, TG>([&](auto uu) LCV_INLINE {
-                    constexpr int u = decltype(uu)::value;
+            __builtin_amdgcn_s_setprio(0);
+        };
+        // vector step after matrix stage st of a group
+        auto vstep = [&](auto grp, auto stg) LCV_INLINE {
+            constexpr int i0 = 2 * decltype(grp)::value, st = decltype(stg)::value;
+            static_for<i0, i0 + 2>([&](auto ii) LCV_INLINE {
+                constexpr int i = decltype(ii)::value;
+                const int t = wave * 4 + i;
+                if constexpr (st == 1) {
+                    cmul4(xs[i], twr, twi);
+                    opd[i] = to_operand<CT>(xs[i]);
+                } else if constexpr (st == 2 && INV) {
                     f32x4 kr, ki;
-                    unpack_raw_c4v<IO>(rk[i0 + u], kr, ki);
-                    const float d = raw1_to_f32<IO>(dk[i0 + u]) * a.inv_m;  // D folded: (K + D) / M
-                    cmul4(xs[u], kr + d, ki);
-                    opd[u] = to_operand<CT>(xs[u]);
-                });
-                static_for<0, TG>([&](auto uu) LCV_INLINE {
-                    constexpr int u = decltype(uu)::value;
-                    xs[u] = stage_swap<CT>(I1(i0 + u), opd[u]);  // (L = n3, K = k2)
-                });
-                static_for<0, TG>([&](auto uu) LCV_INLINE {
-                    constexpr int u = decltype(uu)::value;
-                    cmulc4(xs[u], twr, twi);
-                    opd[u] = to_operand<CT>(xs[u]);
-                });
-                static_for<0, TG>([&](auto uu) LCV_INLINE {
-                    constexpr int u = decltype(uu)::value;
-                    xs[u] = stage_keep<CT>(I2(i0 + u), opd[u]);  // (L = n3, K = n2)
-                });
-                static_for<0, TG>([&](auto uu) LCV_INLINE {
-                    constexpr int u = decltype(uu)::value;
-                    const int t = wave * 4 + i0 + u;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        lds_put<CT>(XY, t * ST + (4 * g + j) * SR + c, xs[u].re[j], xs[u].im[j]);
-                });
-            } else {
-                // spectrum in transform order, scaled by 1/M
-                static_for<0, TG>([&](auto uu) LCV_INLINE {
-                    constexpr int u = decltype(uu)::value;
-                    const int t = wave * 4 + i0 + u, p = t / R, k1 = t % R;
+                    if constexpr (KF_LDS) {
+                        const uint4 kw = KFL[t * 64 + lane];  // (K + D) / M
+                        unpack_raw_c4v<IO>(&kw, kr, ki);
+                    } else {
+                        unpack_raw_c4v<IO>(rk[i], kr, ki);
+                        kr += raw1_to_f32<IO>(dk[i]) * a.inv_m;  // D folded: (K + D) / M
+                    }
+                    cmul4(xs[i], kr, ki);
+                    opd[i] = to_operand<CT>(xs[i]);
+                } else if constexpr (st == 2) {
+                    // spectrum in transform order, scaled by 1/M
+                    const int p = t / R, k1 = t % R;
                     const int64_t item = it0 + p;
                     if (FULL || item < last) {
                         int64_t base;
@@ -559,38 +616,111 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                             const int64_t h = a.seq0 + (item >> m1s), khi = item & (a.M1 - 1);
                             base = h * a.M + khi * M;
                         }
-                        store_c4v<IO>(a.y, base + ((int64_t)k1 * 64 + lane) * 4, xs[u].re * a.inv_m,
-                                      xs[u].im * a.inv_m);
+                        store_c4v<IO>(a.y, base + ((int64_t)k1 * 64 + lane) * 4, xs[i].re * a.inv_m,
+                                      xs[i].im * a.inv_m);
                     }
-                });
-            }
-        });
+                } else if constexpr (st == 3) {
+                    cmulc4(xs[i], twr, twi);
+                    opd[i] = to_operand<CT>(xs[i]);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        lds_put<CT>(XY, t * ST + (4 * g + j) * SR + c, xs[i].re[j], xs[i].im[j]);
+                }
+            });
+        };
+        using G0 = std::integral_constant<int, 0>;
+        using G1 = std::integral_constant<int, 1>;
+        using S1 = std::integral_constant<int, 1>;
+        using S2 = std::integral_constant<int, 2>;
+        using S3 = std::integral_constant<int, 3>;
+        using S4 = std::integral_constant<int, 4>;
+        ld_op(G0{});
+        ld_op(G1{});
+        mstage(G0{}, S1{});
+        __builtin_amdgcn_sched_barrier(0);
+        mstage(G1{}, S1{}); vstep(G0{}, S1{});
+        __builtin_amdgcn_sched_barrier(0);
+        mstage(G0{}, S2{}); vstep(G1{}, S1{});
+        __builtin_amdgcn_sched_barrier(0);
+        mstage(G1{}, S2{}); vstep(G0{}, S2{});
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (INV) {
+            mstage(G0{}, S3{}); vstep(G1{}, S2{});
+            __builtin_amdgcn_sched_barrier(0);
+            mstage(G1{}, S3{}); vstep(G0{}, S3{});
+            // the next iteration's u, q go out here (consumed in its P0): late enough to keep
+            // their registers out of the busiest part of this phase
+            if constexpr (HALF_IN) issue_in(it0 + P);  // clamped: harmless past the end
+            __builtin_amdgcn_sched_barrier(0);
+            mstage(G0{}, S4{}); vstep(G1{}, S3{});
+            __builtin_amdgcn_sched_barrier(0);
+            mstage(G1{}, S4{}); vstep(G0{}, S4{});
+            __builtin_amdgcn_sched_barrier(0);
+            vstep(G1{}, S4{});
+        } else {
+            vstep(G1{}, S2{});
+            if constexpr (HALF_IN) issue_in(it0 + P);
+        }
         __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (INV) {
             // ================= P3: I3 (inverse radix R over k1, n1 < NOUT), XY -> O ============
-#pragma unroll 2
-            for (int bi = 0; bi < BPW; ++bi) {
-                const int blk = wave * BPW + bi, p = blk >> 4, b = blk & 15;
-                Operand<CT> din[KC3];
-#pragma unroll
-                for (int kc = 0; kc < KC3; ++kc)
-                    din[kc] = lds_operand<CT>(XY, [&](int j) {
-                        const int k1 = 16 * kc + 4 * g + j;
-                        return k1 < R ? (p * R + k1) * ST + b * SR + c : -1;
+            // Same chunked read / multiply / write order as P1.
+            {
+                constexpr int CH3 = BPW < 2 ? BPW : 2;
+                MatImg<CT> img3[RB3][KC3];
+                static_for<0, RB3>([&](auto rr) LCV_INLINE {
+                    static_for<0, KC3>([&](auto kk) LCV_INLINE {
+                        img3[decltype(rr)::value][decltype(kk)::value] = I3(decltype(rr)::value, decltype(kk)::value);
                     });
+                });
+#pragma unroll 1
+                for (int b0 = 0; b0 < BPW; b0 += CH3) {
+                    Operand<CT> din[CH3][KC3];
+                    static_for<0, CH3>([&](auto cc) LCV_INLINE {
+                        constexpr int ci = decltype(cc)::value;
+                        const int blk = wave * BPW + b0 + ci, p = blk >> 4, b = blk & 15;
+                        static_for<0, KC3>([&](auto kk) LCV_INLINE {
+                            constexpr int kc = decltype(kk)::value;
+                            din[ci][kc] = lds_operand<CT>(XY, [&](int j) {
+                                const int k1 = 16 * kc + 4 * g + j;
+                                return k1 < R ? (p * R + k1) * ST + b * SR + c : -1;
+                            });
+                        });
+                    });
+                    Tile acc[CH3][RB3];
+                    static_for<0, CH3>([&](auto cc) LCV_INLINE {
+                        constexpr int ci = decltype(cc)::value;
+                        static_for<0, RB3>([&](auto rr) LCV_INLINE {
+                            constexpr int rb = decltype(rr)::value;
+                            acc[ci][rb].re = f32x4{0.f, 0.f, 0.f, 0.f};
+                            acc[ci][rb].im = f32x4{0.f, 0.f, 0.f, 0.f};
+                            static_for<0, KC3>([&](auto kk) LCV_INLINE {
+                                constexpr int kc = decltype(kk)::value;
+                                stage_keep_acc<CT>(img3[rb][kc], din[ci][kc], acc[ci][rb].re, acc[ci][rb].im);
+                            });
+                        });
+                    });
+                    static_for<0, CH3>([&](auto cc) LCV_INLINE {
+                        constexpr int ci = decltype(cc)::value;
+                        const int blk = wave * BPW + b0 + ci, p = blk >> 4, b = blk & 15;
+                        static_for<0, RB3>([&](auto rr) LCV_INLINE {
+                            constexpr int rb = decltype(rr)::value;
 #pragma unroll
-                for (int rb = 0; rb < RB3; ++rb) {
-                    f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kc = 0; kc < KC3; ++kc) stage_keep_acc<CT>(I3(rb, kc), din[kc], re, im);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int n1 = 16 * rb + 4 * g + j;
-                        if (n1 < NOUT) *(float2*)(O + 2 * ((p * NOUT + n1) * SO + 16 * b + c)) = make_float2(re[j], im[j]);
-                    }
+                            for (int j = 0; j < 4; ++j) {
+                                const int n1 = 16 * rb + 4 * g + j;
+                                if (n1 < NOUT)
+                                    *(float2*)(O + 2 * ((p * NOUT + n1) * SO + 16 * b + c)) =
+                                        make_float2(acc[ci][rb].re[j], acc[ci][rb].im[j]);
+                            }
+                        });
+                    });
                 }
             }
             __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
 
             // ================= P4: epilogue ==================================================
             if constexpr (MODE == MODE_CONV) {
@@ -613,9 +743,11 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
 #pragma unroll
                     for (int i = 0; i < 8; ++i) yi[i] *= t[i];
                 }
-                // odd B: the last pair has one row; its second store repeats the first
+                // odd B, partial iteration: the masked second row must not overwrite the first
+                if constexpr (!FULL) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) yi[i] = o1 != o0 ? yi[i] : yr[i];
+                    for (int i = 0; i < 8; ++i) yi[i] = o1 != o0 ? yi[i] : yr[i];
+                }
                 if (FULL || ok0) {
                     store8<IO>(a.y, o0, yr);
                     store8<IO>(a.y, o1, yi);
