@@ -225,7 +225,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
     constexpr int SO = 260;                    // O: row stride (complex fp32)
     constexpr int V_W = P * NIN * SV * EW;
     constexpr int XY_W = 32 * ST * EW;
-    // fp32 row pass: O (same size as V) aliases V, with one extra barrier per iteration
+    // fp32 row pass: O (same element size as V) aliases V; both are used wave-locally
     constexpr bool O_ALIAS = (MODE == MODE_ROW && CT == CT_F32);
     constexpr int O_W = (INV && !O_ALIAS) ? P * NOUT * SO * 2 : 0;
     constexpr bool RES = (CT != CT_F32);       // matrix images resident in registers
@@ -283,6 +283,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
         }
         if constexpr (IMG_LDS) {
             for (int w = tid; w < IMGS_W / 4; w += 512) ((uint4*)IMGS)[w] = ((const uint4*)(tab + T_F1))[w];
+            __syncthreads();  // every wave reads all of them
         } else {
 #pragma unroll
             for (int rb = 0; rb < RB1; ++rb)
@@ -328,14 +329,25 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
         h = (int64_t)((uint32_t)s / (uint32_t)a.seq_per_h);
     };
 
-    // This thread's slot in P0 / P4: sequence p_io of the iteration, elements n0_io .. +8.
-    const int p_io = tid / (16 * R), n0_io = 8 * (tid % (16 * R));
+    // Slots of P0 / P4: 8 consecutive elements of one sequence row.  A wave's slots are the
+    // columns of its own radix-R blocks (blocks wave*BPW .. +BPW-1, every row n1), so the input
+    // a wave packs into V is exactly what its F1 reads, and the output it stores is exactly
+    // what its I3 wrote to O: no barrier is needed around P0 and P4.  Slot ci of the wave:
+    // row n1 = ci / (2 BPW), block wave*BPW + (ci / 2) % BPW, half ci % 2 of the block.
+    auto slot = [&](int ci, int& p, int& n0) LCV_INLINE {
+        const int n1 = ci / (2 * BPW), blk = wave * BPW + (ci >> 1) % BPW;
+        p = blk >> 4;
+        n0 = 256 * n1 + 16 * (blk & 15) + 8 * (ci & 1);
+    };
+    // Half-length input (one slot per lane): sequence p_io of the iteration, elements n0_io..+8.
+    int p_io, n0_io;
+    slot(lane, p_io, n0_io);
     // Element offsets of the slot's two rows, clamped into range so that every load can be
     // issued unconditionally (out-of-range slots are masked where the data is used).  With no
     // branches around memory instructions the compiler's wait counts stay exact, which keeps
     // the software pipeline below intact.
-    // For R >= 4 the 64 lanes of a wave share one sequence slot (16R is a multiple of 64), so
-    // the row arithmetic is wave-uniform: readfirstlane moves it to the scalar unit.
+    // For R >= 4 the blocks of a wave lie in one sequence, so the row arithmetic is
+    // wave-uniform: readfirstlane moves it to the scalar unit.
     auto io_offsets = [&](int64_t item, int64_t& o0, int64_t& o1, bool& ok0, bool& ok1) LCV_INLINE {
         ok0 = item < last && n0_io < a.N;
         int64_t itc = item < last ? item : last - 1;
@@ -428,7 +440,8 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
             const uint32_t* src = (const uint32_t*)a.u + it0 * (int64_t)M * EW;
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
-                const int n0 = 8 * (tid + 512 * r);
+                int pp, n0;
+                slot(lane + 64 * r, pp, n0);
                 uint32_t* dst = V + ((n0 >> 8) * SV + (n0 & 255)) * EW;
 #pragma unroll
                 for (int i = 0; i < 2 * EW; ++i) ((uint4*)dst)[i] = ((const uint4*)(src + (int64_t)n0 * EW))[i];
@@ -495,7 +508,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
             load_raw<IO>(a.v, o0, rv[0]);
             load_raw<IO>(a.v, o1, rv[1]);
         }
-        __syncthreads();
+        // P1 reads only the V slots this wave wrote (its own blocks): no barrier.
         __builtin_amdgcn_sched_barrier(0);
 
         // ================= P1: F1 (radix R over n1), V -> XY =================================
@@ -635,27 +648,43 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
         using S2 = std::integral_constant<int, 2>;
         using S3 = std::integral_constant<int, 3>;
         using S4 = std::integral_constant<int, 4>;
+        // one matrix product, then a share of the vector work, repeated: the two waves of a SIMD
+        // leave each barrier in step, and fine interleaving lets one wave's products run under
+        // the other's vector instructions
+        auto interleave = [&](auto nv) LCV_INLINE {
+            static_for<0, 4>([&](auto) LCV_INLINE {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, decltype(nv)::value, 0);
+            });
+        };
         ld_op(G0{});
         ld_op(G1{});
         mstage(G0{}, S1{});
         __builtin_amdgcn_sched_barrier(0);
         mstage(G1{}, S1{}); vstep(G0{}, S1{});
+        interleave(std::integral_constant<int, 10>{});
         __builtin_amdgcn_sched_barrier(0);
         mstage(G0{}, S2{}); vstep(G1{}, S1{});
+        interleave(std::integral_constant<int, 10>{});
         __builtin_amdgcn_sched_barrier(0);
         mstage(G1{}, S2{}); vstep(G0{}, S2{});
+        interleave(std::integral_constant<int, 14>{});
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (INV) {
             mstage(G0{}, S3{}); vstep(G1{}, S2{});
+            interleave(std::integral_constant<int, 14>{});
             __builtin_amdgcn_sched_barrier(0);
             mstage(G1{}, S3{}); vstep(G0{}, S3{});
+            interleave(std::integral_constant<int, 10>{});
             // the next iteration's u, q go out here (consumed in its P0): late enough to keep
             // their registers out of the busiest part of this phase
             if constexpr (HALF_IN) issue_in(it0 + P);  // clamped: harmless past the end
             __builtin_amdgcn_sched_barrier(0);
             mstage(G0{}, S4{}); vstep(G1{}, S3{});
+            interleave(std::integral_constant<int, 10>{});
             __builtin_amdgcn_sched_barrier(0);
             mstage(G1{}, S4{}); vstep(G0{}, S4{});
+            interleave(std::integral_constant<int, 4>{});
             __builtin_amdgcn_sched_barrier(0);
             vstep(G1{}, S4{});
         } else {
@@ -718,9 +747,8 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                     });
                 }
             }
-            __syncthreads();
+            // P4 reads only the O slots this wave wrote (its own blocks): no barrier.
             __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_sched_barrier(0);
 
             // ================= P4: epilogue ==================================================
             if constexpr (MODE == MODE_CONV) {
@@ -756,7 +784,8 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                 uint32_t* dstrow = (uint32_t*)a.y + it0 * (int64_t)M * EW;
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
-                    const int n0 = 8 * (tid + 512 * r);
+                    int pp, n0;
+                    slot(lane + 64 * r, pp, n0);
                     const float4* src = (const float4*)(O + 2 * ((n0 >> 8) * SO + (n0 & 255)));
                     float w[16];
 #pragma unroll
@@ -780,8 +809,6 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                     }
                 }
             }
-            // the next iteration's P0 writes only V, which P1 finished reading two barriers ago
-            if constexpr (O_ALIAS) __syncthreads();
         }
     };
 
