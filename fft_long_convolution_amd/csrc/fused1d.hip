@@ -823,6 +823,356 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
+// Pipelined kernel for M = 8192 (R = 32), 16-bit types, whole rows (N = 4096), convolution.
+//
+// Same transform chain as fused1d_kernel, arranged so that the vector/matrix-heavy register
+// chain (P2) of one iteration runs beside the LDS- and memory-heavy wave-local work of its
+// neighbours: segment k holds P2(k) and W(k) = { P3, P4 of k-1; P0, P1 of k+1 }, with one
+// barrier per segment.  XY is double-buffered (iteration parity).  Waves 0-3 run P2 first and
+// waves 4-7 run W first, so each SIMD (which hosts waves w and w+4) pairs the two kinds of work.
+// O is kept in the compute type and shares V's space (both are used wave-locally); the filter
+// spectrum has two LDS copies so the next channel's can be loaded while the current one is read.
+// ------------------------------------------------------------------------------------------
+template <int CT, bool GQ, bool GV>
+__global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
+    constexpr int R = 32, M = 8192, KCF = 2;
+    constexpr int IMG = ImgBytes<CT>::value;
+    constexpr int T_F1 = 0, T_I3 = T_F1 + IMG * 2 * KCF, T_F2 = T_I3 + IMG * KCF * KCF;
+    constexpr int T_F3 = T_F2 + IMG * R, T_I1 = T_F3 + IMG * R, T_I2 = T_I1 + IMG * R, T_TW = T_I2 + IMG * R;
+    constexpr int ST = 260;                      // XY tile stride (words)
+    constexpr int SV = 260;                      // V / O row stride (words, one complex per word)
+    constexpr int XY_W = 32 * ST, V_W = 16 * SV, IM_W = 4 * IMG / 4, KF_W = 32 * 64 * 4;
+    __shared__ __attribute__((aligned(16))) uint32_t lds[2 * XY_W + V_W + IM_W + 2 * KF_W];
+    uint32_t* const XYb = lds;                   // two buffers of XY_W
+    uint32_t* const V = lds + 2 * XY_W;          // input slots (P0 -> P1) and output slots (P3 -> P4)
+    uint32_t* const IMS = V + V_W;               // F1 (rb = 0, 1) and I3 (kc = 0, 1) images
+    uint4* const KFL = (uint4*)(IMS + IM_W);     // two copies of (K + D) / M, 32 tiles x 64 lanes
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    const char* tab = (const char*)a.tables;
+    const int64_t first = (int64_t)blockIdx.x * a.per_wg;
+    const int64_t last = first + a.per_wg < a.nitems ? first + a.per_wg : a.nitems;
+    if (first >= last) return;
+
+    // Tile element (row r, column col) of tile t.  Rows 4g + j of one instruction land in four
+    // different bank groups (the XOR on row / 4); tiles 4g + j of one instruction do too (the
+    // stride 260 = 4 mod 64 words).
+    auto xy_addr = [&](int t, int r, int col) LCV_INLINE { return t * ST + ((16 * r + col) ^ (((r >> 2) & 3) << 4)); };
+
+    // ---- loop-invariant registers and LDS ---------------------------------------------------
+    f32x4 twr, twi;
+    {
+        const float4* tp = (const float4*)(tab + T_TW) + lane * 2;
+        float4 t0 = tp[0], t1 = tp[1];
+        twr = f32x4{t0.x, t0.z, t1.x, t1.z};
+        twi = f32x4{t0.y, t0.w, t1.y, t1.w};
+    }
+    MatImg<CT> mf2[4], mf3[4], mi1[4], mi2[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int k1 = wave * 4 + i;
+        mf2[i] = load_img<CT>(tab + T_F2, k1, lane);
+        mf3[i] = load_img<CT>(tab + T_F3, k1, lane);
+        mi1[i] = load_img<CT>(tab + T_I1, k1, lane);
+        mi2[i] = load_img<CT>(tab + T_I2, k1, lane);
+    }
+    {
+        // F1 blocks (rb, kc = 0) are table images 0 and KCF; I3 blocks (rb = 0, kc) are 0 and 1
+        const int srcs[4] = {T_F1, T_F1 + IMG * KCF, T_I3, T_I3 + IMG};
+        for (int w = tid; w < IM_W / 4; w += 512) {
+            const int img = w / (IMG / 16), off = w % (IMG / 16);
+            ((uint4*)IMS)[w] = ((const uint4*)(tab + srcs[img]))[off];
+        }
+        __syncthreads();  // every wave reads all four
+    }
+
+    // ---- items and addresses --------------------------------------------------------------
+    const uint32_t Bp = (uint32_t)((a.B + 1) / 2);
+    const int64_t HN = a.H * a.N;
+    auto channel = [&](int64_t item) LCV_INLINE {
+        return (int64_t)((uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)item) / Bp);
+    };
+    // this lane's slot: row n1 = lane / 4, columns 32 wave + 8 (lane % 4) .. +8 (the wave's blocks)
+    const int s_n1 = lane >> 2, s_col = 32 * wave + 8 * (lane & 3);
+    const int64_t s_n0 = 256 * s_n1 + s_col;
+    // element offsets of the slot in the item's two batch rows (an odd batch's last pair
+    // repeats its row: same data in, same results out to the same address)
+    auto offsets = [&](int64_t item, int64_t& o0, int64_t& o1) LCV_INLINE {
+        item = item < last ? item : last - 1;
+        const uint32_t it = __builtin_amdgcn_readfirstlane((uint32_t)item), hh = it / Bp;
+        const int64_t b = 2 * (int64_t)(it - hh * Bp);
+        const int64_t row0 = (b * a.H + hh) * a.N;
+        o0 = row0 + s_n0;
+        o1 = (b + 1 < a.B ? row0 + HN : row0) + s_n0;
+    };
+    uint4 ru[2], rq[2], rv[2];
+    auto issue_uq = [&](int64_t item) LCV_INLINE {
+        int64_t o0, o1;
+        offsets(item, o0, o1);
+        load_raw<CT>(a.u, o0, &ru[0]);
+        load_raw<CT>(a.u, o1, &ru[1]);
+        if constexpr (GQ) {
+            load_raw<CT>(a.q, o0, &rq[0]);
+            load_raw<CT>(a.q, o1, &rq[1]);
+        }
+    };
+    auto issue_v = [&](int64_t item) LCV_INLINE {
+        if constexpr (GV) {
+            int64_t o0, o1;
+            offsets(item, o0, o1);
+            load_raw<CT>(a.v, o0, &rv[0]);
+            load_raw<CT>(a.v, o1, &rv[1]);
+        }
+    };
+    // (K + D) / M of channel h into copy kb, this wave's tiles only (read back by this wave)
+    auto load_kf = [&](int64_t h, int kb) LCV_INLINE {
+        const uint4* src = (const uint4*)((const uint32_t*)a.kf + h * M) + wave * 4 * 64 + lane;
+        const uint4 t0 = src[0], t1 = src[64], t2 = src[128], t3 = src[192];
+        const float d = raw1_to_f32<CT>(load1_raw<CT>(a.D, h)) * a.inv_m;
+        auto fold = [&](uint32_t w) LCV_INLINE { return pack2<CT>(unpack_lo<CT>(w) + d, unpack_hi<CT>(w)); };
+        auto fold4 = [&](uint4 t) LCV_INLINE { return make_uint4(fold(t.x), fold(t.y), fold(t.z), fold(t.w)); };
+        uint4* dst = KFL + kb * (KF_W / 4) + wave * 4 * 64 + lane;
+        dst[0] = fold4(t0);
+        dst[64] = fold4(t1);
+        dst[128] = fold4(t2);
+        dst[192] = fold4(t3);
+    };
+
+    // ---- phases ------------------------------------------------------------------------------
+    // P0: gate and pack this lane's slot of the item into V
+    auto P0 = [&]() LCV_INLINE {
+        float xr[8], xi[8];
+        unpack_raw<CT>(&ru[0], xr);
+        unpack_raw<CT>(&ru[1], xi);
+        if constexpr (GQ) {
+            float t[8];
+            unpack_raw<CT>(&rq[0], t);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xr[i] *= t[i];
+            unpack_raw<CT>(&rq[1], t);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xi[i] *= t[i];
+        }
+        uint4 w0, w1;
+        w0.x = pack2<CT>(xr[0], xi[0]); w0.y = pack2<CT>(xr[1], xi[1]);
+        w0.z = pack2<CT>(xr[2], xi[2]); w0.w = pack2<CT>(xr[3], xi[3]);
+        w1.x = pack2<CT>(xr[4], xi[4]); w1.y = pack2<CT>(xr[5], xi[5]);
+        w1.z = pack2<CT>(xr[6], xi[6]); w1.w = pack2<CT>(xr[7], xi[7]);
+        uint4* dst = (uint4*)(V + s_n1 * SV + s_col);
+        dst[0] = w0;
+        dst[1] = w1;
+    };
+    // P1: F1 (radix 32 over n1 < 16) on this wave's two column blocks, V -> XY
+    auto P1 = [&](uint32_t* XY) LCV_INLINE {
+        const MatImg<CT> f0 = load_img_lds<CT>(IMS, 0, lane), f1 = load_img_lds<CT>(IMS, 1, lane);
+        Operand<CT> din[2];
+        static_for<0, 2>([&](auto bb) LCV_INLINE {
+            constexpr int bi = decltype(bb)::value;
+            const int b = 2 * wave + bi;
+            din[bi] = lds_operand<CT>(V, [&](int j) { return (4 * g + j) * SV + 16 * b + c; });
+        });
+        Tile acc[2][2];
+        static_for<0, 2>([&](auto bb) LCV_INLINE {
+            constexpr int bi = decltype(bb)::value;
+            acc[bi][0] = stage_keep<CT>(f0, din[bi]);
+            acc[bi][1] = stage_keep<CT>(f1, din[bi]);
+        });
+        static_for<0, 2>([&](auto bb) LCV_INLINE {
+            constexpr int bi = decltype(bb)::value;
+            const int b = 2 * wave + bi;
+            static_for<0, 2>([&](auto rr) LCV_INLINE {
+                constexpr int rb = decltype(rr)::value;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    lds_put<CT>(XY, xy_addr(16 * rb + 4 * g + j, b, c), acc[bi][rb].re[j], acc[bi][rb].im[j]);
+            });
+        });
+    };
+    // P2: F2, twiddle, F3, product, I1, twiddle, I2 on this wave's four tiles (registers).
+    // Two groups of two tiles, one stage apart; inside a step one product, then a share of
+    // the vector work, repeated.
+    auto P2 = [&](uint32_t* XY, const uint4* kfl) LCV_INLINE {
+        Operand<CT> opd[4];
+        Tile xs[4];
+        auto ld_op = [&](auto grp) LCV_INLINE {
+            constexpr int i0 = 2 * decltype(grp)::value;
+            static_for<i0, i0 + 2>([&](auto ii) LCV_INLINE {
+                constexpr int i = decltype(ii)::value;
+                const int t = wave * 4 + i;
+                opd[i] = lds_operand<CT>(XY, [&](int j) { return xy_addr(t, 4 * g + j, c); });
+            });
+        };
+        auto mstage = [&](auto grp, auto stg) LCV_INLINE {
+            constexpr int i0 = 2 * decltype(grp)::value, st = decltype(stg)::value;
+            __builtin_amdgcn_s_setprio(1);
+            static_for<i0, i0 + 2>([&](auto ii) LCV_INLINE {
+                constexpr int i = decltype(ii)::value;
+                if constexpr (st == 1) xs[i] = stage_swap<CT>(mf2[i], opd[i]);       // (L = k2, K = n3)
+                else if constexpr (st == 2) xs[i] = stage_keep<CT>(mf3[i], opd[i]);  // (L = k2, K = k3)
+                else if constexpr (st == 3) xs[i] = stage_swap<CT>(mi1[i], opd[i]);  // (L = n3, K = k2)
+                else xs[i] = stage_keep<CT>(mi2[i], opd[i]);                         // (L = n3, K = n2)
+            });
+            __builtin_amdgcn_s_setprio(0);
+        };
+        auto vstep = [&](auto grp, auto stg) LCV_INLINE {
+            constexpr int i0 = 2 * decltype(grp)::value, st = decltype(stg)::value;
+            static_for<i0, i0 + 2>([&](auto ii) LCV_INLINE {
+                constexpr int i = decltype(ii)::value;
+                const int t = wave * 4 + i;
+                if constexpr (st == 1) {
+                    cmul4(xs[i], twr, twi);
+                    opd[i] = to_operand<CT>(xs[i]);
+                } else if constexpr (st == 2) {
+                    const uint4 kw = kfl[t * 64 + lane];  // (K + D) / M
+                    f32x4 kr, ki;
+                    unpack_raw_c4v<CT>(&kw, kr, ki);
+                    cmul4(xs[i], kr, ki);
+                    opd[i] = to_operand<CT>(xs[i]);
+                } else if constexpr (st == 3) {
+                    cmulc4(xs[i], twr, twi);
+                    opd[i] = to_operand<CT>(xs[i]);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) lds_put<CT>(XY, xy_addr(t, 4 * g + j, c), xs[i].re[j], xs[i].im[j]);
+                }
+            });
+        };
+        auto interleave = [&](auto nv) LCV_INLINE {
+            static_for<0, 4>([&](auto) LCV_INLINE {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, decltype(nv)::value, 0);
+            });
+        };
+        using G0 = std::integral_constant<int, 0>;
+        using G1 = std::integral_constant<int, 1>;
+        using S1 = std::integral_constant<int, 1>;
+        using S2 = std::integral_constant<int, 2>;
+        using S3 = std::integral_constant<int, 3>;
+        using S4 = std::integral_constant<int, 4>;
+        ld_op(G0{});
+        ld_op(G1{});
+        mstage(G0{}, S1{});
+        __builtin_amdgcn_sched_barrier(0);
+        mstage(G1{}, S1{}); vstep(G0{}, S1{}); interleave(std::integral_constant<int, 10>{});
+        __builtin_amdgcn_sched_barrier(0);
+        mstage(G0{}, S2{}); vstep(G1{}, S1{}); interleave(std::integral_constant<int, 10>{});
+        __builtin_amdgcn_sched_barrier(0);
+        mstage(G1{}, S2{}); vstep(G0{}, S2{}); interleave(std::integral_constant<int, 14>{});
+        __builtin_amdgcn_sched_barrier(0);
+        mstage(G0{}, S3{}); vstep(G1{}, S2{}); interleave(std::integral_constant<int, 14>{});
+        __builtin_amdgcn_sched_barrier(0);
+        mstage(G1{}, S3{}); vstep(G0{}, S3{}); interleave(std::integral_constant<int, 10>{});
+        __builtin_amdgcn_sched_barrier(0);
+        mstage(G0{}, S4{}); vstep(G1{}, S3{}); interleave(std::integral_constant<int, 10>{});
+        __builtin_amdgcn_sched_barrier(0);
+        mstage(G1{}, S4{}); vstep(G0{}, S4{}); interleave(std::integral_constant<int, 4>{});
+        __builtin_amdgcn_sched_barrier(0);
+        vstep(G1{}, S4{});
+    };
+    // P3: I3 (inverse radix 32, rows n1 < 16) on this wave's two column blocks, XY -> O (in V)
+    auto P3 = [&](const uint32_t* XY) LCV_INLINE {
+        const MatImg<CT> i0 = load_img_lds<CT>(IMS, 2, lane), i1 = load_img_lds<CT>(IMS, 3, lane);
+        Operand<CT> din[2][2];
+        static_for<0, 2>([&](auto bb) LCV_INLINE {
+            constexpr int bi = decltype(bb)::value;
+            const int b = 2 * wave + bi;
+            static_for<0, 2>([&](auto kk) LCV_INLINE {
+                constexpr int kc = decltype(kk)::value;
+                din[bi][kc] = lds_operand<CT>(XY, [&](int j) { return xy_addr(16 * kc + 4 * g + j, b, c); });
+            });
+        });
+        Tile acc[2];
+        static_for<0, 2>([&](auto bb) LCV_INLINE {
+            constexpr int bi = decltype(bb)::value;
+            acc[bi].re = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc[bi].im = f32x4{0.f, 0.f, 0.f, 0.f};
+            stage_keep_acc<CT>(i0, din[bi][0], acc[bi].re, acc[bi].im);
+            stage_keep_acc<CT>(i1, din[bi][1], acc[bi].re, acc[bi].im);
+        });
+        static_for<0, 2>([&](auto bb) LCV_INLINE {
+            constexpr int bi = decltype(bb)::value;
+            const int b = 2 * wave + bi;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) V[(4 * g + j) * SV + 16 * b + c] = pack2<CT>(acc[bi].re[j], acc[bi].im[j]);
+        });
+    };
+    // P4: post-gate and store this lane's slot of the item
+    auto P4 = [&](int64_t item) LCV_INLINE {
+        int64_t o0, o1;
+        offsets(item, o0, o1);
+        const uint4* src = (const uint4*)(V + s_n1 * SV + s_col);
+        const uint4 w0 = src[0], w1 = src[1];
+        const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        float yr[8], yi[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            yr[i] = unpack_lo<CT>(w[i]);
+            yi[i] = unpack_hi<CT>(w[i]);
+        }
+        if constexpr (GV) {
+            float t[8];
+            unpack_raw<CT>(&rv[0], t);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) yr[i] *= t[i];
+            unpack_raw<CT>(&rv[1], t);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) yi[i] *= t[i];
+        }
+        store8<CT>(a.y, o0, yr);
+        store8<CT>(a.y, o1, yi);
+    };
+
+    // ---- pipeline ------------------------------------------------------------------------------
+    int64_t kf_h = channel(first);
+    int kb = 0;
+    load_kf(kf_h, 0);
+    issue_uq(first);
+    P0();
+    issue_uq(first + 1);
+    P1(XYb);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    for (int64_t k = first; k < last; ++k) {
+        const int xb = (int)((k - first) & 1);
+        uint32_t* const XYk = XYb + xb * XY_W;
+        uint32_t* const XYo = XYb + (1 - xb) * XY_W;
+        int kb_next = kb;
+#pragma unroll 1
+        for (int s = 0; s < 2; ++s) {
+            if ((s == 0) == (wave < 4)) {
+                P2(XYk, KFL + kb * (KF_W / 4));
+            } else {
+                if (k > first) {
+                    P3(XYo);
+                    P4(k - 1);
+                }
+                if (k + 1 < last) {
+                    const int64_t hn = channel(k + 1);
+                    if (hn != kf_h) {
+                        kb_next = 1 - kb;
+                        load_kf(hn, kb_next);
+                        kf_h = hn;
+                    }
+                }
+                issue_v(k);
+                if (k + 1 < last) {
+                    P0();
+                    issue_uq(k + 2);
+                    P1(XYo);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        kb = kb_next;
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    P3(XYb + ((last - 1 - first) & 1) * XY_W);
+    P4(last - 1);
+}
+
+// ------------------------------------------------------------------------------------------
 // launch
 // ------------------------------------------------------------------------------------------
 
@@ -840,8 +1190,27 @@ static hipError_t launch_t(const Fused1DArgs& a0, int cus, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int CT, bool GQ, bool GV>
+static hipError_t launch_8k(const Fused1DArgs& a0, int cus, hipStream_t st) {
+    Fused1DArgs a = a0;
+    if (a.nitems <= 0) return hipSuccess;
+    int64_t nwg = a.nitems < cus ? a.nitems : cus;
+    a.per_wg = (a.nitems + nwg - 1) / nwg;
+    nwg = (a.nitems + a.per_wg - 1) / a.per_wg;
+    hipLaunchKernelGGL((conv8k_kernel<CT, GQ, GV>), dim3((unsigned)nwg), dim3(512), 0, st, a);
+    return hipGetLastError();
+}
+
 template <int R, int T>
 static hipError_t launch_conv(bool gq, bool gv, const Fused1DArgs& a, int cus, hipStream_t st) {
+    if constexpr (R == 32 && T != CT_F32) {
+        if (a.N == 4096) {  // whole rows: the pipelined kernel
+            if (gq && gv) return launch_8k<T, true, true>(a, cus, st);
+            if (gq) return launch_8k<T, true, false>(a, cus, st);
+            if (gv) return launch_8k<T, false, true>(a, cus, st);
+            return launch_8k<T, false, false>(a, cus, st);
+        }
+    }
     if (gq && gv) return launch_t<R, T, T, MODE_CONV, true, true>(a, cus, st);
     if (gq) return launch_t<R, T, T, MODE_CONV, true, false>(a, cus, st);
     if (gv) return launch_t<R, T, T, MODE_CONV, false, true>(a, cus, st);
