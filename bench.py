@@ -25,6 +25,38 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # dense TFLOP/s
+METRIC = "fftconv GB/s, TFLOP/s, %roofline at B16\u00b7H768\u00b7N4096 bf16 causal, 1 GPU"
+# Hardware-counter summaries (rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by a plain copy, and the
+# matrix-core op count) per workload; they carry the hash of the kernel sources they were taken
+# on and are ignored once those sources change.
+COUNTER_FILES = {"hyena_gated_bf16_b16_h768_n4096": "profiles/conv8k_hyena_gated_bf16_b16_h768_n4096_counters.md"}
+KERNEL_SOURCES = ("fft_long_convolution_amd/csrc/fused1d.hip", "fft_long_convolution_amd/csrc/lconv_device.h")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_summary(workload):
+    """Key/value lines of the workload's counter summary, or {} when absent or stale."""
+    path = COUNTER_FILES.get(workload)
+    if not path or not os.path.exists(os.path.join(ROOT, path)):
+        return {}
+    import re
+    kv = {}
+    for line in open(os.path.join(ROOT, path)):
+        m = re.match(r"^([a-z0-9_]+): (\S+)\s*$", line)
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("source_sha256") != kernel_source_hash():
+        return {}
+    kv["path"] = path
+    return kv
 
 
 def algorithmic_bytes(spec):
@@ -167,19 +199,18 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # timed region: exactly K steps, events on the stream the kernels run on
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # Timed region: exactly K steps.  One event pair on the launch stream (torch's current
+    # stream, which the library is given) around the region times the kernels back to back.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record()
     for i in range(args.steps):
-        starts[i].record()
         step()
-        ends[i].record()
+    ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    avg_ms = float(np.mean(per))
+    avg_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
 
     nbytes = algorithmic_bytes(spec)
@@ -189,7 +220,7 @@ def main():
     achieved = nbytes / (avg_ms * 1e-3) / 1e9
 
     out = {
-        "metric": "fftconv GB/s (algorithmic bytes), causal long conv, 1 GPU",
+        "metric": METRIC,
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -215,6 +246,13 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "kernel_avg_us": round(avg_ms * 1e3, 3)},
     }
+    cs = counter_summary(spec.name)
+    if cs:
+        out["roofline"]["traffic"] = int(float(cs["traffic_bytes_per_launch"]))
+        # matrix-core GFLOP executed per launch (op counter x 512), over this run's kernel time
+        mf = float(cs["mfma_gflop_executed_per_launch"]) * 1e9 / (avg_ms * 1e-3) / 1e12
+        out["mfma"] = {"executed_tflops": round(mf, 1), "peak": MFMA_PEAK[dt],
+                       "util": round(mf / MFMA_PEAK[dt], 4), "counters": cs["path"]}
     if not args.no_cpu and spec.kind == "1d":
         out["cpu_baseline"] = cpu_baseline(d, args.cpu_budget)
     print(json.dumps(out), flush=True)
