@@ -241,7 +241,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
     constexpr int BPW = NBLK / 8;              // blocks per wave
     // The radix-R blocks (F1, I3) are shared by all waves: on the convolution path they live in
     // LDS (copied once), which keeps the per-tile blocks in registers without spills.
-    constexpr bool IMG_LDS = RES && MODE == MODE_CONV;
+    constexpr bool IMG_LDS = RES && (MODE == MODE_CONV || MODE == MODE_ROW);
     constexpr int IMGS_W = IMG_LDS ? (T_F2 - T_F1) / 4 : 0;
     constexpr int IOW = IO == CT_F32 ? 2 : 1;  // uint4 per 8 io elements
     // One sequence per iteration (R = 32) and 16-bit spectra: the filter spectrum of the
@@ -516,7 +516,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
         // products and all writes after them (a write to XY may not be reordered before a read
         // of V, so interleaving them would serialise the chunk on LDS latency).
         {
-            constexpr int CH1 = BPW < 2 ? BPW : 2;
+            constexpr int CH1 = (BPW < 2 || NIN > 16) ? 1 : 2;  // full-length input: one block at a time
             MatImg<CT> img1[RB1][KC1];
             static_for<0, RB1>([&](auto rr) LCV_INLINE {
                 static_for<0, KC1>([&](auto kk) LCV_INLINE {
@@ -697,7 +697,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
             // ================= P3: I3 (inverse radix R over k1, n1 < NOUT), XY -> O ============
             // Same chunked read / multiply / write order as P1.
             {
-                constexpr int CH3 = BPW < 2 ? BPW : 2;
+                constexpr int CH3 = (BPW < 2 || NOUT > 16) ? 1 : 2;
                 MatImg<CT> img3[RB3][KC3];
                 static_for<0, RB3>([&](auto rr) LCV_INLINE {
                     static_for<0, KC3>([&](auto kk) LCV_INLINE {

@@ -11,7 +11,13 @@
 // Pass B (fused1d.hip, row mode): DFT over n_lo, spectral product, inverse DFT over n_lo.
 // Pass C (here): inverse twiddle, inverse DFT over k_hi for n_hi < M1/2 only (the causal
 // truncation), gating, store.
-// The column DFTs are short (M1 = 2..512) and run as radix-2 butterflies in fp32 in LDS.
+//
+// A workgroup owns CB consecutive columns of one sequence (all M1 rows).  Global rows are read
+// and written 8 columns per 16-byte access; the column DFTs run in LDS (fp32 complex, one
+// column-major block) as self-sorting radix-8/4/2 passes (Stockham order: natural order out,
+// no bit reversal), each thread doing whole small DFTs in registers.  The n_lo-dependent
+// twiddle w_M^{n_lo k_hi} is formed once per 8 columns from the two-level table and advanced
+// by w_M^{k_hi} along them.
 #include "kernels.h"
 #include "lconv_device.h"
 
@@ -19,149 +25,338 @@ namespace lcv {
 
 namespace {
 
-constexpr int kColLds = 8192;  // complex fp32 elements of LDS per workgroup (64 KB)
 constexpr int64_t kM2 = 8192;
+constexpr int kThreads = 256;
+constexpr int kLdsBytes = 128 * 1024;   // column block: CB x M1 fp32 complex
 
-__device__ __forceinline__ int bitrev(int x, int bits) { return (int)(__brev((unsigned)x) >> (32 - bits)); }
-
-template <int IO>
-__device__ __forceinline__ float ld1(const void* p, int64_t i) {
-    if constexpr (IO == CT_F32) return ((const float*)p)[i];
-    else return unpack_lo<IO>(((const uint16_t*)p)[i]);
+__device__ __forceinline__ float2 cmulf(float2 a, float2 b) {
+    return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
 }
-template <int IO>
-__device__ __forceinline__ void st1(void* p, int64_t i, float x) {
-    if constexpr (IO == CT_F32) {
-        ((float*)p)[i] = x;
-    } else {
-        ((uint16_t*)p)[i] = (uint16_t)(pack2<IO>(x, 0.f) & 0xffffu);
-    }
-}
-// workspace complex element in compute type CT
-template <int CT>
-__device__ __forceinline__ float2 ws_ld(const void* p, int64_t i) {
-    if constexpr (CT == CT_F32) return ((const float2*)p)[i];
-    else {
-        uint32_t w = ((const uint32_t*)p)[i];
-        return make_float2(unpack_lo<CT>(w), unpack_hi<CT>(w));
-    }
-}
-template <int CT>
-__device__ __forceinline__ void ws_st(void* p, int64_t i, float2 v) {
-    if constexpr (CT == CT_F32) ((float2*)p)[i] = v;
-    else ((uint32_t*)p)[i] = pack2<CT>(v.x, v.y);
+__device__ __forceinline__ float2 cmulcf(float2 a, float2 b) {  // a * conj(b)
+    return make_float2(a.x * b.x + a.y * b.y, a.y * b.x - a.x * b.y);
 }
 
-// exp(-2 pi i r / M) from the two-level table
+// exp(-2 pi i r / M) from the two-level table (r reduced mod M by the caller)
 __device__ __forceinline__ float2 tw_m(const float* lo, const float* hi, int64_t r) {
     float2 a = ((const float2*)lo)[r & 2047];
     float2 b = ((const float2*)hi)[r >> 11];
-    return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+    return cmulf(a, b);
 }
 
-// In-place radix-2 DIT over rows of buf[M1][CB] (input already in bit-reversed row order).
-// sign = -1 forward, +1 inverse (conjugate twiddles).
-__device__ void col_fft(float2* buf, int M1, int CB, const float* tw_col, bool inverse) {
-    const int nb = M1 / 2 * CB;
-    for (int len = 2; len <= M1; len <<= 1) {
-        const int half = len / 2, step = M1 / len;
-        for (int idx = threadIdx.x; idx < nb; idx += blockDim.x) {
-            const int col = idx % CB, bf = idx / CB;
-            const int grp = bf / half, pos = bf % half;
-            const int i0 = grp * len + pos, i1 = i0 + half;
-            float2 w = ((const float2*)tw_col)[pos * step];
-            if (inverse) w.y = -w.y;
-            float2 x0 = buf[i0 * CB + col], x1 = buf[i1 * CB + col];
-            float2 t = make_float2(x1.x * w.x - x1.y * w.y, x1.x * w.y + x1.y * w.x);
-            buf[i0 * CB + col] = make_float2(x0.x + t.x, x0.y + t.y);
-            buf[i1 * CB + col] = make_float2(x0.x - t.x, x0.y - t.y);
+// In-register DFT of length RAD (2, 4 or 8); sign -1 forward, +1 inverse.
+template <int RAD, bool INV>
+__device__ __forceinline__ void dft_small(float2* v) {
+    auto bfly = [](float2& a, float2& b) LCV_INLINE {
+        const float2 t = b;
+        b = make_float2(a.x - t.x, a.y - t.y);
+        a = make_float2(a.x + t.x, a.y + t.y);
+    };
+    // multiply by -i (forward) or +i (inverse)
+    auto rot = [](float2 a) LCV_INLINE { return INV ? make_float2(-a.y, a.x) : make_float2(a.y, -a.x); };
+    if constexpr (RAD == 2) {
+        bfly(v[0], v[1]);
+    } else if constexpr (RAD == 4) {
+        bfly(v[0], v[2]);
+        bfly(v[1], v[3]);
+        v[3] = rot(v[3]);
+        bfly(v[0], v[1]);
+        bfly(v[2], v[3]);
+        const float2 t = v[1];  // outputs in order 0, 2, 1, 3 -> natural
+        v[1] = v[2];
+        v[2] = t;
+    } else {
+        // radix 8 = decimation in frequency: 4 butterflies (stride 4), twiddles w8^k, then two
+        // radix-4 DFTs on the even and odd halves
+        const float h = 0.70710678118654752f;
+        bfly(v[0], v[4]);
+        bfly(v[1], v[5]);
+        bfly(v[2], v[6]);
+        bfly(v[3], v[7]);
+        // v[4..7] *= w8^{0,1,2,3}  (w8 = exp(-+ 2 pi i / 8))
+        v[5] = INV ? make_float2(h * (v[5].x - v[5].y), h * (v[5].x + v[5].y))
+                   : make_float2(h * (v[5].x + v[5].y), h * (v[5].y - v[5].x));
+        v[6] = rot(v[6]);
+        v[7] = INV ? make_float2(-h * (v[7].x + v[7].y), h * (v[7].x - v[7].y))
+                   : make_float2(h * (v[7].y - v[7].x), -h * (v[7].x + v[7].y));
+        float2 e[4] = {v[0], v[1], v[2], v[3]}, o[4] = {v[4], v[5], v[6], v[7]};
+        dft_small<4, INV>(e);
+        dft_small<4, INV>(o);
+        // DIF: outputs 2k from the first half, 2k+1 from the second
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = e[k];
+            v[2 * k + 1] = o[k];
+        }
+    }
+}
+
+// One self-sorting pass of radix RAD over every column of buf (L rows, row stride ld).
+// Sub-transform length before the pass: ns.  FIRST: the second half of the input is zero.
+// The pass is in place: each round reads all items of a set of whole columns, waits, then
+// writes them (columns do not interact, so later rounds never read what earlier ones wrote).
+template <int RAD, bool INV, bool FIRST>
+__device__ __noinline__ void stockham_pass(float2* buf, int L, int ld, int CB, int ns, const float* tw_col, int m1) {
+    constexpr int MAXI = 2;                          // items per thread per round
+    const int groups = L / RAD;                      // <= 256
+    const int cbs = (kThreads * MAXI) / groups < CB ? (kThreads * MAXI) / groups : CB;  // columns per round
+    const int tstep0 = m1 / (ns * RAD);
+    for (int c0 = 0; c0 < CB; c0 += cbs) {
+        float2 v[MAXI][RAD];
+        int jj[MAXI], cc[MAXI];
+#pragma unroll
+        for (int t = 0; t < MAXI; ++t) {
+            const int it = t * kThreads + threadIdx.x;
+            jj[t] = -1;
+            cc[t] = 0;
+            if (it < cbs * groups) {
+                const int col = c0 + it % cbs, j = it / cbs;
+                jj[t] = j;
+                cc[t] = col;
+                // twiddle w_{ns RAD}^{k q} = w_L^{k q L / (ns RAD)}, from the M1-point table
+                const int tstep = tstep0 * (j % ns);
+#pragma unroll
+                for (int q = 0; q < RAD; ++q) {
+                    float2 x = make_float2(0.f, 0.f);
+                    if (!FIRST || q < RAD / 2) x = buf[(j + q * groups) * ld + col];
+                    if (q > 0 && ns > 1) {
+                        const float2 w = ((const float2*)tw_col)[(tstep * q) & (m1 - 1)];
+                        x = INV ? cmulcf(x, w) : cmulf(x, w);
+                    }
+                    v[t][q] = x;
+                }
+            }
         }
         __syncthreads();
+#pragma unroll
+        for (int t = 0; t < MAXI; ++t) {
+            if (jj[t] >= 0) {
+                dft_small<RAD, INV>(v[t]);
+                const int j = jj[t], k = j % ns, b0 = (j / ns) * ns * RAD + k;
+#pragma unroll
+                for (int q = 0; q < RAD; ++q) buf[(b0 + q * ns) * ld + cc[t]] = v[t][q];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Full column DFT of length L = M1 (power of two, 2..512) over the CB columns of buf.
+template <bool INV>
+__device__ void column_dft(float2* buf, int L, int ld, int CB, const float* tw_col, int m1) {
+    int ns = 1;
+    bool first = !INV;  // forward: the input's second half is zero
+    while (ns < L) {
+        const int rem = L / ns;
+        if (rem >= 8) {
+            if (first) stockham_pass<8, INV, true>(buf, L, ld, CB, ns, tw_col, m1);
+            else stockham_pass<8, INV, false>(buf, L, ld, CB, ns, tw_col, m1);
+            ns *= 8;
+        } else if (rem == 4) {
+            if (first) stockham_pass<4, INV, true>(buf, L, ld, CB, ns, tw_col, m1);
+            else stockham_pass<4, INV, false>(buf, L, ld, CB, ns, tw_col, m1);
+            ns *= 4;
+        } else {
+            if (first) stockham_pass<2, INV, true>(buf, L, ld, CB, ns, tw_col, m1);
+            else stockham_pass<2, INV, false>(buf, L, ld, CB, ns, tw_col, m1);
+            ns *= 2;
+        }
+        first = false;
+    }
+}
+
+// 8 consecutive io elements -> fp32 (raw 16-byte words for 16-bit types, 32 bytes for fp32)
+template <int IO>
+__device__ __forceinline__ void ld8(const void* p, int64_t i, float* x) {
+    if constexpr (IO == CT_F32) {
+        const float4 a = ((const float4*)((const float*)p + i))[0], b = ((const float4*)((const float*)p + i))[1];
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else {
+        const uint4 w = *(const uint4*)((const uint16_t*)p + i);
+        x[0] = unpack_lo<IO>(w.x); x[1] = unpack_hi<IO>(w.x); x[2] = unpack_lo<IO>(w.y); x[3] = unpack_hi<IO>(w.y);
+        x[4] = unpack_lo<IO>(w.z); x[5] = unpack_hi<IO>(w.z); x[6] = unpack_lo<IO>(w.w); x[7] = unpack_hi<IO>(w.w);
+    }
+}
+template <int IO>
+__device__ __forceinline__ void st8(void* p, int64_t i, const float* x) {
+    if constexpr (IO == CT_F32) {
+        ((float4*)((float*)p + i))[0] = make_float4(x[0], x[1], x[2], x[3]);
+        ((float4*)((float*)p + i))[1] = make_float4(x[4], x[5], x[6], x[7]);
+    } else {
+        uint4 w;
+        w.x = pack2<IO>(x[0], x[1]); w.y = pack2<IO>(x[2], x[3]);
+        w.z = pack2<IO>(x[4], x[5]); w.w = pack2<IO>(x[6], x[7]);
+        *(uint4*)((uint16_t*)p + i) = w;
+    }
+}
+// 8 consecutive workspace complex values (type CT) <-> fp32
+template <int CT>
+__device__ __forceinline__ void ws_ld8(const void* p, int64_t i, float2* z) {
+    if constexpr (CT == CT_F32) {
+        const float4* s = (const float4*)((const float2*)p + i);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float4 a = s[k];
+            z[2 * k] = make_float2(a.x, a.y);
+            z[2 * k + 1] = make_float2(a.z, a.w);
+        }
+    } else {
+        const uint4* s = (const uint4*)((const uint32_t*)p + i);
+        const uint4 a = s[0], b = s[1];
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) z[k] = make_float2(unpack_lo<CT>(w[k]), unpack_hi<CT>(w[k]));
+    }
+}
+template <int CT>
+__device__ __forceinline__ void ws_st8(void* p, int64_t i, const float2* z) {
+    if constexpr (CT == CT_F32) {
+        float4* d = (float4*)((float2*)p + i);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) d[k] = make_float4(z[2 * k].x, z[2 * k].y, z[2 * k + 1].x, z[2 * k + 1].y);
+    } else {
+        uint4 a, b;
+        a.x = pack2<CT>(z[0].x, z[0].y); a.y = pack2<CT>(z[1].x, z[1].y);
+        a.z = pack2<CT>(z[2].x, z[2].y); a.w = pack2<CT>(z[3].x, z[3].y);
+        b.x = pack2<CT>(z[4].x, z[4].y); b.y = pack2<CT>(z[5].x, z[5].y);
+        b.z = pack2<CT>(z[6].x, z[6].y); b.w = pack2<CT>(z[7].x, z[7].y);
+        uint4* d = (uint4*)((uint32_t*)p + i);
+        d[0] = a;
+        d[1] = b;
+    }
+}
+
+__host__ __device__ constexpr int cols_per_wg(int M1) {
+    return kLdsBytes / (8 * M1) < 256 ? kLdsBytes / (8 * M1) : 256;
+}
+
+// (sequence -> rows) of the chunk's sequence gs
+__device__ __forceinline__ void seq_rows(const ColArgs& a, int64_t gs, int64_t& row0, int64_t& row1) {
+    if (a.filter) {
+        row0 = gs * a.N;
+        row1 = -1;
+    } else {
+        const int64_t h = gs / a.seq_per_h, b = 2 * (gs % a.seq_per_h);
+        row0 = (b * a.H + h) * a.N;
+        row1 = b + 1 < a.B ? row0 + a.H * a.N : -1;
     }
 }
 
 }  // namespace
 
 template <int CT, int IO>
-__global__ void __launch_bounds__(256) col_fwd_kernel(const ColArgs a) {
-    __shared__ float2 buf[kColLds];
-    const int M1 = (int)a.M1, CB = kColLds / M1 < 256 ? kColLds / M1 : 256;
-    const int bits = 31 - __clz(M1);
-    const int64_t s = blockIdx.y;               // sequence within the chunk
-    const int64_t gs = a.seq0 + s;              // global sequence
+__global__ void __launch_bounds__(kThreads) col_fwd_kernel(const ColArgs a) {
+    extern __shared__ float2 buf[];
+    const int M1 = (int)a.M1, CB = cols_per_wg(M1), ld = CB;
+    const int64_t s = blockIdx.y, gs = a.seq0 + s;
     const int64_t n_lo0 = (int64_t)blockIdx.x * CB;
-    int64_t row0 = 0, row1 = -1;
-    if (a.filter) {
-        row0 = gs * a.N;                         // k[h]
-    } else {
-        const int64_t h = gs / a.seq_per_h, b = 2 * (gs % a.seq_per_h);
-        row0 = (b * a.H + h) * a.N;
-        if (b + 1 < a.B) row1 = row0 + a.H * a.N;
-    }
-    // load the nonzero half (n_hi < M1/2) into bit-reversed rows, zero the rest
-    for (int idx = threadIdx.x; idx < M1 * CB; idx += blockDim.x) {
-        const int col = idx % CB, nh = idx / CB;
-        float2 z = make_float2(0.f, 0.f);
-        const int64_t n = kM2 * nh + n_lo0 + col;
-        if (nh < M1 / 2 && n < a.N) {
-            float xr = ld1<IO>(a.u, row0 + n);
-            if (a.q) xr *= ld1<IO>(a.q, row0 + n);
-            float xi = 0.f;
-            if (row1 >= 0) {
-                xi = ld1<IO>(a.u, row1 + n);
-                if (a.q) xi *= ld1<IO>(a.q, row1 + n);
+    int64_t row0, row1;
+    seq_rows(a, gs, row0, row1);
+    const int g8 = CB / 8;  // 8-column groups per row
+    // load rows n_hi < M1/2 (zero past N), gated, as complex pairs (row b, row b+1)
+    for (int it = threadIdx.x; it < (M1 / 2) * g8; it += kThreads) {
+        const int nh = it / g8, cg = it % g8;
+        const int64_t n = kM2 * nh + n_lo0 + 8 * cg;
+        float xr[8], xi[8];
+        if (n < a.N) {  // N is a multiple of 8: a group is all in or all out
+            ld8<IO>(a.u, row0 + n, xr);
+            if (a.q) {
+                float t[8];
+                ld8<IO>(a.q, row0 + n, t);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) xr[k] *= t[k];
             }
-            z = make_float2(xr, xi);
+            if (row1 >= 0) {
+                ld8<IO>(a.u, row1 + n, xi);
+                if (a.q) {
+                    float t[8];
+                    ld8<IO>(a.q, row1 + n, t);
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) xi[k] *= t[k];
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) xi[k] = 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) xr[k] = xi[k] = 0.f;
         }
-        buf[bitrev(nh, bits) * CB + col] = z;
+        float2* d = buf + nh * ld + 8 * cg;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) d[k] = make_float2(xr[k], xi[k]);
     }
     __syncthreads();
-    col_fft(buf, M1, CB, a.tw_col, false);
-    // twiddle w_M^{n_lo k_hi}, store [k_hi][n_lo]
-    for (int idx = threadIdx.x; idx < M1 * CB; idx += blockDim.x) {
-        const int col = idx % CB, kh = idx / CB;
-        const int64_t n_lo = n_lo0 + col;
-        const int64_t r = (n_lo * kh) & (a.M - 1);
-        float2 w = tw_m(a.tw_lo, a.tw_hi, r);
-        float2 x = buf[kh * CB + col];
-        float2 o = make_float2(x.x * w.x - x.y * w.y, x.x * w.y + x.y * w.x);
-        ws_st<CT>(a.ws, (s * a.M1 + kh) * kM2 + n_lo, o);
+    column_dft<false>(buf, M1, ld, CB, a.tw_col, M1);
+    // twiddle w_M^{n_lo k_hi} and store row k_hi, 8 columns per thread
+    for (int it = threadIdx.x; it < M1 * g8; it += kThreads) {
+        const int kh = it / g8, cg = it % g8;
+        const int64_t n_lo = n_lo0 + 8 * cg;
+        float2 w = tw_m(a.tw_lo, a.tw_hi, (n_lo * kh) & (a.M - 1));
+        const float2 step = ((const float2*)a.tw_lo)[kh];  // kh < 2048
+        float2 z[8];
+        const float2* src = buf + kh * ld + 8 * cg;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            z[k] = cmulf(src[k], w);
+            w = cmulf(w, step);
+        }
+        ws_st8<CT>(a.ws, (s * a.M1 + kh) * kM2 + n_lo, z);
     }
 }
 
 template <int CT, int IO>
-__global__ void __launch_bounds__(256) col_inv_kernel(const ColArgs a) {
-    __shared__ float2 buf[kColLds];
-    const int M1 = (int)a.M1, CB = kColLds / M1 < 256 ? kColLds / M1 : 256;
-    const int bits = 31 - __clz(M1);
-    const int64_t s = blockIdx.y;
-    const int64_t gs = a.seq0 + s;
+__global__ void __launch_bounds__(kThreads) col_inv_kernel(const ColArgs a) {
+    extern __shared__ float2 buf[];
+    const int M1 = (int)a.M1, CB = cols_per_wg(M1), ld = CB;
+    const int64_t s = blockIdx.y, gs = a.seq0 + s;
     const int64_t n_lo0 = (int64_t)blockIdx.x * CB;
-    const int64_t h = gs / a.seq_per_h, b = 2 * (gs % a.seq_per_h);
-    const int64_t row0 = (b * a.H + h) * a.N;
-    const int64_t row1 = b + 1 < a.B ? row0 + a.H * a.N : -1;
-    // load [k_hi][n_lo], inverse twiddle, bit-reversed rows
-    for (int idx = threadIdx.x; idx < M1 * CB; idx += blockDim.x) {
-        const int col = idx % CB, kh = idx / CB;
-        const int64_t n_lo = n_lo0 + col;
-        const int64_t r = (n_lo * kh) & (a.M - 1);
-        float2 w = tw_m(a.tw_lo, a.tw_hi, r);
-        float2 x = ws_ld<CT>(a.ws, (s * a.M1 + kh) * kM2 + n_lo);
-        buf[bitrev(kh, bits) * CB + col] = make_float2(x.x * w.x + x.y * w.y, x.y * w.x - x.x * w.y);
+    int64_t row0, row1;
+    seq_rows(a, gs, row0, row1);
+    const int g8 = CB / 8;
+    // load rows k_hi, inverse twiddle conj(w_M^{n_lo k_hi})
+    for (int it = threadIdx.x; it < M1 * g8; it += kThreads) {
+        const int kh = it / g8, cg = it % g8;
+        const int64_t n_lo = n_lo0 + 8 * cg;
+        float2 w = tw_m(a.tw_lo, a.tw_hi, (n_lo * kh) & (a.M - 1));
+        const float2 step = ((const float2*)a.tw_lo)[kh];
+        float2 z[8];
+        ws_ld8<CT>(a.ws, (s * a.M1 + kh) * kM2 + n_lo, z);
+        float2* d = buf + kh * ld + 8 * cg;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            d[k] = cmulcf(z[k], w);
+            w = cmulf(w, step);
+        }
     }
     __syncthreads();
-    col_fft(buf, M1, CB, a.tw_col, true);
-    for (int idx = threadIdx.x; idx < M1 / 2 * CB; idx += blockDim.x) {
-        const int col = idx % CB, nh = idx / CB;
-        const int64_t n = kM2 * nh + n_lo0 + col;
+    column_dft<true>(buf, M1, ld, CB, a.tw_col, M1);
+    // rows n_hi < M1/2 (and n < N): gate and store
+    for (int it = threadIdx.x; it < (M1 / 2) * g8; it += kThreads) {
+        const int nh = it / g8, cg = it % g8;
+        const int64_t n = kM2 * nh + n_lo0 + 8 * cg;
         if (n >= a.N) continue;
-        float2 z = buf[nh * CB + col];
-        float yr = z.x, yi = z.y;
-        if (a.v) yr *= ld1<IO>(a.v, row0 + n);
-        st1<IO>(a.y, row0 + n, yr);
+        const float2* src = buf + nh * ld + 8 * cg;
+        float yr[8], yi[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            yr[k] = src[k].x;
+            yi[k] = src[k].y;
+        }
+        if (a.v) {
+            float t[8];
+            ld8<IO>(a.v, row0 + n, t);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) yr[k] *= t[k];
+        }
+        st8<IO>(a.y, row0 + n, yr);
         if (row1 >= 0) {
-            if (a.v) yi *= ld1<IO>(a.v, row1 + n);
-            st1<IO>(a.y, row1 + n, yi);
+            if (a.v) {
+                float t[8];
+                ld8<IO>(a.v, row1 + n, t);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) yi[k] *= t[k];
+            }
+            st8<IO>(a.y, row1 + n, yi);
         }
     }
 }
@@ -169,10 +364,23 @@ __global__ void __launch_bounds__(256) col_inv_kernel(const ColArgs a) {
 template <int CT, int IO>
 static hipError_t launch_cols(bool fwd, const ColArgs& a, hipStream_t st) {
     if (a.nseq <= 0) return hipSuccess;
-    const int CB = kColLds / (int)a.M1 < 256 ? kColLds / (int)a.M1 : 256;
+    const int M1 = (int)a.M1;
+    if (M1 < 2 || M1 > 512 || (M1 & (M1 - 1))) return hipErrorInvalidValue;
+    const int CB = cols_per_wg(M1);
+    const size_t lds = (size_t)CB * M1 * sizeof(float2);
     dim3 grid((unsigned)(kM2 / CB), (unsigned)a.nseq);
-    if (fwd) hipLaunchKernelGGL((col_fwd_kernel<CT, IO>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((col_inv_kernel<CT, IO>), grid, dim3(256), 0, st, a);
+    // dynamic LDS above the default limit has to be allowed per kernel
+    static bool attr_set[2] = {false, false};
+    auto kfwd = col_fwd_kernel<CT, IO>;
+    auto kinv = col_inv_kernel<CT, IO>;
+    if (!attr_set[fwd ? 0 : 1]) {
+        hipError_t e = hipFuncSetAttribute(fwd ? (const void*)kfwd : (const void*)kinv,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        if (e != hipSuccess) return e;
+        attr_set[fwd ? 0 : 1] = true;
+    }
+    if (fwd) hipLaunchKernelGGL(kfwd, grid, dim3(kThreads), lds, st, a);
+    else hipLaunchKernelGGL(kinv, grid, dim3(kThreads), lds, st, a);
     return hipGetLastError();
 }
 
