@@ -26,7 +26,6 @@ namespace lcv {
 namespace {
 
 constexpr int64_t kM2 = 8192;
-constexpr int kThreads = 256;
 constexpr int kLdsBytes = 128 * 1024;   // column block: CB x M1 fp32 complex
 
 __device__ __forceinline__ float2 cmulf(float2 a, float2 b) {
@@ -94,7 +93,7 @@ __device__ __forceinline__ void dft_small(float2* v) {
 // Sub-transform length before the pass: ns.  FIRST: the second half of the input is zero.
 // The pass is in place: each round reads all items of a set of whole columns, waits, then
 // writes them (columns do not interact, so later rounds never read what earlier ones wrote).
-template <int RAD, bool INV, bool FIRST>
+template <int kThreads, int RAD, bool INV, bool FIRST>
 __device__ __noinline__ void stockham_pass(float2* buf, int L, int ld, int CB, int ns, const float* tw_col, int m1) {
     constexpr int MAXI = 2;                          // items per thread per round
     const int groups = L / RAD;                      // <= 256
@@ -141,23 +140,23 @@ __device__ __noinline__ void stockham_pass(float2* buf, int L, int ld, int CB, i
 }
 
 // Full column DFT of length L = M1 (power of two, 2..512) over the CB columns of buf.
-template <bool INV>
+template <int kThreads, bool INV>
 __device__ void column_dft(float2* buf, int L, int ld, int CB, const float* tw_col, int m1) {
     int ns = 1;
     bool first = !INV;  // forward: the input's second half is zero
     while (ns < L) {
         const int rem = L / ns;
         if (rem >= 8) {
-            if (first) stockham_pass<8, INV, true>(buf, L, ld, CB, ns, tw_col, m1);
-            else stockham_pass<8, INV, false>(buf, L, ld, CB, ns, tw_col, m1);
+            if (first) stockham_pass<kThreads, 8, INV, true>(buf, L, ld, CB, ns, tw_col, m1);
+            else stockham_pass<kThreads, 8, INV, false>(buf, L, ld, CB, ns, tw_col, m1);
             ns *= 8;
         } else if (rem == 4) {
-            if (first) stockham_pass<4, INV, true>(buf, L, ld, CB, ns, tw_col, m1);
-            else stockham_pass<4, INV, false>(buf, L, ld, CB, ns, tw_col, m1);
+            if (first) stockham_pass<kThreads, 4, INV, true>(buf, L, ld, CB, ns, tw_col, m1);
+            else stockham_pass<kThreads, 4, INV, false>(buf, L, ld, CB, ns, tw_col, m1);
             ns *= 4;
         } else {
-            if (first) stockham_pass<2, INV, true>(buf, L, ld, CB, ns, tw_col, m1);
-            else stockham_pass<2, INV, false>(buf, L, ld, CB, ns, tw_col, m1);
+            if (first) stockham_pass<kThreads, 2, INV, true>(buf, L, ld, CB, ns, tw_col, m1);
+            else stockham_pass<kThreads, 2, INV, false>(buf, L, ld, CB, ns, tw_col, m1);
             ns *= 2;
         }
         first = false;
@@ -243,7 +242,7 @@ __device__ __forceinline__ void seq_rows(const ColArgs& a, int64_t gs, int64_t& 
 
 }  // namespace
 
-template <int CT, int IO>
+template <int CT, int IO, int kThreads>
 __global__ void __launch_bounds__(kThreads) col_fwd_kernel(const ColArgs a) {
     extern __shared__ float2 buf[];
     const int M1 = (int)a.M1, CB = cols_per_wg(M1), ld = CB;
@@ -286,7 +285,7 @@ __global__ void __launch_bounds__(kThreads) col_fwd_kernel(const ColArgs a) {
         for (int k = 0; k < 8; ++k) d[k] = make_float2(xr[k], xi[k]);
     }
     __syncthreads();
-    column_dft<false>(buf, M1, ld, CB, a.tw_col, M1);
+    column_dft<kThreads, false>(buf, M1, ld, CB, a.tw_col, M1);
     // twiddle w_M^{n_lo k_hi} and store row k_hi, 8 columns per thread
     for (int it = threadIdx.x; it < M1 * g8; it += kThreads) {
         const int kh = it / g8, cg = it % g8;
@@ -304,7 +303,7 @@ __global__ void __launch_bounds__(kThreads) col_fwd_kernel(const ColArgs a) {
     }
 }
 
-template <int CT, int IO>
+template <int CT, int IO, int kThreads>
 __global__ void __launch_bounds__(kThreads) col_inv_kernel(const ColArgs a) {
     extern __shared__ float2 buf[];
     const int M1 = (int)a.M1, CB = cols_per_wg(M1), ld = CB;
@@ -329,7 +328,7 @@ __global__ void __launch_bounds__(kThreads) col_inv_kernel(const ColArgs a) {
         }
     }
     __syncthreads();
-    column_dft<true>(buf, M1, ld, CB, a.tw_col, M1);
+    column_dft<kThreads, true>(buf, M1, ld, CB, a.tw_col, M1);
     // rows n_hi < M1/2 (and n < N): gate and store
     for (int it = threadIdx.x; it < (M1 / 2) * g8; it += kThreads) {
         const int nh = it / g8, cg = it % g8;
@@ -361,27 +360,34 @@ __global__ void __launch_bounds__(kThreads) col_inv_kernel(const ColArgs a) {
     }
 }
 
-template <int CT, int IO>
-static hipError_t launch_cols(bool fwd, const ColArgs& a, hipStream_t st) {
-    if (a.nseq <= 0) return hipSuccess;
+template <int CT, int IO, int TPB>
+static hipError_t launch_cols_t(bool fwd, const ColArgs& a, hipStream_t st) {
     const int M1 = (int)a.M1;
-    if (M1 < 2 || M1 > 512 || (M1 & (M1 - 1))) return hipErrorInvalidValue;
     const int CB = cols_per_wg(M1);
     const size_t lds = (size_t)CB * M1 * sizeof(float2);
     dim3 grid((unsigned)(kM2 / CB), (unsigned)a.nseq);
     // dynamic LDS above the default limit has to be allowed per kernel
     static bool attr_set[2] = {false, false};
-    auto kfwd = col_fwd_kernel<CT, IO>;
-    auto kinv = col_inv_kernel<CT, IO>;
+    auto kfwd = col_fwd_kernel<CT, IO, TPB>;
+    auto kinv = col_inv_kernel<CT, IO, TPB>;
     if (!attr_set[fwd ? 0 : 1]) {
         hipError_t e = hipFuncSetAttribute(fwd ? (const void*)kfwd : (const void*)kinv,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
         if (e != hipSuccess) return e;
         attr_set[fwd ? 0 : 1] = true;
     }
-    if (fwd) hipLaunchKernelGGL(kfwd, grid, dim3(kThreads), lds, st, a);
-    else hipLaunchKernelGGL(kinv, grid, dim3(kThreads), lds, st, a);
+    if (fwd) hipLaunchKernelGGL(kfwd, grid, dim3(TPB), lds, st, a);
+    else hipLaunchKernelGGL(kinv, grid, dim3(TPB), lds, st, a);
     return hipGetLastError();
+}
+
+template <int CT, int IO>
+static hipError_t launch_cols(bool fwd, const ColArgs& a, hipStream_t st) {
+    if (a.nseq <= 0) return hipSuccess;
+    const int M1 = (int)a.M1;
+    if (M1 < 2 || M1 > 512 || (M1 & (M1 - 1))) return hipErrorInvalidValue;
+    // short columns: many small blocks per CU; long columns (one 128 KB block per CU): 8 waves
+    return M1 <= 64 ? launch_cols_t<CT, IO, 256>(fwd, a, st) : launch_cols_t<CT, IO, 512>(fwd, a, st);
 }
 
 // dtype: io type.  The workspace holds the compute type: fp32 for fp32 io and for filters,
