@@ -42,7 +42,7 @@ __device__ __forceinline__ float2 tw_m(const float* lo, const float* hi, int64_t
     return cmulf(a, b);
 }
 
-// In-register DFT of length RAD (2, 4 or 8); sign -1 forward, +1 inverse.
+// In-register DFT of length RAD (1, 2, 4 or 8); sign -1 forward, +1 inverse.
 template <int RAD, bool INV>
 __device__ __forceinline__ void dft_small(float2* v) {
     auto bfly = [](float2& a, float2& b) LCV_INLINE {
@@ -52,7 +52,8 @@ __device__ __forceinline__ void dft_small(float2* v) {
     };
     // multiply by -i (forward) or +i (inverse)
     auto rot = [](float2 a) LCV_INLINE { return INV ? make_float2(-a.y, a.x) : make_float2(a.y, -a.x); };
-    if constexpr (RAD == 2) {
+    if constexpr (RAD == 1) {
+    } else if constexpr (RAD == 2) {
         bfly(v[0], v[1]);
     } else if constexpr (RAD == 4) {
         bfly(v[0], v[2]);
@@ -360,6 +361,164 @@ __global__ void __launch_bounds__(kThreads) col_inv_kernel(const ColArgs a) {
     }
 }
 
+
+// ---- short columns (M1 <= 16): one column per thread, DFT in registers ----------------------
+// Forward, H = M1/2 nonzero inputs: X[2m + e] = DFT_H( x[n] w_M1^{n e} )[m], e = 0, 1.
+// Inverse, outputs n < H only:  y[n] = E[n] + w_M1^{-n} O[n] with E, O the inverse DFT_H of the
+// even and odd inputs.  Rows pass through LDS so global rows are read and written 8 columns per
+// 16-byte access; each thread then owns one of the 256 columns of the block.
+template <int CT, int IO, int M1>
+__global__ void __launch_bounds__(256) col_small_fwd_kernel(const ColArgs a) {
+    constexpr int H = M1 / 2, CB = 256, LDW = CB + 1;
+    __shared__ float2 sin_[H * LDW];
+    __shared__ float2 sout[M1 * LDW];
+    const int64_t s = blockIdx.y, gs = a.seq0 + s;
+    const int64_t n_lo0 = (int64_t)blockIdx.x * CB;
+    int64_t row0, row1;
+    seq_rows(a, gs, row0, row1);
+    constexpr int g8 = CB / 8;
+    for (int it = threadIdx.x; it < H * g8; it += 256) {
+        const int nh = it / g8, cg = it % g8;
+        const int64_t n = kM2 * nh + n_lo0 + 8 * cg;
+        float xr[8], xi[8];
+        if (n < a.N) {
+            ld8<IO>(a.u, row0 + n, xr);
+            if (a.q) {
+                float t[8];
+                ld8<IO>(a.q, row0 + n, t);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) xr[k] *= t[k];
+            }
+            if (row1 >= 0) {
+                ld8<IO>(a.u, row1 + n, xi);
+                if (a.q) {
+                    float t[8];
+                    ld8<IO>(a.q, row1 + n, t);
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) xi[k] *= t[k];
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) xi[k] = 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) xr[k] = xi[k] = 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sin_[nh * LDW + 8 * cg + k] = make_float2(xr[k], xi[k]);
+    }
+    __syncthreads();
+    {
+        const int t = threadIdx.x;
+        float2 ev[H], od[H];
+#pragma unroll
+        for (int n = 0; n < H; ++n) {
+            const float2 x = sin_[n * LDW + t];
+            ev[n] = x;
+            od[n] = n == 0 ? x : cmulf(x, ((const float2*)a.tw_col)[n]);  // w_M1^n
+        }
+        dft_small<H, false>(ev);
+        dft_small<H, false>(od);
+        // four-step twiddle w_M^{n_lo k}, k = 0 .. M1-1, as powers of w_M^{n_lo}
+        const int64_t n_lo = n_lo0 + t;
+        const float2 w1 = tw_m(a.tw_lo, a.tw_hi, n_lo & (a.M - 1));
+        float2 w = make_float2(1.f, 0.f);
+#pragma unroll
+        for (int k = 0; k < M1; ++k) {
+            const float2 x = (k & 1) ? od[k >> 1] : ev[k >> 1];
+            sout[k * LDW + t] = cmulf(x, w);
+            w = cmulf(w, w1);
+        }
+    }
+    __syncthreads();
+    for (int it = threadIdx.x; it < M1 * g8; it += 256) {
+        const int kh = it / g8, cg = it % g8;
+        float2 z[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) z[k] = sout[kh * LDW + 8 * cg + k];
+        ws_st8<CT>(a.ws, (s * a.M1 + kh) * kM2 + n_lo0 + 8 * cg, z);
+    }
+}
+
+template <int CT, int IO, int M1>
+__global__ void __launch_bounds__(256) col_small_inv_kernel(const ColArgs a) {
+    constexpr int H = M1 / 2, CB = 256, LDW = CB + 1;
+    __shared__ float2 sin_[M1 * LDW];
+    __shared__ float2 sout[H * LDW];
+    const int64_t s = blockIdx.y, gs = a.seq0 + s;
+    const int64_t n_lo0 = (int64_t)blockIdx.x * CB;
+    int64_t row0, row1;
+    seq_rows(a, gs, row0, row1);
+    constexpr int g8 = CB / 8;
+    for (int it = threadIdx.x; it < M1 * g8; it += 256) {
+        const int kh = it / g8, cg = it % g8;
+        float2 z[8];
+        ws_ld8<CT>(a.ws, (s * a.M1 + kh) * kM2 + n_lo0 + 8 * cg, z);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sin_[kh * LDW + 8 * cg + k] = z[k];
+    }
+    __syncthreads();
+    {
+        const int t = threadIdx.x;
+        const int64_t n_lo = n_lo0 + t;
+        const float2 w1 = tw_m(a.tw_lo, a.tw_hi, n_lo & (a.M - 1));
+        float2 w = make_float2(1.f, 0.f);
+        float2 ev[H], od[H];
+#pragma unroll
+        for (int k = 0; k < M1; ++k) {
+            const float2 z = cmulcf(sin_[k * LDW + t], w);  // inverse four-step twiddle
+            if (k & 1) od[k >> 1] = z;
+            else ev[k >> 1] = z;
+            w = cmulf(w, w1);
+        }
+        dft_small<H, true>(ev);
+        dft_small<H, true>(od);
+#pragma unroll
+        for (int n = 0; n < H; ++n) {
+            const float2 o = n == 0 ? od[0] : cmulcf(od[n], ((const float2*)a.tw_col)[n]);  // w_M1^{-n}
+            sout[n * LDW + t] = make_float2(ev[n].x + o.x, ev[n].y + o.y);
+        }
+    }
+    __syncthreads();
+    for (int it = threadIdx.x; it < H * g8; it += 256) {
+        const int nh = it / g8, cg = it % g8;
+        const int64_t n = kM2 * nh + n_lo0 + 8 * cg;
+        if (n >= a.N) continue;
+        float yr[8], yi[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float2 z = sout[nh * LDW + 8 * cg + k];
+            yr[k] = z.x;
+            yi[k] = z.y;
+        }
+        if (a.v) {
+            float t[8];
+            ld8<IO>(a.v, row0 + n, t);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) yr[k] *= t[k];
+        }
+        st8<IO>(a.y, row0 + n, yr);
+        if (row1 >= 0) {
+            if (a.v) {
+                float t[8];
+                ld8<IO>(a.v, row1 + n, t);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) yi[k] *= t[k];
+            }
+            st8<IO>(a.y, row1 + n, yi);
+        }
+    }
+}
+
+template <int CT, int IO, int M1>
+static hipError_t launch_small_t(bool fwd, const ColArgs& a, hipStream_t st) {
+    dim3 grid((unsigned)(kM2 / 256), (unsigned)a.nseq);
+    if (fwd) hipLaunchKernelGGL((col_small_fwd_kernel<CT, IO, M1>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((col_small_inv_kernel<CT, IO, M1>), grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
 template <int CT, int IO, int TPB>
 static hipError_t launch_cols_t(bool fwd, const ColArgs& a, hipStream_t st) {
     const int M1 = (int)a.M1;
@@ -386,7 +545,14 @@ static hipError_t launch_cols(bool fwd, const ColArgs& a, hipStream_t st) {
     if (a.nseq <= 0) return hipSuccess;
     const int M1 = (int)a.M1;
     if (M1 < 2 || M1 > 512 || (M1 & (M1 - 1))) return hipErrorInvalidValue;
-    // short columns: many small blocks per CU; long columns (one 128 KB block per CU): 8 waves
+    switch (M1) {  // one column per thread, DFT in registers
+    case 2: return launch_small_t<CT, IO, 2>(fwd, a, st);
+    case 4: return launch_small_t<CT, IO, 4>(fwd, a, st);
+    case 8: return launch_small_t<CT, IO, 8>(fwd, a, st);
+    case 16: return launch_small_t<CT, IO, 16>(fwd, a, st);
+    default: break;
+    }
+    // LDS passes: many small blocks per CU for short columns; 8 waves for one 128 KB block
     return M1 <= 64 ? launch_cols_t<CT, IO, 256>(fwd, a, st) : launch_cols_t<CT, IO, 512>(fwd, a, st);
 }
 
