@@ -26,7 +26,7 @@ namespace lcv {
 namespace {
 
 constexpr int64_t kM2 = 8192;
-constexpr int kLdsBytes = 128 * 1024;   // column block: CB x M1 fp32 complex
+constexpr int kLdsBytes = 128 * 1024;   // column block: CB x M1 fp32 complex (plus one pad row)
 
 __device__ __forceinline__ float2 cmulf(float2 a, float2 b) {
     return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
@@ -90,78 +90,63 @@ __device__ __forceinline__ void dft_small(float2* v) {
     }
 }
 
-// One self-sorting pass of radix RAD over every column of buf (L rows, row stride ld).
-// Sub-transform length before the pass: ns.  FIRST: the second half of the input is zero.
-// The pass is in place: each round reads all items of a set of whole columns, waits, then
-// writes them (columns do not interact, so later rounds never read what earlier ones wrote).
-template <int kThreads, int RAD, bool INV, bool FIRST>
-__device__ __noinline__ void stockham_pass(float2* buf, int L, int ld, int CB, int ns, const float* tw_col, int m1) {
-    constexpr int MAXI = 2;                          // items per thread per round
-    const int groups = L / RAD;                      // <= 256
-    const int cbs = (kThreads * MAXI) / groups < CB ? (kThreads * MAXI) / groups : CB;  // columns per round
-    const int tstep0 = m1 / (ns * RAD);
-    for (int c0 = 0; c0 < CB; c0 += cbs) {
-        float2 v[MAXI][RAD];
-        int jj[MAXI], cc[MAXI];
+// One self-sorting pass of radix RAD over the columns of buf (column-major, column stride ld) that
+// belong to this wave (column c0 + wave + nw * i).  Sub-transform length before the pass: ns.
+// FIRST: the second half of the input is zero.  A column's L / RAD butterfly groups (at most
+// 64) are spread over the lanes, several columns per wave round when there are fewer groups
+// than lanes.  The pass is in place: a round's LDS reads all precede its writes in the wave's
+// own instruction order, and columns do not interact, so no barrier is needed.
+template <int RAD, bool INV, bool FIRST>
+__device__ __forceinline__ void stockham_pass_wave(float2* buf, int L, int ld, int CB, int ns,
+                                                   const float* tw_col, int m1, int wave, int nw, int lane) {
+    const int groups = L / RAD;                     // 1 .. 64
+    const int cpr = 64 / groups;                    // columns per wave round
+    const int sub = lane / groups, j = lane % groups;
+    const int k = j % ns, tstep = (m1 / (ns * RAD)) * k;
+    const int b0 = (j / ns) * ns * RAD + k;
+    for (int c = wave * cpr + sub; c < CB; c += nw * cpr) {
+        float2 v[RAD];
 #pragma unroll
-        for (int t = 0; t < MAXI; ++t) {
-            const int it = t * kThreads + threadIdx.x;
-            jj[t] = -1;
-            cc[t] = 0;
-            if (it < cbs * groups) {
-                const int col = c0 + it % cbs, j = it / cbs;
-                jj[t] = j;
-                cc[t] = col;
-                // twiddle w_{ns RAD}^{k q} = w_L^{k q L / (ns RAD)}, from the M1-point table
-                const int tstep = tstep0 * (j % ns);
-#pragma unroll
-                for (int q = 0; q < RAD; ++q) {
-                    float2 x = make_float2(0.f, 0.f);
-                    if (!FIRST || q < RAD / 2) x = buf[(j + q * groups) * ld + col];
-                    if (q > 0 && ns > 1) {
-                        const float2 w = ((const float2*)tw_col)[(tstep * q) & (m1 - 1)];
-                        x = INV ? cmulcf(x, w) : cmulf(x, w);
-                    }
-                    v[t][q] = x;
-                }
+        for (int q = 0; q < RAD; ++q) {
+            float2 x = make_float2(0.f, 0.f);
+            if (!FIRST || q < RAD / 2) x = buf[c * ld + j + q * groups];
+            if (q > 0 && ns > 1) {
+                const float2 w = ((const float2*)tw_col)[(tstep * q) & (m1 - 1)];
+                x = INV ? cmulcf(x, w) : cmulf(x, w);
             }
+            v[q] = x;
         }
-        __syncthreads();
+        dft_small<RAD, INV>(v);
 #pragma unroll
-        for (int t = 0; t < MAXI; ++t) {
-            if (jj[t] >= 0) {
-                dft_small<RAD, INV>(v[t]);
-                const int j = jj[t], k = j % ns, b0 = (j / ns) * ns * RAD + k;
-#pragma unroll
-                for (int q = 0; q < RAD; ++q) buf[(b0 + q * ns) * ld + cc[t]] = v[t][q];
-            }
-        }
-        __syncthreads();
+        for (int q = 0; q < RAD; ++q) buf[c * ld + b0 + q * ns] = v[q];
     }
 }
 
-// Full column DFT of length L = M1 (power of two, 2..512) over the CB columns of buf.
+// Full column DFT of length L = M1 (power of two, 32..512) over the CB columns of buf; each
+// wave transforms its own columns.  Callers bracket it with block barriers.
 template <int kThreads, bool INV>
 __device__ void column_dft(float2* buf, int L, int ld, int CB, const float* tw_col, int m1) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = kThreads / 64;
     int ns = 1;
     bool first = !INV;  // forward: the input's second half is zero
     while (ns < L) {
         const int rem = L / ns;
         if (rem >= 8) {
-            if (first) stockham_pass<kThreads, 8, INV, true>(buf, L, ld, CB, ns, tw_col, m1);
-            else stockham_pass<kThreads, 8, INV, false>(buf, L, ld, CB, ns, tw_col, m1);
+            if (first) stockham_pass_wave<8, INV, true>(buf, L, ld, CB, ns, tw_col, m1, wave, nw, lane);
+            else stockham_pass_wave<8, INV, false>(buf, L, ld, CB, ns, tw_col, m1, wave, nw, lane);
             ns *= 8;
         } else if (rem == 4) {
-            if (first) stockham_pass<kThreads, 4, INV, true>(buf, L, ld, CB, ns, tw_col, m1);
-            else stockham_pass<kThreads, 4, INV, false>(buf, L, ld, CB, ns, tw_col, m1);
+            if (first) stockham_pass_wave<4, INV, true>(buf, L, ld, CB, ns, tw_col, m1, wave, nw, lane);
+            else stockham_pass_wave<4, INV, false>(buf, L, ld, CB, ns, tw_col, m1, wave, nw, lane);
             ns *= 4;
         } else {
-            if (first) stockham_pass<kThreads, 2, INV, true>(buf, L, ld, CB, ns, tw_col, m1);
-            else stockham_pass<kThreads, 2, INV, false>(buf, L, ld, CB, ns, tw_col, m1);
+            if (first) stockham_pass_wave<2, INV, true>(buf, L, ld, CB, ns, tw_col, m1, wave, nw, lane);
+            else stockham_pass_wave<2, INV, false>(buf, L, ld, CB, ns, tw_col, m1, wave, nw, lane);
             ns *= 2;
         }
         first = false;
     }
+    __syncthreads();
 }
 
 // 8 consecutive io elements -> fp32 (raw 16-byte words for 16-bit types, 32 bytes for fp32)
@@ -246,7 +231,9 @@ __device__ __forceinline__ void seq_rows(const ColArgs& a, int64_t gs, int64_t& 
 template <int CT, int IO, int kThreads>
 __global__ void __launch_bounds__(kThreads) col_fwd_kernel(const ColArgs a) {
     extern __shared__ float2 buf[];
-    const int M1 = (int)a.M1, CB = cols_per_wg(M1), ld = CB;
+    // column-major block, column stride M1 + 1: the column passes walk rows of one column
+    // (consecutive words), the row-wise load and store see at most 2-way bank conflicts
+    const int M1 = (int)a.M1, CB = cols_per_wg(M1), ld = M1 + 1;
     const int64_t s = blockIdx.y, gs = a.seq0 + s;
     const int64_t n_lo0 = (int64_t)blockIdx.x * CB;
     int64_t row0, row1;
@@ -281,9 +268,9 @@ __global__ void __launch_bounds__(kThreads) col_fwd_kernel(const ColArgs a) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) xr[k] = xi[k] = 0.f;
         }
-        float2* d = buf + nh * ld + 8 * cg;
+        float2* d = buf + 8 * cg * ld + nh;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) d[k] = make_float2(xr[k], xi[k]);
+        for (int k = 0; k < 8; ++k) d[k * ld] = make_float2(xr[k], xi[k]);
     }
     __syncthreads();
     column_dft<kThreads, false>(buf, M1, ld, CB, a.tw_col, M1);
@@ -294,10 +281,10 @@ __global__ void __launch_bounds__(kThreads) col_fwd_kernel(const ColArgs a) {
         float2 w = tw_m(a.tw_lo, a.tw_hi, (n_lo * kh) & (a.M - 1));
         const float2 step = ((const float2*)a.tw_lo)[kh];  // kh < 2048
         float2 z[8];
-        const float2* src = buf + kh * ld + 8 * cg;
+        const float2* src = buf + 8 * cg * ld + kh;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            z[k] = cmulf(src[k], w);
+            z[k] = cmulf(src[k * ld], w);
             w = cmulf(w, step);
         }
         ws_st8<CT>(a.ws, (s * a.M1 + kh) * kM2 + n_lo, z);
@@ -307,7 +294,7 @@ __global__ void __launch_bounds__(kThreads) col_fwd_kernel(const ColArgs a) {
 template <int CT, int IO, int kThreads>
 __global__ void __launch_bounds__(kThreads) col_inv_kernel(const ColArgs a) {
     extern __shared__ float2 buf[];
-    const int M1 = (int)a.M1, CB = cols_per_wg(M1), ld = CB;
+    const int M1 = (int)a.M1, CB = cols_per_wg(M1), ld = M1 + 1;  // column-major, as above
     const int64_t s = blockIdx.y, gs = a.seq0 + s;
     const int64_t n_lo0 = (int64_t)blockIdx.x * CB;
     int64_t row0, row1;
@@ -321,10 +308,10 @@ __global__ void __launch_bounds__(kThreads) col_inv_kernel(const ColArgs a) {
         const float2 step = ((const float2*)a.tw_lo)[kh];
         float2 z[8];
         ws_ld8<CT>(a.ws, (s * a.M1 + kh) * kM2 + n_lo, z);
-        float2* d = buf + kh * ld + 8 * cg;
+        float2* d = buf + 8 * cg * ld + kh;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            d[k] = cmulcf(z[k], w);
+            d[k * ld] = cmulcf(z[k], w);
             w = cmulf(w, step);
         }
     }
@@ -335,12 +322,12 @@ __global__ void __launch_bounds__(kThreads) col_inv_kernel(const ColArgs a) {
         const int nh = it / g8, cg = it % g8;
         const int64_t n = kM2 * nh + n_lo0 + 8 * cg;
         if (n >= a.N) continue;
-        const float2* src = buf + nh * ld + 8 * cg;
+        const float2* src = buf + 8 * cg * ld + nh;
         float yr[8], yi[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            yr[k] = src[k].x;
-            yi[k] = src[k].y;
+            yr[k] = src[k * ld].x;
+            yi[k] = src[k * ld].y;
         }
         if (a.v) {
             float t[8];
@@ -523,15 +510,16 @@ template <int CT, int IO, int TPB>
 static hipError_t launch_cols_t(bool fwd, const ColArgs& a, hipStream_t st) {
     const int M1 = (int)a.M1;
     const int CB = cols_per_wg(M1);
-    const size_t lds = (size_t)CB * M1 * sizeof(float2);
+    const size_t lds = (size_t)CB * (M1 + 1) * sizeof(float2);
     dim3 grid((unsigned)(kM2 / CB), (unsigned)a.nseq);
-    // dynamic LDS above the default limit has to be allowed per kernel
+    // dynamic LDS above the default limit has to be allowed per kernel (once, at the device
+    // maximum: the block size depends on M1, at most 133,120 bytes)
     static bool attr_set[2] = {false, false};
     auto kfwd = col_fwd_kernel<CT, IO, TPB>;
     auto kinv = col_inv_kernel<CT, IO, TPB>;
     if (!attr_set[fwd ? 0 : 1]) {
         hipError_t e = hipFuncSetAttribute(fwd ? (const void*)kfwd : (const void*)kinv,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr_set[fwd ? 0 : 1] = true;
     }
