@@ -227,6 +227,172 @@ int oracle_conv1d_points(const void* u, const void* q, const void* v, const void
 }
 
 /* ------------------------------------------------------------------------------------------ */
+/* 1D backward (gradients of the causal convolution)                                           */
+/* ------------------------------------------------------------------------------------------ */
+/*
+ * With s = k * x + D x (causal, truncated to N), y = v s and an output gradient gy, the chain
+ * rule on the plain definition above gives (ds = gy v):
+ *
+ *     dx[b,h,t] = sum_{tau=t..N-1} k[h,tau-t] ds[b,h,tau] + D[h] ds[b,h,t]   (correlation)
+ *     du = q dx,   dq = u dx,   dv = gy s,
+ *     dk[h,tau] = sum_b sum_{t=tau..N-1} ds[b,h,t] x[b,h,t-tau],
+ *     dD[h]     = sum_b sum_t ds[b,h,t] x[b,h,t]        (= dk[h,0]: D acts as an extra lag-0 tap)
+ *
+ * Sums run in ascending index order in double precision, from the exactly widened inputs.
+ */
+typedef struct {
+    or_job j;
+    const void* gy;
+    double *du, *dq, *dv;
+} or_bwd_job;
+
+static void or_row_ds(const or_bwd_job* W, int64_t b, int64_t h, double* ds) {
+    const or_job* J = &W->j;
+    int64_t off = (b * J->H + h) * J->N;
+    or_widen(W->gy, J->dt, off, J->N, ds);
+    if (J->v)
+        for (int64_t t = 0; t < J->N; ++t) ds[t] *= or_load(J->v, J->dt, off + t);
+}
+
+static void* or_bwd_rows_worker(void* arg) {
+    or_bwd_job* W = (or_bwd_job*)arg;
+    const or_job* J = &W->j;
+    const int64_t N = J->N;
+    double* x = (double*)malloc(sizeof(double) * (size_t)N);
+    double* ds = (double*)malloc(sizeof(double) * (size_t)N);
+    double* k = (double*)malloc(sizeof(double) * (size_t)N);
+    for (int64_t r = J->lo; r < J->hi; ++r) {
+        int64_t b = J->sel[2 * r], h = J->sel[2 * r + 1];
+        int64_t off = (b * J->H + h) * N;
+        or_row_x(J, b, h, N, x);
+        or_row_ds(W, b, h, ds);
+        or_widen(J->k, J->dt, h * N, N, k);
+        double d = or_load(J->D, J->dt, h);
+        for (int64_t t = 0; t < N; ++t) {
+            double a = 0;
+            for (int64_t tau = t; tau < N; ++tau) a += k[tau - t] * ds[tau];
+            double dx = a + d * ds[t];
+            if (W->du) W->du[r * N + t] = J->q ? dx * or_load(J->q, J->dt, off + t) : dx;
+            if (W->dq) W->dq[r * N + t] = dx * or_load(J->u, J->dt, off + t);
+            if (W->dv) {
+                double c = 0;
+                for (int64_t s2 = 0; s2 <= t; ++s2) c += k[t - s2] * x[s2];
+                W->dv[r * N + t] = or_load(W->gy, J->dt, off + t) * (c + d * x[t]);
+            }
+        }
+    }
+    free(x);
+    free(ds);
+    free(k);
+    return NULL;
+}
+
+/* Gradient rows for each (b,h) in rows[2*nrows]: du, dq, dv are [nrows][N] (any may be NULL;
+ * dq needs q, dv needs v). */
+int oracle_conv1d_bwd_rows(const void* u, const void* q, const void* v, const void* k, const void* D,
+                           const void* gy, int dt, int64_t B, int64_t H, int64_t N,
+                           const int64_t* rows, int64_t nrows, double* du, double* dq, double* dv,
+                           int nthreads) {
+    if (!u || !k || !D || !gy || (nrows > 0 && !rows)) return -1;
+    if (B < 1 || H < 1 || N < 1 || nrows < 0 || dt < 0 || dt > 2) return -1;
+    if ((dq && !q) || (dv && !v)) return -1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[2 * r] < 0 || rows[2 * r] >= B || rows[2 * r + 1] < 0 || rows[2 * r + 1] >= H)
+            return -1;
+    or_bwd_job W;
+    or_job J = {u, q, v, k, D, dt, B, H, N, rows, NULL, 0, 0};
+    W.j = J;
+    W.gy = gy;
+    W.du = du;
+    W.dq = dq;
+    W.dv = dv;
+    /* thread the row list by hand (the job carries extra fields) */
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((int64_t)nthreads > nrows) nthreads = (int)(nrows > 0 ? nrows : 1);
+    or_bwd_job* jobs = (or_bwd_job*)calloc((size_t)nthreads, sizeof(or_bwd_job));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    int64_t per = (nrows + nthreads - 1) / nthreads;
+    int used = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        int64_t lo = (int64_t)i * per, hi = lo + per < nrows ? lo + per : nrows;
+        if (lo >= hi) break;
+        jobs[used] = W;
+        jobs[used].j.lo = lo;
+        jobs[used].j.hi = hi;
+        pthread_create(&th[used], NULL, or_bwd_rows_worker, &jobs[used]);
+        ++used;
+    }
+    for (int i = 0; i < used; ++i) pthread_join(th[i], NULL);
+    free(th);
+    free(jobs);
+    return 0;
+}
+
+/* dk[h, 0:N] and dD[h] for each channel h in chans[nch]; dk is [nch][N], dD is [nch]. */
+static void* or_dk_worker(void* arg) {
+    or_bwd_job* W = (or_bwd_job*)arg;
+    const or_job* J = &W->j;
+    const int64_t N = J->N, B = J->B;
+    double* x = (double*)malloc(sizeof(double) * (size_t)N);
+    double* ds = (double*)malloc(sizeof(double) * (size_t)N);
+    for (int64_t r = J->lo; r < J->hi; ++r) {
+        int64_t h = J->sel[r];
+        double* dk = W->du + r * N;   /* du carries dk, dq carries dD for this job kind */
+        for (int64_t tau = 0; tau < N; ++tau) dk[tau] = 0;
+        for (int64_t b = 0; b < B; ++b) {
+            or_row_x(J, b, h, N, x);
+            or_row_ds(W, b, h, ds);
+            for (int64_t tau = 0; tau < N; ++tau) {
+                double a = 0;
+                for (int64_t t = tau; t < N; ++t) a += ds[t] * x[t - tau];
+                dk[tau] += a;
+            }
+        }
+        W->dq[r] = dk[0];
+    }
+    free(x);
+    free(ds);
+    return NULL;
+}
+
+int oracle_conv1d_bwd_dk(const void* u, const void* q, const void* v, const void* gy, int dt,
+                         int64_t B, int64_t H, int64_t N, const int64_t* chans, int64_t nch,
+                         double* dk, double* dD, int nthreads) {
+    if (!u || !gy || !dk || !dD || (nch > 0 && !chans)) return -1;
+    if (B < 1 || H < 1 || N < 1 || nch < 0 || dt < 0 || dt > 2) return -1;
+    for (int64_t r = 0; r < nch; ++r)
+        if (chans[r] < 0 || chans[r] >= H) return -1;
+    or_bwd_job W;
+    or_job J = {u, q, v, NULL, NULL, dt, B, H, N, chans, NULL, 0, 0};
+    W.j = J;
+    W.gy = gy;
+    W.du = dk;
+    W.dq = dD;
+    W.dv = NULL;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((int64_t)nthreads > nch) nthreads = (int)(nch > 0 ? nch : 1);
+    or_bwd_job* jobs = (or_bwd_job*)calloc((size_t)nthreads, sizeof(or_bwd_job));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    int64_t per = (nch + nthreads - 1) / nthreads;
+    int used = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        int64_t lo = (int64_t)i * per, hi = lo + per < nch ? lo + per : nch;
+        if (lo >= hi) break;
+        jobs[used] = W;
+        jobs[used].j.lo = lo;
+        jobs[used].j.hi = hi;
+        pthread_create(&th[used], NULL, or_dk_worker, &jobs[used]);
+        ++used;
+    }
+    for (int i = 0; i < used; ++i) pthread_join(th[i], NULL);
+    free(th);
+    free(jobs);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------ */
 /* 2D: direct summation at single positions                                                    */
 /* ------------------------------------------------------------------------------------------ */
 

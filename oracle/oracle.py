@@ -52,7 +52,11 @@ def _load():
         lib.oracle_conv1d_points.argtypes = [vp, vp, vp, vp, vp, ip, i64, i64, i64, vp, i64, dp, ip]
         lib.oracle_conv2d_points.argtypes = [vp, vp, vp, ip, i64, i64, i64, vp, i64, dp, ip]
         lib.oracle_widen.argtypes = [vp, ip, i64, dp]
-        for f in (lib.oracle_conv1d_rows, lib.oracle_conv1d_points, lib.oracle_conv2d_points):
+        lib.oracle_conv1d_bwd_rows.argtypes = [vp, vp, vp, vp, vp, vp, ip, i64, i64, i64, vp, i64,
+                                               dp, dp, dp, ip]
+        lib.oracle_conv1d_bwd_dk.argtypes = [vp, vp, vp, vp, ip, i64, i64, i64, vp, i64, dp, dp, ip]
+        for f in (lib.oracle_conv1d_rows, lib.oracle_conv1d_points, lib.oracle_conv2d_points,
+                  lib.oracle_conv1d_bwd_rows, lib.oracle_conv1d_bwd_dk):
             f.restype = ctypes.c_int
         lib.oracle_widen.restype = None
         _lib = lib
@@ -135,6 +139,46 @@ def conv1d_points(u, k, D, pts, q=None, v=None, dt=None, nthreads=None):
     if rc:
         raise ValueError("oracle_conv1d_points rejected its arguments")
     return out
+
+
+def conv1d_bwd_rows(u, k, D, gy, rows, q=None, v=None, dt=None, nthreads=None):
+    """Gradient rows of the causal convolution for rows = [(b,h), ...], given the output
+    gradient gy [B,H,N]: returns float64 (du, dq, dv), each [len(rows), N] (dq is None without q,
+    dv is None without v).  The chain rule on the plain definition, summed directly (oracle.c)."""
+    dt = _dt_of(u, dt)
+    st = _storage(dt)
+    u, k, D, gy, q, v = (_c(a, st) for a in (u, k, D, gy, q, v))
+    B, H, N = u.shape
+    assert k.shape == (H, N) and D.shape == (H,) and gy.shape == u.shape
+    rows = np.ascontiguousarray(np.asarray(rows, np.int64).reshape(-1, 2))
+    du = np.empty((rows.shape[0], N), np.float64)
+    dq = np.empty_like(du) if q is not None else None
+    dv = np.empty_like(du) if v is not None else None
+    rc = _load().oracle_conv1d_bwd_rows(_ptr(u), _ptr(q), _ptr(v), _ptr(k), _ptr(D), _ptr(gy), dt,
+                                        B, H, N, _ptr(rows), rows.shape[0], du.ctypes.data,
+                                        None if dq is None else dq.ctypes.data,
+                                        None if dv is None else dv.ctypes.data, _threads(nthreads))
+    if rc:
+        raise ValueError("oracle_conv1d_bwd_rows rejected its arguments")
+    return du, dq, dv
+
+
+def conv1d_bwd_dk(u, gy, chans, q=None, v=None, dt=None, nthreads=None):
+    """Filter and skip gradients for channels chans: returns float64 (dk [len(chans), N],
+    dD [len(chans)]), dk[h,tau] = sum_b sum_t ds[b,h,t] x[b,h,t-tau] with ds = gy v, x = q u."""
+    dt = _dt_of(u, dt)
+    st = _storage(dt)
+    u, gy, q, v = (_c(a, st) for a in (u, gy, q, v))
+    B, H, N = u.shape
+    chans = np.ascontiguousarray(np.asarray(chans, np.int64).reshape(-1))
+    dk = np.empty((chans.shape[0], N), np.float64)
+    dD = np.empty(chans.shape[0], np.float64)
+    rc = _load().oracle_conv1d_bwd_dk(_ptr(u), _ptr(q), _ptr(v), _ptr(gy), dt, B, H, N, _ptr(chans),
+                                      chans.shape[0], dk.ctypes.data, dD.ctypes.data,
+                                      _threads(nthreads))
+    if rc:
+        raise ValueError("oracle_conv1d_bwd_dk rejected its arguments")
+    return dk, dD
 
 
 def conv2d_points(u, k, D, pts, dt=None, nthreads=None):
