@@ -20,198 +20,25 @@
 // register-resident tiles and the twiddle folding are this implementation's own.
 #include <type_traits>
 
+#include "fused_io.h"
 #include "kernels.h"
 #include "lconv_device.h"
 
 namespace lcv {
 
-namespace {
-
-template <int IO>
-__device__ __forceinline__ float load1(const void* base, int64_t i) {
-    if constexpr (IO == CT_F32) {
-        return ((const float*)base)[i];
-    } else {
-        uint32_t w = ((const uint16_t*)base)[i];
-        return unpack_lo<IO>(w);
-    }
-}
-
-template <int IO>
-__device__ __forceinline__ void load8(const void* base, int64_t off, float* x) {
-    if constexpr (IO == CT_F32) {
-        const float4* p = (const float4*)((const float*)base + off);
-        float4 a = p[0], b = p[1];
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-    } else {
-        uint4 w = *(const uint4*)((const uint16_t*)base + off);
-        x[0] = unpack_lo<IO>(w.x); x[1] = unpack_hi<IO>(w.x);
-        x[2] = unpack_lo<IO>(w.y); x[3] = unpack_hi<IO>(w.y);
-        x[4] = unpack_lo<IO>(w.z); x[5] = unpack_hi<IO>(w.z);
-        x[6] = unpack_lo<IO>(w.w); x[7] = unpack_hi<IO>(w.w);
-    }
-}
-
-template <int IO>
-__device__ __forceinline__ void store8(void* base, int64_t off, const float* x) {
-    if constexpr (IO == CT_F32) {
-        float4* p = (float4*)((float*)base + off);
-        p[0] = make_float4(x[0], x[1], x[2], x[3]);
-        p[1] = make_float4(x[4], x[5], x[6], x[7]);
-    } else {
-        uint4 w;
-        w.x = pack2<IO>(x[0], x[1]);
-        w.y = pack2<IO>(x[2], x[3]);
-        w.z = pack2<IO>(x[4], x[5]);
-        w.w = pack2<IO>(x[6], x[7]);
-        *(uint4*)((uint16_t*)base + off) = w;
-    }
-}
-
-// 8 consecutive elements as raw bits (1 uint4 for 16-bit types, 2 for fp32) and their unpacking.
-template <int IO>
-__device__ __forceinline__ void load_raw(const void* base, int64_t off, uint4* r) {
-    if constexpr (IO == CT_F32) {
-        const uint4* p = (const uint4*)((const float*)base + off);
-        r[0] = p[0];
-        r[1] = p[1];
-    } else {
-        r[0] = *(const uint4*)((const uint16_t*)base + off);
-    }
-}
-template <int IO>
-__device__ __forceinline__ void unpack_raw(const uint4* r, float* x) {
-    if constexpr (IO == CT_F32) {
-        x[0] = __uint_as_float(r[0].x); x[1] = __uint_as_float(r[0].y);
-        x[2] = __uint_as_float(r[0].z); x[3] = __uint_as_float(r[0].w);
-        x[4] = __uint_as_float(r[1].x); x[5] = __uint_as_float(r[1].y);
-        x[6] = __uint_as_float(r[1].z); x[7] = __uint_as_float(r[1].w);
-    } else {
-        x[0] = unpack_lo<IO>(r[0].x); x[1] = unpack_hi<IO>(r[0].x);
-        x[2] = unpack_lo<IO>(r[0].y); x[3] = unpack_hi<IO>(r[0].y);
-        x[4] = unpack_lo<IO>(r[0].z); x[5] = unpack_hi<IO>(r[0].z);
-        x[6] = unpack_lo<IO>(r[0].w); x[7] = unpack_hi<IO>(r[0].w);
-    }
-}
-// 4 consecutive complex values (raw bits) of a spectrum stored in type IO.
-template <int IO>
-__device__ __forceinline__ void load_raw_c4(const void* base, int64_t off, uint4* r) {
-    if constexpr (IO == CT_F32) {
-        const uint4* p = (const uint4*)((const float*)base + 2 * off);
-        r[0] = p[0];
-        r[1] = p[1];
-    } else {
-        r[0] = *(const uint4*)((const uint32_t*)base + off);
-    }
-}
-template <int IO>
-__device__ __forceinline__ void unpack_raw_c4(const uint4* r, float* re, float* im) {
-    if constexpr (IO == CT_F32) {
-        re[0] = __uint_as_float(r[0].x); im[0] = __uint_as_float(r[0].y);
-        re[1] = __uint_as_float(r[0].z); im[1] = __uint_as_float(r[0].w);
-        re[2] = __uint_as_float(r[1].x); im[2] = __uint_as_float(r[1].y);
-        re[3] = __uint_as_float(r[1].z); im[3] = __uint_as_float(r[1].w);
-    } else {
-        re[0] = unpack_lo<IO>(r[0].x); im[0] = unpack_hi<IO>(r[0].x);
-        re[1] = unpack_lo<IO>(r[0].y); im[1] = unpack_hi<IO>(r[0].y);
-        re[2] = unpack_lo<IO>(r[0].z); im[2] = unpack_hi<IO>(r[0].z);
-        re[3] = unpack_lo<IO>(r[0].w); im[3] = unpack_hi<IO>(r[0].w);
-    }
-}
-
-template <int IO>
-__device__ __forceinline__ void unpack_raw_c4v(const uint4* r, f32x4& re, f32x4& im) {
-    float a[4], b[4];
-    unpack_raw_c4<IO>(r, a, b);
-    re = f32x4{a[0], a[1], a[2], a[3]};
-    im = f32x4{b[0], b[1], b[2], b[3]};
-}
-
-// 4 consecutive complex values of a spectrum stored in type IO -> fp32.
-template <int IO>
-__device__ __forceinline__ void load_c4(const void* base, int64_t off, float* re, float* im) {
-    if constexpr (IO == CT_F32) {
-        const float4* p = (const float4*)((const float*)base + 2 * off);
-        float4 a = p[0], b = p[1];
-        re[0] = a.x; im[0] = a.y; re[1] = a.z; im[1] = a.w;
-        re[2] = b.x; im[2] = b.y; re[3] = b.z; im[3] = b.w;
-    } else {
-        uint4 w = *(const uint4*)((const uint32_t*)base + off);
-        re[0] = unpack_lo<IO>(w.x); im[0] = unpack_hi<IO>(w.x);
-        re[1] = unpack_lo<IO>(w.y); im[1] = unpack_hi<IO>(w.y);
-        re[2] = unpack_lo<IO>(w.z); im[2] = unpack_hi<IO>(w.z);
-        re[3] = unpack_lo<IO>(w.w); im[3] = unpack_hi<IO>(w.w);
-    }
-}
-
-template <int IO>
-__device__ __forceinline__ void store_c4v(void* base, int64_t off, const f32x4 re, const f32x4 im) {
-    if constexpr (IO == CT_F32) {
-        float4* p = (float4*)((float*)base + 2 * off);
-        p[0] = make_float4(re[0], im[0], re[1], im[1]);
-        p[1] = make_float4(re[2], im[2], re[3], im[3]);
-    } else {
-        uint4 w;
-        w.x = pack2<IO>(re[0], im[0]);
-        w.y = pack2<IO>(re[1], im[1]);
-        w.z = pack2<IO>(re[2], im[2]);
-        w.w = pack2<IO>(re[3], im[3]);
-        *(uint4*)((uint32_t*)base + off) = w;
-    }
-}
-
-// LDS complex element in compute type: one packed word (16-bit) or two floats.
-template <int CT>
-__device__ __forceinline__ void lds_put(uint32_t* base, int idx, float re, float im) {
-    if constexpr (CT == CT_F32) {
-        *(float2*)(base + 2 * idx) = make_float2(re, im);
-    } else {
-        base[idx] = pack2<CT>(re, im);
-    }
-}
-
-// Read a tile operand: element (K index 4g + j, L index c) at base + idx(j).
-template <int CT, typename F>
-__device__ __forceinline__ Operand<CT> lds_operand(const uint32_t* base, F idx) {
-    Operand<CT> o;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int e = idx(j);
-        if constexpr (CT == CT_F32) {
-            float2 v = e >= 0 ? *(const float2*)(base + 2 * e) : make_float2(0.f, 0.f);
-            o.s[2 * j] = v.x;
-            o.s[2 * j + 1] = v.y;
-        } else {
-            o.w[j] = e >= 0 ? base[e] : 0u;
-        }
-    }
-    return o;
-}
-
-}  // namespace
-
-
-// D[h] as raw bits (converted where it is used, so the load's latency is not waited for early)
-template <int IO>
-__device__ __forceinline__ uint32_t load1_raw(const void* base, int64_t i) {
-    if constexpr (IO == CT_F32) return ((const uint32_t*)base)[i];
-    else return ((const uint16_t*)base)[i];
-}
-template <int IO>
-__device__ __forceinline__ float raw1_to_f32(uint32_t w) {
-    if constexpr (IO == CT_F32) return __uint_as_float(w);
-    else return unpack_lo<IO>(w);
-}
-
-// MODE: conv / filter / row / row-forward.  GQ, GV: pre-gate q and post-gate v present (conv).
+// MODE: conv / filter / row / row-forward / adjoint.  GQ, GV: pre-gate and post-gate present
+// (conv, adjoint).  The adjoint runs the convolution chain on dy (pre-gated by v) with the
+// conjugate spectrum, which turns the causal sum into the correlation sum over later positions,
+// and writes two gated copies of the result: du = q dx and dq = u dx.
 template <int R, int CT, int IO, int MODE, bool GQ, bool GV>
 __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
     constexpr int P = 32 / R;                  // sequences per workgroup iteration
     constexpr int M = 256 * R;
-    constexpr bool HALF_IN = (MODE == MODE_CONV || MODE == MODE_FILTER);
-    constexpr bool HALF_OUT = (MODE == MODE_CONV);
-    constexpr bool INV = (MODE == MODE_CONV || MODE == MODE_ROW);
+    constexpr bool ADJ = MODE == MODE_ADJ;
+    constexpr bool CONV = MODE == MODE_CONV || ADJ;  // batch-row input and output
+    constexpr bool HALF_IN = (CONV || MODE == MODE_FILTER);
+    constexpr bool HALF_OUT = CONV;
+    constexpr bool INV = (CONV || MODE == MODE_ROW);
     constexpr int NIN = HALF_IN ? R / 2 : R;   // nonzero n1 rows
     constexpr int NOUT = HALF_OUT ? R / 2 : R; // n1 rows produced
     constexpr int KCF = (R + 15) / 16;         // table grid (full variant)
@@ -241,13 +68,13 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
     constexpr int BPW = NBLK / 8;              // blocks per wave
     // The radix-R blocks (F1, I3) are shared by all waves: on the convolution path they live in
     // LDS (copied once), which keeps the per-tile blocks in registers without spills.
-    constexpr bool IMG_LDS = RES && (MODE == MODE_CONV || MODE == MODE_ROW);
+    constexpr bool IMG_LDS = RES && (CONV || MODE == MODE_ROW);
     constexpr int IMGS_W = IMG_LDS ? (T_F2 - T_F1) / 4 : 0;
     constexpr int IOW = IO == CT_F32 ? 2 : 1;  // uint4 per 8 io elements
     // One sequence per iteration (R = 32) and 16-bit spectra: the filter spectrum of the
     // current channel stays in LDS and is reloaded only when the channel changes (consecutive
     // items are the batch pairs of one channel).
-    constexpr bool KF_LDS = MODE == MODE_CONV && R == 32 && IO != CT_F32;
+    constexpr bool KF_LDS = CONV && R == 32 && IO != CT_F32;
     constexpr int KF_W = KF_LDS ? 32 * 64 * 4 : 0;
 
     __shared__ __attribute__((aligned(16))) uint32_t lds[V_W + XY_W + O_W + IMGS_W + KF_W];
@@ -353,7 +180,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
         int64_t itc = item < last ? item : last - 1;
         if constexpr (R >= 4) itc = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)itc);
         const int64_t n0c = n0_io < a.N ? n0_io : a.N - 8;
-        if constexpr (MODE == MODE_CONV) {
+        if constexpr (CONV) {
             int64_t h, b;
             decode(itc, h, b);
             const int64_t row0 = (b * a.H + h) * a.N;
@@ -375,7 +202,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
         bool k0, k1;
         io_offsets(it_base + p_io, o0, o1, k0, k1);
         load_raw<IO>(a.u, o0, ru[0]);
-        if constexpr (MODE == MODE_CONV) {
+        if constexpr (CONV) {
             load_raw<IO>(a.u, o1, ru[1]);
             if constexpr (GQ) {
                 load_raw<IO>(a.q, o0, rq[0]);
@@ -398,7 +225,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
             io_offsets(it0 + p_io, o0, o1, ok0, ok1);
             float xr[8], xi[8];
             unpack_raw<IO>(ru[0], xr);
-            if constexpr (MODE == MODE_CONV) {
+            if constexpr (CONV) {
                 unpack_raw<IO>(ru[1], xi);
                 if constexpr (GQ) {
                     float t[8];
@@ -483,7 +310,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                 int64_t item = it0 + (wave * 4 + 2 * s) / R;
                 item = item < last ? item : last - 1;
                 int64_t h;
-                if constexpr (MODE == MODE_CONV) {
+                if constexpr (CONV) {
                     int64_t b;
                     decode(item, h, b);
                     bases[s] = h * M;
@@ -501,7 +328,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                 load_raw_c4<IO>(a.kf, bases[s] + ((int64_t)k1 * 64 + lane) * 4, rk[i]);
             }
         }
-        if constexpr (MODE == MODE_CONV && GV) {
+        if constexpr (CONV && GV) {
             int64_t o0, o1;
             bool k0, k1;
             io_offsets(it0 + p_io, o0, o1, k0, k1);
@@ -615,7 +442,8 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                         unpack_raw_c4v<IO>(rk[i], kr, ki);
                         kr += raw1_to_f32<IO>(dk[i]) * a.inv_m;  // D folded: (K + D) / M
                     }
-                    cmul4(xs[i], kr, ki);
+                    if constexpr (ADJ) cmulc4(xs[i], kr, ki);  // D is real: conj(K + D) = conj(K) + D
+                    else cmul4(xs[i], kr, ki);
                     opd[i] = to_operand<CT>(xs[i]);
                 } else if constexpr (st == 2) {
                     // spectrum in transform order, scaled by 1/M
@@ -694,6 +522,15 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (INV) {
+            // adjoint with gates: u for dq = u dx, loaded here (the transform registers are free)
+            uint4 re2[2][IOW];
+            if constexpr (ADJ && GV) {
+                int64_t o0, o1;
+                bool k0, k1;
+                io_offsets(it0 + p_io, o0, o1, k0, k1);
+                load_raw<IO>(a.e2, o0, re2[0]);
+                load_raw<IO>(a.e2, o1, re2[1]);
+            }
             // ================= P3: I3 (inverse radix R over k1, n1 < NOUT), XY -> O ============
             // Same chunked read / multiply / write order as P1.
             {
@@ -751,7 +588,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
             __builtin_amdgcn_sched_barrier(0);
 
             // ================= P4: epilogue ==================================================
-            if constexpr (MODE == MODE_CONV) {
+            if constexpr (CONV) {
                 int64_t o0, o1;
                 bool ok0, ok1;
                 io_offsets(it0 + p_io, o0, o1, ok0, ok1);
@@ -761,6 +598,24 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                 for (int i = 0; i < 4; ++i) {
                     float4 w = src[i];
                     yr[2 * i] = w.x; yi[2 * i] = w.y; yr[2 * i + 1] = w.z; yi[2 * i + 1] = w.w;
+                }
+                if constexpr (ADJ && GV) {
+                    // dq = u dx (second output), before dx is gated into du below
+                    float t[8], zr[8], zi[8];
+                    unpack_raw<IO>(re2[0], t);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) zr[i] = yr[i] * t[i];
+                    unpack_raw<IO>(re2[1], t);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) zi[i] = yi[i] * t[i];
+                    if constexpr (!FULL) {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) zi[i] = o1 != o0 ? zi[i] : zr[i];
+                    }
+                    if (FULL || ok0) {
+                        store8<IO>(a.y2, o0, zr);
+                        store8<IO>(a.y2, o1, zi);
+                    }
                 }
                 if constexpr (GV) {
                     float t[8];
@@ -832,8 +687,10 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
 // waves 4-7 run W first, so each SIMD (which hosts waves w and w+4) pairs the two kinds of work.
 // O is kept in the compute type and shares V's space (both are used wave-locally); the filter
 // spectrum has two LDS copies so the next channel's can be loaded while the current one is read.
+// ADJ: the adjoint chain (conjugate spectrum; outputs du = q dx and dq = u dx), as in
+// fused1d_kernel.
 // ------------------------------------------------------------------------------------------
-template <int CT, bool GQ, bool GV>
+template <int CT, bool GQ, bool GV, bool ADJ>
 __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
     constexpr int R = 32, M = 8192, KCF = 2;
     constexpr int IMG = ImgBytes<CT>::value;
@@ -906,7 +763,7 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
         o0 = row0 + s_n0;
         o1 = (b + 1 < a.B ? row0 + HN : row0) + s_n0;
     };
-    uint4 ru[2], rq[2], rv[2];
+    uint4 ru[2], rq[2], rv[2], re2[2];
     auto issue_uq = [&](int64_t item) LCV_INLINE {
         int64_t o0, o1;
         offsets(item, o0, o1);
@@ -923,6 +780,15 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
             offsets(item, o0, o1);
             load_raw<CT>(a.v, o0, &rv[0]);
             load_raw<CT>(a.v, o1, &rv[1]);
+        }
+    };
+    // adjoint with gates: u for dq = u dx, issued just before the item's P3
+    auto issue_e2 = [&](int64_t item) LCV_INLINE {
+        if constexpr (ADJ && GV) {
+            int64_t o0, o1;
+            offsets(item, o0, o1);
+            load_raw<CT>(a.e2, o0, &re2[0]);
+            load_raw<CT>(a.e2, o1, &re2[1]);
         }
     };
     // (K + D) / M of channel h into copy kb, this wave's tiles only (read back by this wave)
@@ -1027,7 +893,8 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
                     const uint4 kw = kfl[t * 64 + lane];  // (K + D) / M
                     f32x4 kr, ki;
                     unpack_raw_c4v<CT>(&kw, kr, ki);
-                    cmul4(xs[i], kr, ki);
+                    if constexpr (ADJ) cmulc4(xs[i], kr, ki);
+                    else cmul4(xs[i], kr, ki);
                     opd[i] = to_operand<CT>(xs[i]);
                 } else if constexpr (st == 3) {
                     cmulc4(xs[i], twr, twi);
@@ -1110,6 +977,17 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
             yr[i] = unpack_lo<CT>(w[i]);
             yi[i] = unpack_hi<CT>(w[i]);
         }
+        if constexpr (ADJ && GV) {
+            float t[8], zr[8], zi[8];
+            unpack_raw<CT>(&re2[0], t);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) zr[i] = yr[i] * t[i];
+            unpack_raw<CT>(&re2[1], t);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) zi[i] = yi[i] * t[i];
+            store8<CT>(a.y2, o0, zr);
+            store8<CT>(a.y2, o1, zi);
+        }
         if constexpr (GV) {
             float t[8];
             unpack_raw<CT>(&rv[0], t);
@@ -1144,6 +1022,7 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
                 P2(XYk, KFL + kb * (KF_W / 4));
             } else {
                 if (k > first) {
+                    issue_e2(k - 1);
                     P3(XYo);
                     P4(k - 1);
                 }
@@ -1168,6 +1047,7 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
     }
+    issue_e2(last - 1);
     P3(XYb + ((last - 1 - first) & 1) * XY_W);
     P4(last - 1);
 }
@@ -1190,31 +1070,32 @@ static hipError_t launch_t(const Fused1DArgs& a0, int cus, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int CT, bool GQ, bool GV>
+template <int CT, bool GQ, bool GV, bool ADJ>
 static hipError_t launch_8k(const Fused1DArgs& a0, int cus, hipStream_t st) {
     Fused1DArgs a = a0;
     if (a.nitems <= 0) return hipSuccess;
     int64_t nwg = a.nitems < cus ? a.nitems : cus;
     a.per_wg = (a.nitems + nwg - 1) / nwg;
     nwg = (a.nitems + a.per_wg - 1) / a.per_wg;
-    hipLaunchKernelGGL((conv8k_kernel<CT, GQ, GV>), dim3((unsigned)nwg), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((conv8k_kernel<CT, GQ, GV, ADJ>), dim3((unsigned)nwg), dim3(512), 0, st, a);
     return hipGetLastError();
 }
 
-template <int R, int T>
+template <int R, int T, int MODE>
 static hipError_t launch_conv(bool gq, bool gv, const Fused1DArgs& a, int cus, hipStream_t st) {
+    constexpr bool ADJ = MODE == MODE_ADJ;
     if constexpr (R == 32 && T != CT_F32) {
         if (a.N == 4096) {  // whole rows: the pipelined kernel
-            if (gq && gv) return launch_8k<T, true, true>(a, cus, st);
-            if (gq) return launch_8k<T, true, false>(a, cus, st);
-            if (gv) return launch_8k<T, false, true>(a, cus, st);
-            return launch_8k<T, false, false>(a, cus, st);
+            if (gq && gv) return launch_8k<T, true, true, ADJ>(a, cus, st);
+            if (gq) return launch_8k<T, true, false, ADJ>(a, cus, st);
+            if (gv) return launch_8k<T, false, true, ADJ>(a, cus, st);
+            return launch_8k<T, false, false, ADJ>(a, cus, st);
         }
     }
-    if (gq && gv) return launch_t<R, T, T, MODE_CONV, true, true>(a, cus, st);
-    if (gq) return launch_t<R, T, T, MODE_CONV, true, false>(a, cus, st);
-    if (gv) return launch_t<R, T, T, MODE_CONV, false, true>(a, cus, st);
-    return launch_t<R, T, T, MODE_CONV, false, false>(a, cus, st);
+    if (gq && gv) return launch_t<R, T, T, MODE, true, true>(a, cus, st);
+    if (gq) return launch_t<R, T, T, MODE, true, false>(a, cus, st);
+    if (gv) return launch_t<R, T, T, MODE, false, true>(a, cus, st);
+    return launch_t<R, T, T, MODE, false, false>(a, cus, st);
 }
 
 template <int R>
@@ -1222,9 +1103,13 @@ static hipError_t launch_r(int dtype, int mode, bool gq, bool gv, const Fused1DA
                            hipStream_t st) {
     switch (mode) {
     case MODE_CONV:
-        if (dtype == CT_F32) return launch_conv<R, CT_F32>(gq, gv, a, cus, st);
-        if (dtype == CT_F16) return launch_conv<R, CT_F16>(gq, gv, a, cus, st);
-        return launch_conv<R, CT_BF16>(gq, gv, a, cus, st);
+        if (dtype == CT_F32) return launch_conv<R, CT_F32, MODE_CONV>(gq, gv, a, cus, st);
+        if (dtype == CT_F16) return launch_conv<R, CT_F16, MODE_CONV>(gq, gv, a, cus, st);
+        return launch_conv<R, CT_BF16, MODE_CONV>(gq, gv, a, cus, st);
+    case MODE_ADJ:
+        if (dtype == CT_F32) return launch_conv<R, CT_F32, MODE_ADJ>(gq, gv, a, cus, st);
+        if (dtype == CT_F16) return launch_conv<R, CT_F16, MODE_ADJ>(gq, gv, a, cus, st);
+        return launch_conv<R, CT_BF16, MODE_ADJ>(gq, gv, a, cus, st);
     case MODE_FILTER:
         if (dtype == CT_F32) return launch_t<R, CT_F32, CT_F32, MODE_FILTER, false, false>(a, cus, st);
         if (dtype == CT_F16) return launch_t<R, CT_F32, CT_F16, MODE_FILTER, false, false>(a, cus, st);

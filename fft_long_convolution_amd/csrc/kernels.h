@@ -5,15 +5,21 @@
 
 namespace lcv {
 
-enum Mode1D { MODE_CONV = 0, MODE_FILTER = 1, MODE_ROW = 2, MODE_ROWFWD = 3 };
+// ADJ is the adjoint of CONV: the same chain with the conjugate filter spectrum (a correlation,
+// whose causal truncation keeps the outputs that depend on later inputs).
+enum Mode1D { MODE_CONV = 0, MODE_FILTER = 1, MODE_ROW = 2, MODE_ROWFWD = 3, MODE_ADJ = 4 };
 
 struct Fused1DArgs {
-    const void* u;       // CONV: u [B][H][N]; FILTER: k [H][N]; ROW/ROWFWD: workspace rows
-    const void* q;       // CONV: pre-gate (nullable)
-    const void* v;       // CONV: post-gate (nullable)
-    void* y;             // CONV: y; FILTER/ROWFWD: k_f; ROW: workspace rows (in place)
-    const void* kf;      // CONV/ROW: k_f
-    const void* D;       // CONV/ROW: D [H]
+    const void* u;       // CONV: u [B][H][N]; FILTER: k [H][N]; ROW/ROWFWD: workspace rows;
+                         // ADJ: dy;  DK: u
+    const void* q;       // CONV: pre-gate (nullable); ADJ: v (nullable); DK: q (nullable)
+    const void* v;       // CONV: post-gate (nullable); ADJ: q (du = q dx; nullable); DK: v (nullable)
+    const void* e2;      // ADJ: u (dq = u dx, used when v above is set); DK: dy
+    void* y;             // CONV: y; FILTER/ROWFWD: k_f; ROW: workspace rows (in place);
+                         // ADJ: du;  DK: dk [H][N] fp32 (nullable)
+    void* y2;            // ADJ: dq (when v above is set);  DK: dD [H] fp32 (nullable)
+    const void* kf;      // CONV/ROW/ADJ: k_f
+    const void* D;       // CONV/ROW/ADJ: D [H]
     const void* tables;  // fused-path tables for (R, compute type)
     int64_t B, H, N;     // CONV/FILTER shape
     int64_t nitems;      // CONV: pairs; FILTER: channels; ROW/ROWFWD: rows
@@ -27,9 +33,15 @@ struct Fused1DArgs {
 
 // dtype: io element type (ComputeType values); the compute type is fp32 for fp32 io and for
 // the filter transforms, else the io type.
-// gq / gv: the pre-gate q / post-gate v pointers are set (conv mode).
+// gq / gv: the pre-gate q / post-gate v pointers are set (conv and adj modes).
 hipError_t launch_fused1d(int R, int dtype, int mode, bool gq, bool gv, const Fused1DArgs& a,
                           int cus, hipStream_t stream);
+
+// Filter gradient: per channel h (items = channels), the sum over batch pairs of
+// conj(DFT(q u)) DFT(dy v), inverse-transformed; dk[h][n] for n < N and dD[h] = dk[h][0]
+// (fp32).  gq / gv: q / v pointers are set.
+hipError_t launch_dk1d(int R, int dtype, bool gq, bool gv, const Fused1DArgs& a, int cus,
+                       hipStream_t stream);
 
 struct ColArgs {
     const void* u;       // pass A input: u [B][H][N] (CONV) or k [H][N] (FILTER)

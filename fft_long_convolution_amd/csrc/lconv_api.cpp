@@ -221,6 +221,80 @@ lconv_status_t lconv_fftconv_fwd(const void* u, const void* k_f, const void* D, 
     return LCONV_SUCCESS;
 }
 
+lconv_status_t lconv_fftconv_bwd(const void* dy, const void* u, const void* k_f, const void* D, const void* q,
+                                 const void* v, void* du, void* dq, void* dv, float* dk, float* dD, int64_t B,
+                                 int64_t H, int64_t N, lconv_dtype_t dtype, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
+    if (B < 0 || H < 0 || N < 0) return LCONV_ERR_INVALID_SHAPE;
+    int64_t elems, t, hn;
+    if (!mul_ok(B, H, &t) || !mul_ok(t, N, &elems) || !mul_ok(elems, 8, &t) || !mul_ok(H, N, &hn) ||
+        !mul_ok(hn, 8, &t))
+        return LCONV_ERR_INVALID_SHAPE;
+    if (H == 0 || N == 0) return LCONV_SUCCESS;
+    if (!n_supported(N) || N > LCONV_BWD_MAX_N) return LCONV_ERR_UNSUPPORTED;
+    if (!q) dq = nullptr;  // ignored without the gate it belongs to
+    if (!v) dv = nullptr;
+    if (B == 0) {          // empty batch: the filter gradients are zero sums
+        if ((dk && !aligned16(dk)) || (dD && !aligned16(dD))) return LCONV_ERR_MISALIGNED;
+        if (dk && hipMemsetAsync(dk, 0, (size_t)hn * 4, stream) != hipSuccess) return LCONV_ERR_HIP;
+        if (dD && hipMemsetAsync(dD, 0, (size_t)H * 4, stream) != hipSuccess) return LCONV_ERR_HIP;
+        return LCONV_SUCCESS;
+    }
+    if (!dy || !u || !k_f || !D || !du || (q && !dq) || (v && !dv)) return LCONV_ERR_NULL_POINTER;
+    const void* ptrs[] = {dy, u, k_f, D, q, v, du, dq, dv, dk, dD};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return LCONV_ERR_MISALIGNED;
+    const size_t es = dtype_size(dtype), act = (size_t)elems * es;
+    const size_t kf_bytes = lconv_filter_fft_bytes(H, N, dtype);
+    if (kf_bytes == 0) return LCONV_ERR_INVALID_SHAPE;
+    // every output against every input and every other output
+    const void* ins[] = {dy, u, k_f, D, q, v};
+    const size_t in_sz[] = {act, act, kf_bytes, (size_t)H * es, act, act};
+    const void* outs[] = {du, dq, dv, dk, dD};
+    const size_t out_sz[] = {act, act, act, (size_t)hn * 4, (size_t)H * 4};
+    for (int o = 0; o < 5; ++o) {
+        for (int i = 0; i < 6; ++i)
+            if (overlap(outs[o], out_sz[o], ins[i], in_sz[i])) return LCONV_ERR_ALIASING;
+        for (int o2 = o + 1; o2 < 5; ++o2)
+            if (overlap(outs[o], out_sz[o], outs[o2], out_sz[o2])) return LCONV_ERR_ALIASING;
+    }
+    Plan1D p;
+    make_plan_1d(N, &p);
+    hipError_t err = hipSuccess;
+    const int cus = device_cu_count(&err);
+    if (!cus) return LCONV_ERR_HIP;
+    const int ct = dtype == LCONV_F32 ? CT_F32 : (int)dtype;
+    const void* tabs = fused_tables(p.R, ct, &err);
+    if (!tabs) return LCONV_ERR_HIP;
+    const int64_t seqs = pairs_per_channel(B) * H;
+    Fused1DArgs base{};
+    base.kf = k_f; base.D = D; base.tables = tabs;
+    base.B = B; base.H = H; base.N = N;
+    base.inv_m = 1.0f / (float)p.M; base.M = p.M; base.M1 = 1;
+    // dv = dy (.) (k * x + D x): the forward convolution with dy as its post-gate
+    if (v) {
+        Fused1DArgs a = base;
+        a.u = u; a.q = q; a.v = dy; a.y = dv; a.nitems = seqs;
+        if (launch_fused1d(p.R, dtype, MODE_CONV, q != nullptr, true, a, cus, stream) != hipSuccess)
+            return LCONV_ERR_HIP;
+    }
+    // du = q (.) dx, dq = u (.) dx: the adjoint chain on ds = dy (.) v
+    {
+        Fused1DArgs a = base;
+        a.u = dy; a.q = v; a.v = q; a.e2 = u; a.y = du; a.y2 = dq; a.nitems = seqs;
+        if (launch_fused1d(p.R, dtype, MODE_ADJ, v != nullptr, q != nullptr, a, cus, stream) != hipSuccess)
+            return LCONV_ERR_HIP;
+    }
+    // dk, dD: per channel, the batch sum of the correlation of ds with x
+    if (dk || dD) {
+        Fused1DArgs a = base;
+        a.u = u; a.q = q; a.e2 = dy; a.v = v; a.y = dk; a.y2 = dD; a.nitems = H;
+        if (launch_dk1d(p.R, dtype, q != nullptr, v != nullptr, a, cus, stream) != hipSuccess)
+            return LCONV_ERR_HIP;
+    }
+    return LCONV_SUCCESS;
+}
+
 lconv_status_t lconv_filter_fft2d(const void* k, void* k_f, int64_t C, int64_t S, lconv_dtype_t dtype,
                                   hipStream_t stream) {
     if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;

@@ -5,8 +5,8 @@ C ABI declared in include/lconv.h.  torch provides device memory and the current
 There is no CPU fallback: if the library is missing, importing the entry points fails loudly.
 
 Raw entry points keep the C names (``lconv_filter_fft``, ``lconv_fftconv_fwd``, ...), taking
-integer device pointers.  ``filter_fft``, ``fftconv``, ``filter_fft2d`` and ``fftconv2d`` are
-convenience wrappers over torch tensors.
+integer device pointers.  ``filter_fft``, ``fftconv``, ``fftconv_bwd``, ``filter_fft2d`` and
+``fftconv2d`` are convenience wrappers over torch tensors.
 """
 from __future__ import annotations
 
@@ -50,6 +50,7 @@ def load(path: str = LIB_PATH):
         "lconv_filter_fft2d_bytes": (sz, [i64, i64, i]),
         "lconv_filter_fft": (i, [vp, vp, i64, i64, i, vp, sz, vp]),
         "lconv_fftconv_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i, vp, sz, vp]),
+        "lconv_fftconv_bwd": (i, [vp] * 11 + [i64, i64, i64, i, vp]),
         "lconv_filter_fft2d": (i, [vp, vp, i64, i64, i, vp]),
         "lconv_fftconv2d_fwd": (i, [vp, vp, vp, vp, i64, i64, i64, i, vp]),
         "lconv_status_string": (ctypes.c_char_p, [i]),
@@ -96,6 +97,10 @@ def lconv_filter_fft(k, k_f, H, N, dtype, workspace, workspace_bytes, stream):
 def lconv_fftconv_fwd(u, k_f, D, y, q, v, B, H, N, dtype, workspace, workspace_bytes, stream):
     return load().lconv_fftconv_fwd(u, k_f, D, y, q, v, B, H, N, dtype, workspace,
                                     workspace_bytes, stream)
+
+
+def lconv_fftconv_bwd(dy, u, k_f, D, q, v, du, dq, dv, dk, dD, B, H, N, dtype, stream):
+    return load().lconv_fftconv_bwd(dy, u, k_f, D, q, v, du, dq, dv, dk, dD, B, H, N, dtype, stream)
 
 
 def lconv_filter_fft2d(k, k_f, C, S, dtype, stream):
@@ -176,6 +181,25 @@ def fftconv(u, k_f, D, q=None, v=None, out=None, stream=None):
     _check(lconv_fftconv_fwd(_ptr(u), _ptr(k_f), _ptr(D), _ptr(y), _ptr(q), _ptr(v), B, H, N, dt,
                              _ptr(ws), wsb, _stream(stream)), "lconv_fftconv_fwd")
     return y
+
+
+def fftconv_bwd(dy, u, k_f, D, q=None, v=None, need_dk=True, stream=None):
+    """Gradients of y = v * ((k * (q*u))[:N] + D * (q*u)) given dy [B, H, N].
+
+    Returns (du, dq, dv, dk, dD): du, dq, dv in u's dtype (dq is None without q, dv is None
+    without v); dk [H, N] and dD [H] in float32 (None when need_dk is False)."""
+    torch = _torch()
+    B, H, N = u.shape
+    dt = dtype_code(u.dtype)
+    du = torch.empty_like(u)
+    dq = torch.empty_like(u) if q is not None else None
+    dv = torch.empty_like(u) if v is not None else None
+    dk = torch.empty((H, N), dtype=torch.float32, device=u.device) if need_dk else None
+    dD = torch.empty((H,), dtype=torch.float32, device=u.device) if need_dk else None
+    _check(lconv_fftconv_bwd(_ptr(dy), _ptr(u), _ptr(k_f), _ptr(D), _ptr(q), _ptr(v), _ptr(du),
+                             _ptr(dq), _ptr(dv), _ptr(dk), _ptr(dD), B, H, N, dt, _stream(stream)),
+           "lconv_fftconv_bwd")
+    return du, dq, dv, dk, dD
 
 
 def filter_fft2d(k, stream=None):

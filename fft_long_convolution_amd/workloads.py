@@ -172,6 +172,13 @@ def make_1d(spec: Conv1DSpec) -> dict:
     return out
 
 
+def make_grad_1d(spec: Conv1DSpec) -> np.ndarray:
+    """Output gradient dy [B,H,N] ~ N(0,1) in the workload's storage dtype, from its own seeded
+    stream (seed + 500000), so the forward draws are unchanged."""
+    rng = np.random.default_rng(spec.seed + 500000)
+    return to_storage(rng.standard_normal((spec.B, spec.H, spec.N), dtype=np.float32), spec.dtype)
+
+
 def make_2d(spec: Conv2DSpec) -> dict:
     """Draw u, k, D for a 2D workload (draw order: u, k_raw, D)."""
     rng = np.random.default_rng(spec.seed)

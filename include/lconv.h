@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define LCONV_ABI_VERSION 1
+#define LCONV_ABI_VERSION 2
 
 typedef enum { LCONV_F32 = 0, LCONV_F16 = 1, LCONV_BF16 = 2 } lconv_dtype_t;
 
@@ -110,6 +110,36 @@ lconv_status_t lconv_fftconv_fwd(const void* u, const void* k_f, const void* D, 
                                  const void* q, const void* v, int64_t B, int64_t H, int64_t N,
                                  lconv_dtype_t dtype, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream);
+
+/*
+ * Gradients of the gated causal convolution above, given dy = dL/dy (the training path the
+ * FlashFFTConv abstract reports speed-ups for; the FFT convolution is exact, so its gradient is
+ * that of the plain causal sum).  With x = q (.) u and ds = dy (.) v:
+ *   dx[t] = sum_{s >= t} k[h,s-t] ds[s] + D[h] ds[t]     (correlation: conjugate spectrum)
+ *   du = q (.) dx   (du = dx without q)          dq = u (.) dx
+ *   dv = dy (.) ( (k * x)[:N] + D x )            (the forward convolution, gated by dy)
+ *   dk[h,t] = sum_b sum_{s >= t} ds[b,h,s] x[b,h,s-t],   dD[h] = dk[h,0]
+ *   dy, u     [B][H][N] dtype, device
+ *   k_f, D    as for lconv_fftconv_fwd (the same spectrum)
+ *   q, v      [B][H][N] dtype or NULL, as in the forward call
+ *   du        [B][H][N] dtype, written
+ *   dq        [B][H][N] dtype, written; required when q is given, ignored (may be NULL) otherwise
+ *   dv        [B][H][N] dtype, written; required when v is given, ignored (may be NULL) otherwise
+ *   dk        [H][N] fp32, written (overwritten, not accumulated); NULL: not computed
+ *   dD        [H] fp32, written; NULL: not computed
+ * B = 0 writes zeros to dk and dD.  Outputs must not overlap each other or any input.
+ * Arithmetic as in the forward call; dk and dD are summed over the batch in fp32 in the
+ * frequency domain and transformed once per channel.
+ * Supported: N <= 4096 (transform length M <= 8192, one workgroup per transform), N a multiple
+ * of 8; longer sequences return LCONV_ERR_UNSUPPORTED.  No workspace.
+ */
+lconv_status_t lconv_fftconv_bwd(const void* dy, const void* u, const void* k_f, const void* D,
+                                 const void* q, const void* v, void* du, void* dq, void* dv,
+                                 float* dk, float* dD, int64_t B, int64_t H, int64_t N,
+                                 lconv_dtype_t dtype, hipStream_t stream);
+
+/* Largest sequence length lconv_fftconv_bwd supports. */
+#define LCONV_BWD_MAX_N ((int64_t)4096)
 
 /* ---- 2D (HyenaND-style) ------------------------------------------------------------------ */
 

@@ -27,7 +27,7 @@ def test_exports_every_header_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lconv.lconv_abi_version() == 1
+    assert lconv.lconv_abi_version() == 2
     for s in range(8):
         assert lconv.status_string(s)
     assert "unknown" in lconv.status_string(99)
@@ -110,3 +110,46 @@ def test_no_device_gives_hip_error():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert fwd() == HIPERR
+
+
+# more fake addresses for the gradient call (1 MiB apart, far larger than the test shapes)
+G = [0x10000000 + 0x100000 * i for i in range(12)]
+
+
+def bwd(dy=G[0], u=G[1], kf=G[2], D=G[3], q=None, v=None, du=G[4], dq=None, dv=None, dk=None,
+        dD=None, B=2, H=3, N=64, dt=BF16):
+    return lconv.lconv_fftconv_bwd(dy, u, kf, D, q, v, du, dq, dv, dk, dD, B, H, N, dt, None)
+
+
+def test_bwd_validation_errors():
+    assert bwd(dt=5) == UNSUP
+    assert bwd(B=-1) == SHAPE
+    assert bwd(H=2 ** 40, N=2 ** 30) == SHAPE                           # overflow
+    assert bwd(N=12) == UNSUP
+    assert bwd(N=8192) == UNSUP                                            # beyond one workgroup
+    assert bwd(dy=None) == NULLP
+    assert bwd(u=None) == NULLP
+    assert bwd(kf=None) == NULLP
+    assert bwd(D=None) == NULLP
+    assert bwd(du=None) == NULLP
+    assert bwd(q=G[5]) == NULLP                                            # q without dq
+    assert bwd(v=G[6]) == NULLP                                            # v without dv
+    assert bwd(dk=G[7] + 4) == MISAL
+    assert bwd(q=G[5], dq=G[8] + 8) == MISAL
+    assert bwd(du=G[0]) == ALIAS                                           # du == dy
+    assert bwd(q=G[5], dq=G[4] + 16) == ALIAS                              # dq overlaps du
+    assert bwd(dk=G[3]) == ALIAS                                           # dk overlaps D
+    assert bwd(v=G[6], dv=G[2]) == ALIAS                                   # dv overlaps k_f
+    assert bwd(dk=G[7], dD=G[7] + 16) == ALIAS                             # dD inside dk
+
+
+def test_bwd_empty_and_ignored_outputs():
+    assert bwd(H=0) == OK
+    assert bwd(N=0) == OK
+    assert bwd(B=0) == OK                                                  # nothing to zero
+    assert bwd(B=0, dy=None, u=None, du=None) == OK
+    # dq / dv without their gates are ignored: validation passes, and with no device the
+    # call fails only at the first HIP call
+    import torch
+    if not torch.cuda.is_available():
+        assert bwd(dq=G[0]) == HIPERR
