@@ -4,6 +4,10 @@ One step = one lconv_fftconv_fwd call over the whole synthetic batch (load, gate
 transform, spectral product, inverse transform, truncation, skip, gate, store).  The filter
 spectrum is computed once beforehand (timed separately).  Prints ONE JSON line.
 
+The gradient call (lconv_fftconv_bwd: du, dq, dv, dk, dD from a seeded dy) is timed the same
+way on the same inputs and reported in the line's "backward" object (sequence lengths it
+supports, N <= 4096); it is not part of the step.
+
 Algorithmic bytes (what the method must move): (n_in + 1) * B*H*N * s for the activations
 (n_in = 3 gated, 1 otherwise), plus the filter spectrum once at its minimal size
 H*(N+1)*2*s (Hermitian half in the I/O dtype), plus D.  Nominal flops per row:
@@ -30,7 +34,8 @@ METRIC = "fftconv GB/s, TFLOP/s, %roofline at B16\u00b7H768\u00b7N4096 bf16 caus
 # matrix-core op count) per workload; they carry the hash of the kernel sources they were taken
 # on and are ignored once those sources change.
 COUNTER_FILES = {"hyena_gated_bf16_b16_h768_n4096": "profiles/conv8k_hyena_gated_bf16_b16_h768_n4096_counters.md"}
-KERNEL_SOURCES = ("fft_long_convolution_amd/csrc/fused1d.hip", "fft_long_convolution_amd/csrc/lconv_device.h")
+KERNEL_SOURCES = ("fft_long_convolution_amd/csrc/fused1d.hip", "fft_long_convolution_amd/csrc/fused_io.h",
+                  "fft_long_convolution_amd/csrc/lconv_device.h")
 
 
 def kernel_source_hash():
@@ -70,6 +75,16 @@ def algorithmic_bytes(spec):
     act = (n_in + 1) * spec.B * spec.H * spec.N * s
     kf = spec.H * (spec.N + 1) * 2 * s
     return act + kf + spec.H * s
+
+
+def backward_bytes(spec):
+    """Least data the gradient call must move: read dy, u and the gates, write du and one
+    output per gate, read the filter spectrum (Hermitian half) and D, write dk and dD (fp32)."""
+    s = {"f32": 4, "f16": 2, "bf16": 2}[spec.dtype]
+    act = spec.B * spec.H * spec.N * s
+    g = 2 if spec.gated else 0
+    return (2 + g) * act + (1 + g) * act + spec.H * (spec.N + 1) * 2 * s + spec.H * s + \
+        spec.H * (spec.N + 1) * 4
 
 
 def nominal_flops(spec):
@@ -123,6 +138,44 @@ def cpu_baseline(d, budget_s=12.0):
             "sample": f"{nrows} full rows (b,h) of {spec.name}, direct float64 sum, {el:.1f} s"}
 
 
+def time_backward(lconv, wl, spec, u, kf, D, q, v, args):
+    """K timed gradient calls (after W warm-up calls) on the forward's inputs and a seeded dy."""
+    import torch
+    dy = to_dev(wl.make_grad_1d(spec), spec.dtype)
+    du = torch.empty_like(u)
+    dq = torch.empty_like(u) if q is not None else None
+    dv = torch.empty_like(u) if v is not None else None
+    dk = torch.empty((spec.H, spec.N), dtype=torch.float32, device="cuda")
+    dD = torch.empty((spec.H,), dtype=torch.float32, device="cuda")
+    dtc = lconv.dtype_code(u.dtype)
+    stream = torch.cuda.current_stream()
+    p = lambda t: None if t is None else t.data_ptr()
+
+    def call():
+        st = lconv.lconv_fftconv_bwd(dy.data_ptr(), u.data_ptr(), kf.data_ptr(), D.data_ptr(), p(q),
+                                     p(v), du.data_ptr(), p(dq), p(dv), dk.data_ptr(), dD.data_ptr(),
+                                     spec.B, spec.H, spec.N, dtc, stream.cuda_stream)
+        if st != 0:
+            raise lconv.LconvError(st, "lconv_fftconv_bwd")
+    for _ in range(args.warmup):
+        call()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        call()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    nbytes = backward_bytes(spec)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms_per_call": round(ms, 5), "algorithmic_bytes": nbytes, "achieved": round(gbs, 2),
+            "unit": "GB/s", "peak": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "outputs": "du, dq, dv (dtype); dk, dD (fp32)",
+            "launches": "forward kernel gated by dy (dv); adjoint kernel (du, dq); "
+                        "filter-gradient kernel (dk, dD)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +183,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the gradient call's timing")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="run only a plain 256 MiB device copy (reads and writes 256 MiB per "
@@ -253,6 +307,8 @@ def main():
         mf = float(cs["mfma_gflop_executed_per_launch"]) * 1e9 / (avg_ms * 1e-3) / 1e12
         out["mfma"] = {"executed_tflops": round(mf, 1), "peak": MFMA_PEAK[dt],
                        "util": round(mf / MFMA_PEAK[dt], 4), "counters": cs["path"]}
+    if not args.no_bwd and spec.kind == "1d" and spec.N <= 4096:
+        out["backward"] = time_backward(lconv, wl, spec, u, kf, D, q, v, args)
     if not args.no_cpu and spec.kind == "1d":
         out["cpu_baseline"] = cpu_baseline(d, args.cpu_budget)
     print(json.dumps(out), flush=True)
