@@ -85,6 +85,7 @@ typedef struct {
     const int64_t* sel;
     double* out;
     int64_t lo, hi;
+    int64_t L;         /* short-filter sums: filter length (k is [H][L]) */
 } or_job;
 
 static void or_parallel(void* (*fn)(void*), or_job proto, int64_t n, int nthreads) {
@@ -207,7 +208,7 @@ int oracle_conv1d_rows(const void* u, const void* q, const void* v, const void* 
     for (int64_t r = 0; r < nrows; ++r)
         if (rows[2 * r] < 0 || rows[2 * r] >= B || rows[2 * r + 1] < 0 || rows[2 * r + 1] >= H)
             return -1;
-    or_job J = {u, q, v, k, D, dt, B, H, N, rows, out, 0, 0};
+    or_job J = {u, q, v, k, D, dt, B, H, N, rows, out, 0, 0, 0};
     or_parallel(or_rows_worker, J, nrows, nthreads);
     return 0;
 }
@@ -221,8 +222,51 @@ int oracle_conv1d_points(const void* u, const void* q, const void* v, const void
         if (pts[3 * r] < 0 || pts[3 * r] >= B || pts[3 * r + 1] < 0 || pts[3 * r + 1] >= H ||
             pts[3 * r + 2] < 0 || pts[3 * r + 2] >= N)
             return -1;
-    or_job J = {u, q, v, k, D, dt, B, H, N, pts, out, 0, 0};
+    or_job J = {u, q, v, k, D, dt, B, H, N, pts, out, 0, 0, 0};
     or_parallel(or_points_worker, J, npts, nthreads);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* 1D with a short filter (partial convolution: FlashFFTConv abstract)                         */
+/* ------------------------------------------------------------------------------------------ */
+/* The filter has L taps, k[h][0..L), and is zero beyond them; the sequence has N >= 1 positions
+ * (N may be larger or smaller than L).  The plain causal sum then runs over the last L inputs:
+ *     y[b,h,t] = v * ( sum_{s = max(0, t-L+1)}^{t} k[h,t-s] x[b,h,s] + D[h] x[b,h,t] ),
+ * x = q u, in ascending s.  Equal to the full-length sum with k zero-extended to N taps. */
+static void* or_short_points_worker(void* arg) {
+    or_job* J = (or_job*)arg;
+    const int64_t N = J->N, L = J->L;
+    for (int64_t r = J->lo; r < J->hi; ++r) {
+        int64_t b = J->sel[3 * r], h = J->sel[3 * r + 1], t = J->sel[3 * r + 2];
+        int64_t off = (b * J->H + h) * N;
+        int64_t s0 = t - L + 1 > 0 ? t - L + 1 : 0;
+        double a = 0;
+        for (int64_t s = s0; s <= t; ++s) {
+            double xs = or_load(J->u, J->dt, off + s);
+            if (J->q) xs *= or_load(J->q, J->dt, off + s);
+            a += or_load(J->k, J->dt, h * L + (t - s)) * xs;
+        }
+        double xt = or_load(J->u, J->dt, off + t);
+        if (J->q) xt *= or_load(J->q, J->dt, off + t);
+        double val = a + or_load(J->D, J->dt, h) * xt;
+        if (J->v) val *= or_load(J->v, J->dt, off + t);
+        J->out[r] = val;
+    }
+    return NULL;
+}
+
+/* y[b,h,t] with a length-L filter for each (b,h,t) in pts[3*npts]; out is [npts]. */
+int oracle_conv1d_short_points(const void* u, const void* q, const void* v, const void* k,
+                               const void* D, int dt, int64_t B, int64_t H, int64_t N, int64_t L,
+                               const int64_t* pts, int64_t npts, double* out, int nthreads) {
+    if (or_check1d(u, k, D, pts, npts, out, B, H, N, dt) || L < 1) return -1;
+    for (int64_t r = 0; r < npts; ++r)
+        if (pts[3 * r] < 0 || pts[3 * r] >= B || pts[3 * r + 1] < 0 || pts[3 * r + 1] >= H ||
+            pts[3 * r + 2] < 0 || pts[3 * r + 2] >= N)
+            return -1;
+    or_job J = {u, q, v, k, D, dt, B, H, N, pts, out, 0, 0, L};
+    or_parallel(or_short_points_worker, J, npts, nthreads);
     return 0;
 }
 
@@ -300,7 +344,7 @@ int oracle_conv1d_bwd_rows(const void* u, const void* q, const void* v, const vo
         if (rows[2 * r] < 0 || rows[2 * r] >= B || rows[2 * r + 1] < 0 || rows[2 * r + 1] >= H)
             return -1;
     or_bwd_job W;
-    or_job J = {u, q, v, k, D, dt, B, H, N, rows, NULL, 0, 0};
+    or_job J = {u, q, v, k, D, dt, B, H, N, rows, NULL, 0, 0, 0};
     W.j = J;
     W.gy = gy;
     W.du = du;
@@ -364,7 +408,7 @@ int oracle_conv1d_bwd_dk(const void* u, const void* q, const void* v, const void
     for (int64_t r = 0; r < nch; ++r)
         if (chans[r] < 0 || chans[r] >= H) return -1;
     or_bwd_job W;
-    or_job J = {u, q, v, NULL, NULL, dt, B, H, N, chans, NULL, 0, 0};
+    or_job J = {u, q, v, NULL, NULL, dt, B, H, N, chans, NULL, 0, 0, 0};
     W.j = J;
     W.gy = gy;
     W.du = dk;
@@ -430,7 +474,7 @@ int oracle_conv2d_points(const void* u, const void* k, const void* D, int dt, in
             pts[4 * r + 2] < 0 || pts[4 * r + 2] >= S || pts[4 * r + 3] < 0 ||
             pts[4 * r + 3] >= S)
             return -1;
-    or_job J = {u, NULL, NULL, k, D, dt, B, C, S, pts, out, 0, 0};
+    or_job J = {u, NULL, NULL, k, D, dt, B, C, S, pts, out, 0, 0, 0};
     or_parallel(or_points2d_worker, J, npts, nthreads);
     return 0;
 }

@@ -50,6 +50,8 @@ def _load():
         vp, i64, dp, ip = ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         lib.oracle_conv1d_rows.argtypes = [vp, vp, vp, vp, vp, ip, i64, i64, i64, vp, i64, dp, ip]
         lib.oracle_conv1d_points.argtypes = [vp, vp, vp, vp, vp, ip, i64, i64, i64, vp, i64, dp, ip]
+        lib.oracle_conv1d_short_points.argtypes = [vp, vp, vp, vp, vp, ip, i64, i64, i64, i64, vp, i64,
+                                                   dp, ip]
         lib.oracle_conv2d_points.argtypes = [vp, vp, vp, ip, i64, i64, i64, vp, i64, dp, ip]
         lib.oracle_widen.argtypes = [vp, ip, i64, dp]
         lib.oracle_conv1d_bwd_rows.argtypes = [vp, vp, vp, vp, vp, vp, ip, i64, i64, i64, vp, i64,
@@ -138,6 +140,25 @@ def conv1d_points(u, k, D, pts, q=None, v=None, dt=None, nthreads=None):
                                       _threads(nthreads))
     if rc:
         raise ValueError("oracle_conv1d_points rejected its arguments")
+    return out
+
+
+def conv1d_short_points(u, k, D, pts, q=None, v=None, dt=None, nthreads=None):
+    """Single outputs y[b,h,t] with a short filter k [H, L] (zero beyond L taps; N may exceed L):
+    the causal sum over the last L inputs (oracle.c).  Returns float64 [len(pts)]."""
+    dt = _dt_of(u, dt)
+    st = _storage(dt)
+    u, k, D, q, v = (_c(a, st) for a in (u, k, D, q, v))
+    B, H, N = u.shape
+    L = k.shape[1]
+    assert k.shape == (H, L) and D.shape == (H,)
+    pts = np.ascontiguousarray(np.asarray(pts, np.int64).reshape(-1, 3))
+    out = np.empty(pts.shape[0], np.float64)
+    rc = _load().oracle_conv1d_short_points(_ptr(u), _ptr(q), _ptr(v), _ptr(k), _ptr(D), dt, B, H,
+                                            N, L, _ptr(pts), pts.shape[0], out.ctypes.data,
+                                            _threads(nthreads))
+    if rc:
+        raise ValueError("oracle_conv1d_short_points rejected its arguments")
     return out
 
 
