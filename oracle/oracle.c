@@ -271,6 +271,81 @@ int oracle_conv1d_short_points(const void* u, const void* q, const void* v, cons
 }
 
 /* ------------------------------------------------------------------------------------------ */
+/* 1D with a length-M float64 filter, circular (frequency-sparse convolutions)                  */
+/* ------------------------------------------------------------------------------------------ */
+/* kS[h][0..M) is any real float64 filter of the transform length M >= 2N (for a
+ * frequency-sparse convolution: the inverse DFT of the masked filter spectrum).  The output is
+ * the length-M circular convolution of the zero-padded x with kS, truncated to N:
+ *     y[b,h,t] = v * ( sum_{s=0}^{N-1} kS[h,(t-s) mod M] x[b,h,s] + D[h] x[b,h,t] ),  x = q u,
+ * in ascending s.  With kS = k zero-padded this is the causal sum (nothing wraps: M >= 2N). */
+typedef struct {
+    or_job j;
+    const double* kS;
+    int64_t M;
+} or_circ_job;
+
+static void* or_circ_rows_worker(void* arg) {
+    or_circ_job* W = (or_circ_job*)arg;
+    const or_job* J = &W->j;
+    const int64_t N = J->N, M = W->M;
+    double* x = (double*)malloc(sizeof(double) * (size_t)N);
+    for (int64_t r = J->lo; r < J->hi; ++r) {
+        int64_t b = J->sel[2 * r], h = J->sel[2 * r + 1];
+        or_row_x(J, b, h, N, x);
+        const double* k = W->kS + h * M;
+        double d = or_load(J->D, J->dt, h);
+        int64_t off = (b * J->H + h) * N;
+        for (int64_t t = 0; t < N; ++t) {
+            double a = 0;
+            for (int64_t s = 0; s < N; ++s) {
+                int64_t m = t - s;
+                if (m < 0) m += M;
+                a += k[m] * x[s];
+            }
+            double val = a + d * x[t];
+            if (J->v) val *= or_load(J->v, J->dt, off + t);
+            J->out[r * N + t] = val;
+        }
+    }
+    free(x);
+    return NULL;
+}
+
+static void* or_circ_trampoline(void* arg) { return or_circ_rows_worker(arg); }
+
+/* Full rows with a float64 length-M filter kS [H][M] (circular, truncated to N). */
+int oracle_conv1d_circ_rows(const void* u, const void* q, const void* v, const double* kS,
+                            const void* D, int dt, int64_t B, int64_t H, int64_t N, int64_t M,
+                            const int64_t* rows, int64_t nrows, double* out, int nthreads) {
+    if (!u || !kS || !D || !out || (nrows > 0 && !rows)) return -1;
+    if (B < 1 || H < 1 || N < 1 || M < 2 * N || nrows < 0 || dt < 0 || dt > 2) return -1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[2 * r] < 0 || rows[2 * r] >= B || rows[2 * r + 1] < 0 || rows[2 * r + 1] >= H)
+            return -1;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((int64_t)nthreads > nrows) nthreads = (int)(nrows > 0 ? nrows : 1);
+    or_circ_job* jobs = (or_circ_job*)calloc((size_t)nthreads, sizeof(or_circ_job));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    int64_t per = (nrows + nthreads - 1) / nthreads;
+    int used = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        int64_t lo = (int64_t)i * per, hi = lo + per < nrows ? lo + per : nrows;
+        if (lo >= hi) break;
+        or_job J = {u, q, v, NULL, D, dt, B, H, N, rows, out, lo, hi, 0};
+        jobs[used].j = J;
+        jobs[used].kS = kS;
+        jobs[used].M = M;
+        pthread_create(&th[used], NULL, or_circ_trampoline, &jobs[used]);
+        ++used;
+    }
+    for (int i = 0; i < used; ++i) pthread_join(th[i], NULL);
+    free(th);
+    free(jobs);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------ */
 /* 1D backward (gradients of the causal convolution)                                           */
 /* ------------------------------------------------------------------------------------------ */
 /*

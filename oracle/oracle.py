@@ -50,6 +50,8 @@ def _load():
         vp, i64, dp, ip = ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         lib.oracle_conv1d_rows.argtypes = [vp, vp, vp, vp, vp, ip, i64, i64, i64, vp, i64, dp, ip]
         lib.oracle_conv1d_points.argtypes = [vp, vp, vp, vp, vp, ip, i64, i64, i64, vp, i64, dp, ip]
+        lib.oracle_conv1d_circ_rows.argtypes = [vp, vp, vp, dp, vp, ip, i64, i64, i64, i64, vp, i64,
+                                                dp, ip]
         lib.oracle_conv1d_short_points.argtypes = [vp, vp, vp, vp, vp, ip, i64, i64, i64, i64, vp, i64,
                                                    dp, ip]
         lib.oracle_conv2d_points.argtypes = [vp, vp, vp, ip, i64, i64, i64, vp, i64, dp, ip]
@@ -159,6 +161,54 @@ def conv1d_short_points(u, k, D, pts, q=None, v=None, dt=None, nthreads=None):
                                             _threads(nthreads))
     if rc:
         raise ValueError("oracle_conv1d_short_points rejected its arguments")
+    return out
+
+
+def transform_length(N: int) -> int:
+    """The transform length the method uses for N: the power of two M >= max(512, 2N)."""
+    M = 512
+    while M < 2 * N:
+        M *= 2
+    return M
+
+
+def sparse_filter(k, keep, M=None, dt=None):
+    """Frequency-sparse filter (FlashFFTConv abstract: skip blocks of the decomposition): the
+    length-M DFT of the zero-padded filter k [H, N], kept only at frequencies f whose residue
+    f mod R (R = M / 256, the blocks of the M = 256 R decomposition) is in `keep`, then inverse
+    transformed.  `keep` must hold R - r with every r (else the filter would not be real).
+    numpy's FFT serves as the DFT step.  Returns float64 [H, M]."""
+    dt = _dt_of(k, dt)
+    kk = widen(_c(k, _storage(dt)), dt).reshape(k.shape)
+    H, N = kk.shape
+    M = transform_length(N) if M is None else M
+    R = M // 256
+    keep = sorted(set(int(r) for r in keep))
+    if any(r < 0 or r >= R for r in keep) or any((R - r) % R not in keep for r in keep):
+        raise ValueError("keep must be a subset of range(R) closed under r -> (R - r) mod R")
+    mask = np.isin(np.arange(M) % R, keep)
+    pad = np.zeros((H, M))
+    pad[:, :N] = kk
+    return np.fft.ifft(np.fft.fft(pad, axis=1) * mask[None, :], axis=1).real
+
+
+def conv1d_circ_rows(u, kS, D, rows, q=None, v=None, dt=None, nthreads=None):
+    """Full rows of the circular convolution with a float64 filter kS [H, M] (M >= 2N), truncated
+    to N (oracle.c).  Returns float64 [len(rows), N]."""
+    dt = _dt_of(u, dt)
+    st = _storage(dt)
+    u, D, q, v = (_c(a, st) for a in (u, D, q, v))
+    kS = np.ascontiguousarray(kS, np.float64)
+    B, H, N = u.shape
+    M = kS.shape[1]
+    assert kS.shape == (H, M) and D.shape == (H,)
+    rows = np.ascontiguousarray(np.asarray(rows, np.int64).reshape(-1, 2))
+    out = np.empty((rows.shape[0], N), np.float64)
+    rc = _load().oracle_conv1d_circ_rows(_ptr(u), _ptr(q), _ptr(v), kS.ctypes.data, _ptr(D), dt, B,
+                                         H, N, M, _ptr(rows), rows.shape[0], out.ctypes.data,
+                                         _threads(nthreads))
+    if rc:
+        raise ValueError("oracle_conv1d_circ_rows rejected its arguments")
     return out
 
 
