@@ -73,7 +73,7 @@ def algorithmic_bytes(spec):
         return act + kf + spec.C * s
     n_in = 3 if spec.gated else 1
     act = (n_in + 1) * spec.B * spec.H * spec.N * s
-    kf = spec.H * (spec.N + 1) * 2 * s
+    kf = spec.H * (spec.taps + 1) * 2 * s          # the filter's spectrum: taps, not N
     return act + kf + spec.H * s
 
 
@@ -92,8 +92,15 @@ def nominal_flops(spec):
         P = 2 * spec.S
         per = 2 * 2.5 * P * P * math.log2(P * P) + 6 * P * (P // 2 + 1) + 2 * spec.S ** 2
         return per * spec.B * spec.C
-    M = 2 * spec.N
     g = 4 if spec.gated else 2
+    if spec.L:  # partial: one transform pair of length M = 2 C per block of C outputs
+        M = 512
+        while M < 2 * spec.L:
+            M *= 2
+        blocks = -(-spec.N // (M // 2))
+        per = blocks * (2 * 2.5 * M * math.log2(M) + 6 * (M // 2 + 1)) + g * spec.N
+        return per * spec.B * spec.H
+    M = 2 * spec.N
     per = 2 * 2.5 * M * math.log2(M) + 6 * (spec.N + 1) + g * spec.N
     return per * spec.B * spec.H
 
@@ -122,6 +129,22 @@ def cpu_baseline(d, budget_s=12.0):
     if spec.kind == "2d":
         raise NotImplementedError
     n_in = 3 if spec.gated else 1
+    if spec.L:  # short filter: single positions (each costs L multiply-adds)
+        npts = 4096
+        while True:
+            pts = np.stack([rng.integers(0, spec.B, npts), rng.integers(0, spec.H, npts),
+                            rng.integers(0, spec.N, npts)], 1)
+            t0 = time.perf_counter()
+            oracle.conv1d_short_points(d["u"], d["k"], d["D"], pts, q=d["q"], v=d["v"], dt=dt,
+                                       nthreads=cores)
+            el = time.perf_counter() - t0
+            if el >= budget_s or npts >= 1 << 26:
+                break
+            npts = int(max(npts * 2, npts * budget_s / max(el, 1e-3) * 1.05))
+        gbs = npts * (n_in + 1) * s / el / 1e9
+        return {"value": round(gbs, 6), "unit": "GB/s", "cores": cores, "kind": "oracle",
+                "sample": f"{npts} output positions of {spec.name}, direct float64 window sums, "
+                          f"{el:.1f} s"}
     row_bytes = (n_in + 1) * spec.N * s
     # calibrate on a few rows, then size the sample for about budget_s seconds
     nrows = cores
@@ -221,6 +244,21 @@ def main():
         kf = run_filter()
         y = torch.empty_like(u)
         step = lambda: lconv.fftconv2d(u, kf, D, out=y)
+    elif spec.L:  # partial convolution: short filter, any sequence length
+        u, q, v, k, D = (to_dev(d[x], dt) for x in ("u", "q", "v", "k", "D"))
+        run_filter = lambda: lconv.filter_fft(k)
+        kf = run_filter()
+        y = torch.empty_like(u)
+        dtc = lconv.dtype_code(u.dtype)
+        stream = torch.cuda.current_stream()
+        p = lambda t: None if t is None else t.data_ptr()
+
+        def step():
+            st = lconv.lconv_fftconv_partial_fwd(u.data_ptr(), kf.data_ptr(), D.data_ptr(), y.data_ptr(),
+                                                 p(q), p(v), spec.B, spec.H, spec.N, spec.L, dtc,
+                                                 stream.cuda_stream)
+            if st != 0:
+                raise lconv.LconvError(st, "lconv_fftconv_partial_fwd")
     else:
         u, q, v, k, D = (to_dev(d[x], dt) for x in ("u", "q", "v", "k", "D"))
         run_filter = lambda: lconv.filter_fft(k)
@@ -286,7 +324,7 @@ def main():
         "vs_baseline": None,
         "dtype": dt,
         "data": "synthetic",
-        "config": {"workload": spec.name, "B": spec.B,
+        "config": {"workload": spec.name, "B": spec.B, **({"L": spec.L} if getattr(spec, "L", 0) else {}),
                    ("H" if spec.kind == "1d" else "C"): (spec.H if spec.kind == "1d" else spec.C),
                    ("N" if spec.kind == "1d" else "S"): (spec.N if spec.kind == "1d" else spec.S),
                    "gated": bool(getattr(spec, "gated", False)), "parallelism": "none"},
@@ -307,7 +345,7 @@ def main():
         mf = float(cs["mfma_gflop_executed_per_launch"]) * 1e9 / (avg_ms * 1e-3) / 1e12
         out["mfma"] = {"executed_tflops": round(mf, 1), "peak": MFMA_PEAK[dt],
                        "util": round(mf / MFMA_PEAK[dt], 4), "counters": cs["path"]}
-    if not args.no_bwd and spec.kind == "1d" and spec.N <= 4096:
+    if not args.no_bwd and spec.kind == "1d" and spec.N <= 4096 and not spec.L:
         out["backward"] = time_backward(lconv, wl, spec, u, kf, D, q, v, args)
     if not args.no_cpu and spec.kind == "1d":
         out["cpu_baseline"] = cpu_baseline(d, args.cpu_budget)

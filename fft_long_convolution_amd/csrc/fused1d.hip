@@ -26,34 +26,46 @@
 
 namespace lcv {
 
-// MODE: conv / filter / row / row-forward / adjoint.  GQ, GV: pre-gate and post-gate present
-// (conv, adjoint).  The adjoint runs the convolution chain on dy (pre-gated by v) with the
-// conjugate spectrum, which turns the causal sum into the correlation sum over later positions,
-// and writes two gated copies of the result: du = q dx and dq = u dx.
+// MODE: conv / filter / row / row-forward / adjoint / partial.  GQ, GV: pre-gate and post-gate
+// present (conv, adjoint, partial).  The adjoint runs the convolution chain on dy (pre-gated by v)
+// with the conjugate spectrum, which turns the causal sum into the correlation sum over later
+// positions, and writes two gated copies of the result: du = q dx and dq = u dx.
+// The partial mode (a filter of at most M/2 taps on a sequence of any length) takes one block of
+// C = M/2 output positions per item: the window [jC - C, jC + C) of the input fills the whole
+// transform, and the upper half of the circular result is exactly the block's linear
+// convolution (the lower half, where the window wraps, is not computed).
 template <int R, int CT, int IO, int MODE, bool GQ, bool GV>
 __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
     constexpr int P = 32 / R;                  // sequences per workgroup iteration
     constexpr int M = 256 * R;
+    constexpr int C = M / 2;                   // partial mode: output positions per item
     constexpr bool ADJ = MODE == MODE_ADJ;
-    constexpr bool CONV = MODE == MODE_CONV || ADJ;  // batch-row input and output
+    constexpr bool PART = MODE == MODE_PART;
+    constexpr bool CONV = MODE == MODE_CONV || ADJ;  // batch-row input and output, half input
+    constexpr bool BATCH = CONV || PART;             // batch rows, gates, filter per channel
     constexpr bool HALF_IN = (CONV || MODE == MODE_FILTER);
-    constexpr bool HALF_OUT = CONV;
-    constexpr bool INV = (CONV || MODE == MODE_ROW);
+    constexpr bool HALF_OUT = BATCH;
+    constexpr bool INV = (BATCH || MODE == MODE_ROW);
     constexpr int NIN = HALF_IN ? R / 2 : R;   // nonzero n1 rows
     constexpr int NOUT = HALF_OUT ? R / 2 : R; // n1 rows produced
+    constexpr int OUT0 = PART ? R / 2 : 0;     // first n1 row produced
     constexpr int KCF = (R + 15) / 16;         // table grid (full variant)
     constexpr int KC1 = (NIN + 15) / 16;
     constexpr int RB1 = (R + 15) / 16;
     constexpr int KC3 = (R + 15) / 16;
     constexpr int RB3 = (NOUT + 15) / 16;
+    constexpr int RB3_0 = OUT0 / 16;           // first I3 row block of the table used
     constexpr int EW = CT == CT_F32 ? 2 : 1;   // LDS words per complex element
     constexpr int SV = 260;                    // V: row stride (elements) per n1 row
     constexpr int ST = 324, SR = 20;           // XY: tile stride, row stride inside a tile
     constexpr int SO = 260;                    // O: row stride (complex fp32)
     constexpr int V_W = P * NIN * SV * EW;
     constexpr int XY_W = 32 * ST * EW;
-    // fp32 row pass: O (same element size as V) aliases V; both are used wave-locally
-    constexpr bool O_ALIAS = (MODE == MODE_ROW && CT == CT_F32);
+    // fp32 row and partial passes: O (same element size as V) aliases V; both are used
+    // wave-locally, and O then keeps V's rows per sequence so that a wave's O rows lie in its
+    // own V columns
+    constexpr bool O_ALIAS = ((MODE == MODE_ROW || PART) && CT == CT_F32);
+    constexpr int OSEQ = O_ALIAS ? NIN : NOUT; // O rows per sequence
     constexpr int O_W = (INV && !O_ALIAS) ? P * NOUT * SO * 2 : 0;
     constexpr bool RES = (CT != CT_F32);       // matrix images resident in registers
     constexpr int IMG = ImgBytes<CT>::value;
@@ -68,13 +80,13 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
     constexpr int BPW = NBLK / 8;              // blocks per wave
     // The radix-R blocks (F1, I3) are shared by all waves: on the convolution path they live in
     // LDS (copied once), which keeps the per-tile blocks in registers without spills.
-    constexpr bool IMG_LDS = RES && (CONV || MODE == MODE_ROW);
+    constexpr bool IMG_LDS = RES && (BATCH || MODE == MODE_ROW);
     constexpr int IMGS_W = IMG_LDS ? (T_F2 - T_F1) / 4 : 0;
     constexpr int IOW = IO == CT_F32 ? 2 : 1;  // uint4 per 8 io elements
     // One sequence per iteration (R = 32) and 16-bit spectra: the filter spectrum of the
     // current channel stays in LDS and is reloaded only when the channel changes (consecutive
     // items are the batch pairs of one channel).
-    constexpr bool KF_LDS = CONV && R == 32 && IO != CT_F32;
+    constexpr bool KF_LDS = BATCH && R == 32 && IO != CT_F32;
     constexpr int KF_W = KF_LDS ? 32 * 64 * 4 : 0;
 
     __shared__ __attribute__((aligned(16))) uint32_t lds[V_W + XY_W + O_W + IMGS_W + KF_W];
@@ -120,7 +132,8 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
 #pragma unroll
                 for (int rb = 0; rb < RB3; ++rb)
 #pragma unroll
-                    for (int kc = 0; kc < KC3; ++kc) mi3[rb][kc] = load_img<CT>(tab + T_I3, rb * KCF + kc, lane);
+                    for (int kc = 0; kc < KC3; ++kc)
+                        mi3[rb][kc] = load_img<CT>(tab + T_I3, (RB3_0 + rb) * KCF + kc, lane);
             }
         }
     }
@@ -128,9 +141,9 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
         if constexpr (IMG_LDS) return load_img_lds<CT>(IMGS, rb * KCF + kc, lane);
         else return RES ? mf1[rb][kc] : load_img<CT>(tab + T_F1, rb * KCF + kc, lane);
     };
-    auto I3 = [&](int rb, int kc) LCV_INLINE {
-        if constexpr (IMG_LDS) return load_img_lds<CT>(IMGS + (T_I3 - T_F1) / 4, rb * KCF + kc, lane);
-        else return RES ? mi3[rb][kc] : load_img<CT>(tab + T_I3, rb * KCF + kc, lane);
+    auto I3 = [&](int rb, int kc) LCV_INLINE {  // rb counts from the first row block produced
+        if constexpr (IMG_LDS) return load_img_lds<CT>(IMGS + (T_I3 - T_F1) / 4, (RB3_0 + rb) * KCF + kc, lane);
+        else return RES ? mi3[rb][kc] : load_img<CT>(tab + T_I3, (RB3_0 + rb) * KCF + kc, lane);
     };
     auto F2 = [&](int i) LCV_INLINE { return RES ? mf2[i] : load_img<CT>(tab + T_F2, (wave * 4 + i) % R, lane); };
     auto F3 = [&](int i) LCV_INLINE { return RES ? mf3[i] : load_img<CT>(tab + T_F3, (wave * 4 + i) % R, lane); };
@@ -148,6 +161,24 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
         const uint32_t it = (uint32_t)item, hh = it / Bp;
         h = hh;
         b = 2 * (int64_t)(it - hh * Bp);
+    };
+    // PART: the sequences of a channel are its (batch row b, block j) windows, s = b nch + j; an
+    // item is a pair of consecutive sequences (s0, s0 + 1) of one channel, so two blocks of one
+    // row share a transform when the batch is odd or 1.  item -> (channel h, first sequence s0).
+    const uint32_t nch = (uint32_t)(PART ? a.nchunk : 1);
+    const uint32_t nseq = (uint32_t)(PART ? a.B * a.nchunk : 1);   // sequences per channel
+    const uint32_t sp = (nseq + 1) / 2;                              // sequence pairs per channel
+    auto decode_part = [&](int64_t item, int64_t& h, int64_t& s0) LCV_INLINE {
+        const uint32_t it = (uint32_t)item, hh = it / sp;
+        h = hh;
+        s0 = 2 * (int64_t)(it - hh * sp);
+    };
+    // channel of a CONV or PART item
+    auto channel_of = [&](int64_t item) LCV_INLINE {
+        int64_t h, b;
+        if constexpr (PART) decode_part(item, h, b);
+        else decode(item, h, b);
+        return h;
     };
     // ROW/ROWFWD item -> (channel h, row k_hi)
     auto decode_row = [&](int64_t item, int64_t& h, int64_t& khi) LCV_INLINE {
@@ -194,10 +225,47 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
             ok1 = false;
         }
     };
+    // PART: for each sequence (b, j) of the item's pair, the slot's window half `half` (0: the
+    // previous block, 1: block j) is position (j - 1 + half) C + n0_io of row b; outside [0, N),
+    // or past the channel's last sequence, it reads as zero and is never stored.  The two
+    // sequences can lie in different rows at different positions: ok0 and ok1 are independent.
+    auto part_offsets = [&](int64_t item, int half, int64_t& o0, int64_t& o1, bool& ok0, bool& ok1) LCV_INLINE {
+        int64_t itc = item < last ? item : last - 1;
+        if constexpr (R >= 4) itc = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)itc);
+        int64_t h, s0;
+        decode_part(itc, h, s0);
+        auto one = [&](int64_t sq, int64_t& o, bool& ok) LCV_INLINE {
+            const bool valid = sq < (int64_t)nseq;
+            const uint32_t sc = (uint32_t)(valid ? sq : s0), b = sc / nch, j = sc - b * nch;
+            const int64_t pos = ((int64_t)j - 1 + half) * C + n0_io;
+            ok = item < last && valid && pos >= 0 && pos < a.N;
+            const int64_t posc = pos < 0 ? 0 : (pos < a.N ? pos : a.N - 8);
+            o = ((int64_t)b * a.H + h) * a.N + posc;
+        };
+        one(s0, o0, ok0);
+        one(s0 + 1, o1, ok1);
+    };
     // Software pipeline: u, q of the NEXT iteration and v of this one are in flight while the
-    // transforms run, so HBM latency overlaps the work.
-    uint4 ru[2][IOW], rq[2][IOW], rv[2][IOW];
+    // transforms run, so HBM latency overlaps the work.  PART holds both window halves
+    // (index 2 half + row).
+    constexpr int NRAW = PART ? 4 : 2;
+    uint4 ru[NRAW][IOW], rq[NRAW][IOW], rv[2][IOW];
     auto issue_in = [&](int64_t it_base) LCV_INLINE {
+        if constexpr (PART) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                int64_t o0, o1;
+                bool k0, k1;
+                part_offsets(it_base + p_io, half, o0, o1, k0, k1);
+                load_raw<IO>(a.u, o0, ru[2 * half]);
+                load_raw<IO>(a.u, o1, ru[2 * half + 1]);
+                if constexpr (GQ) {
+                    load_raw<IO>(a.q, o0, rq[2 * half]);
+                    load_raw<IO>(a.q, o1, rq[2 * half + 1]);
+                }
+            }
+            return;
+        }
         int64_t o0, o1;
         bool k0, k1;
         io_offsets(it_base + p_io, o0, o1, k0, k1);
@@ -210,7 +278,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
             }
         }
     };
-    if constexpr (HALF_IN) issue_in(first);
+    if constexpr (HALF_IN || PART) issue_in(first);
     int64_t kf_h = -1;   // channel whose spectrum KFL holds (wave-uniform)
 
     // One iteration.  FULL: every slot is in range (no stores need guarding).
@@ -263,6 +331,46 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                 ((uint4*)dst)[0] = w0;
                 ((uint4*)dst)[1] = w1;
             }
+        } else if constexpr (PART) {
+            // both window halves of the slot: rows n1 < R/2 (previous block), then n1 >= R/2
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                int64_t o0, o1;
+                bool ok0, ok1;
+                part_offsets(it0 + p_io, half, o0, o1, ok0, ok1);
+                float xr[8], xi[8];
+                unpack_raw<IO>(ru[2 * half], xr);
+                unpack_raw<IO>(ru[2 * half + 1], xi);
+                if constexpr (GQ) {
+                    float t[8];
+                    unpack_raw<IO>(rq[2 * half], t);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) xr[i] *= t[i];
+                    unpack_raw<IO>(rq[2 * half + 1], t);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) xi[i] *= t[i];
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    xr[i] = ok0 ? xr[i] : 0.f;
+                    xi[i] = ok1 ? xi[i] : 0.f;
+                }
+                const int n0 = n0_io + half * C;
+                uint32_t* dst = V + ((p_io * NIN + (n0 >> 8)) * SV + (n0 & 255)) * EW;
+                if constexpr (CT == CT_F32) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        ((float4*)dst)[i] = make_float4(xr[2 * i], xi[2 * i], xr[2 * i + 1], xi[2 * i + 1]);
+                } else {
+                    uint4 w0, w1;
+                    w0.x = pack2<CT>(xr[0], xi[0]); w0.y = pack2<CT>(xr[1], xi[1]);
+                    w0.z = pack2<CT>(xr[2], xi[2]); w0.w = pack2<CT>(xr[3], xi[3]);
+                    w1.x = pack2<CT>(xr[4], xi[4]); w1.y = pack2<CT>(xr[5], xi[5]);
+                    w1.z = pack2<CT>(xr[6], xi[6]); w1.w = pack2<CT>(xr[7], xi[7]);
+                    ((uint4*)dst)[0] = w0;
+                    ((uint4*)dst)[1] = w1;
+                }
+            }
         } else {  // ROW / ROWFWD: one complex row of 8192 from the workspace (P == 1)
             const uint32_t* src = (const uint32_t*)a.u + it0 * (int64_t)M * EW;
 #pragma unroll
@@ -285,8 +393,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
             // tiles), so no barrier is needed; the loads are waited for inside the branch,
             // which is taken once per channel.
             const int64_t item = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)(it0 < last ? it0 : last - 1));
-            int64_t h, b;
-            decode(item, h, b);
+            const int64_t h = channel_of(item);
             if (h != kf_h) {
                 // D is folded in here, (K + D) / M, rounded once to the spectrum's type
                 const uint4* src = (const uint4*)((const uint32_t*)a.kf + h * M) + wave * 4 * 64 + lane;
@@ -310,9 +417,8 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                 int64_t item = it0 + (wave * 4 + 2 * s) / R;
                 item = item < last ? item : last - 1;
                 int64_t h;
-                if constexpr (CONV) {
-                    int64_t b;
-                    decode(item, h, b);
+                if constexpr (BATCH) {
+                    h = channel_of(item);
                     bases[s] = h * M;
                 } else {
                     int64_t khi;
@@ -328,10 +434,11 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                 load_raw_c4<IO>(a.kf, bases[s] + ((int64_t)k1 * 64 + lane) * 4, rk[i]);
             }
         }
-        if constexpr (CONV && GV) {
+        if constexpr (BATCH && GV) {
             int64_t o0, o1;
             bool k0, k1;
-            io_offsets(it0 + p_io, o0, o1, k0, k1);
+            if constexpr (PART) part_offsets(it0 + p_io, 1, o0, o1, k0, k1);  // the block's outputs
+            else io_offsets(it0 + p_io, o0, o1, k0, k1);
             load_raw<IO>(a.v, o0, rv[0]);
             load_raw<IO>(a.v, o1, rv[1]);
         }
@@ -506,7 +613,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
             interleave(std::integral_constant<int, 10>{});
             // the next iteration's u, q go out here (consumed in its P0): late enough to keep
             // their registers out of the busiest part of this phase
-            if constexpr (HALF_IN) issue_in(it0 + P);  // clamped: harmless past the end
+            if constexpr (HALF_IN || PART) issue_in(it0 + P);  // clamped: harmless past the end
             __builtin_amdgcn_sched_barrier(0);
             mstage(G0{}, S4{}); vstep(G1{}, S3{});
             interleave(std::integral_constant<int, 10>{});
@@ -575,9 +682,10 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                             constexpr int rb = decltype(rr)::value;
 #pragma unroll
                             for (int j = 0; j < 4; ++j) {
-                                const int n1 = 16 * rb + 4 * g + j;
-                                if (n1 < NOUT)
-                                    *(float2*)(O + 2 * ((p * NOUT + n1) * SO + 16 * b + c)) =
+                                // output row: transform row n1 = 16 (RB3_0 + rb) + 4g + j, minus OUT0
+                                const int o = 16 * (RB3_0 + rb) + 4 * g + j - OUT0;
+                                if (o >= 0 && o < NOUT)
+                                    *(float2*)(O + 2 * ((p * OSEQ + o) * SO + 16 * b + c)) =
                                         make_float2(acc[ci][rb].re[j], acc[ci][rb].im[j]);
                             }
                         });
@@ -588,11 +696,12 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
             __builtin_amdgcn_sched_barrier(0);
 
             // ================= P4: epilogue ==================================================
-            if constexpr (CONV) {
+            if constexpr (BATCH) {
                 int64_t o0, o1;
                 bool ok0, ok1;
-                io_offsets(it0 + p_io, o0, o1, ok0, ok1);
-                const float4* src = (const float4*)(O + 2 * ((p_io * NOUT + (n0_io >> 8)) * SO + (n0_io & 255)));
+                if constexpr (PART) part_offsets(it0 + p_io, 1, o0, o1, ok0, ok1);  // block outputs
+                else io_offsets(it0 + p_io, o0, o1, ok0, ok1);
+                const float4* src = (const float4*)(O + 2 * ((p_io * OSEQ + (n0_io >> 8)) * SO + (n0_io & 255)));
                 float yr[8], yi[8];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -626,14 +735,20 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
 #pragma unroll
                     for (int i = 0; i < 8; ++i) yi[i] *= t[i];
                 }
-                // odd B, partial iteration: the masked second row must not overwrite the first
-                if constexpr (!FULL) {
+                if constexpr (PART) {
+                    // the two sequences are stored independently (different rows or blocks)
+                    if (ok0) store8<IO>(a.y, o0, yr);
+                    if (ok1) store8<IO>(a.y, o1, yi);
+                } else {
+                    // odd B, partial iteration: the masked second row must not overwrite the first
+                    if constexpr (!FULL) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) yi[i] = o1 != o0 ? yi[i] : yr[i];
-                }
-                if (FULL || ok0) {
-                    store8<IO>(a.y, o0, yr);
-                    store8<IO>(a.y, o1, yi);
+                        for (int i = 0; i < 8; ++i) yi[i] = o1 != o0 ? yi[i] : yr[i];
+                    }
+                    if (FULL || ok0) {
+                        store8<IO>(a.y, o0, yr);
+                        store8<IO>(a.y, o1, yi);
+                    }
                 }
             } else {  // ROW: complex row back to the workspace, in compute type
                 uint32_t* dstrow = (uint32_t*)a.y + it0 * (int64_t)M * EW;
@@ -641,7 +756,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                 for (int r = 0; r < 2; ++r) {
                     int pp, n0;
                     slot(lane + 64 * r, pp, n0);
-                    const float4* src = (const float4*)(O + 2 * ((n0 >> 8) * SO + (n0 & 255)));
+                    const float4* src = (const float4*)(O + 2 * ((n0 >> 8) * SO + (n0 & 255)));  // P == 1
                     float w[16];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -669,7 +784,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
 
     // Full iterations (every slot in range) run without store guards; a partial last
     // iteration, or a length that does not fill the half transform, takes the guarded body.
-    const bool whole_rows = !HALF_IN || a.N == M / 2;
+    const bool whole_rows = !PART && (!HALF_IN || a.N == M / 2);
     int64_t it0 = first;
     if (whole_rows) {
         for (; it0 + P <= last; it0 += P) body(it0, std::integral_constant<bool, true>{});
@@ -1098,6 +1213,14 @@ static hipError_t launch_conv(bool gq, bool gv, const Fused1DArgs& a, int cus, h
     return launch_t<R, T, T, MODE, false, false>(a, cus, st);
 }
 
+template <int R, int T>
+static hipError_t launch_part(bool gq, bool gv, const Fused1DArgs& a, int cus, hipStream_t st) {
+    if (gq && gv) return launch_t<R, T, T, MODE_PART, true, true>(a, cus, st);
+    if (gq) return launch_t<R, T, T, MODE_PART, true, false>(a, cus, st);
+    if (gv) return launch_t<R, T, T, MODE_PART, false, true>(a, cus, st);
+    return launch_t<R, T, T, MODE_PART, false, false>(a, cus, st);
+}
+
 template <int R>
 static hipError_t launch_r(int dtype, int mode, bool gq, bool gv, const Fused1DArgs& a, int cus,
                            hipStream_t st) {
@@ -1110,6 +1233,10 @@ static hipError_t launch_r(int dtype, int mode, bool gq, bool gv, const Fused1DA
         if (dtype == CT_F32) return launch_conv<R, CT_F32, MODE_ADJ>(gq, gv, a, cus, st);
         if (dtype == CT_F16) return launch_conv<R, CT_F16, MODE_ADJ>(gq, gv, a, cus, st);
         return launch_conv<R, CT_BF16, MODE_ADJ>(gq, gv, a, cus, st);
+    case MODE_PART:
+        if (dtype == CT_F32) return launch_part<R, CT_F32>(gq, gv, a, cus, st);
+        if (dtype == CT_F16) return launch_part<R, CT_F16>(gq, gv, a, cus, st);
+        return launch_part<R, CT_BF16>(gq, gv, a, cus, st);
     case MODE_FILTER:
         if (dtype == CT_F32) return launch_t<R, CT_F32, CT_F32, MODE_FILTER, false, false>(a, cus, st);
         if (dtype == CT_F16) return launch_t<R, CT_F32, CT_F16, MODE_FILTER, false, false>(a, cus, st);

@@ -6,8 +6,9 @@
 namespace lcv {
 
 // ADJ is the adjoint of CONV: the same chain with the conjugate filter spectrum (a correlation,
-// whose causal truncation keeps the outputs that depend on later inputs).
-enum Mode1D { MODE_CONV = 0, MODE_FILTER = 1, MODE_ROW = 2, MODE_ROWFWD = 3, MODE_ADJ = 4 };
+// whose causal truncation keeps the outputs that depend on later inputs).  PART is CONV for a
+// filter of at most M/2 taps on a sequence of any length, one block of M/2 outputs per item.
+enum Mode1D { MODE_CONV = 0, MODE_FILTER = 1, MODE_ROW = 2, MODE_ROWFWD = 3, MODE_ADJ = 4, MODE_PART = 5 };
 
 struct Fused1DArgs {
     const void* u;       // CONV: u [B][H][N]; FILTER: k [H][N]; ROW/ROWFWD: workspace rows;
@@ -21,8 +22,9 @@ struct Fused1DArgs {
     const void* kf;      // CONV/ROW/ADJ: k_f
     const void* D;       // CONV/ROW/ADJ: D [H]
     const void* tables;  // fused-path tables for (R, compute type)
-    int64_t B, H, N;     // CONV/FILTER shape
-    int64_t nitems;      // CONV: pairs; FILTER: channels; ROW/ROWFWD: rows
+    int64_t B, H, N;     // CONV/FILTER/PART shape
+    int64_t nitems;      // CONV: pairs; FILTER: channels; ROW/ROWFWD: rows; PART: pairs x blocks
+    int64_t nchunk;      // PART: blocks of M/2 positions per row
     int64_t per_wg;      // items per workgroup (set by the launcher)
     float inv_m;         // 1 / M
     int64_t M;           // full transform length (ROW/ROWFWD: M1 * 8192)

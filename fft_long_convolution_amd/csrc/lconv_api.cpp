@@ -221,6 +221,46 @@ lconv_status_t lconv_fftconv_fwd(const void* u, const void* k_f, const void* D, 
     return LCONV_SUCCESS;
 }
 
+lconv_status_t lconv_fftconv_partial_fwd(const void* u, const void* k_f, const void* D, void* y, const void* q,
+                                         const void* v, int64_t B, int64_t H, int64_t N, int64_t L,
+                                         lconv_dtype_t dtype, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
+    if (B < 0 || H < 0 || N < 0 || L < 0) return LCONV_ERR_INVALID_SHAPE;
+    int64_t elems, t;
+    if (!mul_ok(B, H, &t) || !mul_ok(t, N, &elems) || !mul_ok(elems, 8, &t)) return LCONV_ERR_INVALID_SHAPE;
+    if (B == 0 || H == 0 || N == 0) return LCONV_SUCCESS;
+    if (L < 8 || L > 4096 || (L % 8) != 0 || (N % 8) != 0 || N > ((int64_t)1 << 40)) return LCONV_ERR_UNSUPPORTED;
+    Plan1D p;
+    if (!make_plan_1d(L, &p) || p.multipass) return LCONV_ERR_UNSUPPORTED;
+    // sequences of a channel: (batch row, block) windows, transformed two at a time
+    const int64_t C = p.M / 2, nch = (N + C - 1) / C;
+    int64_t nseq, items;
+    if (!mul_ok(B, nch, &nseq) || !mul_ok((nseq + 1) / 2, H, &items) || nseq >= ((int64_t)1 << 32) ||
+        items >= ((int64_t)1 << 31))
+        return LCONV_ERR_UNSUPPORTED;
+    if (!u || !k_f || !D || !y) return LCONV_ERR_NULL_POINTER;
+    if (!aligned16(u) || !aligned16(k_f) || !aligned16(D) || !aligned16(y) || (q && !aligned16(q)) ||
+        (v && !aligned16(v)))
+        return LCONV_ERR_MISALIGNED;
+    const size_t es = dtype_size(dtype), act = (size_t)elems * es;
+    const size_t kf_bytes = lconv_filter_fft_bytes(H, L, dtype);
+    if (kf_bytes == 0) return LCONV_ERR_INVALID_SHAPE;
+    if (overlap(y, act, u, act) || overlap(y, act, q, act) || overlap(y, act, v, act) ||
+        overlap(y, act, k_f, kf_bytes) || overlap(y, act, D, (size_t)H * es))
+        return LCONV_ERR_ALIASING;
+    hipError_t err = hipSuccess;
+    const int cus = device_cu_count(&err);
+    if (!cus) return LCONV_ERR_HIP;
+    const int ct = dtype == LCONV_F32 ? CT_F32 : (int)dtype;
+    const void* tabs = fused_tables(p.R, ct, &err);
+    if (!tabs) return LCONV_ERR_HIP;
+    Fused1DArgs a{};
+    a.u = u; a.q = q; a.v = v; a.y = y; a.kf = k_f; a.D = D; a.tables = tabs;
+    a.B = B; a.H = H; a.N = N; a.nitems = items; a.nchunk = nch;
+    a.inv_m = 1.0f / (float)p.M; a.M = p.M; a.M1 = 1;
+    return hip_status(launch_fused1d(p.R, dtype, MODE_PART, q != nullptr, v != nullptr, a, cus, stream));
+}
+
 lconv_status_t lconv_fftconv_bwd(const void* dy, const void* u, const void* k_f, const void* D, const void* q,
                                  const void* v, void* du, void* dq, void* dv, float* dk, float* dD, int64_t B,
                                  int64_t H, int64_t N, lconv_dtype_t dtype, hipStream_t stream) {

@@ -5,8 +5,8 @@ C ABI declared in include/lconv.h.  torch provides device memory and the current
 There is no CPU fallback: if the library is missing, importing the entry points fails loudly.
 
 Raw entry points keep the C names (``lconv_filter_fft``, ``lconv_fftconv_fwd``, ...), taking
-integer device pointers.  ``filter_fft``, ``fftconv``, ``fftconv_bwd``, ``filter_fft2d`` and
-``fftconv2d`` are convenience wrappers over torch tensors.
+integer device pointers.  ``filter_fft``, ``fftconv``, ``fftconv_partial``, ``fftconv_bwd``,
+``filter_fft2d`` and ``fftconv2d`` are convenience wrappers over torch tensors.
 """
 from __future__ import annotations
 
@@ -51,6 +51,7 @@ def load(path: str = LIB_PATH):
         "lconv_filter_fft": (i, [vp, vp, i64, i64, i, vp, sz, vp]),
         "lconv_fftconv_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i, vp, sz, vp]),
         "lconv_fftconv_bwd": (i, [vp] * 11 + [i64, i64, i64, i, vp]),
+        "lconv_fftconv_partial_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i, vp]),
         "lconv_filter_fft2d": (i, [vp, vp, i64, i64, i, vp]),
         "lconv_fftconv2d_fwd": (i, [vp, vp, vp, vp, i64, i64, i64, i, vp]),
         "lconv_status_string": (ctypes.c_char_p, [i]),
@@ -101,6 +102,10 @@ def lconv_fftconv_fwd(u, k_f, D, y, q, v, B, H, N, dtype, workspace, workspace_b
 
 def lconv_fftconv_bwd(dy, u, k_f, D, q, v, du, dq, dv, dk, dD, B, H, N, dtype, stream):
     return load().lconv_fftconv_bwd(dy, u, k_f, D, q, v, du, dq, dv, dk, dD, B, H, N, dtype, stream)
+
+
+def lconv_fftconv_partial_fwd(u, k_f, D, y, q, v, B, H, N, L, dtype, stream):
+    return load().lconv_fftconv_partial_fwd(u, k_f, D, y, q, v, B, H, N, L, dtype, stream)
 
 
 def lconv_filter_fft2d(k, k_f, C, S, dtype, stream):
@@ -200,6 +205,18 @@ def fftconv_bwd(dy, u, k_f, D, q=None, v=None, need_dk=True, stream=None):
                              _ptr(dq), _ptr(dv), _ptr(dk), _ptr(dD), B, H, N, dt, _stream(stream)),
            "lconv_fftconv_bwd")
     return du, dq, dv, dk, dD
+
+
+def fftconv_partial(u, k_f, D, L, q=None, v=None, out=None, stream=None):
+    """y = v * ((k * (q*u))[:N] + D * (q*u)) for a filter of L taps (k_f = filter_fft(k [H, L]))
+    and u [B, H, N] of any length N."""
+    torch = _torch()
+    B, H, N = u.shape
+    y = torch.empty_like(u) if out is None else out
+    _check(lconv_fftconv_partial_fwd(_ptr(u), _ptr(k_f), _ptr(D), _ptr(y), _ptr(q), _ptr(v), B, H, N,
+                                     L, dtype_code(u.dtype), _stream(stream)),
+           "lconv_fftconv_partial_fwd")
+    return y
 
 
 def filter_fft2d(k, stream=None):

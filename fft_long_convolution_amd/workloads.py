@@ -96,10 +96,15 @@ class Conv1DSpec:
     decay_loguniform: Optional[tuple] = None  # per-channel decay, log-uniform in [lo, hi]
     squash: Optional[float] = None           # squash threshold lambda
     seed: int = 0
+    L: int = 0                                # filter taps (0: the filter is N long)
 
     @property
     def kind(self):
         return "1d"
+
+    @property
+    def taps(self):
+        return self.L if self.L else self.N
 
 
 @dataclasses.dataclass(frozen=True)
@@ -130,6 +135,10 @@ WORKLOADS = {
         "very_long_bf16_b1_h64_n2097152", 1, 64, 2097152, "bf16", decay=1e-6, seed=1004),
     "hyenand_2d_bf16_b8_c256_s128": Conv2DSpec(
         "hyenand_2d_bf16_b8_c256_s128", 8, 256, 128, "bf16", decay=0.05, seed=1005),
+    # the 2^21-long shape with a short (4096-tap) filter: the partial convolution
+    "partial_bf16_b1_h64_n2097152_l4096": Conv1DSpec(
+        "partial_bf16_b1_h64_n2097152_l4096", 1, 64, 2097152, "bf16", decay=1e-3, seed=1006,
+        L=4096),
 }
 
 # The headline workload the bench times.
@@ -146,8 +155,15 @@ def spec_1d(B, H, N, dtype, gated=False, seed=7, decay=None, decay_loguniform=(1
                       seed=seed)
 
 
+def spec_partial(B, H, N, L, dtype, gated=False, seed=7, decay=1e-3) -> Conv1DSpec:
+    """A 1D workload with a short filter of L taps (k is [H, L])."""
+    return Conv1DSpec(f"partial_{dtype}_b{B}_h{H}_n{N}_l{L}", B, H, N, dtype, gated=gated,
+                      decay=decay, seed=seed, L=L)
+
+
 def make_1d(spec: Conv1DSpec) -> dict:
-    """Draw u, q, v, k, D for a 1D workload (draw order: u, q, v, k_raw, alpha, D)."""
+    """Draw u, q, v, k, D for a 1D workload (draw order: u, q, v, k_raw, alpha, D); k is
+    [H, taps] (taps = N unless the workload has a short filter)."""
     rng = np.random.default_rng(spec.seed)
     B, H, N = spec.B, spec.H, spec.N
     out = {"spec": spec, "dtype": spec.dtype}
@@ -157,8 +173,9 @@ def make_1d(spec: Conv1DSpec) -> dict:
         out["v"] = to_storage(rng.standard_normal((B, H, N), dtype=np.float32), spec.dtype)
     else:
         out["q"] = out["v"] = None
-    k = rng.standard_normal((H, N))
-    t = np.arange(N, dtype=np.float64)
+    T = spec.taps
+    k = rng.standard_normal((H, T))
+    t = np.arange(T, dtype=np.float64)
     if spec.decay_loguniform is not None:
         lo, hi = spec.decay_loguniform
         alpha = np.exp(rng.uniform(math.log(lo), math.log(hi), size=H))

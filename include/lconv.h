@@ -112,6 +112,29 @@ lconv_status_t lconv_fftconv_fwd(const void* u, const void* k_f, const void* D, 
                                  hipStream_t stream);
 
 /*
+ * Partial convolution: the same gated causal convolution with a filter of L taps (zero beyond
+ * them) on sequences of any length N ("FlashFFTConv" abstract: partial convolutions, computed by
+ * skipping blocks of the decomposition, save memory and compute and let a model run on
+ * sequences far longer than its filters).  The causal convolution matrix is then banded: each
+ * block of C = M/2 outputs (M the transform length of the filter, from lconv_filter_fft with
+ * length L) depends only on its own input block and the previous one, so every block is one
+ * fused M-point transform of that window and all other blocks of the matrix are skipped.  Cost
+ * O(N log L); the filter spectrum is stored at length L.
+ *   y[b,h,t] = v * ( sum_{s = max(0, t-L+1)}^{t} k[h,t-s] x[b,h,s] + D[h] x[b,h,t] ),  x = q u
+ *   u, y, q, v   [B][H][N] dtype, device (q, v may be NULL), y written
+ *   k_f          from lconv_filter_fft(k, ..., H, L, dtype) with k [H][L]
+ *   D            [H] dtype
+ * The windows of a channel (batch row, block) are transformed two at a time as the real and
+ * imaginary parts of one complex sequence, so B = 1 wastes nothing.
+ * Supported: 8 <= L <= 4096 with L a multiple of 8; N >= 1 a multiple of 8 (N may be smaller or
+ * larger than L, up to 2^40); H * ceil(B * ceil(N / C) / 2) < 2^31.  No workspace.
+ */
+lconv_status_t lconv_fftconv_partial_fwd(const void* u, const void* k_f, const void* D, void* y,
+                                         const void* q, const void* v, int64_t B, int64_t H,
+                                         int64_t N, int64_t L, lconv_dtype_t dtype,
+                                         hipStream_t stream);
+
+/*
  * Gradients of the gated causal convolution above, given dy = dL/dy (the training path the
  * FlashFFTConv abstract reports speed-ups for; the FFT convolution is exact, so its gradient is
  * that of the plain causal sum).  With x = q (.) u and ds = dy (.) v:

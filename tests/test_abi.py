@@ -153,3 +153,31 @@ def test_bwd_empty_and_ignored_outputs():
     import torch
     if not torch.cuda.is_available():
         assert bwd(dq=G[0]) == HIPERR
+
+
+def part(u=G[0], kf=G[1], D=G[2], y=G[3], q=None, v=None, B=2, H=3, N=64, L=32, dt=BF16):
+    return lconv.lconv_fftconv_partial_fwd(u, kf, D, y, q, v, B, H, N, L, dt, None)
+
+
+def test_partial_validation_errors():
+    assert part(dt=5) == UNSUP
+    assert part(B=-1) == SHAPE
+    assert part(L=-8) == SHAPE
+    assert part(L=12) == UNSUP                                            # L % 8
+    assert part(L=8192) == UNSUP                                          # beyond one transform
+    assert part(L=0) == UNSUP
+    assert part(N=12) == UNSUP                                            # N % 8
+    assert part(N=2 ** 41) == UNSUP
+    assert part(B=2 ** 20, H=2 ** 10, N=2 ** 20, L=8) == UNSUP            # too many blocks
+    assert part(u=None) == NULLP
+    assert part(kf=None) == NULLP
+    assert part(y=None) == NULLP
+    assert part(D=G[2] + 4) == MISAL
+    assert part(y=G[0]) == ALIAS
+    assert part(q=G[3] + 16) == ALIAS
+
+
+def test_partial_empty_is_noop():
+    assert part(B=0) == OK
+    assert part(H=0) == OK
+    assert part(N=0) == OK

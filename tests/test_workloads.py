@@ -81,3 +81,12 @@ def test_sample_points_in_range_and_structured():
     assert any(t % 256 == 255 for t in ts) and any(t % 4096 == 0 and t > 0 for t in ts)
     p2 = wl.sample_points_2d(8, 256, 128)
     assert p2.shape == (4096, 4) and p2[:, 2:].max() < 128
+
+
+def test_short_filter_workload_draws_l_taps():
+    spec = wl.spec_partial(2, 3, 256, 24, "bf16", gated=True, seed=3)
+    d = wl.make(spec)
+    assert d["k"].shape == (3, 24) and d["u"].shape == (2, 3, 256)
+    assert spec.taps == 24 and wl.spec_1d(1, 1, 64, "f32").taps == 64
+    long = wl.WORKLOADS["partial_bf16_b1_h64_n2097152_l4096"]
+    assert (long.N, long.L, long.dtype) == (2 ** 21, 4096, "bf16")
