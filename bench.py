@@ -34,8 +34,8 @@ METRIC = "fftconv GB/s, TFLOP/s, %roofline at B16\u00b7H768\u00b7N4096 bf16 caus
 # matrix-core op count) per workload; they carry the hash of the kernel sources they were taken
 # on and are ignored once those sources change.
 COUNTER_FILES = {"hyena_gated_bf16_b16_h768_n4096": "profiles/conv8k_hyena_gated_bf16_b16_h768_n4096_counters.md"}
-KERNEL_SOURCES = ("fft_long_convolution_amd/csrc/fused1d.hip", "fft_long_convolution_amd/csrc/fused_io.h",
-                  "fft_long_convolution_amd/csrc/lconv_device.h")
+KERNEL_SOURCES = ("fft_long_convolution_amd/csrc/fused1d_kernels.h", "fft_long_convolution_amd/csrc/fused1d_conv.hip",
+                  "fft_long_convolution_amd/csrc/fused_io.h", "fft_long_convolution_amd/csrc/lconv_device.h")
 
 
 def kernel_source_hash():
@@ -207,6 +207,9 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the gradient call's timing")
+    ap.add_argument("--keep", default=None,
+                    help="frequency-sparse call: bit mask (e.g. 0xe000000f) of the frequency "
+                         "blocks kept (f mod R); the step is lconv_fftconv_sparse_fwd")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="run only a plain 256 MiB device copy (reads and writes 256 MiB per "
@@ -244,6 +247,22 @@ def main():
         kf = run_filter()
         y = torch.empty_like(u)
         step = lambda: lconv.fftconv2d(u, kf, D, out=y)
+    elif args.keep is not None:  # frequency-sparse convolution
+        keep = int(args.keep, 0)
+        u, q, v, k, D = (to_dev(d[x], dt) for x in ("u", "q", "v", "k", "D"))
+        run_filter = lambda: lconv.filter_fft(k)
+        kf = run_filter()
+        y = torch.empty_like(u)
+        dtc = lconv.dtype_code(u.dtype)
+        stream = torch.cuda.current_stream()
+        p = lambda t: None if t is None else t.data_ptr()
+
+        def step():
+            st = lconv.lconv_fftconv_sparse_fwd(u.data_ptr(), kf.data_ptr(), D.data_ptr(), y.data_ptr(),
+                                                p(q), p(v), spec.B, spec.H, spec.N, keep, dtc,
+                                                stream.cuda_stream)
+            if st != 0:
+                raise lconv.LconvError(st, "lconv_fftconv_sparse_fwd")
     elif spec.L:  # partial convolution: short filter, any sequence length
         u, q, v, k, D = (to_dev(d[x], dt) for x in ("u", "q", "v", "k", "D"))
         run_filter = lambda: lconv.filter_fft(k)
@@ -307,6 +326,11 @@ def main():
 
     nbytes = algorithmic_bytes(spec)
     flops = nominal_flops(spec)
+    if args.keep is not None:  # only the kept blocks of the filter spectrum are needed
+        R = lconv.lconv_freq_blocks(spec.N)
+        frac = bin(int(args.keep, 0) & ((1 << R) - 1)).count("1") / R
+        s_ = {"f32": 4, "f16": 2, "bf16": 2}[dt]
+        nbytes -= int(round((1 - frac) * spec.H * (spec.N + 1) * 2 * s_))
     elems = spec.B * (spec.H if spec.kind == "1d" else spec.C) * (spec.N if spec.kind == "1d" else spec.S ** 2)
     gbs = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (avg_ms * 1e-3) / 1e9
@@ -325,6 +349,7 @@ def main():
         "dtype": dt,
         "data": "synthetic",
         "config": {"workload": spec.name, "B": spec.B, **({"L": spec.L} if getattr(spec, "L", 0) else {}),
+                   **({"keep": args.keep} if args.keep is not None else {}),
                    ("H" if spec.kind == "1d" else "C"): (spec.H if spec.kind == "1d" else spec.C),
                    ("N" if spec.kind == "1d" else "S"): (spec.N if spec.kind == "1d" else spec.S),
                    "gated": bool(getattr(spec, "gated", False)), "parallelism": "none"},
@@ -338,14 +363,14 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "kernel_avg_us": round(avg_ms * 1e3, 3)},
     }
-    cs = counter_summary(spec.name)
+    cs = counter_summary(spec.name) if args.keep is None else {}  # counters are of the dense call
     if cs:
         out["roofline"]["traffic"] = int(float(cs["traffic_bytes_per_launch"]))
         # matrix-core GFLOP executed per launch (op counter x 512), over this run's kernel time
         mf = float(cs["mfma_gflop_executed_per_launch"]) * 1e9 / (avg_ms * 1e-3) / 1e12
         out["mfma"] = {"executed_tflops": round(mf, 1), "peak": MFMA_PEAK[dt],
                        "util": round(mf / MFMA_PEAK[dt], 4), "counters": cs["path"]}
-    if not args.no_bwd and spec.kind == "1d" and spec.N <= 4096 and not spec.L:
+    if not args.no_bwd and spec.kind == "1d" and spec.N <= 4096 and not spec.L and args.keep is None:
         out["backward"] = time_backward(lconv, wl, spec, u, kf, D, q, v, args)
     if not args.no_cpu and spec.kind == "1d":
         out["cpu_baseline"] = cpu_baseline(d, args.cpu_budget)

@@ -8,7 +8,9 @@ namespace lcv {
 // ADJ is the adjoint of CONV: the same chain with the conjugate filter spectrum (a correlation,
 // whose causal truncation keeps the outputs that depend on later inputs).  PART is CONV for a
 // filter of at most M/2 taps on a sequence of any length, one block of M/2 outputs per item.
-enum Mode1D { MODE_CONV = 0, MODE_FILTER = 1, MODE_ROW = 2, MODE_ROWFWD = 3, MODE_ADJ = 4, MODE_PART = 5 };
+// SPARSE is CONV with the filter spectrum kept only on the frequency blocks set in `keep`.
+enum Mode1D { MODE_CONV = 0, MODE_FILTER = 1, MODE_ROW = 2, MODE_ROWFWD = 3, MODE_ADJ = 4, MODE_PART = 5,
+              MODE_SPARSE = 6 };
 
 struct Fused1DArgs {
     const void* u;       // CONV: u [B][H][N]; FILTER: k [H][N]; ROW/ROWFWD: workspace rows;
@@ -25,6 +27,7 @@ struct Fused1DArgs {
     int64_t B, H, N;     // CONV/FILTER/PART shape
     int64_t nitems;      // CONV: pairs; FILTER: channels; ROW/ROWFWD: rows; PART: pairs x blocks
     int64_t nchunk;      // PART: blocks of M/2 positions per row
+    uint32_t keep;       // SPARSE: bit k1 set = frequency block k1 (f mod R = k1) kept
     int64_t per_wg;      // items per workgroup (set by the launcher)
     float inv_m;         // 1 / M
     int64_t M;           // full transform length (ROW/ROWFWD: M1 * 8192)
@@ -38,6 +41,17 @@ struct Fused1DArgs {
 // gq / gv: the pre-gate q / post-gate v pointers are set (conv and adj modes).
 hipError_t launch_fused1d(int R, int dtype, int mode, bool gq, bool gv, const Fused1DArgs& a,
                           int cus, hipStream_t stream);
+
+// Per-mode instantiations (fused1d_conv.hip, fused1d_adj.hip, fused1d_part.hip), called by
+// launch_fused1d.
+hipError_t launch_fused1d_conv(int R, int dtype, bool gq, bool gv, const Fused1DArgs& a, int cus,
+                               hipStream_t stream);
+hipError_t launch_fused1d_adj(int R, int dtype, bool gq, bool gv, const Fused1DArgs& a, int cus,
+                              hipStream_t stream);
+hipError_t launch_fused1d_part(int R, int dtype, bool gq, bool gv, const Fused1DArgs& a, int cus,
+                               hipStream_t stream);
+hipError_t launch_fused1d_sparse(int R, int dtype, bool gq, bool gv, const Fused1DArgs& a, int cus,
+                                 hipStream_t stream);
 
 // Filter gradient: per channel h (items = channels), the sum over batch pairs of
 // conj(DFT(q u)) DFT(dy v), inverse-transformed; dk[h][n] for n < N and dD[h] = dk[h][0]

@@ -221,6 +221,50 @@ lconv_status_t lconv_fftconv_fwd(const void* u, const void* k_f, const void* D, 
     return LCONV_SUCCESS;
 }
 
+int lconv_freq_blocks(int64_t N) {
+    Plan1D p;
+    if (!n_supported(N) || N > LCONV_BWD_MAX_N || !make_plan_1d(N, &p) || p.multipass) return 0;
+    return p.R;
+}
+
+lconv_status_t lconv_fftconv_sparse_fwd(const void* u, const void* k_f, const void* D, void* y, const void* q,
+                                        const void* v, int64_t B, int64_t H, int64_t N, uint32_t keep,
+                                        lconv_dtype_t dtype, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
+    if (B < 0 || H < 0 || N < 0) return LCONV_ERR_INVALID_SHAPE;
+    int64_t elems, t;
+    if (!mul_ok(B, H, &t) || !mul_ok(t, N, &elems) || !mul_ok(elems, 8, &t)) return LCONV_ERR_INVALID_SHAPE;
+    if (B == 0 || H == 0 || N == 0) return LCONV_SUCCESS;
+    const int R = lconv_freq_blocks(N);
+    if (R == 0) return LCONV_ERR_UNSUPPORTED;
+    if (R < 32 && (keep >> R) != 0) return LCONV_ERR_UNSUPPORTED;
+    for (int r = 0; r < R; ++r)
+        if (((keep >> r) & 1u) != ((keep >> ((R - r) % R)) & 1u)) return LCONV_ERR_UNSUPPORTED;
+    if (!u || !k_f || !D || !y) return LCONV_ERR_NULL_POINTER;
+    if (!aligned16(u) || !aligned16(k_f) || !aligned16(D) || !aligned16(y) || (q && !aligned16(q)) ||
+        (v && !aligned16(v)))
+        return LCONV_ERR_MISALIGNED;
+    const size_t es = dtype_size(dtype), act = (size_t)elems * es;
+    const size_t kf_bytes = lconv_filter_fft_bytes(H, N, dtype);
+    if (kf_bytes == 0) return LCONV_ERR_INVALID_SHAPE;
+    if (overlap(y, act, u, act) || overlap(y, act, q, act) || overlap(y, act, v, act) ||
+        overlap(y, act, k_f, kf_bytes) || overlap(y, act, D, (size_t)H * es))
+        return LCONV_ERR_ALIASING;
+    Plan1D p;
+    make_plan_1d(N, &p);
+    hipError_t err = hipSuccess;
+    const int cus = device_cu_count(&err);
+    if (!cus) return LCONV_ERR_HIP;
+    const int ct = dtype == LCONV_F32 ? CT_F32 : (int)dtype;
+    const void* tabs = fused_tables(p.R, ct, &err);
+    if (!tabs) return LCONV_ERR_HIP;
+    Fused1DArgs a{};
+    a.u = u; a.q = q; a.v = v; a.y = y; a.kf = k_f; a.D = D; a.tables = tabs;
+    a.B = B; a.H = H; a.N = N; a.nitems = pairs_per_channel(B) * H; a.keep = keep;
+    a.inv_m = 1.0f / (float)p.M; a.M = p.M; a.M1 = 1;
+    return hip_status(launch_fused1d(p.R, dtype, MODE_SPARSE, q != nullptr, v != nullptr, a, cus, stream));
+}
+
 lconv_status_t lconv_fftconv_partial_fwd(const void* u, const void* k_f, const void* D, void* y, const void* q,
                                          const void* v, int64_t B, int64_t H, int64_t N, int64_t L,
                                          lconv_dtype_t dtype, hipStream_t stream) {

@@ -5,8 +5,8 @@ C ABI declared in include/lconv.h.  torch provides device memory and the current
 There is no CPU fallback: if the library is missing, importing the entry points fails loudly.
 
 Raw entry points keep the C names (``lconv_filter_fft``, ``lconv_fftconv_fwd``, ...), taking
-integer device pointers.  ``filter_fft``, ``fftconv``, ``fftconv_partial``, ``fftconv_bwd``,
-``filter_fft2d`` and ``fftconv2d`` are convenience wrappers over torch tensors.
+integer device pointers.  ``filter_fft``, ``fftconv``, ``fftconv_partial``, ``fftconv_sparse``,
+``fftconv_bwd``, ``filter_fft2d`` and ``fftconv2d`` are convenience wrappers over torch tensors.
 """
 from __future__ import annotations
 
@@ -52,6 +52,8 @@ def load(path: str = LIB_PATH):
         "lconv_fftconv_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i, vp, sz, vp]),
         "lconv_fftconv_bwd": (i, [vp] * 11 + [i64, i64, i64, i, vp]),
         "lconv_fftconv_partial_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i, vp]),
+        "lconv_fftconv_sparse_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_uint32, i, vp]),
+        "lconv_freq_blocks": (i, [i64]),
         "lconv_filter_fft2d": (i, [vp, vp, i64, i64, i, vp]),
         "lconv_fftconv2d_fwd": (i, [vp, vp, vp, vp, i64, i64, i64, i, vp]),
         "lconv_status_string": (ctypes.c_char_p, [i]),
@@ -106,6 +108,14 @@ def lconv_fftconv_bwd(dy, u, k_f, D, q, v, du, dq, dv, dk, dD, B, H, N, dtype, s
 
 def lconv_fftconv_partial_fwd(u, k_f, D, y, q, v, B, H, N, L, dtype, stream):
     return load().lconv_fftconv_partial_fwd(u, k_f, D, y, q, v, B, H, N, L, dtype, stream)
+
+
+def lconv_fftconv_sparse_fwd(u, k_f, D, y, q, v, B, H, N, keep, dtype, stream):
+    return load().lconv_fftconv_sparse_fwd(u, k_f, D, y, q, v, B, H, N, keep, dtype, stream)
+
+
+def lconv_freq_blocks(N):
+    return load().lconv_freq_blocks(N)
 
 
 def lconv_filter_fft2d(k, k_f, C, S, dtype, stream):
@@ -216,6 +226,20 @@ def fftconv_partial(u, k_f, D, L, q=None, v=None, out=None, stream=None):
     _check(lconv_fftconv_partial_fwd(_ptr(u), _ptr(k_f), _ptr(D), _ptr(y), _ptr(q), _ptr(v), B, H, N,
                                      L, dtype_code(u.dtype), _stream(stream)),
            "lconv_fftconv_partial_fwd")
+    return y
+
+
+def fftconv_sparse(u, k_f, D, keep, q=None, v=None, out=None, stream=None):
+    """Frequency-sparse convolution: as fftconv, with the filter spectrum kept only on the
+    frequency blocks r (f mod R = r, R = lconv_freq_blocks(N)) in `keep` (an iterable of block
+    indices closed under r -> R - r, or a bit mask)."""
+    torch = _torch()
+    B, H, N = u.shape
+    mask = keep if isinstance(keep, int) else sum(1 << int(r) for r in set(keep))
+    y = torch.empty_like(u) if out is None else out
+    _check(lconv_fftconv_sparse_fwd(_ptr(u), _ptr(k_f), _ptr(D), _ptr(y), _ptr(q), _ptr(v), B, H, N,
+                                    mask, dtype_code(u.dtype), _stream(stream)),
+           "lconv_fftconv_sparse_fwd")
     return y
 
 

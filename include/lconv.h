@@ -112,6 +112,29 @@ lconv_status_t lconv_fftconv_fwd(const void* u, const void* k_f, const void* D, 
                                  hipStream_t stream);
 
 /*
+ * Frequency-sparse convolution: the gated causal convolution with the filter spectrum kept only
+ * on some blocks of the decomposition ("FlashFFTConv" abstract: frequency-sparse convolutions,
+ * computed by skipping blocks of the matrix decomposition, speed up pretrained models).  With
+ * the transform length M = 256 R of the forward call, frequency block r (0 <= r < R) is the set
+ * of frequencies f with f mod R = r; bit r of `keep` keeps it.  The result is
+ *   y = v (.) ( IDFT_M( DFT_M(x) . K_keep )[:N] + D x ),   x = q (.) u,
+ * K_keep the filter spectrum on the kept blocks and 0 elsewhere (so the effective filter is the
+ * real length-M sequence IDFT(K_keep), applied circularly and truncated to N).  Dropped blocks
+ * cost no transform work.  `keep` must be closed under r -> (R - r) mod R (otherwise the filter
+ * would not be real): LCONV_ERR_UNSUPPORTED otherwise, as for bits at or above R.
+ *   u, y, q, v, k_f, D   as for lconv_fftconv_fwd (k_f from lconv_filter_fft(k, ..., H, N, dtype))
+ * Supported: N <= 4096 (one workgroup per transform).  R: lconv_freq_blocks(N).  No workspace.
+ */
+lconv_status_t lconv_fftconv_sparse_fwd(const void* u, const void* k_f, const void* D, void* y,
+                                        const void* q, const void* v, int64_t B, int64_t H,
+                                        int64_t N, uint32_t keep, lconv_dtype_t dtype,
+                                        hipStream_t stream);
+
+/* Number of frequency blocks R = M / 256 of the transform for N (0 if N is unsupported by
+ * lconv_fftconv_sparse_fwd). */
+int lconv_freq_blocks(int64_t N);
+
+/*
  * Partial convolution: the same gated causal convolution with a filter of L taps (zero beyond
  * them) on sequences of any length N ("FlashFFTConv" abstract: partial convolutions, computed by
  * skipping blocks of the decomposition, save memory and compute and let a model run on

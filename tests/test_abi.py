@@ -181,3 +181,28 @@ def test_partial_empty_is_noop():
     assert part(B=0) == OK
     assert part(H=0) == OK
     assert part(N=0) == OK
+
+
+def sparse(u=G[0], kf=G[1], D=G[2], y=G[3], q=None, v=None, B=2, H=3, N=1000, keep=0b10000011, dt=BF16):
+    return lconv.lconv_fftconv_sparse_fwd(u, kf, D, y, q, v, B, H, N, keep, dt, None)
+
+
+def test_sparse_blocks_and_validation():
+    assert lconv.lconv_freq_blocks(64) == 2          # M = 512
+    assert lconv.lconv_freq_blocks(1000) == 8        # M = 2048
+    assert lconv.lconv_freq_blocks(4096) == 32       # M = 8192
+    assert lconv.lconv_freq_blocks(8192) == 0        # beyond one transform
+    assert lconv.lconv_freq_blocks(12) == 0
+    assert sparse(dt=5) == UNSUP
+    assert sparse(B=-1) == SHAPE
+    assert sparse(N=8192) == UNSUP
+    assert sparse(keep=0b110) == UNSUP               # R = 8: mirror of 1 is 7, not 2
+    assert sparse(keep=1 << 8) == UNSUP              # beyond R
+    assert sparse(u=None) == NULLP
+    assert sparse(D=G[2] + 2) == MISAL
+    assert sparse(y=G[0]) == ALIAS
+    assert sparse(B=0) == OK
+    import torch
+    if not torch.cuda.is_available():
+        assert sparse(keep=0) == HIPERR               # valid (nothing kept): fails only at HIP
+        assert sparse(N=4096, keep=0xffffffff) == HIPERR
