@@ -91,60 +91,80 @@ __device__ __forceinline__ void dft_small(float2* v) {
 }
 
 // One self-sorting pass of radix RAD over the columns of buf (column-major, column stride ld) that
-// belong to this wave (column c0 + wave + nw * i).  Sub-transform length before the pass: ns.
-// FIRST: the second half of the input is zero.  A column's L / RAD butterfly groups (at most
-// 64) are spread over the lanes, several columns per wave round when there are fewer groups
-// than lanes.  The pass is in place: a round's LDS reads all precede its writes in the wave's
-// own instruction order, and columns do not interact, so no barrier is needed.
-template <int RAD, bool INV, bool FIRST>
-__device__ __forceinline__ void stockham_pass_wave(float2* buf, int L, int ld, int CB, int ns,
+// belong to this wave: columns wave + nw * i, the same set in every pass, so no column moves
+// between waves and no barrier is needed between passes.  Sub-transform length before the
+// pass: ns.  FIRST: the second half of the input is zero.  A column's L / RAD butterfly groups
+// are spread over the lanes: several of the wave's columns per round when there are fewer
+// groups than lanes, or ROUNDS = groups / 64 groups per lane when there are more.  The pass is
+// in place: all of a column's LDS reads (every round) precede its writes in the wave's own
+// instruction order, and columns do not interact.  Not inlined: each (radix, rounds) variant
+// keeps its own register budget instead of raising the calling kernel's to the largest one.
+template <int RAD, bool INV, bool FIRST, int ROUNDS>
+__device__ __attribute__((noinline)) void stockham_pass_wave(float2* buf, int L, int ld, int CB, int ns,
                                                    const float* tw_col, int m1, int wave, int nw, int lane) {
-    const int groups = L / RAD;                     // 1 .. 64
-    const int cpr = 64 / groups;                    // columns per wave round
-    const int sub = lane / groups, j = lane % groups;
-    const int k = j % ns, tstep = (m1 / (ns * RAD)) * k;
-    const int b0 = (j / ns) * ns * RAD + k;
-    for (int c = wave * cpr + sub; c < CB; c += nw * cpr) {
-        float2 v[RAD];
+    const int groups = L / RAD;
+    const int cpr = groups >= 64 ? 1 : 64 / groups;  // this wave's columns per round
+    const int sub = groups >= 64 ? 0 : lane / groups;
+    const int tmul = m1 / (ns * RAD);
+    for (int idx = sub; wave + nw * idx < CB; idx += cpr) {
+        const int c = wave + nw * idx;
+        float2 v[ROUNDS][RAD];
 #pragma unroll
-        for (int q = 0; q < RAD; ++q) {
-            float2 x = make_float2(0.f, 0.f);
-            if (!FIRST || q < RAD / 2) x = buf[c * ld + j + q * groups];
-            if (q > 0 && ns > 1) {
-                const float2 w = ((const float2*)tw_col)[(tstep * q) & (m1 - 1)];
-                x = INV ? cmulcf(x, w) : cmulf(x, w);
+        for (int r = 0; r < ROUNDS; ++r) {
+            const int j = groups >= 64 ? lane + 64 * r : lane % groups;
+            const int tstep = tmul * (j % ns);
+#pragma unroll
+            for (int q = 0; q < RAD; ++q) {
+                float2 x = make_float2(0.f, 0.f);
+                if (!FIRST || q < RAD / 2) x = buf[c * ld + j + q * groups];
+                if (q > 0 && ns > 1) {
+                    const float2 w = ((const float2*)tw_col)[(tstep * q) & (m1 - 1)];
+                    x = INV ? cmulcf(x, w) : cmulf(x, w);
+                }
+                v[r][q] = x;
             }
-            v[q] = x;
         }
-        dft_small<RAD, INV>(v);
 #pragma unroll
-        for (int q = 0; q < RAD; ++q) buf[c * ld + b0 + q * ns] = v[q];
+        for (int r = 0; r < ROUNDS; ++r) dft_small<RAD, INV>(v[r]);
+#pragma unroll
+        for (int r = 0; r < ROUNDS; ++r) {
+            const int j = groups >= 64 ? lane + 64 * r : lane % groups;
+            const int k = j % ns, b0 = (j / ns) * ns * RAD + k;
+#pragma unroll
+            for (int q = 0; q < RAD; ++q) buf[c * ld + b0 + q * ns] = v[r][q];
+        }
     }
 }
 
-// Full column DFT of length L = M1 (power of two, 32..512) over the CB columns of buf; each
+// Full column DFT of length L = M1 (power of two, 32..1024) over the CB columns of buf; each
 // wave transforms its own columns.  Callers bracket it with block barriers.
 template <int kThreads, bool INV>
 __device__ void column_dft(float2* buf, int L, int ld, int CB, const float* tw_col, int m1) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = kThreads / 64;
     int ns = 1;
     bool first = !INV;  // forward: the input's second half is zero
+    // one pass of radix RAD, with the rounds its group count needs (L <= 1024)
+    auto pass = [&](auto rad) {
+        constexpr int RAD = decltype(rad)::value;
+        const int rounds = L / RAD <= 64 ? 1 : L / RAD / 64;
+        auto go = [&](auto rr) {
+            constexpr int RR = decltype(rr)::value;
+            if (first) stockham_pass_wave<RAD, INV, true, RR>(buf, L, ld, CB, ns, tw_col, m1, wave, nw, lane);
+            else stockham_pass_wave<RAD, INV, false, RR>(buf, L, ld, CB, ns, tw_col, m1, wave, nw, lane);
+        };
+        constexpr int MAXR = 1024 / RAD / 64;  // rounds a length of at most 1024 can need
+        if (rounds == 1 || MAXR < 2) go(std::integral_constant<int, 1>{});
+        else if (rounds == 2 || MAXR < 4) go(std::integral_constant<int, (MAXR < 2 ? 1 : 2)>{});
+        else if (rounds == 4 || MAXR < 8) go(std::integral_constant<int, (MAXR < 4 ? 1 : 4)>{});
+        else go(std::integral_constant<int, (MAXR < 8 ? 1 : 8)>{});
+        ns *= RAD;
+        first = false;
+    };
     while (ns < L) {
         const int rem = L / ns;
-        if (rem >= 8) {
-            if (first) stockham_pass_wave<8, INV, true>(buf, L, ld, CB, ns, tw_col, m1, wave, nw, lane);
-            else stockham_pass_wave<8, INV, false>(buf, L, ld, CB, ns, tw_col, m1, wave, nw, lane);
-            ns *= 8;
-        } else if (rem == 4) {
-            if (first) stockham_pass_wave<4, INV, true>(buf, L, ld, CB, ns, tw_col, m1, wave, nw, lane);
-            else stockham_pass_wave<4, INV, false>(buf, L, ld, CB, ns, tw_col, m1, wave, nw, lane);
-            ns *= 4;
-        } else {
-            if (first) stockham_pass_wave<2, INV, true>(buf, L, ld, CB, ns, tw_col, m1, wave, nw, lane);
-            else stockham_pass_wave<2, INV, false>(buf, L, ld, CB, ns, tw_col, m1, wave, nw, lane);
-            ns *= 2;
-        }
-        first = false;
+        if (rem >= 8) pass(std::integral_constant<int, 8>{});
+        else if (rem == 4) pass(std::integral_constant<int, 4>{});
+        else pass(std::integral_constant<int, 2>{});
     }
     __syncthreads();
 }
@@ -532,7 +552,7 @@ template <int CT, int IO>
 static hipError_t launch_cols(bool fwd, const ColArgs& a, hipStream_t st) {
     if (a.nseq <= 0) return hipSuccess;
     const int M1 = (int)a.M1;
-    if (M1 < 2 || M1 > 512 || (M1 & (M1 - 1))) return hipErrorInvalidValue;
+    if (M1 < 2 || M1 > 1024 || (M1 & (M1 - 1))) return hipErrorInvalidValue;
     switch (M1) {  // one column per thread, DFT in registers
     case 2: return launch_small_t<CT, IO, 2>(fwd, a, st);
     case 4: return launch_small_t<CT, IO, 4>(fwd, a, st);

@@ -19,7 +19,7 @@
 namespace lcv {
 
 bool make_plan_1d(int64_t N, Plan1D* p) {
-    if (N < 1 || N > ((int64_t)1 << 21)) return false;
+    if (N < 1 || N > ((int64_t)1 << 22)) return false;
     int64_t M = 512;
     while (M < 2 * N) M *= 2;
     p->N = N;

@@ -62,7 +62,7 @@ typedef enum {
 } lconv_status_t;
 
 /* Largest supported sequence length (1D) and the only supported 2D side. */
-#define LCONV_MAX_N   ((int64_t)1 << 21)
+#define LCONV_MAX_N   ((int64_t)1 << 22)
 #define LCONV_2D_SIDE 128
 
 /* ---- size queries (pure host functions; 0 for invalid or unsupported arguments) ---------- */

@@ -42,7 +42,8 @@ def test_size_queries():
     assert lconv.lconv_fftconv_workspace_bytes(4, 256, 65536, F16) > 0    # multi-pass
     assert lconv.lconv_filter_fft_workspace_bytes(64, 2 ** 21, BF16) > 0
     assert lconv.lconv_filter_fft_bytes(1, 12, BF16) == 0                 # N % 8 != 0
-    assert lconv.lconv_filter_fft_bytes(1, 2 ** 22, BF16) == 0            # too long
+    assert lconv.lconv_filter_fft_bytes(1, 2 ** 22 + 8, BF16) == 0        # too long
+    assert lconv.lconv_filter_fft_bytes(1, 2300000, BF16) == 2 ** 23 * 4   # 2.3M: M = 2^23
     assert lconv.lconv_filter_fft_bytes(1, 8, 7) == 0                     # bad dtype
     assert lconv.lconv_filter_fft2d_bytes(256, 128, BF16) == 256 * 256 * 256 * 4
     assert lconv.lconv_filter_fft2d_bytes(1, 64, BF16) == 0
@@ -58,7 +59,7 @@ def test_fwd_validation_errors():
     assert fwd(N=-8) == SHAPE
     assert fwd(B=2 ** 40, H=2 ** 20, N=2 ** 10) == SHAPE                 # overflow
     assert fwd(N=12) == UNSUP
-    assert fwd(N=2 ** 22) == UNSUP
+    assert fwd(N=2 ** 22 + 8) == UNSUP
     assert fwd(u=None) == NULLP
     assert fwd(kf=None) == NULLP
     assert fwd(D=None) == NULLP
