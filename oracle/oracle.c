@@ -553,3 +553,58 @@ int oracle_conv2d_points(const void* u, const void* k, const void* D, int dt, in
     or_parallel(or_points2d_worker, J, npts, nthreads);
     return 0;
 }
+
+/* ------------------------------------------------------------------------------------------ */
+/* 3D (HyenaND-style, volumes)                                                                  */
+/* ------------------------------------------------------------------------------------------ */
+/* The 2D definition one dimension up ("Native Multi-Dimensional Subquadratic Operators via Input
+ * Dependent Long Convolutions", abstract: global convolutions on the native multi-dimensional
+ * grid): a linear convolution with a centred full-size kernel (tap (a,e,f) at offset
+ * (a-S/2, e-S/2, f-S/2)), cropped to the input window, plus the skip D u:
+ *   y[b,c,i,j,l] = sum_{a,e,f} k[c,a,e,f] u[b,c,i+S/2-a,j+S/2-e,l+S/2-f] + D[c] u[b,c,i,j,l],
+ * summed with a outermost, then e, then f, ascending; out-of-range input taps contribute 0. */
+static void* or_points3d_worker(void* arg) {
+    or_job* J = (or_job*)arg;
+    const int64_t S = J->N, C = J->H, half = S / 2;
+    for (int64_t r = J->lo; r < J->hi; ++r) {
+        int64_t b = J->sel[5 * r], c = J->sel[5 * r + 1];
+        int64_t i = J->sel[5 * r + 2], j = J->sel[5 * r + 3], l = J->sel[5 * r + 4];
+        int64_t uoff = (b * C + c) * S * S * S, koff = c * S * S * S;
+        double acc = 0;
+        for (int64_t a = 0; a < S; ++a) {
+            int64_t ii = i + half - a;
+            if (ii < 0 || ii >= S) continue;
+            for (int64_t e = 0; e < S; ++e) {
+                int64_t jj = j + half - e;
+                if (jj < 0 || jj >= S) continue;
+                for (int64_t f = 0; f < S; ++f) {
+                    int64_t ll = l + half - f;
+                    if (ll < 0 || ll >= S) continue;
+                    acc += or_load(J->k, J->dt, koff + (a * S + e) * S + f) *
+                           or_load(J->u, J->dt, uoff + (ii * S + jj) * S + ll);
+                }
+            }
+        }
+        J->out[r] = acc + or_load(J->D, J->dt, c) * or_load(J->u, J->dt, uoff + (i * S + j) * S + l);
+    }
+    return NULL;
+}
+
+/* y[b,c,i,j,l] for each (b,c,i,j,l) in pts[5*npts]; u is [B][C][S][S][S], k is [C][S][S][S],
+ * D is [C]. */
+int oracle_conv3d_points(const void* u, const void* k, const void* D, int dt, int64_t B,
+                         int64_t C, int64_t S, const int64_t* pts, int64_t npts, double* out,
+                         int nthreads) {
+    if (!u || !k || !D || !out || (npts > 0 && !pts)) return -1;
+    if (B < 1 || C < 1 || S < 1 || npts < 0 || dt < 0 || dt > 2) return -1;
+    for (int64_t r = 0; r < npts; ++r) {
+        const int64_t* p = pts + 5 * r;
+        if (p[0] < 0 || p[0] >= B || p[1] < 0 || p[1] >= C) return -1;
+        for (int d = 2; d < 5; ++d)
+            if (p[d] < 0 || p[d] >= S) return -1;
+    }
+    or_job J = {u, NULL, NULL, k, D, dt, B, C, S, pts, out, 0, 0, 0};
+    or_parallel(or_points3d_worker, J, npts, nthreads);
+    return 0;
+}
+

@@ -55,6 +55,7 @@ def _load():
         lib.oracle_conv1d_short_points.argtypes = [vp, vp, vp, vp, vp, ip, i64, i64, i64, i64, vp, i64,
                                                    dp, ip]
         lib.oracle_conv2d_points.argtypes = [vp, vp, vp, ip, i64, i64, i64, vp, i64, dp, ip]
+        lib.oracle_conv3d_points.argtypes = [vp, vp, vp, ip, i64, i64, i64, vp, i64, dp, ip]
         lib.oracle_widen.argtypes = [vp, ip, i64, dp]
         lib.oracle_conv1d_bwd_rows.argtypes = [vp, vp, vp, vp, vp, vp, ip, i64, i64, i64, vp, i64,
                                                dp, dp, dp, ip]
@@ -265,6 +266,23 @@ def conv2d_points(u, k, D, pts, dt=None, nthreads=None):
                                       pts.shape[0], out.ctypes.data, _threads(nthreads))
     if rc:
         raise ValueError("oracle_conv2d_points rejected its arguments")
+    return out
+
+
+def conv3d_points(u, k, D, pts, dt=None, nthreads=None):
+    """Direct 3D sums y[b,c,i,j,l] for pts = [(b,c,i,j,l), ...] (u [B,C,S,S,S], k [C,S,S,S],
+    centred kernel, cropped to the window, plus D u); returns float64 [len(pts)]."""
+    dt = _dt_of(u, dt)
+    st = _storage(dt)
+    u, k, D = (_c(a, st) for a in (u, k, D))
+    B, C, S = u.shape[:3]
+    assert u.shape == (B, C, S, S, S) and k.shape == (C, S, S, S) and D.shape == (C,)
+    pts = np.ascontiguousarray(np.asarray(pts, np.int64).reshape(-1, 5))
+    out = np.empty(pts.shape[0], np.float64)
+    rc = _load().oracle_conv3d_points(_ptr(u), _ptr(k), _ptr(D), dt, B, C, S, _ptr(pts),
+                                      pts.shape[0], out.ctypes.data, _threads(nthreads))
+    if rc:
+        raise ValueError("oracle_conv3d_points rejected its arguments")
     return out
 
 
