@@ -71,6 +71,11 @@ def algorithmic_bytes(spec):
         act = 2 * spec.B * spec.C * spec.S * spec.S * s
         kf = spec.C * P * (P // 2 + 1) * 2 * s
         return act + kf + spec.C * s
+    if spec.kind == "3d":
+        P = 2 * spec.S
+        act = 2 * spec.B * spec.C * spec.S ** 3 * s
+        kf = spec.C * P * P * (P // 2 + 1) * 2 * s
+        return act + kf + spec.C * s
     n_in = 3 if spec.gated else 1
     act = (n_in + 1) * spec.B * spec.H * spec.N * s
     kf = spec.H * (spec.taps + 1) * 2 * s          # the filter's spectrum: taps, not N
@@ -91,6 +96,10 @@ def nominal_flops(spec):
     if spec.kind == "2d":
         P = 2 * spec.S
         per = 2 * 2.5 * P * P * math.log2(P * P) + 6 * P * (P // 2 + 1) + 2 * spec.S ** 2
+        return per * spec.B * spec.C
+    if spec.kind == "3d":
+        P = 2 * spec.S
+        per = 2 * 2.5 * P ** 3 * math.log2(P ** 3) + 6 * P * P * (P // 2 + 1) + 2 * spec.S ** 3
         return per * spec.B * spec.C
     g = 4 if spec.gated else 2
     if spec.L:  # partial: one transform pair of length M = 2 C per block of C outputs
@@ -247,6 +256,21 @@ def main():
         kf = run_filter()
         y = torch.empty_like(u)
         step = lambda: lconv.fftconv2d(u, kf, D, out=y)
+    elif spec.kind == "3d":
+        u, k, D = (to_dev(d[x], dt) for x in ("u", "k", "D"))
+        run_filter = lambda: lconv.filter_fft3d(k)
+        kf = run_filter()
+        y = torch.empty_like(u)
+        dtc = lconv.dtype_code(u.dtype)
+        wsb3 = lconv.lconv_fftconv3d_workspace_bytes(spec.B, spec.C, spec.S, dtc)
+        ws3 = torch.empty(max(wsb3, 1), dtype=torch.uint8, device="cuda")
+        stream = torch.cuda.current_stream()
+
+        def step():
+            st = lconv.lconv_fftconv3d_fwd(u.data_ptr(), kf.data_ptr(), D.data_ptr(), y.data_ptr(), spec.B,
+                                           spec.C, spec.S, dtc, ws3.data_ptr(), wsb3, stream.cuda_stream)
+            if st != 0:
+                raise lconv.LconvError(st, "lconv_fftconv3d_fwd")
     elif args.keep is not None:  # frequency-sparse convolution
         keep = int(args.keep, 0)
         u, q, v, k, D = (to_dev(d[x], dt) for x in ("u", "q", "v", "k", "D"))
@@ -331,7 +355,8 @@ def main():
         frac = bin(int(args.keep, 0) & ((1 << R) - 1)).count("1") / R
         s_ = {"f32": 4, "f16": 2, "bf16": 2}[dt]
         nbytes -= int(round((1 - frac) * spec.H * (spec.N + 1) * 2 * s_))
-    elems = spec.B * (spec.H if spec.kind == "1d" else spec.C) * (spec.N if spec.kind == "1d" else spec.S ** 2)
+    elems = spec.B * (spec.H if spec.kind == "1d" else spec.C) * \
+        {"1d": getattr(spec, "N", 0), "2d": getattr(spec, "S", 0) ** 2, "3d": getattr(spec, "S", 0) ** 3}[spec.kind]
     gbs = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (avg_ms * 1e-3) / 1e9
 

@@ -95,4 +95,21 @@ struct Conv2DArgs {
 };
 hipError_t launch_conv2d(int dtype, const Conv2DArgs& a, hipStream_t stream);
 
+// 3D (volumes of S^3, S = 16 or 32): the three passes for one chunk of units.  A unit is one
+// pair of batch images of one channel (unit = c * ceil(B/2) + pair), or one channel's kernel in
+// filter mode (unit = c).
+struct Conv3DArgs {
+    const void* u;       // [B][C][S][S][S]; filter mode: k [C][S][S][S]
+    const void* kf;      // filter spectrum [C][P][P][P] complex (io type), P = 2S
+    const void* D;       // [C]
+    void* y;             // [B][C][S][S][S]; filter mode: the filter spectrum
+    void* ws;            // workspace [nunit][S][P][P] complex (compute type; fp32 in filter mode)
+    const float* tw;     // exp(-2 pi i e / P), e < P (fp32 complex)
+    int64_t B, C, S;
+    int64_t unit0, nunit;
+    float inv_p3;        // 1 / P^3
+    int filter;
+};
+hipError_t launch_conv3d(int dtype, const Conv3DArgs& a, hipStream_t stream);
+
 }  // namespace lcv

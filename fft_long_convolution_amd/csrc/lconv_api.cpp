@@ -421,6 +421,107 @@ lconv_status_t lconv_fftconv2d_fwd(const void* u, const void* k_f, const void* D
     return hip_status(launch_conv2d(dtype, a, stream));
 }
 
+// ---- 3D ---------------------------------------------------------------------------------------
+
+namespace {
+bool s3_ok(int64_t S) { return S == 16 || S == 32; }
+// workspace bytes per unit: S slices of (2S)^2 complex in the pass's compute type
+size_t ws3_unit(int64_t S, size_t csz) { return (size_t)S * 4 * S * S * csz; }
+int64_t chunk3(int64_t units, int64_t S, size_t csz) {
+    int64_t per = (int64_t)(kChunkTarget / ws3_unit(S, csz));
+    if (per < 1) per = 1;
+    return per < units ? per : units;
+}
+}  // namespace
+
+size_t lconv_filter_fft3d_bytes(int64_t C, int64_t S, lconv_dtype_t dtype) {
+    int64_t t;
+    if (!dtype_ok(dtype) || C < 0 || !s3_ok(S)) return 0;
+    if (!mul_ok(C, 8 * S * S * S, &t) || !mul_ok(t, 2 * (int64_t)dtype_size(dtype), &t)) return 0;
+    return (size_t)t;
+}
+
+size_t lconv_filter_fft3d_workspace_bytes(int64_t C, int64_t S, lconv_dtype_t dtype) {
+    if (!dtype_ok(dtype) || C <= 0 || !s3_ok(S)) return 0;
+    return (size_t)chunk3(C, S, 8) * ws3_unit(S, 8);
+}
+
+size_t lconv_fftconv3d_workspace_bytes(int64_t B, int64_t C, int64_t S, lconv_dtype_t dtype) {
+    int64_t units;
+    if (!dtype_ok(dtype) || B <= 0 || C <= 0 || !s3_ok(S)) return 0;
+    if (!mul_ok(pairs_per_channel(B), C, &units)) return 0;
+    const size_t csz = work_complex_size(dtype, false);
+    return (size_t)chunk3(units, S, csz) * ws3_unit(S, csz);
+}
+
+lconv_status_t lconv_filter_fft3d(const void* k, void* k_f, int64_t C, int64_t S, lconv_dtype_t dtype,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
+    if (C < 0 || S < 0) return LCONV_ERR_INVALID_SHAPE;
+    if (C == 0) return LCONV_SUCCESS;
+    if (!s3_ok(S)) return LCONV_ERR_UNSUPPORTED;
+    if (!k || !k_f) return LCONV_ERR_NULL_POINTER;
+    if (!aligned16(k) || !aligned16(k_f)) return LCONV_ERR_MISALIGNED;
+    const size_t kf_bytes = lconv_filter_fft3d_bytes(C, S, dtype);
+    const size_t k_bytes = (size_t)(C * S * S * S) * dtype_size(dtype);
+    if (kf_bytes == 0) return LCONV_ERR_INVALID_SHAPE;
+    if (overlap(k_f, kf_bytes, k, k_bytes)) return LCONV_ERR_ALIASING;
+    const size_t need = lconv_filter_fft3d_workspace_bytes(C, S, dtype);
+    if (!workspace || workspace_bytes < need) return LCONV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return LCONV_ERR_MISALIGNED;
+    if (overlap(workspace, need, k_f, kf_bytes) || overlap(workspace, need, k, k_bytes)) return LCONV_ERR_ALIASING;
+    hipError_t err = hipSuccess;
+    const float* tw = dft_table(2 * S, &err);
+    if (!tw) return LCONV_ERR_HIP;
+    const int64_t per = chunk3(C, S, 8);
+    for (int64_t u0 = 0; u0 < C; u0 += per) {
+        Conv3DArgs a{};
+        a.u = k; a.y = k_f; a.ws = workspace; a.tw = tw;
+        a.B = 1; a.C = C; a.S = S; a.unit0 = u0; a.nunit = per < C - u0 ? per : C - u0;
+        a.inv_p3 = 1.0f / (float)(8 * S * S * S); a.filter = 1;
+        if (launch_conv3d(dtype, a, stream) != hipSuccess) return LCONV_ERR_HIP;
+    }
+    return LCONV_SUCCESS;
+}
+
+lconv_status_t lconv_fftconv3d_fwd(const void* u, const void* k_f, const void* D, void* y, int64_t B, int64_t C,
+                                   int64_t S, lconv_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+    if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
+    if (B < 0 || C < 0 || S < 0) return LCONV_ERR_INVALID_SHAPE;
+    int64_t elems, t;
+    if (!mul_ok(B, C, &t) || !mul_ok(S, S, &elems) || !mul_ok(elems, S, &elems) || !mul_ok(t, elems, &elems) ||
+        !mul_ok(elems, 8, &t))
+        return LCONV_ERR_INVALID_SHAPE;
+    if (B == 0 || C == 0) return LCONV_SUCCESS;
+    if (!s3_ok(S)) return LCONV_ERR_UNSUPPORTED;
+    if (!u || !k_f || !D || !y) return LCONV_ERR_NULL_POINTER;
+    if (!aligned16(u) || !aligned16(k_f) || !aligned16(D) || !aligned16(y)) return LCONV_ERR_MISALIGNED;
+    const size_t es = dtype_size(dtype), act = (size_t)elems * es;
+    const size_t kf_bytes = lconv_filter_fft3d_bytes(C, S, dtype);
+    if (overlap(y, act, u, act) || overlap(y, act, k_f, kf_bytes) || overlap(y, act, D, (size_t)C * es))
+        return LCONV_ERR_ALIASING;
+    const size_t need = lconv_fftconv3d_workspace_bytes(B, C, S, dtype);
+    if (!workspace || workspace_bytes < need) return LCONV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return LCONV_ERR_MISALIGNED;
+    if (overlap(workspace, need, y, act) || overlap(workspace, need, u, act) ||
+        overlap(workspace, need, k_f, kf_bytes) || overlap(workspace, need, D, (size_t)C * es))
+        return LCONV_ERR_ALIASING;
+    hipError_t err = hipSuccess;
+    const float* tw = dft_table(2 * S, &err);
+    if (!tw) return LCONV_ERR_HIP;
+    const int64_t units = pairs_per_channel(B) * C;
+    const int64_t per = chunk3(units, S, work_complex_size(dtype, false));
+    for (int64_t u0 = 0; u0 < units; u0 += per) {
+        Conv3DArgs a{};
+        a.u = u; a.kf = k_f; a.D = D; a.y = y; a.ws = workspace; a.tw = tw;
+        a.B = B; a.C = C; a.S = S; a.unit0 = u0; a.nunit = per < units - u0 ? per : units - u0;
+        a.inv_p3 = 1.0f / (float)(8 * S * S * S); a.filter = 0;
+        if (launch_conv3d(dtype, a, stream) != hipSuccess) return LCONV_ERR_HIP;
+    }
+    return LCONV_SUCCESS;
+}
+
 lconv_status_t lconv_release(void) {
     release_tables();
     return LCONV_SUCCESS;

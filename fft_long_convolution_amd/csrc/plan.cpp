@@ -190,6 +190,16 @@ const void* get_or_build(int kind, int ct, int64_t a, int64_t b,
 
 std::vector<uint8_t> build_any(int kind, int ct, int64_t a, int64_t b) {
     if (kind == 0) return build_fused_tables((int)a, ct);
+    if (kind == 2) {  // P-point DFT twiddles
+        std::vector<uint8_t> t((size_t)a * 8);
+        float* f = (float*)t.data();
+        for (int64_t e = 0; e < a; ++e) {
+            cplx w = omega(e, a);
+            f[2 * e] = (float)w.re;
+            f[2 * e + 1] = (float)w.im;
+        }
+        return t;
+    }
     // kind 1: column twiddles for (M = a, M1 = b)
     const int64_t M = a, M1 = b;
     const int64_t nlo = 2048, nhi = M / 2048 > 0 ? M / 2048 : 1;
@@ -236,6 +246,10 @@ bool col_tables(int64_t M, int64_t M1, ColTables* out, hipError_t* err) {
     out->hi = out->lo + 2 * nlo;
     out->col = out->hi + 2 * nhi;
     return true;
+}
+
+const float* dft_table(int64_t P, hipError_t* err) {
+    return (const float*)get_or_build(2, 0, P, 0, build_any, err);
 }
 
 int device_cu_count(hipError_t* err) {

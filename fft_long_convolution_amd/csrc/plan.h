@@ -50,6 +50,9 @@ struct ColTables {
 };
 bool col_tables(int64_t M, int64_t M1, ColTables* out, hipError_t* err);
 
+// exp(-2 pi i e / P) for e < P, fp32 complex, on the current device (3D path).
+const float* dft_table(int64_t P, hipError_t* err);
+
 // Cached device properties of the current device.
 int device_cu_count(hipError_t* err);
 

@@ -55,6 +55,11 @@ def load(path: str = LIB_PATH):
         "lconv_fftconv_sparse_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_uint32, i, vp]),
         "lconv_freq_blocks": (i, [i64]),
         "lconv_filter_fft2d": (i, [vp, vp, i64, i64, i, vp]),
+        "lconv_filter_fft3d_bytes": (sz, [i64, i64, i]),
+        "lconv_filter_fft3d_workspace_bytes": (sz, [i64, i64, i]),
+        "lconv_fftconv3d_workspace_bytes": (sz, [i64, i64, i64, i]),
+        "lconv_filter_fft3d": (i, [vp, vp, i64, i64, i, vp, sz, vp]),
+        "lconv_fftconv3d_fwd": (i, [vp, vp, vp, vp, i64, i64, i64, i, vp, sz, vp]),
         "lconv_fftconv2d_fwd": (i, [vp, vp, vp, vp, i64, i64, i64, i, vp]),
         "lconv_status_string": (ctypes.c_char_p, [i]),
         "lconv_abi_version": (i, []),
@@ -124,6 +129,26 @@ def lconv_filter_fft2d(k, k_f, C, S, dtype, stream):
 
 def lconv_fftconv2d_fwd(u, k_f, D, y, B, C, S, dtype, stream):
     return load().lconv_fftconv2d_fwd(u, k_f, D, y, B, C, S, dtype, stream)
+
+
+def lconv_filter_fft3d_bytes(C, S, dtype):
+    return load().lconv_filter_fft3d_bytes(C, S, dtype)
+
+
+def lconv_filter_fft3d_workspace_bytes(C, S, dtype):
+    return load().lconv_filter_fft3d_workspace_bytes(C, S, dtype)
+
+
+def lconv_fftconv3d_workspace_bytes(B, C, S, dtype):
+    return load().lconv_fftconv3d_workspace_bytes(B, C, S, dtype)
+
+
+def lconv_filter_fft3d(k, k_f, C, S, dtype, workspace, workspace_bytes, stream):
+    return load().lconv_filter_fft3d(k, k_f, C, S, dtype, workspace, workspace_bytes, stream)
+
+
+def lconv_fftconv3d_fwd(u, k_f, D, y, B, C, S, dtype, workspace, workspace_bytes, stream):
+    return load().lconv_fftconv3d_fwd(u, k_f, D, y, B, C, S, dtype, workspace, workspace_bytes, stream)
 
 
 def lconv_abi_version():
@@ -251,6 +276,32 @@ def filter_fft2d(k, stream=None):
     k_f = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k.device)
     _check(lconv_filter_fft2d(_ptr(k), k_f.data_ptr(), C, S, dt, _stream(stream)), "lconv_filter_fft2d")
     return k_f
+
+
+def filter_fft3d(k, stream=None):
+    """Opaque 3D filter spectrum for k [C, S, S, S]."""
+    torch = _torch()
+    C, S = k.shape[0], k.shape[1]
+    dt = dtype_code(k.dtype)
+    k_f = torch.empty(max(lconv_filter_fft3d_bytes(C, S, dt), 1), dtype=torch.uint8, device=k.device)
+    wsb = lconv_filter_fft3d_workspace_bytes(C, S, dt)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=k.device)
+    _check(lconv_filter_fft3d(_ptr(k), k_f.data_ptr(), C, S, dt, ws.data_ptr(), wsb, _stream(stream)),
+           "lconv_filter_fft3d")
+    return k_f
+
+
+def fftconv3d(u, k_f, D, out=None, stream=None):
+    """3D centred linear convolution plus skip for u [B, C, S, S, S]."""
+    torch = _torch()
+    B, C, S = u.shape[:3]
+    dt = dtype_code(u.dtype)
+    y = torch.empty_like(u) if out is None else out
+    wsb = lconv_fftconv3d_workspace_bytes(B, C, S, dt)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=u.device)
+    _check(lconv_fftconv3d_fwd(_ptr(u), _ptr(k_f), _ptr(D), _ptr(y), B, C, S, dt, ws.data_ptr(), wsb,
+                               _stream(stream)), "lconv_fftconv3d_fwd")
+    return y
 
 
 def fftconv2d(u, k_f, D, out=None, stream=None):

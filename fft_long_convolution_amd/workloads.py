@@ -122,6 +122,21 @@ class Conv2DSpec:
         return "2d"
 
 
+@dataclasses.dataclass(frozen=True)
+class Conv3DSpec:
+    name: str
+    B: int
+    C: int
+    S: int
+    dtype: str
+    decay: float = 0.1                        # exp(-decay * (|da| + |de| + |df|)), centred taps
+    seed: int = 0
+
+    @property
+    def kind(self):
+        return "3d"
+
+
 # The five workloads (seed 1000 + i for the i-th, 1-based).
 WORKLOADS = {
     "causal_f32_b1_h4_n1024": Conv1DSpec(
@@ -135,6 +150,9 @@ WORKLOADS = {
         "very_long_bf16_b1_h64_n2097152", 1, 64, 2097152, "bf16", decay=1e-6, seed=1004),
     "hyenand_2d_bf16_b8_c256_s128": Conv2DSpec(
         "hyenand_2d_bf16_b8_c256_s128", 8, 256, 128, "bf16", decay=0.05, seed=1005),
+    # volumes: the 2D operation one dimension up
+    "hyenand_3d_bf16_b4_c128_s32": Conv3DSpec(
+        "hyenand_3d_bf16_b4_c128_s32", 4, 128, 32, "bf16", decay=0.1, seed=1007),
     # the 2^21-long shape with a short (4096-tap) filter: the partial convolution
     "partial_bf16_b1_h64_n2097152_l4096": Conv1DSpec(
         "partial_bf16_b1_h64_n2097152_l4096", 1, 64, 2097152, "bf16", decay=1e-3, seed=1006,
@@ -210,9 +228,37 @@ def make_2d(spec: Conv2DSpec) -> dict:
     return out
 
 
+def spec_3d(B, C, S, dtype, seed=7, decay=0.1) -> Conv3DSpec:
+    return Conv3DSpec(f"custom3d_{dtype}_b{B}_c{C}_s{S}", B, C, S, dtype, decay=decay, seed=seed)
+
+
+def make_3d(spec: Conv3DSpec) -> dict:
+    """Draw u [B,C,S,S,S], k [C,S,S,S] (centred envelope), D [C] (draw order u, k_raw, D)."""
+    rng = np.random.default_rng(spec.seed)
+    B, C, S = spec.B, spec.C, spec.S
+    out = {"spec": spec, "dtype": spec.dtype}
+    out["u"] = to_storage(rng.standard_normal((B, C, S, S, S), dtype=np.float32), spec.dtype)
+    k = rng.standard_normal((C, S, S, S))
+    r = np.abs(np.arange(S) - S // 2).astype(np.float64)
+    env = np.exp(-spec.decay * (r[:, None, None] + r[None, :, None] + r[None, None, :]))
+    out["k"] = to_storage(k * env[None], spec.dtype)
+    out["D"] = to_storage(rng.standard_normal(C), spec.dtype)
+    return out
+
+
+def sample_points_3d(B, C, S, n=4096, seed=2007):
+    """(b,c,i,j,l) voxels: uniform draws plus the corners and faces of the window."""
+    rng = np.random.default_rng(seed)
+    uni = np.stack([rng.integers(0, B, n), rng.integers(0, C, n)] +
+                   [rng.integers(0, S, n) for _ in range(3)], axis=1)
+    edge = [0, 1, S // 2 - 1, S // 2, S - 2, S - 1]
+    special = [(B - 1, C - 1, i, j, l) for i in edge for j in (0, S - 1) for l in edge]
+    return np.ascontiguousarray(np.concatenate([uni, np.asarray(special)], 0).astype(np.int64))
+
+
 def make(name_or_spec) -> dict:
     spec = WORKLOADS[name_or_spec] if isinstance(name_or_spec, str) else name_or_spec
-    return make_1d(spec) if spec.kind == "1d" else make_2d(spec)
+    return {"1d": make_1d, "2d": make_2d, "3d": make_3d}[spec.kind](spec)
 
 
 # --------------------------------------------------------------------------------------------

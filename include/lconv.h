@@ -207,6 +207,33 @@ lconv_status_t lconv_fftconv2d_fwd(const void* u, const void* k_f, const void* D
                                    int64_t B, int64_t C, int64_t S, lconv_dtype_t dtype,
                                    hipStream_t stream);
 
+/* ---- 3D (HyenaND-style volumes) ------------------------------------------------------------ */
+
+/*
+ * The 2D operation one dimension up ("Native Multi-Dimensional Subquadratic Operators via Input
+ * Dependent Long Convolutions", abstract: global convolutions on the native multi-dimensional
+ * grid): a linear convolution with a centred full-size kernel (tap (a,e,f) at offset
+ * (a-S/2, e-S/2, f-S/2)), cropped to the input window, plus the skip:
+ *   y[b,c,i,j,l] = sum_{a,e,f} k[c,a,e,f] u[b,c,i+S/2-a,j+S/2-e,l+S/2-f] + D[c] u[b,c,i,j,l]
+ * u, y [B][C][S][S][S] dtype; k [C][S][S][S]; D [C].  Supported: S = 16 or 32, any dtype.
+ * The (2S)^3 transform does not fit one workgroup: both calls run passes over a caller-owned
+ * workspace (sizes from the queries below; processed in chunks of at most 64 MB).
+ */
+size_t lconv_filter_fft3d_bytes(int64_t C, int64_t S, lconv_dtype_t dtype);
+size_t lconv_filter_fft3d_workspace_bytes(int64_t C, int64_t S, lconv_dtype_t dtype);
+size_t lconv_fftconv3d_workspace_bytes(int64_t B, int64_t C, int64_t S, lconv_dtype_t dtype);
+
+/* 3D filter spectrum: the (2S)^3 DFT of each zero-padded kernel, scaled by 1/(2S)^3, in the
+ * library's order (opaque), computed in fp32 and stored in dtype. */
+lconv_status_t lconv_filter_fft3d(const void* k, void* k_f, int64_t C, int64_t S,
+                                  lconv_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/* 3D convolution (definition above); k_f from lconv_filter_fft3d. */
+lconv_status_t lconv_fftconv3d_fwd(const void* u, const void* k_f, const void* D, void* y,
+                                   int64_t B, int64_t C, int64_t S, lconv_dtype_t dtype,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ---- misc ------------------------------------------------------------------------------- */
 
 const char* lconv_status_string(lconv_status_t s);

@@ -207,3 +207,22 @@ def test_sparse_blocks_and_validation():
     if not torch.cuda.is_available():
         assert sparse(keep=0) == HIPERR               # valid (nothing kept): fails only at HIP
         assert sparse(N=4096, keep=0xffffffff) == HIPERR
+
+
+def test_3d_sizes_and_validation():
+    assert lconv.lconv_filter_fft3d_bytes(4, 32, BF16) == 4 * 64 ** 3 * 4
+    assert lconv.lconv_filter_fft3d_bytes(4, 16, F32) == 4 * 32 ** 3 * 8
+    assert lconv.lconv_filter_fft3d_bytes(4, 24, BF16) == 0                # S must be 16 or 32
+    assert lconv.lconv_fftconv3d_workspace_bytes(4, 128, 32, BF16) > 0
+    assert lconv.lconv_filter_fft3d_workspace_bytes(128, 32, BF16) > 0
+    f3 = lambda u=G[0], kf=G[1], D=G[2], y=G[3], B=2, C=3, S=16, dt=BF16, ws=G[4], wsb=1 << 30: \
+        lconv.lconv_fftconv3d_fwd(u, kf, D, y, B, C, S, dt, ws, wsb, None)
+    assert f3(dt=5) == UNSUP
+    assert f3(S=24) == UNSUP
+    assert f3(B=-1) == SHAPE
+    assert f3(u=None) == NULLP
+    assert f3(D=G[2] + 2) == MISAL
+    assert f3(y=G[0]) == ALIAS
+    assert f3(ws=None) == WSERR
+    assert f3(wsb=16) == WSERR
+    assert f3(B=0) == OK

@@ -90,3 +90,14 @@ def test_short_filter_workload_draws_l_taps():
     assert spec.taps == 24 and wl.spec_1d(1, 1, 64, "f32").taps == 64
     long = wl.WORKLOADS["partial_bf16_b1_h64_n2097152_l4096"]
     assert (long.N, long.L, long.dtype) == (2 ** 21, 4096, "bf16")
+
+
+def test_3d_workload_draws():
+    spec = wl.spec_3d(3, 2, 16, "f32", seed=5)
+    d = wl.make(spec)
+    assert d["u"].shape == (3, 2, 16, 16, 16) and d["k"].shape == (2, 16, 16, 16)
+    assert d["D"].shape == (2,)
+    k = d["k"].astype(np.float64)
+    assert np.abs(k[:, 8, 8, 8]).mean() > np.abs(k[:, 0, 0, 0]).mean()   # centred envelope
+    pts = wl.sample_points_3d(3, 2, 16)
+    assert pts.shape[1] == 5 and pts[:, 2:].max() < 16
