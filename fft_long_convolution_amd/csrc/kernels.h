@@ -95,6 +95,12 @@ struct Conv2DArgs {
 };
 hipError_t launch_conv2d(int dtype, const Conv2DArgs& a, hipStream_t stream);
 
+// Row staging for N not a multiple of 8 (stage.hip): [rows][N] <-> [rows][N8] with a zero tail.
+hipError_t launch_pad_rows(const void* src, void* dst, int64_t rows, int64_t N, int64_t N8, int esize,
+                           hipStream_t stream);
+hipError_t launch_unpad_rows(const void* src, void* dst, int64_t rows, int64_t N, int64_t N8, int esize,
+                             hipStream_t stream);
+
 // 3D (volumes of S^3, S = 16 or 32): the three passes for one chunk of units.  A unit is one
 // pair of batch images of one channel (unit = c * ceil(B/2) + pair), or one channel's kernel in
 // filter mode (unit = c).

@@ -34,7 +34,17 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
-bool n_supported(int64_t N) { return N >= 1 && N <= LCONV_MAX_N && (N % 8) == 0; }
+// lengths the forward call and the filter transform take (any N: ragged rows are staged)
+bool n_in_range(int64_t N) { return N >= 1 && N <= LCONV_MAX_N; }
+// lengths the kernels take directly: rows of whole 16-byte groups
+bool n_supported(int64_t N) { return n_in_range(N) && (N % 8) == 0; }
+int64_t round8(int64_t N) { return (N + 7) / 8 * 8; }
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+// staging for N not a multiple of 8: `tensors` zero-padded copies of [rows][round8(N)]
+size_t staging_bytes(int64_t rows, int64_t N, lconv_dtype_t dt, int tensors) {
+    if (N % 8 == 0) return 0;
+    return (size_t)tensors * round256((size_t)rows * (size_t)round8(N) * dtype_size(dt));
+}
 
 // sequences = complex transforms: pairs of batch rows per channel
 int64_t pairs_per_channel(int64_t B) { return (B + 1) / 2; }
@@ -46,6 +56,13 @@ int64_t chunk_seqs(int64_t total, int64_t M, size_t csz) {
 }
 
 lconv_status_t hip_status(hipError_t e) { return e == hipSuccess ? LCONV_SUCCESS : LCONV_ERR_HIP; }
+
+// the calls on rows of whole 16-byte groups (N a multiple of 8), after validation
+lconv_status_t filter_fft_aligned(const void* k, void* k_f, int64_t H, int64_t N, lconv_dtype_t dtype,
+                                  void* workspace, hipStream_t stream);
+lconv_status_t fftconv_fwd_aligned(const void* u, const void* k_f, const void* D, void* y, const void* q,
+                                   const void* v, int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype,
+                                   void* workspace, hipStream_t stream);
 
 }  // namespace
 
@@ -70,27 +87,31 @@ const char* lconv_status_string(lconv_status_t s) {
 size_t lconv_filter_fft_bytes(int64_t H, int64_t N, lconv_dtype_t dtype) {
     Plan1D p;
     int64_t t;
-    if (!dtype_ok(dtype) || H < 0 || !n_supported(N) || !make_plan_1d(N, &p)) return 0;
+    if (!dtype_ok(dtype) || H < 0 || !n_in_range(N) || !make_plan_1d(N, &p)) return 0;
     if (!mul_ok(H, p.M, &t) || !mul_ok(t, 2 * (int64_t)dtype_size(dtype), &t)) return 0;
     return (size_t)t;
 }
 
 size_t lconv_filter_fft_workspace_bytes(int64_t H, int64_t N, lconv_dtype_t dtype) {
     Plan1D p;
-    if (!dtype_ok(dtype) || H < 0 || !n_supported(N) || !make_plan_1d(N, &p)) return 0;
-    if (!p.multipass || H == 0) return 0;
+    if (!dtype_ok(dtype) || H < 0 || !n_in_range(N) || !make_plan_1d(N, &p)) return 0;
+    if (H == 0) return 0;
+    const size_t stage = staging_bytes(H, N, dtype, 1);
+    if (!p.multipass) return stage;
     const size_t csz = work_complex_size(dtype, true);
-    return (size_t)chunk_seqs(H, p.M, csz) * (size_t)p.M * csz;
+    return stage + (size_t)chunk_seqs(H, p.M, csz) * (size_t)p.M * csz;
 }
 
 size_t lconv_fftconv_workspace_bytes(int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype) {
     Plan1D p;
-    int64_t seqs;
-    if (!dtype_ok(dtype) || B < 0 || H < 0 || !n_supported(N) || !make_plan_1d(N, &p)) return 0;
-    if (!p.multipass || B == 0 || H == 0) return 0;
-    if (!mul_ok(pairs_per_channel(B), H, &seqs)) return 0;
+    int64_t seqs, rows;
+    if (!dtype_ok(dtype) || B < 0 || H < 0 || !n_in_range(N) || !make_plan_1d(N, &p)) return 0;
+    if (B == 0 || H == 0) return 0;
+    if (!mul_ok(pairs_per_channel(B), H, &seqs) || !mul_ok(B, H, &rows)) return 0;
+    const size_t stage = staging_bytes(rows, N, dtype, 4);  // u, q, v, y
+    if (!p.multipass) return stage;
     const size_t csz = work_complex_size(dtype, false);
-    return (size_t)chunk_seqs(seqs, p.M, csz) * (size_t)p.M * csz;
+    return stage + (size_t)chunk_seqs(seqs, p.M, csz) * (size_t)p.M * csz;
 }
 
 size_t lconv_filter_fft2d_bytes(int64_t C, int64_t S, lconv_dtype_t dtype) {
@@ -108,7 +129,7 @@ lconv_status_t lconv_filter_fft(const void* k, void* k_f, int64_t H, int64_t N, 
     int64_t t;
     if (!mul_ok(H, N, &t) || !mul_ok(t, 8, &t)) return LCONV_ERR_INVALID_SHAPE;
     if (H == 0 || N == 0) return LCONV_SUCCESS;
-    if (!n_supported(N)) return LCONV_ERR_UNSUPPORTED;
+    if (!n_in_range(N)) return LCONV_ERR_UNSUPPORTED;
     if (!k || !k_f) return LCONV_ERR_NULL_POINTER;
     if (!aligned16(k) || !aligned16(k_f)) return LCONV_ERR_MISALIGNED;
     const size_t kf_bytes = lconv_filter_fft_bytes(H, N, dtype);
@@ -121,6 +142,21 @@ lconv_status_t lconv_filter_fft(const void* k, void* k_f, int64_t H, int64_t N, 
         if (overlap(workspace, need, k_f, kf_bytes) || overlap(workspace, need, k, (size_t)(H * N) * dtype_size(dtype)))
             return LCONV_ERR_ALIASING;
     }
+    if (N % 8 != 0) {  // ragged rows: stage zero-padded copies (the padding taps are zero)
+        const size_t stage = staging_bytes(H, N, dtype, 1);
+        if (launch_pad_rows(k, workspace, H, N, round8(N), (int)dtype_size(dtype), stream) != hipSuccess)
+            return LCONV_ERR_HIP;
+        return filter_fft_aligned(workspace, k_f, H, round8(N), dtype, (char*)workspace + stage, stream);
+    }
+    return filter_fft_aligned(k, k_f, H, N, dtype, workspace, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+lconv_status_t filter_fft_aligned(const void* k, void* k_f, int64_t H, int64_t N, lconv_dtype_t dtype,
+                                  void* workspace, hipStream_t stream) {
     Plan1D p;
     make_plan_1d(N, &p);
     hipError_t err = hipSuccess;
@@ -156,6 +192,10 @@ lconv_status_t lconv_filter_fft(const void* k, void* k_f, int64_t H, int64_t N, 
     return LCONV_SUCCESS;
 }
 
+}  // namespace
+
+extern "C" {
+
 lconv_status_t lconv_fftconv_fwd(const void* u, const void* k_f, const void* D, void* y, const void* q,
                                  const void* v, int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -164,7 +204,7 @@ lconv_status_t lconv_fftconv_fwd(const void* u, const void* k_f, const void* D, 
     int64_t elems, t;
     if (!mul_ok(B, H, &t) || !mul_ok(t, N, &elems) || !mul_ok(elems, 8, &t)) return LCONV_ERR_INVALID_SHAPE;
     if (B == 0 || H == 0 || N == 0) return LCONV_SUCCESS;
-    if (!n_supported(N)) return LCONV_ERR_UNSUPPORTED;
+    if (!n_in_range(N)) return LCONV_ERR_UNSUPPORTED;
     if (!u || !k_f || !D || !y) return LCONV_ERR_NULL_POINTER;
     if (!aligned16(u) || !aligned16(k_f) || !aligned16(D) || !aligned16(y) || (q && !aligned16(q)) ||
         (v && !aligned16(v)))
@@ -184,6 +224,31 @@ lconv_status_t lconv_fftconv_fwd(const void* u, const void* k_f, const void* D, 
             overlap(workspace, need, k_f, kf_bytes) || overlap(workspace, need, D, (size_t)H * es))
             return LCONV_ERR_ALIASING;
     }
+    if (N % 8 != 0) {
+        // ragged rows: zero-padded copies of u, q, v (zero inputs past N change no output before
+        // N), the aligned path at round8(N), and the first N outputs of each row copied back
+        const int64_t rows = B * H, N8 = round8(N);
+        const size_t one = staging_bytes(rows, N, dtype, 1);
+        char* st = (char*)workspace;
+        void *su = st, *sq = q ? st + one : nullptr, *sv = v ? st + 2 * one : nullptr, *sy = st + 3 * one;
+        const int esz = (int)es;
+        if (launch_pad_rows(u, su, rows, N, N8, esz, stream) != hipSuccess) return LCONV_ERR_HIP;
+        if (q && launch_pad_rows(q, sq, rows, N, N8, esz, stream) != hipSuccess) return LCONV_ERR_HIP;
+        if (v && launch_pad_rows(v, sv, rows, N, N8, esz, stream) != hipSuccess) return LCONV_ERR_HIP;
+        const lconv_status_t r = fftconv_fwd_aligned(su, k_f, D, sy, sq, sv, B, H, N8, dtype, st + 4 * one, stream);
+        if (r != LCONV_SUCCESS) return r;
+        return hip_status(launch_unpad_rows(sy, y, rows, N, N8, esz, stream));
+    }
+    return fftconv_fwd_aligned(u, k_f, D, y, q, v, B, H, N, dtype, workspace, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+lconv_status_t fftconv_fwd_aligned(const void* u, const void* k_f, const void* D, void* y, const void* q,
+                                   const void* v, int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype,
+                                   void* workspace, hipStream_t stream) {
     Plan1D p;
     make_plan_1d(N, &p);
     hipError_t err = hipSuccess;
@@ -221,11 +286,16 @@ lconv_status_t lconv_fftconv_fwd(const void* u, const void* k_f, const void* D, 
     return LCONV_SUCCESS;
 }
 
+}  // namespace
+
+extern "C" {
+
 int lconv_freq_blocks(int64_t N) {
     Plan1D p;
     if (!n_supported(N) || N > LCONV_BWD_MAX_N || !make_plan_1d(N, &p) || p.multipass) return 0;
     return p.R;
 }
+
 
 lconv_status_t lconv_fftconv_sparse_fwd(const void* u, const void* k_f, const void* D, void* y, const void* q,
                                         const void* v, int64_t B, int64_t H, int64_t N, uint32_t keep,

@@ -86,7 +86,8 @@ size_t lconv_filter_fft2d_bytes(int64_t C, int64_t S, lconv_dtype_t dtype);
  *   k         [H][N] dtype, device
  *   k_f       lconv_filter_fft_bytes(H, N, dtype) bytes, device, written
  *   workspace lconv_filter_fft_workspace_bytes(H, N, dtype) bytes (may be NULL if that is 0)
- * Supported: 1 <= N <= LCONV_MAX_N, N a multiple of 8.
+ * Supported: 1 <= N <= LCONV_MAX_N.  When N is not a multiple of 8 the rows are staged into
+ * the workspace, zero-padded to the next multiple of 8 (the zero taps change nothing).
  */
 lconv_status_t lconv_filter_fft(const void* k, void* k_f, int64_t H, int64_t N,
                                 lconv_dtype_t dtype, void* workspace, size_t workspace_bytes,
@@ -103,6 +104,9 @@ lconv_status_t lconv_filter_fft(const void* k, void* k_f, int64_t H, int64_t N,
  *   D         [H] dtype, device
  *   q, v      [B][H][N] dtype, device, or NULL (then treated as all ones)
  *   workspace lconv_fftconv_workspace_bytes(B, H, N, dtype) bytes (may be NULL if that is 0)
+ * Supported: 1 <= N <= LCONV_MAX_N.  When N is not a multiple of 8, u, q, v are staged into the
+ * workspace zero-padded to the next multiple of 8 (inputs past N change no output before N),
+ * and the first N outputs of each row are copied back: two more passes over the data.
  * Arithmetic: fp32 I/O uses fp32 matrix-core products; bf16 and fp16 use bf16/fp16
  * matrix-core operands with fp32 accumulation, fp32 twiddles and fp32 pointwise products.
  */
@@ -123,7 +127,8 @@ lconv_status_t lconv_fftconv_fwd(const void* u, const void* k_f, const void* D, 
  * cost no transform work.  `keep` must be closed under r -> (R - r) mod R (otherwise the filter
  * would not be real): LCONV_ERR_UNSUPPORTED otherwise, as for bits at or above R.
  *   u, y, q, v, k_f, D   as for lconv_fftconv_fwd (k_f from lconv_filter_fft(k, ..., H, N, dtype))
- * Supported: N <= 4096 (one workgroup per transform).  R: lconv_freq_blocks(N).  No workspace.
+ * Supported: N <= 4096 (one workgroup per transform), N a multiple of 8.  R: lconv_freq_blocks(N).
+ * No workspace.
  */
 lconv_status_t lconv_fftconv_sparse_fwd(const void* u, const void* k_f, const void* D, void* y,
                                         const void* q, const void* v, int64_t B, int64_t H,

@@ -41,7 +41,10 @@ def test_size_queries():
     assert lconv.lconv_fftconv_workspace_bytes(16, 768, 4096, BF16) == 0  # single pass
     assert lconv.lconv_fftconv_workspace_bytes(4, 256, 65536, F16) > 0    # multi-pass
     assert lconv.lconv_filter_fft_workspace_bytes(64, 2 ** 21, BF16) > 0
-    assert lconv.lconv_filter_fft_bytes(1, 12, BF16) == 0                 # N % 8 != 0
+    assert lconv.lconv_filter_fft_bytes(1, 12, BF16) == 512 * 4           # any N (ragged rows staged)
+    assert lconv.lconv_fftconv_workspace_bytes(2, 3, 12, BF16) == 4 * 256  # 4 staged [6][16] tensors
+    assert lconv.lconv_fftconv_workspace_bytes(2, 3, 16, BF16) == 0
+    assert lconv.lconv_filter_fft_workspace_bytes(3, 12, BF16) == 256
     assert lconv.lconv_filter_fft_bytes(1, 2 ** 22 + 8, BF16) == 0        # too long
     assert lconv.lconv_filter_fft_bytes(1, 2300000, BF16) == 2 ** 23 * 4   # 2.3M: M = 2^23
     assert lconv.lconv_filter_fft_bytes(1, 8, 7) == 0                     # bad dtype
@@ -58,7 +61,7 @@ def test_fwd_validation_errors():
     assert fwd(B=-1) == SHAPE
     assert fwd(N=-8) == SHAPE
     assert fwd(B=2 ** 40, H=2 ** 20, N=2 ** 10) == SHAPE                 # overflow
-    assert fwd(N=12) == UNSUP
+    assert fwd(N=12) == WSERR                                              # ragged: staging space
     assert fwd(N=2 ** 22 + 8) == UNSUP
     assert fwd(u=None) == NULLP
     assert fwd(kf=None) == NULLP

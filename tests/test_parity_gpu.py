@@ -147,3 +147,40 @@ def test_empty_and_stream(lc):
         y1 = lc.fftconv(u, kf, D, stream=s)
     s.synchronize()
     assert np.array_equal(from_dev(y1, "bf16"), y0)
+
+
+RAGGED_N = [1, 7, 13, 100, 1001, 4095, 4097]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("N", RAGGED_N)
+@pytest.mark.parametrize("B,gated", [(1, False), (3, True)])
+def test_ragged_lengths_full_rows(lc, nthreads, dtype, N, B, gated):
+    """N not a multiple of 8: rows staged zero-padded through the workspace."""
+    H = 2
+    spec = wl.spec_1d(B, H, N, dtype, gated=gated, seed=1300 + N + B)
+    say(f"[ragged] dtype={dtype} B={B} H={H} N={N} gated={gated} seed={spec.seed}")
+    d = wl.make(spec)
+    y, _ = run_1d(lc, d)
+    assert y.shape == (B, H, N) and np.all(np.isfinite(y))
+    rows = [(b, h) for b in range(B) for h in range(H)]
+    ref = oracle_rows(d, rows, nthreads).reshape(B, H, N)
+    err = rel_l2_rows(y, ref).max()
+    say(f"   max rel L2 = {err:.3e} (tol {TOL[dtype]})")
+    assert err <= TOL[dtype]
+
+
+def test_ragged_multipass_sampled(lc, nthreads):
+    """A ragged length past one workgroup (multi-pass path), sampled."""
+    B, H, N = 3, 2, 65537
+    spec = wl.spec_1d(B, H, N, "bf16", gated=True, seed=1399, decay=1e-4)
+    say(f"[ragged long] B={B} H={H} N={N} seed={spec.seed}")
+    d = wl.make(spec)
+    y, _ = run_1d(lc, d)
+    pts = wl.sample_points_1d(B, H, N, seed=2400)
+    ref = oracle.conv1d_points(d["u"], d["k"], d["D"], pts, q=d["q"], v=d["v"], dt=oracle.DT_BF16,
+                               nthreads=nthreads)
+    got = y[pts[:, 0], pts[:, 1], pts[:, 2]]
+    err = rel_l2(got, ref)
+    say(f"   pooled rel L2 over {len(pts)} positions = {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= TOL["bf16"]
