@@ -1,5 +1,5 @@
 """float64 CPU oracle for the causal long convolution (1D: forward, short filters, frequency-sparse
-filters, gradients) and the cropped 2D and 3D linear convolutions.
+filters, state-space filters, gradients) and the cropped 2D and 3D linear convolutions.
 
 TEST INFRASTRUCTURE ONLY: tests, the smoke check and the bench's CPU-baseline leg may import it;
 the product path (the HIP library and its Python binding) never does, and the two share no code.
@@ -7,6 +7,7 @@ the product path (the HIP library and its Python binding) never does, and the tw
 from .oracle import (  # noqa: F401
     DT_F32, DT_F16, DT_BF16,
     build, conv1d_rows, conv1d_points, conv2d_points, conv2d_dft, conv3d_points, widen,
+    ssm_kernel, ssm_rows,
     conv1d_bwd_rows, conv1d_bwd_dk, conv1d_short_points, conv1d_circ_rows, sparse_filter,
     transform_length,
     conv1d_toeplitz, conv1d_python_int,

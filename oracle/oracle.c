@@ -608,3 +608,88 @@ int oracle_conv3d_points(const void* u, const void* k, const void* D, int dt, in
     return 0;
 }
 
+/* ------------------------------------------------------------------------------------------ */
+/* Diagonal state-space filters (FlashConv page, Mechanism: state passed between chunks)        */
+/* ------------------------------------------------------------------------------------------ */
+/* A channel's filter is generated by NS complex modes: k[h,t] = Re sum_n W[h,n] lam[h,n]^t.  The
+ * convolution with it is the state recurrence run forward in time,
+ *     s_n[t] = lam_n s_n[t-1] + x[t]   (s_n[-1] = 0),    y[t] = Re sum_n W_n s_n[t] + D x[t],
+ * x = q u, then y *= v; this evaluates it that way (float64 complex, t ascending).  lam and W
+ * are float64 complex [H][NS] (interleaved re, im). */
+typedef struct {
+    or_job j;
+    const double *lam, *W;
+    int64_t NS;
+} or_ssm_job;
+
+static void* or_ssm_rows_worker(void* arg) {
+    or_ssm_job* S = (or_ssm_job*)arg;
+    const or_job* J = &S->j;
+    const int64_t N = J->N, NS = S->NS;
+    double* x = (double*)malloc(sizeof(double) * (size_t)N);
+    double* sr = (double*)malloc(sizeof(double) * (size_t)NS);
+    double* si = (double*)malloc(sizeof(double) * (size_t)NS);
+    for (int64_t r = J->lo; r < J->hi; ++r) {
+        int64_t b = J->sel[2 * r], h = J->sel[2 * r + 1];
+        or_row_x(J, b, h, N, x);
+        const double* lam = S->lam + 2 * h * NS;
+        const double* W = S->W + 2 * h * NS;
+        double d = or_load(J->D, J->dt, h);
+        int64_t off = (b * J->H + h) * N;
+        for (int64_t n = 0; n < NS; ++n) sr[n] = si[n] = 0;
+        for (int64_t t = 0; t < N; ++t) {
+            double acc = 0;
+            for (int64_t n = 0; n < NS; ++n) {
+                const double lr = lam[2 * n], li = lam[2 * n + 1];
+                const double nr = lr * sr[n] - li * si[n] + x[t];
+                const double ni = lr * si[n] + li * sr[n];
+                sr[n] = nr;
+                si[n] = ni;
+                acc += W[2 * n] * nr - W[2 * n + 1] * ni;
+            }
+            double val = acc + d * x[t];
+            if (J->v) val *= or_load(J->v, J->dt, off + t);
+            J->out[r * N + t] = val;
+        }
+    }
+    free(x);
+    free(sr);
+    free(si);
+    return NULL;
+}
+
+static void* or_ssm_trampoline(void* arg) { return or_ssm_rows_worker(arg); }
+
+/* Full rows of the convolution with the state-space filter (lam, W), by the recurrence. */
+int oracle_ssm_rows(const void* u, const void* q, const void* v, const double* lam, const double* W,
+                    const void* D, int dt, int64_t B, int64_t H, int64_t N, int64_t NS,
+                    const int64_t* rows, int64_t nrows, double* out, int nthreads) {
+    if (!u || !lam || !W || !D || !out || (nrows > 0 && !rows)) return -1;
+    if (B < 1 || H < 1 || N < 1 || NS < 1 || nrows < 0 || dt < 0 || dt > 2) return -1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[2 * r] < 0 || rows[2 * r] >= B || rows[2 * r + 1] < 0 || rows[2 * r + 1] >= H)
+            return -1;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((int64_t)nthreads > nrows) nthreads = (int)(nrows > 0 ? nrows : 1);
+    or_ssm_job* jobs = (or_ssm_job*)calloc((size_t)nthreads, sizeof(or_ssm_job));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    int64_t per = (nrows + nthreads - 1) / nthreads;
+    int used = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        int64_t lo = (int64_t)i * per, hi = lo + per < nrows ? lo + per : nrows;
+        if (lo >= hi) break;
+        or_job J = {u, q, v, NULL, D, dt, B, H, N, rows, out, lo, hi, 0};
+        jobs[used].j = J;
+        jobs[used].lam = lam;
+        jobs[used].W = W;
+        jobs[used].NS = NS;
+        pthread_create(&th[used], NULL, or_ssm_trampoline, &jobs[used]);
+        ++used;
+    }
+    for (int i = 0; i < used; ++i) pthread_join(th[i], NULL);
+    free(th);
+    free(jobs);
+    return 0;
+}
+

@@ -56,6 +56,7 @@ def _load():
                                                    dp, ip]
         lib.oracle_conv2d_points.argtypes = [vp, vp, vp, ip, i64, i64, i64, vp, i64, dp, ip]
         lib.oracle_conv3d_points.argtypes = [vp, vp, vp, ip, i64, i64, i64, vp, i64, dp, ip]
+        lib.oracle_ssm_rows.argtypes = [vp, vp, vp, dp, dp, vp, ip, i64, i64, i64, i64, vp, i64, dp, ip]
         lib.oracle_widen.argtypes = [vp, ip, i64, dp]
         lib.oracle_conv1d_bwd_rows.argtypes = [vp, vp, vp, vp, vp, vp, ip, i64, i64, i64, vp, i64,
                                                dp, dp, dp, ip]
@@ -266,6 +267,41 @@ def conv2d_points(u, k, D, pts, dt=None, nthreads=None):
                                       pts.shape[0], out.ctypes.data, _threads(nthreads))
     if rc:
         raise ValueError("oracle_conv2d_points rejected its arguments")
+    return out
+
+
+def ssm_kernel(lam, W, N):
+    """The filter of a diagonal state-space model: k[h, t] = Re sum_n W[h, n] lam[h, n]^t for
+    t < N (lam, W complex [H, NS]), by repeated multiplication in float64 complex."""
+    lam = np.asarray(lam, np.complex128)
+    W = np.asarray(W, np.complex128)
+    H, NS = lam.shape
+    k = np.empty((H, N))
+    p = np.ones((H, NS), np.complex128)
+    for t in range(N):
+        k[:, t] = (W * p).sum(axis=1).real
+        p = p * lam
+    return k
+
+
+def ssm_rows(u, lam, W, D, rows, q=None, v=None, dt=None, nthreads=None):
+    """Full output rows of the convolution with the state-space filter (lam, W complex [H, NS]),
+    evaluated by the state recurrence (oracle.c).  Returns float64 [len(rows), N]."""
+    dt = _dt_of(u, dt)
+    st = _storage(dt)
+    u, D, q, v = (_c(a, st) for a in (u, D, q, v))
+    lam = np.ascontiguousarray(np.asarray(lam, np.complex128))
+    W = np.ascontiguousarray(np.asarray(W, np.complex128))
+    B, H, N = u.shape
+    NS = lam.shape[1]
+    assert lam.shape == (H, NS) and W.shape == (H, NS) and D.shape == (H,)
+    rows = np.ascontiguousarray(np.asarray(rows, np.int64).reshape(-1, 2))
+    out = np.empty((rows.shape[0], N), np.float64)
+    rc = _load().oracle_ssm_rows(_ptr(u), _ptr(q), _ptr(v), lam.ctypes.data, W.ctypes.data, _ptr(D),
+                                 dt, B, H, N, NS, _ptr(rows), rows.shape[0], out.ctypes.data,
+                                 _threads(nthreads))
+    if rc:
+        raise ValueError("oracle_ssm_rows rejected its arguments")
     return out
 
 
