@@ -79,6 +79,8 @@ def algorithmic_bytes(spec):
     n_in = 3 if spec.gated else 1
     act = (n_in + 1) * spec.B * spec.H * spec.N * s
     kf = spec.H * (spec.taps + 1) * 2 * s          # the filter's spectrum: taps, not N
+    if spec.name.startswith("ssm_"):               # the filter is its modes: nothing of length N
+        kf = 0
     return act + kf + spec.H * s
 
 
@@ -271,6 +273,27 @@ def main():
                                            spec.C, spec.S, dtc, ws3.data_ptr(), wsb3, stream.cuda_stream)
             if st != 0:
                 raise lconv.LconvError(st, "lconv_fftconv3d_fwd")
+    elif spec.name.startswith("ssm_"):  # state-space filter, chunks with state passing
+        NS, T = 64, 4096
+        u, q, v, D = (to_dev(d[x], dt) for x in ("u", "q", "v", "D"))
+        lam_h, W_h = wl.ssm_modes(spec.H, NS, seed=spec.seed + 1)
+        lam_d = torch.from_numpy(lam_h.astype(np.complex64)).cuda()
+        W_d = torch.from_numpy(W_h.astype(np.complex64)).cuda()
+        run_filter = lambda: lconv.ssm_prepare(lam_d, W_d, T, u.dtype)
+        kf = run_filter()
+        y = torch.empty_like(u)
+        dtc = lconv.dtype_code(u.dtype)
+        wss = lconv.lconv_fftconv_ssm_workspace_bytes(spec.B, spec.H, spec.N, NS, T)
+        wsd = torch.empty(max(wss, 1), dtype=torch.uint8, device="cuda")
+        stream = torch.cuda.current_stream()
+        p = lambda t: None if t is None else t.data_ptr()
+
+        def step():
+            st = lconv.lconv_fftconv_ssm_fwd(u.data_ptr(), kf.data_ptr(), D.data_ptr(), y.data_ptr(), p(q), p(v),
+                                             spec.B, spec.H, spec.N, NS, T, dtc, wsd.data_ptr(), wss,
+                                             stream.cuda_stream)
+            if st != 0:
+                raise lconv.LconvError(st, "lconv_fftconv_ssm_fwd")
     elif args.keep is not None:  # frequency-sparse convolution
         keep = int(args.keep, 0)
         u, q, v, k, D = (to_dev(d[x], dt) for x in ("u", "q", "v", "k", "D"))
@@ -395,9 +418,10 @@ def main():
         mf = float(cs["mfma_gflop_executed_per_launch"]) * 1e9 / (avg_ms * 1e-3) / 1e12
         out["mfma"] = {"executed_tflops": round(mf, 1), "peak": MFMA_PEAK[dt],
                        "util": round(mf / MFMA_PEAK[dt], 4), "counters": cs["path"]}
-    if not args.no_bwd and spec.kind == "1d" and spec.N <= 4096 and not spec.L and args.keep is None:
+    if not args.no_bwd and spec.kind == "1d" and spec.N <= 4096 and not spec.L and args.keep is None \
+            and not spec.name.startswith("ssm_"):
         out["backward"] = time_backward(lconv, wl, spec, u, kf, D, q, v, args)
-    if not args.no_cpu and spec.kind == "1d":
+    if not args.no_cpu and spec.kind == "1d" and not spec.name.startswith("ssm_"):
         out["cpu_baseline"] = cpu_baseline(d, args.cpu_budget)
     print(json.dumps(out), flush=True)
 

@@ -255,7 +255,9 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
             const bool valid = sq < (int64_t)nseq;
             const uint32_t sc = (uint32_t)(valid ? sq : s0), b = sc / nch, j = sc - b * nch;
             const int64_t pos = ((int64_t)j - 1 + half) * C + n0_io;
-            ok = item < last && valid && pos >= 0 && pos < a.N;
+            // chunk-local (a.local): the previous block reads as zero, so the result is block j's
+            // own causal convolution
+            ok = item < last && valid && pos >= 0 && pos < a.N && (half == 1 || !a.local);
             const int64_t posc = pos < 0 ? 0 : (pos < a.N ? pos : a.N - 8);
             o = ((int64_t)b * a.H + h) * a.N + posc;
         };

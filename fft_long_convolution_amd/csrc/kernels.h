@@ -28,6 +28,7 @@ struct Fused1DArgs {
     int64_t nitems;      // CONV: pairs; FILTER: channels; ROW/ROWFWD: rows; PART: pairs x blocks
     int64_t nchunk;      // PART: blocks of M/2 positions per row
     uint32_t keep;       // SPARSE: bit k1 set = frequency block k1 (f mod R = k1) kept
+    int local;           // PART: 1 = each block convolved on its own (previous block taken as zero)
     int64_t per_wg;      // items per workgroup (set by the launcher)
     float inv_m;         // 1 / M
     int64_t M;           // full transform length (ROW/ROWFWD: M1 * 8192)
@@ -94,6 +95,24 @@ struct Conv2DArgs {
     int cus;             // compute units (persistent grid size)
 };
 hipError_t launch_conv2d(int dtype, const Conv2DArgs& a, hipStream_t stream);
+
+// State passing for diagonal state-space filters (ssm.hip).
+struct SsmArgs {
+    const void* u;       // [B][H][N] io
+    const void* q;       // pre-gate (nullable)
+    const void* v;       // post-gate (nullable)
+    void* y;             // [B][H][N] io: the chunk-local result, corrected in place
+    void* lw;            // [H][NS][2] fp32 complex: (lam, W)
+    void* pw;            // [H][NS][T/8 + 1] fp32 complex: lam^(8 m)
+    void* pwt;           // [H][T/8 + 1][NS] fp32 complex: the same, transposed
+    void* g;             // [B*H][nch][NS] fp32 complex: chunk sums
+    void* hs;            // [B*H][nch][NS] fp32 complex: states before each chunk
+    void* kchunk;        // prepare: k[H][T] io (the chunk filter)
+    int64_t B, H, N, NS, T, nch;
+};
+hipError_t launch_ssm_prepare(int dtype, const float* lam, const float* W, const SsmArgs& a,
+                              hipStream_t stream);
+hipError_t launch_ssm_state(int dtype, const SsmArgs& a, bool gq, bool gv, hipStream_t stream);
 
 // Row staging for N not a multiple of 8 (stage.hip): [rows][N] <-> [rows][N8] with a zero tail.
 hipError_t launch_pad_rows(const void* src, void* dst, int64_t rows, int64_t N, int64_t N8, int esize,

@@ -335,9 +335,13 @@ lconv_status_t lconv_fftconv_sparse_fwd(const void* u, const void* k_f, const vo
     return hip_status(launch_fused1d(p.R, dtype, MODE_SPARSE, q != nullptr, v != nullptr, a, cus, stream));
 }
 
-lconv_status_t lconv_fftconv_partial_fwd(const void* u, const void* k_f, const void* D, void* y, const void* q,
-                                         const void* v, int64_t B, int64_t H, int64_t N, int64_t L,
-                                         lconv_dtype_t dtype, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+lconv_status_t partial_impl(const void* u, const void* k_f, const void* D, void* y, const void* q, const void* v,
+                            int64_t B, int64_t H, int64_t N, int64_t L, lconv_dtype_t dtype, int local,
+                            hipStream_t stream) {
     if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
     if (B < 0 || H < 0 || N < 0 || L < 0) return LCONV_ERR_INVALID_SHAPE;
     int64_t elems, t;
@@ -371,8 +375,18 @@ lconv_status_t lconv_fftconv_partial_fwd(const void* u, const void* k_f, const v
     Fused1DArgs a{};
     a.u = u; a.q = q; a.v = v; a.y = y; a.kf = k_f; a.D = D; a.tables = tabs;
     a.B = B; a.H = H; a.N = N; a.nitems = items; a.nchunk = nch;
-    a.inv_m = 1.0f / (float)p.M; a.M = p.M; a.M1 = 1;
+    a.inv_m = 1.0f / (float)p.M; a.M = p.M; a.M1 = 1; a.local = local;
     return hip_status(launch_fused1d(p.R, dtype, MODE_PART, q != nullptr, v != nullptr, a, cus, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+lconv_status_t lconv_fftconv_partial_fwd(const void* u, const void* k_f, const void* D, void* y, const void* q,
+                                         const void* v, int64_t B, int64_t H, int64_t N, int64_t L,
+                                         lconv_dtype_t dtype, hipStream_t stream) {
+    return partial_impl(u, k_f, D, y, q, v, B, H, N, L, dtype, 0, stream);
 }
 
 lconv_status_t lconv_fftconv_bwd(const void* dy, const void* u, const void* k_f, const void* D, const void* q,
@@ -590,6 +604,101 @@ lconv_status_t lconv_fftconv3d_fwd(const void* u, const void* k_f, const void* D
         if (launch_conv3d(dtype, a, stream) != hipSuccess) return LCONV_ERR_HIP;
     }
     return LCONV_SUCCESS;
+}
+
+// ---- state-space filters, chunked with state passing --------------------------------------------
+
+namespace {
+bool ssm_t_ok(int64_t T) { return T >= 256 && T <= 4096 && (T & (T - 1)) == 0; }
+// prep layout: [k_f of the chunk filter][pw][lw][k chunk], each 256-byte aligned
+struct SsmPrep {
+    size_t kf, pw, pwt, lw, kc, total;
+};
+bool ssm_layout(int64_t H, int64_t NS, int64_t T, lconv_dtype_t dt, SsmPrep* L) {
+    if (!dtype_ok(dt) || H < 1 || NS < 1 || NS > 256 || !ssm_t_ok(T)) return false;
+    const size_t kf = lconv_filter_fft_bytes(H, T, dt);
+    if (kf == 0) return false;
+    size_t o = 0;
+    L->kf = o; o += round256(kf);
+    L->pw = o; o += round256((size_t)H * NS * (T / 8 + 1) * 8);
+    L->pwt = o; o += round256((size_t)H * NS * (T / 8 + 1) * 8);
+    L->lw = o; o += round256((size_t)H * NS * 16);
+    L->kc = o; o += round256((size_t)H * T * dtype_size(dt));
+    L->total = o;
+    return true;
+}
+}  // namespace
+
+size_t lconv_ssm_prep_bytes(int64_t H, int64_t NS, int64_t T, lconv_dtype_t dtype) {
+    SsmPrep L;
+    return ssm_layout(H, NS, T, dtype, &L) ? L.total : 0;
+}
+
+lconv_status_t lconv_ssm_prepare(const float* lam, const float* W, void* prep, int64_t H, int64_t NS,
+                                 int64_t T, lconv_dtype_t dtype, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
+    if (H < 0 || NS < 0 || T < 0) return LCONV_ERR_INVALID_SHAPE;
+    if (H == 0) return LCONV_SUCCESS;
+    SsmPrep L;
+    if (!ssm_layout(H, NS, T, dtype, &L)) return LCONV_ERR_UNSUPPORTED;
+    if (!lam || !W || !prep) return LCONV_ERR_NULL_POINTER;
+    if (!aligned16(lam) || !aligned16(W) || !aligned16(prep)) return LCONV_ERR_MISALIGNED;
+    const size_t pbytes = (size_t)H * NS * 8;
+    if (overlap(prep, L.total, lam, pbytes) || overlap(prep, L.total, W, pbytes)) return LCONV_ERR_ALIASING;
+    char* P = (char*)prep;
+    SsmArgs a{};
+    a.lw = P + L.lw; a.pw = P + L.pw; a.pwt = P + L.pwt; a.kchunk = P + L.kc;
+    a.H = H; a.NS = NS; a.T = T;
+    if (launch_ssm_prepare(dtype, lam, W, a, stream) != hipSuccess) return LCONV_ERR_HIP;
+    // the chunk filter's spectrum (single pass: T <= 4096 needs no workspace)
+    return lconv_filter_fft(P + L.kc, P + L.kf, H, T, dtype, nullptr, 0, stream);
+}
+
+size_t lconv_fftconv_ssm_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t NS, int64_t T) {
+    int64_t rows, t;
+    if (B < 1 || H < 1 || N < 1 || NS < 1 || NS > 256 || !ssm_t_ok(T)) return 0;
+    const int64_t nch = (N + T - 1) / T;
+    if (!mul_ok(B, H, &rows) || !mul_ok(rows, nch, &t) || !mul_ok(t, NS, &t) || !mul_ok(t, 8, &t)) return 0;
+    return 2 * round256((size_t)t);  // chunk sums and boundary states
+}
+
+lconv_status_t lconv_fftconv_ssm_fwd(const void* u, const void* prep, const void* D, void* y, const void* q,
+                                     const void* v, int64_t B, int64_t H, int64_t N, int64_t NS, int64_t T,
+                                     lconv_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+    if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
+    if (B < 0 || H < 0 || N < 0 || NS < 0 || T < 0) return LCONV_ERR_INVALID_SHAPE;
+    int64_t elems, t;
+    if (!mul_ok(B, H, &t) || !mul_ok(t, N, &elems) || !mul_ok(elems, 8, &t)) return LCONV_ERR_INVALID_SHAPE;
+    if (B == 0 || H == 0 || N == 0) return LCONV_SUCCESS;
+    SsmPrep L;
+    if (!ssm_layout(H, NS, T, dtype, &L) || (N % 8) != 0 || N > ((int64_t)1 << 40)) return LCONV_ERR_UNSUPPORTED;
+    const size_t need = lconv_fftconv_ssm_workspace_bytes(B, H, N, NS, T);
+    if (need == 0) return LCONV_ERR_UNSUPPORTED;
+    if (!u || !prep || !D || !y) return LCONV_ERR_NULL_POINTER;
+    if (!aligned16(u) || !aligned16(prep) || !aligned16(D) || !aligned16(y) || (q && !aligned16(q)) ||
+        (v && !aligned16(v)))
+        return LCONV_ERR_MISALIGNED;
+    const size_t es = dtype_size(dtype), act = (size_t)elems * es;
+    if (overlap(y, act, u, act) || overlap(y, act, q, act) || overlap(y, act, v, act) ||
+        overlap(y, act, prep, L.total) || overlap(y, act, D, (size_t)H * es))
+        return LCONV_ERR_ALIASING;
+    if (!workspace || workspace_bytes < need) return LCONV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return LCONV_ERR_MISALIGNED;
+    if (overlap(workspace, need, y, act) || overlap(workspace, need, u, act) || overlap(workspace, need, q, act) ||
+        overlap(workspace, need, v, act) || overlap(workspace, need, prep, L.total))
+        return LCONV_ERR_ALIASING;
+    const char* P = (const char*)prep;
+    // 1. each chunk's own convolution with k[0:T] (+ D x, gated): the partial mode, previous block zero
+    const lconv_status_t r = partial_impl(u, P + L.kf, D, y, q, v, B, H, N, T, dtype, 1, stream);
+    if (r != LCONV_SUCCESS) return r;
+    // 2-4. chunk sums, scan of the boundary states, correction of every output
+    SsmArgs a{};
+    a.u = u; a.q = q; a.v = v; a.y = y;
+    a.lw = (void*)(P + L.lw); a.pw = (void*)(P + L.pw); a.pwt = (void*)(P + L.pwt);
+    a.g = workspace; a.hs = (char*)workspace + need / 2;
+    a.B = B; a.H = H; a.N = N; a.NS = NS; a.T = T; a.nch = (N + T - 1) / T;
+    return hip_status(launch_ssm_state(dtype, a, q != nullptr, v != nullptr, stream));
 }
 
 lconv_status_t lconv_release(void) {

@@ -55,6 +55,10 @@ def load(path: str = LIB_PATH):
         "lconv_fftconv_sparse_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_uint32, i, vp]),
         "lconv_freq_blocks": (i, [i64]),
         "lconv_filter_fft2d": (i, [vp, vp, i64, i64, i, vp]),
+        "lconv_ssm_prep_bytes": (sz, [i64, i64, i64, i]),
+        "lconv_ssm_prepare": (i, [vp, vp, vp, i64, i64, i64, i, vp]),
+        "lconv_fftconv_ssm_workspace_bytes": (sz, [i64, i64, i64, i64, i64]),
+        "lconv_fftconv_ssm_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i, vp, sz, vp]),
         "lconv_filter_fft3d_bytes": (sz, [i64, i64, i]),
         "lconv_filter_fft3d_workspace_bytes": (sz, [i64, i64, i]),
         "lconv_fftconv3d_workspace_bytes": (sz, [i64, i64, i64, i]),
@@ -129,6 +133,23 @@ def lconv_filter_fft2d(k, k_f, C, S, dtype, stream):
 
 def lconv_fftconv2d_fwd(u, k_f, D, y, B, C, S, dtype, stream):
     return load().lconv_fftconv2d_fwd(u, k_f, D, y, B, C, S, dtype, stream)
+
+
+def lconv_ssm_prep_bytes(H, NS, T, dtype):
+    return load().lconv_ssm_prep_bytes(H, NS, T, dtype)
+
+
+def lconv_ssm_prepare(lam, W, prep, H, NS, T, dtype, stream):
+    return load().lconv_ssm_prepare(lam, W, prep, H, NS, T, dtype, stream)
+
+
+def lconv_fftconv_ssm_workspace_bytes(B, H, N, NS, T):
+    return load().lconv_fftconv_ssm_workspace_bytes(B, H, N, NS, T)
+
+
+def lconv_fftconv_ssm_fwd(u, prep, D, y, q, v, B, H, N, NS, T, dtype, workspace, workspace_bytes, stream):
+    return load().lconv_fftconv_ssm_fwd(u, prep, D, y, q, v, B, H, N, NS, T, dtype, workspace,
+                                        workspace_bytes, stream)
 
 
 def lconv_filter_fft3d_bytes(C, S, dtype):
@@ -276,6 +297,36 @@ def filter_fft2d(k, stream=None):
     k_f = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k.device)
     _check(lconv_filter_fft2d(_ptr(k), k_f.data_ptr(), C, S, dt, _stream(stream)), "lconv_filter_fft2d")
     return k_f
+
+
+def ssm_prepare(lam, W, T, dtype, stream=None):
+    """Tables for the state-space filter k[h, t] = Re sum_n W lam^t: lam, W complex64 device
+    tensors [H, NS]; T the chunk length.  Returns the opaque prep buffer."""
+    torch = _torch()
+    H, NS = lam.shape
+    dt = dtype_code(dtype)
+    nbytes = lconv_ssm_prep_bytes(H, NS, T, dt)
+    if nbytes == 0:
+        raise LconvError(3, "lconv_ssm_prep_bytes")
+    prep = torch.empty(nbytes, dtype=torch.uint8, device=lam.device)
+    lam_f = torch.view_as_real(lam.contiguous()).contiguous()
+    W_f = torch.view_as_real(W.contiguous()).contiguous()
+    _check(lconv_ssm_prepare(lam_f.data_ptr(), W_f.data_ptr(), prep.data_ptr(), H, NS, T, dt, _stream(stream)),
+           "lconv_ssm_prepare")
+    return prep
+
+
+def fftconv_ssm(u, prep, D, NS, T, q=None, v=None, out=None, stream=None):
+    """Causal convolution with a state-space filter, chunked with state passing."""
+    torch = _torch()
+    B, H, N = u.shape
+    y = torch.empty_like(u) if out is None else out
+    wsb = lconv_fftconv_ssm_workspace_bytes(B, H, N, NS, T)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=u.device)
+    _check(lconv_fftconv_ssm_fwd(_ptr(u), _ptr(prep), _ptr(D), _ptr(y), _ptr(q), _ptr(v), B, H, N, NS, T,
+                                 dtype_code(u.dtype), ws.data_ptr(), wsb, _stream(stream)),
+           "lconv_fftconv_ssm_fwd")
+    return y
 
 
 def filter_fft3d(k, stream=None):

@@ -150,6 +150,10 @@ WORKLOADS = {
         "very_long_bf16_b1_h64_n2097152", 1, 64, 2097152, "bf16", decay=1e-6, seed=1004),
     "hyenand_2d_bf16_b8_c256_s128": Conv2DSpec(
         "hyenand_2d_bf16_b8_c256_s128", 8, 256, 128, "bf16", decay=0.05, seed=1005),
+    # the 2^21-long shape with a 64-mode state-space filter (chunks with state passing; the
+    # modes come from ssm_modes(H, 64, seed + 1))
+    "ssm_bf16_b1_h64_n2097152_ns64": Conv1DSpec(
+        "ssm_bf16_b1_h64_n2097152_ns64", 1, 64, 2097152, "bf16", decay=1e-6, seed=1008),
     # volumes: the 2D operation one dimension up
     "hyenand_3d_bf16_b4_c128_s32": Conv3DSpec(
         "hyenand_3d_bf16_b4_c128_s32", 4, 128, 32, "bf16", decay=0.1, seed=1007),
@@ -226,6 +230,17 @@ def make_2d(spec: Conv2DSpec) -> dict:
     out["k"] = to_storage(k, spec.dtype)
     out["D"] = to_storage(rng.standard_normal(C), spec.dtype)
     return out
+
+
+def ssm_modes(H, NS, seed=0, decay=(1e-4, 1e-1)):
+    """Diagonal state-space modes per channel: lam = exp(-a + i theta) with a log-uniform in
+    `decay` and theta uniform in [0, pi); W complex Gaussian / sqrt(NS).  complex128 [H, NS]."""
+    rng = np.random.default_rng(seed)
+    a = np.exp(rng.uniform(math.log(decay[0]), math.log(decay[1]), (H, NS)))
+    th = rng.uniform(0.0, math.pi, (H, NS))
+    lam = np.exp(-a + 1j * th)
+    W = (rng.standard_normal((H, NS)) + 1j * rng.standard_normal((H, NS))) / math.sqrt(NS)
+    return lam, W
 
 
 def spec_3d(B, C, S, dtype, seed=7, decay=0.1) -> Conv3DSpec:

@@ -212,6 +212,34 @@ lconv_status_t lconv_fftconv2d_fwd(const void* u, const void* k_f, const void* D
                                    int64_t B, int64_t C, int64_t S, lconv_dtype_t dtype,
                                    hipStream_t stream);
 
+/* ---- state-space filters: chunks with state passing --------------------------------------- */
+
+/*
+ * Long convolutions whose filter comes from a diagonal state-space model, run in chunks with the
+ * boundary state passed between them ("FlashConv" page, Mechanism: when the sequence exceeds the
+ * on-chip capacity, convolve chunk by chunk and propagate the state-space boundary state).
+ * Filter: k[h,t] = Re sum_n W[h,n] lam[h,n]^t with NS complex modes per channel.  With chunk
+ * length T and x = q (.) u, for t = jT + tau:
+ *   y[t] = v * ( sum_{s in chunk j, s <= t} k[t-s] x[s] + Re sum_n W_n lam_n^(tau+1) h_j[n] + D x[t] )
+ *   h_0 = 0,  h_{j+1}[n] = lam_n^T h_j[n] + sum_{tau<T} lam_n^(T-1-tau) x[jT + tau]
+ * which equals the causal convolution with the whole filter.  The chunk convolution is the fused
+ * transform of length 2T; the state terms cost O(NS) per element.
+ *   lam, W   [H][NS] fp32 complex (interleaved re, im), device; |lam| < 1 for a decaying filter
+ *   prep     lconv_ssm_prep_bytes(H, NS, T, dtype) bytes, written by lconv_ssm_prepare: the chunk
+ *            filter's spectrum and tables of powers of lam (opaque)
+ *   u, y, q, v [B][H][N] dtype (q, v may be NULL);  D [H] dtype
+ *   workspace  lconv_fftconv_ssm_workspace_bytes(B, H, N, NS, T) bytes (chunk sums, states)
+ * Supported: T a power of two in [256, 4096]; 1 <= NS <= 256; N a multiple of 8.
+ */
+size_t lconv_ssm_prep_bytes(int64_t H, int64_t NS, int64_t T, lconv_dtype_t dtype);
+lconv_status_t lconv_ssm_prepare(const float* lam, const float* W, void* prep, int64_t H, int64_t NS,
+                                 int64_t T, lconv_dtype_t dtype, hipStream_t stream);
+size_t lconv_fftconv_ssm_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t NS, int64_t T);
+lconv_status_t lconv_fftconv_ssm_fwd(const void* u, const void* prep, const void* D, void* y,
+                                     const void* q, const void* v, int64_t B, int64_t H, int64_t N,
+                                     int64_t NS, int64_t T, lconv_dtype_t dtype, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
 /* ---- 3D (HyenaND-style volumes) ------------------------------------------------------------ */
 
 /*

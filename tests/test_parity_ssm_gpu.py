@@ -1,0 +1,82 @@
+"""GPU parity of the chunked state-space convolution (lconv_ssm_prepare + lconv_fftconv_ssm_fwd)
+against the float64 state recurrence (oracle.ssm_rows), which the CPU pins tie to the causal
+convolution with the generated filter.
+
+Tolerance as for the forward: max relative L2 error 1e-4 (fp32), 2e-2 (bf16 / fp16) per row.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from fft_long_convolution_amd import workloads as wl
+from tests.gpu_util import DT_ORACLE, TOL, from_dev, rel_l2_rows, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lc():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from fft_long_convolution_amd import lconv
+    lconv.load()
+    return lconv
+
+
+def run_ssm(lc, d, lam, W, T, q, v):
+    import torch
+    dt = d["dtype"]
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dt]
+    lam_d = torch.from_numpy(lam.astype(np.complex64)).cuda()
+    W_d = torch.from_numpy(W.astype(np.complex64)).cuda()
+    prep = lc.ssm_prepare(lam_d, W_d, T, tdt)
+    y = lc.fftconv_ssm(to_dev(d["u"], dt), prep, to_dev(d["D"], dt), lam.shape[1], T,
+                       q=to_dev(q, dt), v=to_dev(v, dt))
+    torch.cuda.synchronize()
+    return from_dev(y, dt)
+
+
+# (B, H, N, NS, T, gates)
+CASES = [
+    (1, 2, 256, 4, 256, ""),          # one chunk
+    (3, 2, 2048, 8, 256, "qv"),       # 8 chunks
+    (2, 3, 5000, 16, 1024, "q"),      # ragged last chunk
+    (2, 2, 16384, 64, 4096, "qv"),    # 4 chunks of the largest transform
+    (1, 2, 40960, 32, 512, "v"),      # 80 chunks
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("B,H,N,NS,T,gates", CASES)
+def test_ssm_full_rows(lc, nthreads, dtype, B, H, N, NS, T, gates):
+    spec = wl.spec_1d(B, H, N, dtype, gated=True, seed=1500 + N + NS)
+    say(f"[ssm] dtype={dtype} B={B} H={H} N={N} NS={NS} T={T} gates={gates!r} seed={spec.seed}")
+    d = wl.make(spec)
+    lam, W = wl.ssm_modes(H, NS, seed=spec.seed + 1)
+    q = d["q"] if "q" in gates else None
+    v = d["v"] if "v" in gates else None
+    y = run_ssm(lc, d, lam, W, T, q, v)
+    assert np.all(np.isfinite(y))
+    rows = [(b, h) for b in range(B) for h in range(H)]
+    ref = oracle.ssm_rows(d["u"], lam, W, d["D"], rows, q=q, v=v, dt=DT_ORACLE[dtype],
+                          nthreads=nthreads).reshape(B, H, N)
+    err = float(rel_l2_rows(y, ref).max())
+    say(f"   max rel L2 = {err:.3e} (tol {TOL[dtype]})")
+    assert err <= TOL[dtype]
+
+
+def test_ssm_long_workload_rows(lc, nthreads):
+    """The 2^21-long shape with a 64-mode filter, chunks of 4096: a few full rows."""
+    spec = wl.WORKLOADS["ssm_bf16_b1_h64_n2097152_ns64"]
+    say(f"[ssm long] {spec.name} seed={spec.seed}")
+    d = wl.make(spec)
+    lam, W = wl.ssm_modes(spec.H, 64, seed=spec.seed + 1)
+    y = run_ssm(lc, d, lam, W, 4096, d["q"], d["v"])
+    rows = [(0, 0), (0, 37), (0, 63)]
+    ref = oracle.ssm_rows(d["u"], lam, W, d["D"], rows, q=d["q"], v=d["v"], dt=DT_ORACLE["bf16"],
+                          nthreads=nthreads)
+    got = np.stack([y[b, h] for b, h in rows])
+    err = float(rel_l2_rows(got, ref).max())
+    say(f"   max rel L2 over {len(rows)} rows = {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= TOL["bf16"]
