@@ -927,7 +927,8 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
 
     // ---- items and addresses --------------------------------------------------------------
     const uint32_t Bp = (uint32_t)((a.B + 1) / 2);
-    const int64_t HN = a.H * a.N;
+    // element strides between batch rows and between channels ([B][H][N] unless set)
+    const int64_t sB = a.sb ? a.sb : a.H * a.N, sH = a.sh ? a.sh : a.N;
     auto channel = [&](int64_t item) LCV_INLINE {
         return (int64_t)((uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)item) / Bp);
     };
@@ -940,9 +941,9 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
         item = item < last ? item : last - 1;
         const uint32_t it = __builtin_amdgcn_readfirstlane((uint32_t)item), hh = it / Bp;
         const int64_t b = 2 * (int64_t)(it - hh * Bp);
-        const int64_t row0 = (b * a.H + hh) * a.N;
+        const int64_t row0 = b * sB + hh * sH;
         o0 = row0 + s_n0;
-        o1 = (b + 1 < a.B ? row0 + HN : row0) + s_n0;
+        o1 = (b + 1 < a.B ? row0 + sB : row0) + s_n0;
     };
     uint4 ru[2], rq[2], rv[2], re2[2];
     auto issue_uq = [&](int64_t item) LCV_INLINE {
@@ -1266,13 +1267,14 @@ template <int R, int T, int MODE>
 static hipError_t launch_conv(bool gq, bool gv, const Fused1DArgs& a, int cus, hipStream_t st) {
     constexpr bool ADJ = MODE == MODE_ADJ;
     if constexpr (R == 32 && T != CT_F32) {
-        if (a.N == 4096) {  // whole rows: the pipelined kernel
+        if (a.N == 4096) {  // whole rows: the pipelined kernel (the only one with row strides)
             if (gq && gv) return launch_8k<T, true, true, ADJ>(a, cus, st);
             if (gq) return launch_8k<T, true, false, ADJ>(a, cus, st);
             if (gv) return launch_8k<T, false, true, ADJ>(a, cus, st);
             return launch_8k<T, false, false, ADJ>(a, cus, st);
         }
     }
+    if (a.sb != 0 || a.sh != 0) return hipErrorInvalidValue;
     if (gq && gv) return launch_t<R, T, T, MODE, true, true>(a, cus, st);
     if (gq) return launch_t<R, T, T, MODE, true, false>(a, cus, st);
     if (gv) return launch_t<R, T, T, MODE, false, true>(a, cus, st);

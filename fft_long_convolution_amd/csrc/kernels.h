@@ -29,6 +29,8 @@ struct Fused1DArgs {
     int64_t nchunk;      // PART: blocks of M/2 positions per row
     uint32_t keep;       // SPARSE: bit k1 set = frequency block k1 (f mod R = k1) kept
     int local;           // PART: 1 = each block convolved on its own (previous block taken as zero)
+    int64_t sb, sh;      // CONV with N = 4096, 16-bit: element strides between batch rows and between
+                         // channels (0: the contiguous [B][H][N] layout); other kernels require 0
     int64_t per_wg;      // items per workgroup (set by the launcher)
     float inv_m;         // 1 / M
     int64_t M;           // full transform length (ROW/ROWFWD: M1 * 8192)
@@ -96,19 +98,31 @@ struct Conv2DArgs {
 };
 hipError_t launch_conv2d(int dtype, const Conv2DArgs& a, hipStream_t stream);
 
-// State passing for diagonal state-space filters (ssm.hip).
+// State passing for diagonal state-space filters (ssm.hip).  Modes are handled in blocks of
+// ssm_block_modes(NS) = 64 (the last block zero-padded); NSP = blocks * block modes.
+inline int ssm_block_modes(int64_t) { return 64; }
+inline int ssm_blocks(int64_t NS) { return (int)((NS + ssm_block_modes(NS) - 1) / ssm_block_modes(NS)); }
+// Bytes of one channel's operand images (sums or correction): per block, 4 tile positions x
+// 4 NQ ops x 2 parts x 1 KiB.
+constexpr int64_t kSsmMaxParts = 64;   // parts of the scan over chunks
+inline int64_t ssm_image_bytes(int64_t NS) { return (int64_t)ssm_blocks(NS) * (ssm_block_modes(NS) / 16) * 32768; }
 struct SsmArgs {
     const void* u;       // [B][H][N] io
     const void* q;       // pre-gate (nullable)
     const void* v;       // post-gate (nullable)
     void* y;             // [B][H][N] io: the chunk-local result, corrected in place
-    void* lw;            // [H][NS][2] fp32 complex: (lam, W)
-    void* pw;            // [H][NS][T/8 + 1] fp32 complex: lam^(8 m)
-    void* pwt;           // [H][T/8 + 1][NS] fp32 complex: the same, transposed
+    void* md;            // [H][NS][4] fp32 complex: lam, W lam, lam^T, 0
+    void* pw;            // [H][17][NSP] fp32 complex: lam^(64 e), zero for padding modes
+    void* ts;            // [H][blocks] operand images of the chunk sums (bf16 hi / lo)
+    void* tc;            // [H][blocks] operand images of the correction (bf16 hi / lo)
     void* g;             // [B*H][nch][NS] fp32 complex: chunk sums
-    void* hs;            // [B*H][nch][NS] fp32 complex: states before each chunk
+    void* cs;            // [B*H][nch][NS] fp32 complex: W lam h_j, h_j the state before chunk j
+    void* sp;            // [B*H][nparts][NS] fp32 complex: each part's final state from a zero start
     void* kchunk;        // prepare: k[H][T] io (the chunk filter)
     int64_t B, H, N, NS, T, nch;
+    int64_t nparts, plen;   // the scan over chunks: parts of plen chunks
+    int nsb, nmb;        // modes per block, blocks
+    int mb;              // correction launch: its mode block
 };
 hipError_t launch_ssm_prepare(int dtype, const float* lam, const float* W, const SsmArgs& a,
                               hipStream_t stream);

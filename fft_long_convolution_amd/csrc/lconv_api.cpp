@@ -372,6 +372,22 @@ lconv_status_t partial_impl(const void* u, const void* k_f, const void* D, void*
     const int ct = dtype == LCONV_F32 ? CT_F32 : (int)dtype;
     const void* tabs = fused_tables(p.R, ct, &err);
     if (!tabs) return LCONV_ERR_HIP;
+    if (local && p.M == 8192 && dtype != LCONV_F32 && N % C == 0) {
+        // whole blocks convolved on their own: per batch row, the blocks of a channel are the
+        // batch rows (stride C) of a plain convolution of length C on the pipelined kernel
+        for (int64_t b = 0; b < B; ++b) {
+            const int64_t off = b * H * N * (int64_t)es;
+            Fused1DArgs a{};
+            a.u = (const char*)u + off; a.y = (char*)y + off;
+            a.q = q ? (const char*)q + off : nullptr; a.v = v ? (const char*)v + off : nullptr;
+            a.kf = k_f; a.D = D; a.tables = tabs;
+            a.B = nch; a.H = H; a.N = C; a.sb = C; a.sh = N; a.nitems = (nch + 1) / 2 * H;
+            a.inv_m = 1.0f / (float)p.M; a.M = p.M; a.M1 = 1;
+            const hipError_t e = launch_fused1d(p.R, dtype, MODE_CONV, q != nullptr, v != nullptr, a, cus, stream);
+            if (e != hipSuccess) return hip_status(e);
+        }
+        return LCONV_SUCCESS;
+    }
     Fused1DArgs a{};
     a.u = u; a.q = q; a.v = v; a.y = y; a.kf = k_f; a.D = D; a.tables = tabs;
     a.B = B; a.H = H; a.N = N; a.nitems = items; a.nchunk = nch;
@@ -610,9 +626,9 @@ lconv_status_t lconv_fftconv3d_fwd(const void* u, const void* k_f, const void* D
 
 namespace {
 bool ssm_t_ok(int64_t T) { return T >= 256 && T <= 4096 && (T & (T - 1)) == 0; }
-// prep layout: [k_f of the chunk filter][pw][lw][k chunk], each 256-byte aligned
+// prep layout: [k_f of the chunk filter][md][pw][ts][tc][k chunk], each 256-byte aligned
 struct SsmPrep {
-    size_t kf, pw, pwt, lw, kc, total;
+    size_t kf, md, pw, ts, tc, kc, total;
 };
 bool ssm_layout(int64_t H, int64_t NS, int64_t T, lconv_dtype_t dt, SsmPrep* L) {
     if (!dtype_ok(dt) || H < 1 || NS < 1 || NS > 256 || !ssm_t_ok(T)) return false;
@@ -620,9 +636,11 @@ bool ssm_layout(int64_t H, int64_t NS, int64_t T, lconv_dtype_t dt, SsmPrep* L) 
     if (kf == 0) return false;
     size_t o = 0;
     L->kf = o; o += round256(kf);
-    L->pw = o; o += round256((size_t)H * NS * (T / 8 + 1) * 8);
-    L->pwt = o; o += round256((size_t)H * NS * (T / 8 + 1) * 8);
-    L->lw = o; o += round256((size_t)H * NS * 16);
+    const size_t nsp = (size_t)ssm_blocks(NS) * ssm_block_modes(NS);
+    L->md = o; o += round256((size_t)H * NS * 32);
+    L->pw = o; o += round256((size_t)H * 17 * nsp * 8);
+    L->ts = o; o += round256((size_t)H * ssm_image_bytes(NS));
+    L->tc = o; o += round256((size_t)H * ssm_image_bytes(NS));
     L->kc = o; o += round256((size_t)H * T * dtype_size(dt));
     L->total = o;
     return true;
@@ -647,8 +665,8 @@ lconv_status_t lconv_ssm_prepare(const float* lam, const float* W, void* prep, i
     if (overlap(prep, L.total, lam, pbytes) || overlap(prep, L.total, W, pbytes)) return LCONV_ERR_ALIASING;
     char* P = (char*)prep;
     SsmArgs a{};
-    a.lw = P + L.lw; a.pw = P + L.pw; a.pwt = P + L.pwt; a.kchunk = P + L.kc;
-    a.H = H; a.NS = NS; a.T = T;
+    a.md = P + L.md; a.pw = P + L.pw; a.ts = P + L.ts; a.tc = P + L.tc; a.kchunk = P + L.kc;
+    a.H = H; a.NS = NS; a.T = T; a.nsb = ssm_block_modes(NS); a.nmb = ssm_blocks(NS);
     if (launch_ssm_prepare(dtype, lam, W, a, stream) != hipSuccess) return LCONV_ERR_HIP;
     // the chunk filter's spectrum (single pass: T <= 4096 needs no workspace)
     return lconv_filter_fft(P + L.kc, P + L.kf, H, T, dtype, nullptr, 0, stream);
@@ -659,7 +677,9 @@ size_t lconv_fftconv_ssm_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_
     if (B < 1 || H < 1 || N < 1 || NS < 1 || NS > 256 || !ssm_t_ok(T)) return 0;
     const int64_t nch = (N + T - 1) / T;
     if (!mul_ok(B, H, &rows) || !mul_ok(rows, nch, &t) || !mul_ok(t, NS, &t) || !mul_ok(t, 8, &t)) return 0;
-    return 2 * round256((size_t)t);  // chunk sums and boundary states
+    const int64_t parts = nch < kSsmMaxParts ? nch : kSsmMaxParts;
+    // chunk sums, boundary states, the scan's part states
+    return 2 * round256((size_t)t) + round256((size_t)(rows * parts * NS * 8));
 }
 
 lconv_status_t lconv_fftconv_ssm_fwd(const void* u, const void* prep, const void* D, void* y, const void* q,
@@ -695,9 +715,18 @@ lconv_status_t lconv_fftconv_ssm_fwd(const void* u, const void* prep, const void
     // 2-4. chunk sums, scan of the boundary states, correction of every output
     SsmArgs a{};
     a.u = u; a.q = q; a.v = v; a.y = y;
-    a.lw = (void*)(P + L.lw); a.pw = (void*)(P + L.pw); a.pwt = (void*)(P + L.pwt);
-    a.g = workspace; a.hs = (char*)workspace + need / 2;
-    a.B = B; a.H = H; a.N = N; a.NS = NS; a.T = T; a.nch = (N + T - 1) / T;
+    a.md = (void*)(P + L.md); a.pw = (void*)(P + L.pw); a.ts = (void*)(P + L.ts); a.tc = (void*)(P + L.tc);
+    const int64_t nch = (N + T - 1) / T;
+    const size_t gbytes = round256((size_t)(B * H * nch * NS * 8));
+    a.g = workspace; a.cs = (char*)workspace + gbytes; a.sp = (char*)workspace + 2 * gbytes;
+    a.B = B; a.H = H; a.N = N; a.NS = NS; a.T = T; a.nch = nch;
+    // scan parts: enough (row, part, mode) threads to fill the device, at most kSsmMaxParts
+    int64_t parts = (32768 + B * H * NS - 1) / (B * H * NS);
+    parts = parts < kSsmMaxParts ? parts : kSsmMaxParts;
+    parts = parts < nch ? parts : nch;
+    a.plen = (nch + parts - 1) / parts;
+    a.nparts = (nch + a.plen - 1) / a.plen;
+    a.nsb = ssm_block_modes(NS); a.nmb = ssm_blocks(NS);
     return hip_status(launch_ssm_state(dtype, a, q != nullptr, v != nullptr, stream));
 }
 

@@ -236,7 +236,8 @@ def test_ssm_sizes_and_validation():
     assert lconv.lconv_ssm_prep_bytes(64, 64, 3000, BF16) == 0            # T a power of two
     assert lconv.lconv_ssm_prep_bytes(64, 300, 4096, BF16) == 0           # NS <= 256
     assert lconv.lconv_ssm_prep_bytes(64, 64, 8192, BF16) == 0
-    assert lconv.lconv_fftconv_ssm_workspace_bytes(1, 64, 2 ** 21, 64, 4096) == 2 * 64 * 512 * 64 * 8
+    # chunk sums and states (64 rows x 512 chunks x 64 modes), plus 64 scan parts per row
+    assert lconv.lconv_fftconv_ssm_workspace_bytes(1, 64, 2 ** 21, 64, 4096) == 2 * 64 * 512 * 64 * 8 + 64 * 64 * 64 * 8
     sf = lambda u=G[0], prep=G[1], D=G[2], y=G[3], q=None, v=None, B=2, H=3, N=1024, NS=8, T=256, dt=BF16, \
         ws=G[4], wsb=1 << 30: lconv.lconv_fftconv_ssm_fwd(u, prep, D, y, q, v, B, H, N, NS, T, dt, ws, wsb, None)
     assert sf(dt=5) == UNSUP

@@ -44,6 +44,9 @@ CASES = [
     (2, 3, 5000, 16, 1024, "q"),      # ragged last chunk
     (2, 2, 16384, 64, 4096, "qv"),    # 4 chunks of the largest transform
     (1, 2, 40960, 32, 512, "v"),      # 80 chunks
+    (1, 3, 4096, 20, 1024, ""),       # modes padded within a block of 64
+    (2, 2, 3072, 96, 512, "qv"),      # two blocks of 64 modes, the second half padding
+    (1, 1, 8200, 200, 2048, "q"),     # four blocks, ragged last chunk and tile
 ]
 
 
