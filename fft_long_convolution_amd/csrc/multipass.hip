@@ -27,7 +27,7 @@ namespace lcv {
 namespace {
 
 constexpr int64_t kM2 = 8192;
-constexpr int kLdsBytes = 128 * 1024;   // column block: CB x M1 fp32 complex (plus one pad row)
+constexpr int kLdsBytes = 64 * 1024;    // column block: CB x M1 fp32 complex (plus one pad row)
 
 // exp(-2 pi i r / M) from the two-level table (r reduced mod M by the caller)
 __device__ __forceinline__ float2 tw_m(const float* lo, const float* hi, int64_t r) {
@@ -339,7 +339,7 @@ static hipError_t launch_cols_t(bool fwd, const ColArgs& a, hipStream_t st) {
     const size_t lds = (size_t)CB * (M1 + 1) * sizeof(float2);
     dim3 grid((unsigned)(kM2 / CB), (unsigned)a.nseq);
     // dynamic LDS above the default limit has to be allowed per kernel (once, at the device
-    // maximum: the block size depends on M1, at most 133,120 bytes)
+    // maximum: the block size depends on M1, at most 66,560 bytes)
     static bool attr_set[2] = {false, false};
     auto kfwd = col_fwd_kernel<CT, IO, TPB>;
     auto kinv = col_inv_kernel<CT, IO, TPB>;
@@ -366,7 +366,8 @@ static hipError_t launch_cols(bool fwd, const ColArgs& a, hipStream_t st) {
     case 16: return launch_small_t<CT, IO, 16>(fwd, a, st);
     default: break;
     }
-    // LDS passes: many small blocks per CU for short columns; 8 waves for one 128 KB block
+    // LDS passes: many small blocks per CU for short columns; 8 waves for a 64 KB block (two
+    // blocks per CU, so that one block's loads and stores overlap the other's column DFTs)
     return M1 <= 64 ? launch_cols_t<CT, IO, 256>(fwd, a, st) : launch_cols_t<CT, IO, 512>(fwd, a, st);
 }
 
