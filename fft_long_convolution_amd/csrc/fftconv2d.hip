@@ -73,10 +73,13 @@ __global__ void __launch_bounds__(512) conv2d_kernel(const Conv2DArgs a) {
         twi = f32x4{t0.y, t0.w, t1.y, t1.w};
     }
 
-    const int64_t Bp = (a.B + 1) / 2, nitems = Bp * a.C;
-    const int64_t per = (nitems + gridDim.x - 1) / gridDim.x;
-    const int64_t first = (int64_t)blockIdx.x * per;
-    const int64_t last = first + per < nitems ? first + per : nitems;
+    // Items are channel-major (a channel's batch pairs are consecutive).  A workgroup takes items
+    // v, v + G, v + 2G, ... (G workgroups), where v renumbers the workgroups XCD by XCD: the
+    // dispatcher deals workgroup ids round-robin over the 8 XCDs, so consecutive v, and hence
+    // the pairs of one channel at one step, run on the same XCD and share its L2 copy of the
+    // channel's 256 KB spectrum.
+    const int64_t Bp = (a.B + 1) / 2, nitems = Bp * a.C, G = gridDim.x;
+    const int64_t v = G % 8 == 0 ? (int64_t)(blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : (int64_t)blockIdx.x;
     constexpr int64_t IMGSZ = (int64_t)S2D * S2D;
 
     // staged input chunk of this thread: row (tid / 16) of a 32-row quarter, elements 8*(tid%16)..
@@ -89,9 +92,9 @@ __global__ void __launch_bounds__(512) conv2d_kernel(const Conv2DArgs a) {
         pre0 = *(const uint4*)((const uint16_t*)a.u + base0);
         pre1 = *(const uint4*)((const uint16_t*)a.u + base1);
     };
-    if (first < last) issue(first, 0);
+    if (v < nitems) issue(v, 0);
 
-    for (int64_t item = first; item < last; ++item) {
+    for (int64_t item = v; item < nitems; item += G) {
         const int64_t ch = item / Bp, b = 2 * (item % Bp);
         const bool has1 = b + 1 < a.B;
 
@@ -113,7 +116,7 @@ __global__ void __launch_bounds__(512) conv2d_kernel(const Conv2DArgs a) {
             }
             // next chunk: next quarter, or the next item's first quarter
             if (q < 3) issue(item, q + 1);
-            else if (item + 1 < last) issue(item + 1, 0);
+            else if (item + G < nitems) issue(item + G, 0);
             __syncthreads();
             // 4 row tiles per wave: rows r = 32 q + 4 wave + i
             Operand<CT> opd[4];
