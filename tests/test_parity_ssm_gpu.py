@@ -47,6 +47,7 @@ CASES = [
     (1, 3, 4096, 20, 1024, ""),       # modes padded within a block of 64
     (2, 2, 3072, 96, 512, "qv"),      # two blocks of 64 modes, the second half padding
     (1, 1, 8200, 200, 2048, "q"),     # four blocks, ragged last chunk and tile
+    (2, 2, 12296, 64, 4096, "v"),     # T = 4096 with a ragged last chunk: partial-mode chunk convolutions
 ]
 
 
