@@ -223,12 +223,14 @@ lconv_status_t lconv_fftconv2d_fwd(const void* u, const void* k_f, const void* D
  *   y[t] = v * ( sum_{s in chunk j, s <= t} k[t-s] x[s] + Re sum_n W_n lam_n^(tau+1) h_j[n] + D x[t] )
  *   h_0 = 0,  h_{j+1}[n] = lam_n^T h_j[n] + sum_{tau<T} lam_n^(T-1-tau) x[jT + tau]
  * which equals the causal convolution with the whole filter.  The chunk convolution is the fused
- * transform of length 2T; the state terms cost O(NS) per element.
+ * transform of length 2T; the state terms cost O(NS) per element and run as matrix-core products
+ * over 64-long segments (bf16 operands; for fp32 data split into high and remainder parts).
  *   lam, W   [H][NS] fp32 complex (interleaved re, im), device; |lam| < 1 for a decaying filter
  *   prep     lconv_ssm_prep_bytes(H, NS, T, dtype) bytes, written by lconv_ssm_prepare: the chunk
  *            filter's spectrum and tables of powers of lam (opaque)
  *   u, y, q, v [B][H][N] dtype (q, v may be NULL);  D [H] dtype
- *   workspace  lconv_fftconv_ssm_workspace_bytes(B, H, N, NS, T) bytes (chunk sums, states)
+ *   workspace  lconv_fftconv_ssm_workspace_bytes(B, H, N, NS, T) bytes (chunk sums, boundary
+ *              states, the per-part states of the scan over chunks)
  * Supported: T a power of two in [256, 4096]; 1 <= NS <= 256; N a multiple of 8.
  */
 size_t lconv_ssm_prep_bytes(int64_t H, int64_t NS, int64_t T, lconv_dtype_t dtype);
