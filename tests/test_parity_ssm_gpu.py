@@ -48,6 +48,8 @@ CASES = [
     (2, 2, 3072, 96, 512, "qv"),      # two blocks of 64 modes, the second half padding
     (1, 1, 8200, 200, 2048, "q"),     # four blocks, ragged last chunk and tile
     (2, 2, 12296, 64, 4096, "v"),     # T = 4096 with a ragged last chunk: partial-mode chunk convolutions
+    (1, 2, 1000, 1, 4096, "q"),       # one mode; the sequence shorter than one chunk
+    (3, 2, 8192, 64, 1024, "qv"),     # odd batch, chunks of one tile each
 ]
 
 
