@@ -203,11 +203,47 @@ def time_backward(lconv, wl, spec, u, kf, D, q, v, args):
     ms = ev0.elapsed_time(ev1) / args.steps
     nbytes = backward_bytes(spec)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"ms_per_call": round(ms, 5), "algorithmic_bytes": nbytes, "achieved": round(gbs, 2),
-            "unit": "GB/s", "peak": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "outputs": "du, dq, dv (dtype); dk, dD (fp32)",
-            "launches": "forward kernel gated by dy (dv); adjoint kernel (du, dq); "
-                        "filter-gradient kernel (dk, dD)"}
+    out = {"ms_per_call": round(ms, 5), "algorithmic_bytes": nbytes, "achieved": round(gbs, 2),
+           "unit": "GB/s", "peak": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
+           "outputs": "du, dq, dv (dtype); dk, dD (fp32)",
+           "launches": "forward kernel gated by dy (dv); adjoint kernel (du, dq); "
+                       "filter-gradient kernel (dk, dD)"}
+    if v is not None:
+        # the training pair: the forward that also saves the pre-gate output c, and the gradient
+        # that takes dv = dy * c from it (one elementwise pass instead of the dy-gated transform)
+        y = torch.empty_like(u)
+        c = torch.empty_like(u)
+
+        def fwd_save():
+            st = lconv.lconv_fftconv_fwd_save(u.data_ptr(), kf.data_ptr(), D.data_ptr(), y.data_ptr(),
+                                              c.data_ptr(), p(q), p(v), spec.B, spec.H, spec.N, dtc,
+                                              stream.cuda_stream)
+            if st != 0:
+                raise lconv.LconvError(st, "lconv_fftconv_fwd_save")
+
+        def bwd_saved():
+            st = lconv.lconv_fftconv_bwd_saved(dy.data_ptr(), u.data_ptr(), kf.data_ptr(), D.data_ptr(), p(q),
+                                               p(v), c.data_ptr(), du.data_ptr(), p(dq), p(dv), dk.data_ptr(),
+                                               dD.data_ptr(), spec.B, spec.H, spec.N, dtc, stream.cuda_stream)
+            if st != 0:
+                raise lconv.LconvError(st, "lconv_fftconv_bwd_saved")
+
+        def timed(fn):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            ev0.record()
+            for _ in range(args.steps):
+                fn()
+            ev1.record()
+            torch.cuda.synchronize()
+            return ev0.elapsed_time(ev1) / args.steps
+
+        ms_f, ms_b = timed(fwd_save), timed(bwd_saved)
+        out["saved"] = {"fwd_save_ms": round(ms_f, 5), "bwd_saved_ms": round(ms_b, 5),
+                        "launches": "forward kernel that also stores c; dv = dy * c (elementwise); "
+                                    "adjoint kernel; filter-gradient kernel"}
+    return out
 
 
 def main():

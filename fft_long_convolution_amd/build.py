@@ -20,7 +20,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblconv.so")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["fused1d_conv.hip", "fused1d_adj.hip", "fused1d_part.hip", "fused1d_sparse.hip",
+HIP_SOURCES = ["fused1d_conv.hip", "fused1d_adj.hip", "fused1d_part.hip", "fused1d_sparse.hip", "fused1d_save.hip",
                "fused1d.hip", "bwd1d.hip", "multipass.hip", "fftconv2d.hip", "fftconv3d.hip",
                "stage.hip", "ssm.hip"]
 CPP_SOURCES = ["plan.cpp", "lconv_api.cpp"]

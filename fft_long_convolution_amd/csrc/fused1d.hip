@@ -32,6 +32,7 @@ hipError_t launch_fused1d(int R, int dtype, int mode, bool gq, bool gv, const Fu
     case MODE_ADJ: return launch_fused1d_adj(R, dtype, gq, gv, a, cus, stream);
     case MODE_PART: return launch_fused1d_part(R, dtype, gq, gv, a, cus, stream);
     case MODE_SPARSE: return launch_fused1d_sparse(R, dtype, gq, gv, a, cus, stream);
+    case MODE_SAVE: return launch_fused1d_save(R, dtype, gq, gv, a, cus, stream);
     default:
         return for_r(R, [&](auto r) { return launch_misc<decltype(r)::value>(dtype, mode, a, cus, stream); });
     }

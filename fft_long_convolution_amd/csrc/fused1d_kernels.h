@@ -50,7 +50,8 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
     constexpr bool ADJ = MODE == MODE_ADJ;
     constexpr bool PART = MODE == MODE_PART;
     constexpr bool SPARSE = MODE == MODE_SPARSE;
-    constexpr bool CONV = MODE == MODE_CONV || ADJ || SPARSE;  // batch-row input and output, half input
+    constexpr bool SAVE = MODE == MODE_SAVE;
+    constexpr bool CONV = MODE == MODE_CONV || ADJ || SPARSE || SAVE;  // batch-row input and output, half input
     constexpr bool BATCH = CONV || PART;             // batch rows, gates, filter per channel
     constexpr bool HALF_IN = (CONV || MODE == MODE_FILTER);
     constexpr bool HALF_OUT = BATCH;
@@ -792,6 +793,16 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                         store8<IO>(a.y2, o1, zi);
                     }
                 }
+                if constexpr (SAVE) {
+                    // the pre-gate output c, masked like y below
+                    float ci[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) ci[i] = FULL || o1 != o0 ? yi[i] : yr[i];
+                    if (FULL || ok0) {
+                        store8<IO>(a.y2, o0, yr);
+                        store8<IO>(a.y2, o1, ci);
+                    }
+                }
                 if constexpr (GV) {
                     float t[8];
                     unpack_raw<IO>(rv[0], t);
@@ -871,7 +882,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
 // ADJ: the adjoint chain (conjugate spectrum; outputs du = q dx and dq = u dx), as in
 // fused1d_kernel.
 // ------------------------------------------------------------------------------------------
-template <int CT, bool GQ, bool GV, bool ADJ>
+template <int CT, bool GQ, bool GV, bool ADJ, bool SAVE = false>
 __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
     constexpr int R = 32, M = 8192, KCF = 2;
     constexpr int IMG = ImgBytes<CT>::value;
@@ -1170,6 +1181,10 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
             store8<CT>(a.y2, o0, zr);
             store8<CT>(a.y2, o1, zi);
         }
+        if constexpr (SAVE) {   // the pre-gate output c
+            store8<CT>(a.y2, o0, yr);
+            store8<CT>(a.y2, o1, yi);
+        }
         if constexpr (GV) {
             float t[8];
             unpack_raw<CT>(&rv[0], t);
@@ -1252,14 +1267,14 @@ static hipError_t launch_t(const Fused1DArgs& a0, int cus, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int CT, bool GQ, bool GV, bool ADJ>
+template <int CT, bool GQ, bool GV, bool ADJ, bool SAVE>
 static hipError_t launch_8k(const Fused1DArgs& a0, int cus, hipStream_t st) {
     Fused1DArgs a = a0;
     if (a.nitems <= 0) return hipSuccess;
     int64_t nwg = a.nitems < cus ? a.nitems : cus;
     a.per_wg = (a.nitems + nwg - 1) / nwg;
     nwg = (a.nitems + a.per_wg - 1) / a.per_wg;
-    hipLaunchKernelGGL((conv8k_kernel<CT, GQ, GV, ADJ>), dim3((unsigned)nwg), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((conv8k_kernel<CT, GQ, GV, ADJ, SAVE>), dim3((unsigned)nwg), dim3(512), 0, st, a);
     return hipGetLastError();
 }
 
@@ -1268,10 +1283,11 @@ static hipError_t launch_conv(bool gq, bool gv, const Fused1DArgs& a, int cus, h
     constexpr bool ADJ = MODE == MODE_ADJ;
     if constexpr (R == 32 && T != CT_F32) {
         if (a.N == 4096) {  // whole rows: the pipelined kernel (the only one with row strides)
-            if (gq && gv) return launch_8k<T, true, true, ADJ>(a, cus, st);
-            if (gq) return launch_8k<T, true, false, ADJ>(a, cus, st);
-            if (gv) return launch_8k<T, false, true, ADJ>(a, cus, st);
-            return launch_8k<T, false, false, ADJ>(a, cus, st);
+            constexpr bool SAVE = MODE == MODE_SAVE;
+            if (gq && gv) return launch_8k<T, true, true, ADJ, SAVE>(a, cus, st);
+            if (gq) return launch_8k<T, true, false, ADJ, SAVE>(a, cus, st);
+            if (gv) return launch_8k<T, false, true, ADJ, SAVE>(a, cus, st);
+            return launch_8k<T, false, false, ADJ, SAVE>(a, cus, st);
         }
     }
     if (a.sb != 0 || a.sh != 0) return hipErrorInvalidValue;

@@ -9,8 +9,9 @@ namespace lcv {
 // whose causal truncation keeps the outputs that depend on later inputs).  PART is CONV for a
 // filter of at most M/2 taps on a sequence of any length, one block of M/2 outputs per item.
 // SPARSE is CONV with the filter spectrum kept only on the frequency blocks set in `keep`.
+// SAVE is CONV that also stores the pre-gate output c (the value v multiplies) to y2.
 enum Mode1D { MODE_CONV = 0, MODE_FILTER = 1, MODE_ROW = 2, MODE_ROWFWD = 3, MODE_ADJ = 4, MODE_PART = 5,
-              MODE_SPARSE = 6 };
+              MODE_SPARSE = 6, MODE_SAVE = 7 };
 
 struct Fused1DArgs {
     const void* u;       // CONV: u [B][H][N]; FILTER: k [H][N]; ROW/ROWFWD: workspace rows;
@@ -20,7 +21,8 @@ struct Fused1DArgs {
     const void* e2;      // ADJ: u (dq = u dx, used when v above is set); DK: dy
     void* y;             // CONV: y; FILTER/ROWFWD: k_f; ROW: workspace rows (in place);
                          // ADJ: du;  DK: dk [H][N] fp32 (nullable)
-    void* y2;            // ADJ: dq (when v above is set);  DK: dD [H] fp32 (nullable)
+    void* y2;            // ADJ: dq (when v above is set);  SAVE: c (pre-gate output);  DK: dD [H] fp32
+                         // (nullable)
     const void* kf;      // CONV/ROW/ADJ: k_f
     const void* D;       // CONV/ROW/ADJ: D [H]
     const void* tables;  // fused-path tables for (R, compute type)
@@ -55,6 +57,10 @@ hipError_t launch_fused1d_part(int R, int dtype, bool gq, bool gv, const Fused1D
                                hipStream_t stream);
 hipError_t launch_fused1d_sparse(int R, int dtype, bool gq, bool gv, const Fused1DArgs& a, int cus,
                                  hipStream_t stream);
+hipError_t launch_fused1d_save(int R, int dtype, bool gq, bool gv, const Fused1DArgs& a, int cus,
+                               hipStream_t stream);
+// y[i] = dy[i] * c[i] for n elements of type dtype (stage.hip): dv from a saved pre-gate output.
+hipError_t launch_mul_rows(const void* dy, const void* c, void* y, int64_t n, int dtype, hipStream_t stream);
 
 // Filter gradient: per channel h (items = channels), the sum over batch pairs of
 // conj(DFT(q u)) DFT(dy v), inverse-transformed; dk[h][n] for n < N and dD[h] = dk[h][0]

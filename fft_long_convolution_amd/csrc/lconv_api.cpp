@@ -405,9 +405,15 @@ lconv_status_t lconv_fftconv_partial_fwd(const void* u, const void* k_f, const v
     return partial_impl(u, k_f, D, y, q, v, B, H, N, L, dtype, 0, stream);
 }
 
-lconv_status_t lconv_fftconv_bwd(const void* dy, const void* u, const void* k_f, const void* D, const void* q,
-                                 const void* v, void* du, void* dq, void* dv, float* dk, float* dD, int64_t B,
-                                 int64_t H, int64_t N, lconv_dtype_t dtype, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The gradient call; with c (the forward's saved pre-gate output) dv = dy (.) c replaces the
+// forward-by-dy launch.
+lconv_status_t bwd_impl(const void* dy, const void* u, const void* k_f, const void* D, const void* q,
+                        const void* v, const void* c, void* du, void* dq, void* dv, float* dk, float* dD,
+                        int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype, hipStream_t stream) {
     if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
     if (B < 0 || H < 0 || N < 0) return LCONV_ERR_INVALID_SHAPE;
     int64_t elems, t, hn;
@@ -425,19 +431,19 @@ lconv_status_t lconv_fftconv_bwd(const void* dy, const void* u, const void* k_f,
         return LCONV_SUCCESS;
     }
     if (!dy || !u || !k_f || !D || !du || (q && !dq) || (v && !dv)) return LCONV_ERR_NULL_POINTER;
-    const void* ptrs[] = {dy, u, k_f, D, q, v, du, dq, dv, dk, dD};
+    const void* ptrs[] = {dy, u, k_f, D, q, v, c, du, dq, dv, dk, dD};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return LCONV_ERR_MISALIGNED;
     const size_t es = dtype_size(dtype), act = (size_t)elems * es;
     const size_t kf_bytes = lconv_filter_fft_bytes(H, N, dtype);
     if (kf_bytes == 0) return LCONV_ERR_INVALID_SHAPE;
     // every output against every input and every other output
-    const void* ins[] = {dy, u, k_f, D, q, v};
-    const size_t in_sz[] = {act, act, kf_bytes, (size_t)H * es, act, act};
+    const void* ins[] = {dy, u, k_f, D, q, v, c};
+    const size_t in_sz[] = {act, act, kf_bytes, (size_t)H * es, act, act, act};
     const void* outs[] = {du, dq, dv, dk, dD};
     const size_t out_sz[] = {act, act, act, (size_t)hn * 4, (size_t)H * 4};
     for (int o = 0; o < 5; ++o) {
-        for (int i = 0; i < 6; ++i)
+        for (int i = 0; i < 7; ++i)
             if (overlap(outs[o], out_sz[o], ins[i], in_sz[i])) return LCONV_ERR_ALIASING;
         for (int o2 = o + 1; o2 < 5; ++o2)
             if (overlap(outs[o], out_sz[o], outs[o2], out_sz[o2])) return LCONV_ERR_ALIASING;
@@ -455,8 +461,11 @@ lconv_status_t lconv_fftconv_bwd(const void* dy, const void* u, const void* k_f,
     base.kf = k_f; base.D = D; base.tables = tabs;
     base.B = B; base.H = H; base.N = N;
     base.inv_m = 1.0f / (float)p.M; base.M = p.M; base.M1 = 1;
-    // dv = dy (.) (k * x + D x): the forward convolution with dy as its post-gate
-    if (v) {
+    // dv = dy (.) (k * x + D x): from the saved pre-gate output, or the forward convolution with
+    // dy as its post-gate
+    if (v && c) {
+        if (launch_mul_rows(dy, c, dv, elems, (int)ct, stream) != hipSuccess) return LCONV_ERR_HIP;
+    } else if (v) {
         Fused1DArgs a = base;
         a.u = u; a.q = q; a.v = dy; a.y = dv; a.nitems = seqs;
         if (launch_fused1d(p.R, dtype, MODE_CONV, q != nullptr, true, a, cus, stream) != hipSuccess)
@@ -477,6 +486,60 @@ lconv_status_t lconv_fftconv_bwd(const void* dy, const void* u, const void* k_f,
             return LCONV_ERR_HIP;
     }
     return LCONV_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+lconv_status_t lconv_fftconv_bwd(const void* dy, const void* u, const void* k_f, const void* D, const void* q,
+                                 const void* v, void* du, void* dq, void* dv, float* dk, float* dD, int64_t B,
+                                 int64_t H, int64_t N, lconv_dtype_t dtype, hipStream_t stream) {
+    return bwd_impl(dy, u, k_f, D, q, v, nullptr, du, dq, dv, dk, dD, B, H, N, dtype, stream);
+}
+
+lconv_status_t lconv_fftconv_bwd_saved(const void* dy, const void* u, const void* k_f, const void* D,
+                                       const void* q, const void* v, const void* c, void* du, void* dq, void* dv,
+                                       float* dk, float* dD, int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype,
+                                       hipStream_t stream) {
+    if (!c && v && B > 0 && H > 0 && N > 0) return LCONV_ERR_NULL_POINTER;
+    return bwd_impl(dy, u, k_f, D, q, v, c, du, dq, dv, dk, dD, B, H, N, dtype, stream);
+}
+
+lconv_status_t lconv_fftconv_fwd_save(const void* u, const void* k_f, const void* D, void* y, void* c,
+                                      const void* q, const void* v, int64_t B, int64_t H, int64_t N,
+                                      lconv_dtype_t dtype, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
+    if (B < 0 || H < 0 || N < 0) return LCONV_ERR_INVALID_SHAPE;
+    int64_t elems, t;
+    if (!mul_ok(B, H, &t) || !mul_ok(t, N, &elems) || !mul_ok(elems, 8, &t)) return LCONV_ERR_INVALID_SHAPE;
+    if (B == 0 || H == 0 || N == 0) return LCONV_SUCCESS;
+    if (!n_supported(N) || N > LCONV_BWD_MAX_N) return LCONV_ERR_UNSUPPORTED;
+    if (!u || !k_f || !D || !y || !c) return LCONV_ERR_NULL_POINTER;
+    const void* ptrs[] = {u, k_f, D, y, c, q, v};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return LCONV_ERR_MISALIGNED;
+    const size_t es = dtype_size(dtype), act = (size_t)elems * es;
+    const size_t kf_bytes = lconv_filter_fft_bytes(H, N, dtype);
+    if (kf_bytes == 0) return LCONV_ERR_INVALID_SHAPE;
+    const void* ins[] = {u, k_f, D, q, v};
+    const size_t in_sz[] = {act, kf_bytes, (size_t)H * es, act, act};
+    for (int i = 0; i < 5; ++i)
+        if (overlap(y, act, ins[i], in_sz[i]) || overlap(c, act, ins[i], in_sz[i])) return LCONV_ERR_ALIASING;
+    if (overlap(y, act, c, act)) return LCONV_ERR_ALIASING;
+    Plan1D p;
+    make_plan_1d(N, &p);
+    hipError_t err = hipSuccess;
+    const int cus = device_cu_count(&err);
+    if (!cus) return LCONV_ERR_HIP;
+    const int ct = dtype == LCONV_F32 ? CT_F32 : (int)dtype;
+    const void* tabs = fused_tables(p.R, ct, &err);
+    if (!tabs) return LCONV_ERR_HIP;
+    Fused1DArgs a{};
+    a.u = u; a.q = q; a.v = v; a.y = y; a.y2 = c; a.kf = k_f; a.D = D; a.tables = tabs;
+    a.B = B; a.H = H; a.N = N; a.nitems = pairs_per_channel(B) * H;
+    a.inv_m = 1.0f / (float)p.M; a.M = p.M; a.M1 = 1;
+    return hip_status(launch_fused1d(p.R, dtype, MODE_SAVE, q != nullptr, v != nullptr, a, cus, stream));
 }
 
 lconv_status_t lconv_filter_fft2d(const void* k, void* k_f, int64_t C, int64_t S, lconv_dtype_t dtype,

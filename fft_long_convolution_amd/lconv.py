@@ -6,7 +6,8 @@ There is no CPU fallback: if the library is missing, importing the entry points 
 
 Raw entry points keep the C names (``lconv_filter_fft``, ``lconv_fftconv_fwd``, ...), taking
 integer device pointers.  ``filter_fft``, ``fftconv``, ``fftconv_partial``, ``fftconv_sparse``,
-``fftconv_bwd``, ``filter_fft2d`` and ``fftconv2d`` are convenience wrappers over torch tensors.
+``fftconv_bwd``, ``fftconv_save``, ``filter_fft2d`` and ``fftconv2d`` are convenience wrappers over torch
+tensors.
 """
 from __future__ import annotations
 
@@ -51,6 +52,8 @@ def load(path: str = LIB_PATH):
         "lconv_filter_fft": (i, [vp, vp, i64, i64, i, vp, sz, vp]),
         "lconv_fftconv_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i, vp, sz, vp]),
         "lconv_fftconv_bwd": (i, [vp] * 11 + [i64, i64, i64, i, vp]),
+        "lconv_fftconv_fwd_save": (i, [vp] * 7 + [i64, i64, i64, i, vp]),
+        "lconv_fftconv_bwd_saved": (i, [vp] * 12 + [i64, i64, i64, i, vp]),
         "lconv_fftconv_partial_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i, vp]),
         "lconv_fftconv_sparse_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_uint32, i, vp]),
         "lconv_freq_blocks": (i, [i64]),
@@ -113,6 +116,14 @@ def lconv_fftconv_fwd(u, k_f, D, y, q, v, B, H, N, dtype, workspace, workspace_b
 
 def lconv_fftconv_bwd(dy, u, k_f, D, q, v, du, dq, dv, dk, dD, B, H, N, dtype, stream):
     return load().lconv_fftconv_bwd(dy, u, k_f, D, q, v, du, dq, dv, dk, dD, B, H, N, dtype, stream)
+
+
+def lconv_fftconv_fwd_save(u, k_f, D, y, c, q, v, B, H, N, dtype, stream):
+    return load().lconv_fftconv_fwd_save(u, k_f, D, y, c, q, v, B, H, N, dtype, stream)
+
+
+def lconv_fftconv_bwd_saved(dy, u, k_f, D, q, v, c, du, dq, dv, dk, dD, B, H, N, dtype, stream):
+    return load().lconv_fftconv_bwd_saved(dy, u, k_f, D, q, v, c, du, dq, dv, dk, dD, B, H, N, dtype, stream)
 
 
 def lconv_fftconv_partial_fwd(u, k_f, D, y, q, v, B, H, N, L, dtype, stream):
@@ -244,9 +255,23 @@ def fftconv(u, k_f, D, q=None, v=None, out=None, stream=None):
     return y
 
 
-def fftconv_bwd(dy, u, k_f, D, q=None, v=None, need_dk=True, stream=None):
+def fftconv_save(u, k_f, D, q=None, v=None, stream=None):
+    """(y, c): y = v * c with the pre-gate output c = (k * (q*u))[:N] + D * (q*u), for the
+    gradient call (N <= 4096)."""
+    torch = _torch()
+    B, H, N = u.shape
+    dt = dtype_code(u.dtype)
+    y = torch.empty_like(u)
+    c = torch.empty_like(u)
+    _check(lconv_fftconv_fwd_save(_ptr(u), _ptr(k_f), _ptr(D), _ptr(y), _ptr(c), _ptr(q), _ptr(v),
+                                  B, H, N, dt, _stream(stream)), "lconv_fftconv_fwd_save")
+    return y, c
+
+
+def fftconv_bwd(dy, u, k_f, D, q=None, v=None, need_dk=True, c=None, stream=None):
     """Gradients of y = v * ((k * (q*u))[:N] + D * (q*u)) given dy [B, H, N].
 
+    With c (the pre-gate output from fftconv_save), dv = dy * c without a transform.
     Returns (du, dq, dv, dk, dD): du, dq, dv in u's dtype (dq is None without q, dv is None
     without v); dk [H, N] and dD [H] in float32 (None when need_dk is False)."""
     torch = _torch()
@@ -257,9 +282,14 @@ def fftconv_bwd(dy, u, k_f, D, q=None, v=None, need_dk=True, stream=None):
     dv = torch.empty_like(u) if v is not None else None
     dk = torch.empty((H, N), dtype=torch.float32, device=u.device) if need_dk else None
     dD = torch.empty((H,), dtype=torch.float32, device=u.device) if need_dk else None
-    _check(lconv_fftconv_bwd(_ptr(dy), _ptr(u), _ptr(k_f), _ptr(D), _ptr(q), _ptr(v), _ptr(du),
-                             _ptr(dq), _ptr(dv), _ptr(dk), _ptr(dD), B, H, N, dt, _stream(stream)),
-           "lconv_fftconv_bwd")
+    if c is None:
+        _check(lconv_fftconv_bwd(_ptr(dy), _ptr(u), _ptr(k_f), _ptr(D), _ptr(q), _ptr(v), _ptr(du),
+                                 _ptr(dq), _ptr(dv), _ptr(dk), _ptr(dD), B, H, N, dt, _stream(stream)),
+               "lconv_fftconv_bwd")
+    else:
+        _check(lconv_fftconv_bwd_saved(_ptr(dy), _ptr(u), _ptr(k_f), _ptr(D), _ptr(q), _ptr(v), _ptr(c),
+                                       _ptr(du), _ptr(dq), _ptr(dv), _ptr(dk), _ptr(dD), B, H, N, dt,
+                                       _stream(stream)), "lconv_fftconv_bwd_saved")
     return du, dq, dv, dk, dD
 
 

@@ -192,6 +192,30 @@ lconv_status_t lconv_fftconv_bwd(const void* dy, const void* u, const void* k_f,
 /* Largest sequence length lconv_fftconv_bwd supports. */
 #define LCONV_BWD_MAX_N ((int64_t)4096)
 
+/*
+ * Forward call for training: lconv_fftconv_fwd that also writes the pre-gate output
+ *   c = (k * x)[:N] + D x        (y = v (.) c; c = y when v is NULL)
+ * which the gradient of v needs (dv = dy (.) c, the same quantity lconv_fftconv_bwd otherwise
+ * recomputes with a forward transform).
+ *   c  [B][H][N] dtype, device, written; must not overlap y or any input
+ * Other arguments as for lconv_fftconv_fwd.  Supported: N <= LCONV_BWD_MAX_N, N a multiple of 8.
+ */
+lconv_status_t lconv_fftconv_fwd_save(const void* u, const void* k_f, const void* D, void* y, void* c,
+                                      const void* q, const void* v, int64_t B, int64_t H, int64_t N,
+                                      lconv_dtype_t dtype, hipStream_t stream);
+
+/*
+ * lconv_fftconv_bwd with the pre-gate output c saved by lconv_fftconv_fwd_save: dv = dy (.) c
+ * (one elementwise pass) instead of the forward transform gated by dy; du, dq, dk, dD as there.
+ *   c  [B][H][N] dtype, device, as written by lconv_fftconv_fwd_save on the same u, q, k_f, D;
+ *      required when v is given (LCONV_ERR_NULL_POINTER otherwise), ignored without v.
+ * Other arguments, outputs and limits as for lconv_fftconv_bwd.
+ */
+lconv_status_t lconv_fftconv_bwd_saved(const void* dy, const void* u, const void* k_f, const void* D,
+                                       const void* q, const void* v, const void* c, void* du, void* dq,
+                                       void* dv, float* dk, float* dD, int64_t B, int64_t H, int64_t N,
+                                       lconv_dtype_t dtype, hipStream_t stream);
+
 /* ---- 2D (HyenaND-style) ------------------------------------------------------------------ */
 
 /*

@@ -159,6 +159,41 @@ def test_bwd_empty_and_ignored_outputs():
         assert bwd(dq=G[0]) == HIPERR
 
 
+def fsave(u=G[0], kf=G[1], D=G[2], y=G[3], c=G[4], q=None, v=None, B=2, H=3, N=64, dt=BF16):
+    return lconv.lconv_fftconv_fwd_save(u, kf, D, y, c, q, v, B, H, N, dt, None)
+
+
+def bsaved(dy=G[0], u=G[1], kf=G[2], D=G[3], q=None, v=None, c=None, du=G[4], dq=None, dv=None,
+           dk=None, dD=None, B=2, H=3, N=64, dt=BF16):
+    return lconv.lconv_fftconv_bwd_saved(dy, u, kf, D, q, v, c, du, dq, dv, dk, dD, B, H, N, dt, None)
+
+
+def test_forward_save_validation_errors():
+    assert fsave(dt=5) == UNSUP
+    assert fsave(B=-1) == SHAPE
+    assert fsave(N=12) == UNSUP                                            # N % 8
+    assert fsave(N=8192) == UNSUP                                          # single transform only
+    assert fsave(c=None) == NULLP
+    assert fsave(y=None) == NULLP
+    assert fsave(c=G[4] + 8) == MISAL
+    assert fsave(c=G[3]) == ALIAS                                          # c == y
+    assert fsave(c=G[0] + 64) == ALIAS                                     # c overlaps u
+    assert fsave(v=G[5], y=G[5] + 32) == ALIAS                             # y overlaps v
+    assert fsave(B=0) == OK and fsave(H=0) == OK and fsave(N=0) == OK
+
+
+def test_saved_gradient_validation_errors():
+    assert bsaved(v=G[6], dv=G[7]) == NULLP                                # v without c
+    assert bsaved(v=G[6], dv=G[7], c=G[8] + 4) == MISAL
+    assert bsaved(v=G[6], dv=G[7], c=G[4]) == ALIAS                        # du overlaps c
+    assert bsaved(v=G[6], dv=G[8], c=G[8]) == ALIAS                        # dv == c
+    assert bsaved(N=8192) == UNSUP
+    assert bsaved(B=0) == OK
+    import torch
+    if not torch.cuda.is_available():                                      # c ignored without v
+        assert bsaved(c=None) == HIPERR
+
+
 def part(u=G[0], kf=G[1], D=G[2], y=G[3], q=None, v=None, B=2, H=3, N=64, L=32, dt=BF16):
     return lconv.lconv_fftconv_partial_fwd(u, kf, D, y, q, v, B, H, N, L, dt, None)
 
