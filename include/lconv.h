@@ -46,7 +46,10 @@
 extern "C" {
 #endif
 
-#define LCONV_ABI_VERSION 2
+/* Bumped when entry points are added or a size query's result changes (3: the training pair
+ * lconv_fftconv_fwd_save / lconv_fftconv_bwd_saved; the state-space workspace holds the scan's
+ * part states). */
+#define LCONV_ABI_VERSION 3
 
 typedef enum { LCONV_F32 = 0, LCONV_F16 = 1, LCONV_BF16 = 2 } lconv_dtype_t;
 

@@ -27,7 +27,7 @@ def test_exports_every_header_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lconv.lconv_abi_version() == 2
+    assert lconv.lconv_abi_version() == 3
     for s in range(8):
         assert lconv.status_string(s)
     assert "unknown" in lconv.status_string(99)
