@@ -122,9 +122,8 @@ static void or_row_x(const or_job* J, int64_t b, int64_t h, int64_t len, double*
         for (int64_t s = 0; s < len; ++s) x[s] *= or_load(J->q, J->dt, off + s);
 }
 
-/* Full output rows.  Four outputs are carried at once so that their independent sums overlap
- * in the FPU; each one is still accumulated in ascending s, exactly as the one-at-a-time
- * loop would do it. */
+/* Full output rows: for each t, the causal sum over s = 0..t in ascending s, then the skip
+ * term and the post-gate. */
 static void* or_rows_worker(void* arg) {
     or_job* J = (or_job*)arg;
     const int64_t N = J->N;
@@ -136,32 +135,11 @@ static void* or_rows_worker(void* arg) {
         or_widen(J->k, J->dt, h * N, N, k);
         double d = or_load(J->D, J->dt, h);
         double* y = J->out + r * N;
-        int64_t t0 = 0;
-        for (; t0 + 4 <= N; t0 += 4) {
-            double a0 = 0, a1 = 0, a2 = 0, a3 = 0;
-            for (int64_t s = 0; s <= t0; ++s) {
-                double xs = x[s];
-                a0 += k[t0 - s] * xs;
-                a1 += k[t0 + 1 - s] * xs;
-                a2 += k[t0 + 2 - s] * xs;
-                a3 += k[t0 + 3 - s] * xs;
-            }
-            a1 += k[0] * x[t0 + 1];
-            a2 += k[1] * x[t0 + 1];
-            a2 += k[0] * x[t0 + 2];
-            a3 += k[2] * x[t0 + 1];
-            a3 += k[1] * x[t0 + 2];
-            a3 += k[0] * x[t0 + 3];
-            y[t0] = a0; y[t0 + 1] = a1; y[t0 + 2] = a2; y[t0 + 3] = a3;
-        }
-        for (; t0 < N; ++t0) {
-            double a = 0;
-            for (int64_t s = 0; s <= t0; ++s) a += k[t0 - s] * x[s];
-            y[t0] = a;
-        }
         int64_t off = (b * J->H + h) * N;
         for (int64_t t = 0; t < N; ++t) {
-            double val = y[t] + d * x[t];
+            double a = 0;
+            for (int64_t s = 0; s <= t; ++s) a += k[t - s] * x[s];
+            double val = a + d * x[t];
             if (J->v) val *= or_load(J->v, J->dt, off + t);
             y[t] = val;
         }

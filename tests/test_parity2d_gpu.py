@@ -62,6 +62,8 @@ def test_2d_delta_kernel_is_identity(lc):
 
 
 def test_2d_workload_hyenand(lc, nthreads):
+    """B8 C256 128x128: every one of the 2,048 images against the naive-DFT oracle, plus 4096
+    sampled positions by direct summation."""
     name = "hyenand_2d_bf16_b8_c256_s128"
     d = wl.make(name)
     say(f"[workload] {name}")
@@ -70,27 +72,16 @@ def test_2d_workload_hyenand(lc, nthreads):
     pts = wl.sample_points_2d(8, 256, 128, seed=2005)
     refp = oracle.conv2d_points(d["u"], d["k"], d["D"], pts, dt=oracle.DT_BF16, nthreads=nthreads)
     err = rel_l2(y[pts[:, 0], pts[:, 1], pts[:, 2], pts[:, 3]], refp)
-    rng = np.random.default_rng(3005)
-    imgs = [(int(rng.integers(0, 8)), int(rng.integers(0, 256))) for _ in range(6)] + [(7, 255)]
-    ref = oracle.conv2d_dft(d["u"], d["k"], d["D"], imgs, dt=oracle.DT_BF16)
-    got = np.stack([y[b, c] for b, c in imgs])
-    err_img = rel_l2_rows(got.reshape(len(imgs), -1), ref.reshape(len(imgs), -1)).max()
-    say(f"   sampled pooled rel L2 = {err:.3e}, full images max rel L2 = {err_img:.3e}")
-    assert err <= 2e-2 and err_img <= 2e-2
-
-
-def test_2d_more_items_than_workgroups(lc):
-    """300 channels of one batch pair on at most 256 workgroups: workgroups renumbered XCD by XCD,
-    some taking a second item.  Full images of channels on both sides of the first round."""
-    B, C = 2, 300
-    spec = wl.Conv2DSpec("t2d_bf16_2_300", B, C, 128, "bf16", seed=77)
-    say(f"[2d] B={B} C={C} seed={spec.seed}")
-    d = wl.make(spec)
-    y = run_2d(lc, d)
-    chans = [0, 1, 7, 8, 31, 32, 255, 256, 257, 299]
-    imgs = [(b, c) for b in range(B) for c in chans]
-    ref = oracle.conv2d_dft(d["u"], d["k"], d["D"], imgs, dt=DT_ORACLE["bf16"]).reshape(len(imgs), -1)
-    got = np.stack([y[b, c].reshape(-1) for b, c in imgs])
-    err = rel_l2_rows(got, ref).max()
-    say(f"   max rel L2 = {err:.3e}")
-    assert np.all(np.isfinite(got)) and err <= 2e-2
+    worst, worst_at, max_abs = 0.0, None, 0.0
+    for c0 in range(0, 256, 32):   # 32 channels (256 images) at a time bounds the oracle's memory
+        imgs = [(b, c) for c in range(c0, c0 + 32) for b in range(8)]
+        ref = oracle.conv2d_dft(d["u"], d["k"], d["D"], imgs, dt=oracle.DT_BF16)
+        got = np.stack([y[b, c] for b, c in imgs])
+        e = rel_l2_rows(got.reshape(len(imgs), -1), ref.reshape(len(imgs), -1))
+        i = int(np.argmax(e))
+        if e[i] > worst:
+            worst, worst_at = float(e[i]), imgs[i]
+        max_abs = max(max_abs, float(np.max(np.abs(got - ref))))
+    say(f"   all 2048 images: max rel L2 = {worst:.3e} at (b,c)={worst_at}, max abs err {max_abs:.3e}; "
+        f"sampled pooled rel L2 = {err:.3e}")
+    assert err <= 2e-2 and worst <= 2e-2

@@ -72,24 +72,25 @@ def test_workload_causal_f32(lc, nthreads):
 
 
 def test_workload_hyena_gated_bf16(lc, nthreads):
-    """B16 H768 N4096: 4096 sampled positions plus 64 seeded full rows."""
+    """B16 H768 N4096: every one of the 12,288 (b,h) rows against the oracle, plus the 4096
+    sampled positions (pooled) that the larger workloads use."""
     name = "hyena_gated_bf16_b16_h768_n4096"
     d = wl.make(name)
     say(f"[workload] {name}")
     y, _ = run_1d(lc, d)
     assert np.all(np.isfinite(y))
-    rng = np.random.default_rng(3002)
-    rows = np.stack([rng.integers(0, 16, 64), rng.integers(0, 768, 64)], 1)
-    rows[0] = (15, 767)
-    ref = oracle_rows(d, rows, nthreads)
-    got = y[rows[:, 0], rows[:, 1]]
-    err_rows = rel_l2_rows(got, ref).max()
+    rows = [(b, h) for b in range(16) for h in range(768)]
+    ref = oracle_rows(d, rows, nthreads).reshape(16, 768, 4096)
+    per_row = rel_l2_rows(y, ref)
+    worst = np.unravel_index(int(np.argmax(per_row)), per_row.shape)
+    max_abs = float(np.max(np.abs(y - ref)))
     pts = wl.sample_points_1d(16, 768, 4096, seed=2002)
     refp = oracle.conv1d_points(d["u"], d["k"], d["D"], pts, q=d["q"], v=d["v"],
                                 dt=oracle.DT_BF16, nthreads=nthreads)
     err_pts = rel_l2(y[pts[:, 0], pts[:, 1], pts[:, 2]], refp)
-    say(f"   rows max rel L2 = {err_rows:.3e}, sampled pooled rel L2 = {err_pts:.3e}")
-    assert err_rows <= 2e-2 and err_pts <= 2e-2
+    say(f"   all 12288 rows: max rel L2 = {per_row.max():.3e} at (b,h)={tuple(int(i) for i in worst)}, "
+        f"median {np.median(per_row):.3e}, max abs err {max_abs:.3e}; sampled pooled rel L2 = {err_pts:.3e}")
+    assert per_row.max() <= 2e-2 and err_pts <= 2e-2
 
 
 def _sampled_long(lc, name, nthreads, n_rows_full=0):

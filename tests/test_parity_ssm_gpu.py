@@ -24,12 +24,20 @@ def lc():
     return lconv
 
 
+def modes(H, NS, seed):
+    """Seeded modes rounded once to complex64: the kernel and the oracle take the same values
+    (the oracle widens them exactly to complex128)."""
+    lam, W = wl.ssm_modes(H, NS, seed=seed)
+    return lam.astype(np.complex64), W.astype(np.complex64)
+
+
 def run_ssm(lc, d, lam, W, T, q, v):
     import torch
     dt = d["dtype"]
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dt]
-    lam_d = torch.from_numpy(lam.astype(np.complex64)).cuda()
-    W_d = torch.from_numpy(W.astype(np.complex64)).cuda()
+    assert lam.dtype == np.complex64 and W.dtype == np.complex64
+    lam_d = torch.from_numpy(lam).cuda()
+    W_d = torch.from_numpy(W).cuda()
     prep = lc.ssm_prepare(lam_d, W_d, T, tdt)
     y = lc.fftconv_ssm(to_dev(d["u"], dt), prep, to_dev(d["D"], dt), lam.shape[1], T,
                        q=to_dev(q, dt), v=to_dev(v, dt))
@@ -59,7 +67,7 @@ def test_ssm_full_rows(lc, nthreads, dtype, B, H, N, NS, T, gates):
     spec = wl.spec_1d(B, H, N, dtype, gated=True, seed=1500 + N + NS)
     say(f"[ssm] dtype={dtype} B={B} H={H} N={N} NS={NS} T={T} gates={gates!r} seed={spec.seed}")
     d = wl.make(spec)
-    lam, W = wl.ssm_modes(H, NS, seed=spec.seed + 1)
+    lam, W = modes(H, NS, seed=spec.seed + 1)
     q = d["q"] if "q" in gates else None
     v = d["v"] if "v" in gates else None
     y = run_ssm(lc, d, lam, W, T, q, v)
@@ -77,7 +85,7 @@ def test_ssm_long_workload_rows(lc, nthreads):
     spec = wl.WORKLOADS["ssm_bf16_b1_h64_n2097152_ns64"]
     say(f"[ssm long] {spec.name} seed={spec.seed}")
     d = wl.make(spec)
-    lam, W = wl.ssm_modes(spec.H, 64, seed=spec.seed + 1)
+    lam, W = modes(spec.H, 64, seed=spec.seed + 1)
     y = run_ssm(lc, d, lam, W, 4096, d["q"], d["v"])
     rows = [(0, 0), (0, 37), (0, 63)]
     ref = oracle.ssm_rows(d["u"], lam, W, d["D"], rows, q=d["q"], v=d["v"], dt=DT_ORACLE["bf16"],
