@@ -85,3 +85,20 @@ def test_2d_workload_hyenand(lc, nthreads):
     say(f"   all 2048 images: max rel L2 = {worst:.3e} at (b,c)={worst_at}, max abs err {max_abs:.3e}; "
         f"sampled pooled rel L2 = {err:.3e}")
     assert err <= 2e-2 and worst <= 2e-2
+
+
+def test_2d_more_items_than_workgroups(lc):
+    """300 channels of one batch pair on at most 256 workgroups: workgroups renumbered XCD by XCD,
+    some taking a second item.  Full images of channels on both sides of the first round."""
+    B, C = 2, 300
+    spec = wl.Conv2DSpec("t2d_bf16_2_300", B, C, 128, "bf16", seed=77)
+    say(f"[2d] B={B} C={C} seed={spec.seed}")
+    d = wl.make(spec)
+    y = run_2d(lc, d)
+    chans = [0, 1, 7, 8, 31, 32, 255, 256, 257, 299]
+    imgs = [(b, c) for b in range(B) for c in chans]
+    ref = oracle.conv2d_dft(d["u"], d["k"], d["D"], imgs, dt=DT_ORACLE["bf16"]).reshape(len(imgs), -1)
+    got = np.stack([y[b, c].reshape(-1) for b, c in imgs])
+    err = rel_l2_rows(got, ref).max()
+    say(f"   max rel L2 = {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= 2e-2
