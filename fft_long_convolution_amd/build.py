@@ -45,8 +45,18 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every source and link liblconv.so; returns its path."""
+def _stale(obj: str, src: str) -> bool:
+    """True when obj is missing or older than its source or any header it may include."""
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    deps = [src] + [os.path.join(d, f) for d in (CSRC, INCLUDE) for f in os.listdir(d) if f.endswith(".h")]
+    return any(os.path.getmtime(p) > t for p in deps)
+
+
+def build(verbose: bool = False, jobs: int = 8, incremental: bool = False) -> str:
+    """Compile every source (only the stale ones with incremental=True) and link liblconv.so;
+    returns its path."""
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
     cmds = []
@@ -56,12 +66,14 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         if not os.path.exists(src):
             continue
         obj = os.path.join(BUILD, s + ".o")
-        cmds.append([hipcc, *COMMON, *DEVICE, "-c", src, "-o", obj])
+        if not incremental or _stale(obj, src):
+            cmds.append([hipcc, *COMMON, *DEVICE, "-c", src, "-o", obj])
         objs.append(obj)
     for s in CPP_SOURCES:
         src = os.path.join(CSRC, s)
         obj = os.path.join(BUILD, s + ".o")
-        cmds.append([hipcc, *COMMON, "-c", src, "-o", obj])
+        if not incremental or _stale(obj, src):
+            cmds.append([hipcc, *COMMON, "-c", src, "-o", obj])
         objs.append(obj)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         for out in ex.map(_run, cmds):
@@ -74,4 +86,4 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv))
