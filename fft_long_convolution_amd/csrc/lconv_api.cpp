@@ -5,6 +5,7 @@
 #include <cstdint>
 #include <cstring>
 
+#include "api_internal.h"
 #include "kernels.h"
 #include "plan.h"
 
@@ -49,8 +50,8 @@ size_t staging_bytes(int64_t rows, int64_t N, lconv_dtype_t dt, int tensors) {
 // sequences = complex transforms: pairs of batch rows per channel
 int64_t pairs_per_channel(int64_t B) { return (B + 1) / 2; }
 
-int64_t chunk_seqs(int64_t total, int64_t M, size_t csz) {
-    int64_t per = (int64_t)(kChunkTarget / ((size_t)M * csz));
+int64_t chunk_seqs(int64_t total, int64_t M, size_t csz, size_t target = kChunkTarget) {
+    int64_t per = (int64_t)(target / ((size_t)M * csz));
     if (per < 1) per = 1;
     return per < total ? per : total;
 }
@@ -62,7 +63,25 @@ lconv_status_t filter_fft_aligned(const void* k, void* k_f, int64_t H, int64_t N
                                   void* workspace, hipStream_t stream);
 lconv_status_t fftconv_fwd_aligned(const void* u, const void* k_f, const void* D, void* y, const void* q,
                                    const void* v, int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype,
-                                   void* workspace, hipStream_t stream);
+                                   void* workspace, size_t chunk_target, bool may_build, hipStream_t stream);
+
+bool tables_ready(const Plan1D& p, lconv_dtype_t dtype);
+
+// Workspace of the forward call when the multi-pass chunks hold at most `target` bytes:
+// staging (N not a multiple of 8) followed by one chunk.  0 if nothing is needed; SIZE_MAX for
+// invalid arguments or when not even one sequence fits the target.
+size_t fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype, size_t target) {
+    Plan1D p;
+    int64_t seqs, rows;
+    if (!dtype_ok(dtype) || B < 0 || H < 0 || !n_in_range(N) || !make_plan_1d(N, &p)) return SIZE_MAX;
+    if (B == 0 || H == 0) return 0;
+    if (!mul_ok(pairs_per_channel(B), H, &seqs) || !mul_ok(B, H, &rows)) return SIZE_MAX;
+    const size_t stage = staging_bytes(rows, N, dtype, 4);  // u, q, v, y
+    if (!p.multipass) return stage;
+    const size_t csz = work_complex_size(dtype, false);
+    if (target < (size_t)p.M * csz) return SIZE_MAX;
+    return stage + (size_t)chunk_seqs(seqs, p.M, csz, target) * (size_t)p.M * csz;
+}
 
 }  // namespace
 
@@ -80,6 +99,8 @@ const char* lconv_status_string(lconv_status_t s) {
     case LCONV_ERR_ALIASING: return "the output overlaps an input";
     case LCONV_ERR_WORKSPACE: return "workspace missing or too small";
     case LCONV_ERR_HIP: return "HIP runtime error";
+    case LCONV_ERR_NOT_PREPARED: return "lconv_prepare was not called for this device, length and dtype";
+    case LCONV_ERR_SCRATCH_LIMIT: return "the call needs more scratch than the static buffer holds";
     }
     return "unknown status";
 }
@@ -103,15 +124,8 @@ size_t lconv_filter_fft_workspace_bytes(int64_t H, int64_t N, lconv_dtype_t dtyp
 }
 
 size_t lconv_fftconv_workspace_bytes(int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype) {
-    Plan1D p;
-    int64_t seqs, rows;
-    if (!dtype_ok(dtype) || B < 0 || H < 0 || !n_in_range(N) || !make_plan_1d(N, &p)) return 0;
-    if (B == 0 || H == 0) return 0;
-    if (!mul_ok(pairs_per_channel(B), H, &seqs) || !mul_ok(B, H, &rows)) return 0;
-    const size_t stage = staging_bytes(rows, N, dtype, 4);  // u, q, v, y
-    if (!p.multipass) return stage;
-    const size_t csz = work_complex_size(dtype, false);
-    return stage + (size_t)chunk_seqs(seqs, p.M, csz) * (size_t)p.M * csz;
+    const size_t w = fwd_workspace_bytes(B, H, N, dtype, kChunkTarget);
+    return w == SIZE_MAX ? 0 : w;
 }
 
 size_t lconv_filter_fft2d_bytes(int64_t C, int64_t S, lconv_dtype_t dtype) {
@@ -199,6 +213,18 @@ extern "C" {
 lconv_status_t lconv_fftconv_fwd(const void* u, const void* k_f, const void* D, void* y, const void* q,
                                  const void* v, int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return fftconv_fwd_call(u, k_f, D, y, q, v, B, H, N, dtype, workspace, workspace_bytes, kChunkTarget,
+                            true, stream);
+}
+
+}  // extern "C"
+
+namespace lcv {
+
+lconv_status_t fftconv_fwd_call(const void* u, const void* k_f, const void* D, void* y, const void* q,
+                                const void* v, int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype,
+                                void* workspace, size_t workspace_bytes, size_t chunk_target, bool may_build,
+                                hipStream_t stream) {
     if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
     if (B < 0 || H < 0 || N < 0) return LCONV_ERR_INVALID_SHAPE;
     int64_t elems, t;
@@ -215,7 +241,8 @@ lconv_status_t lconv_fftconv_fwd(const void* u, const void* k_f, const void* D, 
     if (overlap(y, act, u, act) || overlap(y, act, q, act) || overlap(y, act, v, act) ||
         overlap(y, act, k_f, kf_bytes) || overlap(y, act, D, (size_t)H * es))
         return LCONV_ERR_ALIASING;
-    const size_t need = lconv_fftconv_workspace_bytes(B, H, N, dtype);
+    const size_t need = fwd_workspace_bytes(B, H, N, dtype, chunk_target);
+    if (need == SIZE_MAX) return LCONV_ERR_WORKSPACE;
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return LCONV_ERR_WORKSPACE;
         if (!aligned16(workspace)) return LCONV_ERR_MISALIGNED;
@@ -232,30 +259,67 @@ lconv_status_t lconv_fftconv_fwd(const void* u, const void* k_f, const void* D, 
         char* st = (char*)workspace;
         void *su = st, *sq = q ? st + one : nullptr, *sv = v ? st + 2 * one : nullptr, *sy = st + 3 * one;
         const int esz = (int)es;
+        // the tables first: without them (may_build false) nothing is launched
+        Plan1D p8;
+        make_plan_1d(N8, &p8);
+        if (!may_build && !tables_ready(p8, dtype)) return LCONV_ERR_NOT_PREPARED;
         if (launch_pad_rows(u, su, rows, N, N8, esz, stream) != hipSuccess) return LCONV_ERR_HIP;
         if (q && launch_pad_rows(q, sq, rows, N, N8, esz, stream) != hipSuccess) return LCONV_ERR_HIP;
         if (v && launch_pad_rows(v, sv, rows, N, N8, esz, stream) != hipSuccess) return LCONV_ERR_HIP;
-        const lconv_status_t r = fftconv_fwd_aligned(su, k_f, D, sy, sq, sv, B, H, N8, dtype, st + 4 * one, stream);
+        const lconv_status_t r = fftconv_fwd_aligned(su, k_f, D, sy, sq, sv, B, H, N8, dtype, st + 4 * one,
+                                                     chunk_target, may_build, stream);
         if (r != LCONV_SUCCESS) return r;
         return hip_status(launch_unpad_rows(sy, y, rows, N, N8, esz, stream));
     }
-    return fftconv_fwd_aligned(u, k_f, D, y, q, v, B, H, N, dtype, workspace, stream);
+    return fftconv_fwd_aligned(u, k_f, D, y, q, v, B, H, N, dtype, workspace, chunk_target, may_build, stream);
 }
 
-}  // extern "C"
+size_t fftconv_fwd_staging_bytes(int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype) {
+    int64_t rows;
+    if (!dtype_ok(dtype) || B < 0 || H < 0 || !n_in_range(N) || !mul_ok(B, H, &rows)) return 0;
+    return staging_bytes(rows, N, dtype, 4);
+}
+
+lconv_status_t prepare_tables(int64_t N, lconv_dtype_t dtype) {
+    if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
+    if (!n_in_range(N)) return LCONV_ERR_UNSUPPORTED;
+    Plan1D p;
+    make_plan_1d(round8(N), &p);
+    hipError_t err = hipSuccess;
+    if (!device_cu_count(&err)) return LCONV_ERR_HIP;
+    const int ct = dtype == LCONV_F32 ? CT_F32 : (int)dtype;
+    if (!fused_tables(p.R, ct, &err)) return LCONV_ERR_HIP;
+    if (p.multipass) {
+        ColTables ctab;
+        if (!col_tables(p.M, p.M1, &ctab, &err)) return LCONV_ERR_HIP;
+    }
+    return LCONV_SUCCESS;
+}
+
+}  // namespace lcv
 
 namespace {
 
+// every constant table the forward call needs for plan p is built on the current device
+bool tables_ready(const Plan1D& p, lconv_dtype_t dtype) {
+    hipError_t err = hipSuccess;
+    const int ct = dtype == LCONV_F32 ? CT_F32 : (int)dtype;
+    if (!fused_tables(p.R, ct, &err, false)) return false;
+    ColTables ctab;
+    return !p.multipass || col_tables(p.M, p.M1, &ctab, &err, false);
+}
+
 lconv_status_t fftconv_fwd_aligned(const void* u, const void* k_f, const void* D, void* y, const void* q,
                                    const void* v, int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype,
-                                   void* workspace, hipStream_t stream) {
+                                   void* workspace, size_t chunk_target, bool may_build, hipStream_t stream) {
     Plan1D p;
     make_plan_1d(N, &p);
+    if (!may_build && !tables_ready(p, dtype)) return LCONV_ERR_NOT_PREPARED;
     hipError_t err = hipSuccess;
     const int cus = device_cu_count(&err);
     if (!cus) return LCONV_ERR_HIP;
     const int ct = dtype == LCONV_F32 ? CT_F32 : (int)dtype;
-    const void* tabs = fused_tables(p.R, ct, &err);
+    const void* tabs = fused_tables(p.R, ct, &err, may_build);
     if (!tabs) return LCONV_ERR_HIP;
     const int64_t Bp = pairs_per_channel(B), seqs = Bp * H;
     if (!p.multipass) {
@@ -266,8 +330,8 @@ lconv_status_t fftconv_fwd_aligned(const void* u, const void* k_f, const void* D
         return hip_status(launch_fused1d(p.R, dtype, MODE_CONV, q != nullptr, v != nullptr, a, cus, stream));
     }
     ColTables ctab;
-    if (!col_tables(p.M, p.M1, &ctab, &err)) return LCONV_ERR_HIP;
-    const int64_t per = chunk_seqs(seqs, p.M, work_complex_size(dtype, false));
+    if (!col_tables(p.M, p.M1, &ctab, &err, may_build)) return LCONV_ERR_HIP;
+    const int64_t per = chunk_seqs(seqs, p.M, work_complex_size(dtype, false), chunk_target);
     for (int64_t s0 = 0; s0 < seqs; s0 += per) {
         const int64_t ns = per < seqs - s0 ? per : seqs - s0;
         ColArgs c{};

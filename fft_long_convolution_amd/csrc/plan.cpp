@@ -168,7 +168,8 @@ std::map<std::tuple<int, int, int, int64_t, int64_t>, DevBuf> g_cache;  // (dev,
 std::map<int, int> g_cu;
 
 const void* get_or_build(int kind, int ct, int64_t a, int64_t b,
-                         std::vector<uint8_t> (*build)(int, int, int64_t, int64_t), hipError_t* err) {
+                         std::vector<uint8_t> (*build)(int, int, int64_t, int64_t), hipError_t* err,
+                         bool may_build = true) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) { *err = e; return nullptr; }
@@ -176,6 +177,7 @@ const void* get_or_build(int kind, int ct, int64_t a, int64_t b,
     auto key = std::make_tuple(dev, kind, ct, a, b);
     auto it = g_cache.find(key);
     if (it != g_cache.end()) return it->second.ptr;
+    if (!may_build) { *err = hipErrorNotReady; return nullptr; }
     DevBuf buf;
     buf.host = build(kind, ct, a, b);
     e = hipMalloc(&buf.ptr, buf.host.size());
@@ -234,12 +236,12 @@ FusedTableLayout fused_table_layout(int R, int ct) {
     return L;
 }
 
-const void* fused_tables(int R, int ct, hipError_t* err) {
-    return get_or_build(0, ct, R, 0, build_any, err);
+const void* fused_tables(int R, int ct, hipError_t* err, bool build) {
+    return get_or_build(0, ct, R, 0, build_any, err, build);
 }
 
-bool col_tables(int64_t M, int64_t M1, ColTables* out, hipError_t* err) {
-    const void* p = get_or_build(1, 0, M, M1, build_any, err);
+bool col_tables(int64_t M, int64_t M1, ColTables* out, hipError_t* err, bool build) {
+    const void* p = get_or_build(1, 0, M, M1, build_any, err, build);
     if (!p) return false;
     const int64_t nlo = 2048, nhi = M / 2048 > 0 ? M / 2048 : 1;
     out->lo = (const float*)p;

@@ -37,8 +37,9 @@ struct FusedTableLayout {
 FusedTableLayout fused_table_layout(int R, int ct);
 
 // Device pointer to the fused-path tables for (R, ct) on the current device (built on first
-// use).  Returns nullptr and sets *err on failure.
-const void* fused_tables(int R, int ct, hipError_t* err);
+// use).  Returns nullptr and sets *err on failure.  With build = false a table that is not
+// built yet is not built (nullptr, *err = hipErrorNotReady): no allocation, no copy.
+const void* fused_tables(int R, int ct, hipError_t* err, bool build = true);
 
 // Column-pass twiddles for the multi-pass path, on the current device:
 //   w_lo[r] = exp(-2 pi i r / M) for r < 2048, w_hi[r] = exp(-2 pi i 2048 r / M) for r < M/2048,
@@ -48,7 +49,7 @@ struct ColTables {
     const float* hi;
     const float* col;
 };
-bool col_tables(int64_t M, int64_t M1, ColTables* out, hipError_t* err);
+bool col_tables(int64_t M, int64_t M1, ColTables* out, hipError_t* err, bool build = true);
 
 // exp(-2 pi i e / P) for e < P, fp32 complex, on the current device (3D path).
 const float* dft_table(int64_t P, hipError_t* err);

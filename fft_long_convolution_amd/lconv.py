@@ -22,7 +22,9 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "lconv.h")
 F32, F16, BF16 = 0, 1, 2
 STATUS = {0: "LCONV_SUCCESS", 1: "LCONV_ERR_NULL_POINTER", 2: "LCONV_ERR_INVALID_SHAPE",
           3: "LCONV_ERR_UNSUPPORTED", 4: "LCONV_ERR_MISALIGNED", 5: "LCONV_ERR_ALIASING",
-          6: "LCONV_ERR_WORKSPACE", 7: "LCONV_ERR_HIP"}
+          6: "LCONV_ERR_WORKSPACE", 7: "LCONV_ERR_HIP", 8: "LCONV_ERR_NOT_PREPARED",
+          9: "LCONV_ERR_SCRATCH_LIMIT"}
+NOALLOC_SCRATCH_BYTES = 64 << 20   # LCONV_NOALLOC_SCRATCH_BYTES
 
 
 class LconvError(RuntimeError):
@@ -68,6 +70,8 @@ def load(path: str = LIB_PATH):
         "lconv_filter_fft3d": (i, [vp, vp, i64, i64, i, vp, sz, vp]),
         "lconv_fftconv3d_fwd": (i, [vp, vp, vp, vp, i64, i64, i64, i, vp, sz, vp]),
         "lconv_fftconv2d_fwd": (i, [vp, vp, vp, vp, i64, i64, i64, i, vp]),
+        "lconv_prepare": (i, [i64, i]),
+        "lconv_fftconv_fwd_noalloc": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i, vp]),
         "lconv_status_string": (ctypes.c_char_p, [i]),
         "lconv_abi_version": (i, []),
         "lconv_release": (i, []),
@@ -112,6 +116,14 @@ def lconv_filter_fft(k, k_f, H, N, dtype, workspace, workspace_bytes, stream):
 def lconv_fftconv_fwd(u, k_f, D, y, q, v, B, H, N, dtype, workspace, workspace_bytes, stream):
     return load().lconv_fftconv_fwd(u, k_f, D, y, q, v, B, H, N, dtype, workspace,
                                     workspace_bytes, stream)
+
+
+def lconv_prepare(N, dtype):
+    return load().lconv_prepare(N, dtype)
+
+
+def lconv_fftconv_fwd_noalloc(u, k_f, D, y, q, v, B, H, N, dtype, stream):
+    return load().lconv_fftconv_fwd_noalloc(u, k_f, D, y, q, v, B, H, N, dtype, stream)
 
 
 def lconv_fftconv_bwd(dy, u, k_f, D, q, v, du, dq, dv, dk, dD, B, H, N, dtype, stream):

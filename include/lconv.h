@@ -48,8 +48,8 @@ extern "C" {
 
 /* Bumped when entry points are added or a size query's result changes (3: the training pair
  * lconv_fftconv_fwd_save / lconv_fftconv_bwd_saved; the state-space workspace holds the scan's
- * part states). */
-#define LCONV_ABI_VERSION 3
+ * part states.  4: lconv_prepare and lconv_fftconv_fwd_noalloc, two status codes). */
+#define LCONV_ABI_VERSION 4
 
 typedef enum { LCONV_F32 = 0, LCONV_F16 = 1, LCONV_BF16 = 2 } lconv_dtype_t;
 
@@ -61,7 +61,11 @@ typedef enum {
     LCONV_ERR_MISALIGNED = 4,    /* a pointer is not 16-byte aligned                        */
     LCONV_ERR_ALIASING = 5,      /* y overlaps an input                                     */
     LCONV_ERR_WORKSPACE = 6,     /* workspace NULL or smaller than the *_workspace_bytes    */
-    LCONV_ERR_HIP = 7            /* a HIP runtime call failed (including: no device)        */
+    LCONV_ERR_HIP = 7,           /* a HIP runtime call failed (including: no device)        */
+    LCONV_ERR_NOT_PREPARED = 8,  /* lconv_fftconv_fwd_noalloc: lconv_prepare was not called for
+                                    this device, length and dtype                          */
+    LCONV_ERR_SCRATCH_LIMIT = 9  /* lconv_fftconv_fwd_noalloc: the call needs more scratch than
+                                    LCONV_NOALLOC_SCRATCH_BYTES                            */
 } lconv_status_t;
 
 /* Largest supported sequence length (1D) and the only supported 2D side. */
@@ -295,6 +299,40 @@ lconv_status_t lconv_filter_fft3d(const void* k, void* k_f, int64_t C, int64_t S
 lconv_status_t lconv_fftconv3d_fwd(const void* u, const void* k_f, const void* D, void* y,
                                    int64_t B, int64_t C, int64_t S, lconv_dtype_t dtype,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- set-up, and the forward call for callers that cannot allocate ------------------------ */
+
+/*
+ * Builds, on the current device, every constant table lconv_fftconv_fwd uses for sequences of
+ * length N in `dtype` (DFT-block images, twiddles), and sets up the device's scratch buffer for
+ * lconv_fftconv_fwd_noalloc.  The other entry points build their tables on first use, which
+ * allocates device memory and uploads it with one blocking copy; calling this first moves that
+ * work here.  Synchronous; call it once per (device, N, dtype) before capturing or timing.
+ */
+lconv_status_t lconv_prepare(int64_t N, lconv_dtype_t dtype);
+
+/* Size of the library's static scratch buffer (one per GPU, held until the process ends). */
+#define LCONV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * For callers that cannot allocate device memory -- code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc: lconv_fftconv_fwd with its workspace taken from a
+ * library-owned static device buffer of LCONV_NOALLOC_SCRATCH_BYTES, so the call makes no
+ * allocation, no free and no host-to-device copy.  The caller still passes u, k_f, D, y, q, v.
+ *   * lconv_prepare(N, dtype) must have been called on the current device first
+ *     (LCONV_ERR_NOT_PREPARED otherwise; nothing is launched).
+ *   * The multi-pass path (N > 4096) runs in chunks that fit the buffer; a call that needs more
+ *     than it holds (staging for N not a multiple of 8 plus one sequence's transform) returns
+ *     LCONV_ERR_SCRATCH_LIMIT before any launch.  For N a multiple of 8 every supported length
+ *     fits.
+ *   * All calls on one GPU share its buffer, which keeps the last call's contents (no part of it
+ *     needs to start at zero): calls that overlap in time on one GPU (on different streams, or
+ *     from different threads without ordering) race and give wrong results.  Order them.
+ * Arguments, results and the other errors are those of lconv_fftconv_fwd.
+ */
+lconv_status_t lconv_fftconv_fwd_noalloc(const void* u, const void* k_f, const void* D, void* y,
+                                         const void* q, const void* v, int64_t B, int64_t H, int64_t N,
+                                         lconv_dtype_t dtype, hipStream_t stream);
 
 /* ---- misc ------------------------------------------------------------------------------- */
 

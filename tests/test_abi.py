@@ -7,7 +7,7 @@ import pytest
 from fft_long_convolution_amd import lconv
 
 F32, F16, BF16 = lconv.F32, lconv.F16, lconv.BF16
-OK, NULLP, SHAPE, UNSUP, MISAL, ALIAS, WSERR, HIPERR = range(8)
+OK, NULLP, SHAPE, UNSUP, MISAL, ALIAS, WSERR, HIPERR, NOTPREP, SCRATCH = range(10)
 
 # fake, 16-byte aligned "device" addresses: validation must reject before touching them
 A, Bq, C, Dd, Y, W = (0x100000 * (i + 1) for i in range(6))
@@ -27,8 +27,8 @@ def test_exports_every_header_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lconv.lconv_abi_version() == 3
-    for s in range(8):
+    assert lconv.lconv_abi_version() == 4
+    for s in range(10):
         assert lconv.status_string(s)
     assert "unknown" in lconv.status_string(99)
 
@@ -114,6 +114,16 @@ def test_no_device_gives_hip_error():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert fwd() == HIPERR
+    # the set-up call and the allocation-free forward call ask for the current device first
+    assert lconv.lconv_prepare(4096, BF16) == HIPERR
+    assert lconv.lconv_fftconv_fwd_noalloc(A, Bq, C, Y, None, None, 2, 3, 64, BF16, None) == HIPERR
+
+
+def test_noalloc_scratch_size():
+    assert lconv.NOALLOC_SCRATCH_BYTES == 64 << 20
+    # every supported length that is a multiple of 8 fits the scratch buffer with one sequence
+    # per chunk: the largest transform (M = 2^23) in fp32 is exactly 64 MiB
+    assert lconv.lconv_fftconv_workspace_bytes(1, 1, 2 ** 22, F32) == 64 << 20
 
 
 # more fake addresses for the gradient call (1 MiB apart, far larger than the test shapes)
