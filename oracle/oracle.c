@@ -20,13 +20,14 @@
  *                                                          (v = 1 when absent)
  *
  *  2D, non-causal.  "Native Multi-Dimensional Subquadratic Operators via Input Dependent Long
- *  Convolutions" (abstract) convolves images on their native grid with global kernels.  The
- *  kernel k[c] has S x S taps, tap (a,b) sitting at offset (a - S/2, b - S/2); the full
- *  linear convolution (size 2S-1) is cropped to the S x S window starting at (S/2, S/2):
+ *  Convolutions" (abstract) convolves images on their native grid with global kernels.  For
+ *  Hs x Ws images the kernel k[c] has Hs x Ws taps, tap (a,e) sitting at offset
+ *  (a - Hs/2, e - Ws/2) (halves rounded down); the full linear convolution is cropped to the
+ *  Hs x Ws window starting at (Hs/2, Ws/2):
  *
- *      y[b,c,i,j] = sum_{a,bb} k[c,a,bb] * u[b,c, i + S/2 - a, j + S/2 - bb] + D[c] * u[b,c,i,j]
+ *      y[b,c,i,j] = sum_{a,e} k[c,a,e] * u[b,c, i + Hs/2 - a, j + Ws/2 - e] + D[c] * u[b,c,i,j]
  *
- *  with u = 0 outside [0,S)^2.
+ *  with u = 0 outside [0,Hs) x [0,Ws).
  *
  * Inputs arrive in their storage dtype (fp32, fp16 or bf16 bit patterns) and are widened
  * exactly to double.  All sums run in ascending index order in double precision.
@@ -493,41 +494,44 @@ int oracle_conv1d_bwd_dk(const void* u, const void* q, const void* v, const void
 /* 2D: direct summation at single positions                                                    */
 /* ------------------------------------------------------------------------------------------ */
 
+/* Images of Hs x Ws with a kernel of the same size whose centre tap is (Hs/2, Ws/2), halves
+ * rounded down (the square S x S case has its centre at (S/2, S/2)):
+ *   y[b,c,i,j] = sum_{a,e} k[c,a,e] u[b,c, i + Hs/2 - a, j + Ws/2 - e] + D[c] u[b,c,i,j],
+ * summed with a outermost, then e, ascending; out-of-range input taps contribute 0. */
 static void* or_points2d_worker(void* arg) {
     or_job* J = (or_job*)arg;
-    const int64_t S = J->N, C = J->H, half = S / 2;
+    const int64_t Hs = J->N, Ws = J->L, C = J->H, hh = Hs / 2, hw = Ws / 2;
     for (int64_t r = J->lo; r < J->hi; ++r) {
         int64_t b = J->sel[4 * r], c = J->sel[4 * r + 1];
         int64_t i = J->sel[4 * r + 2], j = J->sel[4 * r + 3];
-        int64_t uoff = (b * C + c) * S * S, koff = c * S * S;
+        int64_t uoff = (b * C + c) * Hs * Ws, koff = c * Hs * Ws;
         double acc = 0;
-        for (int64_t a = 0; a < S; ++a) {
-            int64_t ii = i + half - a;
-            if (ii < 0 || ii >= S) continue;
-            for (int64_t bb = 0; bb < S; ++bb) {
-                int64_t jj = j + half - bb;
-                if (jj < 0 || jj >= S) continue;
-                acc += or_load(J->k, J->dt, koff + a * S + bb) *
-                       or_load(J->u, J->dt, uoff + ii * S + jj);
+        for (int64_t a = 0; a < Hs; ++a) {
+            int64_t ii = i + hh - a;
+            if (ii < 0 || ii >= Hs) continue;
+            for (int64_t e = 0; e < Ws; ++e) {
+                int64_t jj = j + hw - e;
+                if (jj < 0 || jj >= Ws) continue;
+                acc += or_load(J->k, J->dt, koff + a * Ws + e) *
+                       or_load(J->u, J->dt, uoff + ii * Ws + jj);
             }
         }
-        J->out[r] = acc + or_load(J->D, J->dt, c) * or_load(J->u, J->dt, uoff + i * S + j);
+        J->out[r] = acc + or_load(J->D, J->dt, c) * or_load(J->u, J->dt, uoff + i * Ws + j);
     }
     return NULL;
 }
 
-/* y[b,c,i,j] for each (b,c,i,j) in pts[4*npts]; u is [B][C][S][S], k is [C][S][S], D is [C]. */
 int oracle_conv2d_points(const void* u, const void* k, const void* D, int dt, int64_t B,
-                         int64_t C, int64_t S, const int64_t* pts, int64_t npts, double* out,
-                         int nthreads) {
+                         int64_t C, int64_t Hs, int64_t Ws, const int64_t* pts, int64_t npts,
+                         double* out, int nthreads) {
     if (!u || !k || !D || !out || (npts > 0 && !pts)) return -1;
-    if (B < 1 || C < 1 || S < 2 || (S % 2) || npts < 0 || dt < 0 || dt > 2) return -1;
+    if (B < 1 || C < 1 || Hs < 1 || Ws < 1 || npts < 0 || dt < 0 || dt > 2) return -1;
     for (int64_t r = 0; r < npts; ++r)
         if (pts[4 * r] < 0 || pts[4 * r] >= B || pts[4 * r + 1] < 0 || pts[4 * r + 1] >= C ||
-            pts[4 * r + 2] < 0 || pts[4 * r + 2] >= S || pts[4 * r + 3] < 0 ||
-            pts[4 * r + 3] >= S)
+            pts[4 * r + 2] < 0 || pts[4 * r + 2] >= Hs || pts[4 * r + 3] < 0 ||
+            pts[4 * r + 3] >= Ws)
             return -1;
-    or_job J = {u, NULL, NULL, k, D, dt, B, C, S, pts, out, 0, 0, 0};
+    or_job J = {u, NULL, NULL, k, D, dt, B, C, Hs, pts, out, 0, 0, Ws};
     or_parallel(or_points2d_worker, J, npts, nthreads);
     return 0;
 }

@@ -10,8 +10,9 @@ Definitions (restated from the pages; the derivation is in oracle.c's header):
   on the "RubiConv" page (causality from one-sided zero padding plus truncation):
       y[b,h,t] = v[b,h,t] * ( sum_{s<=t} k[h,t-s] x[b,h,s] + D[h] x[b,h,t] ),  x = q*u.
 * 2D linear (non-circular) convolution with a centred, full-size kernel -- "Native
-  Multi-Dimensional Subquadratic Operators via Input Dependent Long Convolutions" (abstract):
-      y[b,c,i,j] = sum_{a,bb} k[c,a,bb] u[b,c,i+S/2-a,j+S/2-bb] + D[c] u[b,c,i,j].
+  Multi-Dimensional Subquadratic Operators via Input Dependent Long Convolutions" (abstract),
+  for Hs x Ws images (halves rounded down):
+      y[b,c,i,j] = sum_{a,e} k[c,a,e] u[b,c,i+Hs/2-a,j+Ws/2-e] + D[c] u[b,c,i,j].
 
 Arrays are passed in their storage dtype: float32, float16, or bfloat16 carried as uint16 bit
 patterns (the caller says which via ``dt``).  The C code widens them exactly to float64.
@@ -54,7 +55,7 @@ def _load():
                                                 dp, ip]
         lib.oracle_conv1d_short_points.argtypes = [vp, vp, vp, vp, vp, ip, i64, i64, i64, i64, vp, i64,
                                                    dp, ip]
-        lib.oracle_conv2d_points.argtypes = [vp, vp, vp, ip, i64, i64, i64, vp, i64, dp, ip]
+        lib.oracle_conv2d_points.argtypes = [vp, vp, vp, ip, i64, i64, i64, i64, vp, i64, dp, ip]
         lib.oracle_conv3d_points.argtypes = [vp, vp, vp, ip, i64, i64, i64, vp, i64, dp, ip]
         lib.oracle_ssm_rows.argtypes = [vp, vp, vp, dp, dp, vp, ip, i64, i64, i64, i64, vp, i64, dp, ip]
         lib.oracle_widen.argtypes = [vp, ip, i64, dp]
@@ -255,15 +256,16 @@ def conv1d_bwd_dk(u, gy, chans, q=None, v=None, dt=None, nthreads=None):
 
 
 def conv2d_points(u, k, D, pts, dt=None, nthreads=None):
-    """Direct 2D sums y[b,c,i,j] for pts = [(b,c,i,j), ...]; returns float64 [len(pts)]."""
+    """Direct 2D sums y[b,c,i,j] for pts = [(b,c,i,j), ...] (u [B,C,Hs,Ws], k [C,Hs,Ws], centre
+    tap (Hs//2, Ws//2)); returns float64 [len(pts)]."""
     dt = _dt_of(u, dt)
     st = _storage(dt)
     u, k, D = (_c(a, st) for a in (u, k, D))
-    B, C, S, S2 = u.shape
-    assert S == S2 and k.shape == (C, S, S) and D.shape == (C,)
+    B, C, Hs, Ws = u.shape
+    assert k.shape == (C, Hs, Ws) and D.shape == (C,)
     pts = np.ascontiguousarray(np.asarray(pts, np.int64).reshape(-1, 4))
     out = np.empty(pts.shape[0], np.float64)
-    rc = _load().oracle_conv2d_points(_ptr(u), _ptr(k), _ptr(D), dt, B, C, S, _ptr(pts),
+    rc = _load().oracle_conv2d_points(_ptr(u), _ptr(k), _ptr(D), dt, B, C, Hs, Ws, _ptr(pts),
                                       pts.shape[0], out.ctypes.data, _threads(nthreads))
     if rc:
         raise ValueError("oracle_conv2d_points rejected its arguments")
@@ -334,30 +336,34 @@ def _dft_matrix(P: int, rows, cols, sign: int) -> np.ndarray:
 def conv2d_dft(u, k, D, images, dt=None, P=None):
     """Naive separable-DFT 2D oracle (independent of the direct sums).
 
-    For each image (b,c): zero pad u and k from S x S to P x P (P >= 2S-1, default 2S, so the
-    product of spectra is a *linear* convolution), multiply the 2D DFTs, invert only the
-    S x S window of rows/columns [S/2, S/2+S) and add D*u.  The DFTs are explicit matrices
-    applied with matmul; no FFT routine is involved.  Returns float64 [len(images), S, S].
+    For each image (b,c) of Hs x Ws: zero pad u and k to Ph x Pw (Ph >= 2Hs-1, Pw >= 2Ws-1,
+    default 2Hs x 2Ws, so the product of spectra is a *linear* convolution), multiply the 2D
+    DFTs, invert only the Hs x Ws window of rows [Hs/2, Hs/2+Hs) and columns [Ws/2, Ws/2+Ws)
+    (halves rounded down) and add D*u.  The DFTs are explicit matrices applied with matmul; no
+    FFT routine is involved.  P = (Ph, Pw) or one side for both.  Returns float64
+    [len(images), Hs, Ws].
     """
     dt = _dt_of(u, dt)
     uw = widen(u, dt)
     kw = widen(k, dt)
     Dw = widen(D, dt)
-    B, C, S, _ = uw.shape
-    P = P or 2 * S
-    assert P >= 2 * S - 1
-    F = _dft_matrix(P, range(P), range(S), -1)                 # [P, S]  forward, nonzero part
-    G = _dft_matrix(P, range(S // 2, S // 2 + S), range(P), +1)  # [S, P] inverse, crop rows
+    B, C, Hs, Ws = uw.shape
+    Ph, Pw = (P, P) if isinstance(P, int) else (P or (2 * Hs, 2 * Ws))
+    assert Ph >= 2 * Hs - 1 and Pw >= 2 * Ws - 1
+    Fh = _dft_matrix(Ph, range(Ph), range(Hs), -1)                        # [Ph, Hs] forward
+    Fw = _dft_matrix(Pw, range(Pw), range(Ws), -1)                        # [Pw, Ws]
+    Gh = _dft_matrix(Ph, range(Hs // 2, Hs // 2 + Hs), range(Ph), +1)     # [Hs, Ph] inverse, crop
+    Gw = _dft_matrix(Pw, range(Ws // 2, Ws // 2 + Ws), range(Pw), +1)     # [Ws, Pw]
     out = []
     kf_cache = {}
     for (b, c) in np.asarray(images, np.int64).reshape(-1, 2):
         b, c = int(b), int(c)
         if c not in kf_cache:
-            kf_cache[c] = F @ kw[c] @ F.T
-        U = F @ uw[b, c] @ F.T
-        Y = (G @ (U * kf_cache[c]) @ G.T) / (P * P)
+            kf_cache[c] = Fh @ kw[c] @ Fw.T
+        U = Fh @ uw[b, c] @ Fw.T
+        Y = (Gh @ (U * kf_cache[c]) @ Gw.T) / (Ph * Pw)
         out.append(Y.real + Dw[c] * uw[b, c])
-    return np.stack(out) if out else np.zeros((0, S, S))
+    return np.stack(out) if out else np.zeros((0, Hs, Ws))
 
 
 # --------------------------------------------------------------------------------------------

@@ -286,78 +286,96 @@ def test_rejects_bad_arguments():
 # 2D pins
 # --------------------------------------------------------------------------------------------
 
-def _img_all_points(B, C, S):
-    g = np.stack(np.meshgrid(np.arange(B), np.arange(C), np.arange(S), np.arange(S),
+def _img_all_points(B, C, Hs, Ws):
+    g = np.stack(np.meshgrid(np.arange(B), np.arange(C), np.arange(Hs), np.arange(Ws),
                              indexing="ij"), -1)
     return g.reshape(-1, 4)
 
 
 def _conv2d_direct_full(u, k, D):
-    B, C, S, _ = u.shape
-    return oracle.conv2d_points(u, k, D, _img_all_points(B, C, S)).reshape(B, C, S, S)
+    B, C, Hs, Ws = u.shape
+    return oracle.conv2d_points(u, k, D, _img_all_points(B, C, Hs, Ws)).reshape(B, C, Hs, Ws)
 
 
+# square, rectangular, odd sides (centre tap at the rounded-down half)
+SHAPES_2D = [(16, 16), (8, 24), (9, 16), (12, 7), (1, 8)]
+
+
+@pytest.mark.parametrize("Hs,Ws", SHAPES_2D)
 @pytest.mark.parametrize("which", ["direct", "dft"])
-def test_2d_delta_at_centre_is_identity_plus_skip(which):
-    S, B, C = 16, 2, 3
-    u = _f32(RNG.standard_normal((B, C, S, S)))
-    k = np.zeros((C, S, S), np.float32); k[:, S // 2, S // 2] = 1
+def test_2d_delta_at_centre_is_identity_plus_skip(which, Hs, Ws):
+    B, C = 2, 3
+    u = _f32(RNG.standard_normal((B, C, Hs, Ws)))
+    k = np.zeros((C, Hs, Ws), np.float32); k[:, Hs // 2, Ws // 2] = 1
     D = _f32(RNG.standard_normal(C))
     y = (_conv2d_direct_full(u, k, D) if which == "direct" else
-         oracle.conv2d_dft(u, k, D, [(b, c) for b in range(B) for c in range(C)]).reshape(B, C, S, S))
+         oracle.conv2d_dft(u, k, D, [(b, c) for b in range(B) for c in range(C)]).reshape(B, C, Hs, Ws))
     ref = u.astype(np.float64) * (1 + D.astype(np.float64))[None, :, None, None]
     tol = 0 if which == "direct" else 1e-12
     np.testing.assert_allclose(y, ref, rtol=tol, atol=tol)
 
 
+@pytest.mark.parametrize("Hs,Ws", SHAPES_2D)
 @pytest.mark.parametrize("which", ["direct", "dft"])
-def test_2d_shifted_delta_is_shifted_copy(which):
-    S, dx, dy = 16, 3, -2
-    u = _f32(RNG.standard_normal((1, 1, S, S)))
-    k = np.zeros((1, S, S), np.float32); k[0, S // 2 + dx, S // 2 + dy] = 1
+def test_2d_shifted_delta_is_shifted_copy(which, Hs, Ws):
+    dx, dy = min(3, Hs - 1 - Hs // 2), -min(2, Ws // 2)
+    u = _f32(RNG.standard_normal((1, 1, Hs, Ws)))
+    k = np.zeros((1, Hs, Ws), np.float32); k[0, Hs // 2 + dx, Ws // 2 + dy] = 1
     D = np.zeros(1, np.float32)
     if which == "direct":
         y = _conv2d_direct_full(u, k, D)[0, 0]
     else:
         y = oracle.conv2d_dft(u, k, D, [(0, 0)])[0]
-    ref = np.zeros((S, S))
-    for i in range(S):
-        for j in range(S):
+    ref = np.zeros((Hs, Ws))
+    for i in range(Hs):
+        for j in range(Ws):
             ii, jj = i - dx, j - dy
-            if 0 <= ii < S and 0 <= jj < S:
+            if 0 <= ii < Hs and 0 <= jj < Ws:
                 ref[i, j] = u[0, 0, ii, jj]
     np.testing.assert_allclose(y, ref, rtol=0, atol=1e-12)
 
 
-def test_2d_matches_scipy_convolve2d_crop():
-    S, B, C = 16, 2, 2
-    u = _f32(RNG.standard_normal((B, C, S, S)))
-    k = _f32(RNG.standard_normal((C, S, S)))
+@pytest.mark.parametrize("Hs,Ws", SHAPES_2D)
+def test_2d_matches_scipy_convolve2d_crop(Hs, Ws):
+    B, C = 2, 2
+    u = _f32(RNG.standard_normal((B, C, Hs, Ws)))
+    k = _f32(RNG.standard_normal((C, Hs, Ws)))
     D = _f32(RNG.standard_normal(C))
     yd = _conv2d_direct_full(u, k, D)
-    yf = oracle.conv2d_dft(u, k, D, [(b, c) for b in range(B) for c in range(C)]).reshape(B, C, S, S)
+    yf = oracle.conv2d_dft(u, k, D, [(b, c) for b in range(B) for c in range(C)]).reshape(B, C, Hs, Ws)
+    h, w = Hs // 2, Ws // 2
     for b in range(B):
         for c in range(C):
             full = scipy.signal.convolve2d(u[b, c].astype(np.float64), k[c].astype(np.float64),
                                            mode="full")
-            ref = full[S // 2:S // 2 + S, S // 2:S // 2 + S] + float(D[c]) * u[b, c].astype(np.float64)
+            ref = full[h:h + Hs, w:w + Ws] + float(D[c]) * u[b, c].astype(np.float64)
             np.testing.assert_allclose(yd[b, c], ref, rtol=1e-12, atol=1e-12)
             np.testing.assert_allclose(yf[b, c], ref, rtol=1e-12, atol=1e-12)
 
 
-def test_2d_separable_kernel_reduces_to_1d_centred_convs():
-    S = 16
-    u = _f32(RNG.standard_normal((1, 1, S, S)))
-    f = RNG.integers(-4, 5, S).astype(np.float32)
-    g = RNG.integers(-4, 5, S).astype(np.float32)
+@pytest.mark.parametrize("Hs,Ws", SHAPES_2D)
+def test_2d_separable_kernel_reduces_to_1d_centred_convs(Hs, Ws):
+    u = _f32(RNG.standard_normal((1, 1, Hs, Ws)))
+    f = RNG.integers(-4, 5, Hs).astype(np.float32)
+    g = RNG.integers(-4, 5, Ws).astype(np.float32)
     k = np.outer(f, g).astype(np.float32)[None]
     y = _conv2d_direct_full(u, k, np.zeros(1, np.float32))[0, 0]
-    # rows with g, then columns with f; each a centred 1D linear conv cropped at S/2
-    tmp = np.stack([np.convolve(r, g.astype(np.float64))[S // 2:S // 2 + S]
+    # rows with g, then columns with f; each a centred 1D linear conv cropped at the half
+    tmp = np.stack([np.convolve(r, g.astype(np.float64))[Ws // 2:Ws // 2 + Ws]
                     for r in u[0, 0].astype(np.float64)])
-    ref = np.stack([np.convolve(col, f.astype(np.float64))[S // 2:S // 2 + S]
+    ref = np.stack([np.convolve(col, f.astype(np.float64))[Hs // 2:Hs // 2 + Hs]
                     for col in tmp.T]).T
     np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_2d_dft_larger_padding_agrees():
+    """Any padding Ph >= 2Hs - 1, Pw >= 2Ws - 1 gives the same linear convolution."""
+    u = _f32(RNG.standard_normal((1, 2, 9, 12)))
+    k = _f32(RNG.standard_normal((2, 9, 12)))
+    D = _f32(RNG.standard_normal(2))
+    a = oracle.conv2d_dft(u, k, D, [(0, 0), (0, 1)])
+    b = oracle.conv2d_dft(u, k, D, [(0, 0), (0, 1)], P=(17, 30))
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
 
 
 def test_2d_dft_matches_direct_at_sampled_points_full_size():
