@@ -2,9 +2,16 @@
 //
 // "Native Multi-Dimensional Subquadratic Operators via Input Dependent Long Convolutions"
 // (abstract) applies global convolutions on the native 2D grid and fuses the FFT-convolution
-// path.  For S x S images and S x S kernels the linear convolution fits a P x P = 2S x 2S
-// transform (P >= 2S - 1, so nothing wraps around); the output is the S x S window starting at
-// (S/2, S/2) of the full convolution, i.e. the kernel's tap (S/2, S/2) is its centre.
+// path.  For Hs x Ws images (sides up to 128) and kernels of the same size the linear
+// convolution fits a 256 x 256 transform; the output is the Hs x Ws window starting at
+// (Hs/2, Ws/2) of the full convolution (halves rounded down), i.e. the kernel's tap
+// (Hs/2, Ws/2) is its centre.
+//
+// Placement in the 256 x 256 grid: the image sits at rows [0, Hs) and columns [0, Ws); the
+// kernel's tap (a, e) at (64 - Hs/2 + a, 64 - Ws/2 + e).  The full convolution then lies in
+// rows [64 - Hs/2, 62 + 2 Hs - Hs/2] (inside [0, 256): nothing wraps) and output (i, j) is grid
+// point (64 + i, 64 + j), so every shape reads the same window rows and columns 64 .. 191.  The
+// D skip is a delta at grid (64, 64).
 //
 // One workgroup handles two images of the same channel as one complex image (their spectra
 // multiply by the same real kernel's spectrum):
@@ -80,17 +87,25 @@ __global__ void __launch_bounds__(512) conv2d_kernel(const Conv2DArgs a) {
     // channel's 256 KB spectrum.
     const int64_t Bp = (a.B + 1) / 2, nitems = Bp * a.C, G = gridDim.x;
     const int64_t v = G % 8 == 0 ? (int64_t)(blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : (int64_t)blockIdx.x;
-    constexpr int64_t IMGSZ = (int64_t)S2D * S2D;
+    const int Hs = a.Hs, Ws = a.Ws;
+    const int64_t IMGSZ = (int64_t)Hs * Ws;
 
     // staged input chunk of this thread: row (tid / 16) of a 32-row quarter, elements 8*(tid%16)..
+    // (zero outside the Hs x Ws image)
     const int srow = tid >> 4, scol = 8 * (tid & 15);
     uint4 pre0, pre1;  // u of image b and b+1 (next chunk)
     auto issue = [&](int64_t item, int q) LCV_INLINE {
         const int64_t ch = item / Bp, b = 2 * (item % Bp);
-        const int64_t base0 = (b * a.C + ch) * IMGSZ + (int64_t)(32 * q + srow) * S2D + scol;
-        const int64_t base1 = b + 1 < a.B ? base0 + a.C * IMGSZ : base0;
-        pre0 = *(const uint4*)((const uint16_t*)a.u + base0);
-        pre1 = *(const uint4*)((const uint16_t*)a.u + base1);
+        const int row = 32 * q + srow;
+        if (row < Hs && scol < Ws) {
+            const int64_t base0 = (b * a.C + ch) * IMGSZ + (int64_t)row * Ws + scol;
+            const int64_t base1 = b + 1 < a.B ? base0 + a.C * IMGSZ : base0;
+            pre0 = *(const uint4*)((const uint16_t*)a.u + base0);
+            pre1 = *(const uint4*)((const uint16_t*)a.u + base1);
+        } else {
+            pre0 = make_uint4(0u, 0u, 0u, 0u);
+            pre1 = pre0;
+        }
     };
     if (v < nitems) issue(v, 0);
 
@@ -274,10 +289,11 @@ __global__ void __launch_bounds__(512) conv2d_kernel(const Conv2DArgs a) {
         if (a.y) {
             for (int rr = 0; rr < S2D; rr += 32) {
                 const int r = rr + srow;
+                if (r >= Hs || scol >= Ws) continue;
                 uint32_t w[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) w[i] = BUF[r * RS + scol + i];
-                const int64_t o0 = (b * a.C + ch) * IMGSZ + (int64_t)r * S2D + scol;
+                const int64_t o0 = (b * a.C + ch) * IMGSZ + (int64_t)r * Ws + scol;
                 uint4 y0, y1;
                 y0.x = __byte_perm(w[0], w[1], 0x5410); y0.y = __byte_perm(w[2], w[3], 0x5410);
                 y0.z = __byte_perm(w[4], w[5], 0x5410); y0.w = __byte_perm(w[6], w[7], 0x5410);
@@ -291,28 +307,30 @@ __global__ void __launch_bounds__(512) conv2d_kernel(const Conv2DArgs a) {
     }
 }
 
-// 2D filter spectrum: K[u][v] = sum_{a,b} k[a][b] w^(u a + v b) / P^2 (w = exp(-2 pi i / 256)),
+// 2D filter spectrum of the kernel placed at grid rows 64 - Hs/2 + a, columns 64 - Ws/2 + e:
+// K[u][v] = sum_{a,e} k[a][e] w^(u (a + dr) + v (e + dc)) / P^2 (w = exp(-2 pi i / 256)),
 // computed as two explicit DFT-matrix passes in fp32 (one-off, not on the convolution path),
 // stored in the order the column stage reads it: [channel][v][lane][jj], u = lane%16 +
 // 16 (4 (lane/16) + jj).
 template <int IO>
-__global__ void __launch_bounds__(256) filter2d_kernel(const void* k, void* kf, float inv_p2) {
+__global__ void __launch_bounds__(256) filter2d_kernel(const void* k, void* kf, float inv_p2, int Hs, int Ws) {
     __shared__ float2 T[S2D][32];
     __shared__ float2 W[P2D];
     const int ch = blockIdx.x, vb = blockIdx.y, tid = threadIdx.x;
+    const int dr = 64 - Hs / 2, dc = 64 - Ws / 2;
     for (int e = tid; e < P2D; e += blockDim.x) {
         double s, cc;
         sincospi(-2.0 * e / P2D, &s, &cc);
         W[e] = make_float2((float)cc, (float)s);
     }
     __syncthreads();
-    const uint16_t* kc = (const uint16_t*)k + (int64_t)ch * S2D * S2D;
-    for (int idx = tid; idx < S2D * 32; idx += blockDim.x) {
+    const uint16_t* kc = (const uint16_t*)k + (int64_t)ch * Hs * Ws;
+    for (int idx = tid; idx < Hs * 32; idx += blockDim.x) {
         const int ar = idx / 32, vv = idx % 32, v = 32 * vb + vv;
         float re = 0.f, im = 0.f;
-        for (int bb = 0; bb < S2D; ++bb) {
-            const float x = unpack_lo<IO>(kc[ar * S2D + bb]);
-            const float2 w = W[(v * bb) & (P2D - 1)];
+        for (int e = 0; e < Ws; ++e) {
+            const float x = unpack_lo<IO>(kc[ar * Ws + e]);
+            const float2 w = W[(v * (e + dc)) & (P2D - 1)];
             re += x * w.x;
             im += x * w.y;
         }
@@ -322,8 +340,8 @@ __global__ void __launch_bounds__(256) filter2d_kernel(const void* k, void* kf, 
     for (int idx = tid; idx < P2D * 32; idx += blockDim.x) {
         const int vv = idx / P2D, u = idx % P2D, v = 32 * vb + vv;
         float re = 0.f, im = 0.f;
-        for (int ar = 0; ar < S2D; ++ar) {
-            const float2 t = T[ar][vv], w = W[(u * ar) & (P2D - 1)];
+        for (int ar = 0; ar < Hs; ++ar) {
+            const float2 t = T[ar][vv], w = W[(u * (ar + dr)) & (P2D - 1)];
             re += t.x * w.x - t.y * w.y;
             im += t.x * w.y + t.y * w.x;
         }
@@ -335,8 +353,10 @@ __global__ void __launch_bounds__(256) filter2d_kernel(const void* k, void* kf, 
 hipError_t launch_conv2d(int dtype, const Conv2DArgs& a, hipStream_t st) {
     if (a.filter) {
         dim3 grid((unsigned)a.C, P2D / 32);
-        if (dtype == CT_F16) hipLaunchKernelGGL((filter2d_kernel<CT_F16>), grid, dim3(256), 0, st, a.u, (void*)a.kf, a.inv_p2);
-        else hipLaunchKernelGGL((filter2d_kernel<CT_BF16>), grid, dim3(256), 0, st, a.u, (void*)a.kf, a.inv_p2);
+        if (dtype == CT_F16)
+            hipLaunchKernelGGL((filter2d_kernel<CT_F16>), grid, dim3(256), 0, st, a.u, (void*)a.kf, a.inv_p2, a.Hs, a.Ws);
+        else
+            hipLaunchKernelGGL((filter2d_kernel<CT_BF16>), grid, dim3(256), 0, st, a.u, (void*)a.kf, a.inv_p2, a.Hs, a.Ws);
         return hipGetLastError();
     }
     const int64_t nitems = (a.B + 1) / 2 * a.C;

@@ -92,12 +92,13 @@ hipError_t launch_col_fwd(int dtype, const ColArgs& a, hipStream_t stream);
 hipError_t launch_col_inv(int dtype, const ColArgs& a, hipStream_t stream);
 
 struct Conv2DArgs {
-    const void* u;       // [B][C][S][S]
+    const void* u;       // [B][C][Hs][Ws]
     const void* kf;      // 2D spectrum (transform order)
     const void* D;       // [C]
-    void* y;             // [B][C][S][S]
+    void* y;             // [B][C][Hs][Ws]
     const void* tables;
     int64_t B, C;
+    int Hs, Ws;          // image sides: 1 <= Hs <= 128, 8 <= Ws <= 128 with Ws a multiple of 8
     float inv_p2;        // 1 / (2S)^2
     int filter;          // 1: u = k [C][S][S]; the spectrum is written to kf
     int cus;             // compute units (persistent grid size)
@@ -133,6 +134,22 @@ struct SsmArgs {
 hipError_t launch_ssm_prepare(int dtype, const float* lam, const float* W, const SsmArgs& a,
                               hipStream_t stream);
 hipError_t launch_ssm_state(int dtype, const SsmArgs& a, bool gq, bool gv, hipStream_t stream);
+
+// Row reversals for the gradients of long sequences (stage.hip), rows of N (a multiple of 8)
+// elements of type dtype:
+//   out = rev(a (.) b)                          (b nullable)
+//   d1 = g1 (.) rev(t),  d2 = g2 (.) rev(t)      (g1 nullable: d1 = rev(t); d2 nullable: skipped)
+//   dk[h][t] = sum_b r[b][h][N-1-t] (fp32), dD[h] = dk[h][0]   (either nullable)
+hipError_t launch_rev_gate(const void* a, const void* b, void* out, int64_t rows, int64_t N, int dtype,
+                           hipStream_t stream);
+hipError_t launch_rev_gated_out(const void* t, const void* g1, const void* g2, void* d1, void* d2, int64_t rows,
+                                int64_t N, int dtype, hipStream_t stream);
+hipError_t launch_rev_batch_sum(const void* r, float* dk, float* dD, int64_t B, int64_t H, int64_t N, int dtype,
+                                hipStream_t stream);
+
+// Zero n 32-bit words (stage.hip): a kernel, so that callers under graph capture record no
+// memset node.
+hipError_t launch_zero_words(void* p, int64_t n, hipStream_t stream);
 
 // Row staging for N not a multiple of 8 (stage.hip): [rows][N] <-> [rows][N8] with a zero tail.
 hipError_t launch_pad_rows(const void* src, void* dst, int64_t rows, int64_t N, int64_t N8, int esize,

@@ -47,6 +47,12 @@ size_t staging_bytes(int64_t rows, int64_t N, lconv_dtype_t dt, int tensors) {
     return (size_t)tensors * round256((size_t)rows * (size_t)round8(N) * dtype_size(dt));
 }
 
+// 2D sides the fused kernel takes: rows 1..128, columns 8..128 in whole 16-byte groups
+constexpr int64_t kP2D = 256;
+bool sides2d_ok(int64_t Hs, int64_t Ws) {
+    return Hs >= 1 && Hs <= LCONV_2D_MAX_SIDE && Ws >= 8 && Ws <= LCONV_2D_MAX_SIDE && Ws % 8 == 0;
+}
+
 // sequences = complex transforms: pairs of batch rows per channel
 int64_t pairs_per_channel(int64_t B) { return (B + 1) / 2; }
 
@@ -128,12 +134,17 @@ size_t lconv_fftconv_workspace_bytes(int64_t B, int64_t H, int64_t N, lconv_dtyp
     return w == SIZE_MAX ? 0 : w;
 }
 
-size_t lconv_filter_fft2d_bytes(int64_t C, int64_t S, lconv_dtype_t dtype) {
+size_t lconv_filter_fft2d_bytes(int64_t C, int64_t Hs, int64_t Ws, lconv_dtype_t dtype) {
     int64_t t;
-    if (!dtype_ok(dtype) || dtype == LCONV_F32 || C < 0 || S != LCONV_2D_SIDE) return 0;
-    // spectrum of the (2S x 2S) transform in the 2D kernel's order, complex in dtype
-    if (!mul_ok(C, 4 * S * S, &t) || !mul_ok(t, 2 * (int64_t)dtype_size(dtype), &t)) return 0;
+    if (!dtype_ok(dtype) || C < 0 || !sides2d_ok(Hs, Ws) || dtype == LCONV_F32) return 0;
+    // spectrum of the 256 x 256 transform in the 2D kernel's order, complex in dtype
+    if (!mul_ok(C, (int64_t)kP2D * kP2D, &t) || !mul_ok(t, 2 * (int64_t)dtype_size(dtype), &t)) return 0;
     return (size_t)t;
+}
+
+size_t lconv_fftconv2d_workspace_bytes(int64_t B, int64_t C, int64_t Hs, int64_t Ws, lconv_dtype_t dtype) {
+    (void)B; (void)C; (void)Hs; (void)Ws; (void)dtype;
+    return 0;  // one fused kernel per image pair: the intermediate stays in LDS
 }
 
 lconv_status_t lconv_filter_fft(const void* k, void* k_f, int64_t H, int64_t N, lconv_dtype_t dtype,
@@ -490,8 +501,9 @@ lconv_status_t bwd_impl(const void* dy, const void* u, const void* k_f, const vo
     if (!v) dv = nullptr;
     if (B == 0) {          // empty batch: the filter gradients are zero sums
         if ((dk && !aligned16(dk)) || (dD && !aligned16(dD))) return LCONV_ERR_MISALIGNED;
-        if (dk && hipMemsetAsync(dk, 0, (size_t)hn * 4, stream) != hipSuccess) return LCONV_ERR_HIP;
-        if (dD && hipMemsetAsync(dD, 0, (size_t)H * 4, stream) != hipSuccess) return LCONV_ERR_HIP;
+        // a fill kernel, not a memset node: the call stays safe to capture in a graph
+        if (dk && launch_zero_words(dk, hn, stream) != hipSuccess) return LCONV_ERR_HIP;
+        if (dD && launch_zero_words(dD, H, stream) != hipSuccess) return LCONV_ERR_HIP;
         return LCONV_SUCCESS;
     }
     if (!dy || !u || !k_f || !D || !du || (q && !dq) || (v && !dv)) return LCONV_ERR_NULL_POINTER;
@@ -606,34 +618,39 @@ lconv_status_t lconv_fftconv_fwd_save(const void* u, const void* k_f, const void
     return hip_status(launch_fused1d(p.R, dtype, MODE_SAVE, q != nullptr, v != nullptr, a, cus, stream));
 }
 
-lconv_status_t lconv_filter_fft2d(const void* k, void* k_f, int64_t C, int64_t S, lconv_dtype_t dtype,
+lconv_status_t lconv_filter_fft2d(const void* k, void* k_f, int64_t C, int64_t Hs, int64_t Ws, lconv_dtype_t dtype,
                                   hipStream_t stream) {
     if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
-    if (C < 0 || S < 0) return LCONV_ERR_INVALID_SHAPE;
+    if (C < 0 || Hs < 0 || Ws < 0) return LCONV_ERR_INVALID_SHAPE;
     if (C == 0) return LCONV_SUCCESS;
-    if (S != LCONV_2D_SIDE || dtype == LCONV_F32) return LCONV_ERR_UNSUPPORTED;
+    if (!sides2d_ok(Hs, Ws) || dtype == LCONV_F32) return LCONV_ERR_UNSUPPORTED;
     if (!k || !k_f) return LCONV_ERR_NULL_POINTER;
     if (!aligned16(k) || !aligned16(k_f)) return LCONV_ERR_MISALIGNED;
-    const size_t kf_bytes = lconv_filter_fft2d_bytes(C, S, dtype);
-    if (overlap(k_f, kf_bytes, k, (size_t)(C * S * S) * dtype_size(dtype))) return LCONV_ERR_ALIASING;
+    const size_t kf_bytes = lconv_filter_fft2d_bytes(C, Hs, Ws, dtype);
+    if (kf_bytes == 0) return LCONV_ERR_INVALID_SHAPE;
+    if (overlap(k_f, kf_bytes, k, (size_t)(C * Hs * Ws) * dtype_size(dtype))) return LCONV_ERR_ALIASING;
     Conv2DArgs a{};
     a.u = k; a.kf = k_f; a.C = C; a.B = 1; a.filter = 1;
-    a.inv_p2 = 1.0f / (float)(4 * S * S);
+    a.Hs = (int)Hs; a.Ws = (int)Ws;
+    a.inv_p2 = 1.0f / (float)(kP2D * kP2D);
     return hip_status(launch_conv2d(dtype, a, stream));
 }
 
 lconv_status_t lconv_fftconv2d_fwd(const void* u, const void* k_f, const void* D, void* y, int64_t B, int64_t C,
-                                   int64_t S, lconv_dtype_t dtype, hipStream_t stream) {
+                                   int64_t Hs, int64_t Ws, lconv_dtype_t dtype, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+    (void)workspace; (void)workspace_bytes;  // lconv_fftconv2d_workspace_bytes is 0: nothing to check
     if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
-    if (B < 0 || C < 0 || S < 0) return LCONV_ERR_INVALID_SHAPE;
+    if (B < 0 || C < 0 || Hs < 0 || Ws < 0) return LCONV_ERR_INVALID_SHAPE;
     int64_t elems, t;
-    if (!mul_ok(B, C, &t) || !mul_ok(t, S * S, &elems)) return LCONV_ERR_INVALID_SHAPE;
+    if (!mul_ok(B, C, &t) || !mul_ok(Hs, Ws, &elems) || !mul_ok(t, elems, &elems) || !mul_ok(elems, 8, &t))
+        return LCONV_ERR_INVALID_SHAPE;
     if (B == 0 || C == 0) return LCONV_SUCCESS;
-    if (S != LCONV_2D_SIDE || dtype == LCONV_F32) return LCONV_ERR_UNSUPPORTED;
+    if (!sides2d_ok(Hs, Ws) || dtype == LCONV_F32) return LCONV_ERR_UNSUPPORTED;
     if (!u || !k_f || !D || !y) return LCONV_ERR_NULL_POINTER;
     if (!aligned16(u) || !aligned16(k_f) || !aligned16(D) || !aligned16(y)) return LCONV_ERR_MISALIGNED;
     const size_t es = dtype_size(dtype), act = (size_t)elems * es;
-    if (overlap(y, act, u, act) || overlap(y, act, k_f, lconv_filter_fft2d_bytes(C, S, dtype)) ||
+    if (overlap(y, act, u, act) || overlap(y, act, k_f, lconv_filter_fft2d_bytes(C, Hs, Ws, dtype)) ||
         overlap(y, act, D, (size_t)C * es))
         return LCONV_ERR_ALIASING;
     hipError_t err = hipSuccess;
@@ -644,7 +661,8 @@ lconv_status_t lconv_fftconv2d_fwd(const void* u, const void* k_f, const void* D
     Conv2DArgs a{};
     a.u = u; a.kf = k_f; a.D = D; a.y = y; a.tables = tabs;
     a.B = B; a.C = C; a.filter = 0; a.cus = cus;
-    a.inv_p2 = 1.0f / (float)(4 * S * S);
+    a.Hs = (int)Hs; a.Ws = (int)Ws;
+    a.inv_p2 = 1.0f / (float)(kP2D * kP2D);
     return hip_status(launch_conv2d(dtype, a, stream));
 }
 

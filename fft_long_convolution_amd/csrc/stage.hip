@@ -4,7 +4,7 @@
 // causal convolution's first N outputs do not depend on inputs or taps past N, so the zero tail
 // changes nothing.  Elements are copied as raw 2- or 4-byte words (zero bits are 0.0 in every
 // supported type).  Also the elementwise product that gives the v-gradient from a saved
-// pre-gate output.
+// pre-gate output, and a zero fill.
 #include "coldft.h"
 #include "kernels.h"
 
@@ -48,7 +48,132 @@ __global__ void __launch_bounds__(256) mul_rows_kernel(const void* a, const void
     }
 }
 
+// Time reversal within rows, for the gradients of long sequences: the correlation sums of the
+// gradient are causal convolutions of reversed rows (dx = rev(k * rev(ds)), and
+// dk[t] = (x * rev(ds))[N-1-t]).  Rows are [rows][N] with N a multiple of 8; thread g handles
+// the 8-element group g of the output, whose sources are the mirrored group, reversed.
+
+// out = rev(a (.) b)   (b optional)
+template <int IO>
+__global__ void __launch_bounds__(256) rev_gate_kernel(const void* a, const void* b, void* out, int64_t rows,
+                                                       int64_t N) {
+    const int64_t gpr = N / 8, total = rows * gpr;
+    for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < total; g += (int64_t)gridDim.x * 256) {
+        const int64_t r = g / gpr, j = g - r * gpr, src = r * N + 8 * (gpr - 1 - j);
+        float x[8], w[8], o[8];
+        ld8<IO>(a, src, x);
+        if (b) {
+            ld8<IO>(b, src, w);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] *= w[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = x[7 - i];
+        st8<IO>(out, r * N + 8 * j, o);
+    }
+}
+
+// d1 = g1 (.) rev(t), d2 = g2 (.) rev(t)   (g1 optional: d1 = rev(t); d2 only when set)
+template <int IO>
+__global__ void __launch_bounds__(256) rev_gated_out_kernel(const void* t, const void* g1, const void* g2, void* d1,
+                                                            void* d2, int64_t rows, int64_t N) {
+    const int64_t gpr = N / 8, total = rows * gpr;
+    for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < total; g += (int64_t)gridDim.x * 256) {
+        const int64_t r = g / gpr, j = g - r * gpr, dst = r * N + 8 * j;
+        float x[8], rt[8], w[8];
+        ld8<IO>(t, r * N + 8 * (gpr - 1 - j), x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rt[i] = x[7 - i];
+        if (d2) {
+            ld8<IO>(g2, dst, w);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w[i] *= rt[i];
+            st8<IO>(d2, dst, w);
+        }
+        if (g1) {
+            ld8<IO>(g1, dst, w);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) rt[i] *= w[i];
+        }
+        st8<IO>(d1, dst, rt);
+    }
+}
+
+// dk[h][t] = sum_b r[b][h][N-1-t] (fp32, ascending b), dD[h] = dk[h][0]   (either may be null)
+template <int IO>
+__global__ void __launch_bounds__(256) rev_batch_sum_kernel(const void* rr, float* dk, float* dD, int64_t B,
+                                                            int64_t H, int64_t N) {
+    const int64_t gpr = N / 8, total = H * gpr;
+    for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < total; g += (int64_t)gridDim.x * 256) {
+        const int64_t h = g / gpr, j = g - h * gpr;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int64_t b = 0; b < B; ++b) {
+            float x[8];
+            ld8<IO>(rr, (b * H + h) * N + 8 * (gpr - 1 - j), x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += x[7 - i];
+        }
+        if (dk) {
+            float4* o = (float4*)(dk + h * N + 8 * j);
+            o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        }
+        if (dD && j == 0) dD[h] = acc[0];
+    }
+}
+
+__global__ void __launch_bounds__(256) zero_words_kernel(uint32_t* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+
 }  // namespace
+
+unsigned grid_groups(int64_t groups) {
+    const int64_t b = (groups + 255) / 256;
+    return (unsigned)(b < 8192 ? (b > 0 ? b : 1) : 8192);
+}
+
+hipError_t launch_rev_gate(const void* a, const void* b, void* out, int64_t rows, int64_t N, int dtype,
+                           hipStream_t st) {
+    if (rows <= 0 || N <= 0) return hipSuccess;
+    if (N % 8 != 0) return hipErrorInvalidValue;
+    const dim3 grid(grid_groups(rows * (N / 8)));
+    if (dtype == CT_F32) hipLaunchKernelGGL(rev_gate_kernel<CT_F32>, grid, dim3(256), 0, st, a, b, out, rows, N);
+    else if (dtype == CT_F16) hipLaunchKernelGGL(rev_gate_kernel<CT_F16>, grid, dim3(256), 0, st, a, b, out, rows, N);
+    else hipLaunchKernelGGL(rev_gate_kernel<CT_BF16>, grid, dim3(256), 0, st, a, b, out, rows, N);
+    return hipGetLastError();
+}
+
+hipError_t launch_rev_gated_out(const void* t, const void* g1, const void* g2, void* d1, void* d2, int64_t rows,
+                                int64_t N, int dtype, hipStream_t st) {
+    if (rows <= 0 || N <= 0) return hipSuccess;
+    if (N % 8 != 0) return hipErrorInvalidValue;
+    const dim3 grid(grid_groups(rows * (N / 8)));
+    if (dtype == CT_F32)
+        hipLaunchKernelGGL(rev_gated_out_kernel<CT_F32>, grid, dim3(256), 0, st, t, g1, g2, d1, d2, rows, N);
+    else if (dtype == CT_F16)
+        hipLaunchKernelGGL(rev_gated_out_kernel<CT_F16>, grid, dim3(256), 0, st, t, g1, g2, d1, d2, rows, N);
+    else
+        hipLaunchKernelGGL(rev_gated_out_kernel<CT_BF16>, grid, dim3(256), 0, st, t, g1, g2, d1, d2, rows, N);
+    return hipGetLastError();
+}
+
+hipError_t launch_rev_batch_sum(const void* r, float* dk, float* dD, int64_t B, int64_t H, int64_t N, int dtype,
+                                hipStream_t st) {
+    if (H <= 0 || N <= 0) return hipSuccess;
+    if (N % 8 != 0) return hipErrorInvalidValue;
+    const dim3 grid(grid_groups(H * (N / 8)));
+    if (dtype == CT_F32) hipLaunchKernelGGL(rev_batch_sum_kernel<CT_F32>, grid, dim3(256), 0, st, r, dk, dD, B, H, N);
+    else if (dtype == CT_F16) hipLaunchKernelGGL(rev_batch_sum_kernel<CT_F16>, grid, dim3(256), 0, st, r, dk, dD, B, H, N);
+    else hipLaunchKernelGGL(rev_batch_sum_kernel<CT_BF16>, grid, dim3(256), 0, st, r, dk, dD, B, H, N);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_words(void* p, int64_t n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_words_kernel, dim3(grid_for(n)), dim3(256), 0, st, (uint32_t*)p, n);
+    return hipGetLastError();
+}
 
 hipError_t launch_mul_rows(const void* dy, const void* c, void* y, int64_t n, int dtype, hipStream_t st) {
     if (n <= 0) return hipSuccess;

@@ -50,7 +50,8 @@ def load(path: str = LIB_PATH):
         "lconv_filter_fft_bytes": (sz, [i64, i64, i]),
         "lconv_filter_fft_workspace_bytes": (sz, [i64, i64, i]),
         "lconv_fftconv_workspace_bytes": (sz, [i64, i64, i64, i]),
-        "lconv_filter_fft2d_bytes": (sz, [i64, i64, i]),
+        "lconv_filter_fft2d_bytes": (sz, [i64, i64, i64, i]),
+        "lconv_fftconv2d_workspace_bytes": (sz, [i64, i64, i64, i64, i]),
         "lconv_filter_fft": (i, [vp, vp, i64, i64, i, vp, sz, vp]),
         "lconv_fftconv_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i, vp, sz, vp]),
         "lconv_fftconv_bwd": (i, [vp] * 11 + [i64, i64, i64, i, vp]),
@@ -59,7 +60,7 @@ def load(path: str = LIB_PATH):
         "lconv_fftconv_partial_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i, vp]),
         "lconv_fftconv_sparse_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_uint32, i, vp]),
         "lconv_freq_blocks": (i, [i64]),
-        "lconv_filter_fft2d": (i, [vp, vp, i64, i64, i, vp]),
+        "lconv_filter_fft2d": (i, [vp, vp, i64, i64, i64, i, vp]),
         "lconv_ssm_prep_bytes": (sz, [i64, i64, i64, i]),
         "lconv_ssm_prepare": (i, [vp, vp, vp, i64, i64, i64, i, vp]),
         "lconv_fftconv_ssm_workspace_bytes": (sz, [i64, i64, i64, i64, i64]),
@@ -69,7 +70,7 @@ def load(path: str = LIB_PATH):
         "lconv_fftconv3d_workspace_bytes": (sz, [i64, i64, i64, i]),
         "lconv_filter_fft3d": (i, [vp, vp, i64, i64, i, vp, sz, vp]),
         "lconv_fftconv3d_fwd": (i, [vp, vp, vp, vp, i64, i64, i64, i, vp, sz, vp]),
-        "lconv_fftconv2d_fwd": (i, [vp, vp, vp, vp, i64, i64, i64, i, vp]),
+        "lconv_fftconv2d_fwd": (i, [vp, vp, vp, vp, i64, i64, i64, i64, i, vp, sz, vp]),
         "lconv_prepare": (i, [i64, i]),
         "lconv_fftconv_fwd_noalloc": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i, vp]),
         "lconv_status_string": (ctypes.c_char_p, [i]),
@@ -105,8 +106,12 @@ def lconv_fftconv_workspace_bytes(B, H, N, dtype):
     return load().lconv_fftconv_workspace_bytes(B, H, N, dtype)
 
 
-def lconv_filter_fft2d_bytes(C, S, dtype):
-    return load().lconv_filter_fft2d_bytes(C, S, dtype)
+def lconv_filter_fft2d_bytes(C, Hs, Ws, dtype):
+    return load().lconv_filter_fft2d_bytes(C, Hs, Ws, dtype)
+
+
+def lconv_fftconv2d_workspace_bytes(B, C, Hs, Ws, dtype):
+    return load().lconv_fftconv2d_workspace_bytes(B, C, Hs, Ws, dtype)
 
 
 def lconv_filter_fft(k, k_f, H, N, dtype, workspace, workspace_bytes, stream):
@@ -150,12 +155,12 @@ def lconv_freq_blocks(N):
     return load().lconv_freq_blocks(N)
 
 
-def lconv_filter_fft2d(k, k_f, C, S, dtype, stream):
-    return load().lconv_filter_fft2d(k, k_f, C, S, dtype, stream)
+def lconv_filter_fft2d(k, k_f, C, Hs, Ws, dtype, stream):
+    return load().lconv_filter_fft2d(k, k_f, C, Hs, Ws, dtype, stream)
 
 
-def lconv_fftconv2d_fwd(u, k_f, D, y, B, C, S, dtype, stream):
-    return load().lconv_fftconv2d_fwd(u, k_f, D, y, B, C, S, dtype, stream)
+def lconv_fftconv2d_fwd(u, k_f, D, y, B, C, Hs, Ws, dtype, workspace, workspace_bytes, stream):
+    return load().lconv_fftconv2d_fwd(u, k_f, D, y, B, C, Hs, Ws, dtype, workspace, workspace_bytes, stream)
 
 
 def lconv_ssm_prep_bytes(H, NS, T, dtype):
@@ -238,9 +243,69 @@ def _check(status, where):
         raise LconvError(status, where)
 
 
+def _need(name, t, shape, dtype, optional=False):
+    """Host-side checks the C ABI cannot make on a torch tensor: the dtype, the shape and a dense
+    layout (the kernels read memory as contiguous rows, so a transposed or strided view would be
+    read wrongly, not rejected).  The device is checked by _on_gpu once every operand passed."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (a strided or transposed view would be read as dense rows)")
+
+
+def _need_buf(name, t, nbytes):
+    """An opaque library buffer (filter spectrum, state-space tables): a contiguous 1-D uint8
+    tensor of exactly the size the library's size query gives for this shape and dtype (a buffer
+    made for another shape or dtype would be read out of bounds)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or t.dim() != 1:
+        raise ValueError(f"{name} must be the 1-D uint8 tensor the library wrote")
+    if t.numel() not in (nbytes, max(nbytes, 1)):
+        raise ValueError(f"{name} holds {t.numel()} bytes; this shape and dtype need {nbytes} "
+                         "(it was made for another shape or dtype)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_gpu(**operands):
+    """Every given operand is a GPU tensor, all on the same device; returns that device."""
+    dev = None
+    for name, t in operands.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor, got device {t.device}")
+        if dev is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other operands on {dev}")
+        dev = t.device
+    return dev
+
+
+def _act(u, name="u", dims=3):
+    """(torch dtype, shape) of the activation that fixes the call's shape."""
+    torch = _torch()
+    if not isinstance(u, torch.Tensor) or u.dim() != dims:
+        raise ValueError(f"{name} must be a {dims}-D torch tensor")
+    if u.dtype not in (torch.float32, torch.float16, torch.bfloat16):
+        raise ValueError(f"{name} has dtype {u.dtype}; supported: float32, float16, bfloat16")
+    _need(name, u, u.shape, u.dtype)
+    return u.dtype, tuple(u.shape)
+
+
 def filter_fft(k, stream=None):
     """Opaque filter spectrum (uint8 device tensor) for k [H, N]."""
     torch = _torch()
+    _act(k, "k", dims=2)
+    _on_gpu(k=k)
     H, N = k.shape
     dt = dtype_code(k.dtype)
     nbytes = lconv_filter_fft_bytes(H, N, dt)
@@ -254,10 +319,25 @@ def filter_fft(k, stream=None):
     return k_f
 
 
+def _gated_inputs(u, k_f, D, q, v, out, L=None, **more):
+    """Checks of the 1D calls' operands; the spectrum was made for [H, L] (L = N if None).
+    `more`: further [B, H, N] operands of u's dtype (None: absent)."""
+    tdt, (B, H, N) = _act(u)
+    _need("D", D, (H,), tdt)
+    _need("q", q, (B, H, N), tdt, optional=True)
+    _need("v", v, (B, H, N), tdt, optional=True)
+    _need("out", out, (B, H, N), tdt, optional=True)
+    for name, t in more.items():
+        _need(name, t, (B, H, N), tdt, optional=True)
+    _need_buf("k_f", k_f, lconv_filter_fft_bytes(H, N if L is None else L, dtype_code(tdt)))
+    _on_gpu(u=u, k_f=k_f, D=D, q=q, v=v, out=out, **more)
+    return B, H, N
+
+
 def fftconv(u, k_f, D, q=None, v=None, out=None, stream=None):
     """y = v * ((k * (q*u))[:N] + D * (q*u)) for u [B, H, N]."""
     torch = _torch()
-    B, H, N = u.shape
+    B, H, N = _gated_inputs(u, k_f, D, q, v, out)
     dt = dtype_code(u.dtype)
     y = torch.empty_like(u) if out is None else out
     wsb = lconv_fftconv_workspace_bytes(B, H, N, dt)
@@ -271,7 +351,7 @@ def fftconv_save(u, k_f, D, q=None, v=None, stream=None):
     """(y, c): y = v * c with the pre-gate output c = (k * (q*u))[:N] + D * (q*u), for the
     gradient call (N <= 4096)."""
     torch = _torch()
-    B, H, N = u.shape
+    B, H, N = _gated_inputs(u, k_f, D, q, v, None)
     dt = dtype_code(u.dtype)
     y = torch.empty_like(u)
     c = torch.empty_like(u)
@@ -287,7 +367,9 @@ def fftconv_bwd(dy, u, k_f, D, q=None, v=None, need_dk=True, c=None, stream=None
     Returns (du, dq, dv, dk, dD): du, dq, dv in u's dtype (dq is None without q, dv is None
     without v); dk [H, N] and dD [H] in float32 (None when need_dk is False)."""
     torch = _torch()
-    B, H, N = u.shape
+    if dy is None:
+        raise ValueError("dy is required")
+    B, H, N = _gated_inputs(u, k_f, D, q, v, None, dy=dy, c=c)
     dt = dtype_code(u.dtype)
     du = torch.empty_like(u)
     dq = torch.empty_like(u) if q is not None else None
@@ -309,7 +391,7 @@ def fftconv_partial(u, k_f, D, L, q=None, v=None, out=None, stream=None):
     """y = v * ((k * (q*u))[:N] + D * (q*u)) for a filter of L taps (k_f = filter_fft(k [H, L]))
     and u [B, H, N] of any length N."""
     torch = _torch()
-    B, H, N = u.shape
+    B, H, N = _gated_inputs(u, k_f, D, q, v, out, L=L)
     y = torch.empty_like(u) if out is None else out
     _check(lconv_fftconv_partial_fwd(_ptr(u), _ptr(k_f), _ptr(D), _ptr(y), _ptr(q), _ptr(v), B, H, N,
                                      L, dtype_code(u.dtype), _stream(stream)),
@@ -322,7 +404,7 @@ def fftconv_sparse(u, k_f, D, keep, q=None, v=None, out=None, stream=None):
     frequency blocks r (f mod R = r, R = lconv_freq_blocks(N)) in `keep` (an iterable of block
     indices closed under r -> R - r, or a bit mask)."""
     torch = _torch()
-    B, H, N = u.shape
+    B, H, N = _gated_inputs(u, k_f, D, q, v, out)
     mask = keep if isinstance(keep, int) else sum(1 << int(r) for r in set(keep))
     y = torch.empty_like(u) if out is None else out
     _check(lconv_fftconv_sparse_fwd(_ptr(u), _ptr(k_f), _ptr(D), _ptr(y), _ptr(q), _ptr(v), B, H, N,
@@ -332,12 +414,17 @@ def fftconv_sparse(u, k_f, D, keep, q=None, v=None, out=None, stream=None):
 
 
 def filter_fft2d(k, stream=None):
+    """Opaque 2D filter spectrum for centred kernels k [C, Hs, Ws]."""
     torch = _torch()
-    C, S, _ = k.shape
+    _act(k, "k", dims=3)
+    _on_gpu(k=k)
+    C, Hs, Ws = k.shape
     dt = dtype_code(k.dtype)
-    nbytes = lconv_filter_fft2d_bytes(C, S, dt)
+    nbytes = lconv_filter_fft2d_bytes(C, Hs, Ws, dt)
+    if nbytes == 0 and C > 0:
+        raise LconvError(3, "lconv_filter_fft2d_bytes")
     k_f = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k.device)
-    _check(lconv_filter_fft2d(_ptr(k), k_f.data_ptr(), C, S, dt, _stream(stream)), "lconv_filter_fft2d")
+    _check(lconv_filter_fft2d(_ptr(k), k_f.data_ptr(), C, Hs, Ws, dt, _stream(stream)), "lconv_filter_fft2d")
     return k_f
 
 
@@ -345,7 +432,12 @@ def ssm_prepare(lam, W, T, dtype, stream=None):
     """Tables for the state-space filter k[h, t] = Re sum_n W lam^t: lam, W complex64 device
     tensors [H, NS]; T the chunk length.  Returns the opaque prep buffer."""
     torch = _torch()
+    if not isinstance(lam, torch.Tensor) or lam.dim() != 2:
+        raise ValueError("lam must be a 2-D complex64 tensor [H, NS]")
     H, NS = lam.shape
+    _need("lam", lam, (H, NS), torch.complex64)
+    _need("W", W, (H, NS), torch.complex64)
+    _on_gpu(lam=lam, W=W)
     dt = dtype_code(dtype)
     nbytes = lconv_ssm_prep_bytes(H, NS, T, dt)
     if nbytes == 0:
@@ -361,7 +453,13 @@ def ssm_prepare(lam, W, T, dtype, stream=None):
 def fftconv_ssm(u, prep, D, NS, T, q=None, v=None, out=None, stream=None):
     """Causal convolution with a state-space filter, chunked with state passing."""
     torch = _torch()
-    B, H, N = u.shape
+    tdt, (B, H, N) = _act(u)
+    _need("D", D, (H,), tdt)
+    _need("q", q, (B, H, N), tdt, optional=True)
+    _need("v", v, (B, H, N), tdt, optional=True)
+    _need("out", out, (B, H, N), tdt, optional=True)
+    _need_buf("prep", prep, lconv_ssm_prep_bytes(H, NS, T, dtype_code(tdt)))
+    _on_gpu(u=u, prep=prep, D=D, q=q, v=v, out=out)
     y = torch.empty_like(u) if out is None else out
     wsb = lconv_fftconv_ssm_workspace_bytes(B, H, N, NS, T)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=u.device)
@@ -374,7 +472,11 @@ def fftconv_ssm(u, prep, D, NS, T, q=None, v=None, out=None, stream=None):
 def filter_fft3d(k, stream=None):
     """Opaque 3D filter spectrum for k [C, S, S, S]."""
     torch = _torch()
+    _act(k, "k", dims=4)
+    _on_gpu(k=k)
     C, S = k.shape[0], k.shape[1]
+    if tuple(k.shape) != (C, S, S, S):
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected a cube [C, S, S, S]")
     dt = dtype_code(k.dtype)
     k_f = torch.empty(max(lconv_filter_fft3d_bytes(C, S, dt), 1), dtype=torch.uint8, device=k.device)
     wsb = lconv_filter_fft3d_workspace_bytes(C, S, dt)
@@ -387,8 +489,15 @@ def filter_fft3d(k, stream=None):
 def fftconv3d(u, k_f, D, out=None, stream=None):
     """3D centred linear convolution plus skip for u [B, C, S, S, S]."""
     torch = _torch()
-    B, C, S = u.shape[:3]
-    dt = dtype_code(u.dtype)
+    tdt, shape = _act(u, dims=5)
+    B, C, S = shape[:3]
+    if shape != (B, C, S, S, S):
+        raise ValueError(f"u has shape {shape}, expected [B, C, S, S, S]")
+    dt = dtype_code(tdt)
+    _need("D", D, (C,), tdt)
+    _need("out", out, shape, tdt, optional=True)
+    _need_buf("k_f", k_f, lconv_filter_fft3d_bytes(C, S, dt))
+    _on_gpu(u=u, k_f=k_f, D=D, out=out)
     y = torch.empty_like(u) if out is None else out
     wsb = lconv_fftconv3d_workspace_bytes(B, C, S, dt)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=u.device)
@@ -398,10 +507,17 @@ def fftconv3d(u, k_f, D, out=None, stream=None):
 
 
 def fftconv2d(u, k_f, D, out=None, stream=None):
+    """2D centred linear convolution plus skip for u [B, C, Hs, Ws]."""
     torch = _torch()
-    B, C, S, _ = u.shape
-    dt = dtype_code(u.dtype)
+    tdt, (B, C, Hs, Ws) = _act(u, dims=4)
+    dt = dtype_code(tdt)
+    _need("D", D, (C,), tdt)
+    _need("out", out, (B, C, Hs, Ws), tdt, optional=True)
+    _need_buf("k_f", k_f, lconv_filter_fft2d_bytes(C, Hs, Ws, dt))
+    dev = _on_gpu(u=u, k_f=k_f, D=D, out=out)
     y = torch.empty_like(u) if out is None else out
-    _check(lconv_fftconv2d_fwd(_ptr(u), _ptr(k_f), _ptr(D), _ptr(y), B, C, S, dt, _stream(stream)),
-           "lconv_fftconv2d_fwd")
+    wsb = lconv_fftconv2d_workspace_bytes(B, C, Hs, Ws, dt)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+    _check(lconv_fftconv2d_fwd(_ptr(u), _ptr(k_f), _ptr(D), _ptr(y), B, C, Hs, Ws, dt, _ptr(ws), wsb,
+                               _stream(stream)), "lconv_fftconv2d_fwd")
     return y

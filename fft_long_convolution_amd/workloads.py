@@ -112,14 +112,23 @@ class Conv2DSpec:
     name: str
     B: int
     C: int
-    S: int
+    S: int                                    # rows (Hs); also the columns unless Ws is set
     dtype: str
     decay: float = 0.05                       # exp(-decay * (|dx| + |dy|)), centred taps
     seed: int = 0
+    Ws: int = 0                               # columns of a rectangular image (0: S)
 
     @property
     def kind(self):
         return "2d"
+
+    @property
+    def Hs(self):
+        return self.S
+
+    @property
+    def cols(self):
+        return self.Ws or self.S
 
 
 @dataclasses.dataclass(frozen=True)
@@ -221,12 +230,13 @@ def make_grad_1d(spec: Conv1DSpec) -> np.ndarray:
 def make_2d(spec: Conv2DSpec) -> dict:
     """Draw u, k, D for a 2D workload (draw order: u, k_raw, D)."""
     rng = np.random.default_rng(spec.seed)
-    B, C, S = spec.B, spec.C, spec.S
+    B, C, Hs, Ws = spec.B, spec.C, spec.Hs, spec.cols
     out = {"spec": spec, "dtype": spec.dtype}
-    out["u"] = to_storage(rng.standard_normal((B, C, S, S), dtype=np.float32), spec.dtype)
-    k = rng.standard_normal((C, S, S))
-    off = np.abs(np.arange(S, dtype=np.float64) - S // 2)
-    k *= np.exp(-spec.decay * (off[:, None] + off[None, :]))[None]
+    out["u"] = to_storage(rng.standard_normal((B, C, Hs, Ws), dtype=np.float32), spec.dtype)
+    k = rng.standard_normal((C, Hs, Ws))
+    offh = np.abs(np.arange(Hs, dtype=np.float64) - Hs // 2)
+    offw = np.abs(np.arange(Ws, dtype=np.float64) - Ws // 2)
+    k *= np.exp(-spec.decay * (offh[:, None] + offw[None, :]))[None]
     out["k"] = to_storage(k, spec.dtype)
     out["D"] = to_storage(rng.standard_normal(C), spec.dtype)
     return out

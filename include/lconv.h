@@ -15,18 +15,19 @@
  *   1D:  x = q (.) u                       (q optional, elementwise)
  *        y = v (.) ( irfft(rfft(x, M) * rfft(k, M))[:N] + D * x )   (v optional), M >= 2N
  *        i.e. y[b,h,t] = v[b,h,t] * ( sum_{s<=t} k[h,t-s] x[b,h,s] + D[h] x[b,h,t] ).
- *   2D:  y[b,c,i,j] = sum_{a,e} k[c,a,e] u[b,c,i+S/2-a,j+S/2-e] + D[c] u[b,c,i,j]
- *        (linear, not circular; kernel tap (a,e) sits at offset (a-S/2, e-S/2)).
+ *   2D:  y[b,c,i,j] = sum_{a,e} k[c,a,e] u[b,c,i+Hs/2-a,j+Ws/2-e] + D[c] u[b,c,i,j]
+ *        (linear, not circular; kernel tap (a,e) sits at offset (a-Hs/2, e-Ws/2)).
  *
  * Conventions shared by every entry point
  *   * All data pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors) on the
  *     current HIP device.  The caller owns and frees every buffer, including k_f and any
  *     workspace; sizes come from the *_bytes queries below.
  *   * Layouts are dense row-major: u, q, v, y are [B][H][N] with N contiguous; k is [H][N];
- *     D is [H].  2D: u, y are [B][C][S][S]; k is [C][S][S]; D is [C].  All share `dtype`.
+ *     D is [H].  2D: u, y are [B][C][Hs][Ws]; k is [C][Hs][Ws]; D is [C].  All share `dtype`.
  *   * k_f (the filter spectrum) is OPAQUE: produced by lconv_filter_fft* for one
- *     (H, N, dtype) or (C, S, dtype) and valid only for that shape and dtype.  Its size is
- *     lconv_filter_fft*_bytes().
+ *     (H, N, dtype) or (C, Hs, Ws, dtype) and valid only for that shape and dtype.  Its size is
+ *     lconv_filter_fft*_bytes(); the library cannot check the size of a buffer it is given,
+ *     so a spectrum made for another shape or dtype is the caller's error.
  *   * Every call is asynchronous on `stream` (0 = the null stream); nothing synchronises.
  *     Faults during execution surface at the caller's next synchronising call.
  *   * Arguments are validated on the host before any HIP call.  On any error nothing is
@@ -48,8 +49,9 @@ extern "C" {
 
 /* Bumped when entry points are added or a size query's result changes (3: the training pair
  * lconv_fftconv_fwd_save / lconv_fftconv_bwd_saved; the state-space workspace holds the scan's
- * part states.  4: lconv_prepare and lconv_fftconv_fwd_noalloc, two status codes). */
-#define LCONV_ABI_VERSION 4
+ * part states.  4: lconv_prepare and lconv_fftconv_fwd_noalloc, two status codes.  5: 2D calls
+ * take Hs x Ws images and a workspace; lconv_fftconv2d_workspace_bytes). */
+#define LCONV_ABI_VERSION 5
 
 typedef enum { LCONV_F32 = 0, LCONV_F16 = 1, LCONV_BF16 = 2 } lconv_dtype_t;
 
@@ -68,9 +70,9 @@ typedef enum {
                                     LCONV_NOALLOC_SCRATCH_BYTES                            */
 } lconv_status_t;
 
-/* Largest supported sequence length (1D) and the only supported 2D side. */
-#define LCONV_MAX_N   ((int64_t)1 << 22)
-#define LCONV_2D_SIDE 128
+/* Largest supported sequence length (1D) and the largest supported 2D side. */
+#define LCONV_MAX_N       ((int64_t)1 << 22)
+#define LCONV_2D_MAX_SIDE 128
 
 /* ---- size queries (pure host functions; 0 for invalid or unsupported arguments) ---------- */
 
@@ -80,8 +82,10 @@ size_t lconv_filter_fft_bytes(int64_t H, int64_t N, lconv_dtype_t dtype);
 size_t lconv_filter_fft_workspace_bytes(int64_t H, int64_t N, lconv_dtype_t dtype);
 /* Scratch bytes lconv_fftconv_fwd needs (0 when the whole transform fits one workgroup). */
 size_t lconv_fftconv_workspace_bytes(int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype);
-/* Bytes of the opaque 2D filter spectrum for C channels of S x S kernels. */
-size_t lconv_filter_fft2d_bytes(int64_t C, int64_t S, lconv_dtype_t dtype);
+/* Bytes of the opaque 2D filter spectrum for C channels of Hs x Ws kernels. */
+size_t lconv_filter_fft2d_bytes(int64_t C, int64_t Hs, int64_t Ws, lconv_dtype_t dtype);
+/* Scratch bytes lconv_fftconv2d_fwd needs (0 for every supported shape: one fused kernel). */
+size_t lconv_fftconv2d_workspace_bytes(int64_t B, int64_t C, int64_t Hs, int64_t Ws, lconv_dtype_t dtype);
 
 /* ---- 1D --------------------------------------------------------------------------------- */
 
@@ -226,22 +230,38 @@ lconv_status_t lconv_fftconv_bwd_saved(const void* dy, const void* u, const void
 /* ---- 2D (HyenaND-style) ------------------------------------------------------------------ */
 
 /*
- * 2D filter spectrum from k[C][S][S] (S = LCONV_2D_SIDE): the (2S x 2S) DFT of each
- * zero-padded kernel, scaled by 1/(2S)^2, in the library's transform order.  fp32 arithmetic.
+ * 2D filter spectrum ("Native Multi-Dimensional Subquadratic Operators via Input Dependent Long
+ * Convolutions", abstract: global convolutions applied on the native 2D grid of the data; the
+ * FlashConv page, Mechanism: the pointwise spectral product needs the filter's spectrum, built
+ * once per filter).  The 256 x 256 DFT of each kernel placed with its centre tap (Hs/2, Ws/2) at
+ * grid point (64, 64), scaled by 1/256^2, in the library's transform order (opaque).  fp32
+ * arithmetic, stored in dtype.
+ *   k    [C][Hs][Ws] dtype, device
+ *   k_f  lconv_filter_fft2d_bytes(C, Hs, Ws, dtype) bytes, device, written
+ * Supported: 1 <= Hs <= 128; 8 <= Ws <= 128 with Ws a multiple of 8; dtype bf16 or fp16
+ * (LCONV_ERR_UNSUPPORTED otherwise, fp32 included).  C = 0 is a no-op.
  */
-lconv_status_t lconv_filter_fft2d(const void* k, void* k_f, int64_t C, int64_t S,
+lconv_status_t lconv_filter_fft2d(const void* k, void* k_f, int64_t C, int64_t Hs, int64_t Ws,
                                   lconv_dtype_t dtype, hipStream_t stream);
 
 /*
- * 2D linear convolution with centred full-size kernels, cropped to the input window, plus
- * the D skip ("Native Multi-Dimensional Subquadratic Operators..." abstract):
- *   u, y [B][C][S][S] dtype, device;  k_f from lconv_filter_fft2d;  D [C] dtype, device.
- * One fused kernel: row DFTs, column DFTs, spectral product, inverse column and row DFTs
- * restricted to the output window.  Supported: S = LCONV_2D_SIDE, dtype bf16 or fp16.
+ * 2D linear (not circular) convolution with centred full-size kernels, cropped to the input
+ * window, plus the D skip (same abstract: global convolutions on the native multi-dimensional
+ * grid, with a fused FFT-convolution path):
+ *   y[b,c,i,j] = sum_{a,e} k[c,a,e] u[b,c, i + Hs/2 - a, j + Ws/2 - e] + D[c] u[b,c,i,j]
+ * (halves rounded down; u = 0 outside the image).
+ *   u, y      [B][C][Hs][Ws] dtype, device (y written, must not overlap any input)
+ *   k_f       from lconv_filter_fft2d(k, ..., C, Hs, Ws, dtype)
+ *   D         [C] dtype, device
+ *   workspace lconv_fftconv2d_workspace_bytes(...) bytes (0 for every supported shape; may be
+ *             NULL)
+ * One fused kernel per pair of images of one channel: row DFTs, column DFTs, spectral product,
+ * inverse column and row DFTs restricted to the output window, all through LDS.  Supported
+ * shapes and dtypes as for lconv_filter_fft2d.  B = 0 or C = 0 is a no-op.
  */
 lconv_status_t lconv_fftconv2d_fwd(const void* u, const void* k_f, const void* D, void* y,
-                                   int64_t B, int64_t C, int64_t S, lconv_dtype_t dtype,
-                                   hipStream_t stream);
+                                   int64_t B, int64_t C, int64_t Hs, int64_t Ws, lconv_dtype_t dtype,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---- state-space filters: chunks with state passing --------------------------------------- */
 

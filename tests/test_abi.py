@@ -27,7 +27,7 @@ def test_exports_every_header_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lconv.lconv_abi_version() == 4
+    assert lconv.lconv_abi_version() == 5
     for s in range(10):
         assert lconv.status_string(s)
     assert "unknown" in lconv.status_string(99)
@@ -48,8 +48,12 @@ def test_size_queries():
     assert lconv.lconv_filter_fft_bytes(1, 2 ** 22 + 8, BF16) == 0        # too long
     assert lconv.lconv_filter_fft_bytes(1, 2300000, BF16) == 2 ** 23 * 4   # 2.3M: M = 2^23
     assert lconv.lconv_filter_fft_bytes(1, 8, 7) == 0                     # bad dtype
-    assert lconv.lconv_filter_fft2d_bytes(256, 128, BF16) == 256 * 256 * 256 * 4
-    assert lconv.lconv_filter_fft2d_bytes(1, 64, BF16) == 0
+    assert lconv.lconv_filter_fft2d_bytes(256, 128, 128, BF16) == 256 * 256 * 256 * 4
+    assert lconv.lconv_filter_fft2d_bytes(3, 64, 48, F16) == 3 * 256 * 256 * 4   # any sides <= 128
+    assert lconv.lconv_filter_fft2d_bytes(1, 129, 128, BF16) == 0                # too large
+    assert lconv.lconv_filter_fft2d_bytes(1, 128, 12, BF16) == 0                 # Ws not a multiple of 8
+    assert lconv.lconv_filter_fft2d_bytes(1, 128, 128, F32) == 0                 # fp32: not built
+    assert lconv.lconv_fftconv2d_workspace_bytes(8, 256, 128, 128, BF16) == 0    # one fused kernel
 
 
 def fwd(u=A, kf=Bq, D=C, y=Y, q=None, v=None, B=2, H=3, N=64, dt=BF16, ws=None, wsb=0):
@@ -83,7 +87,8 @@ def test_empty_is_noop():
     assert fwd(N=0) == OK
     assert fwd(B=0, u=None, y=None) == OK
     assert lconv.lconv_filter_fft(None, None, 0, 64, BF16, None, 0, None) == OK
-    assert lconv.lconv_fftconv2d_fwd(None, None, None, None, 0, 4, 128, BF16, None) == OK
+    assert lconv.lconv_fftconv2d_fwd(None, None, None, None, 0, 4, 128, 128, BF16, None, 0, None) == OK
+    assert lconv.lconv_filter_fft2d(None, None, 0, 128, 128, BF16, None) == OK
 
 
 def test_filter_fft_validation_errors():
@@ -99,13 +104,24 @@ def test_filter_fft_validation_errors():
 
 
 def test_2d_validation_errors():
-    f = lconv.lconv_fftconv2d_fwd
-    assert f(A, Bq, C, Y, 2, 3, 64, BF16, None) == UNSUP
-    assert f(A, Bq, C, Y, 2, 3, 128, F32, None) == UNSUP
-    assert f(None, Bq, C, Y, 2, 3, 128, BF16, None) == NULLP
-    assert f(A + 2, Bq, C, Y, 2, 3, 128, BF16, None) == MISAL
-    assert f(A, Bq, C, A, 2, 3, 128, BF16, None) == ALIAS
-    assert f(A, Bq, C, Y, -2, 3, 128, BF16, None) == SHAPE
+    f = lambda u, kf, D, y, B, C, Hs, Ws, dt: lconv.lconv_fftconv2d_fwd(u, kf, D, y, B, C, Hs, Ws, dt,
+                                                                         None, 0, None)
+    assert f(A, Bq, C, Y, 2, 3, 256, 128, BF16) == UNSUP     # sides up to 128
+    assert f(A, Bq, C, Y, 2, 3, 128, 20, BF16) == UNSUP      # columns in whole groups of 8
+    assert f(A, Bq, C, Y, 2, 3, 128, 0, BF16) == UNSUP
+    assert f(A, Bq, C, Y, 2, 3, 128, 128, F32) == UNSUP
+    assert f(A, Bq, C, Y, 2, 3, 128, 128, 7) == UNSUP
+    assert f(None, Bq, C, Y, 2, 3, 128, 128, BF16) == NULLP
+    assert f(A + 2, Bq, C, Y, 2, 3, 128, 128, BF16) == MISAL
+    assert f(A, Bq, C, A, 2, 3, 128, 128, BF16) == ALIAS
+    assert f(A, Bq, C, Y, -2, 3, 128, 128, BF16) == SHAPE
+    assert f(A, Bq, C, Y, 2, 3, -1, 128, BF16) == SHAPE
+    g = lconv.lconv_filter_fft2d
+    assert g(A, Y, 3, 128, 128, F32, None) == UNSUP
+    assert g(A, Y, 3, 130, 128, BF16, None) == UNSUP
+    assert g(None, Y, 3, 100, 64, BF16, None) == NULLP
+    assert g(A + 4, Y, 3, 100, 64, BF16, None) == MISAL
+    assert g(A, A, 3, 100, 64, BF16, None) == ALIAS
 
 
 def test_no_device_gives_hip_error():
@@ -294,3 +310,60 @@ def test_ssm_sizes_and_validation():
     assert sf(y=G[0]) == ALIAS
     assert sf(ws=None) == WSERR
     assert sf(B=0) == OK
+
+
+def _header_decls():
+    """{name: (return type, [parameter types])} of every function include/lconv.h declares."""
+    import re
+    src = open(lconv.HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    out = {}
+    for m in re.finditer(r"([A-Za-z_][A-Za-z0-9_ \*]*?)\b(lconv_[a-z0-9_]+)\s*\(([^;{]*?)\)\s*;", src):
+        ret, name, params = " ".join(m.group(1).split()), m.group(2), m.group(3)
+        types = []
+        for p in params.split(","):
+            p = " ".join(p.replace("*", " * ").split())
+            if not p or p == "void":
+                continue
+            toks = p.split(" ")
+            types.append(" ".join(toks[:-1]).replace(" *", "*"))   # drop the parameter name
+        out[name] = (ret, types)
+    return out
+
+
+# The boundary's entry points with their parameter types (the filter transform also takes a
+# workspace: the multi-pass filter spectrum and the staging of ragged rows need one).
+BOUNDARY = {
+    "lconv_filter_fft_bytes": ("size_t", ["int64_t", "int64_t", "lconv_dtype_t"]),
+    "lconv_filter_fft2d_bytes": ("size_t", ["int64_t", "int64_t", "int64_t", "lconv_dtype_t"]),
+    "lconv_fftconv_workspace_bytes": ("size_t", ["int64_t", "int64_t", "int64_t", "lconv_dtype_t"]),
+    "lconv_fftconv2d_workspace_bytes": ("size_t", ["int64_t", "int64_t", "int64_t", "int64_t",
+                                                   "lconv_dtype_t"]),
+    "lconv_filter_fft": ("lconv_status_t", ["const void*", "void*", "int64_t", "int64_t", "lconv_dtype_t",
+                                            "void*", "size_t", "hipStream_t"]),
+    "lconv_filter_fft2d": ("lconv_status_t", ["const void*", "void*", "int64_t", "int64_t", "int64_t",
+                                              "lconv_dtype_t", "hipStream_t"]),
+    "lconv_fftconv_fwd": ("lconv_status_t", ["const void*", "const void*", "const void*", "void*",
+                                             "const void*", "const void*", "int64_t", "int64_t", "int64_t",
+                                             "lconv_dtype_t", "void*", "size_t", "hipStream_t"]),
+    "lconv_fftconv2d_fwd": ("lconv_status_t", ["const void*", "const void*", "const void*", "void*",
+                                               "int64_t", "int64_t", "int64_t", "int64_t", "lconv_dtype_t",
+                                               "void*", "size_t", "hipStream_t"]),
+    "lconv_status_string": ("const char*", ["lconv_status_t"]),
+}
+
+
+def test_boundary_signatures():
+    decls = _header_decls()
+    for name, (ret, types) in BOUNDARY.items():
+        assert name in decls, name
+        assert decls[name] == (ret, types), (name, decls[name])
+
+
+def test_binding_arity_matches_header(lib):
+    """The ctypes binding passes exactly the parameters each declaration has."""
+    decls = _header_decls()
+    assert set(decls) == set(lconv.header_functions())
+    for name, (_, types) in decls.items():
+        assert len(getattr(lib, name).argtypes) == len(types), name

@@ -47,6 +47,24 @@ def test_2d_full_images(lc, dtype, B, C):
     assert err <= 2e-2
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("Hs,Ws,B,C", [(128, 64, 2, 3), (100, 128, 3, 2), (37, 24, 2, 2), (1, 8, 3, 1),
+                                       (64, 128, 1, 4), (127, 120, 2, 1)])
+def test_2d_rectangular_full_images(lc, dtype, Hs, Ws, B, C):
+    """Hs x Ws images, sides up to 128 (odd rows included): every image against the naive-DFT
+    oracle with the centre tap at (Hs // 2, Ws // 2)."""
+    spec = wl.Conv2DSpec(f"t2d_{dtype}_{Hs}x{Ws}", B, C, Hs, dtype, seed=600 + Hs + Ws, Ws=Ws)
+    say(f"[2d rect] dtype={dtype} B={B} C={C} Hs={Hs} Ws={Ws} seed={spec.seed}")
+    d = wl.make(spec)
+    y = run_2d(lc, d)
+    assert y.shape == (B, C, Hs, Ws) and np.all(np.isfinite(y))
+    imgs = [(b, c) for b in range(B) for c in range(C)]
+    ref = oracle.conv2d_dft(d["u"], d["k"], d["D"], imgs, dt=DT_ORACLE[dtype]).reshape(B, C, -1)
+    err = rel_l2_rows(y.reshape(B, C, -1), ref).max()
+    say(f"   max rel L2 = {err:.3e}")
+    assert err <= 2e-2
+
+
 def test_2d_delta_kernel_is_identity(lc):
     """Centre tap 1 and D = 0: the output reproduces the input (up to bf16 rounding)."""
     spec = wl.Conv2DSpec("delta2d", 2, 3, 128, "bf16", seed=9)
