@@ -8,6 +8,12 @@ The gradient call (lconv_fftconv_bwd: du, dq, dv, dk, dD from a seeded dy) is ti
 way on the same inputs and reported in the line's "backward" object (sequence lengths it
 supports, N <= 4096); it is not part of the step.
 
+Timing: W warm-up steps, then exactly K steps between two synchronizations, bracketed by one
+event pair on the launch stream and preceded by a bounded spin kernel so the GPU runs the K
+kernels back to back (ms_per_step = event time / K; the host wall time is reported beside it).
+The "timing" object adds per-launch median / min / p90, back to back and after a 512 MiB cache
+scrub.
+
 Algorithmic bytes (what the method must move): (n_in + 1) * B*H*N * s for the activations
 (n_in = 3 gated, 1 otherwise), plus the filter spectrum once at its minimal size
 H*(N+1)*2*s (Hermitian half in the I/O dtype), plus D.  Nominal flops per row:
@@ -172,6 +178,46 @@ def cpu_baseline(d, budget_s=12.0):
             "sample": f"{nrows} full rows (b,h) of {spec.name}, direct float64 sum, {el:.1f} s"}
 
 
+def prime(launches):
+    """Queue a bounded spin kernel (about 25 us of GPU time per launch to follow) on the current
+    stream, so that the GPU is still busy when the host has queued the next launches."""
+    import torch
+    torch.cuda._sleep(int(50_000 * max(launches, 1)))
+
+
+def _stats_us(ms):
+    a = np.sort(np.asarray(ms, np.float64)) * 1e3
+    return {"median": round(float(np.median(a)), 3), "min": round(float(a[0]), 3),
+            "p90": round(float(np.percentile(a, 90)), 3)}
+
+
+def launch_distribution(step, args):
+    """Per-launch times after the timed region: R launches each between its own event pair,
+    back to back ("hot"), then R launches each preceded by a write of a 512 MiB buffer outside
+    the events ("scrubbed": the 256 MB last-level cache then holds none of the inputs).  Returns
+    median / min / p90 in microseconds for both, or {} with --dist 0."""
+    import torch
+    R = args.dist
+    if R <= 0:
+        return {}
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R)]
+    out = {"launches": R, "scrub_bytes": scrub.numel()}
+    for mode in ("hot", "scrubbed"):
+        torch.cuda.synchronize()
+        prime(R)
+        for i, (e0, e1) in enumerate(evs):
+            if mode == "scrubbed":
+                scrub.fill_(i & 0x7f)
+            e0.record()
+            step()
+            e1.record()
+        torch.cuda.synchronize()
+        out[mode + "_us"] = _stats_us([e0.elapsed_time(e1) for e0, e1 in evs])
+    del scrub
+    return out
+
+
 def time_backward(lconv, wl, spec, u, kf, D, q, v, args):
     """K timed gradient calls (after W warm-up calls) on the forward's inputs and a seeded dy."""
     import torch
@@ -195,6 +241,7 @@ def time_backward(lconv, wl, spec, u, kf, D, q, v, args):
         call()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    prime(3 * args.steps)
     ev0.record()
     for _ in range(args.steps):
         call()
@@ -232,6 +279,7 @@ def time_backward(lconv, wl, spec, u, kf, D, q, v, args):
             for _ in range(args.warmup):
                 fn()
             torch.cuda.synchronize()
+            prime(3 * args.steps)
             ev0.record()
             for _ in range(args.steps):
                 fn()
@@ -258,6 +306,9 @@ def main():
                     help="frequency-sparse call: bit mask (e.g. 0xe000000f) of the frequency "
                          "blocks kept (f mod R); the step is lconv_fftconv_sparse_fwd")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--dist", type=int, default=20,
+                    help="launches for the per-launch median / min / p90, hot and after a cache "
+                         "scrub (0: skip)")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="run only a plain 256 MiB device copy (reads and writes 256 MiB per "
                          "launch): the reference for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -393,10 +444,14 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # Timed region: exactly K steps.  One event pair on the launch stream (torch's current
-    # stream, which the library is given) around the region times the kernels back to back.
+    # Timed region: exactly K steps between two synchronizations.  One event pair on the launch
+    # stream (torch's current stream, which the library is given) brackets the K launches.  A
+    # bounded spin kernel queued first keeps the GPU busy while the host queues the region, so
+    # the first launch does not wait on the host and the events time the K kernels back to
+    # back: the step time is the event time / K, the same quantity a kernel trace averages.
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    prime(args.steps)
     t0 = time.perf_counter()
     ev0.record()
     for i in range(args.steps):
@@ -405,7 +460,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     avg_ms = ev0.elapsed_time(ev1) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = avg_ms
+
+    timing = launch_distribution(step, args)
 
     nbytes = algorithmic_bytes(spec)
     flops = nominal_flops(spec)
@@ -427,6 +484,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "host_wall_ms": round(wall * 1e3, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -447,6 +505,9 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "kernel_avg_us": round(avg_ms * 1e3, 3)},
     }
+    if timing:
+        out["timing"] = timing
+        out["timing"]["region_avg_us"] = round(avg_ms * 1e3, 3)
     cs = counter_summary(spec.name) if args.keep is None else {}  # counters are of the dense call
     if cs:
         out["roofline"]["traffic"] = int(float(cs["traffic_bytes_per_launch"]))
