@@ -8,7 +8,8 @@ from .oracle import (  # noqa: F401
     DT_F32, DT_F16, DT_BF16,
     build, conv1d_rows, conv1d_points, conv2d_points, conv2d_dft, conv3d_points, widen,
     ssm_kernel, ssm_rows,
-    conv1d_bwd_rows, conv1d_bwd_dk, conv1d_short_points, conv1d_circ_rows, sparse_filter,
+    conv1d_bwd_rows, conv1d_bwd_dk, conv1d_bwd_points, conv1d_bwd_dk_points,
+    conv1d_short_points, conv1d_circ_rows, sparse_filter,
     transform_length,
     conv1d_toeplitz, conv1d_python_int,
 )

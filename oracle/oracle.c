@@ -490,6 +490,117 @@ int oracle_conv1d_bwd_dk(const void* u, const void* q, const void* v, const void
     return 0;
 }
 
+/* The same gradients at single positions, for sequences too long for full rows.  pts holds
+ * (b, h, t) triples for du, dq, dv (each NULL when not wanted); dk_pts holds (h, tau) pairs for
+ * dk.  Each value is summed exactly as the row versions above sum it. */
+static double or_ds_at(const or_job* J, const void* gy, int64_t off, int64_t t) {
+    double d = or_load(gy, J->dt, off + t);
+    return J->v ? d * or_load(J->v, J->dt, off + t) : d;
+}
+static double or_x_at(const or_job* J, int64_t off, int64_t t) {
+    double x = or_load(J->u, J->dt, off + t);
+    return J->q ? x * or_load(J->q, J->dt, off + t) : x;
+}
+
+static void* or_bwd_points_worker(void* arg) {
+    or_bwd_job* W = (or_bwd_job*)arg;
+    const or_job* J = &W->j;
+    const int64_t N = J->N;
+    for (int64_t r = J->lo; r < J->hi; ++r) {
+        int64_t b = J->sel[3 * r], h = J->sel[3 * r + 1], t = J->sel[3 * r + 2];
+        int64_t off = (b * J->H + h) * N;
+        double d = or_load(J->D, J->dt, h);
+        double a = 0;
+        for (int64_t tau = t; tau < N; ++tau) a += or_load(J->k, J->dt, h * N + (tau - t)) * or_ds_at(J, W->gy, off, tau);
+        double dx = a + d * or_ds_at(J, W->gy, off, t);
+        if (W->du) W->du[r] = J->q ? dx * or_load(J->q, J->dt, off + t) : dx;
+        if (W->dq) W->dq[r] = dx * or_load(J->u, J->dt, off + t);
+        if (W->dv) {
+            double c = 0;
+            for (int64_t s2 = 0; s2 <= t; ++s2) c += or_load(J->k, J->dt, h * N + (t - s2)) * or_x_at(J, off, s2);
+            W->dv[r] = or_load(W->gy, J->dt, off + t) * (c + d * or_x_at(J, off, t));
+        }
+    }
+    return NULL;
+}
+
+static void* or_dk_points_worker(void* arg) {
+    or_bwd_job* W = (or_bwd_job*)arg;
+    const or_job* J = &W->j;
+    const int64_t N = J->N, B = J->B;
+    for (int64_t r = J->lo; r < J->hi; ++r) {
+        int64_t h = J->sel[2 * r], tau = J->sel[2 * r + 1];
+        double acc = 0;
+        for (int64_t b = 0; b < B; ++b) {
+            int64_t off = (b * J->H + h) * N;
+            double a = 0;
+            for (int64_t t = tau; t < N; ++t) a += or_ds_at(J, W->gy, off, t) * or_x_at(J, off, t - tau);
+            acc += a;
+        }
+        W->du[r] = acc;
+    }
+    return NULL;
+}
+
+static void or_bwd_parallel(void* (*fn)(void*), or_bwd_job W, int64_t n, int nthreads) {
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((int64_t)nthreads > n) nthreads = (int)(n > 0 ? n : 1);
+    or_bwd_job* jobs = (or_bwd_job*)calloc((size_t)nthreads, sizeof(or_bwd_job));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    int64_t per = (n + nthreads - 1) / nthreads;
+    int used = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        int64_t lo = (int64_t)i * per, hi = lo + per < n ? lo + per : n;
+        if (lo >= hi) break;
+        jobs[used] = W;
+        jobs[used].j.lo = lo;
+        jobs[used].j.hi = hi;
+        pthread_create(&th[used], NULL, fn, &jobs[used]);
+        ++used;
+    }
+    for (int i = 0; i < used; ++i) pthread_join(th[i], NULL);
+    free(th);
+    free(jobs);
+}
+
+int oracle_conv1d_bwd_points(const void* u, const void* q, const void* v, const void* k, const void* D,
+                             const void* gy, int dt, int64_t B, int64_t H, int64_t N, const int64_t* pts,
+                             int64_t npts, double* du, double* dq, double* dv, int nthreads) {
+    if (or_check1d(u, k, D, pts, npts, du ? du : (dq ? dq : dv), B, H, N, dt) || !gy) return -1;
+    for (int64_t r = 0; r < npts; ++r)
+        if (pts[3 * r] < 0 || pts[3 * r] >= B || pts[3 * r + 1] < 0 || pts[3 * r + 1] >= H ||
+            pts[3 * r + 2] < 0 || pts[3 * r + 2] >= N)
+            return -1;
+    or_bwd_job W;
+    or_job J = {u, q, v, k, D, dt, B, H, N, pts, NULL, 0, 0, 0};
+    W.j = J;
+    W.gy = gy;
+    W.du = du;
+    W.dq = q ? dq : NULL;
+    W.dv = v ? dv : NULL;
+    or_bwd_parallel(or_bwd_points_worker, W, npts, nthreads);
+    return 0;
+}
+
+int oracle_conv1d_bwd_dk_points(const void* u, const void* q, const void* v, const void* gy, int dt,
+                                int64_t B, int64_t H, int64_t N, const int64_t* pts, int64_t npts,
+                                double* dk, int nthreads) {
+    if (!u || !gy || !dk || (npts > 0 && !pts)) return -1;
+    if (B < 1 || H < 1 || N < 1 || npts < 0 || dt < 0 || dt > 2) return -1;
+    for (int64_t r = 0; r < npts; ++r)
+        if (pts[2 * r] < 0 || pts[2 * r] >= H || pts[2 * r + 1] < 0 || pts[2 * r + 1] >= N) return -1;
+    or_bwd_job W;
+    or_job J = {u, q, v, NULL, NULL, dt, B, H, N, pts, NULL, 0, 0, 0};
+    W.j = J;
+    W.gy = gy;
+    W.du = dk;
+    W.dq = NULL;
+    W.dv = NULL;
+    or_bwd_parallel(or_dk_points_worker, W, npts, nthreads);
+    return 0;
+}
+
 /* ------------------------------------------------------------------------------------------ */
 /* 2D: direct summation at single positions                                                    */
 /* ------------------------------------------------------------------------------------------ */

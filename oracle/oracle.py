@@ -62,6 +62,9 @@ def _load():
         lib.oracle_conv1d_bwd_rows.argtypes = [vp, vp, vp, vp, vp, vp, ip, i64, i64, i64, vp, i64,
                                                dp, dp, dp, ip]
         lib.oracle_conv1d_bwd_dk.argtypes = [vp, vp, vp, vp, ip, i64, i64, i64, vp, i64, dp, dp, ip]
+        lib.oracle_conv1d_bwd_points.argtypes = [vp, vp, vp, vp, vp, vp, ip, i64, i64, i64, vp, i64,
+                                                 dp, dp, dp, ip]
+        lib.oracle_conv1d_bwd_dk_points.argtypes = [vp, vp, vp, vp, ip, i64, i64, i64, vp, i64, dp, ip]
         for f in (lib.oracle_conv1d_rows, lib.oracle_conv1d_points, lib.oracle_conv2d_points,
                   lib.oracle_conv1d_bwd_rows, lib.oracle_conv1d_bwd_dk):
             f.restype = ctypes.c_int
@@ -253,6 +256,44 @@ def conv1d_bwd_dk(u, gy, chans, q=None, v=None, dt=None, nthreads=None):
     if rc:
         raise ValueError("oracle_conv1d_bwd_dk rejected its arguments")
     return dk, dD
+
+
+def conv1d_bwd_points(u, k, D, gy, pts, q=None, v=None, dt=None, nthreads=None):
+    """The gradients du, dq, dv of conv1d_bwd_rows at single positions pts = [(b,h,t), ...],
+    summed exactly as the row version sums them.  Returns float64 (du, dq, dv) of len(pts) each
+    (dq None without q, dv None without v)."""
+    dt = _dt_of(u, dt)
+    st = _storage(dt)
+    u, k, D, gy, q, v = (_c(a, st) for a in (u, k, D, gy, q, v))
+    B, H, N = u.shape
+    assert k.shape == (H, N) and D.shape == (H,) and gy.shape == u.shape
+    pts = np.ascontiguousarray(np.asarray(pts, np.int64).reshape(-1, 3))
+    du = np.empty(pts.shape[0], np.float64)
+    dq = np.empty_like(du) if q is not None else None
+    dv = np.empty_like(du) if v is not None else None
+    rc = _load().oracle_conv1d_bwd_points(_ptr(u), _ptr(q), _ptr(v), _ptr(k), _ptr(D), _ptr(gy), dt, B, H,
+                                          N, _ptr(pts), pts.shape[0], du.ctypes.data,
+                                          None if dq is None else dq.ctypes.data,
+                                          None if dv is None else dv.ctypes.data, _threads(nthreads))
+    if rc:
+        raise ValueError("oracle_conv1d_bwd_points rejected its arguments")
+    return du, dq, dv
+
+
+def conv1d_bwd_dk_points(u, gy, pts, q=None, v=None, dt=None, nthreads=None):
+    """dk[h, tau] of conv1d_bwd_dk at pairs pts = [(h, tau), ...], summed exactly as the channel
+    version sums them.  Returns float64 [len(pts)]."""
+    dt = _dt_of(u, dt)
+    st = _storage(dt)
+    u, gy, q, v = (_c(a, st) for a in (u, gy, q, v))
+    B, H, N = u.shape
+    pts = np.ascontiguousarray(np.asarray(pts, np.int64).reshape(-1, 2))
+    dk = np.empty(pts.shape[0], np.float64)
+    rc = _load().oracle_conv1d_bwd_dk_points(_ptr(u), _ptr(q), _ptr(v), _ptr(gy), dt, B, H, N, _ptr(pts),
+                                             pts.shape[0], dk.ctypes.data, _threads(nthreads))
+    if rc:
+        raise ValueError("oracle_conv1d_bwd_dk_points rejected its arguments")
+    return dk
 
 
 def conv2d_points(u, k, D, pts, dt=None, nthreads=None):

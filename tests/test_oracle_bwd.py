@@ -189,3 +189,28 @@ def test_bwd_rejects_bad_arguments():
         oracle.conv1d_bwd_rows(u, k, D, gy, [(1, 0)], q=q, v=v)
     with pytest.raises(ValueError):
         oracle.conv1d_bwd_dk(u, gy, [3], q=q, v=v)
+
+
+@pytest.mark.parametrize("gated", [True, False])
+def test_points_match_rows_bitwise(gated):
+    """The single-position gradients sum exactly as the row and channel versions do."""
+    B, H, N = 3, 2, 64
+    u, q, v, k, D, gy = _draw(B, H, N, seed=91, gated=gated)
+    rows = [(b, h) for b in range(B) for h in range(H)]
+    du, dq, dv = oracle.conv1d_bwd_rows(u, k, D, gy, rows, q=q, v=v)
+    dk, dD = oracle.conv1d_bwd_dk(u, gy, list(range(H)), q=q, v=v)
+    rng = np.random.default_rng(5)
+    pts = np.stack([rng.integers(0, B, 200), rng.integers(0, H, 200), rng.integers(0, N, 200)], 1)
+    pts[:4] = [(0, 0, 0), (B - 1, H - 1, N - 1), (1, 0, N - 2), (2, 1, 1)]
+    pu, pq, pv = oracle.conv1d_bwd_points(u, k, D, gy, pts, q=q, v=v)
+    idx = pts[:, 0] * H + pts[:, 1]
+    assert np.array_equal(pu, du[idx, pts[:, 2]])
+    if gated:
+        assert np.array_equal(pq, dq[idx, pts[:, 2]]) and np.array_equal(pv, dv[idx, pts[:, 2]])
+    else:
+        assert pq is None and pv is None
+    kp = np.stack([rng.integers(0, H, 100), rng.integers(0, N, 100)], 1)
+    kp[:2] = [(0, 0), (H - 1, N - 1)]
+    pk = oracle.conv1d_bwd_dk_points(u, gy, kp, q=q, v=v)
+    assert np.array_equal(pk, dk[kp[:, 0], kp[:, 1]])
+    assert np.array_equal(oracle.conv1d_bwd_dk_points(u, gy, [(h, 0) for h in range(H)], q=q, v=v), dD)
