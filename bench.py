@@ -230,11 +230,15 @@ def time_backward(lconv, wl, spec, u, kf, D, q, v, args):
     dtc = lconv.dtype_code(u.dtype)
     stream = torch.cuda.current_stream()
     p = lambda t: None if t is None else t.data_ptr()
+    wsb = lconv.lconv_fftconv_bwd_workspace_bytes(spec.B, spec.H, spec.N, dtc)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    fwsb = lconv.lconv_fftconv_workspace_bytes(spec.B, spec.H, spec.N, dtc)
+    fws = torch.empty(max(fwsb, 1), dtype=torch.uint8, device="cuda")
 
     def call():
         st = lconv.lconv_fftconv_bwd(dy.data_ptr(), u.data_ptr(), kf.data_ptr(), D.data_ptr(), p(q),
                                      p(v), du.data_ptr(), p(dq), p(dv), dk.data_ptr(), dD.data_ptr(),
-                                     spec.B, spec.H, spec.N, dtc, stream.cuda_stream)
+                                     spec.B, spec.H, spec.N, dtc, ws.data_ptr(), wsb, stream.cuda_stream)
         if st != 0:
             raise lconv.LconvError(st, "lconv_fftconv_bwd")
     for _ in range(args.warmup):
@@ -253,8 +257,12 @@ def time_backward(lconv, wl, spec, u, kf, D, q, v, args):
     out = {"ms_per_call": round(ms, 5), "algorithmic_bytes": nbytes, "achieved": round(gbs, 2),
            "unit": "GB/s", "peak": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
            "outputs": "du, dq, dv (dtype); dk, dD (fp32)",
-           "launches": "forward kernel gated by dy (dv); adjoint kernel (du, dq); "
-                       "filter-gradient kernel (dk, dD)"}
+           "launches": ("forward kernel gated by dy (dv); adjoint kernel (du, dq); "
+                        "filter-gradient kernel (dk, dD)") if spec.N <= 4096 else
+                       ("multi-pass forward gated by dy (dv); rev(dy v); multi-pass forward of it "
+                        "(dx); du, dq; filter spectra of the rows q u; multi-pass forward of rev(dy v) "
+                        "with them; batch sum (dk, dD)"),
+           "workspace_bytes": wsb}
     if v is not None:
         # the training pair: the forward that also saves the pre-gate output c, and the gradient
         # that takes dv = dy * c from it (one elementwise pass instead of the dy-gated transform)
@@ -264,14 +272,15 @@ def time_backward(lconv, wl, spec, u, kf, D, q, v, args):
         def fwd_save():
             st = lconv.lconv_fftconv_fwd_save(u.data_ptr(), kf.data_ptr(), D.data_ptr(), y.data_ptr(),
                                               c.data_ptr(), p(q), p(v), spec.B, spec.H, spec.N, dtc,
-                                              stream.cuda_stream)
+                                              fws.data_ptr(), fwsb, stream.cuda_stream)
             if st != 0:
                 raise lconv.LconvError(st, "lconv_fftconv_fwd_save")
 
         def bwd_saved():
             st = lconv.lconv_fftconv_bwd_saved(dy.data_ptr(), u.data_ptr(), kf.data_ptr(), D.data_ptr(), p(q),
                                                p(v), c.data_ptr(), du.data_ptr(), p(dq), p(dv), dk.data_ptr(),
-                                               dD.data_ptr(), spec.B, spec.H, spec.N, dtc, stream.cuda_stream)
+                                               dD.data_ptr(), spec.B, spec.H, spec.N, dtc, ws.data_ptr(), wsb,
+                                               stream.cuda_stream)
             if st != 0:
                 raise lconv.LconvError(st, "lconv_fftconv_bwd_saved")
 
@@ -515,7 +524,7 @@ def main():
         mf = float(cs["mfma_gflop_executed_per_launch"]) * 1e9 / (avg_ms * 1e-3) / 1e12
         out["mfma"] = {"executed_tflops": round(mf, 1), "peak": MFMA_PEAK[dt],
                        "util": round(mf / MFMA_PEAK[dt], 4), "counters": cs["path"]}
-    if not args.no_bwd and spec.kind == "1d" and spec.N <= 4096 and not spec.L and args.keep is None \
+    if not args.no_bwd and spec.kind == "1d" and spec.N % 8 == 0 and not spec.L and args.keep is None \
             and not spec.name.startswith("ssm_"):
         out["backward"] = time_backward(lconv, wl, spec, u, kf, D, q, v, args)
     if not args.no_cpu and spec.kind == "1d" and not spec.name.startswith("ssm_"):

@@ -367,7 +367,7 @@ extern "C" {
 
 int lconv_freq_blocks(int64_t N) {
     Plan1D p;
-    if (!n_supported(N) || N > LCONV_BWD_MAX_N || !make_plan_1d(N, &p) || p.multipass) return 0;
+    if (!n_supported(N) || !make_plan_1d(N, &p) || p.multipass) return 0;
     return p.R;
 }
 
@@ -486,9 +486,91 @@ namespace {
 
 // The gradient call; with c (the forward's saved pre-gate output) dv = dy (.) c replaces the
 // forward-by-dy launch.
+// Workspace of the gradient for sequences past one workgroup (zero otherwise), in 256-byte
+// aligned parts: the forward call's chunk workspace (for [B][H] and for [1][B*H] rows), rev(ds),
+// the forward results, x = q (.) u, the rows' spectra with their transform workspace, and the
+// zero skip of the row filters.
+struct BwdLongLayout {
+    size_t fws, ds, t, xs, kf, kfws, zd;
+    size_t o_ds, o_t, o_xs, o_kf, o_kfws, o_zd, total;
+};
+
+bool bwd_long_layout(int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype, BwdLongLayout* L) {
+    int64_t rows, elems;
+    if (!mul_ok(B, H, &rows) || !mul_ok(rows, N, &elems) || rows == 0) return false;
+    const size_t es = dtype_size(dtype), act = round256((size_t)elems * es);
+    const size_t f1 = fwd_workspace_bytes(B, H, N, dtype, kChunkTarget);
+    const size_t f2 = fwd_workspace_bytes(1, rows, N, dtype, kChunkTarget);
+    const size_t kf = lconv_filter_fft_bytes(rows, N, dtype);
+    if (f1 == SIZE_MAX || f2 == SIZE_MAX || kf == 0) return false;
+    L->fws = round256(f1 > f2 ? f1 : f2);
+    L->ds = L->t = L->xs = act;
+    L->kf = round256(kf);
+    L->kfws = round256(lconv_filter_fft_workspace_bytes(rows, N, dtype));
+    L->zd = round256((size_t)rows * es);
+    L->o_ds = L->fws;
+    L->o_t = L->o_ds + L->ds;
+    L->o_xs = L->o_t + L->t;
+    L->o_kf = L->o_xs + L->xs;
+    L->o_kfws = L->o_kf + L->kf;
+    L->o_zd = L->o_kfws + L->kfws;
+    L->total = L->o_zd + L->zd;
+    return true;
+}
+
+// The gradient of a long sequence through the multi-pass forward call.  Reversing a row turns a
+// correlation over later positions into a causal convolution:
+//   dx = rev(k * rev(ds)) + D ds            (ds = dy (.) v);  du = q (.) dx, dq = u (.) dx
+//   dk[h][t] = sum_b (x_b * rev(ds_b))[N-1-t]   with x_b = q (.) u the filter of row b
+// so every transform is the forward path's; the reversals and gates are elementwise passes.
+lconv_status_t bwd_long(const void* dy, const void* u, const void* k_f, const void* D, const void* q,
+                        const void* v, const void* c, void* du, void* dq, void* dv, float* dk, float* dD,
+                        int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype, void* workspace,
+                        hipStream_t stream) {
+    BwdLongLayout L;
+    bwd_long_layout(B, H, N, dtype, &L);
+    char* w = (char*)workspace;
+    void *fws = w, *ds = w + L.o_ds, *t = w + L.o_t, *xs = w + L.o_xs, *kf = w + L.o_kf, *kfws = w + L.o_kfws,
+         *zd = w + L.o_zd;
+    const int ct = dtype == LCONV_F32 ? CT_F32 : (int)dtype;
+    const int64_t rows = B * H, elems = rows * N;
+    lconv_status_t st;
+    // dv = dy (.) (k * x + D x)
+    if (v && c) {
+        if (launch_mul_rows(dy, c, dv, elems, ct, stream) != hipSuccess) return LCONV_ERR_HIP;
+    } else if (v) {
+        st = fftconv_fwd_call(u, k_f, D, dv, q, dy, B, H, N, dtype, fws, L.fws, kChunkTarget, true, stream);
+        if (st != LCONV_SUCCESS) return st;
+    }
+    // rev(ds), then t = k * rev(ds) + D rev(ds), then du = q (.) rev(t), dq = u (.) rev(t)
+    if (launch_rev_gate(dy, v, ds, rows, N, ct, stream) != hipSuccess) return LCONV_ERR_HIP;
+    st = fftconv_fwd_call(ds, k_f, D, t, nullptr, nullptr, B, H, N, dtype, fws, L.fws, kChunkTarget, true, stream);
+    if (st != LCONV_SUCCESS) return st;
+    if (launch_rev_gated_out(t, q, q ? u : nullptr, du, q ? dq : nullptr, rows, N, ct, stream) != hipSuccess)
+        return LCONV_ERR_HIP;
+    // dk, dD: each row's x as a filter of its own (B*H channels of one row each), applied to
+    // rev(ds) with a zero skip, then reversed and summed over the batch
+    if (dk || dD) {
+        const void* x = u;
+        if (q) {
+            if (launch_mul_rows(q, u, xs, elems, ct, stream) != hipSuccess) return LCONV_ERR_HIP;
+            x = xs;
+        }
+        st = lconv_filter_fft(x, kf, rows, N, dtype, kfws, L.kfws, stream);
+        if (st != LCONV_SUCCESS) return st;
+        if (launch_zero_words(zd, (int64_t)(L.zd / 4), stream) != hipSuccess) return LCONV_ERR_HIP;
+        st = fftconv_fwd_call(ds, kf, zd, t, nullptr, nullptr, 1, rows, N, dtype, fws, L.fws, kChunkTarget, true,
+                              stream);
+        if (st != LCONV_SUCCESS) return st;
+        if (launch_rev_batch_sum(t, dk, dD, B, H, N, ct, stream) != hipSuccess) return LCONV_ERR_HIP;
+    }
+    return LCONV_SUCCESS;
+}
+
 lconv_status_t bwd_impl(const void* dy, const void* u, const void* k_f, const void* D, const void* q,
                         const void* v, const void* c, void* du, void* dq, void* dv, float* dk, float* dD,
-                        int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype, hipStream_t stream) {
+                        int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
     if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
     if (B < 0 || H < 0 || N < 0) return LCONV_ERR_INVALID_SHAPE;
     int64_t elems, t, hn;
@@ -496,7 +578,7 @@ lconv_status_t bwd_impl(const void* dy, const void* u, const void* k_f, const vo
         !mul_ok(hn, 8, &t))
         return LCONV_ERR_INVALID_SHAPE;
     if (H == 0 || N == 0) return LCONV_SUCCESS;
-    if (!n_supported(N) || N > LCONV_BWD_MAX_N) return LCONV_ERR_UNSUPPORTED;
+    if (!n_supported(N)) return LCONV_ERR_UNSUPPORTED;
     if (!q) dq = nullptr;  // ignored without the gate it belongs to
     if (!v) dv = nullptr;
     if (B == 0) {          // empty batch: the filter gradients are zero sums
@@ -526,6 +608,17 @@ lconv_status_t bwd_impl(const void* dy, const void* u, const void* k_f, const vo
     }
     Plan1D p;
     make_plan_1d(N, &p);
+    if (p.multipass) {
+        const size_t need = lconv_fftconv_bwd_workspace_bytes(B, H, N, dtype);
+        if (need == 0) return LCONV_ERR_INVALID_SHAPE;
+        if (!workspace || workspace_bytes < need) return LCONV_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return LCONV_ERR_MISALIGNED;
+        for (int i = 0; i < 7; ++i)
+            if (overlap(workspace, need, ins[i], in_sz[i])) return LCONV_ERR_ALIASING;
+        for (int o = 0; o < 5; ++o)
+            if (overlap(workspace, need, outs[o], out_sz[o])) return LCONV_ERR_ALIASING;
+        return bwd_long(dy, u, k_f, D, q, v, c, du, dq, dv, dk, dD, B, H, N, dtype, workspace, stream);
+    }
     hipError_t err = hipSuccess;
     const int cus = device_cu_count(&err);
     if (!cus) return LCONV_ERR_HIP;
@@ -568,29 +661,41 @@ lconv_status_t bwd_impl(const void* dy, const void* u, const void* k_f, const vo
 
 extern "C" {
 
+size_t lconv_fftconv_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype) {
+    Plan1D p;
+    if (!dtype_ok(dtype) || B < 0 || H < 0 || !n_supported(N) || !make_plan_1d(N, &p)) return 0;
+    if (!p.multipass || B == 0 || H == 0) return 0;
+    BwdLongLayout L;
+    return bwd_long_layout(B, H, N, dtype, &L) ? L.total : 0;
+}
+
 lconv_status_t lconv_fftconv_bwd(const void* dy, const void* u, const void* k_f, const void* D, const void* q,
                                  const void* v, void* du, void* dq, void* dv, float* dk, float* dD, int64_t B,
-                                 int64_t H, int64_t N, lconv_dtype_t dtype, hipStream_t stream) {
-    return bwd_impl(dy, u, k_f, D, q, v, nullptr, du, dq, dv, dk, dD, B, H, N, dtype, stream);
+                                 int64_t H, int64_t N, lconv_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+    return bwd_impl(dy, u, k_f, D, q, v, nullptr, du, dq, dv, dk, dD, B, H, N, dtype, workspace, workspace_bytes,
+                    stream);
 }
 
 lconv_status_t lconv_fftconv_bwd_saved(const void* dy, const void* u, const void* k_f, const void* D,
                                        const void* q, const void* v, const void* c, void* du, void* dq, void* dv,
                                        float* dk, float* dD, int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype,
-                                       hipStream_t stream) {
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!c && v && B > 0 && H > 0 && N > 0) return LCONV_ERR_NULL_POINTER;
-    return bwd_impl(dy, u, k_f, D, q, v, c, du, dq, dv, dk, dD, B, H, N, dtype, stream);
+    return bwd_impl(dy, u, k_f, D, q, v, c, du, dq, dv, dk, dD, B, H, N, dtype, workspace, workspace_bytes,
+                    stream);
 }
 
 lconv_status_t lconv_fftconv_fwd_save(const void* u, const void* k_f, const void* D, void* y, void* c,
                                       const void* q, const void* v, int64_t B, int64_t H, int64_t N,
-                                      lconv_dtype_t dtype, hipStream_t stream) {
+                                      lconv_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
     if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
     if (B < 0 || H < 0 || N < 0) return LCONV_ERR_INVALID_SHAPE;
     int64_t elems, t;
     if (!mul_ok(B, H, &t) || !mul_ok(t, N, &elems) || !mul_ok(elems, 8, &t)) return LCONV_ERR_INVALID_SHAPE;
     if (B == 0 || H == 0 || N == 0) return LCONV_SUCCESS;
-    if (!n_supported(N) || N > LCONV_BWD_MAX_N) return LCONV_ERR_UNSUPPORTED;
+    if (!n_supported(N)) return LCONV_ERR_UNSUPPORTED;
     if (!u || !k_f || !D || !y || !c) return LCONV_ERR_NULL_POINTER;
     const void* ptrs[] = {u, k_f, D, y, c, q, v};
     for (const void* p : ptrs)
@@ -605,6 +710,21 @@ lconv_status_t lconv_fftconv_fwd_save(const void* u, const void* k_f, const void
     if (overlap(y, act, c, act)) return LCONV_ERR_ALIASING;
     Plan1D p;
     make_plan_1d(N, &p);
+    if (p.multipass) {
+        // the multi-pass forward without the post-gate gives c; y = v (.) c (or a copy of c)
+        const size_t need = lconv_fftconv_workspace_bytes(B, H, N, dtype);
+        if (!workspace || workspace_bytes < need) return LCONV_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return LCONV_ERR_MISALIGNED;
+        for (int i = 0; i < 5; ++i)
+            if (overlap(workspace, need, ins[i], in_sz[i])) return LCONV_ERR_ALIASING;
+        if (overlap(workspace, need, y, act) || overlap(workspace, need, c, act)) return LCONV_ERR_ALIASING;
+        const lconv_status_t st = fftconv_fwd_call(u, k_f, D, c, q, nullptr, B, H, N, dtype, workspace,
+                                                   workspace_bytes, kChunkTarget, true, stream);
+        if (st != LCONV_SUCCESS) return st;
+        const int ctv = dtype == LCONV_F32 ? CT_F32 : (int)dtype;
+        if (v) return hip_status(launch_mul_rows(c, v, y, elems, ctv, stream));
+        return hip_status(hipMemcpyAsync(y, c, act, hipMemcpyDeviceToDevice, stream));
+    }
     hipError_t err = hipSuccess;
     const int cus = device_cu_count(&err);
     if (!cus) return LCONV_ERR_HIP;

@@ -54,9 +54,10 @@ def load(path: str = LIB_PATH):
         "lconv_fftconv2d_workspace_bytes": (sz, [i64, i64, i64, i64, i]),
         "lconv_filter_fft": (i, [vp, vp, i64, i64, i, vp, sz, vp]),
         "lconv_fftconv_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i, vp, sz, vp]),
-        "lconv_fftconv_bwd": (i, [vp] * 11 + [i64, i64, i64, i, vp]),
-        "lconv_fftconv_fwd_save": (i, [vp] * 7 + [i64, i64, i64, i, vp]),
-        "lconv_fftconv_bwd_saved": (i, [vp] * 12 + [i64, i64, i64, i, vp]),
+        "lconv_fftconv_bwd_workspace_bytes": (sz, [i64, i64, i64, i]),
+        "lconv_fftconv_bwd": (i, [vp] * 11 + [i64, i64, i64, i, vp, sz, vp]),
+        "lconv_fftconv_fwd_save": (i, [vp] * 7 + [i64, i64, i64, i, vp, sz, vp]),
+        "lconv_fftconv_bwd_saved": (i, [vp] * 12 + [i64, i64, i64, i, vp, sz, vp]),
         "lconv_fftconv_partial_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i, vp]),
         "lconv_fftconv_sparse_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_uint32, i, vp]),
         "lconv_freq_blocks": (i, [i64]),
@@ -131,16 +132,25 @@ def lconv_fftconv_fwd_noalloc(u, k_f, D, y, q, v, B, H, N, dtype, stream):
     return load().lconv_fftconv_fwd_noalloc(u, k_f, D, y, q, v, B, H, N, dtype, stream)
 
 
-def lconv_fftconv_bwd(dy, u, k_f, D, q, v, du, dq, dv, dk, dD, B, H, N, dtype, stream):
-    return load().lconv_fftconv_bwd(dy, u, k_f, D, q, v, du, dq, dv, dk, dD, B, H, N, dtype, stream)
+def lconv_fftconv_bwd_workspace_bytes(B, H, N, dtype):
+    return load().lconv_fftconv_bwd_workspace_bytes(B, H, N, dtype)
 
 
-def lconv_fftconv_fwd_save(u, k_f, D, y, c, q, v, B, H, N, dtype, stream):
-    return load().lconv_fftconv_fwd_save(u, k_f, D, y, c, q, v, B, H, N, dtype, stream)
+def lconv_fftconv_bwd(dy, u, k_f, D, q, v, du, dq, dv, dk, dD, B, H, N, dtype, workspace, workspace_bytes,
+                      stream):
+    return load().lconv_fftconv_bwd(dy, u, k_f, D, q, v, du, dq, dv, dk, dD, B, H, N, dtype, workspace,
+                                    workspace_bytes, stream)
 
 
-def lconv_fftconv_bwd_saved(dy, u, k_f, D, q, v, c, du, dq, dv, dk, dD, B, H, N, dtype, stream):
-    return load().lconv_fftconv_bwd_saved(dy, u, k_f, D, q, v, c, du, dq, dv, dk, dD, B, H, N, dtype, stream)
+def lconv_fftconv_fwd_save(u, k_f, D, y, c, q, v, B, H, N, dtype, workspace, workspace_bytes, stream):
+    return load().lconv_fftconv_fwd_save(u, k_f, D, y, c, q, v, B, H, N, dtype, workspace, workspace_bytes,
+                                         stream)
+
+
+def lconv_fftconv_bwd_saved(dy, u, k_f, D, q, v, c, du, dq, dv, dk, dD, B, H, N, dtype, workspace,
+                            workspace_bytes, stream):
+    return load().lconv_fftconv_bwd_saved(dy, u, k_f, D, q, v, c, du, dq, dv, dk, dD, B, H, N, dtype,
+                                          workspace, workspace_bytes, stream)
 
 
 def lconv_fftconv_partial_fwd(u, k_f, D, y, q, v, B, H, N, L, dtype, stream):
@@ -349,14 +359,16 @@ def fftconv(u, k_f, D, q=None, v=None, out=None, stream=None):
 
 def fftconv_save(u, k_f, D, q=None, v=None, stream=None):
     """(y, c): y = v * c with the pre-gate output c = (k * (q*u))[:N] + D * (q*u), for the
-    gradient call (N <= 4096)."""
+    gradient call."""
     torch = _torch()
     B, H, N = _gated_inputs(u, k_f, D, q, v, None)
     dt = dtype_code(u.dtype)
     y = torch.empty_like(u)
     c = torch.empty_like(u)
+    wsb = lconv_fftconv_workspace_bytes(B, H, N, dt)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=u.device) if wsb else None
     _check(lconv_fftconv_fwd_save(_ptr(u), _ptr(k_f), _ptr(D), _ptr(y), _ptr(c), _ptr(q), _ptr(v),
-                                  B, H, N, dt, _stream(stream)), "lconv_fftconv_fwd_save")
+                                  B, H, N, dt, _ptr(ws), wsb, _stream(stream)), "lconv_fftconv_fwd_save")
     return y, c
 
 
@@ -376,14 +388,16 @@ def fftconv_bwd(dy, u, k_f, D, q=None, v=None, need_dk=True, c=None, stream=None
     dv = torch.empty_like(u) if v is not None else None
     dk = torch.empty((H, N), dtype=torch.float32, device=u.device) if need_dk else None
     dD = torch.empty((H,), dtype=torch.float32, device=u.device) if need_dk else None
+    wsb = lconv_fftconv_bwd_workspace_bytes(B, H, N, dt)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=u.device) if wsb else None
     if c is None:
         _check(lconv_fftconv_bwd(_ptr(dy), _ptr(u), _ptr(k_f), _ptr(D), _ptr(q), _ptr(v), _ptr(du),
-                                 _ptr(dq), _ptr(dv), _ptr(dk), _ptr(dD), B, H, N, dt, _stream(stream)),
-               "lconv_fftconv_bwd")
+                                 _ptr(dq), _ptr(dv), _ptr(dk), _ptr(dD), B, H, N, dt, _ptr(ws), wsb,
+                                 _stream(stream)), "lconv_fftconv_bwd")
     else:
         _check(lconv_fftconv_bwd_saved(_ptr(dy), _ptr(u), _ptr(k_f), _ptr(D), _ptr(q), _ptr(v), _ptr(c),
                                        _ptr(du), _ptr(dq), _ptr(dv), _ptr(dk), _ptr(dD), B, H, N, dt,
-                                       _stream(stream)), "lconv_fftconv_bwd_saved")
+                                       _ptr(ws), wsb, _stream(stream)), "lconv_fftconv_bwd_saved")
     return du, dq, dv, dk, dD
 
 

@@ -50,8 +50,9 @@ extern "C" {
 /* Bumped when entry points are added or a size query's result changes (3: the training pair
  * lconv_fftconv_fwd_save / lconv_fftconv_bwd_saved; the state-space workspace holds the scan's
  * part states.  4: lconv_prepare and lconv_fftconv_fwd_noalloc, two status codes.  5: 2D calls
- * take Hs x Ws images and a workspace; lconv_fftconv2d_workspace_bytes). */
-#define LCONV_ABI_VERSION 5
+ * take Hs x Ws images and a workspace; lconv_fftconv2d_workspace_bytes.  6: gradients and the
+ * training pair for every supported N, with workspace arguments). */
+#define LCONV_ABI_VERSION 6
 
 typedef enum { LCONV_F32 = 0, LCONV_F16 = 1, LCONV_BF16 = 2 } lconv_dtype_t;
 
@@ -175,8 +176,9 @@ lconv_status_t lconv_fftconv_partial_fwd(const void* u, const void* k_f, const v
 
 /*
  * Gradients of the gated causal convolution above, given dy = dL/dy (the training path the
- * FlashFFTConv abstract reports speed-ups for; the FFT convolution is exact, so its gradient is
- * that of the plain causal sum).  With x = q (.) u and ds = dy (.) v:
+ * FlashFFTConv abstract reports speed-ups for, and the 64K-long training of the "Simple
+ * Hardware-Efficient Long Convolutions" abstract; the FFT convolution is exact, so its gradient
+ * is that of the plain causal sum).  With x = q (.) u and ds = dy (.) v:
  *   dx[t] = sum_{s >= t} k[h,s-t] ds[s] + D[h] ds[t]     (correlation: conjugate spectrum)
  *   du = q (.) dx   (du = dx without q)          dq = u (.) dx
  *   dv = dy (.) ( (k * x)[:N] + D x )            (the forward convolution, gated by dy)
@@ -189,43 +191,54 @@ lconv_status_t lconv_fftconv_partial_fwd(const void* u, const void* k_f, const v
  *   dv        [B][H][N] dtype, written; required when v is given, ignored (may be NULL) otherwise
  *   dk        [H][N] fp32, written (overwritten, not accumulated); NULL: not computed
  *   dD        [H] fp32, written; NULL: not computed
- * B = 0 writes zeros to dk and dD.  Outputs must not overlap each other or any input.
- * Arithmetic as in the forward call; dk and dD are summed over the batch in fp32 in the
- * frequency domain and transformed once per channel.
- * Supported: N <= 4096 (transform length M <= 8192, one workgroup per transform), N a multiple
- * of 8; longer sequences return LCONV_ERR_UNSUPPORTED.  No workspace.
+ *   workspace lconv_fftconv_bwd_workspace_bytes(B, H, N, dtype) bytes (0, may be NULL, for
+ *             N <= 4096)
+ * B = 0 writes zeros to dk and dD.  Outputs must not overlap each other, any input or the
+ * workspace.
+ * N <= 4096 (one workgroup per transform): three fused launches; dk and dD are summed over the
+ * batch in fp32 in the frequency domain and transformed once per channel.
+ * 4096 < N <= LCONV_MAX_N: the correlations become causal convolutions of time-reversed rows,
+ *   dx = rev(k * rev(ds)) + D ds,   dk[h,t] = sum_b (x_b * rev(ds_b))[N-1-t],
+ * each run through the chunked multi-pass forward path (x_b as the filter of its own row), with
+ * the reversals, gates and the batch sum as elementwise passes.  rev(ds) and the convolution
+ * results pass through the workspace in dtype (one rounding each for 16-bit types).
+ * Supported: N a multiple of 8, N <= LCONV_MAX_N.
  */
+size_t lconv_fftconv_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype);
 lconv_status_t lconv_fftconv_bwd(const void* dy, const void* u, const void* k_f, const void* D,
                                  const void* q, const void* v, void* du, void* dq, void* dv,
                                  float* dk, float* dD, int64_t B, int64_t H, int64_t N,
-                                 lconv_dtype_t dtype, hipStream_t stream);
-
-/* Largest sequence length lconv_fftconv_bwd supports. */
-#define LCONV_BWD_MAX_N ((int64_t)4096)
+                                 lconv_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
 
 /*
  * Forward call for training: lconv_fftconv_fwd that also writes the pre-gate output
  *   c = (k * x)[:N] + D x        (y = v (.) c; c = y when v is NULL)
  * which the gradient of v needs (dv = dy (.) c, the same quantity lconv_fftconv_bwd otherwise
  * recomputes with a forward transform).
- *   c  [B][H][N] dtype, device, written; must not overlap y or any input
- * Other arguments as for lconv_fftconv_fwd.  Supported: N <= LCONV_BWD_MAX_N, N a multiple of 8.
+ *   c          [B][H][N] dtype, device, written; must not overlap y or any input
+ *   workspace  lconv_fftconv_workspace_bytes(B, H, N, dtype) bytes, as for lconv_fftconv_fwd
+ * N <= 4096: c is stored by the fused kernel beside y.  Longer: the multi-pass forward writes c
+ * and one elementwise pass gives y = v (.) c.  Other arguments as for lconv_fftconv_fwd.
+ * Supported: N a multiple of 8, N <= LCONV_MAX_N.
  */
 lconv_status_t lconv_fftconv_fwd_save(const void* u, const void* k_f, const void* D, void* y, void* c,
                                       const void* q, const void* v, int64_t B, int64_t H, int64_t N,
-                                      lconv_dtype_t dtype, hipStream_t stream);
+                                      lconv_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
 
 /*
  * lconv_fftconv_bwd with the pre-gate output c saved by lconv_fftconv_fwd_save: dv = dy (.) c
  * (one elementwise pass) instead of the forward transform gated by dy; du, dq, dk, dD as there.
  *   c  [B][H][N] dtype, device, as written by lconv_fftconv_fwd_save on the same u, q, k_f, D;
  *      required when v is given (LCONV_ERR_NULL_POINTER otherwise), ignored without v.
- * Other arguments, outputs and limits as for lconv_fftconv_bwd.
+ * Other arguments, outputs, workspace and limits as for lconv_fftconv_bwd.
  */
 lconv_status_t lconv_fftconv_bwd_saved(const void* dy, const void* u, const void* k_f, const void* D,
                                        const void* q, const void* v, const void* c, void* du, void* dq,
                                        void* dv, float* dk, float* dD, int64_t B, int64_t H, int64_t N,
-                                       lconv_dtype_t dtype, hipStream_t stream);
+                                       lconv_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
 
 /* ---- 2D (HyenaND-style) ------------------------------------------------------------------ */
 

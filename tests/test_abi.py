@@ -27,7 +27,7 @@ def test_exports_every_header_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lconv.lconv_abi_version() == 5
+    assert lconv.lconv_abi_version() == 6
     for s in range(10):
         assert lconv.status_string(s)
     assert "unknown" in lconv.status_string(99)
@@ -147,8 +147,8 @@ G = [0x10000000 + 0x100000 * i for i in range(12)]
 
 
 def bwd(dy=G[0], u=G[1], kf=G[2], D=G[3], q=None, v=None, du=G[4], dq=None, dv=None, dk=None,
-        dD=None, B=2, H=3, N=64, dt=BF16):
-    return lconv.lconv_fftconv_bwd(dy, u, kf, D, q, v, du, dq, dv, dk, dD, B, H, N, dt, None)
+        dD=None, B=2, H=3, N=64, dt=BF16, ws=None, wsb=0):
+    return lconv.lconv_fftconv_bwd(dy, u, kf, D, q, v, du, dq, dv, dk, dD, B, H, N, dt, ws, wsb, None)
 
 
 def test_bwd_validation_errors():
@@ -156,7 +156,17 @@ def test_bwd_validation_errors():
     assert bwd(B=-1) == SHAPE
     assert bwd(H=2 ** 40, N=2 ** 30) == SHAPE                           # overflow
     assert bwd(N=12) == UNSUP
-    assert bwd(N=8192) == UNSUP                                            # beyond one workgroup
+    assert bwd(N=2 ** 22 + 8) == UNSUP
+    # beyond one workgroup: the multi-pass gradient needs its workspace (fake addresses far apart)
+    far = [1 << 40 + i for i in range(8)]
+    big = dict(dy=far[0], u=far[1], kf=far[2], D=far[3], du=far[4], N=8192)
+    need = lconv.lconv_fftconv_bwd_workspace_bytes(2, 3, 8192, BF16)
+    assert need > 0
+    assert bwd(**big) == WSERR
+    assert bwd(**big, ws=far[5], wsb=need - 1) == WSERR
+    assert bwd(**big, ws=far[5] + 8, wsb=need) == MISAL
+    assert bwd(**big, ws=far[1], wsb=need) == ALIAS                        # workspace over u
+    assert bwd(**big, ws=far[4] - 256, wsb=need) == ALIAS                  # workspace over du
     assert bwd(dy=None) == NULLP
     assert bwd(u=None) == NULLP
     assert bwd(kf=None) == NULLP
@@ -185,20 +195,23 @@ def test_bwd_empty_and_ignored_outputs():
         assert bwd(dq=G[0]) == HIPERR
 
 
-def fsave(u=G[0], kf=G[1], D=G[2], y=G[3], c=G[4], q=None, v=None, B=2, H=3, N=64, dt=BF16):
-    return lconv.lconv_fftconv_fwd_save(u, kf, D, y, c, q, v, B, H, N, dt, None)
+def fsave(u=G[0], kf=G[1], D=G[2], y=G[3], c=G[4], q=None, v=None, B=2, H=3, N=64, dt=BF16, ws=None,
+          wsb=0):
+    return lconv.lconv_fftconv_fwd_save(u, kf, D, y, c, q, v, B, H, N, dt, ws, wsb, None)
 
 
 def bsaved(dy=G[0], u=G[1], kf=G[2], D=G[3], q=None, v=None, c=None, du=G[4], dq=None, dv=None,
            dk=None, dD=None, B=2, H=3, N=64, dt=BF16):
-    return lconv.lconv_fftconv_bwd_saved(dy, u, kf, D, q, v, c, du, dq, dv, dk, dD, B, H, N, dt, None)
+    return lconv.lconv_fftconv_bwd_saved(dy, u, kf, D, q, v, c, du, dq, dv, dk, dD, B, H, N, dt, None, 0,
+                                         None)
 
 
 def test_forward_save_validation_errors():
     assert fsave(dt=5) == UNSUP
     assert fsave(B=-1) == SHAPE
     assert fsave(N=12) == UNSUP                                            # N % 8
-    assert fsave(N=8192) == UNSUP                                          # single transform only
+    far = [1 << 40 + i for i in range(6)]
+    assert fsave(u=far[0], kf=far[1], D=far[2], y=far[3], c=far[4], N=8192) == WSERR   # multi-pass: workspace
     assert fsave(c=None) == NULLP
     assert fsave(y=None) == NULLP
     assert fsave(c=G[4] + 8) == MISAL
@@ -213,7 +226,7 @@ def test_saved_gradient_validation_errors():
     assert bsaved(v=G[6], dv=G[7], c=G[8] + 4) == MISAL
     assert bsaved(v=G[6], dv=G[7], c=G[4]) == ALIAS                        # du overlaps c
     assert bsaved(v=G[6], dv=G[8], c=G[8]) == ALIAS                        # dv == c
-    assert bsaved(N=8192) == UNSUP
+    assert bsaved(N=8192) == WSERR                                         # multi-pass: workspace
     assert bsaved(B=0) == OK
     import torch
     if not torch.cuda.is_available():                                      # c ignored without v

@@ -151,8 +151,121 @@ def test_bwd_empty_batch_zeroes_filter_gradient(lc):
     dk = torch.full((H, N), 7.0, device="cuda")
     dD = torch.full((H,), 7.0, device="cuda")
     st = lc.lconv_fftconv_bwd(None, None, None, None, None, None, None, None, None,
-                              dk.data_ptr(), dD.data_ptr(), 0, H, N, lc.BF16,
+                              dk.data_ptr(), dD.data_ptr(), 0, H, N, lc.BF16, None, 0,
                               torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert st == 0
     assert float(dk.abs().max()) == 0.0 and float(dD.abs().max()) == 0.0
+
+
+# ---- sequences past one workgroup: the multi-pass gradient ----------------------------------
+
+LONG_N = [8192, 16384, 40960]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("N", LONG_N)
+@pytest.mark.parametrize("B,gates", [(3, "qv"), (2, ""), (1, "q")])
+def test_bwd_long_full(lc, nthreads, dtype, N, B, gates):
+    """N > 4096 (chunked multi-pass transforms): every row of du, dq, dv and every channel of
+    dk, dD against the oracle."""
+    H = 2
+    spec = wl.spec_1d(B, H, N, dtype, gated=True, seed=700 + N + B, decay=1e-4)
+    say(f"[bwd long] dtype={dtype} B={B} H={H} N={N} gates={gates!r} seed={spec.seed}")
+    d, dy, q, v = inputs(spec, gates)
+    du, dq, dv, dk, dD = run_bwd(lc, d, dy, q, v)
+    rows = [(b, h) for b in range(B) for h in range(H)]
+    errs = check_rows((du, dq, dv), d, dy, q, v, rows, nthreads)
+    errs.update(check_dk(dk, dD, d, dy, q, v, list(range(H)), nthreads))
+    say("   " + " ".join(f"{k}={e:.3e}" for k, e in errs.items()) + f" (tol {TOL[dtype]})")
+    for k, e in errs.items():
+        assert e <= TOL[dtype], (k, e)
+
+
+def _sampled_bwd(lc, nthreads, d, dy, q, v, n_pts=768, n_dk=192, seed=0):
+    """Pooled relative L2 of du, dq, dv at sampled (b,h,t) and of dk at sampled (h,tau), with the
+    first and last positions of rows and of multi-pass chunk boundaries always included."""
+    spec = d["spec"]
+    B, H, N, dt = spec.B, spec.H, spec.N, spec.dtype
+    du, dq, dv, dk, dD = run_bwd(lc, d, dy, q, v)
+    rng = np.random.default_rng(seed)
+    pts = np.stack([rng.integers(0, B, n_pts), rng.integers(0, H, n_pts), rng.integers(0, N, n_pts)], 1)
+    special = [0, 1, N - 2, N - 1, 8191, 8192, N // 2 - 1, N // 2]
+    pts[:len(special), 2] = special
+    r_du, r_dq, r_dv = oracle.conv1d_bwd_points(d["u"], d["k"], d["D"], dy, pts, q=q, v=v,
+                                                dt=DT_ORACLE[dt], nthreads=nthreads)
+    errs = {}
+    for name, g, r in (("du", du, r_du), ("dq", dq, r_dq), ("dv", dv, r_dv)):
+        if r is None:
+            assert g is None
+            continue
+        gg = g[pts[:, 0], pts[:, 1], pts[:, 2]]
+        assert np.all(np.isfinite(gg)), name
+        errs[name] = rel_l2(gg, r)
+    kp = np.stack([rng.integers(0, H, n_dk), rng.integers(0, N, n_dk)], 1)
+    kp[:len(special), 1] = special
+    r_dk = oracle.conv1d_bwd_dk_points(d["u"], dy, kp, q=q, v=v, dt=DT_ORACLE[dt], nthreads=nthreads)
+    gk = dk[kp[:, 0], kp[:, 1]]
+    assert np.all(np.isfinite(gk)) and np.array_equal(dD, dk[:, 0])
+    errs["dk"] = rel_l2(gk, r_dk)
+    return errs
+
+
+def test_bwd_long_workload_shape_sampled(lc, nthreads):
+    """The 64K workload's shape (B4 H256 N65536, fp16, ungated), sampled, plus a gated variant
+    at the same length with fewer channels."""
+    spec = wl.WORKLOADS["long_f16_b4_h256_n65536"]
+    say(f"[bwd 64K] {spec.name} seed={spec.seed}")
+    d, dy, q, v = inputs(spec, "")
+    errs = _sampled_bwd(lc, nthreads, d, dy, q, v, seed=1)
+    say("   " + " ".join(f"{k}={e:.3e}" for k, e in errs.items()))
+    for k, e in errs.items():
+        assert e <= TOL["f16"], (k, e)
+    spec2 = wl.spec_1d(3, 4, 65536, "bf16", gated=True, seed=7001, decay=1e-4)
+    say(f"[bwd 64K gated] B=3 H=4 seed={spec2.seed}")
+    d, dy, q, v = inputs(spec2, "qv")
+    errs = _sampled_bwd(lc, nthreads, d, dy, q, v, seed=2)
+    say("   " + " ".join(f"{k}={e:.3e}" for k, e in errs.items()))
+    for k, e in errs.items():
+        assert e <= TOL["bf16"], (k, e)
+
+
+def test_bwd_very_long_sampled(lc, nthreads):
+    """2^21 (the very long workload's shape, B1 H64 bf16), sampled positions."""
+    spec = wl.WORKLOADS["very_long_bf16_b1_h64_n2097152"]
+    say(f"[bwd 2M] {spec.name} seed={spec.seed}")
+    d, dy, q, v = inputs(spec, "")
+    errs = _sampled_bwd(lc, nthreads, d, dy, q, v, n_pts=256, n_dk=96, seed=3)
+    say("   " + " ".join(f"{k}={e:.3e}" for k, e in errs.items()))
+    for k, e in errs.items():
+        assert e <= TOL["bf16"], (k, e)
+
+
+def test_training_pair_long(lc, nthreads):
+    """The training pair past one workgroup: fftconv_save's y equals the plain forward call's, c is
+    the pre-gate output, and the saved-output gradient equals the plain gradient."""
+    import torch
+    B, H, N, dt = 3, 2, 16384, "bf16"
+    spec = wl.spec_1d(B, H, N, dt, gated=True, seed=7100, decay=1e-4)
+    say(f"[train pair long] B={B} H={H} N={N} seed={spec.seed}")
+    d, dy, q, v = inputs(spec, "qv")
+    u_, q_, v_, D_, dy_ = (to_dev(x, dt) for x in (d["u"], q, v, d["D"], dy))
+    kf = lc.filter_fft(to_dev(d["k"], dt))
+    y_ref = lc.fftconv(u_, kf, D_, q=q_, v=v_)
+    y, c = lc.fftconv_save(u_, kf, D_, q=q_, v=v_)
+    c_ref = lc.fftconv(u_, kf, D_, q=q_)
+    plain = lc.fftconv_bwd(dy_, u_, kf, D_, q=q_, v=v_)
+    saved = lc.fftconv_bwd(dy_, u_, kf, D_, q=q_, v=v_, c=c)
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int16), c_ref.view(torch.int16))
+    # y = v * c rounds once from the rounded c; the plain call rounds v * c from fp32
+    assert rel_l2(from_dev(y, dt), from_dev(y_ref, dt)) <= 1e-2
+    for name, a, b in zip(("du", "dq"), saved[:2], plain[:2]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), name
+    assert torch.equal(saved[3], plain[3]) and torch.equal(saved[4], plain[4])
+    rows = [(b, h) for b in range(B) for h in range(H)]
+    errs = check_rows(tuple(from_dev(t, dt) if t is not None else None for t in saved[:3]), d, dy, q, v, rows,
+                      nthreads)
+    say("   " + " ".join(f"{k}={e:.3e}" for k, e in errs.items()))
+    for k, e in errs.items():
+        assert e <= TOL[dt], (k, e)
