@@ -193,22 +193,24 @@ def _stats_us(ms):
 
 def launch_distribution(step, args):
     """Per-launch times after the timed region: R launches each between its own event pair,
-    back to back ("hot"), then R launches each preceded by a write of a 512 MiB buffer outside
-    the events ("scrubbed": the 256 MB last-level cache then holds none of the inputs).  Returns
+    back to back ("hot"), then R launches each preceded by a read of a 512 MiB buffer outside
+    the events ("scrubbed": the 256 MB last-level cache then holds none of the inputs; a read,
+    not a write, so no dirty lines are still draining to HBM when the launch starts).  Returns
     median / min / p90 in microseconds for both, or {} with --dist 0."""
     import torch
     R = args.dist
     if R <= 0:
         return {}
-    scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    scrub = torch.ones((512 << 20) // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty((1,), dtype=torch.float32, device="cuda")
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R)]
-    out = {"launches": R, "scrub_bytes": scrub.numel()}
+    out = {"launches": R, "scrub_bytes": scrub.numel() * 4, "scrub": "read"}
     for mode in ("hot", "scrubbed"):
         torch.cuda.synchronize()
         prime(R)
         for i, (e0, e1) in enumerate(evs):
             if mode == "scrubbed":
-                scrub.fill_(i & 0x7f)
+                torch.sum(scrub, dim=0, keepdim=True, out=sink)
             e0.record()
             step()
             e1.record()

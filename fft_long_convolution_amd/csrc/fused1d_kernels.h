@@ -985,17 +985,30 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
         }
     };
     // (K + D) / M of channel h into copy kb, this wave's tiles only (read back by this wave)
+    // The filter is real, so its spectrum is Hermitian, K[M - f] = conj(K[f]): with
+    // f = k1 + 32 k2 + 512 k3 held at tile k1, lane 16 g + k2, value j (k3 = 4 g + j), tile
+    // 32 - k1 (k1 = 1 .. 15) is tile k1 read at lane 63 - l with the four values reversed and
+    // conjugated.  Only tiles 0 .. 16 are read from memory (the loads stay unconditional: a
+    // mirrored tile selects its source address and then its values).
     auto load_kf = [&](int64_t h, int kb) LCV_INLINE {
-        const uint4* src = (const uint4*)((const uint32_t*)a.kf + h * M) + wave * 4 * 64 + lane;
-        const uint4 t0 = src[0], t1 = src[64], t2 = src[128], t3 = src[192];
+        const uint4* base = (const uint4*)((const uint32_t*)a.kf + h * M);
+        uint4 t[4];
+        static_for<0, 4>([&](auto ii) LCV_INLINE {
+            constexpr int i = decltype(ii)::value;
+            const int k1 = wave * 4 + i;
+            const bool mir = k1 > 16;
+            const uint4 m = base[(mir ? 32 - k1 : k1) * 64 + (mir ? 63 - lane : lane)];
+            constexpr uint32_t S = 0x80000000u;   // sign of the imaginary half
+            t[i] = mir ? make_uint4(m.w ^ S, m.z ^ S, m.y ^ S, m.x ^ S) : m;
+        });
         const float d = raw1_to_f32<CT>(load1_raw<CT>(a.D, h)) * a.inv_m;
         auto fold = [&](uint32_t w) LCV_INLINE { return pack2<CT>(unpack_lo<CT>(w) + d, unpack_hi<CT>(w)); };
-        auto fold4 = [&](uint4 t) LCV_INLINE { return make_uint4(fold(t.x), fold(t.y), fold(t.z), fold(t.w)); };
+        auto fold4 = [&](uint4 v) LCV_INLINE { return make_uint4(fold(v.x), fold(v.y), fold(v.z), fold(v.w)); };
         uint4* dst = KFL + kb * (KF_W / 4) + wave * 4 * 64 + lane;
-        dst[0] = fold4(t0);
-        dst[64] = fold4(t1);
-        dst[128] = fold4(t2);
-        dst[192] = fold4(t3);
+        dst[0] = fold4(t[0]);
+        dst[64] = fold4(t[1]);
+        dst[128] = fold4(t[2]);
+        dst[192] = fold4(t[3]);
     };
 
     // ---- phases ------------------------------------------------------------------------------

@@ -176,6 +176,12 @@ __global__ void __launch_bounds__(kThreads) col_inv_kernel(const ColArgs a) {
 
 
 // ---- short columns (M1 <= 16): one column per thread, DFT in registers ----------------------
+// LDS column position of column c in a row of the 256-column block: the three low bits rotated
+// by bits 5-7.  A row-wise access of one instruction (thread cg of a row at columns 8 cg + k, k
+// fixed) then spreads over all the banks instead of landing every fourth group on the same
+// ones; the column-wise access (thread t at column t) stays a permutation inside groups of 8.
+__device__ __forceinline__ int col_swz(int c) { return (c & ~7) | ((c + (c >> 5)) & 7); }
+
 // Forward, H = M1/2 nonzero inputs: X[2m + e] = DFT_H( x[n] w_M1^{n e} )[m], e = 0, 1.
 // Inverse, outputs n < H only:  y[n] = E[n] + w_M1^{-n} O[n] with E, O the inverse DFT_H of the
 // even and odd inputs.  Rows pass through LDS so global rows are read and written 8 columns per
@@ -219,15 +225,15 @@ __global__ void __launch_bounds__(256) col_small_fwd_kernel(const ColArgs a) {
             for (int k = 0; k < 8; ++k) xr[k] = xi[k] = 0.f;
         }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) sin_[nh * LDW + 8 * cg + k] = make_float2(xr[k], xi[k]);
+        for (int k = 0; k < 8; ++k) sin_[nh * LDW + col_swz(8 * cg + k)] = make_float2(xr[k], xi[k]);
     }
     __syncthreads();
     {
-        const int t = threadIdx.x;
+        const int t = threadIdx.x, ts = col_swz(t);
         float2 ev[H], od[H];
 #pragma unroll
         for (int n = 0; n < H; ++n) {
-            const float2 x = sin_[n * LDW + t];
+            const float2 x = sin_[n * LDW + ts];
             ev[n] = x;
             od[n] = n == 0 ? x : cmulf(x, ((const float2*)a.tw_col)[n]);  // w_M1^n
         }
@@ -240,7 +246,7 @@ __global__ void __launch_bounds__(256) col_small_fwd_kernel(const ColArgs a) {
 #pragma unroll
         for (int k = 0; k < M1; ++k) {
             const float2 x = (k & 1) ? od[k >> 1] : ev[k >> 1];
-            sout[k * LDW + t] = cmulf(x, w);
+            sout[k * LDW + ts] = cmulf(x, w);
             w = cmulf(w, w1);
         }
     }
@@ -249,7 +255,7 @@ __global__ void __launch_bounds__(256) col_small_fwd_kernel(const ColArgs a) {
         const int kh = it / g8, cg = it % g8;
         float2 z[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) z[k] = sout[kh * LDW + 8 * cg + k];
+        for (int k = 0; k < 8; ++k) z[k] = sout[kh * LDW + col_swz(8 * cg + k)];
         ws_st8<CT>(a.ws, (s * a.M1 + kh) * kM2 + n_lo0 + 8 * cg, z);
     }
 }
@@ -269,18 +275,18 @@ __global__ void __launch_bounds__(256) col_small_inv_kernel(const ColArgs a) {
         float2 z[8];
         ws_ld8<CT>(a.ws, (s * a.M1 + kh) * kM2 + n_lo0 + 8 * cg, z);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) sin_[kh * LDW + 8 * cg + k] = z[k];
+        for (int k = 0; k < 8; ++k) sin_[kh * LDW + col_swz(8 * cg + k)] = z[k];
     }
     __syncthreads();
     {
-        const int t = threadIdx.x;
+        const int t = threadIdx.x, ts = col_swz(t);
         const int64_t n_lo = n_lo0 + t;
         const float2 w1 = tw_m(a.tw_lo, a.tw_hi, n_lo & (a.M - 1));
         float2 w = make_float2(1.f, 0.f);
         float2 ev[H], od[H];
 #pragma unroll
         for (int k = 0; k < M1; ++k) {
-            const float2 z = cmulcf(sin_[k * LDW + t], w);  // inverse four-step twiddle
+            const float2 z = cmulcf(sin_[k * LDW + ts], w);  // inverse four-step twiddle
             if (k & 1) od[k >> 1] = z;
             else ev[k >> 1] = z;
             w = cmulf(w, w1);
@@ -290,7 +296,7 @@ __global__ void __launch_bounds__(256) col_small_inv_kernel(const ColArgs a) {
 #pragma unroll
         for (int n = 0; n < H; ++n) {
             const float2 o = n == 0 ? od[0] : cmulcf(od[n], ((const float2*)a.tw_col)[n]);  // w_M1^{-n}
-            sout[n * LDW + t] = make_float2(ev[n].x + o.x, ev[n].y + o.y);
+            sout[n * LDW + ts] = make_float2(ev[n].x + o.x, ev[n].y + o.y);
         }
     }
     __syncthreads();
@@ -301,7 +307,7 @@ __global__ void __launch_bounds__(256) col_small_inv_kernel(const ColArgs a) {
         float yr[8], yi[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const float2 z = sout[nh * LDW + 8 * cg + k];
+            const float2 z = sout[nh * LDW + col_swz(8 * cg + k)];
             yr[k] = z.x;
             yi[k] = z.y;
         }
