@@ -45,13 +45,30 @@ def _run(cmd):
     return out
 
 
+def _deps(src: str) -> set:
+    """src and every project header it includes, directly or through other headers."""
+    import re
+    seen, todo = set(), [src]
+    while todo:
+        f = todo.pop()
+        if f in seen or not os.path.exists(f):
+            continue
+        seen.add(f)
+        for name in re.findall(r'^\s*#\s*include\s+"([^"]+)"', open(f).read(), flags=re.M):
+            for d in (CSRC, INCLUDE):
+                cand = os.path.join(d, name)
+                if os.path.exists(cand):
+                    todo.append(cand)
+                    break
+    return seen
+
+
 def _stale(obj: str, src: str) -> bool:
-    """True when obj is missing or older than its source or any header it may include."""
+    """True when obj is missing or older than its source or a header it includes."""
     if not os.path.exists(obj):
         return True
     t = os.path.getmtime(obj)
-    deps = [src] + [os.path.join(d, f) for d in (CSRC, INCLUDE) for f in os.listdir(d) if f.endswith(".h")]
-    return any(os.path.getmtime(p) > t for p in deps)
+    return any(os.path.getmtime(p) > t for p in _deps(src))
 
 
 def build(verbose: bool = False, jobs: int = 8, incremental: bool = False) -> str:

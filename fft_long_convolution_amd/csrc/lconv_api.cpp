@@ -3,7 +3,12 @@
 #include "lconv.h"
 
 #include <cstdint>
+#include <cstdio>
 #include <cstring>
+#include <mutex>
+#include <set>
+#include <string>
+#include <tuple>
 
 #include "api_internal.h"
 #include "kernels.h"
@@ -54,7 +59,7 @@ bool sides2d_ok(int64_t Hs, int64_t Ws) {
 }
 
 // sequences = complex transforms: pairs of batch rows per channel
-int64_t pairs_per_channel(int64_t B) { return (B + 1) / 2; }
+int64_t pairs_per_channel(int64_t B) { return B / 2 + (B & 1); }  // ceil(B / 2) without overflow
 
 int64_t chunk_seqs(int64_t total, int64_t M, size_t csz, size_t target = kChunkTarget) {
     int64_t per = (int64_t)(target / ((size_t)M * csz));
@@ -63,6 +68,23 @@ int64_t chunk_seqs(int64_t total, int64_t M, size_t csz, size_t target = kChunkT
 }
 
 lconv_status_t hip_status(hipError_t e) { return e == hipSuccess ? LCONV_SUCCESS : LCONV_ERR_HIP; }
+
+// LCONV_LOG: one stderr line per distinct (call, B, H, N, dtype) with the plan it runs
+void log_plan(const char* call, int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype, const Plan1D& p,
+              int64_t chunk_seqs_) {
+    if (!log_enabled()) return;
+    static std::mutex mu;
+    static std::set<std::tuple<std::string, int64_t, int64_t, int64_t, int>> seen;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!seen.insert(std::make_tuple(std::string(call), B, H, N, (int)dtype)).second) return;
+    std::fprintf(stderr, "lconv: %s B=%lld H=%lld N=%lld dtype=%s: M=%lld, %s (R=%d, M1=%lld%s)",
+                 call, (long long)B, (long long)H, (long long)N,
+                 dtype == LCONV_F32 ? "f32" : dtype == LCONV_F16 ? "f16" : "bf16", (long long)p.M,
+                 p.multipass ? "multi-pass" : "one workgroup per transform", p.R, (long long)p.M1,
+                 force_multipass() ? ", forced" : "");
+    if (p.multipass) std::fprintf(stderr, ", %lld sequences per chunk", (long long)chunk_seqs_);
+    std::fprintf(stderr, "\n");
+}
 
 // the calls on rows of whole 16-byte groups (N a multiple of 8), after validation
 lconv_status_t filter_fft_aligned(const void* k, void* k_f, int64_t H, int64_t N, lconv_dtype_t dtype,
@@ -333,6 +355,8 @@ lconv_status_t fftconv_fwd_aligned(const void* u, const void* k_f, const void* D
     const void* tabs = fused_tables(p.R, ct, &err, may_build);
     if (!tabs) return LCONV_ERR_HIP;
     const int64_t Bp = pairs_per_channel(B), seqs = Bp * H;
+    log_plan("fftconv_fwd", B, H, N, dtype, p,
+             p.multipass ? chunk_seqs(seqs, p.M, work_complex_size(dtype, false), chunk_target) : 0);
     if (!p.multipass) {
         Fused1DArgs a{};
         a.u = u; a.q = q; a.v = v; a.y = y; a.kf = k_f; a.D = D; a.tables = tabs;
@@ -428,7 +452,7 @@ lconv_status_t partial_impl(const void* u, const void* k_f, const void* D, void*
     // sequences of a channel: (batch row, block) windows, transformed two at a time
     const int64_t C = p.M / 2, nch = (N + C - 1) / C;
     int64_t nseq, items;
-    if (!mul_ok(B, nch, &nseq) || !mul_ok((nseq + 1) / 2, H, &items) || nseq >= ((int64_t)1 << 32) ||
+    if (!mul_ok(B, nch, &nseq) || !mul_ok(nseq / 2 + (nseq & 1), H, &items) || nseq >= ((int64_t)1 << 32) ||
         items >= ((int64_t)1 << 31))
         return LCONV_ERR_UNSUPPORTED;
     if (!u || !k_f || !D || !y) return LCONV_ERR_NULL_POINTER;

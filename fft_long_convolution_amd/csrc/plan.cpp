@@ -9,6 +9,7 @@
 #include "plan.h"
 
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -18,10 +19,29 @@
 
 namespace lcv {
 
+bool force_multipass() {
+    static const bool f = [] {
+        const char* e = std::getenv("LCONV_FORCE_PATH");
+        return e && std::strcmp(e, "multipass") == 0;
+    }();
+    return f;
+}
+
+bool log_enabled() {
+    static const bool f = [] {
+        const char* e = std::getenv("LCONV_LOG");
+        return e && *e && std::strcmp(e, "0") != 0;
+    }();
+    return f;
+}
+
 bool make_plan_1d(int64_t N, Plan1D* p) {
     if (N < 1 || N > ((int64_t)1 << 22)) return false;
     int64_t M = 512;
     while (M < 2 * N) M *= 2;
+    // testing switch: every length on the multi-pass path, with at least two columns (any
+    // M >= 2N gives the same linear convolution)
+    if (force_multipass() && M < 2 * kRowLen) M = 2 * kRowLen;
     p->N = N;
     p->M = M;
     if (M <= 256 * kMaxFusedR) {

@@ -25,8 +25,15 @@ struct Plan1D {
     bool multipass;
 };
 
-// Returns false when N is outside the supported set.
+// Returns false when N is outside the supported set.  With LCONV_FORCE_PATH=multipass in the
+// environment (read once; for testing) every length takes the multi-pass plan with M >= 16384:
+// the calls that need one workgroup per transform (partial, frequency-sparse, state-space) then
+// return LCONV_ERR_UNSUPPORTED.
 bool make_plan_1d(int64_t N, Plan1D* p);
+bool force_multipass();
+// LCONV_LOG set (and not "0"): the forward and filter calls print their plan to stderr, once per
+// distinct call shape.
+bool log_enabled();
 
 // Layout of the fused-path table for (R, compute type), offsets in bytes.
 struct FusedTableLayout {

@@ -54,7 +54,9 @@ extern "C" {
  * training pair for every supported N, with workspace arguments). */
 #define LCONV_ABI_VERSION 6
 
-typedef enum { LCONV_F32 = 0, LCONV_F16 = 1, LCONV_BF16 = 2 } lconv_dtype_t;
+/* The last enumerator only widens the type's range to every int, so that any value a C caller
+ * passes is a valid value of the type (unknown ones are rejected with LCONV_ERR_UNSUPPORTED). */
+typedef enum { LCONV_F32 = 0, LCONV_F16 = 1, LCONV_BF16 = 2, LCONV_DTYPE_MAX_ENUM = 0x7fffffff } lconv_dtype_t;
 
 typedef enum {
     LCONV_SUCCESS = 0,
