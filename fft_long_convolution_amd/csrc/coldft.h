@@ -18,6 +18,27 @@ __device__ __forceinline__ float2 cmulcf(float2 a, float2 b) {  // a * conj(b)
     return make_float2(a.x * b.x + a.y * b.y, a.y * b.x - a.x * b.y);
 }
 
+// exp(-2 pi i r / M) from the two-level table (r reduced mod M by the caller)
+__device__ __forceinline__ float2 tw_m(const float* lo, const float* hi, int64_t r) {
+    float2 a = ((const float2*)lo)[r & 2047];
+    float2 b = ((const float2*)hi)[r >> 11];
+    return cmulf(a, b);
+}
+
+// (sequence -> rows) of a column pass's sequence gs: the pair of batch rows (b, b+1) of one
+// channel (row1 = -1 past the last row), or one filter channel
+template <typename A>
+__device__ __forceinline__ void seq_rows(const A& a, int64_t gs, int64_t& row0, int64_t& row1) {
+    if (a.filter) {
+        row0 = gs * a.N;
+        row1 = -1;
+    } else {
+        const int64_t h = gs / a.seq_per_h, b = 2 * (gs % a.seq_per_h);
+        row0 = (b * a.H + h) * a.N;
+        row1 = b + 1 < a.B ? row0 + a.H * a.N : -1;
+    }
+}
+
 // In-register DFT of length RAD (1, 2, 4 or 8); sign -1 forward, +1 inverse.
 template <int RAD, bool INV>
 __device__ __forceinline__ void dft_small(float2* v) {

@@ -83,6 +83,7 @@ struct ColArgs {
     int64_t nseq;        // sequences in this chunk
     int64_t seq_per_h;   // pairs per channel (CONV) or 1 (FILTER)
     int filter;          // 1: input is k (one real channel per sequence)
+    const void* img;     // matrix-core column images (16-bit, column lengths 256..1024), or null
 };
 
 // Pass A: per sequence and column n_lo, DFT over n_hi < M1/2 (zero above), twiddle
@@ -90,6 +91,8 @@ struct ColArgs {
 hipError_t launch_col_fwd(int dtype, const ColArgs& a, hipStream_t stream);
 // Pass C: inverse twiddle, inverse DFT over k_hi for n_hi < M1/2, gate, store y.
 hipError_t launch_col_inv(int dtype, const ColArgs& a, hipStream_t stream);
+// The same two passes on the matrix cores, for 16-bit types and M1 = 256, 512 or 1024 (a.img set).
+hipError_t launch_colmx(bool fwd, int dtype, const ColArgs& a, hipStream_t stream);
 
 struct Conv2DArgs {
     const void* u;       // [B][C][Hs][Ws]

@@ -325,6 +325,7 @@ lconv_status_t prepare_tables(int64_t N, lconv_dtype_t dtype) {
     if (p.multipass) {
         ColTables ctab;
         if (!col_tables(p.M, p.M1, &ctab, &err)) return LCONV_ERR_HIP;
+        if (ct != CT_F32 && colmx_supported(p.M1) && !colmx_tables(p.M1, ct, &err)) return LCONV_ERR_HIP;
     }
     return LCONV_SUCCESS;
 }
@@ -338,8 +339,10 @@ bool tables_ready(const Plan1D& p, lconv_dtype_t dtype) {
     hipError_t err = hipSuccess;
     const int ct = dtype == LCONV_F32 ? CT_F32 : (int)dtype;
     if (!fused_tables(p.R, ct, &err, false)) return false;
+    if (!p.multipass) return true;
     ColTables ctab;
-    return !p.multipass || col_tables(p.M, p.M1, &ctab, &err, false);
+    if (!col_tables(p.M, p.M1, &ctab, &err, false)) return false;
+    return ct == CT_F32 || !colmx_supported(p.M1) || colmx_tables(p.M1, ct, &err, false);
 }
 
 lconv_status_t fftconv_fwd_aligned(const void* u, const void* k_f, const void* D, void* y, const void* q,
@@ -366,6 +369,11 @@ lconv_status_t fftconv_fwd_aligned(const void* u, const void* k_f, const void* D
     }
     ColTables ctab;
     if (!col_tables(p.M, p.M1, &ctab, &err, may_build)) return LCONV_ERR_HIP;
+    const void* cimg = nullptr;  // matrix-core column images (16-bit long columns)
+    if (ct != CT_F32 && colmx_supported(p.M1)) {
+        cimg = colmx_tables(p.M1, ct, &err, may_build);
+        if (!cimg) return LCONV_ERR_HIP;
+    }
     const int64_t per = chunk_seqs(seqs, p.M, work_complex_size(dtype, false), chunk_target);
     for (int64_t s0 = 0; s0 < seqs; s0 += per) {
         const int64_t ns = per < seqs - s0 ? per : seqs - s0;
@@ -373,7 +381,7 @@ lconv_status_t fftconv_fwd_aligned(const void* u, const void* k_f, const void* D
         c.u = u; c.q = q; c.v = v; c.y = y; c.ws = workspace;
         c.tw_lo = ctab.lo; c.tw_hi = ctab.hi; c.tw_col = ctab.col;
         c.B = B; c.H = H; c.N = N; c.M = p.M; c.M1 = p.M1; c.seq0 = s0; c.nseq = ns;
-        c.seq_per_h = Bp; c.filter = 0;
+        c.seq_per_h = Bp; c.filter = 0; c.img = cimg;
         if (launch_col_fwd(dtype, c, stream) != hipSuccess) return LCONV_ERR_HIP;
         Fused1DArgs a{};
         a.u = workspace; a.y = workspace; a.kf = k_f; a.D = D; a.tables = tabs;

@@ -29,27 +29,8 @@ namespace {
 constexpr int64_t kM2 = 8192;
 constexpr int kLdsBytes = 64 * 1024;    // column block: CB x M1 fp32 complex (plus one pad row)
 
-// exp(-2 pi i r / M) from the two-level table (r reduced mod M by the caller)
-__device__ __forceinline__ float2 tw_m(const float* lo, const float* hi, int64_t r) {
-    float2 a = ((const float2*)lo)[r & 2047];
-    float2 b = ((const float2*)hi)[r >> 11];
-    return cmulf(a, b);
-}
-
 __host__ __device__ constexpr int cols_per_wg(int M1) {
     return kLdsBytes / (8 * M1) < 256 ? kLdsBytes / (8 * M1) : 256;
-}
-
-// (sequence -> rows) of the chunk's sequence gs
-__device__ __forceinline__ void seq_rows(const ColArgs& a, int64_t gs, int64_t& row0, int64_t& row1) {
-    if (a.filter) {
-        row0 = gs * a.N;
-        row1 = -1;
-    } else {
-        const int64_t h = gs / a.seq_per_h, b = 2 * (gs % a.seq_per_h);
-        row0 = (b * a.H + h) * a.N;
-        row1 = b + 1 < a.B ? row0 + a.H * a.N : -1;
-    }
 }
 
 }  // namespace
@@ -365,6 +346,9 @@ static hipError_t launch_cols(bool fwd, const ColArgs& a, hipStream_t st) {
     if (a.nseq <= 0) return hipSuccess;
     const int M1 = (int)a.M1;
     if (M1 < 2 || M1 > 1024 || (M1 & (M1 - 1))) return hipErrorInvalidValue;
+    if constexpr (CT != CT_F32) {  // 16-bit long columns: the matrix-core passes (colmx.hip)
+        if (!a.filter && a.img && colmx_supported(M1)) return launch_colmx(fwd, CT, a, st);
+    }
     switch (M1) {  // one column per thread, DFT in registers
     case 2: return launch_small_t<CT, IO, 2>(fwd, a, st);
     case 4: return launch_small_t<CT, IO, 4>(fwd, a, st);

@@ -178,6 +178,28 @@ std::vector<uint8_t> build_fused_tables(int R, int ct) {
     return t;
 }
 
+std::vector<uint8_t> build_colmx_tables(int P, int ct) {
+    const ColMxGrid G = colmx_grid(P);
+    std::vector<uint8_t> t;
+    // forward first stage: rows k1 = 16 rb + x, inputs n1 = 16 kc + ci (zero input past H)
+    for (int rb = 0; rb < G.rbk; ++rb)
+        for (int kc = 0; kc < G.hb; ++kc)
+            append_image(t, ct, [&](int x, int ci) {
+                const int k1 = 16 * rb + x, n1 = 16 * kc + ci;
+                return n1 < G.H ? omega((int64_t)k1 * n1, G.R) : cplx{0, 0};
+            });
+    // inverse first stage: rows n1 = 16 rb + x (kept only below H), inputs k1 = 16 kc + ci
+    for (int rb = 0; rb < G.hb; ++rb)
+        for (int kc = 0; kc < G.rbk; ++kc)
+            append_image(t, ct, [&](int x, int ci) {
+                const int n1 = 16 * rb + x, k1 = 16 * kc + ci;
+                return n1 < G.H ? omega(-(int64_t)k1 * n1, G.R) : cplx{0, 0};
+            });
+    append_image(t, ct, [&](int k2, int n2) { return omega((int64_t)n2 * k2, 16); });
+    append_image(t, ct, [&](int n2, int k2) { return omega(-(int64_t)n2 * k2, 16); });
+    return t;
+}
+
 struct DevBuf {
     void* ptr = nullptr;
     std::vector<uint8_t> host;  // kept alive for the lifetime of the cache
@@ -212,6 +234,7 @@ const void* get_or_build(int kind, int ct, int64_t a, int64_t b,
 
 std::vector<uint8_t> build_any(int kind, int ct, int64_t a, int64_t b) {
     if (kind == 0) return build_fused_tables((int)a, ct);
+    if (kind == 3) return build_colmx_tables((int)a, ct);
     if (kind == 2) {  // P-point DFT twiddles
         std::vector<uint8_t> t((size_t)a * 8);
         float* f = (float*)t.data();
@@ -268,6 +291,10 @@ bool col_tables(int64_t M, int64_t M1, ColTables* out, hipError_t* err, bool bui
     out->hi = out->lo + 2 * nlo;
     out->col = out->hi + 2 * nhi;
     return true;
+}
+
+const void* colmx_tables(int64_t P, int ct, hipError_t* err, bool build) {
+    return get_or_build(3, ct, P, 0, build_any, err, build);
 }
 
 const float* dft_table(int64_t P, hipError_t* err) {

@@ -58,6 +58,24 @@ struct ColTables {
 };
 bool col_tables(int64_t M, int64_t M1, ColTables* out, hipError_t* err, bool build = true);
 
+// Matrix-core column passes of the multi-pass path, column length P = 16 R (R = 16, 32, 64),
+// 16-bit compute types.  Digits n_hi = 16 n1 + n2, k_hi = k1 + R k2: the first stage is a
+// radix-R DFT over n1 (forward: only n1 < H = R/2 is nonzero; inverse: only n1 < H is kept),
+// the second a 16-point DFT over n2.  Image indices in the table: the forward first stage
+// (k1 block rb, n1 block kc) at f1 + rb * hb + kc, the inverse first stage (n1 block rb, k1
+// block kc) at i2 + rb * rbk + kc, the 16-point DFT and its inverse at f16 and i16.
+struct ColMxGrid {
+    int R, H, rbk, hb;       // radix, half radix, 16-blocks of k1, 16-blocks of n1 < H
+    int f1, i2, f16, i16, nimg;
+};
+constexpr ColMxGrid colmx_grid(int P) {
+    const int R = P / 16, H = R / 2, rbk = R / 16, hb = (H + 15) / 16;
+    return ColMxGrid{R, H, rbk, hb, 0, rbk * hb, 2 * rbk * hb, 2 * rbk * hb + 1, 2 * rbk * hb + 2};
+}
+constexpr bool colmx_supported(int64_t P) { return P == 256 || P == 512 || P == 1024; }
+// Device pointer to those images for (P, ct) on the current device (ct 16-bit).
+const void* colmx_tables(int64_t P, int ct, hipError_t* err, bool build = true);
+
 // exp(-2 pi i e / P) for e < P, fp32 complex, on the current device (3D path).
 const float* dft_table(int64_t P, hipError_t* err);
 

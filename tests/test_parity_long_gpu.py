@@ -26,13 +26,17 @@ def lc():
     return lconv
 
 
-# (B, H, N, dtype, gated): column lengths M1 = 32, 64, 128, 256, 256, 1024
+# (B, H, N, dtype, gated): column lengths M1 = 32, 64, 128, 256, 256, 256, 512, 1024.  The 16-bit
+# cases with M1 >= 256 run the matrix-core column passes (both batch rows of a pair, an odd
+# batch's lone last row, and one-row sequences); fp32 keeps the vector-ALU ones.
 CASES = [
     (2, 2, 131072, "bf16", True),
     (1, 3, 262144, "f16", False),
     (3, 1, 524288, "bf16", True),
     (1, 2, 1048576, "f32", False),
     (1, 2, 1000000, "bf16", True),      # not a power of two
+    (3, 1, 600000, "f16", True),        # M1 = 256, odd batch
+    (2, 1, 1572864, "f16", True),       # M1 = 512
     (1, 2, 2300000, "bf16", False),     # M = 2^23, M1 = 1024
 ]
 
