@@ -198,10 +198,23 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
         else decode(item, h, b);
         return h;
     };
+    // ROW/ROWFWD item -> workspace row (local sequence * M1 + k_hi).  ROW items run k_hi-major
+    // (item = k_hi * sequences + local sequence): the batch pairs of one channel, consecutive
+    // sequences, then read the same spectrum row one after another on one workgroup.
+    const uint32_t nsq = (uint32_t)(a.nitems >> m1s);
+    auto ws_row = [&](int64_t item) LCV_INLINE -> int64_t {
+        if constexpr (MODE == MODE_ROW) {
+            const uint32_t it = (uint32_t)item, kh = it / nsq, sl = it - kh * nsq;
+            return ((int64_t)sl << m1s) + kh;
+        } else {
+            return item;
+        }
+    };
     // ROW/ROWFWD item -> (channel h, row k_hi)
     auto decode_row = [&](int64_t item, int64_t& h, int64_t& khi) LCV_INLINE {
-        const int64_t s = a.seq0 + (item >> m1s);
-        khi = item & (a.M1 - 1);
+        const int64_t r = ws_row(item);
+        const int64_t s = a.seq0 + (r >> m1s);
+        khi = r & (a.M1 - 1);
         h = (int64_t)((uint32_t)s / (uint32_t)a.seq_per_h);
     };
 
@@ -392,7 +405,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                 }
             }
         } else {  // ROW / ROWFWD: one complex row of 8192 from the workspace (P == 1)
-            const uint32_t* src = (const uint32_t*)a.u + it0 * (int64_t)M * EW;
+            const uint32_t* src = (const uint32_t*)a.u + ws_row(it0) * (int64_t)M * EW;
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
                 int pp, n0;
@@ -828,7 +841,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                     }
                 }
             } else {  // ROW: complex row back to the workspace, in compute type
-                uint32_t* dstrow = (uint32_t*)a.y + it0 * (int64_t)M * EW;
+                uint32_t* dstrow = (uint32_t*)a.y + ws_row(it0) * (int64_t)M * EW;
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
                     int pp, n0;
@@ -881,8 +894,13 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
 // spectrum has two LDS copies so the next channel's can be loaded while the current one is read.
 // ADJ: the adjoint chain (conjugate spectrum; outputs du = q dx and dq = u dx), as in
 // fused1d_kernel.
+// ROW: the row pass of the multi-pass path (the MODE_ROW chain of fused1d_kernel): an item is one
+// complex 8192-point row of the workspace, transformed in full (F1 over all 32 n1, I3 back to
+// all 32 rows), multiplied by its slice of the spectrum (registers, loaded one item ahead) and
+// written back in place.  Items run k_hi-major over the chunk, so that the batch pairs of one
+// channel meet the same spectrum row back to back.
 // ------------------------------------------------------------------------------------------
-template <int CT, bool GQ, bool GV, bool ADJ, bool SAVE = false>
+template <int CT, bool GQ, bool GV, bool ADJ, bool SAVE = false, bool ROW = false>
 __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
     constexpr int R = 32, M = 8192, KCF = 2;
     constexpr int IMG = ImgBytes<CT>::value;
@@ -890,8 +908,11 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
     constexpr int T_F3 = T_F2 + IMG * R, T_I1 = T_F3 + IMG * R, T_I2 = T_I1 + IMG * R, T_TW = T_I2 + IMG * R;
     constexpr int ST = 260;                      // XY tile stride (words)
     constexpr int SV = 260;                      // V / O row stride (words, one complex per word)
-    constexpr int XY_W = 32 * ST, V_W = 16 * SV, IM_W = 4 * IMG / 4, KF_W = 32 * 64 * 4;
-    __shared__ __attribute__((aligned(16))) uint32_t lds[2 * XY_W + V_W + IM_W + 2 * KF_W];
+    constexpr int NR = ROW ? 32 : 16;            // rows n1 of the V / O slots
+    constexpr int NIM = ROW ? 8 : 4;             // F1 and I3 block images kept in LDS
+    constexpr int NKF = ROW ? 0 : 2;             // LDS copies of the spectrum (ROW: registers)
+    constexpr int XY_W = 32 * ST, V_W = NR * SV, IM_W = NIM * IMG / 4, KF_W = 32 * 64 * 4;
+    __shared__ __attribute__((aligned(16))) uint32_t lds[2 * XY_W + V_W + IM_W + NKF * KF_W];
     uint32_t* const XYb = lds;                   // two buffers of XY_W
     uint32_t* const V = lds + 2 * XY_W;          // input slots (P0 -> P1) and output slots (P3 -> P4)
     uint32_t* const IMS = V + V_W;               // F1 (rb = 0, 1) and I3 (kc = 0, 1) images
@@ -927,11 +948,18 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
         mi2[i] = load_img<CT>(tab + T_I2, k1, lane);
     }
     {
-        // F1 blocks (rb, kc = 0) are table images 0 and KCF; I3 blocks (rb = 0, kc) are 0 and 1
-        const int srcs[4] = {T_F1, T_F1 + IMG * KCF, T_I3, T_I3 + IMG};
+        // F1 blocks (rb, kc) are table images rb KCF + kc, I3 blocks (rb, kc) likewise.  CONV:
+        // F1 (0, 0), (1, 0) (inputs n1 < 16) and I3 (0, 0), (0, 1) (outputs n1 < 16).  ROW: all
+        // four of each, F1 (rb, kc) at rb KCF + kc and I3 (rb, kc) at 4 + rb KCF + kc.
+        // (offsets computed, not read from a local array: a dynamically indexed array would be
+        // placed in LDS)
+        auto src_of = [&](int img) LCV_INLINE {
+            if constexpr (ROW) return img < 4 ? T_F1 + IMG * img : T_I3 + IMG * (img - 4);
+            else return img < 2 ? T_F1 + IMG * KCF * img : T_I3 + IMG * (img - 2);
+        };
         for (int w = tid; w < IM_W / 4; w += 512) {
             const int img = w / (IMG / 16), off = w % (IMG / 16);
-            ((uint4*)IMS)[w] = ((const uint4*)(tab + srcs[img]))[off];
+            ((uint4*)IMS)[w] = ((const uint4*)(tab + src_of(img)))[off];
         }
         __syncthreads();  // every wave reads all four
     }
@@ -942,6 +970,15 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
     const int64_t sB = a.sb ? a.sb : a.H * a.N, sH = a.sh ? a.sh : a.N;
     auto channel = [&](int64_t item) LCV_INLINE {
         return (int64_t)((uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)item) / Bp);
+    };
+    // ROW: item -> workspace row (local sequence * M1 + k_hi), item = k_hi * sequences + local
+    // sequence; the row's channel and spectrum row k_hi
+    const int m1s = ROW && a.M1 > 1 ? __builtin_ctzll((unsigned long long)a.M1) : 0;
+    const uint32_t nsq = ROW ? (uint32_t)(a.nitems >> m1s) : 1u;
+    auto ws_row = [&](int64_t item) LCV_INLINE -> int64_t {
+        item = item < last ? item : last - 1;
+        const uint32_t it = __builtin_amdgcn_readfirstlane((uint32_t)item), kh = it / nsq, sl = it - kh * nsq;
+        return ((int64_t)sl << m1s) + kh;
     };
     // this lane's slot: row n1 = lane / 4, columns 32 wave + 8 (lane % 4) .. +8 (the wave's blocks)
     const int s_n1 = lane >> 2, s_col = 32 * wave + 8 * (lane & 3);
@@ -957,7 +994,31 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
         o1 = (b + 1 < a.B ? row0 + sB : row0) + s_n0;
     };
     uint4 ru[2], rq[2], rv[2], re2[2];
+    uint4 rw0, rw1, rw2, rw3;  // ROW: this lane's slot of the row, rows n1 = s_n1 and s_n1 + 16
+    uint4 rk[4];         // ROW: the spectrum slice of this wave's four tiles, one item ahead
+    float rkd = 0.f;     // ROW: D[h] / M of that item
+    auto issue_row = [&](int64_t item) LCV_INLINE {
+        const uint4* src = (const uint4*)((const uint32_t*)a.u + ws_row(item) * M + s_n0);
+        rw0 = src[0];
+        rw1 = src[1];
+        rw2 = src[16 * 256 / 4];
+        rw3 = src[16 * 256 / 4 + 1];
+    };
+    auto issue_kf_row = [&](int64_t item) LCV_INLINE {
+        const int64_t r = ws_row(item);
+        const int64_t h = (int64_t)((uint32_t)(a.seq0 + (r >> m1s)) / (uint32_t)a.seq_per_h);
+        const uint4* src = (const uint4*)((const uint32_t*)a.kf + h * a.M + (r & (a.M1 - 1)) * M);
+        static_for<0, 4>([&](auto ii) LCV_INLINE {
+            constexpr int i = decltype(ii)::value;
+            rk[i] = src[(wave * 4 + i) * 64 + lane];
+        });
+        rkd = raw1_to_f32<CT>(load1_raw<CT>(a.D, h)) * a.inv_m;
+    };
     auto issue_uq = [&](int64_t item) LCV_INLINE {
+        if constexpr (ROW) {
+            issue_row(item);
+            return;
+        }
         int64_t o0, o1;
         offsets(item, o0, o1);
         load_raw<CT>(a.u, o0, &ru[0]);
@@ -1014,6 +1075,15 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
     // ---- phases ------------------------------------------------------------------------------
     // P0: gate and pack this lane's slot of the item into V
     auto P0 = [&]() LCV_INLINE {
+        if constexpr (ROW) {
+            uint4* d0 = (uint4*)(V + s_n1 * SV + s_col);
+            uint4* d1 = (uint4*)(V + (s_n1 + 16) * SV + s_col);
+            d0[0] = rw0;
+            d0[1] = rw1;
+            d1[0] = rw2;
+            d1[1] = rw3;
+            return;
+        }
         float xr[8], xi[8];
         unpack_raw<CT>(&ru[0], xr);
         unpack_raw<CT>(&ru[1], xi);
@@ -1037,6 +1107,31 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
     };
     // P1: F1 (radix 32 over n1 < 16) on this wave's two column blocks, V -> XY
     auto P1 = [&](uint32_t* XY) LCV_INLINE {
+        if constexpr (ROW) {  // all 32 rows n1: two K chunks per output block
+            Operand<CT> din[2][2];
+            static_for<0, 2>([&](auto bb) LCV_INLINE {
+                constexpr int bi = decltype(bb)::value;
+                const int b = 2 * wave + bi;
+                static_for<0, 2>([&](auto kk) LCV_INLINE {
+                    constexpr int kc = decltype(kk)::value;
+                    din[bi][kc] = lds_operand<CT>(V, [&](int j) { return (16 * kc + 4 * g + j) * SV + 16 * b + c; });
+                });
+            });
+            static_for<0, 2>([&](auto rr) LCV_INLINE {
+                constexpr int rb = decltype(rr)::value;
+                const MatImg<CT> f0 = load_img_lds<CT>(IMS, 2 * rb, lane), f1 = load_img_lds<CT>(IMS, 2 * rb + 1, lane);
+                static_for<0, 2>([&](auto bb) LCV_INLINE {
+                    constexpr int bi = decltype(bb)::value;
+                    const int b = 2 * wave + bi;
+                    f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
+                    stage_keep_acc<CT>(f0, din[bi][0], re, im);
+                    stage_keep_acc<CT>(f1, din[bi][1], re, im);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) lds_put<CT>(XY, xy_addr(16 * rb + 4 * g + j, b, c), re[j], im[j]);
+                });
+            });
+            return;
+        }
         const MatImg<CT> f0 = load_img_lds<CT>(IMS, 0, lane), f1 = load_img_lds<CT>(IMS, 1, lane);
         Operand<CT> din[2];
         static_for<0, 2>([&](auto bb) LCV_INLINE {
@@ -1096,9 +1191,14 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
                     cmul4(xs[i], twr, twi);
                     opd[i] = to_operand<CT>(xs[i]);
                 } else if constexpr (st == 2) {
-                    const uint4 kw = kfl[t * 64 + lane];  // (K + D) / M
                     f32x4 kr, ki;
-                    unpack_raw_c4v<CT>(&kw, kr, ki);
+                    if constexpr (ROW) {
+                        unpack_raw_c4v<CT>(&rk[i], kr, ki);
+                        kr += rkd;  // (K + D) / M
+                    } else {
+                        const uint4 kw = kfl[t * 64 + lane];  // (K + D) / M
+                        unpack_raw_c4v<CT>(&kw, kr, ki);
+                    }
                     if constexpr (ADJ) cmulc4(xs[i], kr, ki);
                     else cmul4(xs[i], kr, ki);
                     opd[i] = to_operand<CT>(xs[i]);
@@ -1145,7 +1245,8 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
     };
     // P3: I3 (inverse radix 32, rows n1 < 16) on this wave's two column blocks, XY -> O (in V)
     auto P3 = [&](const uint32_t* XY) LCV_INLINE {
-        const MatImg<CT> i0 = load_img_lds<CT>(IMS, 2, lane), i1 = load_img_lds<CT>(IMS, 3, lane);
+        constexpr int IB = ROW ? 4 : 2;  // first I3 image in LDS
+        const MatImg<CT> i0 = load_img_lds<CT>(IMS, IB, lane), i1 = load_img_lds<CT>(IMS, IB + 1, lane);
         Operand<CT> din[2][2];
         static_for<0, 2>([&](auto bb) LCV_INLINE {
             constexpr int bi = decltype(bb)::value;
@@ -1169,9 +1270,32 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) V[(4 * g + j) * SV + 16 * b + c] = pack2<CT>(acc[bi].re[j], acc[bi].im[j]);
         });
+        if constexpr (ROW) {  // rows n1 = 16 .. 31 as well
+            const MatImg<CT> i2 = load_img_lds<CT>(IMS, IB + 2, lane), i3 = load_img_lds<CT>(IMS, IB + 3, lane);
+            static_for<0, 2>([&](auto bb) LCV_INLINE {
+                constexpr int bi = decltype(bb)::value;
+                const int b = 2 * wave + bi;
+                f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
+                stage_keep_acc<CT>(i2, din[bi][0], re, im);
+                stage_keep_acc<CT>(i3, din[bi][1], re, im);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) V[(16 + 4 * g + j) * SV + 16 * b + c] = pack2<CT>(re[j], im[j]);
+            });
+        }
     };
     // P4: post-gate and store this lane's slot of the item
     auto P4 = [&](int64_t item) LCV_INLINE {
+        if constexpr (ROW) {  // back to the workspace row, in place
+            uint4* dst = (uint4*)((uint32_t*)a.y + ws_row(item) * M + s_n0);
+            const uint4* s0 = (const uint4*)(V + s_n1 * SV + s_col);
+            const uint4* s1 = (const uint4*)(V + (s_n1 + 16) * SV + s_col);
+            const uint4 w0 = s0[0], w1 = s0[1], w2 = s1[0], w3 = s1[1];
+            dst[0] = w0;
+            dst[1] = w1;
+            dst[16 * 256 / 4] = w2;
+            dst[16 * 256 / 4 + 1] = w3;
+            return;
+        }
         int64_t o0, o1;
         offsets(item, o0, o1);
         const uint4* src = (const uint4*)(V + s_n1 * SV + s_col);
@@ -1212,9 +1336,10 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
     };
 
     // ---- pipeline ------------------------------------------------------------------------------
-    int64_t kf_h = channel(first);
+    int64_t kf_h = ROW ? 0 : channel(first);  // (ROW items carry no batch count)
     int kb = 0;
-    load_kf(kf_h, 0);
+    if constexpr (ROW) issue_kf_row(first);
+    else load_kf(kf_h, 0);
     issue_uq(first);
     P0();
     issue_uq(first + 1);
@@ -1230,13 +1355,14 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
         for (int s = 0; s < 2; ++s) {
             if ((s == 0) == (wave < 4)) {
                 P2(XYk, KFL + kb * (KF_W / 4));
+                if constexpr (ROW) issue_kf_row(k + 1);  // clamped past the end
             } else {
                 if (k > first) {
                     issue_e2(k - 1);
                     P3(XYo);
                     P4(k - 1);
                 }
-                if (k + 1 < last) {
+                if (!ROW && k + 1 < last) {
                     const int64_t hn = channel(k + 1);
                     if (hn != kf_h) {
                         kb_next = 1 - kb;
@@ -1280,14 +1406,14 @@ static hipError_t launch_t(const Fused1DArgs& a0, int cus, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int CT, bool GQ, bool GV, bool ADJ, bool SAVE>
+template <int CT, bool GQ, bool GV, bool ADJ, bool SAVE, bool ROW = false>
 static hipError_t launch_8k(const Fused1DArgs& a0, int cus, hipStream_t st) {
     Fused1DArgs a = a0;
     if (a.nitems <= 0) return hipSuccess;
     int64_t nwg = a.nitems < cus ? a.nitems : cus;
     a.per_wg = (a.nitems + nwg - 1) / nwg;
     nwg = (a.nitems + a.per_wg - 1) / a.per_wg;
-    hipLaunchKernelGGL((conv8k_kernel<CT, GQ, GV, ADJ, SAVE>), dim3((unsigned)nwg), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((conv8k_kernel<CT, GQ, GV, ADJ, SAVE, ROW>), dim3((unsigned)nwg), dim3(512), 0, st, a);
     return hipGetLastError();
 }
 
