@@ -13,8 +13,9 @@ static hipError_t launch_misc(int dtype, int mode, const Fused1DArgs& a, int cus
     if constexpr (R == 32) {
         if (mode == MODE_ROW) {
             if (dtype == CT_F32) return launch_t<32, CT_F32, CT_F32, MODE_ROW, false, false>(a, cus, st);
-            if (dtype == CT_F16) return launch_t<32, CT_F16, CT_F16, MODE_ROW, false, false>(a, cus, st);
-            return launch_t<32, CT_BF16, CT_BF16, MODE_ROW, false, false>(a, cus, st);
+            // 16-bit: the pipelined kernel's row variant
+            if (dtype == CT_F16) return launch_8k<CT_F16, false, false, false, false, true>(a, cus, st);
+            return launch_8k<CT_BF16, false, false, false, false, true>(a, cus, st);
         }
         if (mode == MODE_ROWFWD) {
             if (dtype == CT_F32) return launch_t<32, CT_F32, CT_F32, MODE_ROWFWD, false, false>(a, cus, st);
