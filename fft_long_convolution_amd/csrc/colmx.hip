@@ -9,10 +9,11 @@
 //     y[16 n1 + n2] = sum_{k1} w_R^{-n1 k1} w_P^{-n2 k1} sum_{k2} w16^{-n2 k2} Z[k1 + R k2]
 // Both factors are dense DFT blocks on the matrix cores ("FlashFFTConv" abstract; "FlashConv"
 // page, Mechanism), as 16 x 16 complex tiles of v_mfma_f32_16x16x32_{bf16,f16} whose L index
-// is 16 consecutive columns of the block (the tile layout of lconv_device.h).  The w_P twiddle
-// runs on the vector ALU between the two stages, and one LDS exchange moves the contracted
-// digit from n1 to n2 (forward) or from k2 to k1 (inverse).  Global rows go straight between
-// memory and tile registers: one tile instruction touches 16 consecutive columns of 4 rows.
+// runs over 16 columns of the block (the tile layout of lconv_device.h).  The w_P twiddle runs
+// on the vector ALU between the two stages, and one LDS exchange moves the contracted digit
+// from n1 to n2 (forward) or from k2 to k1 (inverse).  Global rows go straight between memory
+// and tile registers: a lane's tiles hold consecutive columns, so one access instruction moves
+// whole 128-byte row segments of 4 rows.
 //
 // A workgroup owns CB = 16384 / P consecutive columns of one sequence; workgroups whose columns
 // share 128-byte lines of a 16-bit row are placed on one XCD (the dispatcher deals workgroup ids
@@ -60,175 +61,628 @@ __device__ __forceinline__ int zaddr(int c, int n2, int k1) {
     return (c & 3) + 4 * ((c >> 2) * Cm<P>::ZC + (Cm<P>::R + 1) * n2 + k1);
 }
 
-template <int CT>
-__device__ __forceinline__ void store1h(void* p, int64_t i, float v) {
-    ((uint16_t*)p)[i] = (uint16_t)(pack2<CT>(v, 0.f) & 0xffffu);
+// K (1, 2, 4 or 8) consecutive 16-bit elements <-> fp32, and K consecutive 32-bit words (one
+// access each; the index is a multiple of K)
+template <int CT, int K>
+__device__ __forceinline__ void ldh(const void* p, int64_t i, float* x) {
+    const uint16_t* q = (const uint16_t*)p + i;
+    if constexpr (K == 1) {
+        x[0] = unpack_lo<CT>(*q);
+    } else if constexpr (K == 2) {
+        const uint32_t w = *(const uint32_t*)q;
+        x[0] = unpack_lo<CT>(w); x[1] = unpack_hi<CT>(w);
+    } else if constexpr (K == 4) {
+        const uint2 w = *(const uint2*)q;
+        x[0] = unpack_lo<CT>(w.x); x[1] = unpack_hi<CT>(w.x); x[2] = unpack_lo<CT>(w.y); x[3] = unpack_hi<CT>(w.y);
+    } else {
+        const uint4 w = *(const uint4*)q;
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { x[2 * i] = unpack_lo<CT>(ww[i]); x[2 * i + 1] = unpack_hi<CT>(ww[i]); }
+    }
+}
+template <int CT, int K>
+__device__ __forceinline__ void sth(void* p, int64_t i, const float* x) {
+    uint16_t* q = (uint16_t*)p + i;
+    if constexpr (K == 1) {
+        *q = (uint16_t)(pack2<CT>(x[0], 0.f) & 0xffffu);
+    } else if constexpr (K == 2) {
+        *(uint32_t*)q = pack2<CT>(x[0], x[1]);
+    } else if constexpr (K == 4) {
+        *(uint2*)q = make_uint2(pack2<CT>(x[0], x[1]), pack2<CT>(x[2], x[3]));
+    } else {
+        *(uint4*)q = make_uint4(pack2<CT>(x[0], x[1]), pack2<CT>(x[2], x[3]), pack2<CT>(x[4], x[5]), pack2<CT>(x[6], x[7]));
+    }
+}
+template <int K>
+__device__ __forceinline__ void ldw(const uint32_t* p, int64_t i, uint32_t* w) {
+    if constexpr (K == 1) {
+        w[0] = p[i];
+    } else if constexpr (K == 2) {
+        const uint2 t = *(const uint2*)(p + i);
+        w[0] = t.x; w[1] = t.y;
+    } else {
+#pragma unroll
+        for (int h = 0; h < K / 4; ++h) {
+            const uint4 t = *(const uint4*)(p + i + 4 * h);
+            w[4 * h] = t.x; w[4 * h + 1] = t.y; w[4 * h + 2] = t.z; w[4 * h + 3] = t.w;
+        }
+    }
+}
+template <int K>
+__device__ __forceinline__ void stw(uint32_t* p, int64_t i, const uint32_t* w) {
+    if constexpr (K == 1) *(p + i) = w[0];
+    else if constexpr (K == 2) *(uint2*)(p + i) = make_uint2(w[0], w[1]);
+    else {
+#pragma unroll
+        for (int h = 0; h < K / 4; ++h) *(uint4*)(p + i + 4 * h) = make_uint4(w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]);
+    }
 }
 
+// Column placement: tile g of the NCG tiles of a stage unit holds, in its L index x, global
+// column NCG x + g of the block, so a lane's NCG tiles cover NCG consecutive columns and every
+// global access moves NCG elements at once (whole 128-byte lines per row and instruction).  In
+// LDS the same value sits at slot 16 g + x.
+
 template <int CT, int P>
-__global__ void __launch_bounds__(512, 2) colmx_fwd_kernel(const ColArgs a) {
+__global__ void __launch_bounds__(512, 4) colmx_fwd_kernel(const ColArgs a) {
     using C = Cm<P>;
     constexpr int R = C::R, H = C::H, RB = C::RB, HB = C::HB, NCG = C::NCG;
     __shared__ uint32_t Y[C::CB * C::YC];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, x = lane & 15;
     const int64_t s = blockIdx.y, n_lo0 = block_col0<P>();
+    const int64_t col0 = n_lo0 + NCG * x;  // this lane's first column
     int64_t row0, row1;
     seq_rows(a, a.seq0 + s, row0, row1);
     const float2* twc = (const float2*)a.tw_col;
 
-    // Stage 1, per (n2, 16-column group): radix R over n1 < H (gated pairs packed as complex
-    // x_b + i x_{b+1}), times w_P^{n2 k1}, into the exchange.
-    MatImg<CT> f1[RB][HB];
-    static_for<0, RB>([&](auto rb) LCV_INLINE {
-        static_for<0, HB>([&](auto kc) LCV_INLINE {
-            f1[rb][kc] = load_img<CT>(a.img, C::G.f1 + decltype(rb)::value * HB + decltype(kc)::value, lane);
-        });
-    });
-    static_for<0, 2 * NCG>([&](auto ii) LCV_INLINE {
-        const int u = wave + 8 * decltype(ii)::value, n2 = u & 15, c = 16 * (u >> 4) + x;
-        const int64_t col = n_lo0 + c;
-        Operand<CT> op[HB];
-        static_for<0, HB>([&](auto kk) LCV_INLINE {
-            constexpr int kc = decltype(kk)::value;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int n1 = 16 * kc + 4 * g + j;
-                const int64_t n = kRow * (16 * n1 + n2) + col;
-                const bool ok = n1 < H && n < a.N;
-                const int64_t e = ok ? n : col;  // a valid element of the same rows
-                float re = load1<CT>(a.u, row0 + e), im = 0.f;
-                if (a.q) re *= load1<CT>(a.q, row0 + e);
-                if (row1 >= 0) {
-                    im = load1<CT>(a.u, row1 + e);
-                    if (a.q) im *= load1<CT>(a.q, row1 + e);
-                }
-                op[kc].w[j] = ok ? pack2<CT>(re, im) : 0u;
-            }
-        });
-        static_for<0, RB>([&](auto r) LCV_INLINE {
-            constexpr int rb = decltype(r)::value;
-            f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
-            static_for<0, HB>([&](auto kk) LCV_INLINE {
-                stage_keep_acc<CT>(f1[rb][decltype(kk)::value], op[decltype(kk)::value], re, im);
+    // Stage 1, per n2 (two per wave), NCG tiles: radix R over n1 < H (gated pairs packed as
+    // complex x_b + i x_{b+1}), times w_P^{n2 k1}, into the exchange.
+    // The first-stage blocks stay in registers when they are few (P <= 512); at P = 1024
+    // (eight blocks) they are read where they are used, from the cache.
+    constexpr bool KEEP_F1 = RB * HB <= 4;
+    MatImg<CT> f1[KEEP_F1 ? RB : 1][KEEP_F1 ? HB : 1];
+    auto f1img = [&](int rb, int kc) LCV_INLINE { return load_img<CT>(a.img, C::G.f1 + rb * HB + kc, lane); };
+    if constexpr (KEEP_F1) {
+        static_for<0, RB>([&](auto rb) LCV_INLINE {
+            static_for<0, HB>([&](auto kc) LCV_INLINE {
+                f1[rb][kc] = f1img(decltype(rb)::value, decltype(kc)::value);
             });
+        });
+    }
+    // All loads of the stage first (raw words: NCG 16-bit columns per access), then the
+    // arithmetic, so one memory latency covers both n2 of the wave.
+    // (P = 1024 has two K chunks per n2: its n2 go one at a time, which keeps it in 128 VGPRs)
+    constexpr int RW = (NCG + 1) / 2;  // 32-bit words per access
+    constexpr int NB = HB == 1 ? 2 : 1;  // n2 values whose loads are issued together
+    uint32_t ru[NB][HB][4][RW], rq[NB][HB][4][RW], ru1[NB][HB][4][RW], rq1[NB][HB][4][RW];
+    bool okv[NB][HB][4];
+    auto ldraw = [&](const void* p, int64_t i, uint32_t* w) LCV_INLINE {
+        const uint16_t* h = (const uint16_t*)p + i;
+        if constexpr (NCG == 1) w[0] = *h;
+        else if constexpr (NCG == 2) w[0] = *(const uint32_t*)h;
+        else { const uint2 t = *(const uint2*)h; w[0] = t.x; w[1] = t.y; }
+    };
+    auto raw_f = [&](const uint32_t* w, int q) LCV_INLINE {
+        return (q & 1) ? unpack_hi<CT>(w[q >> 1]) : unpack_lo<CT>(w[q >> 1]);
+    };
+    static_for<0, 2 / NB>([&](auto gg) LCV_INLINE {
+        constexpr int gi = decltype(gg)::value;
+        static_for<0, NB>([&](auto ii) LCV_INLINE {
+            constexpr int i = decltype(ii)::value;
+            const int n2 = wave + 8 * (NB * gi + i);
+            static_for<0, HB>([&](auto kk) LCV_INLINE {
+                constexpr int kc = decltype(kk)::value;
+                static_for<0, 4>([&](auto jj) LCV_INLINE {
+                    constexpr int j = decltype(jj)::value;
+                    const int n1 = 16 * kc + 4 * g + j;
+                    const int64_t n = kRow * (16 * n1 + n2) + col0;
+                    const bool ok = n1 < H && n < a.N;  // N is a multiple of 8: all NCG columns alike
+                    const int64_t e = ok ? n : col0;    // a valid element of the same rows
+                    okv[i][kc][j] = ok;
+                    ldraw(a.u, row0 + e, ru[i][kc][j]);
+                    if (a.q) ldraw(a.q, row0 + e, rq[i][kc][j]);
+                    if (row1 >= 0) {
+                        ldraw(a.u, row1 + e, ru1[i][kc][j]);
+                        if (a.q) ldraw(a.q, row1 + e, rq1[i][kc][j]);
+                    }
+                });
+            });
+        });
+        static_for<0, NB>([&](auto ii) LCV_INLINE {
+            constexpr int i = decltype(ii)::value;
+            const int n2 = wave + 8 * (NB * gi + i);
+            Operand<CT> op[NCG][HB];
+            static_for<0, HB>([&](auto kk) LCV_INLINE {
+                constexpr int kc = decltype(kk)::value;
+                static_for<0, 4>([&](auto jj) LCV_INLINE {
+                    constexpr int j = decltype(jj)::value;
+                    static_for<0, NCG>([&](auto qq) LCV_INLINE {
+                        constexpr int q = decltype(qq)::value;
+                        float re = raw_f(ru[i][kc][j], q), im = 0.f;
+                        if (a.q) re *= raw_f(rq[i][kc][j], q);
+                        if (row1 >= 0) {
+                            im = raw_f(ru1[i][kc][j], q);
+                            if (a.q) im *= raw_f(rq1[i][kc][j], q);
+                        }
+                        op[q][kc].w[j] = okv[i][kc][j] ? pack2<CT>(re, im) : 0u;
+                    });
+                });
+            });
+            // w_P^{n2 k1} for k1 = 16 rb + 4 g + j: a table value per rb times powers of w_P^{n2}
+            const float2 wstep = twc[n2];
+            static_for<0, RB>([&](auto r) LCV_INLINE {
+                constexpr int rb = decltype(r)::value;
+                float2 tw[4];
+                tw[0] = twc[n2 * (16 * rb + 4 * g)];  // < P
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int k1 = 16 * rb + 4 * g + j;
-                const float2 w = twc[n2 * k1];  // n2 k1 < P
-                float xr = re[j], xi = im[j];
-                cmul(xr, xi, w.x, w.y);
-                Y[yaddr<P>(c, k1, n2)] = pack2<CT>(xr, xi);
-            }
+                for (int j = 1; j < 4; ++j) tw[j] = cmulf(tw[j - 1], wstep);
+                static_for<0, NCG>([&](auto qq) LCV_INLINE {
+                    constexpr int q = decltype(qq)::value;
+                    const int cs = 16 * q + x;
+                    f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
+                    static_for<0, HB>([&](auto kk) LCV_INLINE {
+                        constexpr int kc = decltype(kk)::value;
+                        if constexpr (KEEP_F1) stage_keep_acc<CT>(f1[rb][kc], op[q][kc], re, im);
+                        else stage_keep_acc<CT>(f1img(rb, kc), op[q][kc], re, im);
+                    });
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int k1 = 16 * rb + 4 * g + j;
+                        float xr = re[j], xi = im[j];
+                        cmul(xr, xi, tw[j].x, tw[j].y);
+                        Y[yaddr<P>(cs, k1, n2)] = pack2<CT>(xr, xi);
+                    }
+                });
+            });
         });
     });
     __syncthreads();
 
-    // Stage 2, per (k1, 16-column group): 16-point DFT over n2, the four-step twiddle
+    // Stage 2, per k1 (R/8 per wave), NCG tiles: 16-point DFT over n2, the four-step twiddle
     // w_M^{n_lo k_hi}, store rows k_hi = k1 + R k2 of the workspace.
     const MatImg<CT> f16 = load_img<CT>(a.img, C::G.f16, lane);
     const int64_t mask = a.M - 1;
     uint32_t* ws = (uint32_t*)a.ws;
-    static_for<0, R * NCG / 8>([&](auto ii) LCV_INLINE {
-        const int u = wave + 8 * decltype(ii)::value, k1 = u % R, c = 16 * (u / R) + x;
-        const int64_t n_lo = n_lo0 + c;
-        Operand<CT> op;
+    // w_M^{n_lo k_hi} for k_hi = k1 + R (4 g + j), k1 = wave + 8 i: per column, a base for
+    // i = 0, a step for i, and a step for j (products of fp32 table values; at most 11 steps)
+    float2 wb[NCG], wi[NCG], wj[NCG];
+    static_for<0, NCG>([&](auto qq) LCV_INLINE {
+        constexpr int q = decltype(qq)::value;
+        const int64_t n_lo = col0 + q;
+        wb[q] = tw_m(a.tw_lo, a.tw_hi, (n_lo * (wave + 4 * g * R)) & mask);
+        wi[q] = tw_m(a.tw_lo, a.tw_hi, (n_lo * 8) & mask);
+        wj[q] = tw_m(a.tw_lo, a.tw_hi, (n_lo * R) & mask);
+    });
+    static_for<0, R / 8>([&](auto ii) LCV_INLINE {
+        const int k1 = wave + 8 * decltype(ii)::value;
+        uint32_t out[4][NCG];
+        static_for<0, NCG>([&](auto qq) LCV_INLINE {
+            constexpr int q = decltype(qq)::value;
+            const int cs = 16 * q + x;
+            Operand<CT> op;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) op.w[j] = Y[yaddr<P>(c, k1, 4 * g + j)];
-        Tile t = stage_keep<CT>(f16, op);  // rows k2 = 4 g + j
-        float2 w = tw_m(a.tw_lo, a.tw_hi, (n_lo * (k1 + 4 * g * R)) & mask);
-        const float2 st = tw_m(a.tw_lo, a.tw_hi, (n_lo * R) & mask);
+            for (int j = 0; j < 4; ++j) op.w[j] = Y[yaddr<P>(cs, k1, 4 * g + j)];
+            Tile t = stage_keep<CT>(f16, op);  // rows k2 = 4 g + j
+            float2 w = wb[q];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float xr = t.re[j], xi = t.im[j];
-            cmul(xr, xi, w.x, w.y);
-            w = cmulf(w, st);
-            ws[(s * P + k1 + R * (4 * g + j)) * kRow + n_lo] = pack2<CT>(xr, xi);
-        }
+            for (int j = 0; j < 4; ++j) {
+                float xr = t.re[j], xi = t.im[j];
+                cmul(xr, xi, w.x, w.y);
+                w = cmulf(w, wj[q]);
+                out[j][q] = pack2<CT>(xr, xi);
+            }
+            wb[q] = cmulf(wb[q], wi[q]);
+        });
+#pragma unroll
+        for (int j = 0; j < 4; ++j) stw<NCG>(ws, (s * P + k1 + R * (4 * g + j)) * kRow + col0, out[j]);
     });
 }
 
 template <int CT, int P>
-__global__ void __launch_bounds__(512, 2) colmx_inv_kernel(const ColArgs a) {
+__global__ void __launch_bounds__(512, 4) colmx_inv_kernel(const ColArgs a) {
     using C = Cm<P>;
     constexpr int R = C::R, H = C::H, RB = C::RB, HB = C::HB, NCG = C::NCG;
     __shared__ uint32_t Z[C::CB * C::ZC];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, x = lane & 15;
     const int64_t s = blockIdx.y, n_lo0 = block_col0<P>();
+    const int64_t col0 = n_lo0 + NCG * x;
     int64_t row0, row1;
     seq_rows(a, a.seq0 + s, row0, row1);
     const float2* twc = (const float2*)a.tw_col;
     const int64_t mask = a.M - 1;
     const uint32_t* ws = (const uint32_t*)a.ws;
 
-    // Stage 1, per (k1, 16-column group): rows k_hi = k1 + R k2 of the workspace, times
+    // Stage 1, per k1 (R/8 per wave), NCG tiles: rows k_hi = k1 + R k2 of the workspace, times
     // conj(w_M^{n_lo k_hi}), 16-point inverse DFT over k2, times conj(w_P^{n2 k1}), into the
     // exchange.
     const MatImg<CT> i16 = load_img<CT>(a.img, C::G.i16, lane);
-    static_for<0, R * NCG / 8>([&](auto ii) LCV_INLINE {
-        const int u = wave + 8 * decltype(ii)::value, k1 = u % R, c = 16 * (u / R) + x;
-        const int64_t n_lo = n_lo0 + c;
-        float2 w = tw_m(a.tw_lo, a.tw_hi, (n_lo * (k1 + 4 * g * R)) & mask);
-        const float2 st = tw_m(a.tw_lo, a.tw_hi, (n_lo * R) & mask);
-        Operand<CT> op;
+    // conj(w_M^{n_lo k_hi}) factors as in the forward pass: base, step for i, step for j
+    float2 wb[NCG], wi[NCG], wj[NCG];
+    static_for<0, NCG>([&](auto qq) LCV_INLINE {
+        constexpr int q = decltype(qq)::value;
+        const int64_t n_lo = col0 + q;
+        wb[q] = tw_m(a.tw_lo, a.tw_hi, (n_lo * (wave + 4 * g * R)) & mask);
+        wi[q] = tw_m(a.tw_lo, a.tw_hi, (n_lo * 8) & mask);
+        wj[q] = tw_m(a.tw_lo, a.tw_hi, (n_lo * R) & mask);
+    });
+    uint32_t in[R / 8][4][NCG];
+    static_for<0, R / 8>([&](auto ii) LCV_INLINE {
+        constexpr int i = decltype(ii)::value;
+        const int k1 = wave + 8 * i;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t z = ws[(s * P + k1 + R * (4 * g + j)) * kRow + n_lo];
-            float zr = unpack_lo<CT>(z), zi = unpack_hi<CT>(z);
-            cmulc(zr, zi, w.x, w.y);
-            w = cmulf(w, st);
-            op.w[j] = pack2<CT>(zr, zi);
-        }
-        Tile t = stage_keep<CT>(i16, op);  // rows n2 = 4 g + j
+        for (int j = 0; j < 4; ++j) ldw<NCG>(ws, (s * P + k1 + R * (4 * g + j)) * kRow + col0, in[i][j]);
+    });
+    static_for<0, R / 8>([&](auto ii) LCV_INLINE {
+        constexpr int i = decltype(ii)::value;
+        const int k1 = wave + 8 * i;
+        // conj(w_P^{n2 k1}) for n2 = 4 g + j
+        const float2 p1 = twc[k1];
+        float2 tp[4];
+        tp[0] = twc[4 * g * k1];  // < P
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n2 = 4 * g + j;
-            const float2 wc = twc[n2 * k1];
-            float zr = t.re[j], zi = t.im[j];
-            cmulc(zr, zi, wc.x, wc.y);
-            Z[zaddr<P>(c, n2, k1)] = pack2<CT>(zr, zi);
-        }
+        for (int j = 1; j < 4; ++j) tp[j] = cmulf(tp[j - 1], p1);
+        static_for<0, NCG>([&](auto qq) LCV_INLINE {
+            constexpr int q = decltype(qq)::value;
+            const int cs = 16 * q + x;
+            float2 w = wb[q];
+            Operand<CT> op;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float zr = unpack_lo<CT>(in[i][j][q]), zi = unpack_hi<CT>(in[i][j][q]);
+                cmulc(zr, zi, w.x, w.y);
+                w = cmulf(w, wj[q]);
+                op.w[j] = pack2<CT>(zr, zi);
+            }
+            wb[q] = cmulf(wb[q], wi[q]);
+            Tile t = stage_keep<CT>(i16, op);  // rows n2 = 4 g + j
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n2 = 4 * g + j;
+                float zr = t.re[j], zi = t.im[j];
+                cmulc(zr, zi, tp[j].x, tp[j].y);
+                Z[zaddr<P>(cs, n2, k1)] = pack2<CT>(zr, zi);
+            }
+        });
     });
     __syncthreads();
 
-    // Stage 2, per (n2, 16-column group): inverse radix R over k1 for the kept rows n1 < H,
-    // post-gate, store rows n_hi = 16 n1 + n2 (and n < N) of the output pair.
+    // Stage 2, per n2 (two per wave), NCG tiles: inverse radix R over k1 for the kept rows
+    // n1 < H, post-gate, store rows n_hi = 16 n1 + n2 (and n < N) of the output pair.
     MatImg<CT> i2[HB][RB];
     static_for<0, HB>([&](auto rb) LCV_INLINE {
         static_for<0, RB>([&](auto kc) LCV_INLINE {
             i2[rb][kc] = load_img<CT>(a.img, C::G.i2 + decltype(rb)::value * RB + decltype(kc)::value, lane);
         });
     });
-    static_for<0, 2 * NCG>([&](auto ii) LCV_INLINE {
-        const int u = wave + 8 * decltype(ii)::value, n2 = u & 15, c = 16 * (u >> 4) + x;
-        const int64_t col = n_lo0 + c;
-        Operand<CT> op[RB];
-        static_for<0, RB>([&](auto kk) LCV_INLINE {
-            constexpr int kc = decltype(kk)::value;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) op[kc].w[j] = Z[zaddr<P>(c, n2, 16 * kc + 4 * g + j)];
-        });
+    static_for<0, 2>([&](auto ii) LCV_INLINE {
+        const int n2 = wave + 8 * decltype(ii)::value;
         static_for<0, HB>([&](auto r) LCV_INLINE {
             constexpr int rb = decltype(r)::value;
-            f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
-            static_for<0, RB>([&](auto kk) LCV_INLINE {
-                stage_keep_acc<CT>(i2[rb][decltype(kk)::value], op[decltype(kk)::value], re, im);
+            Tile acc[NCG];
+            static_for<0, NCG>([&](auto qq) LCV_INLINE {
+                constexpr int q = decltype(qq)::value;
+                const int cs = 16 * q + x;
+                f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
+                static_for<0, RB>([&](auto kk) LCV_INLINE {
+                    constexpr int kc = decltype(kk)::value;
+                    Operand<CT> op;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) op.w[j] = Z[zaddr<P>(cs, n2, 16 * kc + 4 * g + j)];
+                    stage_keep_acc<CT>(i2[rb][kc], op, re, im);
+                });
+                acc[q] = Tile{re, im};
             });
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int n1 = 16 * rb + 4 * g + j;
-                const int64_t n = kRow * (16 * n1 + n2) + col;
+                const int64_t n = kRow * (16 * n1 + n2) + col0;
                 const bool ok = n1 < H && n < a.N;
-                const int64_t e = ok ? n : col;
-                float yr = re[j], yi = im[j];
-                if (a.v) yr *= load1<CT>(a.v, row0 + e);
-                if (row1 >= 0 && a.v) yi *= load1<CT>(a.v, row1 + e);
+                const int64_t e = ok ? n : col0;
+                float yr[NCG], yi[NCG], t[NCG];
+                static_for<0, NCG>([&](auto qq) LCV_INLINE {
+                    constexpr int q = decltype(qq)::value;
+                    yr[q] = acc[q].re[j];
+                    yi[q] = acc[q].im[j];
+                });
+                if (a.v) {
+                    ldh<CT, NCG>(a.v, row0 + e, t);
+#pragma unroll
+                    for (int q = 0; q < NCG; ++q) yr[q] *= t[q];
+                    if (row1 >= 0) {
+                        ldh<CT, NCG>(a.v, row1 + e, t);
+#pragma unroll
+                        for (int q = 0; q < NCG; ++q) yi[q] *= t[q];
+                    }
+                }
                 if (ok) {
-                    store1h<CT>(a.y, row0 + n, yr);
-                    if (row1 >= 0) store1h<CT>(a.y, row1 + n, yi);
+                    sth<CT, NCG>(a.y, row0 + n, yr);
+                    if (row1 >= 0) sth<CT, NCG>(a.y, row1 + n, yi);
                 }
             }
         });
     });
+}
+
+// ---- short columns, P = 16 R with R = 1, 2, 4, 8 (M1 = 16 .. 128): registers only -------------
+//
+// The same factorization with a first digit of at most 8 values: its DFT (radix R over n1,
+// R/2 nonzero inputs forward, R/2 kept outputs inverse) runs on the vector ALU with constant
+// coefficients, and the 16-point DFT over n2 on the matrix cores.  A lane's operand already
+// holds the four n2 = 4 g + j of its columns, so no data crosses lanes and nothing goes
+// through LDS: every wave works alone on 16 NCG columns of one sequence, NCG consecutive
+// columns per lane (2 to 16 bytes per row and access).
+
+// exp(-2 pi i e / R) for R <= 8 (constants after unrolling)
+__device__ __forceinline__ float2 w_small(int e, int R) {
+    constexpr float c = 0.70710678118654752f;
+    const float2 t[8] = {{1.f, 0.f}, {c, -c}, {0.f, -1.f}, {-c, -c}, {-1.f, 0.f}, {-c, c}, {0.f, 1.f}, {c, c}};
+    return t[((e % R + R) % R) * (8 / R)];
+}
+
+template <int P>
+struct Cr {
+    static constexpr ColMxGrid G = colmx_grid(P);
+    static constexpr int R = P / 16, H = R > 1 ? R / 2 : 1;  // n1 values in, n1 values kept
+    static constexpr int NCG = 4 / H;                         // columns per lane: 4, 4, 2, 1
+    static constexpr int COLS = 16 * NCG;                     // columns per wave
+};
+
+template <int CT, int P>
+__global__ void __launch_bounds__(256, 4) colreg_fwd_kernel(const ColArgs a) {
+    using C = Cr<P>;
+    constexpr int R = C::R, H = C::H, NCG = C::NCG, RW = (NCG + 1) / 2;
+    const int lane = threadIdx.x & 63, g = lane >> 4, x = lane & 15;
+    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // wave of the sequence
+    const int64_t s = blockIdx.y;
+    const int64_t col0 = wid * C::COLS + NCG * x;
+    int64_t row0, row1;
+    seq_rows(a, a.seq0 + s, row0, row1);
+    const float2* twc = (const float2*)a.tw_col;
+    const int64_t mask = a.M - 1;
+
+    // gated input pairs x[16 n1 + 4 g + j] of this lane's columns, packed in the compute type
+    // (R = 1: only rows 4 g + j < 8 are nonzero)
+    uint32_t xin[H][4][NCG];
+    {
+        uint32_t ru[H][4][RW], rq[H][4][RW], ru1[H][4][RW], rq1[H][4][RW];
+        bool okv[H][4];
+        auto ldraw = [&](const void* p, int64_t i, uint32_t* w) LCV_INLINE {
+            const uint16_t* h = (const uint16_t*)p + i;
+            if constexpr (NCG == 2) w[0] = *(const uint32_t*)h;
+            else if constexpr (NCG == 4) { const uint2 t = *(const uint2*)h; w[0] = t.x; w[1] = t.y; }
+            else { const uint4 t = *(const uint4*)h; w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w; }
+        };
+        static_for<0, H>([&](auto nn) LCV_INLINE {
+            constexpr int n1 = decltype(nn)::value;
+            static_for<0, 4>([&](auto jj) LCV_INLINE {
+                constexpr int j = decltype(jj)::value;
+                const int nh = 16 * n1 + 4 * g + j;
+                const int64_t n = kRow * nh + col0;
+                const bool ok = (R > 1 || nh < 8) && n < a.N;
+                const int64_t e = ok ? n : col0;
+                okv[n1][j] = ok;
+                ldraw(a.u, row0 + e, ru[n1][j]);
+                if (a.q) ldraw(a.q, row0 + e, rq[n1][j]);
+                if (row1 >= 0) {
+                    ldraw(a.u, row1 + e, ru1[n1][j]);
+                    if (a.q) ldraw(a.q, row1 + e, rq1[n1][j]);
+                }
+            });
+        });
+        auto raw_f = [&](const uint32_t* w, int q) LCV_INLINE {
+            return (q & 1) ? unpack_hi<CT>(w[q >> 1]) : unpack_lo<CT>(w[q >> 1]);
+        };
+        static_for<0, H>([&](auto nn) LCV_INLINE {
+            constexpr int n1 = decltype(nn)::value;
+            static_for<0, 4>([&](auto jj) LCV_INLINE {
+                constexpr int j = decltype(jj)::value;
+                static_for<0, NCG>([&](auto qq) LCV_INLINE {
+                    constexpr int q = decltype(qq)::value;
+                    float re = raw_f(ru[n1][j], q), im = 0.f;
+                    if (a.q) re *= raw_f(rq[n1][j], q);
+                    if (row1 >= 0) {
+                        im = raw_f(ru1[n1][j], q);
+                        if (a.q) im *= raw_f(rq1[n1][j], q);
+                    }
+                    xin[n1][j][q] = okv[n1][j] ? pack2<CT>(re, im) : 0u;
+                });
+            });
+        });
+    }
+
+    const MatImg<CT> f16 = load_img<CT>(a.img, C::G.f16, lane);
+    uint32_t* ws = (uint32_t*)a.ws;
+    // four-step twiddle w_M^{n_lo k_hi}, n_lo = col0 + q, k_hi = k1 + R (4 g + j):
+    // w_M^{col0 k_hi} w_M^{q k_hi}, stepped along j by w_M^{col0 R} and w_M^{R}
+    // Per-k1 factors advance from k1 to k1 + 1 by one product each (at most 7 steps), so the
+    // tables are read once:  w_P^{4 g k1}, w_P^{k1}, w_M^{col0 (k1 + 4 g R)}, w_M^{k1 + 4 g R}.
+    const float2 wcR = tw_m(a.tw_lo, a.tw_hi, (col0 * R) & mask);
+    const float2 w1R = ((const float2*)a.tw_lo)[R];
+    const float2 tb1 = twc[4 * g], ts1 = twc[1 % P];
+    const float2 wb1 = tw_m(a.tw_lo, a.tw_hi, col0 & mask), sb1 = ((const float2*)a.tw_lo)[1];
+    float2 tbk = make_float2(1.f, 0.f), tsk = make_float2(1.f, 0.f);
+    float2 wbk = tw_m(a.tw_lo, a.tw_hi, (col0 * 4 * g * R) & mask);
+    float2 sbk = ((const float2*)a.tw_lo)[4 * g * R];
+    static_for<0, R>([&](auto kk) LCV_INLINE {
+        constexpr int k1 = decltype(kk)::value;
+        // first digit: y[j][q] = w_P^{n2 k1} sum_{n1 < H} w_R^{n1 k1} x[n1][j][q], n2 = 4 g + j
+        Operand<CT> op[NCG];
+        const float2 ts = tsk;
+        float2 tw = tbk;
+        static_for<0, 4>([&](auto jj) LCV_INLINE {
+            constexpr int j = decltype(jj)::value;
+            static_for<0, NCG>([&](auto qq) LCV_INLINE {
+                constexpr int q = decltype(qq)::value;
+                float yr = 0.f, yi = 0.f;
+                static_for<0, H>([&](auto nn) LCV_INLINE {
+                    constexpr int n1 = decltype(nn)::value;
+                    const float xr = unpack_lo<CT>(xin[n1][j][q]), xi = unpack_hi<CT>(xin[n1][j][q]);
+                    if constexpr (R == 1 || (n1 * k1) % R == 0) {
+                        yr += xr; yi += xi;
+                    } else {
+                        const float2 w = w_small(n1 * k1, R);
+                        yr += xr * w.x - xi * w.y;
+                        yi += xr * w.y + xi * w.x;
+                    }
+                });
+                if constexpr (k1 > 0) cmul(yr, yi, tw.x, tw.y);
+                op[q].w[j] = pack2<CT>(yr, yi);
+            });
+            tw = cmulf(tw, ts);
+        });
+        // 16-point DFT over n2, rows k2 = 4 g + j; twiddle; store rows k_hi
+        const float2 wb = wbk, sb = sbk;
+        tbk = cmulf(tbk, tb1);
+        tsk = cmulf(tsk, ts1);
+        wbk = cmulf(wbk, wb1);
+        sbk = cmulf(sbk, sb1);
+        uint32_t out[4][NCG];
+        static_for<0, NCG>([&](auto qq) LCV_INLINE {
+            constexpr int q = decltype(qq)::value;
+            Tile t = stage_keep<CT>(f16, op[q]);
+            float2 w = wb, sj = sb;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // w_M^{(col0 + q) k_hi} = w_M^{col0 k_hi} (w_M^{k_hi})^q
+                float2 wq = w;
+#pragma unroll
+                for (int r = 0; r < q; ++r) wq = cmulf(wq, sj);
+                float xr = t.re[j], xi = t.im[j];
+                cmul(xr, xi, wq.x, wq.y);
+                out[j][q] = pack2<CT>(xr, xi);
+                w = cmulf(w, wcR);
+                sj = cmulf(sj, w1R);
+            }
+        });
+#pragma unroll
+        for (int j = 0; j < 4; ++j) stw<NCG>(ws, (s * P + k1 + R * (4 * g + j)) * kRow + col0, out[j]);
+    });
+}
+
+template <int CT, int P>
+__global__ void __launch_bounds__(256, 4) colreg_inv_kernel(const ColArgs a) {
+    using C = Cr<P>;
+    constexpr int R = C::R, H = C::H, NCG = C::NCG;
+    const int lane = threadIdx.x & 63, g = lane >> 4, x = lane & 15;
+    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t s = blockIdx.y;
+    const int64_t col0 = wid * C::COLS + NCG * x;
+    int64_t row0, row1;
+    seq_rows(a, a.seq0 + s, row0, row1);
+    const float2* twc = (const float2*)a.tw_col;
+    const int64_t mask = a.M - 1;
+    const uint32_t* ws = (const uint32_t*)a.ws;
+    const MatImg<CT> i16 = load_img<CT>(a.img, C::G.i16, lane);
+
+    // y[n1][j][q] for rows n_hi = 16 n1 + 4 g + j < P / 2
+    float yr[H][4][NCG], yi[H][4][NCG];
+    const float2 wcR = tw_m(a.tw_lo, a.tw_hi, (col0 * R) & mask);
+    const float2 w1R = ((const float2*)a.tw_lo)[R];
+    // per-k1 factors stepped from k1 to k1 + 1, as in the forward pass
+    const float2 tb1 = twc[4 * g], ts1 = twc[1 % P];
+    const float2 wb1 = tw_m(a.tw_lo, a.tw_hi, col0 & mask), sb1 = ((const float2*)a.tw_lo)[1];
+    float2 tbk = make_float2(1.f, 0.f), tsk = make_float2(1.f, 0.f);
+    float2 wbk = tw_m(a.tw_lo, a.tw_hi, (col0 * 4 * g * R) & mask);
+    float2 sbk = ((const float2*)a.tw_lo)[4 * g * R];
+    uint32_t in[2][4][NCG];  // workspace rows of k1 and k1 + 1
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ldw<NCG>(ws, (s * P + R * (4 * g + j)) * kRow + col0, in[0][j]);
+    static_for<0, R>([&](auto kk) LCV_INLINE {
+        constexpr int k1 = decltype(kk)::value, b = k1 & 1;
+        if constexpr (k1 + 1 < R) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ldw<NCG>(ws, (s * P + k1 + 1 + R * (4 * g + j)) * kRow + col0, in[1 - b][j]);
+        }
+        // conj(w_M^{n_lo k_hi}), stepped as in the forward pass
+        const float2 wb = wbk, sb = sbk, tb = tbk, ts = tsk;
+        tbk = cmulf(tbk, tb1);
+        tsk = cmulf(tsk, ts1);
+        wbk = cmulf(wbk, wb1);
+        sbk = cmulf(sbk, sb1);
+        Operand<CT> op[NCG];
+        {
+            float2 w = wb, sj = sb;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float2 wq = w;
+                static_for<0, NCG>([&](auto qq) LCV_INLINE {
+                    constexpr int q = decltype(qq)::value;
+                    float zr = unpack_lo<CT>(in[b][j][q]), zi = unpack_hi<CT>(in[b][j][q]);
+                    cmulc(zr, zi, wq.x, wq.y);
+                    op[q].w[j] = pack2<CT>(zr, zi);
+                    wq = cmulf(wq, sj);
+                });
+                w = cmulf(w, wcR);
+                sj = cmulf(sj, w1R);
+            }
+        }
+        // 16-point inverse DFT over k2 (rows n2 = 4 g + j), conj(w_P^{n2 k1}), then the first
+        // digit: y[n1] += w_R^{-n1 k1} z for the kept n1 < H
+        static_for<0, NCG>([&](auto qq) LCV_INLINE {
+            constexpr int q = decltype(qq)::value;
+            Tile t = stage_keep<CT>(i16, op[q]);
+            float2 tw = tb;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float zr = t.re[j], zi = t.im[j];
+                if constexpr (k1 > 0) cmulc(zr, zi, tw.x, tw.y);
+                tw = cmulf(tw, ts);
+                static_for<0, H>([&](auto nn) LCV_INLINE {
+                    constexpr int n1 = decltype(nn)::value;
+                    float ar = zr, ai = zi;
+                    if constexpr (R > 1 && (n1 * k1) % R != 0) {
+                        const float2 w = w_small(-n1 * k1, R);
+                        ar = zr * w.x - zi * w.y;
+                        ai = zr * w.y + zi * w.x;
+                    }
+                    if constexpr (k1 == 0) {
+                        yr[n1][j][q] = ar;
+                        yi[n1][j][q] = ai;
+                    } else {
+                        yr[n1][j][q] += ar;
+                        yi[n1][j][q] += ai;
+                    }
+                });
+            }
+        });
+    });
+    // gate and store rows n_hi = 16 n1 + 4 g + j (R = 1: only 4 g + j < 8)
+    static_for<0, H>([&](auto nn) LCV_INLINE {
+        constexpr int n1 = decltype(nn)::value;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int nh = 16 * n1 + 4 * g + j;
+            const int64_t n = kRow * nh + col0;
+            const bool ok = (R > 1 || nh < 8) && n < a.N;
+            const int64_t e = ok ? n : col0;
+            float vr[NCG], vi[NCG], t[NCG];
+#pragma unroll
+            for (int q = 0; q < NCG; ++q) { vr[q] = yr[n1][j][q]; vi[q] = yi[n1][j][q]; }
+            if (a.v) {
+                ldh<CT, NCG>(a.v, row0 + e, t);
+#pragma unroll
+                for (int q = 0; q < NCG; ++q) vr[q] *= t[q];
+                if (row1 >= 0) {
+                    ldh<CT, NCG>(a.v, row1 + e, t);
+#pragma unroll
+                    for (int q = 0; q < NCG; ++q) vi[q] *= t[q];
+                }
+            }
+            if (ok) {
+                sth<CT, NCG>(a.y, row0 + n, vr);
+                if (row1 >= 0) sth<CT, NCG>(a.y, row1 + n, vi);
+            }
+        }
+    });
+}
+
+template <int CT, int P>
+hipError_t launch_r(bool fwd, const ColArgs& a, hipStream_t st) {
+    const dim3 grid((unsigned)(kRow / (4 * Cr<P>::COLS)), (unsigned)a.nseq);
+    if (fwd) hipLaunchKernelGGL((colreg_fwd_kernel<CT, P>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((colreg_inv_kernel<CT, P>), grid, dim3(256), 0, st, a);
+    return hipGetLastError();
 }
 
 template <int CT, int P>
@@ -243,6 +697,10 @@ hipError_t launch_t(bool fwd, const ColArgs& a, hipStream_t st) {
 template <int CT>
 hipError_t launch_ct(bool fwd, const ColArgs& a, hipStream_t st) {
     switch (a.M1) {
+    case 16: return launch_r<CT, 16>(fwd, a, st);
+    case 32: return launch_r<CT, 32>(fwd, a, st);
+    case 64: return launch_r<CT, 64>(fwd, a, st);
+    case 128: return launch_r<CT, 128>(fwd, a, st);
     case 256: return launch_t<CT, 256>(fwd, a, st);
     case 512: return launch_t<CT, 512>(fwd, a, st);
     case 1024: return launch_t<CT, 1024>(fwd, a, st);

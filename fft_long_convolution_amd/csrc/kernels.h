@@ -91,7 +91,7 @@ struct ColArgs {
 hipError_t launch_col_fwd(int dtype, const ColArgs& a, hipStream_t stream);
 // Pass C: inverse twiddle, inverse DFT over k_hi for n_hi < M1/2, gate, store y.
 hipError_t launch_col_inv(int dtype, const ColArgs& a, hipStream_t stream);
-// The same two passes on the matrix cores, for 16-bit types and M1 = 256, 512 or 1024 (a.img set).
+// The same two passes on the matrix cores, for 16-bit types and M1 = 16 .. 1024 (a.img set).
 hipError_t launch_colmx(bool fwd, int dtype, const ColArgs& a, hipStream_t stream);
 
 struct Conv2DArgs {

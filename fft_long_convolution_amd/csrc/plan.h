@@ -58,8 +58,8 @@ struct ColTables {
 };
 bool col_tables(int64_t M, int64_t M1, ColTables* out, hipError_t* err, bool build = true);
 
-// Matrix-core column passes of the multi-pass path, column length P = 16 R (R = 16, 32, 64),
-// 16-bit compute types.  Digits n_hi = 16 n1 + n2, k_hi = k1 + R k2: the first stage is a
+// Matrix-core column passes of the multi-pass path, column length P = 16 R (R = 1 .. 64),
+// 16-bit compute types (for R < 16 only the two 16-point images are used).  Digits n_hi = 16 n1 + n2, k_hi = k1 + R k2: the first stage is a
 // radix-R DFT over n1 (forward: only n1 < H = R/2 is nonzero; inverse: only n1 < H is kept),
 // the second a 16-point DFT over n2.  Image indices in the table: the forward first stage
 // (k1 block rb, n1 block kc) at f1 + rb * hb + kc, the inverse first stage (n1 block rb, k1
@@ -72,7 +72,7 @@ constexpr ColMxGrid colmx_grid(int P) {
     const int R = P / 16, H = R / 2, rbk = R / 16, hb = (H + 15) / 16;
     return ColMxGrid{R, H, rbk, hb, 0, rbk * hb, 2 * rbk * hb, 2 * rbk * hb + 1, 2 * rbk * hb + 2};
 }
-constexpr bool colmx_supported(int64_t P) { return P == 256 || P == 512 || P == 1024; }
+constexpr bool colmx_supported(int64_t P) { return P >= 16 && P <= 1024 && (P & (P - 1)) == 0; }
 // Device pointer to those images for (P, ct) on the current device (ct 16-bit).
 const void* colmx_tables(int64_t P, int ct, hipError_t* err, bool build = true);
 
