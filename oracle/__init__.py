@@ -1,5 +1,5 @@
 """float64 CPU oracle for the causal long convolution (1D: forward, short filters, frequency-sparse
-filters, state-space filters, gradients) and the cropped 2D and 3D linear convolutions.
+filters, state-space filters, gradients, learned Butterfly factors) and the cropped 2D and 3D linear convolutions.
 
 TEST INFRASTRUCTURE ONLY: tests, the smoke check and the bench's CPU-baseline leg may import it;
 the product path (the HIP library and its Python binding) never does, and the two share no code.
@@ -13,3 +13,4 @@ from .oracle import (  # noqa: F401
     transform_length,
     conv1d_toeplitz, conv1d_python_int,
 )
+from . import butterfly  # noqa: F401,E402
