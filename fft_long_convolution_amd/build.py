@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "liblconv.so")
 ARCH = "gfx950"
 HIP_SOURCES = ["fused1d_conv.hip", "fused1d_adj.hip", "fused1d_part.hip", "fused1d_sparse.hip", "fused1d_save.hip",
                "fused1d.hip", "bwd1d.hip", "multipass.hip", "fftconv2d.hip", "fftconv3d.hip",
-               "stage.hip", "ssm.hip", "noalloc.hip", "colmx.hip"]
+               "stage.hip", "ssm.hip", "noalloc.hip", "colmx.hip", "butterfly.hip", "fused1d_lbf.hip"]
 CPP_SOURCES = ["plan.cpp", "lconv_api.cpp"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

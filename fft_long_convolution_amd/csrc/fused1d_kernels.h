@@ -51,7 +51,11 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
     constexpr bool PART = MODE == MODE_PART;
     constexpr bool SPARSE = MODE == MODE_SPARSE;
     constexpr bool SAVE = MODE == MODE_SAVE;
-    constexpr bool CONV = MODE == MODE_CONV || ADJ || SPARSE || SAVE;  // batch-row input and output, half input
+    // learned Butterfly: factor blocks from the caller (a.tables), one real row per transform
+    // (its result is complex: the real part is kept), D x added in the time domain
+    constexpr bool LBF = MODE == MODE_LBF;
+    constexpr bool DTIME = SPARSE || LBF;            // D x added in the time domain
+    constexpr bool CONV = MODE == MODE_CONV || ADJ || SPARSE || SAVE || LBF;  // batch-row input and output, half input
     constexpr bool BATCH = CONV || PART;             // batch rows, gates, filter per channel
     constexpr bool HALF_IN = (CONV || MODE == MODE_FILTER);
     constexpr bool HALF_OUT = BATCH;
@@ -169,7 +173,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
     }
 
     // ---- work decomposition ---------------------------------------------------------------
-    const uint32_t Bp = (uint32_t)((a.B + 1) / 2);  // pairs per channel (CONV)
+    const uint32_t Bp = (uint32_t)(LBF ? a.B : (a.B + 1) / 2);  // pairs (LBF: rows) per channel
     const int64_t first = (int64_t)blockIdx.x * a.per_wg;
     const int64_t last = first + a.per_wg < a.nitems ? first + a.per_wg : a.nitems;
     const int64_t HN = a.H * a.N;
@@ -178,7 +182,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
     auto decode = [&](int64_t item, int64_t& h, int64_t& b) LCV_INLINE {
         const uint32_t it = (uint32_t)item, hh = it / Bp;
         h = hh;
-        b = 2 * (int64_t)(it - hh * Bp);
+        b = (LBF ? 1 : 2) * (int64_t)(it - hh * Bp);
     };
     // PART: the sequences of a channel are its (batch row b, block j) windows, s = b nch + j; an
     // item is a pair of consecutive sequences (s0, s0 + 1) of one channel, so two blocks of one
@@ -246,10 +250,10 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
             int64_t h, b;
             decode(itc, h, b);
             const int64_t row0 = (b * a.H + h) * a.N;
-            const int64_t row1 = b + 1 < a.B ? row0 + HN : row0;
+            const int64_t row1 = !LBF && b + 1 < a.B ? row0 + HN : row0;
             o0 = row0 + n0c;
             o1 = row1 + n0c;
-            ok1 = ok0 && b + 1 < a.B;
+            ok1 = ok0 && !LBF && b + 1 < a.B;
         } else {
             o0 = itc * a.N + n0c;
             o1 = o0;
@@ -304,10 +308,10 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
         io_offsets(it_base + p_io, o0, o1, k0, k1);
         load_raw<IO>(a.u, o0, ru[0]);
         if constexpr (CONV) {
-            load_raw<IO>(a.u, o1, ru[1]);
+            if constexpr (!LBF) load_raw<IO>(a.u, o1, ru[1]);
             if constexpr (GQ) {
                 load_raw<IO>(a.q, o0, rq[0]);
-                load_raw<IO>(a.q, o1, rq[1]);
+                if constexpr (!LBF) load_raw<IO>(a.q, o1, rq[1]);
             }
         }
     };
@@ -326,7 +330,16 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
             io_offsets(it0 + p_io, o0, o1, ok0, ok1);
             float xr[8], xi[8];
             unpack_raw<IO>(ru[0], xr);
-            if constexpr (CONV) {
+            if constexpr (LBF) {
+                if constexpr (GQ) {
+                    float t[8];
+                    unpack_raw<IO>(rq[0], t);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) xr[i] *= t[i];
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) xi[i] = 0.f;
+            } else if constexpr (CONV) {
                 unpack_raw<IO>(ru[1], xi);
                 if constexpr (GQ) {
                     float t[8];
@@ -432,7 +445,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                 const uint4* src = (const uint4*)((const uint32_t*)a.kf + h * M) + wave * 4 * 64 + lane;
                 const uint4 t0 = src[0], t1 = src[64], t2 = src[128], t3 = src[192];
                 // (sparse: no fold, D x is added in the time domain)
-                const float d = SPARSE ? 0.f : raw1_to_f32<IO>(load1_raw<IO>(a.D, h)) * a.inv_m;
+                const float d = DTIME ? 0.f : raw1_to_f32<IO>(load1_raw<IO>(a.D, h)) * a.inv_m;
                 auto fold = [&](uint32_t w) LCV_INLINE { return pack2<IO>(unpack_lo<IO>(w) + d, unpack_hi<IO>(w)); };
                 auto fold4 = [&](uint4 t) LCV_INLINE { return make_uint4(fold(t.x), fold(t.y), fold(t.z), fold(t.w)); };
                 KFL[(wave * 4 + 0) * 64 + lane] = fold4(t0);
@@ -474,7 +487,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
             if constexpr (PART) part_offsets(it0 + p_io, 1, o0, o1, k0, k1);  // the block's outputs
             else io_offsets(it0 + p_io, o0, o1, k0, k1);
             load_raw<IO>(a.v, o0, rv[0]);
-            load_raw<IO>(a.v, o1, rv[1]);
+            if constexpr (!LBF) load_raw<IO>(a.v, o1, rv[1]);
         }
         // P1 reads only the V slots this wave wrote (its own blocks): no barrier.
         __builtin_amdgcn_sched_barrier(0);
@@ -581,7 +594,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                         unpack_raw_c4v<IO>(&kw, kr, ki);
                     } else {
                         unpack_raw_c4v<IO>(rk[i], kr, ki);
-                        if constexpr (!SPARSE) kr += raw1_to_f32<IO>(dk[i]) * a.inv_m;  // (K + D) / M
+                        if constexpr (!DTIME) kr += raw1_to_f32<IO>(dk[i]) * a.inv_m;  // (K + D) / M
                     }
                     if constexpr (SPARSE) {  // a dropped block of a partly kept wave
                         const bool kept = (wave_keep >> i) & 1u;
@@ -768,7 +781,7 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                     float4 w = src[i];
                     yr[2 * i] = w.x; yi[2 * i] = w.y; yr[2 * i + 1] = w.z; yi[2 * i + 1] = w.w;
                 }
-                if constexpr (SPARSE) {
+                if constexpr (DTIME) {
                     // + D x, from the slot's packed pair in V (written by this lane in P0)
                     const int64_t hc = channel_of(it0 + p_io < last ? it0 + p_io : last - 1);
                     const float d = raw1_to_f32<IO>(load1_raw<IO>(a.D, hc));
@@ -821,11 +834,16 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                     unpack_raw<IO>(rv[0], t);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) yr[i] *= t[i];
-                    unpack_raw<IO>(rv[1], t);
+                    if constexpr (!LBF) {
+                        unpack_raw<IO>(rv[1], t);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) yi[i] *= t[i];
+                        for (int i = 0; i < 8; ++i) yi[i] *= t[i];
+                    }
                 }
-                if constexpr (PART) {
+                if constexpr (LBF) {
+                    // one real row: the real part of the result
+                    if (FULL || ok0) store8<IO>(a.y, o0, yr);
+                } else if constexpr (PART) {
                     // the two sequences are stored independently (different rows or blocks)
                     if (ok0) store8<IO>(a.y, o0, yr);
                     if (ok1) store8<IO>(a.y, o1, yi);
@@ -972,7 +990,9 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
         return (int64_t)((uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)item) / Bp);
     };
     // ROW: item -> workspace row (local sequence * M1 + k_hi), item = k_hi * sequences + local
-    // sequence; the row's channel and spectrum row k_hi
+    // sequence: the batch pairs of one channel (consecutive sequences) read the same spectrum
+    // row back to back.  (Visiting rows k_hi and M1 - k_hi together, which read one stored row
+    // through the spectrum's conjugate symmetry, measured slower.)
     const int m1s = ROW && a.M1 > 1 ? __builtin_ctzll((unsigned long long)a.M1) : 0;
     const uint32_t nsq = ROW ? (uint32_t)(a.nitems >> m1s) : 1u;
     auto ws_row = [&](int64_t item) LCV_INLINE -> int64_t {
@@ -1442,6 +1462,14 @@ static hipError_t launch_sparse(bool gq, bool gv, const Fused1DArgs& a, int cus,
     if (gq) return launch_t<R, T, T, MODE_SPARSE, true, false>(a, cus, st);
     if (gv) return launch_t<R, T, T, MODE_SPARSE, false, true>(a, cus, st);
     return launch_t<R, T, T, MODE_SPARSE, false, false>(a, cus, st);
+}
+
+template <int R, int T>
+static hipError_t launch_lbf(bool gq, bool gv, const Fused1DArgs& a, int cus, hipStream_t st) {
+    if (gq && gv) return launch_t<R, T, T, MODE_LBF, true, true>(a, cus, st);
+    if (gq) return launch_t<R, T, T, MODE_LBF, true, false>(a, cus, st);
+    if (gv) return launch_t<R, T, T, MODE_LBF, false, true>(a, cus, st);
+    return launch_t<R, T, T, MODE_LBF, false, false>(a, cus, st);
 }
 
 template <int R, int T>

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "plan.h"
+
 namespace lcv {
 
 // ADJ is the adjoint of CONV: the same chain with the conjugate filter spectrum (a correlation,
@@ -11,7 +13,7 @@ namespace lcv {
 // SPARSE is CONV with the filter spectrum kept only on the frequency blocks set in `keep`.
 // SAVE is CONV that also stores the pre-gate output c (the value v multiplies) to y2.
 enum Mode1D { MODE_CONV = 0, MODE_FILTER = 1, MODE_ROW = 2, MODE_ROWFWD = 3, MODE_ADJ = 4, MODE_PART = 5,
-              MODE_SPARSE = 6, MODE_SAVE = 7 };
+              MODE_SPARSE = 6, MODE_SAVE = 7, MODE_LBF = 8 };
 
 struct Fused1DArgs {
     const void* u;       // CONV: u [B][H][N]; FILTER: k [H][N]; ROW/ROWFWD: workspace rows;
@@ -57,6 +59,12 @@ hipError_t launch_fused1d_part(int R, int dtype, bool gq, bool gv, const Fused1D
                                hipStream_t stream);
 hipError_t launch_fused1d_sparse(int R, int dtype, bool gq, bool gv, const Fused1DArgs& a, int cus,
                                  hipStream_t stream);
+hipError_t launch_fused1d_lbf(int R, int dtype, bool gq, bool gv, const Fused1DArgs& a, int cus,
+                              hipStream_t st);
+// Learned-Butterfly factor blocks (A1, A2, A3, B1, B2, B3; fp32 complex, butterfly.hip) -> matrix
+// images in the fused table layout L for (R, ct); the twiddle section is not touched.
+hipError_t launch_bfly_images(const void* blocks, void* out, int R, int ct, const FusedTableLayout& L,
+                              hipStream_t st);
 hipError_t launch_fused1d_save(int R, int dtype, bool gq, bool gv, const Fused1DArgs& a, int cus,
                                hipStream_t stream);
 // y[i] = dy[i] * c[i] for n elements of type dtype (stage.hip): dv from a saved pre-gate output.

@@ -442,6 +442,123 @@ lconv_status_t lconv_fftconv_sparse_fwd(const void* u, const void* k_f, const vo
     return hip_status(launch_fused1d(p.R, dtype, MODE_SPARSE, q != nullptr, v != nullptr, a, cus, stream));
 }
 
+// ---- learned Butterfly --------------------------------------------------------------------
+
+namespace {
+
+// fused plan for a learned-Butterfly call (R), or 0 when N is not served by one workgroup
+int bfly_radix(int64_t N) {
+    Plan1D p;
+    if (!n_supported(N) || !make_plan_1d(N, &p) || p.multipass) return 0;
+    return p.R;
+}
+
+size_t bfly_conv_offset(int R, lconv_dtype_t dtype) {
+    return dtype == LCONV_F32 ? 0 : fused_table_layout(R, CT_F32).total;
+}
+
+}  // namespace
+
+int64_t lconv_butterfly_blocks_count(int64_t N) {
+    const int R = bfly_radix(N);
+    return R ? 2 * (int64_t)R * R + 4 * 256 * (int64_t)R : 0;
+}
+
+size_t lconv_butterfly_tables_bytes(int64_t N, lconv_dtype_t dtype) {
+    if (!dtype_ok(dtype)) return 0;
+    const int R = bfly_radix(N);
+    if (!R) return 0;
+    return bfly_conv_offset(R, dtype) + fused_table_layout(R, (int)dtype).total;
+}
+
+lconv_status_t lconv_butterfly_tables(const void* blocks, void* tables, int64_t N, lconv_dtype_t dtype,
+                                      hipStream_t stream) {
+    if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
+    if (N < 1) return LCONV_ERR_INVALID_SHAPE;
+    const int R = bfly_radix(N);
+    if (!R) return LCONV_ERR_UNSUPPORTED;
+    if (!blocks || !tables) return LCONV_ERR_NULL_POINTER;
+    if (!aligned16(blocks) || !aligned16(tables)) return LCONV_ERR_MISALIGNED;
+    const size_t nb = (size_t)lconv_butterfly_blocks_count(N) * 8, nt = lconv_butterfly_tables_bytes(N, dtype);
+    if (overlap(blocks, nb, tables, nt)) return LCONV_ERR_ALIASING;
+    hipError_t err = hipSuccess;
+    const void* plan = fused_tables(R, CT_F32, &err);  // for its fixed twiddle section
+    if (!plan) return LCONV_ERR_HIP;
+    const FusedTableLayout L32 = fused_table_layout(R, CT_F32);
+    // fp32 images (the filter transform), then the compute-type images (the convolution)
+    const size_t offs[2] = {0, bfly_conv_offset(R, dtype)};
+    const int cts[2] = {CT_F32, (int)dtype};
+    for (int i = 0; i < (dtype == LCONV_F32 ? 1 : 2); ++i) {
+        const FusedTableLayout L = fused_table_layout(R, cts[i]);
+        char* out = (char*)tables + offs[i];
+        if (launch_bfly_images(blocks, out, R, cts[i], L, stream) != hipSuccess) return LCONV_ERR_HIP;
+        if (hipMemcpyAsync(out + L.tw, (const char*)plan + L32.tw, 64 * 4 * 8, hipMemcpyDeviceToDevice, stream) !=
+            hipSuccess)
+            return LCONV_ERR_HIP;
+    }
+    return LCONV_SUCCESS;
+}
+
+lconv_status_t lconv_butterfly_filter(const void* k, void* k_f, const void* tables, int64_t H, int64_t N,
+                                      lconv_dtype_t dtype, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
+    if (H < 0 || N < 0) return LCONV_ERR_INVALID_SHAPE;
+    if (H == 0 || N == 0) return LCONV_SUCCESS;
+    const int R = bfly_radix(N);
+    if (!R) return LCONV_ERR_UNSUPPORTED;
+    if (!k || !k_f || !tables) return LCONV_ERR_NULL_POINTER;
+    if (!aligned16(k) || !aligned16(k_f) || !aligned16(tables)) return LCONV_ERR_MISALIGNED;
+    int64_t elems;
+    if (!mul_ok(H, N, &elems)) return LCONV_ERR_INVALID_SHAPE;
+    const size_t kf_bytes = lconv_filter_fft_bytes(H, N, dtype);
+    if (kf_bytes == 0) return LCONV_ERR_INVALID_SHAPE;
+    if (overlap(k_f, kf_bytes, k, (size_t)elems * dtype_size(dtype)) ||
+        overlap(k_f, kf_bytes, tables, lconv_butterfly_tables_bytes(N, dtype)))
+        return LCONV_ERR_ALIASING;
+    hipError_t err = hipSuccess;
+    const int cus = device_cu_count(&err);
+    if (!cus) return LCONV_ERR_HIP;
+    const int64_t M = 256 * (int64_t)R;
+    Fused1DArgs a{};
+    a.u = k; a.y = k_f; a.tables = tables;  // the fp32 images come first
+    a.B = 1; a.H = H; a.N = N; a.nitems = H;
+    a.inv_m = 1.0f / (float)M; a.M = M; a.M1 = 1;
+    return hip_status(launch_fused1d(R, dtype, MODE_FILTER, false, false, a, cus, stream));
+}
+
+lconv_status_t lconv_butterfly_fwd(const void* u, const void* k_f, const void* D, void* y, const void* q,
+                                   const void* v, const void* tables, int64_t B, int64_t H, int64_t N,
+                                   lconv_dtype_t dtype, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
+    if (B < 0 || H < 0 || N < 0) return LCONV_ERR_INVALID_SHAPE;
+    int64_t elems, t;
+    if (!mul_ok(B, H, &t) || !mul_ok(t, N, &elems) || !mul_ok(elems, 8, &t)) return LCONV_ERR_INVALID_SHAPE;
+    if (B == 0 || H == 0 || N == 0) return LCONV_SUCCESS;
+    const int R = bfly_radix(N);
+    if (!R) return LCONV_ERR_UNSUPPORTED;
+    if (!u || !k_f || !D || !y || !tables) return LCONV_ERR_NULL_POINTER;
+    if (!aligned16(u) || !aligned16(k_f) || !aligned16(D) || !aligned16(y) || !aligned16(tables) ||
+        (q && !aligned16(q)) || (v && !aligned16(v)))
+        return LCONV_ERR_MISALIGNED;
+    const size_t es = dtype_size(dtype), act = (size_t)elems * es;
+    const size_t kf_bytes = lconv_filter_fft_bytes(H, N, dtype);
+    if (kf_bytes == 0) return LCONV_ERR_INVALID_SHAPE;
+    if (overlap(y, act, u, act) || overlap(y, act, q, act) || overlap(y, act, v, act) ||
+        overlap(y, act, k_f, kf_bytes) || overlap(y, act, D, (size_t)H * es) ||
+        overlap(y, act, tables, lconv_butterfly_tables_bytes(N, dtype)))
+        return LCONV_ERR_ALIASING;
+    hipError_t err = hipSuccess;
+    const int cus = device_cu_count(&err);
+    if (!cus) return LCONV_ERR_HIP;
+    const int64_t M = 256 * (int64_t)R;
+    Fused1DArgs a{};
+    a.u = u; a.q = q; a.v = v; a.y = y; a.kf = k_f; a.D = D;
+    a.tables = (const char*)tables + bfly_conv_offset(R, dtype);
+    a.B = B; a.H = H; a.N = N; a.nitems = B * H;  // one real row per transform
+    a.inv_m = 1.0f / (float)M; a.M = M; a.M1 = 1;
+    return hip_status(launch_fused1d(R, dtype, MODE_LBF, q != nullptr, v != nullptr, a, cus, stream));
+}
+
 }  // extern "C"
 
 namespace {

@@ -61,6 +61,11 @@ def load(path: str = LIB_PATH):
         "lconv_fftconv_partial_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i, vp]),
         "lconv_fftconv_sparse_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_uint32, i, vp]),
         "lconv_freq_blocks": (i, [i64]),
+        "lconv_butterfly_blocks_count": (i64, [i64]),
+        "lconv_butterfly_tables_bytes": (sz, [i64, i]),
+        "lconv_butterfly_tables": (i, [vp, vp, i64, i, vp]),
+        "lconv_butterfly_filter": (i, [vp, vp, vp, i64, i64, i, vp]),
+        "lconv_butterfly_fwd": (i, [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i, vp]),
         "lconv_filter_fft2d": (i, [vp, vp, i64, i64, i64, i, vp]),
         "lconv_ssm_prep_bytes": (sz, [i64, i64, i64, i]),
         "lconv_ssm_prepare": (i, [vp, vp, vp, i64, i64, i64, i, vp]),
@@ -159,6 +164,26 @@ def lconv_fftconv_partial_fwd(u, k_f, D, y, q, v, B, H, N, L, dtype, stream):
 
 def lconv_fftconv_sparse_fwd(u, k_f, D, y, q, v, B, H, N, keep, dtype, stream):
     return load().lconv_fftconv_sparse_fwd(u, k_f, D, y, q, v, B, H, N, keep, dtype, stream)
+
+
+def lconv_butterfly_blocks_count(N):
+    return load().lconv_butterfly_blocks_count(N)
+
+
+def lconv_butterfly_tables_bytes(N, dtype):
+    return load().lconv_butterfly_tables_bytes(N, dtype)
+
+
+def lconv_butterfly_tables(blocks, tables, N, dtype, stream):
+    return load().lconv_butterfly_tables(blocks, tables, N, dtype, stream)
+
+
+def lconv_butterfly_filter(k, k_f, tables, H, N, dtype, stream):
+    return load().lconv_butterfly_filter(k, k_f, tables, H, N, dtype, stream)
+
+
+def lconv_butterfly_fwd(u, k_f, D, y, q, v, tables, B, H, N, dtype, stream):
+    return load().lconv_butterfly_fwd(u, k_f, D, y, q, v, tables, B, H, N, dtype, stream)
 
 
 def lconv_freq_blocks(N):
@@ -424,6 +449,56 @@ def fftconv_sparse(u, k_f, D, keep, q=None, v=None, out=None, stream=None):
     _check(lconv_fftconv_sparse_fwd(_ptr(u), _ptr(k_f), _ptr(D), _ptr(y), _ptr(q), _ptr(v), B, H, N,
                                     mask, dtype_code(u.dtype), _stream(stream)),
            "lconv_fftconv_sparse_fwd")
+    return y
+
+
+def butterfly_tables(blocks, N, dtype, stream=None):
+    """Matrix-core images (uint8 device tensor) of learned-Butterfly factor blocks for length N:
+    `blocks` a complex64 device tensor of lconv_butterfly_blocks_count(N) values (A1, A2, A3,
+    B1, B2, B3 back to back, as include/lconv.h lays them out); dtype a torch dtype."""
+    torch = _torch()
+    dt = dtype_code(dtype)
+    count = lconv_butterfly_blocks_count(N)
+    if count == 0:
+        raise LconvError(4, "lconv_butterfly_blocks_count")
+    _need("blocks", blocks, (count,), torch.complex64)
+    _on_gpu(blocks=blocks)
+    nbytes = lconv_butterfly_tables_bytes(N, dt)
+    tables = torch.empty(nbytes, dtype=torch.uint8, device=blocks.device)
+    _check(lconv_butterfly_tables(blocks.data_ptr(), tables.data_ptr(), N, dt, _stream(stream)),
+           "lconv_butterfly_tables")
+    return tables
+
+
+def butterfly_filter(k, tables, stream=None):
+    """Filter spectrum of k [H, N] through the learned forward factors (same opaque layout as
+    filter_fft)."""
+    torch = _torch()
+    _act(k, "k", dims=2)
+    H, N = k.shape
+    dt = dtype_code(k.dtype)
+    _need_buf("tables", tables, lconv_butterfly_tables_bytes(N, dt))
+    _on_gpu(k=k, tables=tables)
+    nbytes = lconv_filter_fft_bytes(H, N, dt)
+    if nbytes == 0 and H * N > 0:
+        raise LconvError(3, "lconv_filter_fft_bytes")
+    k_f = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k.device)
+    _check(lconv_butterfly_filter(_ptr(k), k_f.data_ptr(), tables.data_ptr(), H, N, dt, _stream(stream)),
+           "lconv_butterfly_filter")
+    return k_f
+
+
+def butterfly(u, k_f, D, tables, q=None, v=None, out=None, stream=None):
+    """Learned-Butterfly convolution y = v * (Re(S (K . T (q*u)))[:N] + D (q*u)) for u [B, H, N],
+    k_f from butterfly_filter, tables from butterfly_tables."""
+    torch = _torch()
+    B, H, N = _gated_inputs(u, k_f, D, q, v, out)
+    dt = dtype_code(u.dtype)
+    _need_buf("tables", tables, lconv_butterfly_tables_bytes(N, dt))
+    _on_gpu(tables=tables)
+    y = torch.empty_like(u) if out is None else out
+    _check(lconv_butterfly_fwd(_ptr(u), _ptr(k_f), _ptr(D), _ptr(y), _ptr(q), _ptr(v), tables.data_ptr(),
+                               B, H, N, dt, _stream(stream)), "lconv_butterfly_fwd")
     return y
 
 

@@ -253,6 +253,20 @@ def ssm_modes(H, NS, seed=0, decay=(1e-4, 1e-1)):
     return lam, W
 
 
+def butterfly_blocks(N, seed=0):
+    """Learned-Butterfly factor blocks for length N (transform M = max(512, next power of two
+    >= 2N) = 256 R): complex Gaussian entries of unit variance, so each factor has about the gain
+    of its DFT counterpart.  Flat complex64, A1 [R][R], A2, A3, B1, B2 [R][16][16], B3 [R][R]."""
+    M = 512
+    while M < 2 * N:
+        M *= 2
+    R = M // 256
+    n = 2 * R * R + 4 * 256 * R
+    rng = np.random.default_rng(seed)
+    z = (rng.standard_normal(n) + 1j * rng.standard_normal(n)) / math.sqrt(2.0)
+    return z.astype(np.complex64)
+
+
 def spec_3d(B, C, S, dtype, seed=7, decay=0.1) -> Conv3DSpec:
     return Conv3DSpec(f"custom3d_{dtype}_b{B}_c{C}_s{S}", B, C, S, dtype, decay=decay, seed=seed)
 

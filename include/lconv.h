@@ -52,7 +52,7 @@ extern "C" {
  * part states.  4: lconv_prepare and lconv_fftconv_fwd_noalloc, two status codes.  5: 2D calls
  * take Hs x Ws images and a workspace; lconv_fftconv2d_workspace_bytes.  6: gradients and the
  * training pair for every supported N, with workspace arguments). */
-#define LCONV_ABI_VERSION 6
+#define LCONV_ABI_VERSION 7
 
 /* The last enumerator only widens the type's range to every int, so that any value a C caller
  * passes is a valid value of the type (unknown ones are rejected with LCONV_ERR_UNSUPPORTED). */
@@ -152,6 +152,43 @@ lconv_status_t lconv_fftconv_sparse_fwd(const void* u, const void* k_f, const vo
 /* Number of frequency blocks R = M / 256 of the transform for N (0 if N is unsupported by
  * lconv_fftconv_sparse_fwd). */
 int lconv_freq_blocks(int64_t N);
+
+/*
+ * Learned Butterfly: the convolution above with its transforms replaced by factored matrices
+ * whose dense blocks are free (learned) parameters ("Simple Hardware-Efficient Long Convolutions
+ * for Sequence Modeling", abstract: the coefficients of the Butterfly decomposition are learned,
+ * at the runtime of the fixed decomposition).  The factorization is the one the fused kernels
+ * run for M = 256 R (N <= 4096): n = 256 n1 + 16 n2 + n3, f = k1 + R k2 + 16 R k3, and
+ *   T[f, n]  = A3[k1][k3][n3] w256^{n3 k2} A2[k1][k2][n2] A1[k1][n1]          (forward)
+ *   S[n, f]  = B3[n1][k1] B2[k1][n2][k2] conj(w256^{n3 k2}) B1[k1][n3][k3]     (inverse)
+ * with w256 = exp(-2 pi i / 256) fixed.  With x = q u zero-padded to M, K = T k / M (k zero-padded):
+ *   y[b,h,t] = v * ( Re( S (K[h] (.) T x[b,h]) )[t] + D[h] x[b,h,t] ),  t < N
+ * For the DFT's blocks (A1 = w_R^{n1 k1}, A2[k1] = w_{16R}^{n2 (k1 + R k2)},
+ * A3[k1] = w_M^{n3 (k1 + 16 R k3)}, B = their conjugate transposes) this is lconv_fftconv_fwd.
+ * Each transform carries one real row (the pair packing of lconv_fftconv_fwd needs the
+ * conjugate symmetry of the DFT), and D x is added in the time domain.
+ *   blocks   fp32 complex (re, im), device: A1 [R][R] (k1, n1), A2 [R][16][16] (k1, k2, n2),
+ *            A3 [R][16][16] (k1, k3, n3), B1 [R][16][16] (k1, n3, k3), B2 [R][16][16]
+ *            (k1, n2, k2), B3 [R][R] (n1, k1), back to back: lconv_butterfly_blocks_count(N)
+ *            complex values.  Only the columns n1 < R/2 of A1 and the rows n1 < R/2 of B3 are
+ *            used (zero padding, causal truncation).
+ *   tables   lconv_butterfly_tables_bytes(N, dtype) bytes, device, written by
+ *            lconv_butterfly_tables (the blocks as matrix-core images, fp32 and dtype)
+ *   k_f      lconv_filter_fft_bytes(H, N, dtype) bytes, written by lconv_butterfly_filter(k [H][N])
+ *   u, y, q, v, D as for lconv_fftconv_fwd.
+ * Supported: 8 <= N <= 4096, N a multiple of 8 (R = lconv_freq_blocks(N)); 0 from the size
+ * queries and LCONV_ERR_UNSUPPORTED otherwise.  No workspace.  Errors as for lconv_fftconv_fwd;
+ * tables overlapping an output give LCONV_ERR_ALIASING.
+ */
+int64_t lconv_butterfly_blocks_count(int64_t N);
+size_t lconv_butterfly_tables_bytes(int64_t N, lconv_dtype_t dtype);
+lconv_status_t lconv_butterfly_tables(const void* blocks, void* tables, int64_t N, lconv_dtype_t dtype,
+                                      hipStream_t stream);
+lconv_status_t lconv_butterfly_filter(const void* k, void* k_f, const void* tables, int64_t H, int64_t N,
+                                      lconv_dtype_t dtype, hipStream_t stream);
+lconv_status_t lconv_butterfly_fwd(const void* u, const void* k_f, const void* D, void* y, const void* q,
+                                   const void* v, const void* tables, int64_t B, int64_t H, int64_t N,
+                                   lconv_dtype_t dtype, hipStream_t stream);
 
 /*
  * Partial convolution: the same gated causal convolution with a filter of L taps (zero beyond

@@ -78,6 +78,14 @@ int main() {
     EXPECT(lconv_fftconv_partial_fwd(A, Bq, C, Y, nullptr, nullptr, 2, 3, 64, 8192, BF, nullptr), LCONV_ERR_UNSUPPORTED);
     EXPECT(lconv_fftconv_sparse_fwd(A, Bq, C, Y, nullptr, nullptr, 2, 3, 4096, 0x3u, BF, nullptr), LCONV_ERR_UNSUPPORTED);
     EXPECT(lconv_fftconv_sparse_fwd(A, Bq, C, Y, nullptr, nullptr, 2, 3, 4096, 0x1u, BF, nullptr), LCONV_ERR_HIP);
+    // learned Butterfly
+    EXPECT(lconv_butterfly_blocks_count(4096) == 2 * 32 * 32 + 1024 * 32 ? LCONV_SUCCESS : LCONV_ERR_INVALID_SHAPE,
+           LCONV_SUCCESS);
+    EXPECT(lconv_butterfly_tables(A, Y, 8192, BF, nullptr), LCONV_ERR_UNSUPPORTED);
+    EXPECT(lconv_butterfly_tables(A, Y, 4096, BF, nullptr), LCONV_ERR_HIP);
+    EXPECT(lconv_butterfly_filter(A, Y, W, 3, 4096, BF, nullptr), LCONV_ERR_HIP);
+    EXPECT(lconv_butterfly_fwd(A, Bq, C, Y, nullptr, nullptr, W, 2, 3, 4096, BF, nullptr), LCONV_ERR_HIP);
+    EXPECT(lconv_butterfly_fwd(A, Bq, C, Y, nullptr, nullptr, Y, 2, 3, 4096, BF, nullptr), LCONV_ERR_ALIASING);
     // 2D, 3D, state-space
     EXPECT(lconv_fftconv2d_fwd(A, Bq, C, Y, 2, 3, 100, 64, BF, nullptr, 0, nullptr), LCONV_ERR_HIP);
     EXPECT(lconv_fftconv2d_fwd(A, Bq, C, Y, 2, 3, 128, 12, BF, nullptr, 0, nullptr), LCONV_ERR_UNSUPPORTED);

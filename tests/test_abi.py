@@ -27,7 +27,7 @@ def test_exports_every_header_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lconv.lconv_abi_version() == 6
+    assert lconv.lconv_abi_version() == 7
     for s in range(10):
         assert lconv.status_string(s)
     assert "unknown" in lconv.status_string(99)
@@ -286,6 +286,36 @@ def test_sparse_blocks_and_validation():
         assert sparse(N=4096, keep=0xffffffff) == HIPERR
 
 
+def bfly(u=G[0], kf=G[1], D=G[2], y=G[3], q=None, v=None, tab=G[4], B=2, H=3, N=1000, dt=BF16):
+    return lconv.lconv_butterfly_fwd(u, kf, D, y, q, v, tab, B, H, N, dt, None)
+
+
+def test_butterfly_sizes_and_validation():
+    # R = M / 256: 2 R^2 + 4 * 256 R complex block values
+    assert lconv.lconv_butterfly_blocks_count(64) == 2 * 4 + 1024 * 2
+    assert lconv.lconv_butterfly_blocks_count(4096) == 2 * 32 * 32 + 1024 * 32
+    assert lconv.lconv_butterfly_blocks_count(8192) == 0          # beyond one transform
+    assert lconv.lconv_butterfly_blocks_count(12) == 0            # not a multiple of 8
+    # fp32 images (filter) + compute-type images (convolution); fp32: one set
+    b32, b16 = lconv.lconv_butterfly_tables_bytes(4096, F32), lconv.lconv_butterfly_tables_bytes(4096, BF16)
+    assert b32 > 0 and b16 > b32
+    assert lconv.lconv_butterfly_tables_bytes(4096, 7) == 0
+    assert lconv.lconv_butterfly_tables(G[0], G[1], 8192, BF16, None) == UNSUP
+    assert lconv.lconv_butterfly_tables(None, G[1], 64, BF16, None) == NULLP
+    assert lconv.lconv_butterfly_tables(G[0], G[0], 64, BF16, None) == ALIAS
+    assert lconv.lconv_butterfly_filter(G[0], G[1], G[2], 3, 4104, BF16, None) == UNSUP
+    assert lconv.lconv_butterfly_filter(G[0], G[1], None, 3, 64, BF16, None) == NULLP
+    assert lconv.lconv_butterfly_filter(G[0], G[1], G[2], 0, 64, BF16, None) == OK
+    assert bfly(dt=5) == UNSUP
+    assert bfly(B=-1) == SHAPE
+    assert bfly(N=8192) == UNSUP
+    assert bfly(tab=None) == NULLP
+    assert bfly(D=G[2] + 2) == MISAL
+    assert bfly(y=G[0]) == ALIAS
+    assert bfly(y=G[4]) == ALIAS                                   # output over the tables
+    assert bfly(B=0) == OK
+
+
 def test_3d_sizes_and_validation():
     assert lconv.lconv_filter_fft3d_bytes(4, 32, BF16) == 4 * 64 ** 3 * 4
     assert lconv.lconv_filter_fft3d_bytes(4, 16, F32) == 4 * 32 ** 3 * 8
@@ -364,6 +394,13 @@ BOUNDARY = {
                                                "int64_t", "int64_t", "int64_t", "int64_t", "lconv_dtype_t",
                                                "void*", "size_t", "hipStream_t"]),
     "lconv_status_string": ("const char*", ["lconv_status_t"]),
+    "lconv_butterfly_tables": ("lconv_status_t", ["const void*", "void*", "int64_t", "lconv_dtype_t",
+                                                  "hipStream_t"]),
+    "lconv_butterfly_filter": ("lconv_status_t", ["const void*", "void*", "const void*", "int64_t", "int64_t",
+                                                  "lconv_dtype_t", "hipStream_t"]),
+    "lconv_butterfly_fwd": ("lconv_status_t", ["const void*", "const void*", "const void*", "void*",
+                                               "const void*", "const void*", "const void*", "int64_t",
+                                               "int64_t", "int64_t", "lconv_dtype_t", "hipStream_t"]),
 }
 
 
