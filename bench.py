@@ -316,6 +316,9 @@ def main():
     ap.add_argument("--keep", default=None,
                     help="frequency-sparse call: bit mask (e.g. 0xe000000f) of the frequency "
                          "blocks kept (f mod R); the step is lconv_fftconv_sparse_fwd")
+    ap.add_argument("--butterfly", action="store_true",
+                    help="learned-Butterfly call (lconv_butterfly_fwd, seeded factor blocks; "
+                         "N <= 4096) instead of the FFT convolution")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--dist", type=int, default=20,
                     help="launches for the per-launch median / min / p90, hot and after a cache "
@@ -392,6 +395,22 @@ def main():
                                              stream.cuda_stream)
             if st != 0:
                 raise lconv.LconvError(st, "lconv_fftconv_ssm_fwd")
+    elif args.butterfly:  # learned Butterfly: caller factor blocks, one real row per transform
+        u, q, v, k, D = (to_dev(d[x], dt) for x in ("u", "q", "v", "k", "D"))
+        blocks = torch.from_numpy(wl.butterfly_blocks(spec.N, seed=spec.seed + 3)).cuda()
+        tables = lconv.butterfly_tables(blocks, spec.N, u.dtype)
+        run_filter = lambda: lconv.butterfly_filter(k, tables)
+        kf = run_filter()
+        y = torch.empty_like(u)
+        dtc = lconv.dtype_code(u.dtype)
+        stream = torch.cuda.current_stream()
+        p = lambda t: None if t is None else t.data_ptr()
+
+        def step():
+            st = lconv.lconv_butterfly_fwd(u.data_ptr(), kf.data_ptr(), D.data_ptr(), y.data_ptr(), p(q), p(v),
+                                           tables.data_ptr(), spec.B, spec.H, spec.N, dtc, stream.cuda_stream)
+            if st != 0:
+                raise lconv.LconvError(st, "lconv_butterfly_fwd")
     elif args.keep is not None:  # frequency-sparse convolution
         keep = int(args.keep, 0)
         u, q, v, k, D = (to_dev(d[x], dt) for x in ("u", "q", "v", "k", "D"))
@@ -503,6 +522,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": spec.name, "B": spec.B, **({"L": spec.L} if getattr(spec, "L", 0) else {}),
                    **({"keep": args.keep} if args.keep is not None else {}),
+                   **({"learned_butterfly": True} if args.butterfly else {}),
                    ("H" if spec.kind == "1d" else "C"): (spec.H if spec.kind == "1d" else spec.C),
                    ("N" if spec.kind == "1d" else "S"): (spec.N if spec.kind == "1d" else spec.S),
                    "gated": bool(getattr(spec, "gated", False)), "parallelism": "none"},
@@ -519,7 +539,7 @@ def main():
     if timing:
         out["timing"] = timing
         out["timing"]["region_avg_us"] = round(avg_ms * 1e3, 3)
-    cs = counter_summary(spec.name) if args.keep is None else {}  # counters are of the dense call
+    cs = counter_summary(spec.name) if args.keep is None and not args.butterfly else {}  # of the FFT call
     if cs:
         out["roofline"]["traffic"] = int(float(cs["traffic_bytes_per_launch"]))
         # matrix-core GFLOP executed per launch (op counter x 512), over this run's kernel time
@@ -527,9 +547,9 @@ def main():
         out["mfma"] = {"executed_tflops": round(mf, 1), "peak": MFMA_PEAK[dt],
                        "util": round(mf / MFMA_PEAK[dt], 4), "counters": cs["path"]}
     if not args.no_bwd and spec.kind == "1d" and spec.N % 8 == 0 and not spec.L and args.keep is None \
-            and not spec.name.startswith("ssm_"):
+            and not args.butterfly and not spec.name.startswith("ssm_"):
         out["backward"] = time_backward(lconv, wl, spec, u, kf, D, q, v, args)
-    if not args.no_cpu and spec.kind == "1d" and not spec.name.startswith("ssm_"):
+    if not args.no_cpu and spec.kind == "1d" and not spec.name.startswith("ssm_") and not args.butterfly:
         out["cpu_baseline"] = cpu_baseline(d, args.cpu_budget)
     print(json.dumps(out), flush=True)
 
