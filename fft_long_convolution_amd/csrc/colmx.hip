@@ -275,7 +275,10 @@ __global__ void __launch_bounds__(512, 4) colmx_fwd_kernel(const ColArgs a) {
             wb[q] = cmulf(wb[q], wi[q]);
         });
 #pragma unroll
-        for (int j = 0; j < 4; ++j) stw<NCG>(ws, (s * P + k1 + R * (4 * g + j)) * kRow + col0, out[j]);
+        for (int j = 0; j < 4; ++j) {
+            const int kh = k1 + R * (4 * g + j);
+            if (kh < a.rows) stw<NCG>(ws, (s * a.rows + kh) * kRow + col0, out[j]);
+        }
     });
 }
 
@@ -306,12 +309,24 @@ __global__ void __launch_bounds__(512, 4) colmx_inv_kernel(const ColArgs a) {
         wi[q] = tw_m(a.tw_lo, a.tw_hi, (n_lo * 8) & mask);
         wj[q] = tw_m(a.tw_lo, a.tw_hi, (n_lo * R) & mask);
     });
+    // Rows k_hi >= a.rows are not stored (one real row per sequence): the column spectrum V of a
+    // real column is conjugate-symmetric, V[P - k] = conj V[k], and with V = conj(w_M^{n_lo k})
+    // times the stored value, row k reads as w_8192^{n_lo} conj(stored row P - k).
     uint32_t in[R / 8][4][NCG];
     static_for<0, R / 8>([&](auto ii) LCV_INLINE {
         constexpr int i = decltype(ii)::value;
         const int k1 = wave + 8 * i;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ldw<NCG>(ws, (s * P + k1 + R * (4 * g + j)) * kRow + col0, in[i][j]);
+        for (int j = 0; j < 4; ++j) {
+            const int kh = k1 + R * (4 * g + j), kr = kh < a.rows ? kh : P - kh;
+            ldw<NCG>(ws, (s * a.rows + kr) * kRow + col0, in[i][j]);
+        }
+    });
+    const bool half = a.rows < P;
+    float2 wrow[NCG];  // w_8192^{n_lo}
+    static_for<0, NCG>([&](auto qq) LCV_INLINE {
+        constexpr int q = decltype(qq)::value;
+        wrow[q] = half ? tw_m(a.tw_lo, a.tw_hi, ((col0 + q) * P) & mask) : make_float2(1.f, 0.f);
     });
     static_for<0, R / 8>([&](auto ii) LCV_INLINE {
         constexpr int i = decltype(ii)::value;
@@ -330,6 +345,11 @@ __global__ void __launch_bounds__(512, 4) colmx_inv_kernel(const ColArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 float zr = unpack_lo<CT>(in[i][j][q]), zi = unpack_hi<CT>(in[i][j][q]);
+                if (k1 + R * (4 * g + j) >= a.rows) {  // mirrored row: w_8192^{n_lo} conj(z)
+                    const float mr = zr, mi = -zi;
+                    zr = mr * wrow[q].x - mi * wrow[q].y;
+                    zi = mr * wrow[q].y + mi * wrow[q].x;
+                }
                 cmulc(zr, zi, w.x, w.y);
                 w = cmulf(w, wj[q]);
                 op.w[j] = pack2<CT>(zr, zi);
@@ -556,7 +576,7 @@ __global__ void __launch_bounds__(256, 4) colreg_fwd_kernel(const ColArgs a) {
             }
         });
 #pragma unroll
-        for (int j = 0; j < 4; ++j) stw<NCG>(ws, (s * P + k1 + R * (4 * g + j)) * kRow + col0, out[j]);
+        for (int j = 0; j < 4; ++j) stw<NCG>(ws, (s * a.rows + k1 + R * (4 * g + j)) * kRow + col0, out[j]);
     });
 }
 
@@ -587,12 +607,12 @@ __global__ void __launch_bounds__(256, 4) colreg_inv_kernel(const ColArgs a) {
     float2 sbk = ((const float2*)a.tw_lo)[4 * g * R];
     uint32_t in[2][4][NCG];  // workspace rows of k1 and k1 + 1
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ldw<NCG>(ws, (s * P + R * (4 * g + j)) * kRow + col0, in[0][j]);
+    for (int j = 0; j < 4; ++j) ldw<NCG>(ws, (s * a.rows + R * (4 * g + j)) * kRow + col0, in[0][j]);
     static_for<0, R>([&](auto kk) LCV_INLINE {
         constexpr int k1 = decltype(kk)::value, b = k1 & 1;
         if constexpr (k1 + 1 < R) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ldw<NCG>(ws, (s * P + k1 + 1 + R * (4 * g + j)) * kRow + col0, in[1 - b][j]);
+            for (int j = 0; j < 4; ++j) ldw<NCG>(ws, (s * a.rows + k1 + 1 + R * (4 * g + j)) * kRow + col0, in[1 - b][j]);
         }
         // conj(w_M^{n_lo k_hi}), stepped as in the forward pass
         const float2 wb = wbk, sb = sbk, tb = tbk, ts = tsk;
@@ -713,6 +733,8 @@ hipError_t launch_ct(bool fwd, const ColArgs& a, hipStream_t st) {
 hipError_t launch_colmx(bool fwd, int dtype, const ColArgs& a, hipStream_t st) {
     if (a.nseq <= 0) return hipSuccess;
     if (!a.img || a.filter || a.nseq > 65535 || a.M != a.M1 * kRow) return hipErrorInvalidValue;
+    // half rows: single real rows only (no second row in any sequence), matrix-core lengths only
+    if (a.rows != a.M1 && (a.rows != a.M1 / 2 + 1 || a.M1 < 256 || a.B != 1)) return hipErrorInvalidValue;
     if (dtype == CT_F16) return launch_ct<CT_F16>(fwd, a, st);
     if (dtype == CT_BF16) return launch_ct<CT_BF16>(fwd, a, st);
     return hipErrorInvalidValue;

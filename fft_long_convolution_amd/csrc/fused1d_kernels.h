@@ -989,16 +989,24 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
     auto channel = [&](int64_t item) LCV_INLINE {
         return (int64_t)((uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)item) / Bp);
     };
-    // ROW: item -> workspace row (local sequence * M1 + k_hi), item = k_hi * sequences + local
+    // ROW: item -> workspace row (local sequence * wr + k_hi), item = k_hi * sequences + local
     // sequence: the batch pairs of one channel (consecutive sequences) read the same spectrum
     // row back to back.  (Visiting rows k_hi and M1 - k_hi together, which read one stored row
     // through the spectrum's conjugate symmetry, measured slower.)
-    const int m1s = ROW && a.M1 > 1 ? __builtin_ctzll((unsigned long long)a.M1) : 0;
-    const uint32_t nsq = ROW ? (uint32_t)(a.nitems >> m1s) : 1u;
-    auto ws_row = [&](int64_t item) LCV_INLINE -> int64_t {
+    // The workspace holds wr rows per sequence: M1, or M1/2 + 1 when each sequence is one real row
+    // (the rest follow by conjugate symmetry and are never formed).
+    const uint32_t wr = ROW ? (uint32_t)(a.wrows ? a.wrows : a.M1) : 1u;
+    const uint32_t nsq = ROW ? (uint32_t)(a.nitems / wr) : 1u;
+    auto row_of = [&](int64_t item, uint32_t& sl, uint32_t& kh) LCV_INLINE {
         item = item < last ? item : last - 1;
-        const uint32_t it = __builtin_amdgcn_readfirstlane((uint32_t)item), kh = it / nsq, sl = it - kh * nsq;
-        return ((int64_t)sl << m1s) + kh;
+        const uint32_t it = __builtin_amdgcn_readfirstlane((uint32_t)item);
+        kh = it / nsq;
+        sl = it - kh * nsq;
+    };
+    auto ws_row = [&](int64_t item) LCV_INLINE -> int64_t {
+        uint32_t sl, kh;
+        row_of(item, sl, kh);
+        return (int64_t)sl * wr + kh;
     };
     // this lane's slot: row n1 = lane / 4, columns 32 wave + 8 (lane % 4) .. +8 (the wave's blocks)
     const int s_n1 = lane >> 2, s_col = 32 * wave + 8 * (lane & 3);
@@ -1025,9 +1033,10 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
         rw3 = src[16 * 256 / 4 + 1];
     };
     auto issue_kf_row = [&](int64_t item) LCV_INLINE {
-        const int64_t r = ws_row(item);
-        const int64_t h = (int64_t)((uint32_t)(a.seq0 + (r >> m1s)) / (uint32_t)a.seq_per_h);
-        const uint4* src = (const uint4*)((const uint32_t*)a.kf + h * a.M + (r & (a.M1 - 1)) * M);
+        uint32_t sl, kh;
+        row_of(item, sl, kh);
+        const int64_t h = (int64_t)((uint32_t)(a.seq0 + sl) / (uint32_t)a.seq_per_h);
+        const uint4* src = (const uint4*)((const uint32_t*)a.kf + h * a.M + (int64_t)kh * M);
         static_for<0, 4>([&](auto ii) LCV_INLINE {
             constexpr int i = decltype(ii)::value;
             rk[i] = src[(wave * 4 + i) * 64 + lane];

@@ -39,6 +39,7 @@ struct Fused1DArgs {
     float inv_m;         // 1 / M
     int64_t M;           // full transform length (ROW/ROWFWD: M1 * 8192)
     int64_t M1;          // ROW/ROWFWD: rows per sequence
+    int64_t wrows;       // ROW (16-bit): workspace rows stored per sequence (0: M1), rows 0 .. wrows-1
     int64_t seq0;        // ROW/ROWFWD: global index of the chunk's first sequence
     int64_t seq_per_h;   // ROW: sequences per channel (h = seq / seq_per_h); ROWFWD: 1
 };
@@ -92,6 +93,9 @@ struct ColArgs {
     int64_t seq_per_h;   // pairs per channel (CONV) or 1 (FILTER)
     int filter;          // 1: input is k (one real channel per sequence)
     const void* img;     // matrix-core column images (16-bit, column lengths 256..1024), or null
+    int64_t rows;        // workspace rows stored per sequence: M1, or M1/2 + 1 when every sequence
+                         // is one real row (its column spectra are conjugate-symmetric in k_hi, so
+                         // rows k_hi > M1/2 are not stored; matrix-core passes with M1 >= 256 only)
 };
 
 // Pass A: per sequence and column n_lo, DFT over n_hi < M1/2 (zero above), twiddle

@@ -374,18 +374,26 @@ lconv_status_t fftconv_fwd_aligned(const void* u, const void* k_f, const void* D
         cimg = colmx_tables(p.M1, ct, &err, may_build);
         if (!cimg) return LCONV_ERR_HIP;
     }
-    const int64_t per = chunk_seqs(seqs, p.M, work_complex_size(dtype, false), chunk_target);
+    const size_t csz = work_complex_size(dtype, false);
+    // One real row per sequence (B = 1) on the matrix-core passes: a real column's spectrum is
+    // conjugate-symmetric in k_hi, so only rows 0 .. M1/2 are stored and row-transformed (the
+    // filter and the output are real as well); the inverse column pass rebuilds the rest.
+    const bool half = B == 1 && cimg && p.M1 >= 256;
+    const int64_t rows = half ? p.M1 / 2 + 1 : p.M1;
+    const int64_t full_per = chunk_seqs(seqs, p.M, csz, chunk_target);
+    // as many sequences as the workspace sized for full rows holds
+    const int64_t per = half ? chunk_seqs(seqs, rows * kRowLen, csz, (size_t)full_per * p.M * csz) : full_per;
     for (int64_t s0 = 0; s0 < seqs; s0 += per) {
         const int64_t ns = per < seqs - s0 ? per : seqs - s0;
         ColArgs c{};
         c.u = u; c.q = q; c.v = v; c.y = y; c.ws = workspace;
         c.tw_lo = ctab.lo; c.tw_hi = ctab.hi; c.tw_col = ctab.col;
         c.B = B; c.H = H; c.N = N; c.M = p.M; c.M1 = p.M1; c.seq0 = s0; c.nseq = ns;
-        c.seq_per_h = Bp; c.filter = 0; c.img = cimg;
+        c.seq_per_h = Bp; c.filter = 0; c.img = cimg; c.rows = rows;
         if (launch_col_fwd(dtype, c, stream) != hipSuccess) return LCONV_ERR_HIP;
         Fused1DArgs a{};
         a.u = workspace; a.y = workspace; a.kf = k_f; a.D = D; a.tables = tabs;
-        a.nitems = ns * p.M1; a.inv_m = 1.0f / (float)p.M; a.M = p.M; a.M1 = p.M1;
+        a.nitems = ns * rows; a.inv_m = 1.0f / (float)p.M; a.M = p.M; a.M1 = p.M1; a.wrows = rows;
         a.seq0 = s0; a.seq_per_h = Bp;
         if (launch_fused1d(32, dtype, MODE_ROW, false, false, a, cus, stream) != hipSuccess) return LCONV_ERR_HIP;
         if (launch_col_inv(dtype, c, stream) != hipSuccess) return LCONV_ERR_HIP;

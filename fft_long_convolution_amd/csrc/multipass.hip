@@ -363,7 +363,16 @@ static hipError_t launch_cols(bool fwd, const ColArgs& a, hipStream_t st) {
 
 // dtype: io type.  The workspace holds the compute type: fp32 for fp32 io and for filters,
 // else the io type.
-hipError_t launch_col_fwd(int dtype, const ColArgs& a, hipStream_t st) {
+// rows = 0 stands for M1 (every row stored); fewer rows only on the matrix-core passes
+static bool rows_ok(ColArgs& a, bool mx) {
+    if (a.rows == 0) a.rows = a.M1;
+    return a.rows == a.M1 || mx;
+}
+
+hipError_t launch_col_fwd(int dtype, const ColArgs& a0, hipStream_t st) {
+    ColArgs a = a0;
+    const bool mx = dtype != CT_F32 && !a.filter && a.img && colmx_supported(a.M1);
+    if (!rows_ok(a, mx)) return hipErrorInvalidValue;
     if (a.filter) {
         if (dtype == CT_F32) return launch_cols<CT_F32, CT_F32>(true, a, st);
         if (dtype == CT_F16) return launch_cols<CT_F32, CT_F16>(true, a, st);
@@ -374,7 +383,10 @@ hipError_t launch_col_fwd(int dtype, const ColArgs& a, hipStream_t st) {
     return launch_cols<CT_BF16, CT_BF16>(true, a, st);
 }
 
-hipError_t launch_col_inv(int dtype, const ColArgs& a, hipStream_t st) {
+hipError_t launch_col_inv(int dtype, const ColArgs& a0, hipStream_t st) {
+    ColArgs a = a0;
+    const bool mx = dtype != CT_F32 && !a.filter && a.img && colmx_supported(a.M1);
+    if (!rows_ok(a, mx)) return hipErrorInvalidValue;
     if (dtype == CT_F32) return launch_cols<CT_F32, CT_F32>(false, a, st);
     if (dtype == CT_F16) return launch_cols<CT_F16, CT_F16>(false, a, st);
     return launch_cols<CT_BF16, CT_BF16>(false, a, st);
