@@ -38,6 +38,10 @@ constexpr int RS = 257;    // LDS row stride (words): odd, so row index enters t
 // Column index swizzle: flips bits 4-5 of v by the 64-blocks of row and column, which makes
 // both the row-tile pattern (fixed r) and the column-tile pattern (fixed v) bank-conflict free.
 __device__ __forceinline__ int swz(int r, int v) { return v ^ ((((r >> 6) ^ (v >> 6)) & 3) << 4); }
+// The same with the 64-blocks given: row block rb = r >> 6, column block vb = v >> 6.  A lane's
+// tile accesses keep rb (rows 16 (4 g + jj) + c lie in block g) or vb (columns c + 16 (4 g + jj)
+// lie in block g) fixed over jj, so the XOR term is computed once per tile, not per element.
+__device__ __forceinline__ int swz_b(int rb, int v) { return v ^ (((rb ^ (v >> 6)) & 3) << 4); }
 
 template <int IO>
 __device__ __forceinline__ uint32_t ld_raw2(const void* p, int64_t i) {
@@ -160,11 +164,11 @@ __global__ void __launch_bounds__(512) conv2d_kernel(const Conv2DArgs a) {
             static_for<0, 4>([&](auto ii) LCV_INLINE {
                 constexpr int i = decltype(ii)::value;
                 const int r = 32 * q + 4 * wave + i;
+                // v = c + 16 (4 g + jj) has v >> 6 = g: swz flips jj by t
+                const int t = ((r >> 6) ^ g) & 3;
+                uint32_t* row = BUF + r * RS + c + 64 * g;
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int v = c + 16 * (4 * g + jj);
-                    BUF[r * RS + swz(r, v)] = pack2<CT>(xs[i].re[jj], xs[i].im[jj]);
-                }
+                for (int jj = 0; jj < 4; ++jj) row[16 * (jj ^ t)] = pack2<CT>(xs[i].re[jj], xs[i].im[jj]);
             });
             __syncthreads();
         }
@@ -183,11 +187,10 @@ __global__ void __launch_bounds__(512) conv2d_kernel(const Conv2DArgs a) {
                 constexpr int i = decltype(ii)::value;
                 const int v = v0 + i;
                 Operand<CT> o;
+                // rows r = 16 (4 g + jj) + c lie in 64-block g
+                const uint32_t* col = BUF + (64 * g + c) * RS + swz_b(g, v);
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int r = 16 * (4 * g + jj) + c;
-                    o.w[jj] = g < 2 ? BUF[r * RS + swz(r, v)] : 0u;
-                }
+                for (int jj = 0; jj < 4; ++jj) o.w[jj] = g < 2 ? col[16 * jj * RS] : 0u;
                 opd[i] = o;
             });
             static_for<0, 4>([&](auto ii) LCV_INLINE {
@@ -238,11 +241,10 @@ __global__ void __launch_bounds__(512) conv2d_kernel(const Conv2DArgs a) {
                 constexpr int i = decltype(ii)::value;
                 const int v = v0 + i;
                 if (g == 1 || g == 2) {  // rows 64 .. 191 of the full convolution
+                    // window rows r = 16 (4 g + jj) + c - 64 lie in 64-block g - 1
+                    uint32_t* col = BUF + (64 * (g - 1) + c) * RS + swz_b(g - 1, v);
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const int r = 16 * (4 * g + jj) + c - 64;
-                        BUF[r * RS + swz(r, v)] = pack2<CT>(xs[i].re[jj], xs[i].im[jj]);
-                    }
+                    for (int jj = 0; jj < 4; ++jj) col[16 * jj * RS] = pack2<CT>(xs[i].re[jj], xs[i].im[jj]);
                 }
             });
         }
@@ -256,8 +258,11 @@ __global__ void __launch_bounds__(512) conv2d_kernel(const Conv2DArgs a) {
                 constexpr int i = decltype(ii)::value;
                 const int r = r0 + i;
                 Operand<CT> o;
+                // columns v = c + 16 (4 g + jj) have v >> 6 = g: swz flips jj by t
+                const int t = ((r >> 6) ^ g) & 3;
+                const uint32_t* row = BUF + r * RS + c + 64 * g;
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) o.w[jj] = BUF[r * RS + swz(r, c + 16 * (4 * g + jj))];
+                for (int jj = 0; jj < 4; ++jj) o.w[jj] = row[16 * (jj ^ t)];
                 opd[i] = o;
             });
             static_for<0, 4>([&](auto ii) LCV_INLINE {

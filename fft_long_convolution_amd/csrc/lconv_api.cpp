@@ -383,8 +383,11 @@ lconv_status_t fftconv_fwd_aligned(const void* u, const void* k_f, const void* D
     const int64_t full_per = chunk_seqs(seqs, p.M, csz, chunk_target);
     // as many sequences as the workspace sized for full rows holds
     const int64_t per = half ? chunk_seqs(seqs, rows * kRowLen, csz, (size_t)full_per * p.M * csz) : full_per;
-    for (int64_t s0 = 0; s0 < seqs; s0 += per) {
-        const int64_t ns = per < seqs - s0 ? per : seqs - s0;
+    // equal chunks (sizes differ by at most one sequence), not full chunks and a short last one
+    const int64_t nch = (seqs + per - 1) / per;
+    for (int64_t ci = 0; ci < nch; ++ci) {
+        const int64_t s0 = seqs / nch * ci + (ci < seqs % nch ? ci : seqs % nch);
+        const int64_t ns = seqs / nch + (ci < seqs % nch ? 1 : 0);
         ColArgs c{};
         c.u = u; c.q = q; c.v = v; c.y = y; c.ws = workspace;
         c.tw_lo = ctab.lo; c.tw_hi = ctab.hi; c.tw_col = ctab.col;
