@@ -1344,12 +1344,12 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
             unpack_raw<CT>(&re2[1], t);
 #pragma unroll
             for (int i = 0; i < 8; ++i) zi[i] = yi[i] * t[i];
-            store8<CT>(a.y2, o0, zr);
-            store8<CT>(a.y2, o1, zi);
+            store8_nt<CT>(a.y2, o0, zr);
+            store8_nt<CT>(a.y2, o1, zi);
         }
         if constexpr (SAVE) {   // the pre-gate output c
-            store8<CT>(a.y2, o0, yr);
-            store8<CT>(a.y2, o1, yi);
+            store8_nt<CT>(a.y2, o0, yr);
+            store8_nt<CT>(a.y2, o1, yi);
         }
         if constexpr (GV) {
             float t[8];
@@ -1360,11 +1360,15 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) yi[i] *= t[i];
         }
-        store8<CT>(a.y, o0, yr);
-        store8<CT>(a.y, o1, yi);
+        store8_nt<CT>(a.y, o0, yr);  // streamed past the caches: nothing here reads y again
+        store8_nt<CT>(a.y, o1, yi);
     };
 
     // ---- pipeline ------------------------------------------------------------------------------
+    // Each wave group runs its own copy of the item loop (P2 first for waves 0-3, W first for
+    // waves 4-7), with the first and last items peeled off: the steady loop has no branch around
+    // a memory instruction but the rare spectrum reload, so the compiler's vmcnt waits count the
+    // loads issued one item ahead instead of draining them.
     int64_t kf_h = ROW ? 0 : channel(first);  // (ROW items carry no batch count)
     int kb = 0;
     if constexpr (ROW) issue_kf_row(first);
@@ -1375,43 +1379,61 @@ __global__ void __launch_bounds__(512) conv8k_kernel(const Fused1DArgs a) {
     P1(XYb);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    for (int64_t k = first; k < last; ++k) {
+    using Yes = std::integral_constant<bool, true>;
+    using No = std::integral_constant<bool, false>;
+    // W(k): P3, P4 of k - 1; the next channel's spectrum; P0, P1 of k + 1 (guarded: the first
+    // and last items; unguarded: first < k < last - 1)
+    auto W = [&](int64_t k, uint32_t* XYo, int& kb_next, auto guarded) LCV_INLINE {
+        constexpr bool GU = decltype(guarded)::value;
+        if (!GU || k > first) {
+            issue_e2(k - 1);
+            P3(XYo);
+            P4(k - 1);
+        }
+        if (!ROW && (!GU || k + 1 < last)) {
+            const int64_t hn = channel(k + 1);
+            if (hn != kf_h) {
+                kb_next = 1 - kb;
+                load_kf(hn, kb_next);
+                kf_h = hn;
+            }
+        }
+        issue_v(k);
+        if (!GU || k + 1 < last) {
+            P0();
+            issue_uq(k + 2);
+            P1(XYo);
+        }
+    };
+    auto iteration = [&](int64_t k, auto p2_first, auto guarded) LCV_INLINE {
         const int xb = (int)((k - first) & 1);
         uint32_t* const XYk = XYb + xb * XY_W;
         uint32_t* const XYo = XYb + (1 - xb) * XY_W;
         int kb_next = kb;
-#pragma unroll 1
-        for (int s = 0; s < 2; ++s) {
-            if ((s == 0) == (wave < 4)) {
-                P2(XYk, KFL + kb * (KF_W / 4));
-                if constexpr (ROW) issue_kf_row(k + 1);  // clamped past the end
-            } else {
-                if (k > first) {
-                    issue_e2(k - 1);
-                    P3(XYo);
-                    P4(k - 1);
-                }
-                if (!ROW && k + 1 < last) {
-                    const int64_t hn = channel(k + 1);
-                    if (hn != kf_h) {
-                        kb_next = 1 - kb;
-                        load_kf(hn, kb_next);
-                        kf_h = hn;
-                    }
-                }
-                issue_v(k);
-                if (k + 1 < last) {
-                    P0();
-                    issue_uq(k + 2);
-                    P1(XYo);
-                }
-            }
+        if constexpr (decltype(p2_first)::value) {
+            P2(XYk, KFL + kb * (KF_W / 4));
+            if constexpr (ROW) issue_kf_row(k + 1);  // clamped past the end
             __builtin_amdgcn_sched_barrier(0);
+            W(k, XYo, kb_next, guarded);
+        } else {
+            W(k, XYo, kb_next, guarded);
+            __builtin_amdgcn_sched_barrier(0);
+            P2(XYk, KFL + kb * (KF_W / 4));
+            if constexpr (ROW) issue_kf_row(k + 1);
         }
+        __builtin_amdgcn_sched_barrier(0);
         kb = kb_next;
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    auto run = [&](auto p2_first) LCV_INLINE {
+        iteration(first, p2_first, Yes{});
+        int64_t k = first + 1;
+        for (; k < last - 1; ++k) iteration(k, p2_first, No{});
+        if (k < last) iteration(k, p2_first, Yes{});
+    };
+    if (wave < 4) run(Yes{});
+    else run(No{});
     issue_e2(last - 1);
     P3(XYb + ((last - 1 - first) & 1) * XY_W);
     P4(last - 1);
