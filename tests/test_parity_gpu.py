@@ -93,6 +93,29 @@ def test_workload_hyena_gated_bf16(lc, nthreads):
     assert per_row.max() <= 2e-2 and err_pts <= 2e-2
 
 
+# The M = 8192 pipelined kernel (N = 4096, 16-bit) gives each workgroup a run of items (batch
+# pairs); its first two and last two items take guarded copies of the loop body.  On 256 compute
+# units these shapes give 2, 3, 4, 5 and 9 items per workgroup, a last workgroup with fewer
+# items, odd batches (a pair repeating its row) and channel changes inside a workgroup's run.
+PIPELINE_SHAPES = [(2, 300), (2, 301), (3, 300), (2, 1000), (5, 400), (6, 700)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("B,H", PIPELINE_SHAPES)
+def test_pipelined_items_per_workgroup(lc, nthreads, dtype, B, H):
+    spec = wl.spec_1d(B, H, 4096, dtype, gated=True, seed=3000 + 7 * B + H)
+    say(f"[pipeline] dtype={dtype} B={B} H={H} N=4096 gated seed={spec.seed}")
+    d = wl.make(spec)
+    y, _ = run_1d(lc, d)
+    assert np.all(np.isfinite(y))
+    rows = [(b, h) for b in range(B) for h in range(H)]
+    ref = oracle_rows(d, rows, nthreads).reshape(B, H, 4096)
+    per_row = rel_l2_rows(y, ref)
+    worst = np.unravel_index(int(np.argmax(per_row)), per_row.shape)
+    say(f"   all {B * H} rows: max rel L2 = {per_row.max():.3e} at (b,h)={tuple(int(i) for i in worst)}")
+    assert per_row.max() <= TOL[dtype]
+
+
 def _sampled_long(lc, name, nthreads, n_rows_full=0):
     d = wl.make(name)
     spec = d["spec"]
