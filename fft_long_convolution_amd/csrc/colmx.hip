@@ -94,6 +94,17 @@ __device__ __forceinline__ void sth(void* p, int64_t i, const float* x) {
         *(uint4*)q = make_uint4(pack2<CT>(x[0], x[1]), pack2<CT>(x[2], x[3]), pack2<CT>(x[4], x[5]), pack2<CT>(x[6], x[7]));
     }
 }
+// sth with the non-temporal hint, for the final output
+template <int CT, int K>
+__device__ __forceinline__ void sth_nt(void* p, int64_t i, const float* x) {
+    if constexpr (K == 1) {
+        sth<CT, 1>(p, i, x);
+    } else {
+        uint32_t* q = (uint32_t*)((uint16_t*)p + i);
+#pragma unroll
+        for (int j = 0; j < K / 2; ++j) __builtin_nontemporal_store(pack2<CT>(x[2 * j], x[2 * j + 1]), q + j);
+    }
+}
 template <int K>
 __device__ __forceinline__ void ldw(const uint32_t* p, int64_t i, uint32_t* w) {
     if constexpr (K == 1) {
@@ -416,8 +427,8 @@ __global__ void __launch_bounds__(512, 4) colmx_inv_kernel(const ColArgs a) {
                     }
                 }
                 if (ok) {
-                    sth<CT, NCG>(a.y, row0 + n, yr);
-                    if (row1 >= 0) sth<CT, NCG>(a.y, row1 + n, yi);
+                    sth_nt<CT, NCG>(a.y, row0 + n, yr);
+                    if (row1 >= 0) sth_nt<CT, NCG>(a.y, row1 + n, yi);
                 }
             }
         });
@@ -690,8 +701,8 @@ __global__ void __launch_bounds__(256, 4) colreg_inv_kernel(const ColArgs a) {
                 }
             }
             if (ok) {
-                sth<CT, NCG>(a.y, row0 + n, vr);
-                if (row1 >= 0) sth<CT, NCG>(a.y, row1 + n, vi);
+                sth_nt<CT, NCG>(a.y, row0 + n, vr);
+                if (row1 >= 0) sth_nt<CT, NCG>(a.y, row1 + n, vi);
             }
         }
     });

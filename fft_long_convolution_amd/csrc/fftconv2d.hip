@@ -304,8 +304,9 @@ __global__ void __launch_bounds__(512) conv2d_kernel(const Conv2DArgs a) {
                 y0.z = __byte_perm(w[4], w[5], 0x5410); y0.w = __byte_perm(w[6], w[7], 0x5410);
                 y1.x = __byte_perm(w[0], w[1], 0x7632); y1.y = __byte_perm(w[2], w[3], 0x7632);
                 y1.z = __byte_perm(w[4], w[5], 0x7632); y1.w = __byte_perm(w[6], w[7], 0x7632);
-                *(uint4*)((uint16_t*)a.y + o0) = y0;
-                if (has1) *(uint4*)((uint16_t*)a.y + o0 + a.C * IMGSZ) = y1;
+                // streamed with the non-temporal hint: nothing here reads y again
+                st4_nt((uint32_t*)((uint16_t*)a.y + o0), y0);
+                if (has1) st4_nt((uint32_t*)((uint16_t*)a.y + o0 + a.C * IMGSZ), y1);
             }
         }
         // the next item's S0 writes STG first and BUF only after a barrier

@@ -815,8 +815,8 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                         for (int i = 0; i < 8; ++i) zi[i] = o1 != o0 ? zi[i] : zr[i];
                     }
                     if (FULL || ok0) {
-                        store8<IO>(a.y2, o0, zr);
-                        store8<IO>(a.y2, o1, zi);
+                        store8_nt<IO>(a.y2, o0, zr);
+                        store8_nt<IO>(a.y2, o1, zi);
                     }
                 }
                 if constexpr (SAVE) {
@@ -825,8 +825,8 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
 #pragma unroll
                     for (int i = 0; i < 8; ++i) ci[i] = FULL || o1 != o0 ? yi[i] : yr[i];
                     if (FULL || ok0) {
-                        store8<IO>(a.y2, o0, yr);
-                        store8<IO>(a.y2, o1, ci);
+                        store8_nt<IO>(a.y2, o0, yr);
+                        store8_nt<IO>(a.y2, o1, ci);
                     }
                 }
                 if constexpr (GV) {
@@ -842,11 +842,11 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                 }
                 if constexpr (LBF) {
                     // one real row: the real part of the result
-                    if (FULL || ok0) store8<IO>(a.y, o0, yr);
+                    if (FULL || ok0) store8_nt<IO>(a.y, o0, yr);
                 } else if constexpr (PART) {
                     // the two sequences are stored independently (different rows or blocks)
-                    if (ok0) store8<IO>(a.y, o0, yr);
-                    if (ok1) store8<IO>(a.y, o1, yi);
+                    if (ok0) store8_nt<IO>(a.y, o0, yr);
+                    if (ok1) store8_nt<IO>(a.y, o1, yi);
                 } else {
                     // odd B, partial iteration: the masked second row must not overwrite the first
                     if constexpr (!FULL) {
@@ -854,8 +854,8 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                         for (int i = 0; i < 8; ++i) yi[i] = o1 != o0 ? yi[i] : yr[i];
                     }
                     if (FULL || ok0) {
-                        store8<IO>(a.y, o0, yr);
-                        store8<IO>(a.y, o1, yi);
+                        store8_nt<IO>(a.y, o0, yr);
+                        store8_nt<IO>(a.y, o1, yi);
                     }
                 }
             } else {  // ROW: complex row back to the workspace, in compute type

@@ -50,15 +50,20 @@ __device__ __forceinline__ void store8(void* base, int64_t off, const float* x) 
 }
 
 // 8 consecutive elements as raw bits (1 uint4 for 16-bit types, 2 for fp32) and their unpacking.
-// store8 with the non-temporal hint (16-bit io): a streamed output
+// store8 with the non-temporal hint: a streamed output that nothing in the call reads again
 template <int IO>
 __device__ __forceinline__ void store8_nt(void* base, int64_t off, const float* x) {
-    static_assert(IO != CT_F32, "16-bit io only");
-    uint32_t* p = (uint32_t*)((uint16_t*)base + off);
-    __builtin_nontemporal_store(pack2<IO>(x[0], x[1]), p);
-    __builtin_nontemporal_store(pack2<IO>(x[2], x[3]), p + 1);
-    __builtin_nontemporal_store(pack2<IO>(x[4], x[5]), p + 2);
-    __builtin_nontemporal_store(pack2<IO>(x[6], x[7]), p + 3);
+    if constexpr (IO == CT_F32) {
+        uint32_t* p = (uint32_t*)((float*)base + off);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) __builtin_nontemporal_store(__float_as_uint(x[i]), p + i);
+    } else {
+        uint32_t* p = (uint32_t*)((uint16_t*)base + off);
+        __builtin_nontemporal_store(pack2<IO>(x[0], x[1]), p);
+        __builtin_nontemporal_store(pack2<IO>(x[2], x[3]), p + 1);
+        __builtin_nontemporal_store(pack2<IO>(x[4], x[5]), p + 2);
+        __builtin_nontemporal_store(pack2<IO>(x[6], x[7]), p + 3);
+    }
 }
 
 template <int IO>

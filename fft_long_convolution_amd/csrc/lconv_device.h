@@ -83,6 +83,14 @@ template <int CT> __device__ __forceinline__ float unpack_hi(uint32_t w) {
     return CT == CT_BF16 ? bf16hi_to_f32(w) : f16hi_to_f32(w);
 }
 
+// 16 bytes stored with the non-temporal hint (one streamed vector store)
+__device__ __forceinline__ void st4_nt(uint32_t* p, uint4 v) {
+    __builtin_nontemporal_store(v.x, p);
+    __builtin_nontemporal_store(v.y, p + 1);
+    __builtin_nontemporal_store(v.z, p + 2);
+    __builtin_nontemporal_store(v.w, p + 3);
+}
+
 // ---- tiles and operands ------------------------------------------------------------------
 
 // fp32 tile: 4 complex values per lane (the MFMA accumulators of the re and im products).
