@@ -148,6 +148,15 @@ __global__ void __launch_bounds__(512, 4) colmx_fwd_kernel(const ColArgs a) {
     int64_t row0, row1;
     seq_rows(a, a.seq0 + s, row0, row1);
     const float2* twc = (const float2*)a.tw_col;
+    // Scalar bases (this block's first column of each input row) and 32-bit lane offsets: the
+    // loads take the scalar-base address form, with no 64-bit arithmetic per element.
+    const uint16_t* const ub0 = (const uint16_t*)a.u + row0 + n_lo0;
+    const uint16_t* const ub1 = (const uint16_t*)a.u + (row1 >= 0 ? row1 : row0) + n_lo0;
+    const uint16_t* const qb0 = (const uint16_t*)a.q + row0 + n_lo0;
+    const uint16_t* const qb1 = (const uint16_t*)a.q + (row1 >= 0 ? row1 : row0) + n_lo0;
+    const uint32_t lane_off = NCG * x;
+    // columns of this block below N, as a 32-bit bound on the lane offsets
+    const uint32_t nlim = (uint32_t)(a.N - n_lo0 < 0 ? 0 : (a.N - n_lo0 > 0xffffffffLL ? 0xffffffffLL : a.N - n_lo0));
 
     // Stage 1, per n2 (two per wave), NCG tiles: radix R over n1 < H (gated pairs packed as
     // complex x_b + i x_{b+1}), times w_P^{n2 k1}, into the exchange.
@@ -189,15 +198,16 @@ __global__ void __launch_bounds__(512, 4) colmx_fwd_kernel(const ColArgs a) {
                 static_for<0, 4>([&](auto jj) LCV_INLINE {
                     constexpr int j = decltype(jj)::value;
                     const int n1 = 16 * kc + 4 * g + j;
-                    const int64_t n = kRow * (16 * n1 + n2) + col0;
-                    const bool ok = n1 < H && n < a.N;  // N is a multiple of 8: all NCG columns alike
-                    const int64_t e = ok ? n : col0;    // a valid element of the same rows
+                    const uint32_t off = (uint32_t)kRow * (16 * n1 + n2) + lane_off;
+                    // N is a multiple of 8: all NCG columns alike
+                    const bool ok = n1 < H && off < nlim;
+                    const int64_t e = ok ? off : lane_off;  // a valid element of the same rows
                     okv[i][kc][j] = ok;
-                    ldraw(a.u, row0 + e, ru[i][kc][j]);
-                    if (a.q) ldraw(a.q, row0 + e, rq[i][kc][j]);
+                    ldraw(ub0, e, ru[i][kc][j]);
+                    if (a.q) ldraw(qb0, e, rq[i][kc][j]);
                     if (row1 >= 0) {
-                        ldraw(a.u, row1 + e, ru1[i][kc][j]);
-                        if (a.q) ldraw(a.q, row1 + e, rq1[i][kc][j]);
+                        ldraw(ub1, e, ru1[i][kc][j]);
+                        if (a.q) ldraw(qb1, e, rq1[i][kc][j]);
                     }
                 });
             });
@@ -256,7 +266,7 @@ __global__ void __launch_bounds__(512, 4) colmx_fwd_kernel(const ColArgs a) {
     // w_M^{n_lo k_hi}, store rows k_hi = k1 + R k2 of the workspace.
     const MatImg<CT> f16 = load_img<CT>(a.img, C::G.f16, lane);
     const int64_t mask = a.M - 1;
-    uint32_t* ws = (uint32_t*)a.ws;
+    uint32_t* const wsb = (uint32_t*)a.ws + s * a.rows * kRow + n_lo0;  // this block's row 0
     // w_M^{n_lo k_hi} for k_hi = k1 + R (4 g + j), k1 = wave + 8 i: per column, a base for
     // i = 0, a step for i, and a step for j (products of fp32 table values; at most 11 steps)
     float2 wb[NCG], wi[NCG], wj[NCG];
@@ -290,7 +300,7 @@ __global__ void __launch_bounds__(512, 4) colmx_fwd_kernel(const ColArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int kh = k1 + R * (4 * g + j);
-            if (kh < a.rows) stw<NCG>(ws, (s * a.rows + kh) * kRow + col0, out[j]);
+            if (kh < a.rows) stw<NCG>(wsb, (int64_t)((uint32_t)kh * (uint32_t)kRow + lane_off), out[j]);
         }
     });
 }
@@ -307,7 +317,15 @@ __global__ void __launch_bounds__(512, 4) colmx_inv_kernel(const ColArgs a) {
     seq_rows(a, a.seq0 + s, row0, row1);
     const float2* twc = (const float2*)a.tw_col;
     const int64_t mask = a.M - 1;
-    const uint32_t* ws = (const uint32_t*)a.ws;
+    // scalar bases and 32-bit lane offsets (as in the forward pass)
+    const uint32_t* const wsb = (const uint32_t*)a.ws + s * a.rows * kRow + n_lo0;
+    const int64_t r1 = row1 >= 0 ? row1 : row0;
+    uint16_t* const yb0 = (uint16_t*)a.y + row0 + n_lo0;
+    uint16_t* const yb1 = (uint16_t*)a.y + r1 + n_lo0;
+    const uint16_t* const vb0 = (const uint16_t*)a.v + row0 + n_lo0;
+    const uint16_t* const vb1 = (const uint16_t*)a.v + r1 + n_lo0;
+    const uint32_t lane_off = NCG * x;
+    const uint32_t nlim = (uint32_t)(a.N - n_lo0 < 0 ? 0 : (a.N - n_lo0 > 0xffffffffLL ? 0xffffffffLL : a.N - n_lo0));
 
     // Stage 1, per k1 (R/8 per wave), NCG tiles: rows k_hi = k1 + R k2 of the workspace, times
     // conj(w_M^{n_lo k_hi}), 16-point inverse DFT over k2, times conj(w_P^{n2 k1}), into the
@@ -332,7 +350,7 @@ __global__ void __launch_bounds__(512, 4) colmx_inv_kernel(const ColArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int kh = k1 + R * (4 * g + j), kr = kh < a.rows ? kh : P - kh;
-            ldw<NCG>(ws, (s * a.rows + kr) * kRow + col0, in[i][j]);
+            ldw<NCG>(wsb, (int64_t)((uint32_t)kr * (uint32_t)kRow + lane_off), in[i][j]);
         }
     });
     const bool half = a.rows < P;
@@ -409,9 +427,9 @@ __global__ void __launch_bounds__(512, 4) colmx_inv_kernel(const ColArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int n1 = 16 * rb + 4 * g + j;
-                const int64_t n = kRow * (16 * n1 + n2) + col0;
-                const bool ok = n1 < H && n < a.N;
-                const int64_t e = ok ? n : col0;
+                const uint32_t off = (uint32_t)kRow * (16 * n1 + n2) + lane_off;
+                const bool ok = n1 < H && off < nlim;
+                const int64_t e = ok ? off : lane_off;
                 float yr[NCG], yi[NCG], t[NCG];
                 static_for<0, NCG>([&](auto qq) LCV_INLINE {
                     constexpr int q = decltype(qq)::value;
@@ -419,18 +437,18 @@ __global__ void __launch_bounds__(512, 4) colmx_inv_kernel(const ColArgs a) {
                     yi[q] = acc[q].im[j];
                 });
                 if (a.v) {
-                    ldh<CT, NCG>(a.v, row0 + e, t);
+                    ldh<CT, NCG>(vb0, e, t);
 #pragma unroll
                     for (int q = 0; q < NCG; ++q) yr[q] *= t[q];
                     if (row1 >= 0) {
-                        ldh<CT, NCG>(a.v, row1 + e, t);
+                        ldh<CT, NCG>(vb1, e, t);
 #pragma unroll
                         for (int q = 0; q < NCG; ++q) yi[q] *= t[q];
                     }
                 }
                 if (ok) {
-                    sth_nt<CT, NCG>(a.y, row0 + n, yr);
-                    if (row1 >= 0) sth_nt<CT, NCG>(a.y, row1 + n, yi);
+                    sth_nt<CT, NCG>(yb0, e, yr);
+                    if (row1 >= 0) sth_nt<CT, NCG>(yb1, e, yi);
                 }
             }
         });
@@ -466,13 +484,22 @@ __global__ void __launch_bounds__(256, 4) colreg_fwd_kernel(const ColArgs a) {
     using C = Cr<P>;
     constexpr int R = C::R, H = C::H, NCG = C::NCG, RW = (NCG + 1) / 2;
     const int lane = threadIdx.x & 63, g = lane >> 4, x = lane & 15;
-    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // wave of the sequence
+    // wave of the sequence (readfirstlane: the compiler keeps what depends on it in scalars)
+    const int64_t wid = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t s = blockIdx.y;
-    const int64_t col0 = wid * C::COLS + NCG * x;
+    const int64_t cw0 = wid * C::COLS;          // the wave's first column
+    const int64_t col0 = cw0 + NCG * x;
     int64_t row0, row1;
     seq_rows(a, a.seq0 + s, row0, row1);
     const float2* twc = (const float2*)a.tw_col;
     const int64_t mask = a.M - 1;
+    // scalar bases and 32-bit lane offsets: no 64-bit arithmetic per element
+    const uint16_t* const ub0 = (const uint16_t*)a.u + row0 + cw0;
+    const uint16_t* const ub1 = (const uint16_t*)a.u + (row1 >= 0 ? row1 : row0) + cw0;
+    const uint16_t* const qb0 = (const uint16_t*)a.q + row0 + cw0;
+    const uint16_t* const qb1 = (const uint16_t*)a.q + (row1 >= 0 ? row1 : row0) + cw0;
+    const uint32_t lane_off = NCG * x;
+    const uint32_t nlim = (uint32_t)(a.N - cw0 < 0 ? 0 : (a.N - cw0 > 0xffffffffLL ? 0xffffffffLL : a.N - cw0));
 
     // gated input pairs x[16 n1 + 4 g + j] of this lane's columns, packed in the compute type
     // (R = 1: only rows 4 g + j < 8 are nonzero)
@@ -491,15 +518,15 @@ __global__ void __launch_bounds__(256, 4) colreg_fwd_kernel(const ColArgs a) {
             static_for<0, 4>([&](auto jj) LCV_INLINE {
                 constexpr int j = decltype(jj)::value;
                 const int nh = 16 * n1 + 4 * g + j;
-                const int64_t n = kRow * nh + col0;
-                const bool ok = (R > 1 || nh < 8) && n < a.N;
-                const int64_t e = ok ? n : col0;
+                const uint32_t off = (uint32_t)kRow * nh + lane_off;
+                const bool ok = (R > 1 || nh < 8) && off < nlim;
+                const int64_t e = ok ? off : lane_off;
                 okv[n1][j] = ok;
-                ldraw(a.u, row0 + e, ru[n1][j]);
-                if (a.q) ldraw(a.q, row0 + e, rq[n1][j]);
+                ldraw(ub0, e, ru[n1][j]);
+                if (a.q) ldraw(qb0, e, rq[n1][j]);
                 if (row1 >= 0) {
-                    ldraw(a.u, row1 + e, ru1[n1][j]);
-                    if (a.q) ldraw(a.q, row1 + e, rq1[n1][j]);
+                    ldraw(ub1, e, ru1[n1][j]);
+                    if (a.q) ldraw(qb1, e, rq1[n1][j]);
                 }
             });
         });
@@ -525,7 +552,7 @@ __global__ void __launch_bounds__(256, 4) colreg_fwd_kernel(const ColArgs a) {
     }
 
     const MatImg<CT> f16 = load_img<CT>(a.img, C::G.f16, lane);
-    uint32_t* ws = (uint32_t*)a.ws;
+    uint32_t* const wsb = (uint32_t*)a.ws + s * a.rows * kRow + cw0;  // the wave's columns, row 0
     // four-step twiddle w_M^{n_lo k_hi}, n_lo = col0 + q, k_hi = k1 + R (4 g + j):
     // w_M^{col0 k_hi} w_M^{q k_hi}, stepped along j by w_M^{col0 R} and w_M^{R}
     // Per-k1 factors advance from k1 to k1 + 1 by one product each (at most 7 steps), so the
@@ -589,7 +616,8 @@ __global__ void __launch_bounds__(256, 4) colreg_fwd_kernel(const ColArgs a) {
             }
         });
 #pragma unroll
-        for (int j = 0; j < 4; ++j) stw<NCG>(ws, (s * a.rows + k1 + R * (4 * g + j)) * kRow + col0, out[j]);
+        for (int j = 0; j < 4; ++j)
+            stw<NCG>(wsb, (int64_t)((uint32_t)(k1 + R * (4 * g + j)) * (uint32_t)kRow + lane_off), out[j]);
     });
 }
 
@@ -598,14 +626,23 @@ __global__ void __launch_bounds__(256, 4) colreg_inv_kernel(const ColArgs a) {
     using C = Cr<P>;
     constexpr int R = C::R, H = C::H, NCG = C::NCG;
     const int lane = threadIdx.x & 63, g = lane >> 4, x = lane & 15;
-    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t wid = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t s = blockIdx.y;
-    const int64_t col0 = wid * C::COLS + NCG * x;
+    const int64_t cw0 = wid * C::COLS;          // the wave's first column
+    const int64_t col0 = cw0 + NCG * x;
     int64_t row0, row1;
     seq_rows(a, a.seq0 + s, row0, row1);
     const float2* twc = (const float2*)a.tw_col;
     const int64_t mask = a.M - 1;
-    const uint32_t* ws = (const uint32_t*)a.ws;
+    // scalar bases and 32-bit lane offsets (as in the forward pass)
+    const uint32_t* const wsb = (const uint32_t*)a.ws + s * a.rows * kRow + cw0;
+    const int64_t r1 = row1 >= 0 ? row1 : row0;
+    uint16_t* const yb0 = (uint16_t*)a.y + row0 + cw0;
+    uint16_t* const yb1 = (uint16_t*)a.y + r1 + cw0;
+    const uint16_t* const vb0 = (const uint16_t*)a.v + row0 + cw0;
+    const uint16_t* const vb1 = (const uint16_t*)a.v + r1 + cw0;
+    const uint32_t lane_off = NCG * x;
+    const uint32_t nlim = (uint32_t)(a.N - cw0 < 0 ? 0 : (a.N - cw0 > 0xffffffffLL ? 0xffffffffLL : a.N - cw0));
     const MatImg<CT> i16 = load_img<CT>(a.img, C::G.i16, lane);
 
     // y[n1][j][q] for rows n_hi = 16 n1 + 4 g + j < P / 2
@@ -620,12 +657,13 @@ __global__ void __launch_bounds__(256, 4) colreg_inv_kernel(const ColArgs a) {
     float2 sbk = ((const float2*)a.tw_lo)[4 * g * R];
     uint32_t in[2][4][NCG];  // workspace rows of k1 and k1 + 1
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ldw<NCG>(ws, (s * a.rows + R * (4 * g + j)) * kRow + col0, in[0][j]);
+    for (int j = 0; j < 4; ++j) ldw<NCG>(wsb, (int64_t)((uint32_t)(R * (4 * g + j)) * (uint32_t)kRow + lane_off), in[0][j]);
     static_for<0, R>([&](auto kk) LCV_INLINE {
         constexpr int k1 = decltype(kk)::value, b = k1 & 1;
         if constexpr (k1 + 1 < R) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ldw<NCG>(ws, (s * a.rows + k1 + 1 + R * (4 * g + j)) * kRow + col0, in[1 - b][j]);
+            for (int j = 0; j < 4; ++j)
+                ldw<NCG>(wsb, (int64_t)((uint32_t)(k1 + 1 + R * (4 * g + j)) * (uint32_t)kRow + lane_off), in[1 - b][j]);
         }
         // conj(w_M^{n_lo k_hi}), stepped as in the forward pass
         const float2 wb = wbk, sb = sbk, tb = tbk, ts = tsk;
@@ -686,25 +724,25 @@ __global__ void __launch_bounds__(256, 4) colreg_inv_kernel(const ColArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int nh = 16 * n1 + 4 * g + j;
-            const int64_t n = kRow * nh + col0;
-            const bool ok = (R > 1 || nh < 8) && n < a.N;
-            const int64_t e = ok ? n : col0;
+            const uint32_t off = (uint32_t)kRow * nh + lane_off;
+            const bool ok = (R > 1 || nh < 8) && off < nlim;
+            const int64_t e = ok ? off : lane_off;
             float vr[NCG], vi[NCG], t[NCG];
 #pragma unroll
             for (int q = 0; q < NCG; ++q) { vr[q] = yr[n1][j][q]; vi[q] = yi[n1][j][q]; }
             if (a.v) {
-                ldh<CT, NCG>(a.v, row0 + e, t);
+                ldh<CT, NCG>(vb0, e, t);
 #pragma unroll
                 for (int q = 0; q < NCG; ++q) vr[q] *= t[q];
                 if (row1 >= 0) {
-                    ldh<CT, NCG>(a.v, row1 + e, t);
+                    ldh<CT, NCG>(vb1, e, t);
 #pragma unroll
                     for (int q = 0; q < NCG; ++q) vi[q] *= t[q];
                 }
             }
             if (ok) {
-                sth_nt<CT, NCG>(a.y, row0 + n, vr);
-                if (row1 >= 0) sth_nt<CT, NCG>(a.y, row1 + n, vi);
+                sth_nt<CT, NCG>(yb0, e, vr);
+                if (row1 >= 0) sth_nt<CT, NCG>(yb1, e, vi);
             }
         }
     });
