@@ -305,20 +305,30 @@ __global__ void __launch_bounds__(512, 4) colmx_fwd_kernel(const ColArgs a) {
     });
 }
 
-template <int CT, int P>
+// PAIR (half rows, one real row per sequence): a block takes two sequences A, B and runs one
+// complex inverse on V_A + i V_B; the real part of the result is A's output and the imaginary
+// part B's (both are real), so the transform and its twiddles are shared by the two.
+template <int CT, int P, bool PAIR>
 __global__ void __launch_bounds__(512, 4) colmx_inv_kernel(const ColArgs a) {
     using C = Cm<P>;
     constexpr int R = C::R, H = C::H, RB = C::RB, HB = C::HB, NCG = C::NCG;
     __shared__ uint32_t Z[C::CB * C::ZC];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, x = lane & 15;
-    const int64_t s = blockIdx.y, n_lo0 = block_col0<P>();
+    const int64_t s = PAIR ? 2 * (int64_t)blockIdx.y : (int64_t)blockIdx.y, n_lo0 = block_col0<P>();
+    const bool hasB = PAIR && s + 1 < a.nseq;  // an odd count's last block has A only
     const int64_t col0 = n_lo0 + NCG * x;
     int64_t row0, row1;
     seq_rows(a, a.seq0 + s, row0, row1);
+    if constexpr (PAIR) {  // row1: B's row (each sequence is one real row)
+        int64_t rb0, rb1;
+        seq_rows(a, a.seq0 + (hasB ? s + 1 : s), rb0, rb1);
+        row1 = hasB ? rb0 : -1;
+    }
     const float2* twc = (const float2*)a.tw_col;
     const int64_t mask = a.M - 1;
     // scalar bases and 32-bit lane offsets (as in the forward pass)
     const uint32_t* const wsb = (const uint32_t*)a.ws + s * a.rows * kRow + n_lo0;
+    const uint32_t* const wsbB = hasB ? wsb + a.rows * kRow : wsb;  // PAIR: B's rows (A's if none)
     const int64_t r1 = row1 >= 0 ? row1 : row0;
     uint16_t* const yb0 = (uint16_t*)a.y + row0 + n_lo0;
     uint16_t* const yb1 = (uint16_t*)a.y + r1 + n_lo0;
@@ -343,25 +353,14 @@ __global__ void __launch_bounds__(512, 4) colmx_inv_kernel(const ColArgs a) {
     // Rows k_hi >= a.rows are not stored (one real row per sequence): the column spectrum V of a
     // real column is conjugate-symmetric, V[P - k] = conj V[k], and with V = conj(w_M^{n_lo k})
     // times the stored value, row k reads as w_8192^{n_lo} conj(stored row P - k).
-    uint32_t in[R / 8][4][NCG];
-    static_for<0, R / 8>([&](auto ii) LCV_INLINE {
-        constexpr int i = decltype(ii)::value;
-        const int k1 = wave + 8 * i;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int kh = k1 + R * (4 * g + j), kr = kh < a.rows ? kh : P - kh;
-            ldw<NCG>(wsb, (int64_t)((uint32_t)kr * (uint32_t)kRow + lane_off), in[i][j]);
-        }
-    });
     const bool half = a.rows < P;
     float2 wrow[NCG];  // w_8192^{n_lo}
     static_for<0, NCG>([&](auto qq) LCV_INLINE {
         constexpr int q = decltype(qq)::value;
         wrow[q] = half ? tw_m(a.tw_lo, a.tw_hi, ((col0 + q) * P) & mask) : make_float2(1.f, 0.f);
     });
-    static_for<0, R / 8>([&](auto ii) LCV_INLINE {
-        constexpr int i = decltype(ii)::value;
-        const int k1 = wave + 8 * i;
+    // one k1: the twiddled, packed operand of column tile q from the raw rows zw (PAIR: and zwB)
+    auto stage1 = [&](int k1, const uint32_t (*zw)[NCG], const uint32_t (*zwB)[NCG]) LCV_INLINE {
         // conj(w_P^{n2 k1}) for n2 = 4 g + j
         const float2 p1 = twc[k1];
         float2 tp[4];
@@ -375,8 +374,22 @@ __global__ void __launch_bounds__(512, 4) colmx_inv_kernel(const ColArgs a) {
             Operand<CT> op;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float zr = unpack_lo<CT>(in[i][j][q]), zi = unpack_hi<CT>(in[i][j][q]);
-                if (k1 + R * (4 * g + j) >= a.rows) {  // mirrored row: w_8192^{n_lo} conj(z)
+                float zr = unpack_lo<CT>(zw[j][q]), zi = unpack_hi<CT>(zw[j][q]);
+                const bool mirrored = k1 + R * (4 * g + j) >= a.rows;
+                if constexpr (PAIR) {
+                    // Z = V_A + i V_B; a mirrored row is w_8192^{n_lo} conj(stored A + i conj stored B)
+                    const float br = hasB ? unpack_lo<CT>(zwB[j][q]) : 0.f;
+                    const float bi = hasB ? unpack_hi<CT>(zwB[j][q]) : 0.f;
+                    if (mirrored) {
+                        const float mr = zr + bi, mi = br - zi;
+                        zr = mr * wrow[q].x - mi * wrow[q].y;
+                        zi = mr * wrow[q].y + mi * wrow[q].x;
+                    } else {
+                        const float mr = zr - bi, mi = zi + br;
+                        zr = mr;
+                        zi = mi;
+                    }
+                } else if (mirrored) {  // mirrored row: w_8192^{n_lo} conj(z)
                     const float mr = zr, mi = -zi;
                     zr = mr * wrow[q].x - mi * wrow[q].y;
                     zi = mr * wrow[q].y + mi * wrow[q].x;
@@ -395,7 +408,38 @@ __global__ void __launch_bounds__(512, 4) colmx_inv_kernel(const ColArgs a) {
                 Z[zaddr<P>(cs, n2, k1)] = pack2<CT>(zr, zi);
             }
         });
-    });
+    };
+    auto ldrows = [&](const uint32_t* base, int k1, uint32_t (*dst)[NCG]) LCV_INLINE {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int kh = k1 + R * (4 * g + j), kr = kh < a.rows ? kh : P - kh;
+            ldw<NCG>(base, (int64_t)((uint32_t)kr * (uint32_t)kRow + lane_off), dst[j]);
+        }
+    };
+    if constexpr (!PAIR) {
+        // all rows' loads first, then the arithmetic
+        uint32_t in[R / 8][4][NCG];
+        static_for<0, R / 8>([&](auto ii) LCV_INLINE {
+            ldrows(wsb, wave + 8 * decltype(ii)::value, in[decltype(ii)::value]);
+        });
+        static_for<0, R / 8>([&](auto ii) LCV_INLINE {
+            constexpr int i = decltype(ii)::value;
+            stage1(wave + 8 * i, in[i], in[i]);
+        });
+    } else {
+        // two sequences: the rows of k1 + 8 load while k1 is computed (double buffer)
+        uint32_t inA[2][4][NCG], inB[2][4][NCG];
+        ldrows(wsb, wave, inA[0]);
+        ldrows(wsbB, wave, inB[0]);
+        static_for<0, R / 8>([&](auto ii) LCV_INLINE {
+            constexpr int i = decltype(ii)::value;
+            if constexpr (i + 1 < R / 8) {
+                ldrows(wsb, wave + 8 * (i + 1), inA[(i + 1) & 1]);
+                ldrows(wsbB, wave + 8 * (i + 1), inB[(i + 1) & 1]);
+            }
+            stage1(wave + 8 * i, inA[i & 1], inB[i & 1]);
+        });
+    }
     __syncthreads();
 
     // Stage 2, per n2 (two per wave), NCG tiles: inverse radix R over k1 for the kept rows
@@ -761,7 +805,12 @@ hipError_t launch_t(bool fwd, const ColArgs& a, hipStream_t st) {
     static_assert(kRow / Cm<P>::CB % (8 * Cm<P>::S) == 0, "the XCD order needs whole groups");
     const dim3 grid((unsigned)(kRow / Cm<P>::CB), (unsigned)a.nseq);
     if (fwd) hipLaunchKernelGGL((colmx_fwd_kernel<CT, P>), grid, dim3(512), 0, st, a);
-    else hipLaunchKernelGGL((colmx_inv_kernel<CT, P>), grid, dim3(512), 0, st, a);
+    else if (P >= 512 && a.rows < P) {  // half rows: sequences in pairs (P = 256's wider tiles would spill)
+        const dim3 gp((unsigned)(kRow / Cm<P>::CB), (unsigned)((a.nseq + 1) / 2));
+        hipLaunchKernelGGL((colmx_inv_kernel<CT, P, true>), gp, dim3(512), 0, st, a);
+    } else {
+        hipLaunchKernelGGL((colmx_inv_kernel<CT, P, false>), grid, dim3(512), 0, st, a);
+    }
     return hipGetLastError();
 }
 
