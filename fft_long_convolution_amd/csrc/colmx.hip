@@ -137,16 +137,25 @@ __device__ __forceinline__ void stw(uint32_t* p, int64_t i, const uint32_t* w) {
 // global access moves NCG elements at once (whole 128-byte lines per row and instruction).  In
 // LDS the same value sits at slot 16 g + x.
 
-template <int CT, int P>
+// PAIR (sequences of one real row, half rows kept): the workgroup transforms sequences s and
+// s + 1 as one complex signal x_s + i x_{s+1} and splits the result in the second stage.
+template <int CT, int P, bool PAIR>
 __global__ void __launch_bounds__(512, 4) colmx_fwd_kernel(const ColArgs a) {
     using C = Cm<P>;
     constexpr int R = C::R, H = C::H, RB = C::RB, HB = C::HB, NCG = C::NCG;
     __shared__ uint32_t Y[C::CB * C::YC];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, x = lane & 15;
-    const int64_t s = blockIdx.y, n_lo0 = block_col0<P>();
+    const int lane = threadIdx.x & 63, g = lane >> 4, x = lane & 15;
+    const int wave = PAIR ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : threadIdx.x >> 6;
+    const int64_t s = PAIR ? 2 * (int64_t)blockIdx.y : blockIdx.y, n_lo0 = block_col0<P>();
+    const bool hasB = PAIR && s + 1 < a.nseq;
     const int64_t col0 = n_lo0 + NCG * x;  // this lane's first column
     int64_t row0, row1;
     seq_rows(a, a.seq0 + s, row0, row1);
+    if constexpr (PAIR) {  // row1: the second sequence's row (each sequence is one real row)
+        int64_t rb0, rb1;
+        seq_rows(a, a.seq0 + (hasB ? s + 1 : s), rb0, rb1);
+        row1 = hasB ? rb0 : -1;
+    }
     const float2* twc = (const float2*)a.tw_col;
     // Scalar bases (this block's first column of each input row) and 32-bit lane offsets: the
     // loads take the scalar-base address form, with no 64-bit arithmetic per element.
@@ -262,47 +271,119 @@ __global__ void __launch_bounds__(512, 4) colmx_fwd_kernel(const ColArgs a) {
     });
     __syncthreads();
 
-    // Stage 2, per k1 (R/8 per wave), NCG tiles: 16-point DFT over n2, the four-step twiddle
-    // w_M^{n_lo k_hi}, store rows k_hi = k1 + R k2 of the workspace.
     const MatImg<CT> f16 = load_img<CT>(a.img, C::G.f16, lane);
     const int64_t mask = a.M - 1;
     uint32_t* const wsb = (uint32_t*)a.ws + s * a.rows * kRow + n_lo0;  // this block's row 0
-    // w_M^{n_lo k_hi} for k_hi = k1 + R (4 g + j), k1 = wave + 8 i: per column, a base for
-    // i = 0, a step for i, and a step for j (products of fp32 table values; at most 11 steps)
-    float2 wb[NCG], wi[NCG], wj[NCG];
-    static_for<0, NCG>([&](auto qq) LCV_INLINE {
-        constexpr int q = decltype(qq)::value;
-        const int64_t n_lo = col0 + q;
-        wb[q] = tw_m(a.tw_lo, a.tw_hi, (n_lo * (wave + 4 * g * R)) & mask);
-        wi[q] = tw_m(a.tw_lo, a.tw_hi, (n_lo * 8) & mask);
-        wj[q] = tw_m(a.tw_lo, a.tw_hi, (n_lo * R) & mask);
-    });
-    static_for<0, R / 8>([&](auto ii) LCV_INLINE {
-        const int k1 = wave + 8 * decltype(ii)::value;
-        uint32_t out[4][NCG];
+    if constexpr (PAIR) {
+        // Stage 2 for z = x_A + i x_B.  Rows k of the two real transforms follow from rows k and
+        // P - k of Z (Hermitian split): X_A[k] = (Z[k] + conj Z[P-k]) / 2 and
+        // X_B[k] = (Z[k] - conj Z[P-k]) / 2i; only rows k <= P/2 are kept.  A slot takes digits
+        // k1a and k1b = R - k1a: the 16-point DFT of k1a (tile rows k2 = 4 g + j) and the
+        // row-reversed one of k1b (rows 15 - k2) leave Z[k] and Z[P - k] in one lane.  Lanes
+        // g < 2 keep the rows of k1a, lanes g >= 2 those of k1b.  The self-paired digits: k1 = 0
+        // takes its partner from the conjugate DFT (rows (16 - k2) mod 16; written as k1b = R),
+        // k1 = R/2 from the reversed one; each keeps its rows k <= P/2 only.
+        const MatImg<CT> f16r = load_img<CT>(a.img, C::G.f16r, lane);
+        uint32_t* const wsbB = wsb + a.rows * kRow;  // B's row 0 (used only with hasB)
+        const bool lo = g < 2;
+        const float sg = lo ? 1.f : -1.f;
+        // w_M^{n_lo k} of a kept row k = e - / + R j: per column, the step in j
+        float2 wjs[NCG];
         static_for<0, NCG>([&](auto qq) LCV_INLINE {
             constexpr int q = decltype(qq)::value;
-            const int cs = 16 * q + x;
-            Operand<CT> op;
+            const float2 w = tw_m(a.tw_lo, a.tw_hi, ((col0 + q) * R) & mask);
+            wjs[q] = lo ? w : make_float2(w.x, -w.y);
+        });
+        auto slot = [&](int k1a, int k1b, const MatImg<CT>& mb, int nkeep) LCV_INLINE {
+            // this lane's kept rows: e + R j (g < 2) or e - R j (g >= 2)
+            const int e = lo ? k1a + 4 * g * R : k1b + R * (15 - 4 * g);
+            uint32_t oa[4][NCG], ob[4][NCG];
+            static_for<0, NCG>([&](auto qq) LCV_INLINE {
+                constexpr int q = decltype(qq)::value;
+                const int cs = 16 * q + x;
+                Operand<CT> opa, opb;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) op.w[j] = Y[yaddr<P>(cs, k1, 4 * g + j)];
-            Tile t = stage_keep<CT>(f16, op);  // rows k2 = 4 g + j
-            float2 w = wb[q];
+                for (int j = 0; j < 4; ++j) {
+                    opa.w[j] = Y[yaddr<P>(cs, k1a, 4 * g + j)];
+                    opb.w[j] = Y[yaddr<P>(cs, k1b & (R - 1), 4 * g + j)];
+                }
+                const Tile ta = stage_keep<CT>(f16, opa), tb = stage_keep<CT>(mb, opb);
+                // the 1/2 of the split rides on the twiddle
+                float2 w = tw_m(a.tw_lo, a.tw_hi, ((col0 + q) * e) & mask);
+                w.x *= 0.5f;
+                w.y *= 0.5f;
+                // with own row a = ta, partner b = tb: X_A = a + conj b, X_B = -i (a - conj b);
+                // swapping a and b (lanes g >= 2) conjugates both
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float ar = ta.re[j] + tb.re[j], ai = sg * (ta.im[j] - tb.im[j]);
+                    float br = ta.im[j] + tb.im[j], bi = sg * (tb.re[j] - ta.re[j]);
+                    cmul(ar, ai, w.x, w.y);
+                    cmul(br, bi, w.x, w.y);
+                    oa[j][q] = pack2<CT>(ar, ai);
+                    ob[j][q] = pack2<CT>(br, bi);
+                    w = cmulf(w, wjs[q]);
+                }
+            });
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float xr = t.re[j], xi = t.im[j];
-                cmul(xr, xi, w.x, w.y);
-                w = cmulf(w, wj[q]);
-                out[j][q] = pack2<CT>(xr, xi);
+                if (lo || 4 * g + j < nkeep) {
+                    const uint32_t kh = lo ? e + R * j : e - R * j;
+                    stw<NCG>(wsb, (int64_t)(kh * (uint32_t)kRow + lane_off), oa[j]);
+                    if (hasB) stw<NCG>(wsbB, (int64_t)(kh * (uint32_t)kRow + lane_off), ob[j]);
+                }
             }
-            wb[q] = cmulf(wb[q], wi[q]);
-        });
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int kh = k1 + R * (4 * g + j);
-            if (kh < a.rows) stw<NCG>(wsb, (int64_t)((uint32_t)kh * (uint32_t)kRow + lane_off), out[j]);
+        };
+        // digit pairs of this wave: k1a = w + 16 i (w = 1, 2, 3), 16 - w + 16 i (w = 5, 6, 7),
+        // 4 + 8 i (w = 4), 8 + 8 i (w = 0, which also takes the self-paired 0 and R/2)
+        const int kb0 = wave == 0 ? 8 : wave == 4 ? 4 : wave < 4 ? wave : 16 - wave;
+        const int ks = (wave & 3) == 0 ? 8 : 16, cnt = wave == 0 ? R / 16 - 1 : R / 16;
+        for (int i = 0; i < cnt; ++i) slot(kb0 + ks * i, R - kb0 - ks * i, f16r, 16);
+        if (wave == 0) {
+            const MatImg<CT> i16 = load_img<CT>(a.img, C::G.i16, lane);  // rows (16 - k2) mod 16
+            slot(0, R, i16, 9);
+            slot(R / 2, R / 2, f16r, 8);
         }
-    });
+    } else {
+        // Stage 2, per k1 (R/8 per wave), NCG tiles: 16-point DFT over n2, the four-step twiddle
+        // w_M^{n_lo k_hi}, store rows k_hi = k1 + R k2 of the workspace.
+        // w_M^{n_lo k_hi} for k_hi = k1 + R (4 g + j), k1 = wave + 8 i: per column, a base for
+        // i = 0, a step for i, and a step for j (products of fp32 table values; at most 11 steps)
+        float2 wb[NCG], wi[NCG], wj[NCG];
+        static_for<0, NCG>([&](auto qq) LCV_INLINE {
+            constexpr int q = decltype(qq)::value;
+            const int64_t n_lo = col0 + q;
+            wb[q] = tw_m(a.tw_lo, a.tw_hi, (n_lo * (wave + 4 * g * R)) & mask);
+            wi[q] = tw_m(a.tw_lo, a.tw_hi, (n_lo * 8) & mask);
+            wj[q] = tw_m(a.tw_lo, a.tw_hi, (n_lo * R) & mask);
+        });
+        static_for<0, R / 8>([&](auto ii) LCV_INLINE {
+            const int k1 = wave + 8 * decltype(ii)::value;
+            uint32_t out[4][NCG];
+            static_for<0, NCG>([&](auto qq) LCV_INLINE {
+                constexpr int q = decltype(qq)::value;
+                const int cs = 16 * q + x;
+                Operand<CT> op;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) op.w[j] = Y[yaddr<P>(cs, k1, 4 * g + j)];
+                Tile t = stage_keep<CT>(f16, op);  // rows k2 = 4 g + j
+                float2 w = wb[q];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float xr = t.re[j], xi = t.im[j];
+                    cmul(xr, xi, w.x, w.y);
+                    w = cmulf(w, wj[q]);
+                    out[j][q] = pack2<CT>(xr, xi);
+                }
+                wb[q] = cmulf(wb[q], wi[q]);
+            });
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int kh = k1 + R * (4 * g + j);
+                if (kh < a.rows) stw<NCG>(wsb, (int64_t)((uint32_t)kh * (uint32_t)kRow + lane_off), out[j]);
+            }
+        });
+    }
 }
 
 // PAIR (half rows, one real row per sequence): a block takes two sequences A, B and runs one
@@ -804,9 +885,10 @@ template <int CT, int P>
 hipError_t launch_t(bool fwd, const ColArgs& a, hipStream_t st) {
     static_assert(kRow / Cm<P>::CB % (8 * Cm<P>::S) == 0, "the XCD order needs whole groups");
     const dim3 grid((unsigned)(kRow / Cm<P>::CB), (unsigned)a.nseq);
-    if (fwd) hipLaunchKernelGGL((colmx_fwd_kernel<CT, P>), grid, dim3(512), 0, st, a);
+    const dim3 gp((unsigned)(kRow / Cm<P>::CB), (unsigned)((a.nseq + 1) / 2));  // sequence pairs
+    if (fwd && a.rows < P) hipLaunchKernelGGL((colmx_fwd_kernel<CT, P, true>), gp, dim3(512), 0, st, a);
+    else if (fwd) hipLaunchKernelGGL((colmx_fwd_kernel<CT, P, false>), grid, dim3(512), 0, st, a);
     else if (P >= 512 && a.rows < P) {  // half rows: sequences in pairs (P = 256's wider tiles would spill)
-        const dim3 gp((unsigned)(kRow / Cm<P>::CB), (unsigned)((a.nseq + 1) / 2));
         hipLaunchKernelGGL((colmx_inv_kernel<CT, P, true>), gp, dim3(512), 0, st, a);
     } else {
         hipLaunchKernelGGL((colmx_inv_kernel<CT, P, false>), grid, dim3(512), 0, st, a);

@@ -197,6 +197,7 @@ std::vector<uint8_t> build_colmx_tables(int P, int ct) {
             });
     append_image(t, ct, [&](int k2, int n2) { return omega((int64_t)n2 * k2, 16); });
     append_image(t, ct, [&](int n2, int k2) { return omega(-(int64_t)n2 * k2, 16); });
+    append_image(t, ct, [&](int r, int n2) { return omega((int64_t)n2 * (15 - r), 16); });
     return t;
 }
 

@@ -63,14 +63,15 @@ bool col_tables(int64_t M, int64_t M1, ColTables* out, hipError_t* err, bool bui
 // radix-R DFT over n1 (forward: only n1 < H = R/2 is nonzero; inverse: only n1 < H is kept),
 // the second a 16-point DFT over n2.  Image indices in the table: the forward first stage
 // (k1 block rb, n1 block kc) at f1 + rb * hb + kc, the inverse first stage (n1 block rb, k1
-// block kc) at i2 + rb * rbk + kc, the 16-point DFT and its inverse at f16 and i16.
+// block kc) at i2 + rb * rbk + kc, the 16-point DFT and its inverse at f16 and i16, and the
+// 16-point DFT with its output rows reversed (row r holds k2 = 15 - r) at f16r.
 struct ColMxGrid {
     int R, H, rbk, hb;       // radix, half radix, 16-blocks of k1, 16-blocks of n1 < H
-    int f1, i2, f16, i16, nimg;
+    int f1, i2, f16, i16, f16r, nimg;
 };
 constexpr ColMxGrid colmx_grid(int P) {
-    const int R = P / 16, H = R / 2, rbk = R / 16, hb = (H + 15) / 16;
-    return ColMxGrid{R, H, rbk, hb, 0, rbk * hb, 2 * rbk * hb, 2 * rbk * hb + 1, 2 * rbk * hb + 2};
+    const int R = P / 16, H = R / 2, rbk = R / 16, hb = (H + 15) / 16, b = 2 * rbk * hb;
+    return ColMxGrid{R, H, rbk, hb, 0, rbk * hb, b, b + 1, b + 2, b + 3};
 }
 constexpr bool colmx_supported(int64_t P) { return P >= 16 && P <= 1024 && (P & (P - 1)) == 0; }
 // Device pointer to those images for (P, ct) on the current device (ct 16-bit).

@@ -40,6 +40,8 @@ CASES = [
     (1, 2, 2300000, "bf16", False),     # M = 2^23, M1 = 1024
     (1, 3, 1572864, "bf16", True),      # M1 = 512, one real row per sequence: paired inverse, odd count
     (1, 5, 2097152, "f16", False),      # M1 = 512, paired inverse, odd count
+    (1, 3, 700000, "f16", True),        # M1 = 256, one real row per sequence, odd count
+    (1, 3, 2200000, "bf16", True),      # M1 = 1024, one real row per sequence, odd count
 ]
 
 
