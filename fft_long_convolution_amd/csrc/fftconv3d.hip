@@ -187,10 +187,232 @@ __global__ void __launch_bounds__(256) k3_slices_inv(const Conv3DArgs a) {
     }
 }
 
+// ---- matrix-core passes: 16-bit compute types, S = 32 (P = 64) -------------------------------
+// Every DFT is the dense 64-point matrix in 4 x 4 blocks of 16 x 16 (dense_dft_tables): forward
+// inputs are half zero and inverse outputs are kept only in the window (rows 16 .. 47), so each
+// transform uses 8 of the 16 blocks, held in registers.  A tile is 16 x 16 complex values, lane
+// (g, c) holding rows 4 g + j of column c (the operand and result layout of lconv_device.h); a
+// stage with the data as the second operand keeps that layout, one with the data as the first
+// operand transposes it, which turns the row DFT's output into the column DFT's input without
+// a trip through LDS.  Each wave works on its own slices or rows: no LDS and no barrier.
+// (The digit split of "FlashFFTConv" (abstract) and the "FlashConv" page's Mechanism, with the
+// whole 64-point DFT as one matrix: at this size the blocks are cheaper than a second split.)
+constexpr int M3_S = 32, M3_P = 64;
+constexpr int M3_ZW = 2;  // slices per wave (passes A and C)
+constexpr int M3_TZ = 8;  // (ky, kx block) rows per wave (pass Z)
+
+template <int CT>
+__device__ __forceinline__ MatImg<CT> img_f(const void* img, int kb, int nb, int lane) {
+    return load_img<CT>(img, 4 * kb + nb, lane);
+}
+template <int CT>
+__device__ __forceinline__ MatImg<CT> img_i(const void* img, int mb, int kb, int lane) {
+    return load_img<CT>(img, 16 + 4 * mb + kb, lane);
+}
+
+// Pass A: per input slice z, DFT over x then over y, into W[z][ky][kx].
+template <int CT>
+__global__ void __launch_bounds__(256) k3m_slices_fwd(const Conv3DArgs a) {
+    constexpr int S = M3_S, P = M3_P;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+    const int64_t ul = blockIdx.y, unit = a.unit0 + ul;
+    int64_t ch, row0, row1;
+    unit_rows(a, unit, (int64_t)S * S * S, ch, row0, row1);
+    MatImg<CT> F[4][2];  // forward blocks (k block, n block < 2)
+    static_for<0, 4>([&](auto kk) LCV_INLINE {
+        static_for<0, 2>([&](auto nn) LCV_INLINE {
+            F[decltype(kk)::value][decltype(nn)::value] = img_f<CT>(a.img, decltype(kk)::value, decltype(nn)::value, lane);
+        });
+    });
+    const uint16_t* const ua = (const uint16_t*)a.u + row0;
+    const uint16_t* const ub = (const uint16_t*)a.u + (row1 >= 0 ? row1 : row0);
+#pragma unroll 1
+    for (int zi = 0; zi < M3_ZW; ++zi) {
+        const int z = (blockIdx.x * 4 + wave) * M3_ZW + zi;
+        // d(xb, yb): rows x = 16 xb + 4 g + j, column y = 16 yb + c; the two images as re, im
+        Operand<CT> d[2][2];
+        static_for<0, 2>([&](auto xx) LCV_INLINE {
+            static_for<0, 2>([&](auto yy) LCV_INLINE {
+                constexpr int xb = decltype(xx)::value, yb = decltype(yy)::value;
+                const int64_t off = ((int64_t)z * S + 16 * yb + c) * S + 16 * xb + 4 * g;
+                const uint2 pa = *(const uint2*)(ua + off);
+                const uint2 pb = row1 >= 0 ? *(const uint2*)(ub + off) : make_uint2(0u, 0u);
+                d[xb][yb].w[0] = __byte_perm(pa.x, pb.x, 0x5410);
+                d[xb][yb].w[1] = __byte_perm(pa.x, pb.x, 0x7632);
+                d[xb][yb].w[2] = __byte_perm(pa.y, pb.y, 0x5410);
+                d[xb][yb].w[3] = __byte_perm(pa.y, pb.y, 0x7632);
+            });
+        });
+        // DFT over x, transposed: x1(yb, kb) holds rows y, column kx
+        Operand<CT> x1[2][4];
+        static_for<0, 2>([&](auto yy) LCV_INLINE {
+            static_for<0, 4>([&](auto kk) LCV_INLINE {
+                constexpr int yb = decltype(yy)::value, kb = decltype(kk)::value;
+                f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
+                stage_swap_acc<CT>(F[kb][0], d[0][yb], re, im);
+                stage_swap_acc<CT>(F[kb][1], d[1][yb], re, im);
+                x1[yb][kb] = to_operand<CT>(tile_from_acc(re, im));
+            });
+        });
+        // DFT over y: rows ky, column kx; stored as W[z][ky][kx]
+        uint32_t* const wz = (uint32_t*)a.ws + (ul * S + z) * P * P;
+        static_for<0, 4>([&](auto kk) LCV_INLINE {
+            static_for<0, 4>([&](auto yy) LCV_INLINE {
+                constexpr int kb = decltype(kk)::value, kyb = decltype(yy)::value;
+                f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
+                stage_keep_acc<CT>(F[kyb][0], x1[0][kb], re, im);
+                stage_keep_acc<CT>(F[kyb][1], x1[1][kb], re, im);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) wz[(16 * kyb + 4 * g + j) * P + 16 * kb + c] = pack2<CT>(re[j], im[j]);
+            });
+        });
+    }
+}
+
+// Pass Z: per row (ky, kx block of 16), DFT over z, product with (K + D (-i)^(kx+ky+kz)) / P^3,
+// inverse DFT for the window slices, written back to W[zo][ky][kx] (the row's own elements).
+template <int CT>
+__global__ void __launch_bounds__(256) k3m_zpass(const Conv3DArgs a) {
+    constexpr int S = M3_S, P = M3_P;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+    const int64_t ul = blockIdx.y, unit = a.unit0 + ul;
+    int64_t ch, row0, row1;
+    unit_rows(a, unit, (int64_t)S * S * S, ch, row0, row1);
+    MatImg<CT> F[4][2], Fi[2][4];  // forward (kz block, z block < 2); inverse (window block, kz block)
+    static_for<0, 4>([&](auto kk) LCV_INLINE {
+        constexpr int k = decltype(kk)::value;
+        static_for<0, 2>([&](auto nn) LCV_INLINE {
+            constexpr int n = decltype(nn)::value;
+            F[k][n] = img_f<CT>(a.img, k, n, lane);
+            Fi[n][k] = img_i<CT>(a.img, 1 + n, k, lane);
+        });
+    });
+    const float dsk = raw1_to_f32<CT>(load1_raw<CT>(a.D, ch)) * a.inv_p3;
+    constexpr uint32_t P2 = P * P;
+    // scalar bases per row, 32-bit lane offsets (slice 4 g + j, column c) fixed for the wave
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lo = (uint32_t)(4 * g) * P2 + (uint32_t)c;
+    uint32_t* const wsu = (uint32_t*)a.ws + ul * S * P2;
+    const uint32_t* const kfc = (const uint32_t*)a.kf + ch * P * P2;
+#pragma unroll 1
+    for (int ti = 0; ti < M3_TZ; ++ti) {
+        const int task = (blockIdx.x * 4 + wv) * M3_TZ + ti;  // < 256, wave-uniform
+        const int ky = task >> 2, kb = task & 3, kx0 = 16 * kb;
+        uint32_t* const wr = wsu + ky * P + kx0;          // + z P^2 + lane offset
+        const uint32_t* const kr = kfc + ky * P + kx0;    // + kz P^2 + lane offset
+        Operand<CT> w[2];
+        static_for<0, 2>([&](auto zz) LCV_INLINE {
+            constexpr int zb = decltype(zz)::value;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w[zb].w[j] = wr[lo + (uint32_t)(16 * zb + j) * P2];
+        });
+        uint32_t kw[4][4];
+        static_for<0, 4>([&](auto kk) LCV_INLINE {
+            constexpr int kzb = decltype(kk)::value;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) kw[kzb][j] = kr[lo + (uint32_t)(16 * kzb + j) * P2];
+        });
+        const int kx = kx0 + c;
+        Operand<CT> zp[4];
+        static_for<0, 4>([&](auto kk) LCV_INLINE {
+            constexpr int kzb = decltype(kk)::value;
+            f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
+            stage_keep_acc<CT>(F[kzb][0], w[0], re, im);
+            stage_keep_acc<CT>(F[kzb][1], w[1], re, im);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // the skip: a delta at the kernel centre, spectrum (-i)^(kx + ky + kz)
+                const int ph = (kx + ky + 16 * kzb + 4 * g + j) & 3;
+                const float kre = unpack_lo<CT>(kw[kzb][j]) + (ph == 0 ? dsk : ph == 2 ? -dsk : 0.f);
+                const float kim = unpack_hi<CT>(kw[kzb][j]) + (ph == 1 ? -dsk : ph == 3 ? dsk : 0.f);
+                float xr = re[j], xi = im[j];
+                cmul(xr, xi, kre, kim);
+                re[j] = xr;
+                im[j] = xi;
+            }
+            zp[kzb] = to_operand<CT>(tile_from_acc(re, im));
+        });
+        static_for<0, 2>([&](auto mm) LCV_INLINE {
+            constexpr int mb = decltype(mm)::value;
+            f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
+            static_for<0, 4>([&](auto kk) LCV_INLINE {
+                stage_keep_acc<CT>(Fi[mb][decltype(kk)::value], zp[decltype(kk)::value], re, im);
+            });
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wr[lo + (uint32_t)(16 * mb + j) * P2] = pack2<CT>(re[j], im[j]);  // zo
+        });
+    }
+}
+
+// Pass C: per window slice zo, inverse DFT over ky (window rows), then over kx (window columns),
+// and the store of both images.
+template <int CT>
+__global__ void __launch_bounds__(256) k3m_slices_inv(const Conv3DArgs a) {
+    constexpr int S = M3_S, P = M3_P;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+    const int64_t ul = blockIdx.y, unit = a.unit0 + ul;
+    int64_t ch, row0, row1;
+    unit_rows(a, unit, (int64_t)S * S * S, ch, row0, row1);
+    MatImg<CT> Fi[2][4];  // inverse blocks (window block, k block)
+    static_for<0, 2>([&](auto mm) LCV_INLINE {
+        static_for<0, 4>([&](auto kk) LCV_INLINE {
+            Fi[decltype(mm)::value][decltype(kk)::value] = img_i<CT>(a.img, 1 + decltype(mm)::value, decltype(kk)::value, lane);
+        });
+    });
+    uint16_t* const ya = (uint16_t*)a.y + row0;
+    uint16_t* const yb2 = (uint16_t*)a.y + (row1 >= 0 ? row1 : row0);
+#pragma unroll 1
+    for (int zi = 0; zi < M3_ZW; ++zi) {
+        const int zo = (blockIdx.x * 4 + wave) * M3_ZW + zi;
+        const uint32_t* const wz = (const uint32_t*)a.ws + (ul * S + zo) * P * P;
+        // inverse DFT over ky, transposed: y1(kxb, myb) holds rows kx, column my (window)
+        Operand<CT> y1[4][2];
+        static_for<0, 4>([&](auto xx) LCV_INLINE {
+            constexpr int kxb = decltype(xx)::value;
+            Operand<CT> w[4];  // rows ky = 16 kyb + 4 g + j, column kx = 16 kxb + c
+            static_for<0, 4>([&](auto yy) LCV_INLINE {
+                constexpr int kyb = decltype(yy)::value;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) w[kyb].w[j] = wz[(16 * kyb + 4 * g + j) * P + 16 * kxb + c];
+            });
+            static_for<0, 2>([&](auto mm) LCV_INLINE {
+                constexpr int myb = decltype(mm)::value;
+                f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
+                static_for<0, 4>([&](auto yy) LCV_INLINE {
+                    stage_swap_acc<CT>(Fi[myb][decltype(yy)::value], w[decltype(yy)::value], re, im);
+                });
+                y1[kxb][myb] = to_operand<CT>(tile_from_acc(re, im));
+            });
+        });
+        // inverse DFT over kx: rows mx (window), column my; image A is the real part, B the
+        // imaginary part: lane (g, c) stores x = 16 mxb + 4 g .. + 3 of row y = 16 myb + c
+        static_for<0, 2>([&](auto xx) LCV_INLINE {
+            static_for<0, 2>([&](auto mm) LCV_INLINE {
+                constexpr int mxb = decltype(xx)::value, myb = decltype(mm)::value;
+                f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
+                static_for<0, 4>([&](auto kk) LCV_INLINE {
+                    stage_keep_acc<CT>(Fi[mxb][decltype(kk)::value], y1[decltype(kk)::value][myb], re, im);
+                });
+                const int64_t off = ((int64_t)zo * S + 16 * myb + c) * S + 16 * mxb + 4 * g;
+                *(uint2*)(ya + off) = make_uint2(pack2<CT>(re[0], re[1]), pack2<CT>(re[2], re[3]));
+                if (row1 >= 0) *(uint2*)(yb2 + off) = make_uint2(pack2<CT>(im[0], im[1]), pack2<CT>(im[2], im[3]));
+            });
+        });
+    }
+}
+
 template <int S, int CT, int IO>
 static hipError_t launch3_t(const Conv3DArgs& a, hipStream_t st) {
     if (a.nunit <= 0) return hipSuccess;
     const dim3 blk(256);
+    if constexpr (S == M3_S && CT != CT_F32) {
+        if (!a.filter && a.img) {
+            hipLaunchKernelGGL((k3m_slices_fwd<CT>), dim3(S / (4 * M3_ZW), (unsigned)a.nunit), blk, 0, st, a);
+            hipLaunchKernelGGL((k3m_zpass<CT>), dim3(M3_P * 4 / (4 * M3_TZ), (unsigned)a.nunit), blk, 0, st, a);
+            hipLaunchKernelGGL((k3m_slices_inv<CT>), dim3(S / (4 * M3_ZW), (unsigned)a.nunit), blk, 0, st, a);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((k3_slices_fwd<S, CT, IO>), dim3(S, (unsigned)a.nunit), blk, 0, st, a);
     if (a.filter) {
         hipLaunchKernelGGL((k3_zpass<S, CT, IO, true>), dim3(2 * S, (unsigned)a.nunit), blk, 0, st, a);

@@ -182,6 +182,7 @@ struct Conv3DArgs {
     void* y;             // [B][C][S][S][S]; filter mode: the filter spectrum
     void* ws;            // workspace [nunit][S][P][P] complex (compute type; fp32 in filter mode)
     const float* tw;     // exp(-2 pi i e / P), e < P (fp32 complex)
+    const void* img;     // dense P-point DFT images (16-bit S = 32 convolution: matrix-core passes)
     int64_t B, C, S;
     int64_t unit0, nunit;
     float inv_p3;        // 1 / P^3

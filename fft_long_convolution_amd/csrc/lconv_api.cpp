@@ -1040,11 +1040,17 @@ lconv_status_t lconv_fftconv3d_fwd(const void* u, const void* k_f, const void* D
     hipError_t err = hipSuccess;
     const float* tw = dft_table(2 * S, &err);
     if (!tw) return LCONV_ERR_HIP;
+    // 16-bit S = 32: the matrix-core passes (dense 64-point DFT blocks)
+    const void* img = nullptr;
+    if (S == 32 && dtype != LCONV_F32) {
+        img = dense_dft_tables(2 * S, (int)dtype, &err);
+        if (!img) return LCONV_ERR_HIP;
+    }
     const int64_t units = pairs_per_channel(B) * C;
     const int64_t per = chunk3(units, S, work_complex_size(dtype, false));
     for (int64_t u0 = 0; u0 < units; u0 += per) {
         Conv3DArgs a{};
-        a.u = u; a.kf = k_f; a.D = D; a.y = y; a.ws = workspace; a.tw = tw;
+        a.u = u; a.kf = k_f; a.D = D; a.y = y; a.ws = workspace; a.tw = tw; a.img = img;
         a.B = B; a.C = C; a.S = S; a.unit0 = u0; a.nunit = per < units - u0 ? per : units - u0;
         a.inv_p3 = 1.0f / (float)(8 * S * S * S); a.filter = 0;
         if (launch_conv3d(dtype, a, stream) != hipSuccess) return LCONV_ERR_HIP;

@@ -201,6 +201,18 @@ std::vector<uint8_t> build_colmx_tables(int P, int ct) {
     return t;
 }
 
+std::vector<uint8_t> build_dense_dft_tables(int P, int ct) {
+    const int NB = P / 16;
+    std::vector<uint8_t> t;
+    for (int kb = 0; kb < NB; ++kb)
+        for (int nb = 0; nb < NB; ++nb)
+            append_image(t, ct, [&](int r, int c) { return omega((int64_t)(16 * kb + r) * (16 * nb + c), P); });
+    for (int mb = 0; mb < NB; ++mb)
+        for (int kb = 0; kb < NB; ++kb)
+            append_image(t, ct, [&](int r, int c) { return omega(-(int64_t)(16 * mb + r) * (16 * kb + c), P); });
+    return t;
+}
+
 struct DevBuf {
     void* ptr = nullptr;
     std::vector<uint8_t> host;  // kept alive for the lifetime of the cache
@@ -236,6 +248,7 @@ const void* get_or_build(int kind, int ct, int64_t a, int64_t b,
 std::vector<uint8_t> build_any(int kind, int ct, int64_t a, int64_t b) {
     if (kind == 0) return build_fused_tables((int)a, ct);
     if (kind == 3) return build_colmx_tables((int)a, ct);
+    if (kind == 4) return build_dense_dft_tables((int)a, ct);
     if (kind == 2) {  // P-point DFT twiddles
         std::vector<uint8_t> t((size_t)a * 8);
         float* f = (float*)t.data();
@@ -300,6 +313,11 @@ const void* colmx_tables(int64_t P, int ct, hipError_t* err, bool build) {
 
 const float* dft_table(int64_t P, hipError_t* err) {
     return (const float*)get_or_build(2, 0, P, 0, build_any, err);
+}
+
+const void* dense_dft_tables(int64_t P, int ct, hipError_t* err) {
+    if (P < 16 || P > 64 || P % 16 != 0 || ct == CT_F32) { *err = hipErrorInvalidValue; return nullptr; }
+    return get_or_build(4, ct, P, 0, build_any, err);
 }
 
 int device_cu_count(hipError_t* err) {

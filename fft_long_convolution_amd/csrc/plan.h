@@ -80,6 +80,11 @@ const void* colmx_tables(int64_t P, int ct, hipError_t* err, bool build = true);
 // exp(-2 pi i e / P) for e < P, fp32 complex, on the current device (3D path).
 const float* dft_table(int64_t P, hipError_t* err);
 
+// The dense P-point DFT (P = 16 NB, NB <= 4) as 16 x 16 matrix-core images, 16-bit compute types:
+// forward block (kb, nb) = w_P^{k n} for k = 16 kb + row, n = 16 nb + column, at kb NB + nb;
+// inverse block (mb, kb) = w_P^{-m k}, at NB^2 + mb NB + kb.
+const void* dense_dft_tables(int64_t P, int ct, hipError_t* err);
+
 // Cached device properties of the current device.
 int device_cu_count(hipError_t* err);
 

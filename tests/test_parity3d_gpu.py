@@ -50,7 +50,26 @@ def test_3d_s16_full(lc, nthreads, dtype, B):
     assert err <= TOL[dtype]
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("B", [1, 2])
+def test_3d_s32_full(lc, nthreads, dtype, B):
+    """S = 32 in 16-bit types (the matrix-core passes): every voxel of every volume, both images
+    of a batch pair (B = 2) and a lone image (B = 1)."""
+    C, S = 1, 32
+    spec = wl.spec_3d(B, C, S, dtype, seed=90 + B)
+    say(f"[3d] dtype={dtype} B={B} C={C} S={S} seed={spec.seed} (every voxel)")
+    d = wl.make(spec)
+    y = run3d(lc, d)
+    assert np.all(np.isfinite(y))
+    g = np.stack(np.meshgrid(np.arange(B), np.arange(C), np.arange(S), np.arange(S), np.arange(S),
+                             indexing="ij"), -1).reshape(-1, 5)
+    ref = oracle.conv3d_points(d["u"], d["k"], d["D"], g, dt=DT_ORACLE[dtype], nthreads=nthreads)
+    err = float(rel_l2_rows(y.reshape(B * C, -1), ref.reshape(B * C, -1)).max())
+    say(f"   max rel L2 per volume = {err:.3e} (tol {TOL[dtype]})")
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_3d_s32_sampled(lc, nthreads, dtype):
     B, C, S = 3, 3, 32
     spec = wl.spec_3d(B, C, S, dtype, seed=77)
