@@ -188,18 +188,24 @@ __global__ void __launch_bounds__(256) k3_slices_inv(const Conv3DArgs a) {
 }
 
 // ---- matrix-core passes: 16-bit compute types, S = 32 (P = 64) -------------------------------
-// Every DFT is the dense 64-point matrix in 4 x 4 blocks of 16 x 16 (dense_dft_tables): forward
-// inputs are half zero and inverse outputs are kept only in the window (rows 16 .. 47), so each
-// transform uses 8 of the 16 blocks, held in registers.  A tile is 16 x 16 complex values, lane
-// (g, c) holding rows 4 g + j of column c (the operand and result layout of lconv_device.h); a
-// stage with the data as the second operand keeps that layout, one with the data as the first
-// operand transposes it, which turns the row DFT's output into the column DFT's input without
-// a trip through LDS.  Each wave works on its own slices or rows: no LDS and no barrier.
+// Every DFT is the dense 64-point matrix in blocks of 16 x 16 (dense_dft_tables): forward inputs
+// are half zero and inverse outputs are kept only in the window (rows 16 .. 47), so each transform
+// uses half of its blocks, held in registers.  A tile is 16 x 16 complex values, lane (g, c)
+// holding rows 4 g + j of column c (the operand and result layout of lconv_device.h); a stage
+// with the data as the second operand keeps that layout, one with the data as the first operand
+// transposes it, which turns the row DFT's output into the column DFT's input without a trip
+// through LDS.  Along kx a lane holds two adjacent columns, 2 c and 2 c + 1 of a 32-column group
+// kp, in two tiles (parity par): every workspace row access moves whole 128-byte lines.  Where a
+// transform produces or contracts that interleaved kx order it uses the interleaved blocks.
+// Each wave works on its own slices or rows: no LDS and no barrier.
 // (The digit split of "FlashFFTConv" (abstract) and the "FlashConv" page's Mechanism, with the
 // whole 64-point DFT as one matrix: at this size the blocks are cheaper than a second split.)
 constexpr int M3_S = 32, M3_P = 64;
 constexpr int M3_ZW = 2;  // slices per wave (passes A and C)
-constexpr int M3_TZ = 8;  // (ky, kx block) rows per wave (pass Z)
+// (ky, 32-column group) rows per wave (pass Z): 4 gives 8 workgroups per unit, so workgroup ids
+// of the two units of a channel differ by a multiple of 8 and the dispatcher puts them on one
+// XCD, whose L2 then serves the channel's spectrum to both
+constexpr int M3_TZ = 4;
 
 template <int CT>
 __device__ __forceinline__ MatImg<CT> img_f(const void* img, int kb, int nb, int lane) {
@@ -208,6 +214,15 @@ __device__ __forceinline__ MatImg<CT> img_f(const void* img, int kb, int nb, int
 template <int CT>
 __device__ __forceinline__ MatImg<CT> img_i(const void* img, int mb, int kb, int lane) {
     return load_img<CT>(img, 16 + 4 * mb + kb, lane);
+}
+// interleaved: forward rows kx = 32 kp + 2 r + par (kq = 2 kp + par); inverse inputs likewise
+template <int CT>
+__device__ __forceinline__ MatImg<CT> img_fq(const void* img, int kq, int nb, int lane) {
+    return load_img<CT>(img, 32 + 4 * kq + nb, lane);
+}
+template <int CT>
+__device__ __forceinline__ MatImg<CT> img_iq(const void* img, int mb, int kq, int lane) {
+    return load_img<CT>(img, 48 + 4 * mb + kq, lane);
 }
 
 // Pass A: per input slice z, DFT over x then over y, into W[z][ky][kx].
@@ -218,10 +233,12 @@ __global__ void __launch_bounds__(256) k3m_slices_fwd(const Conv3DArgs a) {
     const int64_t ul = blockIdx.y, unit = a.unit0 + ul;
     int64_t ch, row0, row1;
     unit_rows(a, unit, (int64_t)S * S * S, ch, row0, row1);
-    MatImg<CT> F[4][2];  // forward blocks (k block, n block < 2)
+    MatImg<CT> Fq[4][2], F[4][2];  // x: interleaved kx rows (kq), inputs x < S; y: rows ky, inputs y < S
     static_for<0, 4>([&](auto kk) LCV_INLINE {
         static_for<0, 2>([&](auto nn) LCV_INLINE {
-            F[decltype(kk)::value][decltype(nn)::value] = img_f<CT>(a.img, decltype(kk)::value, decltype(nn)::value, lane);
+            constexpr int k = decltype(kk)::value, n = decltype(nn)::value;
+            Fq[k][n] = img_fq<CT>(a.img, k, n, lane);
+            F[k][n] = img_f<CT>(a.img, k, n, lane);
         });
     });
     const uint16_t* const ua = (const uint16_t*)a.u + row0;
@@ -243,33 +260,40 @@ __global__ void __launch_bounds__(256) k3m_slices_fwd(const Conv3DArgs a) {
                 d[xb][yb].w[3] = __byte_perm(pa.y, pb.y, 0x7632);
             });
         });
-        // DFT over x, transposed: x1(yb, kb) holds rows y, column kx
+        // DFT over x, transposed: x1(yb, kq) holds rows y, column kx = 32 kp + 2 c + par
         Operand<CT> x1[2][4];
         static_for<0, 2>([&](auto yy) LCV_INLINE {
             static_for<0, 4>([&](auto kk) LCV_INLINE {
-                constexpr int yb = decltype(yy)::value, kb = decltype(kk)::value;
+                constexpr int yb = decltype(yy)::value, kq = decltype(kk)::value;
                 f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
-                stage_swap_acc<CT>(F[kb][0], d[0][yb], re, im);
-                stage_swap_acc<CT>(F[kb][1], d[1][yb], re, im);
-                x1[yb][kb] = to_operand<CT>(tile_from_acc(re, im));
+                stage_swap_acc<CT>(Fq[kq][0], d[0][yb], re, im);
+                stage_swap_acc<CT>(Fq[kq][1], d[1][yb], re, im);
+                x1[yb][kq] = to_operand<CT>(tile_from_acc(re, im));
             });
         });
-        // DFT over y: rows ky, column kx; stored as W[z][ky][kx]
+        // DFT over y: rows ky, columns 2 c, 2 c + 1 of group kp; stored as W[z][ky][kx]
         uint32_t* const wz = (uint32_t*)a.ws + (ul * S + z) * P * P;
-        static_for<0, 4>([&](auto kk) LCV_INLINE {
+        static_for<0, 2>([&](auto pp) LCV_INLINE {
             static_for<0, 4>([&](auto yy) LCV_INLINE {
-                constexpr int kb = decltype(kk)::value, kyb = decltype(yy)::value;
-                f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
-                stage_keep_acc<CT>(F[kyb][0], x1[0][kb], re, im);
-                stage_keep_acc<CT>(F[kyb][1], x1[1][kb], re, im);
+                constexpr int kp = decltype(pp)::value, kyb = decltype(yy)::value;
+                f32x4 re[2], im[2];
+                static_for<0, 2>([&](auto qq) LCV_INLINE {
+                    constexpr int par = decltype(qq)::value;
+                    re[par] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    im[par] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    stage_keep_acc<CT>(F[kyb][0], x1[0][2 * kp + par], re[par], im[par]);
+                    stage_keep_acc<CT>(F[kyb][1], x1[1][2 * kp + par], re[par], im[par]);
+                });
 #pragma unroll
-                for (int j = 0; j < 4; ++j) wz[(16 * kyb + 4 * g + j) * P + 16 * kb + c] = pack2<CT>(re[j], im[j]);
+                for (int j = 0; j < 4; ++j)
+                    *(uint2*)(wz + (16 * kyb + 4 * g + j) * P + 32 * kp + 2 * c) =
+                        make_uint2(pack2<CT>(re[0][j], im[0][j]), pack2<CT>(re[1][j], im[1][j]));
             });
         });
     }
 }
 
-// Pass Z: per row (ky, kx block of 16), DFT over z, product with (K + D (-i)^(kx+ky+kz)) / P^3,
+// Pass Z: per row (ky, 32-column group kp), DFT over z, product with (K + D (-i)^(kx+ky+kz)) / P^3,
 // inverse DFT for the window slices, written back to W[zo][ky][kx] (the row's own elements).
 template <int CT>
 __global__ void __launch_bounds__(256) k3m_zpass(const Conv3DArgs a) {
@@ -289,57 +313,68 @@ __global__ void __launch_bounds__(256) k3m_zpass(const Conv3DArgs a) {
     });
     const float dsk = raw1_to_f32<CT>(load1_raw<CT>(a.D, ch)) * a.inv_p3;
     constexpr uint32_t P2 = P * P;
-    // scalar bases per row, 32-bit lane offsets (slice 4 g + j, column c) fixed for the wave
+    // scalar bases per row, 32-bit lane offsets (slice 4 g + j, columns 2 c, 2 c + 1) fixed for
+    // the wave
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const uint32_t lo = (uint32_t)(4 * g) * P2 + (uint32_t)c;
+    const uint32_t lo = (uint32_t)(4 * g) * P2 + 2 * (uint32_t)c;
     uint32_t* const wsu = (uint32_t*)a.ws + ul * S * P2;
     const uint32_t* const kfc = (const uint32_t*)a.kf + ch * P * P2;
 #pragma unroll 1
     for (int ti = 0; ti < M3_TZ; ++ti) {
-        const int task = (blockIdx.x * 4 + wv) * M3_TZ + ti;  // < 256, wave-uniform
-        const int ky = task >> 2, kb = task & 3, kx0 = 16 * kb;
+        const int task = (blockIdx.x * 4 + wv) * M3_TZ + ti;  // < 128, wave-uniform
+        const int ky = task >> 1, kx0 = 32 * (task & 1);
         uint32_t* const wr = wsu + ky * P + kx0;          // + z P^2 + lane offset
         const uint32_t* const kr = kfc + ky * P + kx0;    // + kz P^2 + lane offset
-        Operand<CT> w[2];
+        Operand<CT> w[2][2];   // [par][z block]
         static_for<0, 2>([&](auto zz) LCV_INLINE {
             constexpr int zb = decltype(zz)::value;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) w[zb].w[j] = wr[lo + (uint32_t)(16 * zb + j) * P2];
-        });
-        uint32_t kw[4][4];
-        static_for<0, 4>([&](auto kk) LCV_INLINE {
-            constexpr int kzb = decltype(kk)::value;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) kw[kzb][j] = kr[lo + (uint32_t)(16 * kzb + j) * P2];
-        });
-        const int kx = kx0 + c;
-        Operand<CT> zp[4];
-        static_for<0, 4>([&](auto kk) LCV_INLINE {
-            constexpr int kzb = decltype(kk)::value;
-            f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
-            stage_keep_acc<CT>(F[kzb][0], w[0], re, im);
-            stage_keep_acc<CT>(F[kzb][1], w[1], re, im);
-#pragma unroll
             for (int j = 0; j < 4; ++j) {
-                // the skip: a delta at the kernel centre, spectrum (-i)^(kx + ky + kz)
-                const int ph = (kx + ky + 16 * kzb + 4 * g + j) & 3;
-                const float kre = unpack_lo<CT>(kw[kzb][j]) + (ph == 0 ? dsk : ph == 2 ? -dsk : 0.f);
-                const float kim = unpack_hi<CT>(kw[kzb][j]) + (ph == 1 ? -dsk : ph == 3 ? dsk : 0.f);
-                float xr = re[j], xi = im[j];
-                cmul(xr, xi, kre, kim);
-                re[j] = xr;
-                im[j] = xi;
+                const uint2 t = *(const uint2*)(wr + lo + (uint32_t)(16 * zb + j) * P2);
+                w[0][zb].w[j] = t.x;
+                w[1][zb].w[j] = t.y;
             }
-            zp[kzb] = to_operand<CT>(tile_from_acc(re, im));
+        });
+        uint2 kw[4][4];
+        static_for<0, 4>([&](auto kk) LCV_INLINE {
+            constexpr int kzb = decltype(kk)::value;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) kw[kzb][j] = *(const uint2*)(kr + lo + (uint32_t)(16 * kzb + j) * P2);
+        });
+        f32x4 yr[2][2], yi[2][2];  // [par][window block]
+        static_for<0, 2>([&](auto qq) LCV_INLINE {
+            constexpr int par = decltype(qq)::value;
+            const int kx = kx0 + 2 * c + par;
+            yr[par][0] = yr[par][1] = yi[par][0] = yi[par][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // per kz block: forward, product, and its share of both window blocks of the inverse
+            static_for<0, 4>([&](auto kk) LCV_INLINE {
+                constexpr int kzb = decltype(kk)::value;
+                f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
+                stage_keep_acc<CT>(F[kzb][0], w[par][0], re, im);
+                stage_keep_acc<CT>(F[kzb][1], w[par][1], re, im);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    // the skip: a delta at the kernel centre, spectrum (-i)^(kx + ky + kz)
+                    const int ph = (kx + ky + 16 * kzb + 4 * g + j) & 3;
+                    const uint32_t kv = par ? kw[kzb][j].y : kw[kzb][j].x;
+                    const float kre = unpack_lo<CT>(kv) + (ph == 0 ? dsk : ph == 2 ? -dsk : 0.f);
+                    const float kim = unpack_hi<CT>(kv) + (ph == 1 ? -dsk : ph == 3 ? dsk : 0.f);
+                    float xr = re[j], xi = im[j];
+                    cmul(xr, xi, kre, kim);
+                    re[j] = xr;
+                    im[j] = xi;
+                }
+                const Operand<CT> zp = to_operand<CT>(tile_from_acc(re, im));
+                stage_keep_acc<CT>(Fi[0][kzb], zp, yr[par][0], yi[par][0]);
+                stage_keep_acc<CT>(Fi[1][kzb], zp, yr[par][1], yi[par][1]);
+            });
         });
         static_for<0, 2>([&](auto mm) LCV_INLINE {
             constexpr int mb = decltype(mm)::value;
-            f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
-            static_for<0, 4>([&](auto kk) LCV_INLINE {
-                stage_keep_acc<CT>(Fi[mb][decltype(kk)::value], zp[decltype(kk)::value], re, im);
-            });
 #pragma unroll
-            for (int j = 0; j < 4; ++j) wr[lo + (uint32_t)(16 * mb + j) * P2] = pack2<CT>(re[j], im[j]);  // zo
+            for (int j = 0; j < 4; ++j)  // slice zo = 16 mb + 4 g + j
+                *(uint2*)(wr + lo + (uint32_t)(16 * mb + j) * P2) =
+                    make_uint2(pack2<CT>(yr[0][mb][j], yi[0][mb][j]), pack2<CT>(yr[1][mb][j], yi[1][mb][j]));
         });
     }
 }
@@ -353,10 +388,12 @@ __global__ void __launch_bounds__(256) k3m_slices_inv(const Conv3DArgs a) {
     const int64_t ul = blockIdx.y, unit = a.unit0 + ul;
     int64_t ch, row0, row1;
     unit_rows(a, unit, (int64_t)S * S * S, ch, row0, row1);
-    MatImg<CT> Fi[2][4];  // inverse blocks (window block, k block)
+    MatImg<CT> Fi[2][4], Fiq[2][4];  // inverse (window block, k block); the same over interleaved kx
     static_for<0, 2>([&](auto mm) LCV_INLINE {
         static_for<0, 4>([&](auto kk) LCV_INLINE {
-            Fi[decltype(mm)::value][decltype(kk)::value] = img_i<CT>(a.img, 1 + decltype(mm)::value, decltype(kk)::value, lane);
+            constexpr int m = decltype(mm)::value, k = decltype(kk)::value;
+            Fi[m][k] = img_i<CT>(a.img, 1 + m, k, lane);
+            Fiq[m][k] = img_iq<CT>(a.img, 1 + m, k, lane);
         });
     });
     uint16_t* const ya = (uint16_t*)a.y + row0;
@@ -365,33 +402,41 @@ __global__ void __launch_bounds__(256) k3m_slices_inv(const Conv3DArgs a) {
     for (int zi = 0; zi < M3_ZW; ++zi) {
         const int zo = (blockIdx.x * 4 + wave) * M3_ZW + zi;
         const uint32_t* const wz = (const uint32_t*)a.ws + (ul * S + zo) * P * P;
-        // inverse DFT over ky, transposed: y1(kxb, myb) holds rows kx, column my (window)
+        // inverse DFT over ky, transposed: y1(kq, myb) holds rows kx = 32 kp + 2 (4 g + j) + par,
+        // column my (window)
         Operand<CT> y1[4][2];
-        static_for<0, 4>([&](auto xx) LCV_INLINE {
-            constexpr int kxb = decltype(xx)::value;
-            Operand<CT> w[4];  // rows ky = 16 kyb + 4 g + j, column kx = 16 kxb + c
+        static_for<0, 2>([&](auto pp) LCV_INLINE {
+            constexpr int kp = decltype(pp)::value;
+            Operand<CT> w[2][4];  // [par][ky block]: rows ky = 16 kyb + 4 g + j, column 32 kp + 2 c + par
             static_for<0, 4>([&](auto yy) LCV_INLINE {
                 constexpr int kyb = decltype(yy)::value;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) w[kyb].w[j] = wz[(16 * kyb + 4 * g + j) * P + 16 * kxb + c];
+                for (int j = 0; j < 4; ++j) {
+                    const uint2 t = *(const uint2*)(wz + (16 * kyb + 4 * g + j) * P + 32 * kp + 2 * c);
+                    w[0][kyb].w[j] = t.x;
+                    w[1][kyb].w[j] = t.y;
+                }
             });
-            static_for<0, 2>([&](auto mm) LCV_INLINE {
-                constexpr int myb = decltype(mm)::value;
-                f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
-                static_for<0, 4>([&](auto yy) LCV_INLINE {
-                    stage_swap_acc<CT>(Fi[myb][decltype(yy)::value], w[decltype(yy)::value], re, im);
+            static_for<0, 2>([&](auto qq) LCV_INLINE {
+                static_for<0, 2>([&](auto mm) LCV_INLINE {
+                    constexpr int par = decltype(qq)::value, myb = decltype(mm)::value;
+                    f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
+                    static_for<0, 4>([&](auto yy) LCV_INLINE {
+                        stage_swap_acc<CT>(Fi[myb][decltype(yy)::value], w[par][decltype(yy)::value], re, im);
+                    });
+                    y1[2 * kp + par][myb] = to_operand<CT>(tile_from_acc(re, im));
                 });
-                y1[kxb][myb] = to_operand<CT>(tile_from_acc(re, im));
             });
         });
-        // inverse DFT over kx: rows mx (window), column my; image A is the real part, B the
-        // imaginary part: lane (g, c) stores x = 16 mxb + 4 g .. + 3 of row y = 16 myb + c
+        // inverse DFT over kx (interleaved blocks): rows mx (window), column my; image A is the
+        // real part, B the imaginary part: lane (g, c) stores x = 16 mxb + 4 g .. + 3 of row
+        // y = 16 myb + c
         static_for<0, 2>([&](auto xx) LCV_INLINE {
             static_for<0, 2>([&](auto mm) LCV_INLINE {
                 constexpr int mxb = decltype(xx)::value, myb = decltype(mm)::value;
                 f32x4 re = {0.f, 0.f, 0.f, 0.f}, im = {0.f, 0.f, 0.f, 0.f};
                 static_for<0, 4>([&](auto kk) LCV_INLINE {
-                    stage_keep_acc<CT>(Fi[mxb][decltype(kk)::value], y1[decltype(kk)::value][myb], re, im);
+                    stage_keep_acc<CT>(Fiq[mxb][decltype(kk)::value], y1[decltype(kk)::value][myb], re, im);
                 });
                 const int64_t off = ((int64_t)zo * S + 16 * myb + c) * S + 16 * mxb + 4 * g;
                 *(uint2*)(ya + off) = make_uint2(pack2<CT>(re[0], re[1]), pack2<CT>(re[2], re[3]));
@@ -408,7 +453,7 @@ static hipError_t launch3_t(const Conv3DArgs& a, hipStream_t st) {
     if constexpr (S == M3_S && CT != CT_F32) {
         if (!a.filter && a.img) {
             hipLaunchKernelGGL((k3m_slices_fwd<CT>), dim3(S / (4 * M3_ZW), (unsigned)a.nunit), blk, 0, st, a);
-            hipLaunchKernelGGL((k3m_zpass<CT>), dim3(M3_P * 4 / (4 * M3_TZ), (unsigned)a.nunit), blk, 0, st, a);
+            hipLaunchKernelGGL((k3m_zpass<CT>), dim3(M3_P * 2 / (4 * M3_TZ), (unsigned)a.nunit), blk, 0, st, a);
             hipLaunchKernelGGL((k3m_slices_inv<CT>), dim3(S / (4 * M3_ZW), (unsigned)a.nunit), blk, 0, st, a);
             return hipGetLastError();
         }

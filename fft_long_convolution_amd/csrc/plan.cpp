@@ -210,6 +210,17 @@ std::vector<uint8_t> build_dense_dft_tables(int P, int ct) {
     for (int mb = 0; mb < NB; ++mb)
         for (int kb = 0; kb < NB; ++kb)
             append_image(t, ct, [&](int r, int c) { return omega(-(int64_t)(16 * mb + r) * (16 * kb + c), P); });
+    // interleaved blocks (NB even): 32-row groups kp split by parity, k = 32 kp + 2 r + par
+    for (int kq = 0; kq < NB; ++kq)  // kq = 2 kp + par: forward, output rows interleaved
+        for (int nb = 0; nb < NB; ++nb)
+            append_image(t, ct, [&](int r, int c) {
+                return omega((int64_t)(32 * (kq / 2) + 2 * r + kq % 2) * (16 * nb + c), P);
+            });
+    for (int mb = 0; mb < NB; ++mb)  // inverse, input columns interleaved
+        for (int kq = 0; kq < NB; ++kq)
+            append_image(t, ct, [&](int r, int c) {
+                return omega(-(int64_t)(16 * mb + r) * (32 * (kq / 2) + 2 * c + kq % 2), P);
+            });
     return t;
 }
 
@@ -316,7 +327,7 @@ const float* dft_table(int64_t P, hipError_t* err) {
 }
 
 const void* dense_dft_tables(int64_t P, int ct, hipError_t* err) {
-    if (P < 16 || P > 64 || P % 16 != 0 || ct == CT_F32) { *err = hipErrorInvalidValue; return nullptr; }
+    if ((P != 32 && P != 64) || ct == CT_F32) { *err = hipErrorInvalidValue; return nullptr; }
     return get_or_build(4, ct, P, 0, build_any, err);
 }
 

@@ -82,7 +82,9 @@ const float* dft_table(int64_t P, hipError_t* err);
 
 // The dense P-point DFT (P = 16 NB, NB <= 4) as 16 x 16 matrix-core images, 16-bit compute types:
 // forward block (kb, nb) = w_P^{k n} for k = 16 kb + row, n = 16 nb + column, at kb NB + nb;
-// inverse block (mb, kb) = w_P^{-m k}, at NB^2 + mb NB + kb.
+// inverse block (mb, kb) = w_P^{-m k}, at NB^2 + mb NB + kb.  Interleaved blocks, kq = 2 kp + par
+// naming the frequencies k = 32 kp + 2 i + par (i < 16): forward rows k, inputs n = 16 nb + c, at
+// 2 NB^2 + kq NB + nb; inverse rows m = 16 mb + r, inputs k, at 3 NB^2 + mb NB + kq.
 const void* dense_dft_tables(int64_t P, int ct, hipError_t* err);
 
 // Cached device properties of the current device.
