@@ -22,6 +22,11 @@ static hipError_t launch_misc(int dtype, int mode, const Fused1DArgs& a, int cus
             if (dtype == CT_F16) return launch_t<32, CT_F32, CT_F16, MODE_ROWFWD, false, false>(a, cus, st);
             return launch_t<32, CT_F32, CT_BF16, MODE_ROWFWD, false, false>(a, cus, st);
         }
+        if (mode == MODE_ROWFWD16) {
+            if (dtype == CT_F16) return launch_t<32, CT_F16, CT_F16, MODE_ROWFWD, false, false>(a, cus, st);
+            if (dtype == CT_BF16) return launch_t<32, CT_BF16, CT_BF16, MODE_ROWFWD, false, false>(a, cus, st);
+            return hipErrorInvalidValue;
+        }
     }
     return hipErrorInvalidValue;
 }

@@ -612,6 +612,10 @@ __global__ void __launch_bounds__(512) fused1d_kernel(const Fused1DArgs a) {
                         int64_t base;
                         if constexpr (MODE == MODE_FILTER) {
                             base = item * M;
+                        } else if (a.wrows) {  // wrows rows per sequence (rows past them not formed)
+                            const uint32_t sl = (uint32_t)item / (uint32_t)a.wrows;
+                            const int64_t khi = (int64_t)((uint32_t)item - sl * (uint32_t)a.wrows);
+                            base = (a.seq0 + sl) * a.M + khi * M;
                         } else {
                             const int64_t h = a.seq0 + (item >> m1s), khi = item & (a.M1 - 1);
                             base = h * a.M + khi * M;

@@ -12,8 +12,10 @@ namespace lcv {
 // filter of at most M/2 taps on a sequence of any length, one block of M/2 outputs per item.
 // SPARSE is CONV with the filter spectrum kept only on the frequency blocks set in `keep`.
 // SAVE is CONV that also stores the pre-gate output c (the value v multiplies) to y2.
+// ROWFWD16 is ROWFWD computed in the 16-bit io type (the spectra of the rows' own inputs in the
+// long-sequence filter gradient), not in fp32.
 enum Mode1D { MODE_CONV = 0, MODE_FILTER = 1, MODE_ROW = 2, MODE_ROWFWD = 3, MODE_ADJ = 4, MODE_PART = 5,
-              MODE_SPARSE = 6, MODE_SAVE = 7, MODE_LBF = 8 };
+              MODE_SPARSE = 6, MODE_SAVE = 7, MODE_LBF = 8, MODE_ROWFWD16 = 9 };
 
 struct Fused1DArgs {
     const void* u;       // CONV: u [B][H][N]; FILTER: k [H][N]; ROW/ROWFWD: workspace rows;

@@ -683,6 +683,52 @@ bool bwd_long_layout(int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype, BwdLo
     return true;
 }
 
+// Spectra of the rows x = q (.) u (u alone without q), each the filter of a channel of its own,
+// for the filter gradient of long one-row sequences: in the 16-bit compute type, through the
+// forward column pass on the matrix cores (two rows per workgroup, gated there) and the row
+// transform, and only the rows k_hi <= M1/2 that the half-row row pass of a one-row-per-sequence
+// call reads (the others are left unwritten).  false: not this path (fp32, or a plan without
+// half rows); the caller then takes lconv_filter_fft.
+bool row_spectra16(const void* u, const void* q, void* kf, int64_t rows, int64_t N, lconv_dtype_t dtype,
+                   void* workspace, hipStream_t stream, lconv_status_t* st) {
+    if (dtype == LCONV_F32) return false;
+    Plan1D p;
+    make_plan_1d(N, &p);
+    if (!p.multipass || !colmx_supported(p.M1) || p.M1 < 256) return false;
+    *st = LCONV_ERR_HIP;
+    hipError_t err = hipSuccess;
+    const int cus = device_cu_count(&err);
+    if (!cus) return true;
+    const int ct = (int)dtype;
+    const void* tabs = fused_tables(32, ct, &err);
+    const void* cimg = colmx_tables(p.M1, ct, &err);
+    ColTables ctab;
+    if (!tabs || !cimg || !col_tables(p.M, p.M1, &ctab, &err)) return true;
+    // the chunks of a one-row-per-sequence forward call over these rows (its workspace size)
+    const size_t csz = work_complex_size(dtype, false);
+    const int64_t wr = p.M1 / 2 + 1;
+    const int64_t full_per = chunk_seqs(rows, p.M, csz, kChunkTarget1D);
+    const int64_t per = chunk_seqs(rows, wr * kRowLen, csz, (size_t)full_per * p.M * csz);
+    const int64_t nch = (rows + per - 1) / per;
+    for (int64_t ci = 0; ci < nch; ++ci) {
+        const int64_t s0 = rows / nch * ci + (ci < rows % nch ? ci : rows % nch);
+        const int64_t ns = rows / nch + (ci < rows % nch ? 1 : 0);
+        ColArgs c{};
+        c.u = u; c.q = q; c.ws = workspace;
+        c.tw_lo = ctab.lo; c.tw_hi = ctab.hi; c.tw_col = ctab.col;
+        c.B = 1; c.H = rows; c.N = N; c.M = p.M; c.M1 = p.M1; c.seq0 = s0; c.nseq = ns;
+        c.seq_per_h = 1; c.filter = 0; c.img = cimg; c.rows = wr;
+        if (launch_col_fwd(dtype, c, stream) != hipSuccess) return true;
+        Fused1DArgs a{};
+        a.u = workspace; a.y = kf; a.tables = tabs;
+        a.nitems = ns * wr; a.inv_m = 1.0f / (float)p.M; a.M = p.M; a.M1 = p.M1; a.wrows = wr;
+        a.seq0 = s0; a.seq_per_h = 1;
+        if (launch_fused1d(32, dtype, MODE_ROWFWD16, false, false, a, cus, stream) != hipSuccess) return true;
+    }
+    *st = LCONV_SUCCESS;
+    return true;
+}
+
 // The gradient of a long sequence through the multi-pass forward call.  Reversing a row turns a
 // correlation over later positions into a causal convolution:
 //   dx = rev(k * rev(ds)) + D ds            (ds = dy (.) v);  du = q (.) dx, dq = u (.) dx
@@ -716,12 +762,14 @@ lconv_status_t bwd_long(const void* dy, const void* u, const void* k_f, const vo
     // dk, dD: each row's x as a filter of its own (B*H channels of one row each), applied to
     // rev(ds) with a zero skip, then reversed and summed over the batch
     if (dk || dD) {
-        const void* x = u;
-        if (q) {
-            if (launch_mul_rows(q, u, xs, elems, ct, stream) != hipSuccess) return LCONV_ERR_HIP;
-            x = xs;
+        if (!row_spectra16(u, q, kf, rows, N, dtype, fws, stream, &st)) {
+            const void* x = u;
+            if (q) {
+                if (launch_mul_rows(q, u, xs, elems, ct, stream) != hipSuccess) return LCONV_ERR_HIP;
+                x = xs;
+            }
+            st = lconv_filter_fft(x, kf, rows, N, dtype, kfws, L.kfws, stream);
         }
-        st = lconv_filter_fft(x, kf, rows, N, dtype, kfws, L.kfws, stream);
         if (st != LCONV_SUCCESS) return st;
         if (launch_zero_words(zd, (int64_t)(L.zd / 4), stream) != hipSuccess) return LCONV_ERR_HIP;
         st = fftconv_fwd_call(ds, kf, zd, t, nullptr, nullptr, 1, rows, N, dtype, fws, L.fws, kChunkTarget1D, true,

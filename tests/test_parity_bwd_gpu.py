@@ -241,6 +241,20 @@ def test_bwd_very_long_sampled(lc, nthreads):
         assert e <= TOL["bf16"], (k, e)
 
 
+@pytest.mark.parametrize("B,H,N,dtype,gates", [(2, 2, 1100000, "bf16", "qv"), (3, 1, 600000, "f16", "q")])
+def test_bwd_long_row_spectra_sampled(lc, nthreads, B, H, N, dtype, gates):
+    """Column lengths M1 = 512 and 256 with batch rows and gates: the filter gradient takes the
+    spectra of x = q (.) u in the 16-bit compute type, gated inside the forward column pass, for the
+    half rows only (B = 2 pairs rows of one channel; B = 3 ends on a lone row)."""
+    spec = wl.spec_1d(B, H, N, dtype, gated=True, seed=7200 + B, decay=1e-5)
+    say(f"[bwd long spectra] dtype={dtype} B={B} H={H} N={N} gates={gates!r} seed={spec.seed}")
+    d, dy, q, v = inputs(spec, gates)
+    errs = _sampled_bwd(lc, nthreads, d, dy, q, v, n_pts=256, n_dk=96, seed=4)
+    say("   " + " ".join(f"{k}={e:.3e}" for k, e in errs.items()) + f" (tol {TOL[dtype]})")
+    for k, e in errs.items():
+        assert e <= TOL[dtype], (k, e)
+
+
 def test_training_pair_long(lc, nthreads):
     """The training pair past one workgroup: fftconv_save's y equals the plain forward call's, c is
     the pre-gate output, and the saved-output gradient equals the plain gradient."""
