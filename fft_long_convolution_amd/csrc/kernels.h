@@ -161,6 +161,14 @@ hipError_t launch_rev_gate(const void* a, const void* b, void* out, int64_t rows
                            hipStream_t stream);
 hipError_t launch_rev_gated_out(const void* t, const void* g1, const void* g2, void* d1, void* d2, int64_t rows,
                                 int64_t N, int dtype, hipStream_t stream);
+// dD[h] and dk[h][0] as the direct fp32 sum over batch and time of (q u)(dy v) (gates optional),
+// through S = dot_slices(N) partial sums per channel in part [H][S] (fp32).
+inline int dot_slices(int64_t N) {
+    const int64_t s = N / 8 / 256;
+    return (int)(s < 1 ? 1 : (s > 64 ? 64 : s));
+}
+hipError_t launch_dot_lag0(const void* u, const void* q, const void* dy, const void* v, float* part, float* dk,
+                           float* dD, int64_t B, int64_t H, int64_t N, int dtype, hipStream_t stream);
 hipError_t launch_rev_batch_sum(const void* r, float* dk, float* dD, int64_t B, int64_t H, int64_t N, int dtype,
                                 hipStream_t stream);
 

@@ -656,8 +656,8 @@ namespace {
 // the forward results, x = q (.) u, the rows' spectra with their transform workspace, and the
 // zero skip of the row filters.
 struct BwdLongLayout {
-    size_t fws, ds, t, xs, kf, kfws, zd;
-    size_t o_ds, o_t, o_xs, o_kf, o_kfws, o_zd, total;
+    size_t fws, ds, t, xs, kf, kfws, zd, part;
+    size_t o_ds, o_t, o_xs, o_kf, o_kfws, o_zd, o_part, total;
 };
 
 bool bwd_long_layout(int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype, BwdLongLayout* L) {
@@ -673,28 +673,30 @@ bool bwd_long_layout(int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype, BwdLo
     L->kf = round256(kf);
     L->kfws = round256(lconv_filter_fft_workspace_bytes(rows, N, dtype));
     L->zd = round256((size_t)rows * es);
+    L->part = round256((size_t)H * dot_slices(N) * sizeof(float));
     L->o_ds = L->fws;
     L->o_t = L->o_ds + L->ds;
     L->o_xs = L->o_t + L->t;
     L->o_kf = L->o_xs + L->xs;
     L->o_kfws = L->o_kf + L->kf;
     L->o_zd = L->o_kfws + L->kfws;
-    L->total = L->o_zd + L->zd;
+    L->o_part = L->o_zd + L->zd;
+    L->total = L->o_part + L->part;
     return true;
 }
 
 // Spectra of the rows x = q (.) u (u alone without q), each the filter of a channel of its own,
-// for the filter gradient of long one-row sequences: in the 16-bit compute type, through the
-// forward column pass on the matrix cores (two rows per workgroup, gated there) and the row
-// transform, and only the rows k_hi <= M1/2 that the half-row row pass of a one-row-per-sequence
-// call reads (the others are left unwritten).  false: not this path (fp32, or a plan without
-// half rows); the caller then takes lconv_filter_fft.
+// for the filter gradient of long sequences: in the 16-bit compute type, through the forward
+// column pass on the matrix cores (gated there) and the row transform.  With M1 >= 256 (two rows
+// per workgroup) only the rows k_hi <= M1/2 are formed: the half-row row pass of the
+// one-row-per-sequence call that follows reads no others.  false: not this path (fp32, or column
+// lengths below 16); the caller then takes lconv_filter_fft.
 bool row_spectra16(const void* u, const void* q, void* kf, int64_t rows, int64_t N, lconv_dtype_t dtype,
                    void* workspace, hipStream_t stream, lconv_status_t* st) {
     if (dtype == LCONV_F32) return false;
     Plan1D p;
     make_plan_1d(N, &p);
-    if (!p.multipass || !colmx_supported(p.M1) || p.M1 < 256) return false;
+    if (!p.multipass || !colmx_supported(p.M1)) return false;
     *st = LCONV_ERR_HIP;
     hipError_t err = hipSuccess;
     const int cus = device_cu_count(&err);
@@ -706,9 +708,10 @@ bool row_spectra16(const void* u, const void* q, void* kf, int64_t rows, int64_t
     if (!tabs || !cimg || !col_tables(p.M, p.M1, &ctab, &err)) return true;
     // the chunks of a one-row-per-sequence forward call over these rows (its workspace size)
     const size_t csz = work_complex_size(dtype, false);
-    const int64_t wr = p.M1 / 2 + 1;
+    const bool half = p.M1 >= 256;
+    const int64_t wr = half ? p.M1 / 2 + 1 : p.M1;
     const int64_t full_per = chunk_seqs(rows, p.M, csz, kChunkTarget1D);
-    const int64_t per = chunk_seqs(rows, wr * kRowLen, csz, (size_t)full_per * p.M * csz);
+    const int64_t per = half ? chunk_seqs(rows, wr * kRowLen, csz, (size_t)full_per * p.M * csz) : full_per;
     const int64_t nch = (rows + per - 1) / per;
     for (int64_t ci = 0; ci < nch; ++ci) {
         const int64_t s0 = rows / nch * ci + (ci < rows % nch ? ci : rows % nch);
@@ -776,6 +779,10 @@ lconv_status_t bwd_long(const void* dy, const void* u, const void* k_f, const vo
                               stream);
         if (st != LCONV_SUCCESS) return st;
         if (launch_rev_batch_sum(t, dk, dD, B, H, N, ct, stream) != hipSuccess) return LCONV_ERR_HIP;
+        // lag 0 again, as the direct fp32 sum: the correlation's rows pass through memory in the
+        // dtype, and at lag 0 their batch sum can cancel
+        if (launch_dot_lag0(u, q, dy, v, (float*)(w + L.o_part), dk, dD, B, H, N, ct, stream) != hipSuccess)
+            return LCONV_ERR_HIP;
     }
     return LCONV_SUCCESS;
 }

@@ -122,6 +122,55 @@ __global__ void __launch_bounds__(256) rev_batch_sum_kernel(const void* rr, floa
     }
 }
 
+// The lag-0 filter gradient directly, in fp32: dD[h] = sum_b sum_t (q u)[b][h][t] (dy v)[b][h][t]
+// (absent gates are 1).  Part 1: workgroup (s, h) sums slice s of the S slices of channel h's rows.
+template <int IO>
+__global__ void __launch_bounds__(256) dot_part_kernel(const void* u, const void* q, const void* dy, const void* v,
+                                                       float* part, int64_t B, int64_t H, int64_t N, int S) {
+    const int64_t h = blockIdx.y, s = blockIdx.x, gpr = N / 8;
+    const int64_t g0 = gpr * s / S, g1 = gpr * (s + 1) / S;
+    float acc = 0.f;
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t base = (b * H + h) * N;
+        for (int64_t gi = g0 + threadIdx.x; gi < g1; gi += 256) {
+            float x[8], e[8], t[8];
+            ld8<IO>(u, base + 8 * gi, x);
+            ld8<IO>(dy, base + 8 * gi, e);
+            if (q) {
+                ld8<IO>(q, base + 8 * gi, t);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x[i] *= t[i];
+            }
+            if (v) {
+                ld8<IO>(v, base + 8 * gi, t);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) e[i] *= t[i];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc = fmaf(x[i], e[i], acc);
+        }
+    }
+    __shared__ float red[256];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) part[h * S + s] = red[0];
+}
+
+// Part 2: dD[h] = sum of the S partial sums (ascending s), also stored as dk[h][0].
+__global__ void __launch_bounds__(256) dot_final_kernel(const float* part, float* dk, float* dD, int64_t H,
+                                                        int64_t N, int S) {
+    for (int64_t h = (int64_t)blockIdx.x * 256 + threadIdx.x; h < H; h += (int64_t)gridDim.x * 256) {
+        float a = 0.f;
+        for (int s = 0; s < S; ++s) a += part[h * S + s];
+        if (dD) dD[h] = a;
+        if (dk) dk[h * N] = a;
+    }
+}
+
 __global__ void __launch_bounds__(256) zero_words_kernel(uint32_t* p, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
 }
@@ -166,6 +215,19 @@ hipError_t launch_rev_batch_sum(const void* r, float* dk, float* dD, int64_t B, 
     if (dtype == CT_F32) hipLaunchKernelGGL(rev_batch_sum_kernel<CT_F32>, grid, dim3(256), 0, st, r, dk, dD, B, H, N);
     else if (dtype == CT_F16) hipLaunchKernelGGL(rev_batch_sum_kernel<CT_F16>, grid, dim3(256), 0, st, r, dk, dD, B, H, N);
     else hipLaunchKernelGGL(rev_batch_sum_kernel<CT_BF16>, grid, dim3(256), 0, st, r, dk, dD, B, H, N);
+    return hipGetLastError();
+}
+
+hipError_t launch_dot_lag0(const void* u, const void* q, const void* dy, const void* v, float* part, float* dk,
+                           float* dD, int64_t B, int64_t H, int64_t N, int dtype, hipStream_t st) {
+    if (H <= 0 || N <= 0 || (!dk && !dD)) return hipSuccess;
+    if (N % 8 != 0 || H > 65535) return hipErrorInvalidValue;
+    const int S = dot_slices(N);
+    const dim3 grid((unsigned)S, (unsigned)H);
+    if (dtype == CT_F32) hipLaunchKernelGGL(dot_part_kernel<CT_F32>, grid, dim3(256), 0, st, u, q, dy, v, part, B, H, N, S);
+    else if (dtype == CT_F16) hipLaunchKernelGGL(dot_part_kernel<CT_F16>, grid, dim3(256), 0, st, u, q, dy, v, part, B, H, N, S);
+    else hipLaunchKernelGGL(dot_part_kernel<CT_BF16>, grid, dim3(256), 0, st, u, q, dy, v, part, B, H, N, S);
+    hipLaunchKernelGGL(dot_final_kernel, dim3(grid_groups(H)), dim3(256), 0, st, part, dk, dD, H, N, S);
     return hipGetLastError();
 }
 
