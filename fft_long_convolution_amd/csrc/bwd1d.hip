@@ -27,6 +27,18 @@
 
 namespace lcv {
 
+// c + lo(a) lo(b) + hi(a) hi(b) for two packed 16-bit pairs, accumulated in fp32
+template <int CT>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    static_assert(CT != CT_F32, "packed 16-bit pairs");
+    if constexpr (CT == CT_BF16) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+    } else {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+    }
+}
+
+
 template <int R, int CT, int IO, bool GQ, bool GV>
 __global__ void __launch_bounds__(512) dk1d_kernel(const Fused1DArgs a) {
     constexpr int P = 32 / R;                  // channels per workgroup iteration
@@ -59,6 +71,7 @@ __global__ void __launch_bounds__(512) dk1d_kernel(const Fused1DArgs a) {
     constexpr int IOW = IO == CT_F32 ? 2 : 1;  // uint4 per 8 io elements
 
     __shared__ __attribute__((aligned(16))) uint32_t lds[V_W + XY_W + O_W + IMGS_W];
+    __shared__ float red[16];   // lag-0 partial sums, one per 32-lane half of a wave
     uint32_t* V = lds;
     uint32_t* XY = lds + V_W;
     float* O = (float*)(lds + V_W + XY_W);
@@ -144,6 +157,10 @@ __global__ void __launch_bounds__(512) dk1d_kernel(const Fused1DArgs a) {
     };
 
     // P0: gate and pack the slot (pair z = row 2j + i row 2j+1) into V
+    // 16-bit types: dD and dk[h][0] from the direct lag-0 sum (fp32 keeps the spectral one, whose
+    // rounding is far below its tolerance)
+    constexpr bool LAG0 = CT != CT_F32;
+    float dsum = 0.f;  // this lane's share of the lag-0 sum of its channel group
     auto P0 = [&](auto which, int64_t it0, int64_t j) LCV_INLINE {
         constexpr bool GATE = decltype(which)::value ? GV : GQ;
         int64_t o0, o1;
@@ -167,6 +184,15 @@ __global__ void __launch_bounds__(512) dk1d_kernel(const Fused1DArgs a) {
             xi[i] = ok1 ? xi[i] : 0.f;
         }
         uint32_t* dst = V + ((p_io * NH + (n0_io >> 8)) * SV + (n0_io & 255)) * EW;
+        if constexpr (decltype(which)::value && LAG0) {
+            // the slot still holds this pair's x (the x pass wrote it; nothing since): lag 0
+            // directly, sum of x ds over the slot, as packed (re, im) pairs of x and of ds (one
+            // two-term dot product per element pair, accumulated in fp32)
+            const uint4 w0 = ((const uint4*)dst)[0], w1 = ((const uint4*)dst)[1];
+            const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dsum = dot2<CT>(w[i], pack2<CT>(xr[i], xi[i]), dsum);
+        }
         if constexpr (CT == CT_F32) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -242,6 +268,7 @@ __global__ void __launch_bounds__(512) dk1d_kernel(const Fused1DArgs a) {
     using DS_ = std::integral_constant<bool, true>;
     issue(X_{}, first, 0);
     for (int64_t it0 = first; it0 < last; it0 += P) {
+        dsum = 0.f;
         Tile acc[4], zx[4];
         static_for<0, 4>([&](auto ii) LCV_INLINE {
             constexpr int i = decltype(ii)::value;
@@ -340,8 +367,32 @@ __global__ void __launch_bounds__(512) dk1d_kernel(const Fused1DArgs a) {
                     dst[0] = make_float4(d[0], d[1], d[2], d[3]);
                     dst[1] = make_float4(d[4], d[5], d[6], d[7]);
                 }
-                if (want_dd && n0_io == 0) ((float*)a.y2)[h] = d[0];
+                if (!LAG0 && want_dd && n0_io == 0) ((float*)a.y2)[h] = d[0];
             }
+        }
+        // ---- lag 0 again, as the direct sum of x ds over the channel's rows (fp32; x as the
+        // transform input held it): the spectral sum's rounding can cancel there.  Summed per
+        // channel over the lanes in a fixed order; dk[h][0] (stored above) is overwritten after
+        // the barrier.
+        if constexpr (LAG0) {
+            // each 32-lane half of a wave holds slots of one channel: sum the half (fixed
+            // shuffle order), then per channel the halves in order
+            float v = dsum;
+#pragma unroll
+            for (int off = 1; off < 32; off <<= 1) v += __shfl_xor(v, off, 64);
+            if ((lane & 31) == 0) red[2 * wave + (lane >> 5)] = v;
+            __syncthreads();
+            if (tid < P && it0 + tid < last) {
+                const int64_t h = it0 + tid;
+                float sum = 0.f;
+                for (int e = 0; e < 16; ++e) {
+                    const int bl = (e >> 1) * BPW + ((32 * (e & 1)) >> 1) % BPW;  // the half's first slot (slot())
+                    if ((bl >> 4) == tid) sum += red[e];
+                }
+                if (want_dk) ((float*)a.y)[h * a.N] = sum;
+                if (want_dd) ((float*)a.y2)[h] = sum;
+            }
+            __syncthreads();
         }
     }
 }
