@@ -10,6 +10,7 @@ from .oracle import (  # noqa: F401
     ssm_kernel, ssm_rows,
     conv1d_bwd_rows, conv1d_bwd_dk, conv1d_bwd_points, conv1d_bwd_dk_points,
     conv1d_short_points, conv1d_circ_rows, sparse_filter,
+    conv1d_short_bwd_rows, conv1d_short_bwd_points, conv1d_short_bwd_dk, conv1d_short_bwd_dk_points,
     transform_length,
     conv1d_toeplitz, conv1d_python_int,
 )

@@ -296,6 +296,55 @@ def conv1d_bwd_dk_points(u, gy, pts, q=None, v=None, dt=None, nthreads=None):
     return dk
 
 
+def _short_as_full(k, N):
+    """A short filter k [H, L] (storage dtype) as the N-tap filter it acts as on length-N rows:
+    its first min(L, N) taps, then zeros (taps at lags >= N never meet an input)."""
+    k = np.asarray(k)
+    H, L = k.shape
+    kN = np.zeros((H, N), k.dtype)  # zero bits are 0.0 in every storage type
+    m = min(L, N)
+    kN[:, :m] = k[:, :m]
+    return kN
+
+
+def conv1d_short_bwd_rows(u, k, D, gy, rows, q=None, v=None, dt=None, nthreads=None):
+    """Gradient rows (du, dq, dv) of the convolution with a short filter k [H, L] (the partial
+    convolution of the FlashFFTConv abstract): the chain rule on the causal sum over the last L
+    inputs, i.e. conv1d_bwd_rows with k taken as the N-tap filter it acts as."""
+    N = np.asarray(u).shape[2]
+    return conv1d_bwd_rows(u, _short_as_full(k, N), D, gy, rows, q=q, v=v, dt=_dt_of(u, dt), nthreads=nthreads)
+
+
+def conv1d_short_bwd_points(u, k, D, gy, pts, q=None, v=None, dt=None, nthreads=None):
+    """conv1d_short_bwd_rows at single positions pts = [(b,h,t), ...]."""
+    N = np.asarray(u).shape[2]
+    return conv1d_bwd_points(u, _short_as_full(k, N), D, gy, pts, q=q, v=v, dt=_dt_of(u, dt), nthreads=nthreads)
+
+
+def conv1d_short_bwd_dk(u, gy, chans, L, q=None, v=None, dt=None, nthreads=None):
+    """Filter and skip gradients of the short-filter convolution: (dk [len(chans), L], dD).  The
+    filter enters only through its taps, so dk[h, tau] is the correlation of conv1d_bwd_dk at
+    lag tau < min(L, N); lags tau >= N have no pair of positions and are zero."""
+    N = np.asarray(u).shape[2]
+    dk, dD = conv1d_bwd_dk(u, gy, chans, q=q, v=v, dt=_dt_of(u, dt), nthreads=nthreads)
+    out = np.zeros((dk.shape[0], L), np.float64)
+    m = min(L, N)
+    out[:, :m] = dk[:, :m]
+    return out, dD
+
+
+def conv1d_short_bwd_dk_points(u, gy, pts, L, q=None, v=None, dt=None, nthreads=None):
+    """dk[h, tau] of conv1d_short_bwd_dk at pairs pts = [(h, tau), ...] with tau < L."""
+    N = np.asarray(u).shape[2]
+    pts = np.asarray(pts, np.int64).reshape(-1, 2)
+    assert np.all(pts[:, 1] < L)
+    out = np.zeros(pts.shape[0], np.float64)
+    inside = pts[:, 1] < N
+    if np.any(inside):
+        out[inside] = conv1d_bwd_dk_points(u, gy, pts[inside], q=q, v=v, dt=_dt_of(u, dt), nthreads=nthreads)
+    return out
+
+
 def conv2d_points(u, k, D, pts, dt=None, nthreads=None):
     """Direct 2D sums y[b,c,i,j] for pts = [(b,c,i,j), ...] (u [B,C,Hs,Ws], k [C,Hs,Ws], centre
     tap (Hs//2, Ws//2)); returns float64 [len(pts)]."""
