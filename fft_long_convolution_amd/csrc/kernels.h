@@ -175,6 +175,8 @@ hipError_t launch_rev_batch_sum(const void* r, float* dk, float* dD, int64_t B, 
 // Zero n 32-bit words (stage.hip): a kernel, so that callers under graph capture record no
 // memset node.
 hipError_t launch_zero_words(void* p, int64_t n, hipStream_t stream);
+// dst [rows][L] fp32 = the first min(N, L) entries of each src [rows][N] row, zeros after
+hipError_t launch_copy_cols(const float* src, float* dst, int64_t rows, int64_t N, int64_t L, hipStream_t stream);
 
 // Row staging for N not a multiple of 8 (stage.hip): [rows][N] <-> [rows][N8] with a zero tail.
 hipError_t launch_pad_rows(const void* src, void* dst, int64_t rows, int64_t N, int64_t N8, int esize,

@@ -732,6 +732,39 @@ bool row_spectra16(const void* u, const void* q, void* kf, int64_t rows, int64_t
     return true;
 }
 
+// dk, dD of a long sequence, from rev(ds) already in the workspace part L.o_ds: each row's
+// x = q (.) u as a filter of its own (B*H channels of one row each), applied to rev(ds) with a
+// zero skip, then reversed and summed over the batch; the part L.o_t is overwritten.
+lconv_status_t dk_long(const void* dy, const void* u, const void* q, const void* v, float* dk, float* dD,
+                       int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype, void* workspace,
+                       const BwdLongLayout& L, hipStream_t stream) {
+    char* w = (char*)workspace;
+    void *fws = w, *ds = w + L.o_ds, *t = w + L.o_t, *xs = w + L.o_xs, *kf = w + L.o_kf, *kfws = w + L.o_kfws,
+         *zd = w + L.o_zd;
+    const int ct = dtype == LCONV_F32 ? CT_F32 : (int)dtype;
+    const int64_t rows = B * H, elems = rows * N;
+    lconv_status_t st;
+    if (!row_spectra16(u, q, kf, rows, N, dtype, fws, stream, &st)) {
+        const void* x = u;
+        if (q) {
+            if (launch_mul_rows(q, u, xs, elems, ct, stream) != hipSuccess) return LCONV_ERR_HIP;
+            x = xs;
+        }
+        st = lconv_filter_fft(x, kf, rows, N, dtype, kfws, L.kfws, stream);
+    }
+    if (st != LCONV_SUCCESS) return st;
+    if (launch_zero_words(zd, (int64_t)(L.zd / 4), stream) != hipSuccess) return LCONV_ERR_HIP;
+    st = fftconv_fwd_call(ds, kf, zd, t, nullptr, nullptr, 1, rows, N, dtype, fws, L.fws, kChunkTarget1D, true,
+                          stream);
+    if (st != LCONV_SUCCESS) return st;
+    if (launch_rev_batch_sum(t, dk, dD, B, H, N, ct, stream) != hipSuccess) return LCONV_ERR_HIP;
+    // lag 0 again, as the direct fp32 sum: the correlation's rows pass through memory in the
+    // dtype, and at lag 0 their batch sum can cancel
+    if (launch_dot_lag0(u, q, dy, v, (float*)(w + L.o_part), dk, dD, B, H, N, ct, stream) != hipSuccess)
+        return LCONV_ERR_HIP;
+    return LCONV_SUCCESS;
+}
+
 // The gradient of a long sequence through the multi-pass forward call.  Reversing a row turns a
 // correlation over later positions into a causal convolution:
 //   dx = rev(k * rev(ds)) + D ds            (ds = dy (.) v);  du = q (.) dx, dq = u (.) dx
@@ -744,8 +777,7 @@ lconv_status_t bwd_long(const void* dy, const void* u, const void* k_f, const vo
     BwdLongLayout L;
     bwd_long_layout(B, H, N, dtype, &L);
     char* w = (char*)workspace;
-    void *fws = w, *ds = w + L.o_ds, *t = w + L.o_t, *xs = w + L.o_xs, *kf = w + L.o_kf, *kfws = w + L.o_kfws,
-         *zd = w + L.o_zd;
+    void *fws = w, *ds = w + L.o_ds, *t = w + L.o_t;
     const int ct = dtype == LCONV_F32 ? CT_F32 : (int)dtype;
     const int64_t rows = B * H, elems = rows * N;
     lconv_status_t st;
@@ -762,28 +794,7 @@ lconv_status_t bwd_long(const void* dy, const void* u, const void* k_f, const vo
     if (st != LCONV_SUCCESS) return st;
     if (launch_rev_gated_out(t, q, q ? u : nullptr, du, q ? dq : nullptr, rows, N, ct, stream) != hipSuccess)
         return LCONV_ERR_HIP;
-    // dk, dD: each row's x as a filter of its own (B*H channels of one row each), applied to
-    // rev(ds) with a zero skip, then reversed and summed over the batch
-    if (dk || dD) {
-        if (!row_spectra16(u, q, kf, rows, N, dtype, fws, stream, &st)) {
-            const void* x = u;
-            if (q) {
-                if (launch_mul_rows(q, u, xs, elems, ct, stream) != hipSuccess) return LCONV_ERR_HIP;
-                x = xs;
-            }
-            st = lconv_filter_fft(x, kf, rows, N, dtype, kfws, L.kfws, stream);
-        }
-        if (st != LCONV_SUCCESS) return st;
-        if (launch_zero_words(zd, (int64_t)(L.zd / 4), stream) != hipSuccess) return LCONV_ERR_HIP;
-        st = fftconv_fwd_call(ds, kf, zd, t, nullptr, nullptr, 1, rows, N, dtype, fws, L.fws, kChunkTarget1D, true,
-                              stream);
-        if (st != LCONV_SUCCESS) return st;
-        if (launch_rev_batch_sum(t, dk, dD, B, H, N, ct, stream) != hipSuccess) return LCONV_ERR_HIP;
-        // lag 0 again, as the direct fp32 sum: the correlation's rows pass through memory in the
-        // dtype, and at lag 0 their batch sum can cancel
-        if (launch_dot_lag0(u, q, dy, v, (float*)(w + L.o_part), dk, dD, B, H, N, ct, stream) != hipSuccess)
-            return LCONV_ERR_HIP;
-    }
+    if (dk || dD) return dk_long(dy, u, q, v, dk, dD, B, H, N, dtype, workspace, L, stream);
     return LCONV_SUCCESS;
 }
 
@@ -877,9 +888,143 @@ lconv_status_t bwd_impl(const void* dy, const void* u, const void* k_f, const vo
     return LCONV_SUCCESS;
 }
 
+// Workspace of the partial convolution's gradient, in 256-byte aligned parts: rev(ds) and the
+// convolution result t (inside the long-sequence layout when N needs the multi-pass path, whose
+// filter-gradient parts follow), then the full-length filter gradient [H][N] fp32.
+struct PartBwdLayout {
+    size_t o_ds, o_t, o_dkf, total;
+    bool lng;
+    BwdLongLayout L;
+};
+
+bool part_bwd_layout(int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype, PartBwdLayout* P) {
+    int64_t rows, elems, hn;
+    if (!mul_ok(B, H, &rows) || !mul_ok(rows, N, &elems) || !mul_ok(H, N, &hn) || rows == 0 || N == 0)
+        return false;
+    Plan1D p;
+    if (!make_plan_1d(N, &p)) return false;
+    P->lng = p.multipass;
+    const size_t act = round256((size_t)elems * dtype_size(dtype));
+    if (P->lng) {
+        if (!bwd_long_layout(B, H, N, dtype, &P->L)) return false;
+        P->o_ds = P->L.o_ds;
+        P->o_t = P->L.o_t;
+        P->o_dkf = P->L.total;
+    } else {
+        P->o_ds = 0;
+        P->o_t = act;
+        P->o_dkf = 2 * act;
+    }
+    P->total = P->o_dkf + round256((size_t)hn * sizeof(float));
+    return true;
+}
+
+// Gradients of the partial convolution.  The filter has L taps, so the correlations keep the
+// banded structure of the forward call:
+//   dv = dy (.) (k * x + D x)                 the partial forward gated by dy
+//   dx = rev(k * rev(ds)) + D ds              the partial forward on time-reversed rows
+//   dk[h][tau] = the full-length correlation's lag tau < min(L, N) (zero for tau >= N)
+// The last comes from the full-length filter gradient (one fused launch for N <= 4096, the
+// multi-pass correlations past that), of which the first L lags are kept.
+lconv_status_t partial_bwd_impl(const void* dy, const void* u, const void* k_f, const void* D, const void* q,
+                                const void* v, void* du, void* dq, void* dv, float* dk, float* dD, int64_t B,
+                                int64_t H, int64_t N, int64_t L, lconv_dtype_t dtype, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
+    if (B < 0 || H < 0 || N < 0 || L < 0) return LCONV_ERR_INVALID_SHAPE;
+    int64_t elems, t, hl;
+    if (!mul_ok(B, H, &t) || !mul_ok(t, N, &elems) || !mul_ok(elems, 8, &t) || !mul_ok(H, L, &hl) ||
+        !mul_ok(hl, 8, &t) || !mul_ok(H, N, &t) || !mul_ok(t, 8, &t))
+        return LCONV_ERR_INVALID_SHAPE;
+    if (H == 0) return LCONV_SUCCESS;
+    if (L < 8 || L > 4096 || (L % 8) != 0 || (N % 8) != 0 || (N > 0 && !n_supported(N)))
+        return LCONV_ERR_UNSUPPORTED;
+    Plan1D pl;
+    if (!make_plan_1d(L, &pl) || pl.multipass) return LCONV_ERR_UNSUPPORTED;
+    if (!q) dq = nullptr;  // ignored without the gate it belongs to
+    if (!v) dv = nullptr;
+    if (B == 0 || N == 0) {  // no pair of positions: the filter gradients are zero sums
+        if ((dk && !aligned16(dk)) || (dD && !aligned16(dD))) return LCONV_ERR_MISALIGNED;
+        if (dk && launch_zero_words(dk, hl, stream) != hipSuccess) return LCONV_ERR_HIP;
+        if (dD && launch_zero_words(dD, H, stream) != hipSuccess) return LCONV_ERR_HIP;
+        return LCONV_SUCCESS;
+    }
+    if (!dy || !u || !k_f || !D || !du || (q && !dq) || (v && !dv)) return LCONV_ERR_NULL_POINTER;
+    const void* ptrs[] = {dy, u, k_f, D, q, v, du, dq, dv, dk, dD, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return LCONV_ERR_MISALIGNED;
+    const size_t es = dtype_size(dtype), act = (size_t)elems * es;
+    const size_t kf_bytes = lconv_filter_fft_bytes(H, L, dtype);
+    if (kf_bytes == 0) return LCONV_ERR_INVALID_SHAPE;
+    PartBwdLayout P;
+    if (!part_bwd_layout(B, H, N, dtype, &P)) return LCONV_ERR_INVALID_SHAPE;
+    if (!workspace || workspace_bytes < P.total) return LCONV_ERR_WORKSPACE;
+    const void* ins[] = {dy, u, k_f, D, q, v};
+    const size_t in_sz[] = {act, act, kf_bytes, (size_t)H * es, act, act};
+    const void* outs[] = {du, dq, dv, dk, dD, workspace};
+    const size_t out_sz[] = {act, act, act, (size_t)hl * 4, (size_t)H * 4, P.total};
+    for (int o = 0; o < 6; ++o) {
+        for (int i = 0; i < 6; ++i)
+            if (overlap(outs[o], out_sz[o], ins[i], in_sz[i])) return LCONV_ERR_ALIASING;
+        for (int o2 = o + 1; o2 < 6; ++o2)
+            if (overlap(outs[o], out_sz[o], outs[o2], out_sz[o2])) return LCONV_ERR_ALIASING;
+    }
+    char* w = (char*)workspace;
+    void *ds = w + P.o_ds, *tt = w + P.o_t;
+    float* dkf = (float*)(w + P.o_dkf);
+    const int ct = dtype == LCONV_F32 ? CT_F32 : (int)dtype;
+    const int64_t rows = B * H;
+    lconv_status_t st;
+    if (v) {
+        st = partial_impl(u, k_f, D, dv, q, dy, B, H, N, L, dtype, 0, stream);
+        if (st != LCONV_SUCCESS) return st;
+    }
+    if (launch_rev_gate(dy, v, ds, rows, N, ct, stream) != hipSuccess) return LCONV_ERR_HIP;
+    st = partial_impl(ds, k_f, D, tt, nullptr, nullptr, B, H, N, L, dtype, 0, stream);
+    if (st != LCONV_SUCCESS) return st;
+    if (launch_rev_gated_out(tt, q, q ? u : nullptr, du, q ? dq : nullptr, rows, N, ct, stream) != hipSuccess)
+        return LCONV_ERR_HIP;
+    if (!dk && !dD) return LCONV_SUCCESS;
+    if (P.lng) {
+        st = dk_long(dy, u, q, v, dkf, dD, B, H, N, dtype, workspace, P.L, stream);
+        if (st != LCONV_SUCCESS) return st;
+    } else {
+        hipError_t err = hipSuccess;
+        const int cus = device_cu_count(&err);
+        if (!cus) return LCONV_ERR_HIP;
+        Plan1D pn;
+        make_plan_1d(N, &pn);
+        const void* tabs = fused_tables(pn.R, ct, &err);
+        if (!tabs) return LCONV_ERR_HIP;
+        Fused1DArgs a{};
+        a.u = u; a.q = q; a.e2 = dy; a.v = v; a.y = dkf; a.y2 = dD; a.tables = tabs;
+        a.B = B; a.H = H; a.N = N; a.nitems = H;
+        a.inv_m = 1.0f / (float)pn.M; a.M = pn.M; a.M1 = 1;
+        if (launch_dk1d(pn.R, dtype, q != nullptr, v != nullptr, a, cus, stream) != hipSuccess)
+            return LCONV_ERR_HIP;
+    }
+    if (dk && launch_copy_cols(dkf, dk, H, N, L, stream) != hipSuccess) return LCONV_ERR_HIP;
+    return LCONV_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t lconv_fftconv_partial_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype) {
+    if (!dtype_ok(dtype) || B <= 0 || H <= 0 || N <= 0 || (N % 8) != 0 || !n_supported(N)) return 0;
+    PartBwdLayout P;
+    return part_bwd_layout(B, H, N, dtype, &P) ? P.total : 0;
+}
+
+lconv_status_t lconv_fftconv_partial_bwd(const void* dy, const void* u, const void* k_f, const void* D,
+                                         const void* q, const void* v, void* du, void* dq, void* dv, float* dk,
+                                         float* dD, int64_t B, int64_t H, int64_t N, int64_t L,
+                                         lconv_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+    return partial_bwd_impl(dy, u, k_f, D, q, v, du, dq, dv, dk, dD, B, H, N, L, dtype, workspace,
+                            workspace_bytes, stream);
+}
 
 size_t lconv_fftconv_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype) {
     Plan1D p;

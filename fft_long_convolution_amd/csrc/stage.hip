@@ -4,7 +4,7 @@
 // causal convolution's first N outputs do not depend on inputs or taps past N, so the zero tail
 // changes nothing.  Elements are copied as raw 2- or 4-byte words (zero bits are 0.0 in every
 // supported type).  Also the elementwise product that gives the v-gradient from a saved
-// pre-gate output, and a zero fill.
+// pre-gate output, a zero fill and a row-prefix copy.
 #include "coldft.h"
 #include "kernels.h"
 
@@ -171,6 +171,17 @@ __global__ void __launch_bounds__(256) dot_final_kernel(const float* part, float
     }
 }
 
+// dst[r][t] = src[r][t] for t < min(N, L), 0 for N <= t < L: the first L lags of fp32 rows of
+// length N (a short filter's gradient from the full-length correlation)
+__global__ void __launch_bounds__(256) copy_cols_kernel(const float* src, float* dst, int64_t rows, int64_t N,
+                                                        int64_t L) {
+    const int64_t total = rows * L;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        const int64_t r = i / L, t = i - r * L;
+        dst[i] = t < N ? src[r * N + t] : 0.f;
+    }
+}
+
 __global__ void __launch_bounds__(256) zero_words_kernel(uint32_t* p, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
 }
@@ -228,6 +239,12 @@ hipError_t launch_dot_lag0(const void* u, const void* q, const void* dy, const v
     else if (dtype == CT_F16) hipLaunchKernelGGL(dot_part_kernel<CT_F16>, grid, dim3(256), 0, st, u, q, dy, v, part, B, H, N, S);
     else hipLaunchKernelGGL(dot_part_kernel<CT_BF16>, grid, dim3(256), 0, st, u, q, dy, v, part, B, H, N, S);
     hipLaunchKernelGGL(dot_final_kernel, dim3(grid_groups(H)), dim3(256), 0, st, part, dk, dD, H, N, S);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_cols(const float* src, float* dst, int64_t rows, int64_t N, int64_t L, hipStream_t st) {
+    if (rows <= 0 || L <= 0) return hipSuccess;
+    hipLaunchKernelGGL(copy_cols_kernel, dim3(grid_for(rows * L)), dim3(256), 0, st, src, dst, rows, N, L);
     return hipGetLastError();
 }
 

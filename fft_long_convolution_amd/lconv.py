@@ -59,6 +59,8 @@ def load(path: str = LIB_PATH):
         "lconv_fftconv_fwd_save": (i, [vp] * 7 + [i64, i64, i64, i, vp, sz, vp]),
         "lconv_fftconv_bwd_saved": (i, [vp] * 12 + [i64, i64, i64, i, vp, sz, vp]),
         "lconv_fftconv_partial_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i, vp]),
+        "lconv_fftconv_partial_bwd_workspace_bytes": (sz, [i64, i64, i64, i]),
+        "lconv_fftconv_partial_bwd": (i, [vp] * 11 + [i64, i64, i64, i64, i, vp, sz, vp]),
         "lconv_fftconv_sparse_fwd": (i, [vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_uint32, i, vp]),
         "lconv_freq_blocks": (i, [i64]),
         "lconv_butterfly_blocks_count": (i64, [i64]),
@@ -160,6 +162,16 @@ def lconv_fftconv_bwd_saved(dy, u, k_f, D, q, v, c, du, dq, dv, dk, dD, B, H, N,
 
 def lconv_fftconv_partial_fwd(u, k_f, D, y, q, v, B, H, N, L, dtype, stream):
     return load().lconv_fftconv_partial_fwd(u, k_f, D, y, q, v, B, H, N, L, dtype, stream)
+
+
+def lconv_fftconv_partial_bwd_workspace_bytes(B, H, N, dtype):
+    return load().lconv_fftconv_partial_bwd_workspace_bytes(B, H, N, dtype)
+
+
+def lconv_fftconv_partial_bwd(dy, u, k_f, D, q, v, du, dq, dv, dk, dD, B, H, N, L, dtype, workspace,
+                              workspace_bytes, stream):
+    return load().lconv_fftconv_partial_bwd(dy, u, k_f, D, q, v, du, dq, dv, dk, dD, B, H, N, L, dtype,
+                                            workspace, workspace_bytes, stream)
 
 
 def lconv_fftconv_sparse_fwd(u, k_f, D, y, q, v, B, H, N, keep, dtype, stream):
@@ -436,6 +448,28 @@ def fftconv_partial(u, k_f, D, L, q=None, v=None, out=None, stream=None):
                                      L, dtype_code(u.dtype), _stream(stream)),
            "lconv_fftconv_partial_fwd")
     return y
+
+
+def fftconv_partial_bwd(dy, u, k_f, D, L, q=None, v=None, need_dk=True, stream=None):
+    """Gradients of fftconv_partial (a filter of L taps, k_f = filter_fft(k [H, L])) given dy
+    [B, H, N].  Returns (du, dq, dv, dk, dD): du, dq, dv in u's dtype (dq None without q, dv None
+    without v); dk [H, L] and dD [H] in float32 (None when need_dk is False)."""
+    torch = _torch()
+    if dy is None:
+        raise ValueError("dy is required")
+    B, H, N = _gated_inputs(u, k_f, D, q, v, None, L=L, dy=dy)
+    dt = dtype_code(u.dtype)
+    du = torch.empty_like(u)
+    dq = torch.empty_like(u) if q is not None else None
+    dv = torch.empty_like(u) if v is not None else None
+    dk = torch.empty((H, L), dtype=torch.float32, device=u.device) if need_dk else None
+    dD = torch.empty((H,), dtype=torch.float32, device=u.device) if need_dk else None
+    wsb = lconv_fftconv_partial_bwd_workspace_bytes(B, H, N, dt)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=u.device) if wsb else None
+    _check(lconv_fftconv_partial_bwd(_ptr(dy), _ptr(u), _ptr(k_f), _ptr(D), _ptr(q), _ptr(v), _ptr(du),
+                                     _ptr(dq), _ptr(dv), _ptr(dk), _ptr(dD), B, H, N, L, dt, _ptr(ws), wsb,
+                                     _stream(stream)), "lconv_fftconv_partial_bwd")
+    return du, dq, dv, dk, dD
 
 
 def fftconv_sparse(u, k_f, D, keep, q=None, v=None, out=None, stream=None):

@@ -52,7 +52,7 @@ extern "C" {
  * part states.  4: lconv_prepare and lconv_fftconv_fwd_noalloc, two status codes.  5: 2D calls
  * take Hs x Ws images and a workspace; lconv_fftconv2d_workspace_bytes.  6: gradients and the
  * training pair for every supported N, with workspace arguments). */
-#define LCONV_ABI_VERSION 7
+#define LCONV_ABI_VERSION 8
 
 /* The last enumerator only widens the type's range to every int, so that any value a C caller
  * passes is a valid value of the type (unknown ones are rejected with LCONV_ERR_UNSUPPORTED). */
@@ -212,6 +212,33 @@ lconv_status_t lconv_fftconv_partial_fwd(const void* u, const void* k_f, const v
                                          const void* q, const void* v, int64_t B, int64_t H,
                                          int64_t N, int64_t L, lconv_dtype_t dtype,
                                          hipStream_t stream);
+
+/*
+ * Gradients of the partial convolution above, given dy = dL/dy (the partial convolutions of the
+ * FlashFFTConv abstract, trained like the full-length ones).  With x = q (.) u, ds = dy (.) v:
+ *   dx[t] = sum_{s = t}^{min(N, t+L)-1} k[h,s-t] ds[s] + D[h] ds[t];   du = q (.) dx, dq = u (.) dx
+ *   dv = dy (.) ( (k * x)[:N] + D x )        (the partial forward call gated by dy)
+ *   dk[h,tau] = sum_b sum_t ds[b,h,t] x[b,h,t-tau]  for tau < L (zero for tau >= N);  dD[h] = sum x ds
+ *   dy, u, q, v, du, dq, dv   [B][H][N] dtype, as for lconv_fftconv_bwd (dq / dv ignored without q / v)
+ *   k_f        from lconv_filter_fft(k, ..., H, L, dtype), as for lconv_fftconv_partial_fwd
+ *   dk         [H][L] fp32, written (overwritten); NULL: not computed
+ *   dD         [H] fp32, written; NULL: not computed
+ *   workspace  lconv_fftconv_partial_bwd_workspace_bytes(B, H, N, dtype) bytes, device, 16-byte
+ *              aligned (never 0 when B, H, N > 0)
+ * dx is the partial forward call on time-reversed rows (the correlation over the next L positions
+ * becomes a causal L-tap convolution), so it keeps the banded O(N log L) cost; rev(ds) and the
+ * result pass through the workspace in dtype.  dk comes from the full-length filter gradient of
+ * lconv_fftconv_bwd (its first L lags; an [H][N] fp32 part of the workspace), O(N log N).
+ * B = 0 or N = 0 writes zeros to dk and dD.  Outputs must not overlap each other, any input or
+ * the workspace.
+ * Supported: as lconv_fftconv_partial_fwd, with N <= LCONV_MAX_N.
+ */
+size_t lconv_fftconv_partial_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, lconv_dtype_t dtype);
+lconv_status_t lconv_fftconv_partial_bwd(const void* dy, const void* u, const void* k_f, const void* D,
+                                         const void* q, const void* v, void* du, void* dq, void* dv,
+                                         float* dk, float* dD, int64_t B, int64_t H, int64_t N,
+                                         int64_t L, lconv_dtype_t dtype, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Gradients of the gated causal convolution above, given dy = dL/dy (the training path the

@@ -27,7 +27,7 @@ def test_exports_every_header_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lconv.lconv_abi_version() == 7
+    assert lconv.lconv_abi_version() == 8
     for s in range(10):
         assert lconv.status_string(s)
     assert "unknown" in lconv.status_string(99)
@@ -259,6 +259,58 @@ def test_partial_empty_is_noop():
     assert part(B=0) == OK
     assert part(H=0) == OK
     assert part(N=0) == OK
+
+
+def pbwd(dy=G[0], u=G[1], kf=G[2], D=G[3], q=None, v=None, du=G[4], dq=None, dv=None, dk=None,
+         dD=None, B=2, H=3, N=64, L=32, dt=BF16, ws="auto", wsb=None):
+    if ws == "auto":
+        wsb = lconv.lconv_fftconv_partial_bwd_workspace_bytes(B, H, N, dt) if wsb is None else wsb
+        ws = G[9] if wsb else None
+    return lconv.lconv_fftconv_partial_bwd(dy, u, kf, D, q, v, du, dq, dv, dk, dD, B, H, N, L, dt, ws,
+                                           wsb or 0, None)
+
+
+def test_partial_bwd_sizes_and_validation():
+    # single pass: rev(ds) and its convolution (dtype), then the [H][N] fp32 filter gradient
+    assert lconv.lconv_fftconv_partial_bwd_workspace_bytes(2, 3, 64, BF16) == 2 * 768 + 768
+    assert lconv.lconv_fftconv_partial_bwd_workspace_bytes(2, 3, 64, 5) == 0
+    assert lconv.lconv_fftconv_partial_bwd_workspace_bytes(0, 3, 64, BF16) == 0
+    assert lconv.lconv_fftconv_partial_bwd_workspace_bytes(2, 3, 12, BF16) == 0
+    assert lconv.lconv_fftconv_partial_bwd_workspace_bytes(1, 1, 2 ** 22 + 8, BF16) == 0
+    # multi-pass N: at least the full gradient's workspace, plus the [H][N] fp32 part
+    assert (lconv.lconv_fftconv_partial_bwd_workspace_bytes(2, 3, 8192, BF16)
+            >= lconv.lconv_fftconv_bwd_workspace_bytes(2, 3, 8192, BF16) + 3 * 8192 * 4)
+    assert pbwd(dt=5) == UNSUP
+    assert pbwd(B=-1) == SHAPE
+    assert pbwd(L=-8) == SHAPE
+    assert pbwd(L=12) == UNSUP and pbwd(L=8192) == UNSUP and pbwd(L=0) == UNSUP
+    assert pbwd(N=12) == UNSUP
+    assert pbwd(N=2 ** 22 + 8) == UNSUP                                   # beyond the gradient's N
+    assert pbwd(dy=None) == NULLP and pbwd(u=None) == NULLP and pbwd(kf=None) == NULLP
+    assert pbwd(D=None) == NULLP and pbwd(du=None) == NULLP
+    assert pbwd(q=G[5]) == NULLP                                          # q without dq
+    assert pbwd(v=G[6]) == NULLP                                          # v without dv
+    assert pbwd(ws=None, wsb=0) == WSERR
+    assert pbwd(wsb=lconv.lconv_fftconv_partial_bwd_workspace_bytes(2, 3, 64, BF16) - 1) == WSERR
+    assert pbwd(ws=G[9] + 8, wsb=4096) == MISAL
+    assert pbwd(dk=G[7] + 4) == MISAL
+    assert pbwd(du=G[0]) == ALIAS                                         # du == dy
+    assert pbwd(dk=G[3]) == ALIAS                                         # dk over D
+    assert pbwd(ws=G[1], wsb=4096) == ALIAS                               # workspace over u
+    assert pbwd(dk=G[7], dD=G[7] + 16) == ALIAS                           # dD inside dk [H][L]
+    import torch
+    if not torch.cuda.is_available():                                     # valid: fails at the first HIP call
+        assert pbwd(dk=G[7], dD=G[7] + 3 * 32 * 4) == HIPERR              # dD just past dk [H][L]
+
+
+def test_partial_bwd_empty():
+    assert pbwd(H=0) == OK
+    assert pbwd(B=0, ws=None, wsb=0) == OK                                # nothing to zero
+    assert pbwd(N=0, ws=None, wsb=0) == OK
+    assert pbwd(B=0, dy=None, u=None, du=None, ws=None, wsb=0) == OK
+    import torch
+    if not torch.cuda.is_available():                                     # zero fill: a HIP call
+        assert pbwd(B=0, dk=G[7], ws=None, wsb=0) == HIPERR
 
 
 def sparse(u=G[0], kf=G[1], D=G[2], y=G[3], q=None, v=None, B=2, H=3, N=1000, keep=0b10000011, dt=BF16):
