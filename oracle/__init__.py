@@ -6,7 +6,7 @@ the product path (the HIP library and its Python binding) never does, and the tw
 """
 from .oracle import (  # noqa: F401
     DT_F32, DT_F16, DT_BF16,
-    build, conv1d_rows, conv1d_points, conv2d_points, conv2d_dft, conv3d_points, widen,
+    build, conv1d_rows, conv1d_points, conv2d_points, conv2d_dft, conv2d_bwd, conv3d_points, widen,
     ssm_kernel, ssm_rows,
     conv1d_bwd_rows, conv1d_bwd_dk, conv1d_bwd_points, conv1d_bwd_dk_points,
     conv1d_short_points, conv1d_circ_rows, sparse_filter,

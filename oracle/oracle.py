@@ -362,6 +362,42 @@ def conv2d_points(u, k, D, pts, dt=None, nthreads=None):
     return out
 
 
+def conv2d_bwd(u, k, D, gy, images=None, chans=None, dt=None):
+    """Gradients of the centred 2D convolution (conv2d_points' definition) given gy = dL/dy
+    [B,C,Hs,Ws], in float64 from the exact values of the storage-dtype inputs:
+        du[b,c,m,n] = sum_{i,j} gy[b,c,i,j] k[c, i+Hs/2-m, j+Ws/2-n] + D[c] gy[b,c,m,n]
+        dk[c,a,e]   = sum_{b,i,j} gy[b,c,i,j] u[b,c, i+Hs/2-a, j+Ws/2-e]
+        dD[c]       = sum_{b,i,j} gy[b,c,i,j] u[b,c,i,j]
+    (halves rounded down, u and k zero outside their extent).  With G = gy placed at rows
+    [Hs/2, Hs/2+Hs) and columns [Ws/2, Ws/2+Ws) of a (2Hs-1) x (2Ws-1) zero grid, du = the valid
+    correlation of G with k plus D gy, and dk = the batch sum of the valid correlations of G with
+    u (scipy.signal.correlate, float64).  images: (b, c) pairs for du (default all); chans: the
+    channels for dk and dD (default all).  Returns (du [len(images),Hs,Ws], dk [len(chans),Hs,Ws],
+    dD [len(chans)])."""
+    from scipy.signal import correlate
+    dt = _dt_of(u, dt)
+    u, k, D, gy = (widen(a, dt) for a in (u, k, D, gy))
+    B, C, Hs, Ws = u.shape
+    assert k.shape == (C, Hs, Ws) and D.shape == (C,) and gy.shape == u.shape
+    h, w = Hs // 2, Ws // 2
+    if images is None:
+        images = [(b, c) for b in range(B) for c in range(C)]
+    if chans is None:
+        chans = list(range(C))
+
+    def grid(b, c):
+        G = np.zeros((2 * Hs - 1, 2 * Ws - 1))
+        G[h:h + Hs, w:w + Ws] = gy[b, c]
+        return G
+
+    du = np.stack([correlate(grid(b, c), k[c], mode="valid") + D[c] * gy[b, c] for b, c in images]) \
+        if len(images) else np.zeros((0, Hs, Ws))
+    dk = np.stack([sum(correlate(grid(b, c), u[b, c], mode="valid") for b in range(B)) for c in chans]) \
+        if len(chans) else np.zeros((0, Hs, Ws))
+    dD = np.asarray([float(np.sum(gy[:, c] * u[:, c])) for c in chans])
+    return du, dk, dD
+
+
 def ssm_kernel(lam, W, N):
     """The filter of a diagonal state-space model: k[h, t] = Re sum_n W[h, n] lam[h, n]^t for
     t < N (lam, W complex [H, NS]), by repeated multiplication in float64 complex."""
