@@ -318,8 +318,11 @@ __global__ void __launch_bounds__(512) conv2d_kernel(const Conv2DArgs a) {
 // computed as two explicit DFT-matrix passes in fp32 (one-off, not on the convolution path),
 // stored in the order the column stage reads it: [channel][v][lane][jj], u = lane%16 +
 // 16 (4 (lane/16) + jj).
+// flip = 1: the kernel rotated by 180 degrees, k[Hs-1-a][Ws-1-e] in place of k[a][e] (the filter
+// gradient's correlation as a convolution).
 template <int IO>
-__global__ void __launch_bounds__(256) filter2d_kernel(const void* k, void* kf, float inv_p2, int Hs, int Ws) {
+__global__ void __launch_bounds__(256) filter2d_kernel(const void* k, void* kf, float inv_p2, int Hs, int Ws,
+                                                       int flip) {
     __shared__ float2 T[S2D][32];
     __shared__ float2 W[P2D];
     const int ch = blockIdx.x, vb = blockIdx.y, tid = threadIdx.x;
@@ -335,7 +338,7 @@ __global__ void __launch_bounds__(256) filter2d_kernel(const void* k, void* kf, 
         const int ar = idx / 32, vv = idx % 32, v = 32 * vb + vv;
         float re = 0.f, im = 0.f;
         for (int e = 0; e < Ws; ++e) {
-            const float x = unpack_lo<IO>(kc[ar * Ws + e]);
+            const float x = unpack_lo<IO>(flip ? kc[(Hs - 1 - ar) * Ws + (Ws - 1 - e)] : kc[ar * Ws + e]);
             const float2 w = W[(v * (e + dc)) & (P2D - 1)];
             re += x * w.x;
             im += x * w.y;
@@ -356,13 +359,102 @@ __global__ void __launch_bounds__(256) filter2d_kernel(const void* k, void* kf, 
     }
 }
 
+// The adjoint operator's spectrum, in the same stored order: (-1)^(u+v) conj(K[u][v]).  The
+// forward reads the window at grid offset 64 of an image placed at offset 0; its adjoint places
+// the output gradient at 64 and reads at 0, which is the same window read of a convolution with
+// the conjugate spectrum shifted by 128 = P/2 in each axis, a sign (-1)^u (-1)^v.  The skip
+// term, a delta at (64, 64), maps to itself, so D is unchanged.  Both factors flip sign bits
+// only (exact).  One thread per stored (re, im) word; u's parity is the lane's parity in the
+// stored order ([channel][v][lane][jj], u = lane % 16 + 16 (4 (lane / 16) + jj)).
+__global__ void __launch_bounds__(256) adj2d_kernel(const uint32_t* kf, uint32_t* ka, int64_t words) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (int64_t)gridDim.x * 256) {
+        const int pos = (int)(i & (P2D - 1)), v = (int)((i >> 8) & (P2D - 1));
+        const int odd = ((pos >> 2) ^ v) & 1;    // parity of u + v
+        // even: conj (flip the imaginary sign); odd: -conj (flip the real sign)
+        ka[i] = kf[i] ^ (odd ? 0x00008000u : 0x80000000u);
+    }
+}
+
+// dk[c][a][e] = sum_b r[b*C + c][Hs-1-a][Ws-1-e] in fp32 (ascending b): the batch sum of the
+// per-image correlations, each computed as a convolution with the rotated output gradient.
+template <int IO>
+__global__ void __launch_bounds__(256) dk2d_sum_kernel(const void* r, float* dk, int64_t B, int64_t C, int Hs,
+                                                       int Ws) {
+    const int64_t img = (int64_t)Hs * Ws, total = C * img;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        const int64_t c = i / img, p = i - c * img;
+        const int a = (int)(p / Ws), e = (int)(p - (int64_t)a * Ws);
+        const int64_t src = (int64_t)(Hs - 1 - a) * Ws + (Ws - 1 - e);
+        float acc = 0.f;
+        for (int64_t b = 0; b < B; ++b) acc += unpack_lo<IO>(((const uint16_t*)r)[(b * C + c) * img + src]);
+        dk[i] = acc;
+    }
+}
+
+// dD[c] = sum_b sum_pixels dy u in fp32: one workgroup per channel, fixed-order tree reduction.
+template <int IO>
+__global__ void __launch_bounds__(256) dd2d_kernel(const void* dy, const void* u, float* dD, int64_t B, int64_t C,
+                                                   int64_t img) {
+    const int64_t c = blockIdx.x;
+    float acc = 0.f;
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t base = (b * C + c) * img;
+        for (int64_t p = threadIdx.x; p < img; p += 256)
+            acc = fmaf(unpack_lo<IO>(((const uint16_t*)dy)[base + p]), unpack_lo<IO>(((const uint16_t*)u)[base + p]),
+                       acc);
+    }
+    __shared__ float red[256];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) dD[c] = red[0];
+}
+
+static unsigned grid2d_for(int64_t n) {
+    const int64_t g = (n + 255) / 256;
+    return (unsigned)(g < 65536 ? (g > 0 ? g : 1) : 65536);
+}
+
+hipError_t launch_adj2d(const void* kf, void* ka, int64_t C, hipStream_t st) {
+    const int64_t words = C * P2D * P2D;
+    if (words <= 0) return hipSuccess;
+    hipLaunchKernelGGL(adj2d_kernel, dim3(grid2d_for(words)), dim3(256), 0, st, (const uint32_t*)kf, (uint32_t*)ka,
+                       words);
+    return hipGetLastError();
+}
+
+hipError_t launch_dk2d_sum(int dtype, const void* r, float* dk, int64_t B, int64_t C, int Hs, int Ws, hipStream_t st) {
+    const int64_t total = C * Hs * Ws;
+    if (total <= 0) return hipSuccess;
+    if (dtype == CT_F16)
+        hipLaunchKernelGGL((dk2d_sum_kernel<CT_F16>), dim3(grid2d_for(total)), dim3(256), 0, st, r, dk, B, C, Hs, Ws);
+    else
+        hipLaunchKernelGGL((dk2d_sum_kernel<CT_BF16>), dim3(grid2d_for(total)), dim3(256), 0, st, r, dk, B, C, Hs, Ws);
+    return hipGetLastError();
+}
+
+hipError_t launch_dd2d(int dtype, const void* dy, const void* u, float* dD, int64_t B, int64_t C, int64_t img,
+                       hipStream_t st) {
+    if (C <= 0) return hipSuccess;
+    if (dtype == CT_F16)
+        hipLaunchKernelGGL((dd2d_kernel<CT_F16>), dim3((unsigned)C), dim3(256), 0, st, dy, u, dD, B, C, img);
+    else
+        hipLaunchKernelGGL((dd2d_kernel<CT_BF16>), dim3((unsigned)C), dim3(256), 0, st, dy, u, dD, B, C, img);
+    return hipGetLastError();
+}
+
 hipError_t launch_conv2d(int dtype, const Conv2DArgs& a, hipStream_t st) {
     if (a.filter) {
         dim3 grid((unsigned)a.C, P2D / 32);
         if (dtype == CT_F16)
-            hipLaunchKernelGGL((filter2d_kernel<CT_F16>), grid, dim3(256), 0, st, a.u, (void*)a.kf, a.inv_p2, a.Hs, a.Ws);
+            hipLaunchKernelGGL((filter2d_kernel<CT_F16>), grid, dim3(256), 0, st, a.u, (void*)a.kf, a.inv_p2, a.Hs, a.Ws,
+                               a.flip);
         else
-            hipLaunchKernelGGL((filter2d_kernel<CT_BF16>), grid, dim3(256), 0, st, a.u, (void*)a.kf, a.inv_p2, a.Hs, a.Ws);
+            hipLaunchKernelGGL((filter2d_kernel<CT_BF16>), grid, dim3(256), 0, st, a.u, (void*)a.kf, a.inv_p2, a.Hs,
+                               a.Ws, a.flip);
         return hipGetLastError();
     }
     const int64_t nitems = (a.B + 1) / 2 * a.C;

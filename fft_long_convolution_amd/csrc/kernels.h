@@ -118,9 +118,17 @@ struct Conv2DArgs {
     int Hs, Ws;          // image sides: 1 <= Hs <= 128, 8 <= Ws <= 128 with Ws a multiple of 8
     float inv_p2;        // 1 / (2S)^2
     int filter;          // 1: u = k [C][S][S]; the spectrum is written to kf
+    int flip;            // filter mode: 1 takes k rotated by 180 degrees
     int cus;             // compute units (persistent grid size)
 };
 hipError_t launch_conv2d(int dtype, const Conv2DArgs& a, hipStream_t stream);
+// 2D gradient passes: the adjoint spectrum (-1)^(u+v) conj(K) in stored order; the batch sum of
+// rotated per-image correlations into dk [C][Hs][Ws] fp32; dD[c] = sum dy u (fp32)
+hipError_t launch_adj2d(const void* kf, void* ka, int64_t C, hipStream_t stream);
+hipError_t launch_dk2d_sum(int dtype, const void* r, float* dk, int64_t B, int64_t C, int Hs, int Ws,
+                           hipStream_t stream);
+hipError_t launch_dd2d(int dtype, const void* dy, const void* u, float* dD, int64_t B, int64_t C, int64_t img,
+                       hipStream_t stream);
 
 // State passing for diagonal state-space filters (ssm.hip).  Modes are handled in blocks of
 // ssm_block_modes(NS) = 64 (the last block zero-padded); NSP = blocks * block modes.

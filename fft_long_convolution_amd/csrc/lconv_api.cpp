@@ -1151,6 +1151,111 @@ lconv_status_t lconv_fftconv2d_fwd(const void* u, const void* k_f, const void* D
     return hip_status(launch_conv2d(dtype, a, stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Workspace of the 2D gradient, in 256-byte aligned parts: the adjoint spectrum [C], the
+// spectra of the rotated output gradients [B*C], their convolutions with u [B*C][Hs][Ws] and a
+// zero skip [B*C] (dtype).
+struct Bwd2DLayout {
+    size_t o_ka, o_kd, o_r, o_zd, total;
+};
+
+bool bwd2d_layout(int64_t B, int64_t C, int64_t Hs, int64_t Ws, lconv_dtype_t dtype, Bwd2DLayout* L) {
+    int64_t bc, elems;
+    if (!mul_ok(B, C, &bc) || !mul_ok(bc, Hs * Ws, &elems) || bc == 0) return false;
+    const size_t ka = lconv_filter_fft2d_bytes(C, Hs, Ws, dtype), kd = lconv_filter_fft2d_bytes(bc, Hs, Ws, dtype);
+    if (ka == 0 || kd == 0) return false;
+    const size_t es = dtype_size(dtype);
+    L->o_ka = 0;
+    L->o_kd = round256(ka);
+    L->o_r = L->o_kd + round256(kd);
+    L->o_zd = L->o_r + round256((size_t)elems * es);
+    L->total = L->o_zd + round256((size_t)bc * es);
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lconv_fftconv2d_bwd_workspace_bytes(int64_t B, int64_t C, int64_t Hs, int64_t Ws, lconv_dtype_t dtype) {
+    if (!dtype_ok(dtype) || dtype == LCONV_F32 || B <= 0 || C <= 0 || !sides2d_ok(Hs, Ws)) return 0;
+    Bwd2DLayout L;
+    return bwd2d_layout(B, C, Hs, Ws, dtype, &L) ? L.total : 0;
+}
+
+lconv_status_t lconv_fftconv2d_bwd(const void* dy, const void* u, const void* k_f, const void* D, void* du,
+                                   float* dk, float* dD, int64_t B, int64_t C, int64_t Hs, int64_t Ws,
+                                   lconv_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+    if (!dtype_ok(dtype)) return LCONV_ERR_UNSUPPORTED;
+    if (B < 0 || C < 0 || Hs < 0 || Ws < 0) return LCONV_ERR_INVALID_SHAPE;
+    int64_t img, elems, t;
+    if (!mul_ok(Hs, Ws, &img) || !mul_ok(B, C, &t) || !mul_ok(t, img, &elems) || !mul_ok(elems, 8, &t) ||
+        !mul_ok(C, img, &t) || !mul_ok(t, 8, &t))
+        return LCONV_ERR_INVALID_SHAPE;
+    if (C == 0) return LCONV_SUCCESS;
+    if (!sides2d_ok(Hs, Ws) || dtype == LCONV_F32) return LCONV_ERR_UNSUPPORTED;
+    if (B == 0) {  // empty batch: the filter gradients are zero sums
+        if ((dk && !aligned16(dk)) || (dD && !aligned16(dD))) return LCONV_ERR_MISALIGNED;
+        if (dk && launch_zero_words(dk, C * img, stream) != hipSuccess) return LCONV_ERR_HIP;
+        if (dD && launch_zero_words(dD, C, stream) != hipSuccess) return LCONV_ERR_HIP;
+        return LCONV_SUCCESS;
+    }
+    if (!dy || !u || !k_f || !D || !du) return LCONV_ERR_NULL_POINTER;
+    const void* ptrs[] = {dy, u, k_f, D, du, dk, dD, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return LCONV_ERR_MISALIGNED;
+    Bwd2DLayout L;
+    if (!bwd2d_layout(B, C, Hs, Ws, dtype, &L)) return LCONV_ERR_INVALID_SHAPE;
+    if (!workspace || workspace_bytes < L.total) return LCONV_ERR_WORKSPACE;
+    const size_t es = dtype_size(dtype), act = (size_t)elems * es;
+    const void* ins[] = {dy, u, k_f, D};
+    const size_t in_sz[] = {act, act, lconv_filter_fft2d_bytes(C, Hs, Ws, dtype), (size_t)C * es};
+    const void* outs[] = {du, dk, dD, workspace};
+    const size_t out_sz[] = {act, (size_t)(C * img) * 4, (size_t)C * 4, L.total};
+    for (int o = 0; o < 4; ++o) {
+        for (int i = 0; i < 4; ++i)
+            if (overlap(outs[o], out_sz[o], ins[i], in_sz[i])) return LCONV_ERR_ALIASING;
+        for (int o2 = o + 1; o2 < 4; ++o2)
+            if (overlap(outs[o], out_sz[o], outs[o2], out_sz[o2])) return LCONV_ERR_ALIASING;
+    }
+    hipError_t err = hipSuccess;
+    const int cus = device_cu_count(&err);
+    if (!cus) return LCONV_ERR_HIP;
+    const void* tabs = fused_tables(1, (int)dtype, &err);  // 256-point transform blocks
+    if (!tabs) return LCONV_ERR_HIP;
+    char* w = (char*)workspace;
+    // du = the forward convolution of dy with the adjoint spectrum (same D)
+    if (launch_adj2d(k_f, w + L.o_ka, C, stream) != hipSuccess) return LCONV_ERR_HIP;
+    Conv2DArgs a{};
+    a.u = dy; a.kf = w + L.o_ka; a.D = D; a.y = du; a.tables = tabs;
+    a.B = B; a.C = C; a.filter = 0; a.cus = cus;
+    a.Hs = (int)Hs; a.Ws = (int)Ws;
+    a.inv_p2 = 1.0f / (float)(kP2D * kP2D);
+    if (launch_conv2d(dtype, a, stream) != hipSuccess) return LCONV_ERR_HIP;
+    if (dk) {
+        // per image, dk_b[a][e] = (u_b conv rot(dy_b))[Hs-1-a][Ws-1-e]: the B*C images as channels
+        // of one image each, with the rotated dy as their filters and a zero skip
+        const int64_t bc = B * C;
+        Conv2DArgs f{};
+        f.u = dy; f.kf = w + L.o_kd; f.C = bc; f.B = 1; f.filter = 1; f.flip = 1;
+        f.Hs = (int)Hs; f.Ws = (int)Ws;
+        f.inv_p2 = 1.0f / (float)(kP2D * kP2D);
+        if (launch_conv2d(dtype, f, stream) != hipSuccess) return LCONV_ERR_HIP;
+        if (launch_zero_words(w + L.o_zd, (int64_t)((bc * es + 3) / 4), stream) != hipSuccess) return LCONV_ERR_HIP;
+        Conv2DArgs c = a;
+        c.u = u; c.kf = w + L.o_kd; c.D = w + L.o_zd; c.y = w + L.o_r; c.B = 1; c.C = bc;
+        if (launch_conv2d(dtype, c, stream) != hipSuccess) return LCONV_ERR_HIP;
+        if (launch_dk2d_sum((int)dtype, w + L.o_r, dk, B, C, (int)Hs, (int)Ws, stream) != hipSuccess)
+            return LCONV_ERR_HIP;
+    }
+    if (dD && launch_dd2d((int)dtype, dy, u, dD, B, C, img, stream) != hipSuccess) return LCONV_ERR_HIP;
+    return LCONV_SUCCESS;
+}
+
 // ---- 3D ---------------------------------------------------------------------------------------
 
 namespace {

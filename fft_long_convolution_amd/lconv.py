@@ -69,6 +69,8 @@ def load(path: str = LIB_PATH):
         "lconv_butterfly_filter": (i, [vp, vp, vp, i64, i64, i, vp]),
         "lconv_butterfly_fwd": (i, [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i, vp]),
         "lconv_filter_fft2d": (i, [vp, vp, i64, i64, i64, i, vp]),
+        "lconv_fftconv2d_bwd_workspace_bytes": (sz, [i64, i64, i64, i64, i]),
+        "lconv_fftconv2d_bwd": (i, [vp] * 7 + [i64, i64, i64, i64, i, vp, sz, vp]),
         "lconv_ssm_prep_bytes": (sz, [i64, i64, i64, i]),
         "lconv_ssm_prepare": (i, [vp, vp, vp, i64, i64, i64, i, vp]),
         "lconv_fftconv_ssm_workspace_bytes": (sz, [i64, i64, i64, i64, i64]),
@@ -208,6 +210,15 @@ def lconv_filter_fft2d(k, k_f, C, Hs, Ws, dtype, stream):
 
 def lconv_fftconv2d_fwd(u, k_f, D, y, B, C, Hs, Ws, dtype, workspace, workspace_bytes, stream):
     return load().lconv_fftconv2d_fwd(u, k_f, D, y, B, C, Hs, Ws, dtype, workspace, workspace_bytes, stream)
+
+
+def lconv_fftconv2d_bwd_workspace_bytes(B, C, Hs, Ws, dtype):
+    return load().lconv_fftconv2d_bwd_workspace_bytes(B, C, Hs, Ws, dtype)
+
+
+def lconv_fftconv2d_bwd(dy, u, k_f, D, du, dk, dD, B, C, Hs, Ws, dtype, workspace, workspace_bytes, stream):
+    return load().lconv_fftconv2d_bwd(dy, u, k_f, D, du, dk, dD, B, C, Hs, Ws, dtype, workspace,
+                                      workspace_bytes, stream)
 
 
 def lconv_ssm_prep_bytes(H, NS, T, dtype):
@@ -644,3 +655,23 @@ def fftconv2d(u, k_f, D, out=None, stream=None):
     _check(lconv_fftconv2d_fwd(_ptr(u), _ptr(k_f), _ptr(D), _ptr(y), B, C, Hs, Ws, dt, _ptr(ws), wsb,
                                _stream(stream)), "lconv_fftconv2d_fwd")
     return y
+
+
+def fftconv2d_bwd(dy, u, k_f, D, need_dk=True, stream=None):
+    """Gradients of fftconv2d given dy [B, C, Hs, Ws]: (du in u's dtype, dk [C, Hs, Ws] and dD [C]
+    in float32; dk and dD are None when need_dk is False)."""
+    torch = _torch()
+    tdt, (B, C, Hs, Ws) = _act(u, dims=4)
+    dt = dtype_code(tdt)
+    _need("dy", dy, (B, C, Hs, Ws), tdt)
+    _need("D", D, (C,), tdt)
+    _need_buf("k_f", k_f, lconv_filter_fft2d_bytes(C, Hs, Ws, dt))
+    dev = _on_gpu(dy=dy, u=u, k_f=k_f, D=D)
+    du = torch.empty_like(u)
+    dk = torch.empty((C, Hs, Ws), dtype=torch.float32, device=dev) if need_dk else None
+    dD = torch.empty((C,), dtype=torch.float32, device=dev) if need_dk else None
+    wsb = lconv_fftconv2d_bwd_workspace_bytes(B, C, Hs, Ws, dt)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+    _check(lconv_fftconv2d_bwd(_ptr(dy), _ptr(u), _ptr(k_f), _ptr(D), _ptr(du), _ptr(dk), _ptr(dD), B, C, Hs, Ws,
+                               dt, _ptr(ws), wsb, _stream(stream)), "lconv_fftconv2d_bwd")
+    return du, dk, dD

@@ -342,6 +342,34 @@ lconv_status_t lconv_fftconv2d_fwd(const void* u, const void* k_f, const void* D
                                    int64_t B, int64_t C, int64_t Hs, int64_t Ws, lconv_dtype_t dtype,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Gradients of the 2D convolution above, given dy = dL/dy (HyenaND abstract: the operator is
+ * trained like its 1D counterpart; it is linear in u, k and D):
+ *   du[b,c,m,n] = sum_{i,j} dy[b,c,i,j] k[c, i+Hs/2-m, j+Ws/2-n] + D[c] dy[b,c,m,n]
+ *   dk[c,a,e]   = sum_{b,i,j} dy[b,c,i,j] u[b,c, i+Hs/2-a, j+Ws/2-e]
+ *   dD[c]       = sum_{b,i,j} dy[b,c,i,j] u[b,c,i,j]
+ *   dy, u      [B][C][Hs][Ws] dtype, device
+ *   k_f, D     as for lconv_fftconv2d_fwd (the same spectrum)
+ *   du         [B][C][Hs][Ws] dtype, written
+ *   dk         [C][Hs][Ws] fp32, written (overwritten); NULL: not computed
+ *   dD         [C] fp32, written; NULL: not computed
+ *   workspace  lconv_fftconv2d_bwd_workspace_bytes(B, C, Hs, Ws, dtype) bytes, device, 16-byte
+ *              aligned
+ * du is the forward kernel on dy with the adjoint spectrum (-1)^(u+v) conj(K) (the output window
+ * at grid offset 64 moved back to the image at offset 0: a shift by half the 256-point grid),
+ * formed from k_f by sign flips alone.  dk runs the forward kernel over the B*C images as
+ * channels of one image, each with its own dy rotated by 180 degrees as the filter (spectra in
+ * the workspace), and sums the rotated results over the batch in fp32; the per-image
+ * correlations pass through the workspace in dtype.  dD is a direct fp32 sum.
+ * B = 0 writes zeros to dk and dD.  Outputs must not overlap each other, any input or the
+ * workspace.  Supported: as lconv_fftconv2d_fwd.
+ */
+size_t lconv_fftconv2d_bwd_workspace_bytes(int64_t B, int64_t C, int64_t Hs, int64_t Ws, lconv_dtype_t dtype);
+lconv_status_t lconv_fftconv2d_bwd(const void* dy, const void* u, const void* k_f, const void* D, void* du,
+                                   float* dk, float* dD, int64_t B, int64_t C, int64_t Hs, int64_t Ws,
+                                   lconv_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
 /* ---- state-space filters: chunks with state passing --------------------------------------- */
 
 /*

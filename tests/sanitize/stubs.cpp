@@ -20,6 +20,9 @@ LCV_STUB(hipError_t launch_rev_gated_out(const void*, const void*, const void*, 
 LCV_STUB(hipError_t launch_rev_batch_sum(const void*, float*, float*, int64_t, int64_t, int64_t, int, hipStream_t))
 LCV_STUB(hipError_t launch_zero_words(void*, int64_t, hipStream_t))
 LCV_STUB(hipError_t launch_copy_cols(const float*, float*, int64_t, int64_t, int64_t, hipStream_t))
+LCV_STUB(hipError_t launch_adj2d(const void*, void*, int64_t, hipStream_t))
+LCV_STUB(hipError_t launch_dk2d_sum(int, const void*, float*, int64_t, int64_t, int, int, hipStream_t))
+LCV_STUB(hipError_t launch_dd2d(int, const void*, const void*, float*, int64_t, int64_t, int64_t, hipStream_t))
 LCV_STUB(hipError_t launch_dot_lag0(const void*, const void*, const void*, const void*, float*, float*, float*, int64_t,
                                     int64_t, int64_t, int, hipStream_t))
 LCV_STUB(hipError_t launch_bfly_images(const void*, void*, int, int, const FusedTableLayout&, hipStream_t))

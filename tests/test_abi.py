@@ -313,6 +313,42 @@ def test_partial_bwd_empty():
         assert pbwd(B=0, dk=G[7], ws=None, wsb=0) == HIPERR
 
 
+def bwd2d(dy=G[0], u=G[1], kf=G[2], D=G[3], du=G[4], dk=None, dD=None, B=2, C=3, Hs=16, Ws=16, dt=BF16,
+          ws="auto", wsb=None):
+    if ws == "auto":
+        wsb = lconv.lconv_fftconv2d_bwd_workspace_bytes(B, C, Hs, Ws, dt) if wsb is None else wsb
+        ws = 1 << 44 if wsb else None        # far from every other fake address
+    return lconv.lconv_fftconv2d_bwd(dy, u, kf, D, du, dk, dD, B, C, Hs, Ws, dt, ws, wsb or 0, None)
+
+
+def test_2d_bwd_sizes_and_validation():
+    spec = 256 * 256 * 4        # one 2D spectrum (16-bit pairs)
+    act = 2 * 3 * 16 * 16 * 2
+    assert lconv.lconv_fftconv2d_bwd_workspace_bytes(2, 3, 16, 16, BF16) == 3 * spec + 6 * spec + act + 256
+    assert lconv.lconv_fftconv2d_bwd_workspace_bytes(2, 3, 16, 16, F32) == 0
+    assert lconv.lconv_fftconv2d_bwd_workspace_bytes(2, 3, 16, 12, BF16) == 0     # Ws % 8
+    assert lconv.lconv_fftconv2d_bwd_workspace_bytes(2, 3, 129, 16, BF16) == 0
+    assert lconv.lconv_fftconv2d_bwd_workspace_bytes(0, 3, 16, 16, BF16) == 0
+    assert bwd2d(dt=F32) == UNSUP
+    assert bwd2d(B=-1) == SHAPE
+    assert bwd2d(Ws=12) == UNSUP and bwd2d(Hs=200) == UNSUP
+    assert bwd2d(dy=None) == NULLP and bwd2d(u=None) == NULLP and bwd2d(kf=None) == NULLP
+    assert bwd2d(D=None) == NULLP and bwd2d(du=None) == NULLP
+    assert bwd2d(ws=None, wsb=0) == WSERR
+    assert bwd2d(wsb=lconv.lconv_fftconv2d_bwd_workspace_bytes(2, 3, 16, 16, BF16) - 1) == WSERR
+    assert bwd2d(dk=G[7] + 4) == MISAL
+    assert bwd2d(du=G[0]) == ALIAS                                       # du == dy
+    assert bwd2d(dk=G[2] + 64) == ALIAS                                  # dk over k_f
+    assert bwd2d(dk=G[7], dD=G[7] + 256) == ALIAS                        # dD inside dk [C][Hs][Ws]
+    assert bwd2d(ws=G[1], wsb=1 << 24) == ALIAS                          # workspace over u
+    assert bwd2d(C=0) == OK
+    assert bwd2d(B=0, ws=None, wsb=0) == OK                              # nothing to zero
+    import torch
+    if not torch.cuda.is_available():
+        assert bwd2d(B=0, dk=G[7], ws=None, wsb=0) == HIPERR             # zero fill: a HIP call
+        assert bwd2d(dk=G[7], dD=G[8]) == HIPERR                         # valid: first HIP call fails
+
+
 def sparse(u=G[0], kf=G[1], D=G[2], y=G[3], q=None, v=None, B=2, H=3, N=1000, keep=0b10000011, dt=BF16):
     return lconv.lconv_fftconv_sparse_fwd(u, kf, D, y, q, v, B, H, N, keep, dt, None)
 
