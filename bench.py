@@ -220,6 +220,90 @@ def launch_distribution(step, args):
     return out
 
 
+def time_calls(call, args):
+    """ms per call over K calls (after W warm-up calls), one event pair on the current stream."""
+    import torch
+    for _ in range(args.warmup):
+        call()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    prime(3 * args.steps)
+    ev0.record()
+    for _ in range(args.steps):
+        call()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / args.steps
+
+
+def grad_report(ms, nbytes, outputs, launches, wsb):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms_per_call": round(ms, 5), "algorithmic_bytes": nbytes, "achieved": round(gbs, 2), "unit": "GB/s",
+            "peak": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4), "outputs": outputs, "launches": launches,
+            "workspace_bytes": wsb}
+
+
+def time_backward_2d(lconv, wl, spec, u, kf, D, args):
+    """The 2D gradient call (du, dk, dD) on the forward's inputs and a seeded dy.  Algorithmic
+    bytes: read dy and u, write du, read the Hermitian half of the spectrum and D, write dk and dD
+    (fp32)."""
+    import torch
+    s = 2
+    dy = to_dev(wl.make_grad_2d(spec), spec.dtype)
+    du = torch.empty_like(u)
+    dk = torch.empty((spec.C, spec.Hs, spec.cols), dtype=torch.float32, device="cuda")
+    dD = torch.empty((spec.C,), dtype=torch.float32, device="cuda")
+    dtc = lconv.dtype_code(u.dtype)
+    wsb = lconv.lconv_fftconv2d_bwd_workspace_bytes(spec.B, spec.C, spec.Hs, spec.cols, dtc)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        st = lconv.lconv_fftconv2d_bwd(dy.data_ptr(), u.data_ptr(), kf.data_ptr(), D.data_ptr(), du.data_ptr(),
+                                       dk.data_ptr(), dD.data_ptr(), spec.B, spec.C, spec.Hs, spec.cols, dtc,
+                                       ws.data_ptr(), wsb, stream.cuda_stream)
+        if st != 0:
+            raise lconv.LconvError(st, "lconv_fftconv2d_bwd")
+    act = spec.B * spec.C * spec.Hs * spec.cols * s
+    P = 2 * spec.S
+    nbytes = 3 * act + spec.C * P * (P // 2 + 1) * 2 * s + spec.C * s + spec.C * spec.Hs * spec.cols * 4 + spec.C * 4
+    return grad_report(time_calls(call, args), nbytes, "du (dtype); dk, dD (fp32)",
+                       "adjoint spectrum; 2D kernel on dy (du); rotated-dy spectra; 2D kernel over B*C "
+                       "one-image channels; batch sum (dk); dot (dD)", wsb)
+
+
+def time_backward_partial(lconv, wl, spec, u, kf, D, q, v, args):
+    """The partial convolution's gradient call on the forward's inputs and a seeded dy.
+    Algorithmic bytes as for the full gradient, with the spectrum and dk at the L taps."""
+    import torch
+    s = {"f32": 4, "f16": 2, "bf16": 2}[spec.dtype]
+    L = spec.L
+    dy = to_dev(wl.make_grad_1d(spec), spec.dtype)
+    du = torch.empty_like(u)
+    dq = torch.empty_like(u) if q is not None else None
+    dv = torch.empty_like(u) if v is not None else None
+    dk = torch.empty((spec.H, L), dtype=torch.float32, device="cuda")
+    dD = torch.empty((spec.H,), dtype=torch.float32, device="cuda")
+    dtc = lconv.dtype_code(u.dtype)
+    wsb = lconv.lconv_fftconv_partial_bwd_workspace_bytes(spec.B, spec.H, spec.N, dtc)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    p = lambda t: None if t is None else t.data_ptr()
+
+    def call():
+        st = lconv.lconv_fftconv_partial_bwd(dy.data_ptr(), u.data_ptr(), kf.data_ptr(), D.data_ptr(), p(q), p(v),
+                                             du.data_ptr(), p(dq), p(dv), dk.data_ptr(), dD.data_ptr(), spec.B,
+                                             spec.H, spec.N, L, dtc, ws.data_ptr(), wsb, stream.cuda_stream)
+        if st != 0:
+            raise lconv.LconvError(st, "lconv_fftconv_partial_bwd")
+    act = spec.B * spec.H * spec.N * s
+    g = 2 if spec.gated else 0
+    nbytes = (2 + g) * act + (1 + g) * act + spec.H * (L + 1) * 2 * s + spec.H * s + spec.H * (L + 1) * 4
+    return grad_report(time_calls(call, args), nbytes, "du, dq, dv (dtype); dk [H, L], dD (fp32)",
+                       "partial forward gated by dy (dv); rev(dy v); partial forward of it (dx); du, dq; "
+                       "full-length filter gradient (first L lags)", wsb)
+
+
 def time_backward(lconv, wl, spec, u, kf, D, q, v, args):
     """K timed gradient calls (after W warm-up calls) on the forward's inputs and a seeded dy."""
     import torch
@@ -549,6 +633,10 @@ def main():
     if not args.no_bwd and spec.kind == "1d" and spec.N % 8 == 0 and not spec.L and args.keep is None \
             and not args.butterfly and not spec.name.startswith("ssm_"):
         out["backward"] = time_backward(lconv, wl, spec, u, kf, D, q, v, args)
+    elif not args.no_bwd and spec.kind == "2d":
+        out["backward"] = time_backward_2d(lconv, wl, spec, u, kf, D, args)
+    elif not args.no_bwd and spec.kind == "1d" and spec.L and args.keep is None and not args.butterfly:
+        out["backward"] = time_backward_partial(lconv, wl, spec, u, kf, D, q, v, args)
     if not args.no_cpu and spec.kind == "1d" and not spec.name.startswith("ssm_") and not args.butterfly:
         out["cpu_baseline"] = cpu_baseline(d, args.cpu_budget)
     print(json.dumps(out), flush=True)
