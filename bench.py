@@ -268,7 +268,7 @@ def time_backward_2d(lconv, wl, spec, u, kf, D, args):
     P = 2 * spec.S
     nbytes = 3 * act + spec.C * P * (P // 2 + 1) * 2 * s + spec.C * s + spec.C * spec.Hs * spec.cols * 4 + spec.C * 4
     return grad_report(time_calls(call, args), nbytes, "du (dtype); dk, dD (fp32)",
-                       "adjoint spectrum; 2D kernel on dy (du); rotated-dy spectra; 2D kernel over B*C "
+                       "adjoint spectrum; 2D kernel on dy (du); 2D kernel in spectrum mode (rotated-dy spectra); 2D kernel over B*C "
                        "one-image channels; batch sum (dk); dot (dD)", wsb)
 
 

@@ -50,7 +50,12 @@ __device__ __forceinline__ uint32_t ld_raw2(const void* p, int64_t i) {
 
 }  // namespace
 
-template <int CT>
+// SPEC: spectrum mode for the filter gradient.  The items are single images (B = 1) and S1 stops
+// after the column DFT: it stores w^(u A + v Bc) conj(Z[u][v]) / P^2 to a.y in the filter spectrum's
+// order, A = Hs-1 + 64 - Hs/2, Bc = Ws-1 + 64 - Ws/2 -- the spectrum of the image rotated by
+// 180 degrees and placed as a kernel (conj(Z) reverses the image, the phase moves its tap (0, 0) to
+// grid point (64 - Hs/2 + Hs-1, 64 - Ws/2 + Ws-1)).  No product, no inverse, no S2 / S3.
+template <int CT, bool SPEC>
 __global__ void __launch_bounds__(512) conv2d_kernel(const Conv2DArgs a) {
     static_assert(CT != CT_F32, "2D path runs 16-bit operands");
     constexpr int IO = CT;
@@ -174,13 +179,15 @@ __global__ void __launch_bounds__(512) conv2d_kernel(const Conv2DArgs a) {
         }
 
         // ================= S1: columns: DFT, spectrum product, inverse DFT (window rows) =====
-        const float dsc = unpack_lo<IO>(ld_raw2<IO>(a.D, ch)) * a.inv_p2;
+        const float dsc = SPEC ? 0.f : unpack_lo<IO>(ld_raw2<IO>(a.D, ch)) * a.inv_p2;
         for (int v0 = 32 * wave; v0 < 32 * wave + 32; v0 += 4) {
             uint4 kr4[4];
-            static_for<0, 4>([&](auto ii) LCV_INLINE {
-                constexpr int i = decltype(ii)::value;
-                kr4[i] = *((const uint4*)a.kf + ((ch * P2D + v0 + i) * 64 + lane));
-            });
+            if constexpr (!SPEC) {
+                static_for<0, 4>([&](auto ii) LCV_INLINE {
+                    constexpr int i = decltype(ii)::value;
+                    kr4[i] = *((const uint4*)a.kf + ((ch * P2D + v0 + i) * 64 + lane));
+                });
+            }
             Operand<CT> opd[4];
             Tile xs[4];
             static_for<0, 4>([&](auto ii) LCV_INLINE {
@@ -206,6 +213,25 @@ __global__ void __launch_bounds__(512) conv2d_kernel(const Conv2DArgs a) {
                 constexpr int i = decltype(ii)::value;
                 xs[i] = stage_keep<CT>(Gf, opd[i]);  // (L = k2, K = k3): u = k2 + 16 k3
             });
+            if constexpr (SPEC) {
+                const int sa = Hs - 1 + 64 - Hs / 2, sb = Ws - 1 + 64 - Ws / 2;
+                static_for<0, 4>([&](auto ii) LCV_INLINE {
+                    constexpr int i = decltype(ii)::value;
+                    const int v = v0 + i;
+                    uint32_t w[4];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int u = c + 16 * (4 * g + jj);
+                        const int idx = (u * sa + v * sb) & (P2D - 1);
+                        float sn, cs;
+                        sincospif(-2.0f * (float)idx / (float)P2D, &sn, &cs);  // exact argument
+                        const float zr = xs[i].re[jj], zi = xs[i].im[jj];
+                        w[jj] = pack2<CT>((cs * zr + sn * zi) * a.inv_p2, (sn * zr - cs * zi) * a.inv_p2);
+                    }
+                    *((uint4*)a.y + ((ch * P2D + v) * 64 + lane)) = make_uint4(w[0], w[1], w[2], w[3]);
+                });
+                continue;
+            }
             static_for<0, 4>([&](auto ii) LCV_INLINE {
                 constexpr int i = decltype(ii)::value;
                 const int v = v0 + i;
@@ -249,6 +275,7 @@ __global__ void __launch_bounds__(512) conv2d_kernel(const Conv2DArgs a) {
             });
         }
         __syncthreads();
+        if constexpr (SPEC) continue;  // the next item's S0 writes BUF only after its barriers
 
         // ================= S2: inverse row DFTs (window columns) ==============================
         for (int r0 = 16 * wave; r0 < 16 * wave + 16; r0 += 4) {
@@ -318,11 +345,8 @@ __global__ void __launch_bounds__(512) conv2d_kernel(const Conv2DArgs a) {
 // computed as two explicit DFT-matrix passes in fp32 (one-off, not on the convolution path),
 // stored in the order the column stage reads it: [channel][v][lane][jj], u = lane%16 +
 // 16 (4 (lane/16) + jj).
-// flip = 1: the kernel rotated by 180 degrees, k[Hs-1-a][Ws-1-e] in place of k[a][e] (the filter
-// gradient's correlation as a convolution).
 template <int IO>
-__global__ void __launch_bounds__(256) filter2d_kernel(const void* k, void* kf, float inv_p2, int Hs, int Ws,
-                                                       int flip) {
+__global__ void __launch_bounds__(256) filter2d_kernel(const void* k, void* kf, float inv_p2, int Hs, int Ws) {
     __shared__ float2 T[S2D][32];
     __shared__ float2 W[P2D];
     const int ch = blockIdx.x, vb = blockIdx.y, tid = threadIdx.x;
@@ -338,7 +362,7 @@ __global__ void __launch_bounds__(256) filter2d_kernel(const void* k, void* kf, 
         const int ar = idx / 32, vv = idx % 32, v = 32 * vb + vv;
         float re = 0.f, im = 0.f;
         for (int e = 0; e < Ws; ++e) {
-            const float x = unpack_lo<IO>(flip ? kc[(Hs - 1 - ar) * Ws + (Ws - 1 - e)] : kc[ar * Ws + e]);
+            const float x = unpack_lo<IO>(kc[ar * Ws + e]);
             const float2 w = W[(v * (e + dc)) & (P2D - 1)];
             re += x * w.x;
             im += x * w.y;
@@ -450,18 +474,22 @@ hipError_t launch_conv2d(int dtype, const Conv2DArgs& a, hipStream_t st) {
     if (a.filter) {
         dim3 grid((unsigned)a.C, P2D / 32);
         if (dtype == CT_F16)
-            hipLaunchKernelGGL((filter2d_kernel<CT_F16>), grid, dim3(256), 0, st, a.u, (void*)a.kf, a.inv_p2, a.Hs, a.Ws,
-                               a.flip);
+            hipLaunchKernelGGL((filter2d_kernel<CT_F16>), grid, dim3(256), 0, st, a.u, (void*)a.kf, a.inv_p2, a.Hs, a.Ws);
         else
-            hipLaunchKernelGGL((filter2d_kernel<CT_BF16>), grid, dim3(256), 0, st, a.u, (void*)a.kf, a.inv_p2, a.Hs,
-                               a.Ws, a.flip);
+            hipLaunchKernelGGL((filter2d_kernel<CT_BF16>), grid, dim3(256), 0, st, a.u, (void*)a.kf, a.inv_p2, a.Hs, a.Ws);
         return hipGetLastError();
     }
     const int64_t nitems = (a.B + 1) / 2 * a.C;
     if (nitems <= 0) return hipSuccess;
     const int64_t nwg = nitems < a.cus ? nitems : a.cus;
-    if (dtype == CT_F16) hipLaunchKernelGGL((conv2d_kernel<CT_F16>), dim3((unsigned)nwg), dim3(512), 0, st, a);
-    else hipLaunchKernelGGL((conv2d_kernel<CT_BF16>), dim3((unsigned)nwg), dim3(512), 0, st, a);
+    if (a.spec) {
+        if (a.B != 1) return hipErrorInvalidValue;  // single images only
+        if (dtype == CT_F16) hipLaunchKernelGGL((conv2d_kernel<CT_F16, true>), dim3((unsigned)nwg), dim3(512), 0, st, a);
+        else hipLaunchKernelGGL((conv2d_kernel<CT_BF16, true>), dim3((unsigned)nwg), dim3(512), 0, st, a);
+        return hipGetLastError();
+    }
+    if (dtype == CT_F16) hipLaunchKernelGGL((conv2d_kernel<CT_F16, false>), dim3((unsigned)nwg), dim3(512), 0, st, a);
+    else hipLaunchKernelGGL((conv2d_kernel<CT_BF16, false>), dim3((unsigned)nwg), dim3(512), 0, st, a);
     return hipGetLastError();
 }
 

@@ -118,7 +118,8 @@ struct Conv2DArgs {
     int Hs, Ws;          // image sides: 1 <= Hs <= 128, 8 <= Ws <= 128 with Ws a multiple of 8
     float inv_p2;        // 1 / (2S)^2
     int filter;          // 1: u = k [C][S][S]; the spectrum is written to kf
-    int flip;            // filter mode: 1 takes k rotated by 180 degrees
+    int spec;            // 1 (with B = 1): store the spectrum of each image rotated by 180 degrees,
+                         // as a filter spectrum, to y (the 2D filter gradient's filters)
     int cus;             // compute units (persistent grid size)
 };
 hipError_t launch_conv2d(int dtype, const Conv2DArgs& a, hipStream_t stream);

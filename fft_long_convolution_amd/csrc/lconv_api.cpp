@@ -1240,10 +1240,8 @@ lconv_status_t lconv_fftconv2d_bwd(const void* dy, const void* u, const void* k_
         // per image, dk_b[a][e] = (u_b conv rot(dy_b))[Hs-1-a][Ws-1-e]: the B*C images as channels
         // of one image each, with the rotated dy as their filters and a zero skip
         const int64_t bc = B * C;
-        Conv2DArgs f{};
-        f.u = dy; f.kf = w + L.o_kd; f.C = bc; f.B = 1; f.filter = 1; f.flip = 1;
-        f.Hs = (int)Hs; f.Ws = (int)Ws;
-        f.inv_p2 = 1.0f / (float)(kP2D * kP2D);
+        Conv2DArgs f = a;   // the 2D kernel's row and column transforms in spectrum mode
+        f.u = dy; f.kf = nullptr; f.D = nullptr; f.y = w + L.o_kd; f.B = 1; f.C = bc; f.spec = 1;
         if (launch_conv2d(dtype, f, stream) != hipSuccess) return LCONV_ERR_HIP;
         if (launch_zero_words(w + L.o_zd, (int64_t)((bc * es + 3) / 4), stream) != hipSuccess) return LCONV_ERR_HIP;
         Conv2DArgs c = a;

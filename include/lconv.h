@@ -359,7 +359,8 @@ lconv_status_t lconv_fftconv2d_fwd(const void* u, const void* k_f, const void* D
  * at grid offset 64 moved back to the image at offset 0: a shift by half the 256-point grid),
  * formed from k_f by sign flips alone.  dk runs the forward kernel over the B*C images as
  * channels of one image, each with its own dy rotated by 180 degrees as the filter (spectra in
- * the workspace), and sums the rotated results over the batch in fp32; the per-image
+ * the workspace, from the same kernel's transforms of dy), and sums the rotated results over
+ * the batch in fp32; the per-image
  * correlations pass through the workspace in dtype.  dD is a direct fp32 sum.
  * B = 0 writes zeros to dk and dD.  Outputs must not overlap each other, any input or the
  * workspace.  Supported: as lconv_fftconv2d_fwd.
