@@ -415,17 +415,25 @@ __global__ void __launch_bounds__(256) dk2d_sum_kernel(const void* r, float* dk,
     }
 }
 
-// dD[c] = sum_b sum_pixels dy u in fp32: one workgroup per channel, fixed-order tree reduction.
+// dD[c] = sum_b sum_pixels dy u in fp32: one workgroup per channel, 8 elements per 16-byte load
+// (Ws is a multiple of 8, so every image starts on a 16-byte boundary), fixed-order tree reduction.
 template <int IO>
 __global__ void __launch_bounds__(256) dd2d_kernel(const void* dy, const void* u, float* dD, int64_t B, int64_t C,
                                                    int64_t img) {
-    const int64_t c = blockIdx.x;
+    const int64_t c = blockIdx.x, img8 = img / 8;
     float acc = 0.f;
     for (int64_t b = 0; b < B; ++b) {
-        const int64_t base = (b * C + c) * img;
-        for (int64_t p = threadIdx.x; p < img; p += 256)
-            acc = fmaf(unpack_lo<IO>(((const uint16_t*)dy)[base + p]), unpack_lo<IO>(((const uint16_t*)u)[base + p]),
-                       acc);
+        const uint4* pd = (const uint4*)((const uint16_t*)dy + (b * C + c) * img);
+        const uint4* pu = (const uint4*)((const uint16_t*)u + (b * C + c) * img);
+        for (int64_t p = threadIdx.x; p < img8; p += 256) {
+            const uint4 wd = pd[p], wu = pu[p];
+            const uint32_t d4[4] = {wd.x, wd.y, wd.z, wd.w}, u4[4] = {wu.x, wu.y, wu.z, wu.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc = fmaf(unpack_lo<IO>(d4[i]), unpack_lo<IO>(u4[i]), acc);
+                acc = fmaf(unpack_hi<IO>(d4[i]), unpack_hi<IO>(u4[i]), acc);
+            }
+        }
     }
     __shared__ float red[256];
     red[threadIdx.x] = acc;
